@@ -1,0 +1,160 @@
+"""fp64 CPU oracle of the LT2 gated-delta mixer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never calls it, and it
+shares no code with the library: the recurrence lives in ``lt2_oracle.c`` (plain
+C, fp64, token by token), the looped driver below uses numpy fp64 matrix
+products plus the C recurrence.
+
+Sources (the LT2 pages):
+  * the state update S_t = Diag(alpha_t)(I - beta_t k_t k_t^T) S_{t-1}
+    + beta_t k_t v_t^T -- LT2 explainer (paithon.it), section "Sostituire il
+    motore", the state-update equation;
+  * the looped composition h^(tau) = (F_N o ... o F_1) h^(tau-1), tau = 1..T,
+    with shared weights -- same page, section "Profondita presa in prestito",
+    first equation.
+Readings where the pages are silent (read-out o_t = S_t^T q_t, no output scale,
+per-head L2 normalisation of q and k in the looped block, beta = sigmoid,
+alpha = exp(-softplus), fresh zero state in every loop) are listed with the
+design notes of the repository.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lt2_oracle.c")
+_LIB = os.path.join(_HERE, "liblt2_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile lt2_oracle.c with gcc (fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared",
+                               "-ffp-contract=off", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.lt2o_prefill.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I]
+        lib.lt2o_prefill.restype = I
+        lib.lt2o_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, I]
+        lib.lt2o_decode_step.restype = I
+        lib.lt2o_max_threads.restype = I
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().lt2o_max_threads())
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def prefill(q, k, v, alpha, beta, S0=None, threads: int = 0):
+    """Token-by-token gated delta rule over [B, L, H, *] inputs.
+
+    Returns (o [B,L,H,d_v], S_final [B,H,d_k,d_v]) in fp64.  alpha is [B,L,H]
+    (scalar gate per head) or [B,L,H,d_k] (per-channel gate)."""
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, L, H) and beta.shape == (B, L, H)
+    channel = 1 if alpha.ndim == 4 else 0
+    assert alpha.shape == ((B, L, H, dk) if channel else (B, L, H))
+    S0 = None if S0 is None else _f64(S0)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.empty((B, L, H, dv), np.float64)
+    S = np.empty((B, H, dk, dv), np.float64)
+    rc = _load().lt2o_prefill(B, L, H, dk, dv, channel, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                              _ptr(beta), _ptr(S0), _ptr(o), _ptr(S), int(threads))
+    if rc != 0:
+        raise RuntimeError("lt2o_prefill failed")
+    return o, S
+
+
+def decode_step(q, k, v, alpha, beta, S, threads: int = 0):
+    """One token for every unit: q,k [B,H,d_k], v [B,H,d_v], alpha [B,H] or
+    [B,H,d_k], beta [B,H], S [B,H,d_k,d_v].  Returns (o, S_new) in fp64."""
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    S = _f64(S).copy()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    channel = 1 if alpha.ndim == 3 else 0
+    o = np.empty((B, H, dv), np.float64)
+    rc = _load().lt2o_decode_step(B, H, dk, dv, channel, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                  _ptr(beta), _ptr(S), _ptr(o), int(threads))
+    if rc != 0:
+        raise RuntimeError("lt2o_decode_step failed")
+    return o, S
+
+
+# ---- looped LT2-linear mixer ------------------------------------------------
+
+def _l2norm_heads(x: np.ndarray, H: int, d: int, eps: float = 1e-6) -> np.ndarray:
+    """Per-head L2 normalisation x / max(||x||_2, eps) over the last d entries."""
+    M = x.shape[0]
+    xh = x.reshape(M, H, d)
+    n = np.sqrt((xh * xh).sum(axis=-1, keepdims=True))
+    return (xh / np.maximum(n, eps)).reshape(M, H * d)
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _softplus(z):
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def looped_layer(h, w_in, w_o, H: int, d: int, threads: int = 0):
+    """One loop iteration of the LT2-linear block on a residual stream h [B,L,D]:
+
+        z = h W_in^T;  q,k,v,z_beta,z_alpha = split(z)
+        q, k <- per-head L2 normalisation;  beta = sigmoid(z_beta);
+        alpha = exp(-softplus(z_alpha));  o = GDN(q,k,v,alpha,beta; S_0 = 0)
+        h <- h + o W_o^T
+
+    W_in is [3*H*d + 2*H, D] (rows of W_q, W_k, W_v, W_beta, W_alpha), W_o is
+    [D, H*d].  Everything in fp64."""
+    h = _f64(h)
+    B, L, D = h.shape
+    hd = H * d
+    x = h.reshape(B * L, D)
+    z = x @ _f64(w_in).T
+    q = _l2norm_heads(z[:, 0:hd], H, d)
+    k = _l2norm_heads(z[:, hd:2 * hd], H, d)
+    v = z[:, 2 * hd:3 * hd]
+    beta = _sigmoid(z[:, 3 * hd:3 * hd + H])
+    alpha = np.exp(-_softplus(z[:, 3 * hd + H:3 * hd + 2 * H]))
+    o, _ = prefill(q.reshape(B, L, H, d), k.reshape(B, L, H, d), v.reshape(B, L, H, d),
+                   alpha.reshape(B, L, H), beta.reshape(B, L, H), None, threads)
+    return h + (o.reshape(B * L, hd) @ _f64(w_o).T).reshape(B, L, D)
+
+
+def looped_mixer(h0, w_in, w_o, H: int, d: int, T: int, threads: int = 0):
+    """T loops of ``looped_layer`` with the same weights, h^(tau) = F(h^(tau-1))."""
+    h = _f64(h0)
+    for _ in range(T):
+        h = looped_layer(h, w_in, w_o, H, d, threads)
+    return h

@@ -1,0 +1,350 @@
+"""Pins of the fp64 oracle against facts the LT2 pages and plain algebra fix.
+
+The pages print no worked numerical example of the recurrence, so the oracle is
+pinned by (a) brute force with explicit dense transition matrices A_t and their
+products (LT2 explainer, paithon.it, "Sostituire il motore" state-update
+equation and "Il giro trasforma il calcolo in contesto" product equation), in
+floating point and in exact rational arithmetic; (b) closed forms of special
+cases of that equation; (c) structural invariants (column independence,
+linearity, state passing, loop composition).  Every mistake of the kind a
+recurrence can hide -- a dropped term, a wrong sign, decay applied before the
+erase, a transposed state, an off-by-one read-out -- fails at least one test.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_looped_amd import synth
+
+
+def rand_unit(rng, n, d):
+    x = rng.standard_normal((n, d))
+    return x / np.linalg.norm(x, axis=1, keepdims=True)
+
+
+def unit_case(rng, L, dk, dv, channel):
+    q = rand_unit(rng, L, dk)
+    k = rand_unit(rng, L, dk)
+    v = rng.standard_normal((L, dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal(L)))
+    alpha = rng.uniform(0.05, 1.0, (L, dk) if channel else L)
+    S0 = rng.standard_normal((dk, dv))
+    return q, k, v, alpha, beta, S0
+
+
+def as_batch(q, k, v, alpha, beta, S0):
+    """[L,*] single-unit arrays -> [1,L,1,*] oracle layout."""
+    return (q[None, :, None], k[None, :, None], v[None, :, None],
+            alpha[None, :, None], beta[None, :, None], None if S0 is None else S0[None, None])
+
+
+def run_unit(q, k, v, alpha, beta, S0):
+    o, S = oracle.prefill(*as_batch(q, k, v, alpha, beta, S0))
+    return o[0, :, 0], S[0, 0]
+
+
+def brute_force(q, k, v, alpha, beta, S0):
+    """S_t = (A_t...A_1) S_0 + sum_i (A_t...A_{i+1}) beta_i k_i v_i^T with dense
+    A_j = Diag(alpha_j)(I - beta_j k_j k_j^T); o_t = S_t^T q_t."""
+    L, dk = k.shape
+    A = []
+    for j in range(L):
+        a = np.full(dk, alpha[j]) if np.ndim(alpha[j]) == 0 else alpha[j]
+        A.append(np.diag(a) @ (np.eye(dk) - beta[j] * np.outer(k[j], k[j])))
+
+    def prod(t, i):  # A_t A_{t-1} ... A_{i+1}
+        M = np.eye(dk)
+        for j in range(i + 1, t + 1):
+            M = A[j] @ M
+        return M
+
+    outs = []
+    for t in range(L):
+        S = prod(t, -1) @ S0
+        for i in range(t + 1):
+            S = S + prod(t, i) @ (beta[i] * np.outer(k[i], v[i]))
+        outs.append(S.T @ q[t])
+    return np.array(outs), S
+
+
+# ---- (a) brute force ---------------------------------------------------------
+
+@pytest.mark.parametrize("channel", [0, 1])
+@pytest.mark.parametrize("L,dk,dv", [(1, 3, 2), (5, 4, 3), (8, 6, 5)])
+def test_brute_force_product_expansion(channel, L, dk, dv):
+    rng = np.random.default_rng(100 + 10 * L + channel)
+    case = unit_case(rng, L, dk, dv, channel)
+    o, S = run_unit(*case)
+    o_bf, S_bf = brute_force(*case)
+    np.testing.assert_allclose(o, o_bf, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(S, S_bf, rtol=0, atol=1e-13)
+
+
+def test_exact_rational_tiny_case():
+    """Exact Fraction arithmetic of the state-update equation, per-channel gate,
+    unnormalised keys, non-zero S_0: agreement to fp64 rounding."""
+    F = Fraction
+    k = [[F(1), F(2)], [F(-1, 2), F(1, 3)], [F(3, 4), F(-1)]]
+    v = [[F(1), F(-2), F(1, 2)], [F(2), F(0), F(-1)], [F(-1, 3), F(1), F(1)]]
+    q = [[F(1, 2), F(1)], [F(0), F(-1)], [F(2), F(1, 5)]]
+    beta = [F(1, 2), F(1, 3), F(3, 4)]
+    alpha = [[F(1, 2), F(3, 4)], [F(1), F(1, 5)], [F(2, 3), F(1, 2)]]
+    S = [[F(1), F(0), F(-1)], [F(1, 2), F(2), F(1, 4)]]
+    S0 = [row[:] for row in S]
+    outs = []
+    for t in range(3):
+        # A_t S = Diag(alpha)(S - beta k (k^T S)); then + beta k v^T
+        kS = [sum(k[t][i] * S[i][j] for i in range(2)) for j in range(3)]
+        S = [[alpha[t][i] * (S[i][j] - beta[t] * k[t][i] * kS[j]) + beta[t] * k[t][i] * v[t][j]
+              for j in range(3)] for i in range(2)]
+        outs.append([sum(S[i][j] * q[t][i] for i in range(2)) for j in range(3)])
+    f = lambda m: np.array([[float(x) for x in r] for r in m])
+    o, S_fin = run_unit(f(q), f(k), f(v), f(alpha), np.array([float(b) for b in beta]), f(S0))
+    np.testing.assert_allclose(o, f(outs), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(S_fin, f(S), rtol=0, atol=1e-15)
+
+
+# ---- (b) closed forms ---------------------------------------------------------
+
+def test_alpha1_beta0_leaves_state_unchanged():
+    rng = np.random.default_rng(1)
+    q, k, v, _, _, S0 = unit_case(rng, 7, 5, 4, 0)
+    o, S = run_unit(q, k, v, np.ones(7), np.zeros(7), S0)
+    np.testing.assert_array_equal(S, S0)
+    np.testing.assert_allclose(o, q @ S0, atol=1e-15)
+
+
+def test_delta_write_recalls_value_exactly():
+    """alpha=1, beta=1, ||k||=1: the new state maps k_t to v_t."""
+    rng = np.random.default_rng(2)
+    L, dk, dv = 6, 8, 5
+    q, k, v, _, _, S0 = unit_case(rng, L, dk, dv, 0)
+    S = S0
+    for t in range(L):
+        _, S = run_unit(q[t:t + 1], k[t:t + 1], v[t:t + 1], np.ones(1), np.ones(1), S)
+        np.testing.assert_allclose(S.T @ k[t], v[t], atol=1e-13)
+
+
+@pytest.mark.parametrize("channel", [0, 1])
+def test_beta0_pure_decay(channel):
+    rng = np.random.default_rng(3 + channel)
+    L, dk, dv = 9, 6, 4
+    q, k, v, alpha, _, S0 = unit_case(rng, L, dk, dv, channel)
+    o, S = run_unit(q, k, v, alpha, np.zeros(L), S0)
+    a = alpha if channel else np.repeat(alpha[:, None], dk, axis=1)
+    gamma = np.cumprod(a, axis=0)  # [L, dk]
+    np.testing.assert_allclose(S, gamma[-1][:, None] * S0, atol=1e-14)
+    np.testing.assert_allclose(o, (gamma * q) @ S0, atol=1e-14)
+
+
+def test_alpha0_keeps_only_current_write():
+    rng = np.random.default_rng(5)
+    L, dk, dv = 7, 5, 6
+    q, k, v, _, beta, S0 = unit_case(rng, L, dk, dv, 0)
+    o, S = run_unit(q, k, v, np.zeros(L), beta, S0)
+    np.testing.assert_allclose(S, beta[-1] * np.outer(k[-1], v[-1]), atol=1e-15)
+    np.testing.assert_allclose(o, (beta * (q * k).sum(1))[:, None] * v, atol=1e-15)
+
+
+def test_orthonormal_keys_replace_state_directions():
+    rng = np.random.default_rng(6)
+    dk, dv, L = 8, 5, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:, :L].T
+    q = rand_unit(rng, L, dk)
+    v = rng.standard_normal((L, dv))
+    S0 = rng.standard_normal((dk, dv))
+    _, S = run_unit(q, k, v, np.ones(L), np.ones(L), S0)
+    expect = (np.eye(dk) - k.T @ k) @ S0 + k.T @ v
+    np.testing.assert_allclose(S, expect, atol=1e-13)
+
+
+def test_erase_precedes_decay_per_channel():
+    """Diag(alpha)(I - beta k k^T): the erase acts on the undecayed state and the
+    write is not decayed.  One token, S_0 = e_0 v0^T, k = e_0 + e_1 (unnormalised)."""
+    dk, dv = 2, 1
+    S0 = np.array([[1.0], [0.0]])
+    k = np.array([[1.0, 1.0]])
+    v = np.array([[0.0]])
+    alpha = np.array([[0.5, 0.25]])
+    beta = np.array([1.0])
+    _, S = run_unit(np.zeros((1, dk)), k, v, alpha, beta, S0)
+    # k^T S0 = 1; S0 - k*1 = [0, -1]; Diag(alpha) -> [0, -0.25]
+    np.testing.assert_allclose(S, [[0.0], [-0.25]], atol=1e-16)
+
+
+# ---- (c) structural invariants ----------------------------------------------
+
+@pytest.mark.parametrize("channel", [0, 1])
+def test_column_independence(channel):
+    rng = np.random.default_rng(7)
+    q, k, v, alpha, beta, S0 = unit_case(rng, 20, 6, 8, channel)
+    o, S = run_unit(q, k, v, alpha, beta, S0)
+    for lo, hi in [(0, 3), (3, 8)]:
+        o2, S2 = run_unit(q, k, v[:, lo:hi], alpha, beta, S0[:, lo:hi])
+        np.testing.assert_array_equal(o2, o[:, lo:hi])
+        np.testing.assert_array_equal(S2, S[:, lo:hi])
+
+
+def test_linearity_in_state_and_values():
+    rng = np.random.default_rng(8)
+    q, k, v, alpha, beta, S0 = unit_case(rng, 15, 5, 4, 1)
+    v2, S02 = rng.standard_normal(v.shape), rng.standard_normal(S0.shape)
+    a, b = 0.7, -1.3
+    o1, S1 = run_unit(q, k, v, alpha, beta, S0)
+    o2, S2 = run_unit(q, k, v2, alpha, beta, S02)
+    o3, S3 = run_unit(q, k, a * v + b * v2, alpha, beta, a * S0 + b * S02)
+    np.testing.assert_allclose(o3, a * o1 + b * o2, atol=1e-12)
+    np.testing.assert_allclose(S3, a * S1 + b * S2, atol=1e-12)
+
+
+@pytest.mark.parametrize("channel", [0, 1])
+def test_state_passing_and_decode_chain(channel):
+    rng = np.random.default_rng(9)
+    L, L1 = 24, 10
+    q, k, v, alpha, beta, S0 = unit_case(rng, L, 6, 5, channel)
+    o, S = run_unit(q, k, v, alpha, beta, S0)
+    oa, Sa = run_unit(q[:L1], k[:L1], v[:L1], alpha[:L1], beta[:L1], S0)
+    ob, Sb = run_unit(q[L1:], k[L1:], v[L1:], alpha[L1:], beta[L1:], Sa)
+    np.testing.assert_array_equal(np.concatenate([oa, ob]), o)
+    np.testing.assert_array_equal(Sb, S)
+    St = S0[None, None].copy()
+    for t in range(L):
+        a = alpha[t][None, None]
+        ot, St = oracle.decode_step(q[t][None, None], k[t][None, None], v[t][None, None],
+                                    a, beta[t][None, None], St)
+        np.testing.assert_array_equal(ot[0, 0], o[t])
+    np.testing.assert_array_equal(St[0, 0], S)
+
+
+def test_batch_layout_and_thread_count():
+    """Units of a [B,L,H,*] batch equal single-unit runs; thread count changes nothing."""
+    shape = synth.GDNShape(2, 33, 3, 8, 6, "channel", 2.0, "f32")
+    x = synth.gdn_inputs(shape, seed=4)
+    S0 = np.random.default_rng(4).standard_normal((2, 3, 8, 6))
+    o1, S1 = oracle.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S0, threads=1)
+    o4, S4 = oracle.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S0, threads=4)
+    np.testing.assert_array_equal(o1, o4)
+    np.testing.assert_array_equal(S1, S4)
+    for b in range(2):
+        for h in range(3):
+            u = synth.gdn_unit(shape, 4, b, h)
+            ou, Su = run_unit(u["q"].astype(float), u["k"].astype(float), u["v"].astype(float),
+                              u["alpha"].astype(float), u["beta"].astype(float), S0[b, h])
+            np.testing.assert_array_equal(ou, o1[b, :, h])
+            np.testing.assert_array_equal(Su, S1[b, h])
+
+
+def test_single_pass_decode_formula():
+    """The one-pass read-out used by a fused decode step,
+    o = S^T(alpha*q) - beta (q.(alpha*k)) S^T k + beta (q.k) v, equals S_new^T q."""
+    rng = np.random.default_rng(10)
+    for channel in (0, 1):
+        q, k, v, alpha, beta, S0 = unit_case(rng, 1, 7, 5, channel)
+        o, _ = run_unit(q, k, v, alpha, beta, S0)
+        a = alpha[0] if channel else np.full(7, alpha[0])
+        kS = S0.T @ k[0]
+        o1 = S0.T @ (a * q[0]) - beta[0] * (q[0] @ (a * k[0])) * kS + beta[0] * (q[0] @ k[0]) * v[0]
+        np.testing.assert_allclose(o[0], o1, atol=1e-14)
+
+
+def test_empty_sequence_returns_initial_state():
+    rng = np.random.default_rng(11)
+    S0 = rng.standard_normal((1, 2, 4, 3))
+    z = np.zeros((1, 0, 2, 4))
+    o, S = oracle.prefill(z, z, np.zeros((1, 0, 2, 3)), np.zeros((1, 0, 2)), np.zeros((1, 0, 2)), S0)
+    assert o.shape == (1, 0, 2, 3)
+    np.testing.assert_array_equal(S, S0)
+
+
+# ---- looped driver -------------------------------------------------------------
+
+def brute_layer(h, w_in, w_o, H, d):
+    """Independent loop iteration: einsum projections, scipy gates, dense-A recurrence."""
+    from scipy.special import expit
+    B, L, D = h.shape
+    hd = H * d
+    z = np.einsum("bld,nd->bln", h, w_in)
+    out = h.copy()
+    for b in range(B):
+        o_all = np.zeros((L, hd))
+        for hh in range(H):
+            q = z[b, :, hh * d:(hh + 1) * d]
+            k = z[b, :, hd + hh * d:hd + (hh + 1) * d]
+            v = z[b, :, 2 * hd + hh * d:2 * hd + (hh + 1) * d]
+            q = q / np.linalg.norm(q, axis=1, keepdims=True)
+            k = k / np.linalg.norm(k, axis=1, keepdims=True)
+            beta = expit(z[b, :, 3 * hd + hh])
+            alpha = expit(-z[b, :, 3 * hd + H + hh])  # exp(-softplus(z)) = sigmoid(-z)
+            o, _ = brute_force(q, k, v, alpha, beta, np.zeros((d, d)))
+            o_all[:, hh * d:(hh + 1) * d] = o
+        out[b] = h[b] + np.einsum("lk,dk->ld", o_all, w_o)
+    return out
+
+
+def small_loop_case(seed=12, B=2, L=6, D=8, H=2, d=3):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((B, L, D))
+    w_in = rng.standard_normal((3 * H * d + 2 * H, D)) / np.sqrt(D)
+    w_o = rng.standard_normal((D, H * d)) / np.sqrt(H * d)
+    return h, w_in, w_o, H, d
+
+
+def test_looped_layer_matches_brute_force():
+    h, w_in, w_o, H, d = small_loop_case()
+    np.testing.assert_allclose(oracle.looped_layer(h, w_in, w_o, H, d),
+                               brute_layer(h, w_in, w_o, H, d), atol=1e-12)
+
+
+def test_looped_mixer_is_composition_of_layers():
+    h, w_in, w_o, H, d = small_loop_case(13)
+    h2 = brute_layer(brute_layer(brute_layer(h, w_in, w_o, H, d), w_in, w_o, H, d), w_in, w_o, H, d)
+    np.testing.assert_allclose(oracle.looped_mixer(h, w_in, w_o, H, d, 3), h2, atol=1e-11)
+    np.testing.assert_array_equal(oracle.looped_mixer(h, w_in, w_o, H, d, 0), h)
+
+
+def test_looped_mixer_zero_value_or_output_weights_is_identity():
+    h, w_in, w_o, H, d = small_loop_case(14)
+    w_in0 = w_in.copy()
+    w_in0[2 * H * d:3 * H * d] = 0.0  # W_v = 0
+    np.testing.assert_array_equal(oracle.looped_mixer(h, w_in0, w_o, H, d, 4), h)
+    np.testing.assert_array_equal(oracle.looped_mixer(h, w_in, np.zeros_like(w_o), H, d, 4), h)
+
+
+def test_looped_layer_causal():
+    """Token t of the output depends only on tokens <= t (prefix computation)."""
+    h, w_in, w_o, H, d = small_loop_case(15, L=9)
+    full = oracle.looped_mixer(h, w_in, w_o, H, d, 2)
+    pre = oracle.looped_mixer(h[:, :5], w_in, w_o, H, d, 2)
+    np.testing.assert_allclose(pre, full[:, :5], atol=1e-13)
+
+
+# ---- input generators (not the method, but both sides read them) --------------
+
+def test_bf16_round_matches_torch():
+    import torch
+    rng = np.random.default_rng(16)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 100000),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.0e38, -1e-40], np.float32)])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(synth.bf16_round(x), ref)
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(synth.bf16_bits(synth.bf16_round(x)), bits)
+
+
+def test_generators_recipe():
+    shape = synth.GDNShape(1, 512, 2, 16, 16, "head", 2.0, "bf16")
+    x = synth.gdn_inputs(shape, seed=0)
+    nk = np.linalg.norm(x["k"], axis=-1)
+    assert np.all(np.abs(nk - 1) < 1e-2)
+    np.testing.assert_array_equal(synth.bf16_round(x["q"]), x["q"])
+    assert 0 < x["beta"].min() and x["beta"].max() < 1
+    assert 0.1 < x["alpha"].mean() < 0.2  # exp(-softplus(N(0,1)+2)) has mean ~0.155
+    y = synth.gdn_inputs(shape, seed=0)
+    for key in x:
+        np.testing.assert_array_equal(x[key], y[key])
+    u = synth.gdn_unit(shape, 0, 0, 1)
+    np.testing.assert_array_equal(u["v"], x["v"][0, :, 1])
