@@ -1,0 +1,157 @@
+/*
+ * lt2.h -- C ABI of liblt2.so, the MI355X (gfx950) gated-delta mixer of LT2
+ * (Linear-Time Looped Transformers).
+ *
+ * The operation (LT2 explainer, paithon.it, section "Sostituire il motore",
+ * the state-update equation):
+ *
+ *     S_t = Diag(alpha_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                     (read-out after the update, no scale)
+ *
+ * per (batch, head) unit, with an fp32 d_k x d_v state.  alpha_t is one value
+ * per head (GDN, "scalar gate") or one value per key channel (KDA form,
+ * "channel gate"); Diag(alpha_t) scales the rows of the state, after the
+ * erase, and the write beta_t k_t v_t^T is not decayed.  The looped driver
+ * applies one shared-weight block T times (same page, section "Profondita
+ * presa in prestito", first equation).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; it only enqueues kernels on
+ *    `stream` (a hipStream_t passed as void*, NULL = the null stream).
+ *  - Every call validates all arguments before enqueueing anything.  On any
+ *    error nothing is launched and no output is touched.  A launch failure
+ *    reported by the HIP runtime maps to LT2_ERR_HIP.
+ *  - Row-major layouts, innermost dimension contiguous, no padding:
+ *        q, k      [B, L, H, d_k]          token-major
+ *        v, out    [B, L, H, d_v]
+ *        beta      [B, L, H]    fp32, in [0, 1]
+ *        alpha     [B, L, H]    fp32 (scalar gate) or [B, L, H, d_k] (channel
+ *                  gate), in [0, 1]; alpha = 0 is allowed (log alpha is
+ *                  clamped at -80 inside, a factor below 2e-35)
+ *        state     [B, H, d_k, d_v] fp32
+ *  - q and k are used exactly as given: no normalisation inside the mixer
+ *    (the looped driver normalises its own projections).
+ *  - Pointers to q, k, v, out and states must be 16-byte aligned, alpha and
+ *    beta 4-byte aligned (LT2_ERR_ALIGN otherwise).
+ *  - Supported sizes: d_k == d_v in {64, 128}; chunk in {16, 32, 64} (prefill);
+ *    any L >= 0 (a ragged last chunk is masked); B >= 0, H >= 1.
+ *  - The library is stateless and re-entrant; calls on one stream run in order.
+ */
+#ifndef LT2_H
+#define LT2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lt2_status {
+    LT2_OK = 0,
+    LT2_ERR_NULL = 1,        /* a required pointer is NULL */
+    LT2_ERR_SHAPE = 2,       /* negative or inconsistent sizes */
+    LT2_ERR_DTYPE = 3,       /* unknown element type */
+    LT2_ERR_UNSUPPORTED = 4, /* valid but not built: head size, chunk, gate */
+    LT2_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+    LT2_ERR_ALIGN = 6,       /* pointer misaligned for its vector loads */
+    LT2_ERR_HIP = 7          /* the HIP runtime reported a launch error */
+} lt2_status;
+
+typedef enum lt2_dtype { LT2_F32 = 0, LT2_BF16 = 1 } lt2_dtype;
+
+typedef enum lt2_gate {
+    LT2_GATE_HEAD = 0,    /* alpha [B, L, H]: one decay per head and token (GDN) */
+    LT2_GATE_CHANNEL = 1  /* alpha [B, L, H, d_k]: one decay per key channel (KDA) */
+} lt2_gate;
+
+/* Shape and types of one gated-delta call. */
+typedef struct lt2_gdn_desc {
+    int32_t B, L, H;     /* batch, tokens, heads */
+    int32_t d_k, d_v;    /* key and value head size */
+    int32_t chunk;       /* prefill chunk length C (16, 32 or 64); ignored by decode */
+    int32_t qkv_dtype;   /* lt2_dtype of q, k and v */
+    int32_t out_dtype;   /* lt2_dtype of out */
+    int32_t gate;        /* lt2_gate */
+} lt2_gdn_desc;
+
+/* Shape of the looped LT2-linear block. */
+typedef struct lt2_loop_desc {
+    int32_t B, L;        /* sequences, tokens per sequence */
+    int32_t d_model;     /* residual width D */
+    int32_t H, d_head;   /* heads and head size (d_k = d_v = d_head) */
+    int32_t T;           /* loops with shared weights */
+    int32_t chunk;       /* prefill chunk length of the mixer */
+} lt2_loop_desc;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *lt2_status_string(lt2_status s);
+
+/*
+ * Workspace bytes lt2_gdn_prefill needs for `desc` (0 if none).  Returns 0 for
+ * an invalid descriptor (lt2_gdn_prefill then reports the error).
+ */
+size_t lt2_gdn_prefill_workspace_size(const lt2_gdn_desc *desc);
+
+/*
+ * Chunked prefill: run the recurrence over all L tokens of every (b, h) unit.
+ *   q, k, v     inputs, element type desc->qkv_dtype, layouts above
+ *   alpha, beta fp32 gates
+ *   state_in    initial state [B,H,d_k,d_v] fp32, or NULL for S_0 = 0
+ *   out         o_t for every token, element type desc->out_dtype
+ *   state_out   final state S_L, or NULL; may equal state_in (in-place)
+ *   ws/ws_bytes device workspace of at least lt2_gdn_prefill_workspace_size()
+ * Inside each chunk of C tokens the state-independent part (the WY/UT factors
+ * of the chunk) is formed in parallel over chunks; the state is then carried
+ * across chunks in fp32, one chunk after the other per unit.
+ */
+lt2_status lt2_gdn_prefill(const lt2_gdn_desc *desc, const void *q, const void *k,
+                           const void *v, const float *alpha, const float *beta,
+                           const float *state_in, void *out, float *state_out,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One decode token (desc->L must be 1) for every (b, h) unit, state updated in
+ * place.  q, k [B,H,d_k], v, out [B,H,d_v] (element types from desc),
+ * alpha [B,H] or [B,H,d_k], beta [B,H] fp32, state [B,H,d_k,d_v] fp32.
+ * The state is read once and written once.  No workspace.
+ */
+lt2_status lt2_gdn_decode_step(const lt2_gdn_desc *desc, const void *q, const void *k,
+                               const void *v, const float *alpha, const float *beta,
+                               float *state, void *out, void *stream);
+
+/*
+ * Workspace bytes lt2_looped_mixer needs (0 for an invalid descriptor).
+ */
+size_t lt2_looped_mixer_workspace_size(const lt2_loop_desc *desc);
+
+/*
+ * T loops of the LT2-linear block with shared weights, fresh zero state in
+ * every loop:
+ *     z = bf16(h) W_in^T                      [B*L, 3*H*d + 2*H]
+ *     q, k = per-head L2 normalisation of z's first two H*d blocks
+ *            (x / max(||x||_2, 1e-6)), v = third block
+ *     beta = sigmoid(z_beta), alpha = exp(-softplus(z_alpha))  (one per head)
+ *     o = gated-delta prefill(q, k, v, alpha, beta; S_0 = 0)    bf16
+ *     h = h + o W_o^T                          fp32 residual stream
+ *   h_in, h_out   [B, L, d_model] fp32 (may be the same buffer)
+ *   W_in          [3*H*d + 2*H, d_model] bf16, rows W_q, W_k, W_v, W_beta, W_alpha
+ *   W_o           [d_model, H*d] bf16
+ * Requirements: d_model % 128 == 0, H*d % 128 == 0, d in {64, 128}.
+ */
+lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *h_in, float *h_out,
+                            const void *W_in, const void *W_o, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * Bandwidth probe: copy `bytes` (a multiple of 16) from src to dst with one
+ * streaming kernel.  Used to measure the achievable HBM bandwidth.
+ */
+lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LT2_H */

@@ -1,0 +1,8 @@
+"""MI355X (gfx950) gated-delta mixer of LT2 (Linear-Time Looped Transformers).
+
+The compute lives in liblt2.so (hand-written HIP, C ABI in include/lt2.h);
+this package only builds it (``build``), binds it (``lt2``) and draws seeded
+synthetic inputs (``synth``).
+"""
+from .lt2 import (Lt2Error, lt2_gdn_decode_step, lt2_gdn_prefill, lt2_gdn_prefill_workspace_size,  # noqa: F401
+                  lt2_hbm_copy, lt2_looped_mixer, lt2_looped_mixer_workspace_size, status_string)

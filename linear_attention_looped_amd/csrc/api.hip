@@ -1,0 +1,134 @@
+// api.hip -- extern "C" entry points of liblt2.so (declared in include/lt2.h).
+//
+// Every entry point validates its whole argument list on the host before it
+// enqueues anything, so an error leaves all outputs untouched.
+#include "lt2.h"
+
+#include "internal.h"
+
+using namespace lt2;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+lt2_status check_desc(const lt2_gdn_desc *d, bool decode) {
+    if (!d) return LT2_ERR_NULL;
+    if (d->B < 0 || d->L < 0 || d->H <= 0 || d->d_k <= 0 || d->d_v <= 0) return LT2_ERR_SHAPE;
+    if (decode && d->L != 1) return LT2_ERR_SHAPE;
+    if ((d->qkv_dtype != LT2_F32 && d->qkv_dtype != LT2_BF16) ||
+        (d->out_dtype != LT2_F32 && d->out_dtype != LT2_BF16))
+        return LT2_ERR_DTYPE;
+    if (d->gate != LT2_GATE_HEAD && d->gate != LT2_GATE_CHANNEL) return LT2_ERR_UNSUPPORTED;
+    if (d->d_k != d->d_v || (d->d_k != 64 && d->d_k != 128)) return LT2_ERR_UNSUPPORTED;
+    if (!decode && d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return LT2_ERR_UNSUPPORTED;
+    // index arithmetic inside the kernels is 64-bit for element offsets; the
+    // grid dimensions must fit their 32-bit and 65535 limits
+    if ((int64_t)d->B * d->H > 0x7fffffffLL) return LT2_ERR_SHAPE;
+    if (!decode && (d->H > 65535 || d->B > 65535)) return LT2_ERR_SHAPE;
+    return LT2_OK;
+}
+
+GdnArgs make_args(const lt2_gdn_desc *d, const void *q, const void *k, const void *v, const float *alpha,
+                  const float *beta, const float *state_in, void *out, float *state_out, void *ws) {
+    GdnArgs a;
+    a.B = d->B; a.L = d->L; a.H = d->H; a.dk = d->d_k; a.dv = d->d_v; a.chunk = d->chunk;
+    a.qkv_bf16 = d->qkv_dtype == LT2_BF16;
+    a.out_bf16 = d->out_dtype == LT2_BF16;
+    a.channel = d->gate == LT2_GATE_CHANNEL;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.state_in = state_in; a.out = out; a.state_out = state_out; a.ws = ws;
+    return a;
+}
+
+size_t prefill_ws(const lt2_gdn_desc *d) {
+    if (d->gate == LT2_GATE_CHANNEL) return prefill_channel_ws_bytes(d->B, d->L, d->H, d->d_k, d->chunk);
+    return prefill_head_ws_bytes(d->B, d->L, d->H, d->chunk);
+}
+
+lt2_status hip_status(hipError_t e) { return e == hipSuccess ? LT2_OK : LT2_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *lt2_status_string(lt2_status s) {
+    switch (s) {
+        case LT2_OK: return "ok";
+        case LT2_ERR_NULL: return "required pointer is NULL";
+        case LT2_ERR_SHAPE: return "invalid or inconsistent shape";
+        case LT2_ERR_DTYPE: return "unknown element type";
+        case LT2_ERR_UNSUPPORTED: return "unsupported configuration (head size, chunk or gate)";
+        case LT2_ERR_WORKSPACE: return "workspace missing or too small";
+        case LT2_ERR_ALIGN: return "pointer not aligned for vector access";
+        case LT2_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t lt2_gdn_prefill_workspace_size(const lt2_gdn_desc *desc) {
+    if (check_desc(desc, false) != LT2_OK) return 0;
+    if (desc->B == 0 || desc->L == 0) return 0;
+    return prefill_ws(desc);
+}
+
+lt2_status lt2_gdn_prefill(const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta, const float *state_in, void *out,
+                           float *state_out, void *ws, size_t ws_bytes, void *stream) {
+    lt2_status st = check_desc(desc, false);
+    if (st != LT2_OK) return st;
+    const bool work = desc->B > 0 && desc->L > 0;
+    if (work && (!q || !k || !v || !alpha || !beta || !out)) return LT2_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(state_in, 16) || !aligned(state_out, 16) || !aligned(alpha, 4) || !aligned(beta, 4))
+        return LT2_ERR_ALIGN;
+    const size_t need = work ? prefill_ws(desc) : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 16)) return LT2_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (desc->B == 0) return LT2_OK;
+    if (desc->L == 0) {
+        if (!state_out) return LT2_OK;
+        const size_t n = (size_t)desc->B * desc->H * desc->d_k * desc->d_v;
+        return hip_status(launch_state_init(state_out, state_in, n, s));
+    }
+    if (desc->gate == LT2_GATE_CHANNEL) return LT2_ERR_UNSUPPORTED;
+    GdnArgs a = make_args(desc, q, k, v, alpha, beta, state_in, out, state_out, ws);
+    return hip_status(a.channel ? launch_prefill_channel(a, s) : launch_prefill_head(a, s));
+}
+
+lt2_status lt2_gdn_decode_step(const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta, float *state, void *out,
+                               void *stream) {
+    lt2_status st = check_desc(desc, true);
+    if (st != LT2_OK) return st;
+    if (desc->B > 0 && (!q || !k || !v || !alpha || !beta || !state || !out)) return LT2_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(state, 16) ||
+        !aligned(alpha, 4) || !aligned(beta, 4))
+        return LT2_ERR_ALIGN;
+    if (desc->B == 0) return LT2_OK;
+    GdnArgs a = make_args(desc, q, k, v, alpha, beta, state, out, state, nullptr);
+    return hip_status(launch_decode(a, (hipStream_t)stream));
+}
+
+lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream) {
+    if (bytes == 0) return LT2_OK;
+    if (!dst || !src) return LT2_ERR_NULL;
+    if (bytes % 16 != 0) return LT2_ERR_SHAPE;
+    if (!aligned(dst, 16) || !aligned(src, 16)) return LT2_ERR_ALIGN;
+    return hip_status(launch_copy(dst, src, bytes, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t lt2_looped_mixer_workspace_size(const lt2_loop_desc *) { return 0; }
+
+lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *, float *, const void *, const void *, void *,
+                            size_t, void *) {
+    if (!desc) return LT2_ERR_NULL;
+    return LT2_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

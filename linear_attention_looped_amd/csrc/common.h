@@ -1,0 +1,132 @@
+// common.h -- device helpers shared by the gfx950 kernels of liblt2.
+//
+// Matrix-core (MFMA) fragments.  Every contraction is cut into 16x16 output
+// tiles and K-blocks of 32.  For one K-block each lane of a 64-wide wave holds
+// eight consecutive K values of one A row and of one B column:
+//     A[i][k]: lane = i + 16*(k/8), slot k%8     (i < 16, k < 32)
+//     B[k][j]: lane = j + 16*(k/8), slot k%8
+// and the accumulator holds D[4*(lane/16) + r][lane%16] in register r.
+// That is the operand layout of v_mfma_f32_16x16x32_bf16.  The fp32 path
+// issues eight v_mfma_f32_16x16x4_f32 over the same fragments (slot s of every
+// lane in instruction s), which sums the same 32 products in another order.
+//
+// bf16 operands that are not exactly representable (fp32 intermediates such
+// as the state) are split into hi = bf16(x) and lo = bf16(x - hi); a product
+// then takes hi*hi + lo*hi + hi*lo, which keeps about 16 significant bits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lt2 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+enum Prec { PREC_F32 = 0, PREC_BF16 = 1 };
+
+struct Frag {
+    float x[8];
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void split_bf16(const Frag &a, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        __bf16 h = (__bf16)a.x[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(a.x[e] - (float)h);
+    }
+}
+
+__device__ __forceinline__ void to_bf16(const Frag &a, bf16x8 &hi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hi[e] = (__bf16)a.x[e];
+}
+
+// acc += A-block * B-block for one K-block of 32.
+// A_EXACT / B_EXACT: the operand holds bf16-representable values (inputs).
+template <int PREC, bool A_EXACT, bool B_EXACT>
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag &a, const Frag &b) {
+    if constexpr (PREC == PREC_F32) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[s], b.x[s], acc, 0, 0, 0);
+    } else {
+        bf16x8 ah, al, bh, bl;
+        if constexpr (A_EXACT) to_bf16(a, ah); else split_bf16(a, ah, al);
+        if constexpr (B_EXACT) to_bf16(b, bh); else split_bf16(b, bh, bl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        if constexpr (!A_EXACT) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+        if constexpr (!B_EXACT) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    }
+}
+
+// Fragment loads: eight consecutive floats from a row of an fp32 buffer.
+__device__ __forceinline__ void load_frag_f32(Frag &f, const float *p) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    f.x[0] = a.x; f.x[1] = a.y; f.x[2] = a.z; f.x[3] = a.w;
+    f.x[4] = b.x; f.x[5] = b.y; f.x[6] = b.z; f.x[7] = b.w;
+}
+
+// Eight floats with a stride (column of a row-major LDS buffer).
+__device__ __forceinline__ void load_frag_strided(Frag &f, const float *p, int stride) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.x[e] = p[e * stride];
+}
+
+__device__ __forceinline__ void zero_frag(Frag &f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.x[e] = 0.f;
+}
+
+// Eight consecutive elements of a global input row, widened to fp32.
+template <typename T>
+__device__ __forceinline__ void load_row8(Frag &f, const T *p);
+
+template <>
+__device__ __forceinline__ void load_row8<float>(Frag &f, const float *p) {
+    load_frag_f32(f, p);
+}
+
+template <>
+__device__ __forceinline__ void load_row8<uint16_t>(Frag &f, const uint16_t *p) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.x[2 * i] = __uint_as_float(w[i] << 16);
+        f.x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ float load1(const T *p);
+template <>
+__device__ __forceinline__ float load1<float>(const float *p) { return *p; }
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+
+template <typename T>
+__device__ __forceinline__ void store1(T *p, float x);
+template <>
+__device__ __forceinline__ void store1<float>(float *p, float x) { *p = x; }
+template <>
+__device__ __forceinline__ void store1<uint16_t>(uint16_t *p, float x) { *p = f32_to_bf16(x); }
+
+// log(alpha) with alpha = 0 mapped to a finite -80 (a factor below 2e-35).
+__device__ __forceinline__ float log_gate(float a) {
+    return fmaxf(logf(fmaxf(a, 1e-38f)), -80.f);
+}
+
+}  // namespace lt2

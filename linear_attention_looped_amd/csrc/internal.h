@@ -1,0 +1,31 @@
+// internal.h -- launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lt2 {
+
+struct GdnArgs {
+    int B, L, H, dk, dv, chunk;
+    int qkv_bf16, out_bf16, channel;
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    const float *state_in;
+    void *out;
+    float *state_out;
+    void *ws;
+};
+
+// Each launcher returns hipSuccess or the launch error; shapes are already
+// validated by the caller.
+hipError_t launch_decode(const GdnArgs &a, hipStream_t s);
+size_t prefill_head_ws_bytes(int B, int L, int H, int C);
+hipError_t launch_prefill_head(const GdnArgs &a, hipStream_t s);
+size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C);
+hipError_t launch_prefill_channel(const GdnArgs &a, hipStream_t s);
+hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t s);
+
+}  // namespace lt2

@@ -1,0 +1,108 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/lt2.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_looped_amd import lt2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "lt2.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lt2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "lt2_gdn_prefill" in names and "lt2_gdn_decode_step" in names and "lt2_looped_mixer" in names
+    L = lt2.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in range(8):
+        assert lt2.status_string(code)
+    assert lt2.status_string(99) == "unknown status"
+
+
+def prefill(desc, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s_in=None, out=FAKE, s_out=None, ws=FAKE,
+            ws_bytes=1 << 40):
+    P = ctypes.c_void_p
+    return lt2.lib().lt2_gdn_prefill(ctypes.byref(desc), P(q), P(k), P(v), P(a), P(b), P(s_in), P(out),
+                                     P(s_out), P(ws), ws_bytes, None)
+
+
+def good_desc(**kw):
+    d = dict(B=2, L=100, H=3, d_k=128, d_v=128, chunk=64, qkv_dtype=1, out_dtype=1, gate=0)
+    d.update(kw)
+    return lt2.lt2_gdn_desc(*[d[n] for n, _ in lt2.lt2_gdn_desc._fields_])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), 2), (dict(L=-5), 2), (dict(H=0), 2), (dict(d_k=0), 2),
+    (dict(qkv_dtype=7), 3), (dict(out_dtype=-1), 3),
+    (dict(d_k=96, d_v=96), 4), (dict(d_k=64, d_v=128), 4), (dict(chunk=48), 4), (dict(chunk=128), 4),
+    (dict(gate=5), 4),
+])
+def test_prefill_rejects_bad_descriptor(kw, code):
+    assert prefill(good_desc(**kw)) == code
+
+
+def test_prefill_rejects_null_misaligned_and_small_workspace():
+    d = good_desc()
+    assert lt2.lib().lt2_gdn_prefill(None, None, None, None, None, None, None, None, None, None, 0, None) == 1
+    assert prefill(d, q=None) == 1
+    assert prefill(d, out=None) == 1
+    assert prefill(d, b=None) == 1
+    assert prefill(d, k=FAKE + 8) == 6
+    assert prefill(d, s_in=FAKE + 4) == 6
+    assert prefill(d, a=FAKE + 2) == 6
+    need = lt2.lt2_gdn_prefill_workspace_size(d)
+    assert need > 0
+    assert prefill(d, ws=None) == 5
+    assert prefill(d, ws_bytes=need - 1) == 5
+    assert prefill(d, ws=FAKE + 4, ws_bytes=need) == 6
+
+
+def test_workspace_size_of_invalid_descriptor_is_zero():
+    assert lt2.lt2_gdn_prefill_workspace_size(good_desc(chunk=7)) == 0
+    assert lt2.lt2_gdn_prefill_workspace_size(good_desc(L=0)) == 0
+
+
+def decode(desc, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s=FAKE, out=FAKE):
+    P = ctypes.c_void_p
+    return lt2.lib().lt2_gdn_decode_step(ctypes.byref(desc), P(q), P(k), P(v), P(a), P(b), P(s), P(out), None)
+
+
+def test_decode_validation():
+    assert decode(good_desc(L=2)) == 2
+    assert decode(good_desc(L=1, d_k=32, d_v=32)) == 4
+    assert decode(good_desc(L=1), s=None) == 1
+    assert decode(good_desc(L=1), out=FAKE + 2) == 6
+    assert decode(good_desc(L=1, qkv_dtype=3)) == 3
+    # an empty batch is valid and launches nothing
+    assert decode(good_desc(L=1, B=0), q=None, k=None, v=None, a=None, b=None, s=None, out=None) == 0
+
+
+def test_copy_validation():
+    L = lt2.lib()
+    P = ctypes.c_void_p
+    assert L.lt2_hbm_copy(P(FAKE), P(FAKE), 0, None) == 0
+    assert L.lt2_hbm_copy(None, P(FAKE), 16, None) == 1
+    assert L.lt2_hbm_copy(P(FAKE), P(FAKE), 17, None) == 2
+    assert L.lt2_hbm_copy(P(FAKE + 4), P(FAKE), 32, None) == 6
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(lt2, "_lib", None)
+    monkeypatch.setattr(lt2, "LIB_PATH", "/nonexistent/liblt2.so")
+    with pytest.raises(RuntimeError):
+        lt2.lib()

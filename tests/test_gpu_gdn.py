@@ -1,0 +1,227 @@
+"""GPU parity of the gated-delta prefill and decode step against the fp64 oracle.
+
+Every case calls liblt2.so through its C ABI (the ctypes binding) and compares
+with oracle/ on the same seeded inputs: max|delta|/max|ref| <= 1e-5 for fp32
+inputs and <= 5e-3 for bf16 inputs with fp32 state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_looped_amd import lt2, synth
+from gpu_util import TOL_BF16, TOL_F32, announce, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(x, shape, chunk, out_dtype=None, S0=None):
+    qdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    q, k, v = dev(x["q"], qdt), dev(x["k"], qdt), dev(x["v"], qdt)
+    a, b = dev(x["alpha"]), dev(x["beta"])
+    s0 = None if S0 is None else dev(S0)
+    o, S = lt2.lt2_gdn_prefill(q, k, v, a, b, state_in=s0, chunk=chunk, out_dtype=out_dtype or qdt)
+    torch.cuda.synchronize()
+    return host(o), host(S)
+
+
+def oracle_prefill(x, S0=None):
+    return oracle.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S0)
+
+
+@pytest.mark.parametrize("chunk", [64, 32, 16])
+def test_tiny_gdn_fp32_chunks(chunk):
+    """B=1 H=1 L=256 d=64 fp32, scalar gate, S0=0: every chunk size matches the oracle."""
+    shape = synth.CONFIGS[1]["shape"]
+    announce(f"tiny fp32 chunk={chunk}")
+    x = synth.gdn_inputs(shape, seed=0)
+    o, S = run_prefill(x, shape, chunk)
+    o_ref, S_ref = oracle_prefill(x)
+    assert rel_err(o, o_ref) <= TOL_F32
+    assert rel_err(S, S_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("L", [1, 15, 37, 64, 65, 200])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_ragged_lengths_with_initial_state_fp32(L, chunk):
+    shape = synth.GDNShape(2, L, 3, 64, 64, "head", 0.0, "f32")
+    announce(f"ragged fp32 L={L} chunk={chunk}")
+    x = synth.gdn_inputs(shape, seed=1)
+    S0 = np.random.default_rng(1).standard_normal((2, 3, 64, 64)).astype(np.float32)
+    o, S = run_prefill(x, shape, chunk, S0=S0)
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(o, o_ref) <= TOL_F32
+    assert rel_err(S, S_ref) <= TOL_F32
+
+
+def test_fp32_d128_prefill():
+    """d=128 fp32 (the state-seeding prefill of the decode workload)."""
+    shape = synth.GDNShape(2, 300, 2, 128, 128, "head", 0.0, "f32")
+    announce("fp32 d128")
+    x = synth.gdn_inputs(shape, seed=2)
+    o, S = run_prefill(x, shape, 64)
+    o_ref, S_ref = oracle_prefill(x)
+    assert rel_err(o, o_ref) <= TOL_F32
+    assert rel_err(S, S_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_bf16_prefill_small(out_dtype):
+    """bf16 q/k/v, fp32 state, strong decay (shift 2), ragged L spanning several chunks."""
+    shape = synth.GDNShape(2, 333, 3, 128, 128, "head", 2.0, "bf16")
+    announce(f"bf16 small out={out_dtype}")
+    x = synth.gdn_inputs(shape, seed=3)
+    S0 = np.random.default_rng(3).standard_normal((2, 3, 128, 128)).astype(np.float32) * 0.1
+    o, S = run_prefill(x, shape, 64, out_dtype=out_dtype, S0=S0)
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(o, o_ref) <= TOL_BF16
+    assert rel_err(S, S_ref) <= TOL_BF16
+
+
+def test_bf16_slow_decay_long():
+    """bf16 with slow decay (shift 0), where the state carries over many chunks."""
+    shape = synth.GDNShape(1, 1024, 2, 128, 128, "head", 0.0, "bf16")
+    announce("bf16 slow decay")
+    x = synth.gdn_inputs(shape, seed=4)
+    o, S = run_prefill(x, shape, 64)
+    o_ref, S_ref = oracle_prefill(x)
+    assert rel_err(o, o_ref) <= TOL_BF16
+    assert rel_err(S, S_ref) <= TOL_BF16
+
+
+def test_state_passing_and_chunk_invariance_bf16():
+    shape = synth.GDNShape(1, 512, 2, 128, 128, "head", 0.0, "bf16")
+    announce("state passing bf16")
+    x = synth.gdn_inputs(shape, seed=5)
+    o_full, S_full = run_prefill(x, shape, 64, out_dtype=torch.float32)
+    L1 = 200
+    xa = {kk: vv[:, :L1] for kk, vv in x.items()}
+    xb = {kk: vv[:, L1:] for kk, vv in x.items()}
+    oa, Sa = run_prefill(xa, synth.GDNShape(1, L1, 2, 128, 128, "head", 0.0, "bf16"), 64, out_dtype=torch.float32)
+    ob, Sb = run_prefill(xb, synth.GDNShape(1, 512 - L1, 2, 128, 128, "head", 0.0, "bf16"), 32,
+                         out_dtype=torch.float32, S0=Sa.astype(np.float32))
+    assert rel_err(np.concatenate([oa, ob], axis=1), o_full) <= TOL_BF16
+    assert rel_err(Sb, S_full) <= TOL_BF16
+    o16, _ = run_prefill(x, shape, 16, out_dtype=torch.float32)
+    assert rel_err(o16, o_full) <= TOL_BF16
+
+
+def test_gate_special_cases_fp32():
+    """alpha=1,beta=0 keeps S0; alpha=0 keeps only the current write (closed forms via the oracle)."""
+    shape = synth.GDNShape(1, 100, 2, 64, 64, "head", 0.0, "f32")
+    x = synth.gdn_inputs(shape, seed=6)
+    S0 = np.random.default_rng(6).standard_normal((1, 2, 64, 64)).astype(np.float32)
+    for name, a, b in (("a1b0", 1.0, 0.0), ("a0", 0.0, None), ("a1b1", 1.0, 1.0)):
+        announce(f"special {name}")
+        y = dict(x)
+        y["alpha"] = np.full_like(x["alpha"], a)
+        if b is not None:
+            y["beta"] = np.full_like(x["beta"], b)
+        o, S = run_prefill(y, shape, 64, S0=S0)
+        o_ref, S_ref = oracle_prefill(y, S0)
+        assert rel_err(o, o_ref) <= TOL_F32, name
+        assert rel_err(S, S_ref) <= TOL_F32, name
+
+
+def test_empty_and_determinism():
+    announce("empty + determinism")
+    shape = synth.GDNShape(1, 0, 2, 64, 64, "head", 0.0, "f32")
+    x = synth.gdn_inputs(shape, seed=7)
+    S0 = np.random.default_rng(7).standard_normal((1, 2, 64, 64)).astype(np.float32)
+    o, S = run_prefill(x, shape, 64, S0=S0)
+    assert o.shape == (1, 0, 2, 64)
+    np.testing.assert_array_equal(S, S0)
+    shape = synth.GDNShape(2, 250, 2, 128, 128, "head", 2.0, "bf16")
+    x = synth.gdn_inputs(shape, seed=8)
+    o1, S1 = run_prefill(x, shape, 64)
+    o2, S2 = run_prefill(x, shape, 64)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+def test_prefill_full_size_bf16_sampled():
+    """B=4 H=16 L=4096 d=128 bf16, chunk 64 (the benchmarked prefill launch):
+    sampled (b, h) units against the oracle."""
+    shape = synth.CONFIGS[2]["shape"]
+    announce("prefill full size bf16")
+    x = synth.gdn_inputs(shape, seed=0)
+    o, S = run_prefill(x, shape, 64)
+    for b, h in [(0, 0), (1, 7), (3, 15)]:
+        u = synth.gdn_unit(shape, 0, b, h)
+        o_ref, S_ref = oracle.prefill(u["q"][None, :, None], u["k"][None, :, None], u["v"][None, :, None],
+                                      u["alpha"][None, :, None], u["beta"][None, :, None])
+        assert rel_err(o[b, :, h], o_ref[0, :, 0]) <= TOL_BF16, (b, h)
+        assert rel_err(S[b, h], S_ref[0, 0]) <= TOL_BF16, (b, h)
+
+
+# ---- decode ---------------------------------------------------------------------
+
+def run_decode(q, k, v, a, b, S, dtype=torch.float32):
+    st = dev(S)
+    o = lt2.lt2_gdn_decode_step(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(a), dev(b), st,
+                                out=torch.empty(v.shape, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    return host(o), host(st)
+
+
+@pytest.mark.parametrize("channel", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_step_fp32(channel, d):
+    announce(f"decode fp32 d={d} channel={channel}")
+    rng = np.random.default_rng(20 + d + channel)
+    B, H = 3, 5
+    q = rng.standard_normal((B, H, d)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((B, H, d)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, d))
+    a = rng.uniform(0.0, 1.0, (B, H, d) if channel else (B, H))
+    b = rng.uniform(0.0, 1.0, (B, H))
+    S = rng.standard_normal((B, H, d, d))
+    args = [x.astype(np.float32) for x in (q, k, v, a, b, S)]
+    o, S1 = run_decode(*args)
+    o_ref, S_ref = oracle.decode_step(*args)
+    assert rel_err(o, o_ref) <= TOL_F32
+    assert rel_err(S1, S_ref) <= TOL_F32
+
+
+def test_decode_chain_equals_prefill_bf16_inputs():
+    """L decode steps reproduce a prefill over the same L tokens."""
+    announce("decode chain vs prefill")
+    shape = synth.GDNShape(2, 40, 3, 128, 128, "head", 0.0, "bf16")
+    x = synth.gdn_inputs(shape, seed=9)
+    o_ref, S_ref = oracle_prefill(x)
+    st = torch.zeros((2, 3, 128, 128), dtype=torch.float32, device="cuda")
+    outs = []
+    for t in range(40):
+        o = lt2.lt2_gdn_decode_step(dev(x["q"][:, t], torch.bfloat16), dev(x["k"][:, t], torch.bfloat16),
+                                    dev(x["v"][:, t], torch.bfloat16), dev(x["alpha"][:, t]),
+                                    dev(x["beta"][:, t]), st,
+                                    out=torch.empty((2, 3, 128), dtype=torch.float32, device="cuda"))
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    assert rel_err(np.stack(outs, axis=1), o_ref) <= TOL_F32
+    assert rel_err(host(st), S_ref) <= TOL_F32
+
+
+def test_decode_full_size_sampled():
+    """256 sequences x 16 heads x d=128 fp32, 4 loops x 6 tokens of fresh inputs
+    (the benchmarked decode launch), sampled units against the oracle."""
+    announce("decode full size")
+    B, H, d, T, steps = 256, 16, 128, 4, 6
+    x = synth.decode_inputs(seed=3, B=B, H=H, T=T, steps=steps, d=d)
+    S0 = np.random.default_rng(3).standard_normal((T, B, H, d, d)).astype(np.float32) * 0.05
+    st = dev(S0)
+    outs = np.empty((steps, T, B, H, d))
+    for s in range(steps):
+        for t in range(T):
+            o = lt2.lt2_gdn_decode_step(dev(x["q"][s, t]), dev(x["k"][s, t]), dev(x["v"][s, t]),
+                                        dev(x["alpha"][s, t]), dev(x["beta"][s, t]), st[t])
+            outs[s, t] = host(o)
+    torch.cuda.synchronize()
+    S_fin = host(st)
+    for (b, h, t) in [(0, 0, 0), (17, 5, 1), (255, 15, 3)]:
+        u = synth.decode_unit(3, b, h, t, steps, d)
+        o_ref, S_ref = oracle.prefill(u["q"][None, :, None], u["k"][None, :, None], u["v"][None, :, None],
+                                      u["alpha"][None, :, None], u["beta"][None, :, None],
+                                      S0[t, b, h][None, None])
+        assert rel_err(outs[:, t, b, h], o_ref[0, :, 0]) <= TOL_F32, (b, h, t)
+        assert rel_err(S_fin[t, b, h], S_ref[0, 0]) <= TOL_F32, (b, h, t)
