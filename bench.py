@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the LT2 gated-delta hot path on one MI355X; prints ONE JSON line.
+
+Headline workload (the step that is timed K times): one chunked gated-delta
+prefill, B=4 H=16 L=4096 d_k=d_v=128, bf16 q/k/v, fp32 state, chunk 64, T=1
+(scalar gate exp(-softplus(N(0,1)+2))).  value = tokens/s per loop = B*L*T / t.
+Inputs are seeded, synthetic and resident in HBM before timing; two input sets
+alternate so that no step re-reads the previous step's data from cache.
+
+Also measured in the same run (reported under "extra"):
+  * decode: 256 sequences x 16 heads x d=128, fp32 state from a seeded 2048-token
+    prefill, T=4 loops per token, 1024 tokens with fresh inputs; one
+    lt2_gdn_decode_step launch per (token, loop); state GB/s against HBM peak and
+    against the copy-probe bandwidth;
+  * copy probe: streaming copy of 2 x 4 GiB, the measured HBM bandwidth;
+  * the per-kernel split of the prefill (prepare / scan) from HIP events.
+cpu_baseline: the fp64 oracle on a bounded sample (one sequence, all heads).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "gated-delta tokens/s per loop (prefill) + decode state GB/s vs HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops_bytes(B, L, H, d, C, qkv_bytes=2, out_bytes=2):
+    """Algorithmic flops and bytes per kernel of the chunked prefill (per launch).
+
+    prepare, per head-token: gated K K^T (strictly lower) and Q K^T (lower incl.)
+      C*d MACs, the unit-lower inverse C^2/6 MACs; reads q, k, alpha, beta;
+      writes Tm and P (2*C*C fp32 per chunk) and g (C fp32 per chunk).
+    scan, per head-token: K S, Q S and K^T U (3*d*d MACs), Tm R and P U (C*d MACs);
+      reads q, k, v, Tm, P, g; writes o; reads/writes the state once per unit.
+    """
+    ht = B * L * H
+    prep_flops = 2.0 * ht * (C * d + C * C / 6.0)
+    scan_flops = 2.0 * ht * (3.0 * d * d + C * d)
+    ws_per_ht = (2 * C * C + C) * 4.0 / C
+    prep_bytes = ht * (2 * d * qkv_bytes + 8 + ws_per_ht)
+    scan_bytes = ht * (3 * d * qkv_bytes + ws_per_ht + d * out_bytes) + B * H * d * d * 4.0
+    path_bytes = ht * (3 * d * qkv_bytes + 8 + d * out_bytes) + B * H * d * d * 4.0
+    return dict(prepare=(prep_flops, prep_bytes), scan=(scan_flops, scan_bytes), path_bytes=path_bytes,
+                path_flops=prep_flops + scan_flops)
+
+
+def bench_prefill(args, torch, lt2, synth):
+    cfg = synth.CONFIGS[2]
+    shape, C = cfg["shape"], cfg["chunk"]
+    B, L, H, d = shape.B, shape.L, shape.H, shape.dk
+    log(f"prefill inputs B={B} L={L} H={H} d={d} (2 seeded sets)")
+    sets = []
+    for seed in (0, 1):
+        x = synth.gdn_inputs(shape, seed=seed)
+        sets.append(dict(q=torch.from_numpy(x["q"]).to("cuda").to(torch.bfloat16),
+                         k=torch.from_numpy(x["k"]).to("cuda").to(torch.bfloat16),
+                         v=torch.from_numpy(x["v"]).to("cuda").to(torch.bfloat16),
+                         alpha=torch.from_numpy(x["alpha"]).to("cuda"),
+                         beta=torch.from_numpy(x["beta"]).to("cuda")))
+        del x
+    out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    desc = lt2.gdn_desc(B, L, H, d, d, C, lt2.LT2_BF16, lt2.LT2_BF16, lt2.LT2_GATE_HEAD)
+    ws_bytes = lt2.lt2_gdn_prefill_workspace_size(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    L_ = lt2.lib()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    calls = []
+    for s in sets:
+        calls.append(((ctypes.byref(desc), P(s["q"]), P(s["k"]), P(s["alpha"]), P(s["beta"]), P(ws), ws_bytes, sp),
+                      (ctypes.byref(desc), P(s["q"]), P(s["k"]), P(s["v"]), None, P(out), P(S), P(ws), ws_bytes, sp)))
+
+    def step(i, ev=None):
+        prep, scan = calls[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        rc = L_.lt2_gdn_prefill_prepare(*prep)
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= L_.lt2_gdn_prefill_scan(*scan)
+        if ev is not None:
+            ev[2].record(stream)
+        if rc:
+            raise RuntimeError(f"prefill failed rc={rc}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    event_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+    fb = prefill_flops_bytes(B, L, H, d, C)
+    log(f"prefill {ms_step:.3f} ms/step (events {event_ms:.3f}: prepare {prep_ms:.3f}, scan {scan_ms:.3f})")
+    kernels = {}
+    for name, ms in (("prepare", prep_ms), ("scan", scan_ms)):
+        fl, by = fb[name]
+        kernels[name] = dict(ms=ms, flops=fl, bytes=by, tflops=fl / ms / 1e9, gbs=by / ms / 1e6)
+    return dict(B=B, L=L, H=H, d=d, C=C, ms_step=ms_step, event_ms=event_ms, kernels=kernels,
+                path_bytes=fb["path_bytes"], path_flops=fb["path_flops"], ws_bytes=ws_bytes)
+
+
+def bench_copy(torch, lt2, nbytes=4 << 30, reps=20):
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        lt2.lt2_hbm_copy(b, a)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lt2.lt2_hbm_copy(b, a)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    del a, b
+    torch.cuda.empty_cache()
+    return dict(bytes_moved=2 * nbytes, ms=ms, gbs=2 * nbytes / ms / 1e6)
+
+
+def bench_decode(args, torch, lt2, synth):
+    cfg = synth.CONFIGS[5]
+    B, H, d, T, steps = cfg["B"], cfg["H"], cfg["d"], cfg["T"], cfg["steps"]
+    if args.decode_steps:
+        steps = args.decode_steps
+    pshape = cfg["prefill"]
+    log(f"decode setup: seeded {pshape.L}-token fp32 prefill for {B}x{H} units")
+    S0 = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    # the seeding prefill runs in batch slabs to bound host memory
+    slab = 32
+    for b0 in range(0, B, slab):
+        sub = synth.GDNShape(slab, pshape.L, H, d, d, "head", pshape.shift, "f32")
+        x = _slab_inputs(synth, pshape, b0, slab)
+        t = {kk: torch.from_numpy(vv).to("cuda") for kk, vv in x.items()}
+        lt2.lt2_gdn_prefill(t["q"], t["k"], t["v"], t["alpha"], t["beta"], state_out=S0[b0:b0 + slab],
+                            out=torch.empty((slab, sub.L, H, d), dtype=torch.float32, device="cuda"))
+        del t, x
+    torch.cuda.synchronize()
+    state = torch.empty((T, B, H, d, d), dtype=torch.float32, device="cuda")
+    for t in range(T):
+        state[t].copy_(S0)
+    del S0
+    log(f"decode inputs: {steps} tokens x {T} loops fresh per step")
+    x = synth.decode_inputs(seed=0, B=B, H=H, T=T, steps=steps, d=d)
+    dx = {kk: torch.from_numpy(vv).to("cuda") for kk, vv in x.items()}
+    del x
+    out = torch.empty((steps, T, B, H, d), dtype=torch.float32, device="cuda")
+    desc = lt2.gdn_desc(B, 1, H, d, d, 64, lt2.LT2_F32, lt2.LT2_F32, lt2.LT2_GATE_HEAD)
+    L_ = lt2.lib()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    calls = [(ctypes.byref(desc), P(dx["q"][s, t]), P(dx["k"][s, t]), P(dx["v"][s, t]), P(dx["alpha"][s, t]),
+              P(dx["beta"][s, t]), P(state[t]), P(out[s, t]), sp) for s in range(steps) for t in range(T)]
+    fn = L_.lt2_gdn_decode_step
+    scratch = state[0].clone()  # warm-up launches update a scratch copy, not the measured states
+    for s in range(min(steps, 4)):
+        if fn(ctypes.byref(desc), P(dx["q"][s, 0]), P(dx["k"][s, 0]), P(dx["v"][s, 0]), P(dx["alpha"][s, 0]),
+              P(dx["beta"][s, 0]), P(scratch), P(out[s, 0]), sp):
+            raise RuntimeError("decode failed")
+    torch.cuda.synchronize()
+    del scratch
+    # pass 1: wall clock over all (token, loop) launches
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for c in calls:
+        if fn(*c):
+            raise RuntimeError("decode failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    span_ms = e0.elapsed_time(e1)
+    bytes_step = B * H * (2 * d * d * 4 + 4 * d * 4 + 8)
+    n = len(calls)
+    # pass 2: kernel time per launch (events around a sample of launches)
+    sample = calls[: min(n, 256)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sample]
+    for c, (a, b) in zip(sample, evs):
+        a.record(stream)
+        fn(*c)
+        b.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    log(f"decode {n} launches: span {span_ms:.1f} ms, {span_ms / n * 1e3:.1f} us/launch, kernel {kern_ms * 1e3:.1f} us")
+    return dict(B=B, H=H, d=d, T=T, tokens=steps, launches=n, bytes_per_launch=bytes_step,
+                span_ms=span_ms, wall_s=wall_s, kernel_us=kern_ms * 1e3,
+                gbs_span=bytes_step * n / span_ms / 1e6, gbs_kernel=bytes_step / kern_ms / 1e6,
+                tokens_per_s_per_loop=B * steps * T / (span_ms / 1e3) / T)
+
+
+def _slab_inputs(synth, shape, b0, nb):
+    """Inputs of batch rows b0..b0+nb of the decode-seeding prefill (per-unit streams)."""
+    L, H, d = shape.L, shape.H, shape.dk
+    out = dict(q=np.empty((nb, L, H, d), np.float32), k=np.empty((nb, L, H, d), np.float32),
+               v=np.empty((nb, L, H, d), np.float32), alpha=np.empty((nb, L, H), np.float32),
+               beta=np.empty((nb, L, H), np.float32))
+    from concurrent.futures import ThreadPoolExecutor
+
+    def fill(bh):
+        b, h = bh
+        u = synth.gdn_unit(shape, 0, b0 + b, h)
+        for kk, vv in u.items():
+            out[kk][b, :, h] = vv
+
+    with ThreadPoolExecutor(16) as ex:
+        list(ex.map(fill, [(b, h) for b in range(nb) for h in range(H)]))
+    return out
+
+
+def cpu_baseline(synth):
+    """The fp64 oracle on the whole headline workload (4 sequences x 4096 tokens x
+    16 heads, seed 0); tokens/s per loop = B*L / t."""
+    import oracle
+    shape = synth.CONFIGS[2]["shape"]
+    x = synth.gdn_inputs(shape, seed=0)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], threads=threads)
+    dt = time.perf_counter() - t0
+    return dict(value=shape.B * shape.L / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"the whole headline workload ({shape.B} x {shape.L} tokens x {shape.H} heads, "
+                       f"d={shape.dk}), fp64 token-by-token recurrence, {dt:.2f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_looped_amd import lt2, synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    lt2.lib()
+    pre = bench_prefill(args, torch, lt2, synth)
+    copy = bench_copy(torch, lt2)
+    log(f"copy probe {copy['gbs']:.0f} GB/s")
+    dec = None if args.no_decode else bench_decode(args, torch, lt2, synth)
+    cpu = None if args.no_cpu else cpu_baseline(synth)
+
+    value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
+    dom_name = max(pre["kernels"], key=lambda n: pre["kernels"][n]["ms"])
+    dom = pre["kernels"][dom_name]
+    roof = dict(kernel=f"prefill {dom_name}", bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=dom["gbs"] / HBM_PEAK_GBS, traffic=None,
+                mfma_tflops=dom["tflops"], mfma_frac=dom["tflops"] / BF16_PEAK_TFLOPS)
+    extra = dict(
+        prefill_kernels=pre["kernels"],
+        prefill_path=dict(ms=pre["event_ms"], gbs=pre["path_bytes"] / pre["event_ms"] / 1e6,
+                          tflops=pre["path_flops"] / pre["event_ms"] / 1e9,
+                          hbm_frac=pre["path_bytes"] / pre["event_ms"] / 1e6 / HBM_PEAK_GBS),
+        copy_probe=copy,
+    )
+    if dec:
+        extra["decode"] = dict(dec, hbm_frac_kernel=dec["gbs_kernel"] / HBM_PEAK_GBS,
+                               copy_frac_kernel=dec["gbs_kernel"] / copy["gbs"],
+                               hbm_frac_span=dec["gbs_span"] / HBM_PEAK_GBS)
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gdn_prefill B=4 H=16 L=4096 d_k=d_v=128 bf16 qkv fp32 state chunk=64 T=1",
+                   "global_batch": pre["B"], "seq_len": pre["L"], "heads": pre["H"], "d_head": pre["d"],
+                   "chunk": pre["C"], "loops": 1, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

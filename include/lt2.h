@@ -112,6 +112,27 @@ lt2_status lt2_gdn_prefill(const lt2_gdn_desc *desc, const void *q, const void *
                            void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The two phases of lt2_gdn_prefill, for callers that schedule them apart
+ * (e.g. overlap the prepare phase of the next batch with the scan of this one,
+ * or time them separately).  lt2_gdn_prefill(...) is exactly
+ * lt2_gdn_prefill_prepare(...) followed by lt2_gdn_prefill_scan(...) on one
+ * stream with the same descriptor and workspace.
+ *   prepare: reads q, k, alpha, beta; writes the state-independent factors
+ *            of every chunk into ws (chunk-parallel).
+ *   scan:    reads q, k, v and the factors in ws; carries the fp32 state
+ *            across the chunks of every unit in order; writes out, state_out.
+ * Arguments, layouts and errors as for lt2_gdn_prefill; the workspace contents
+ * between the two calls are private to the library.
+ */
+lt2_status lt2_gdn_prefill_prepare(const lt2_gdn_desc *desc, const void *q, const void *k,
+                                   const float *alpha, const float *beta, void *ws,
+                                   size_t ws_bytes, void *stream);
+lt2_status lt2_gdn_prefill_scan(const lt2_gdn_desc *desc, const void *q, const void *k,
+                                const void *v, const float *state_in, void *out,
+                                float *state_out, const void *ws, size_t ws_bytes,
+                                void *stream);
+
+/*
  * One decode token (desc->L must be 1) for every (b, h) unit, state updated in
  * place.  q, k [B,H,d_k], v, out [B,H,d_v] (element types from desc),
  * alpha [B,H] or [B,H,d_k], beta [B,H] fp32, state [B,H,d_k,d_v] fp32.

@@ -72,13 +72,20 @@ size_t lt2_gdn_prefill_workspace_size(const lt2_gdn_desc *desc) {
     return prefill_ws(desc);
 }
 
-lt2_status lt2_gdn_prefill(const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,
-                           const float *alpha, const float *beta, const float *state_in, void *out,
-                           float *state_out, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and dispatch of lt2_gdn_prefill and its two phases.
+lt2_status prefill_call(int phase, const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,
+                        const float *alpha, const float *beta, const float *state_in, void *out,
+                        float *state_out, void *ws, size_t ws_bytes, void *stream) {
     lt2_status st = check_desc(desc, false);
     if (st != LT2_OK) return st;
     const bool work = desc->B > 0 && desc->L > 0;
-    if (work && (!q || !k || !v || !alpha || !beta || !out)) return LT2_ERR_NULL;
+    if (work && (!q || !k)) return LT2_ERR_NULL;
+    if (work && (phase & PHASE_PREPARE) && (!alpha || !beta)) return LT2_ERR_NULL;
+    if (work && (phase & PHASE_SCAN) && (!v || !out)) return LT2_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(state_in, 16) || !aligned(state_out, 16) || !aligned(alpha, 4) || !aligned(beta, 4))
         return LT2_ERR_ALIGN;
@@ -88,13 +95,36 @@ lt2_status lt2_gdn_prefill(const lt2_gdn_desc *desc, const void *q, const void *
     hipStream_t s = (hipStream_t)stream;
     if (desc->B == 0) return LT2_OK;
     if (desc->L == 0) {
-        if (!state_out) return LT2_OK;
+        if (!(phase & PHASE_SCAN) || !state_out) return LT2_OK;
         const size_t n = (size_t)desc->B * desc->H * desc->d_k * desc->d_v;
         return hip_status(launch_state_init(state_out, state_in, n, s));
     }
     if (desc->gate == LT2_GATE_CHANNEL) return LT2_ERR_UNSUPPORTED;
     GdnArgs a = make_args(desc, q, k, v, alpha, beta, state_in, out, state_out, ws);
-    return hip_status(a.channel ? launch_prefill_channel(a, s) : launch_prefill_head(a, s));
+    return hip_status(a.channel ? launch_prefill_channel(a, phase, s) : launch_prefill_head(a, phase, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+lt2_status lt2_gdn_prefill(const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta, const float *state_in, void *out,
+                           float *state_out, void *ws, size_t ws_bytes, void *stream) {
+    return prefill_call(PHASE_ALL, desc, q, k, v, alpha, beta, state_in, out, state_out, ws, ws_bytes, stream);
+}
+
+lt2_status lt2_gdn_prefill_prepare(const lt2_gdn_desc *desc, const void *q, const void *k, const float *alpha,
+                                   const float *beta, void *ws, size_t ws_bytes, void *stream) {
+    return prefill_call(PHASE_PREPARE, desc, q, k, nullptr, alpha, beta, nullptr, nullptr, nullptr, ws, ws_bytes,
+                        stream);
+}
+
+lt2_status lt2_gdn_prefill_scan(const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,
+                                const float *state_in, void *out, float *state_out, const void *ws,
+                                size_t ws_bytes, void *stream) {
+    return prefill_call(PHASE_SCAN, desc, q, k, v, nullptr, nullptr, state_in, out, state_out, (void *)ws, ws_bytes,
+                        stream);
 }
 
 lt2_status lt2_gdn_decode_step(const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,

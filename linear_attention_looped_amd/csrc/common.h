@@ -71,6 +71,101 @@ __device__ __forceinline__ void mma(f32x4 &acc, const Frag &a, const Frag &b) {
     }
 }
 
+// Pre-converted MFMA operands, so one fragment can feed several products
+// without repeating the conversion.  fp32 path: the eight floats; bf16 path:
+// hi (and lo for operands that are not bf16-exact).
+template <int PREC, bool EXACT>
+struct Op {
+    bf16x8 hi, lo;
+};
+template <bool EXACT>
+struct Op<PREC_F32, EXACT> {
+    Frag f;
+};
+
+template <int PREC, bool EXACT>
+__device__ __forceinline__ Op<PREC, EXACT> make_op(const Frag &a) {
+    Op<PREC, EXACT> o;
+    if constexpr (PREC == PREC_F32) {
+        o.f = a;
+    } else if constexpr (EXACT) {
+        to_bf16(a, o.hi);
+    } else {
+        split_bf16(a, o.hi, o.lo);
+    }
+    return o;
+}
+
+template <int PREC, bool AE, bool BE>
+__device__ __forceinline__ void mma_op(f32x4 &acc, const Op<PREC, AE> &a, const Op<PREC, BE> &b) {
+    if constexpr (PREC == PREC_F32) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f.x[s], b.f.x[s], acc, 0, 0, 0);
+    } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+        if constexpr (!AE) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+        if constexpr (!BE) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    }
+}
+
+// Raw eight-element input rows (kept in their storage type while in flight).
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+    uint4 u;
+};
+template <>
+struct Raw8<float> {
+    float4 a, b;
+};
+
+template <typename T>
+__device__ __forceinline__ void load_raw8(Raw8<T> &r, const T *p);
+template <>
+__device__ __forceinline__ void load_raw8<uint16_t>(Raw8<uint16_t> &r, const uint16_t *p) {
+    r.u = *reinterpret_cast<const uint4 *>(p);
+}
+template <>
+__device__ __forceinline__ void load_raw8<float>(Raw8<float> &r, const float *p) {
+    r.a = *reinterpret_cast<const float4 *>(p);
+    r.b = *reinterpret_cast<const float4 *>(p + 4);
+}
+
+template <typename T>
+__device__ __forceinline__ void zero_raw8(Raw8<T> &r);
+template <>
+__device__ __forceinline__ void zero_raw8<uint16_t>(Raw8<uint16_t> &r) {
+    r.u = make_uint4(0u, 0u, 0u, 0u);
+}
+template <>
+__device__ __forceinline__ void zero_raw8<float>(Raw8<float> &r) {
+    r.a = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.b = r.a;
+}
+
+__device__ __forceinline__ void raw_to_frag(Frag &f, const Raw8<uint16_t> &r) {
+    const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.x[2 * i] = __uint_as_float(w[i] << 16);
+        f.x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void raw_to_frag(Frag &f, const Raw8<float> &r) {
+    f.x[0] = r.a.x; f.x[1] = r.a.y; f.x[2] = r.a.z; f.x[3] = r.a.w;
+    f.x[4] = r.b.x; f.x[5] = r.b.y; f.x[6] = r.b.z; f.x[7] = r.b.w;
+}
+
+// The hardware hands out the workgroups of a launch to the 8 XCDs (each with
+// its own L2) round-robin by workgroup id.  This maps a 1-D id to a logical
+// index so that the ids one XCD receives get consecutive logical indices, i.e.
+// neighbouring logical work (which shares inputs) lands on the same L2.
+__device__ __forceinline__ int xcd_logical(int bid, int n) {
+    if (n % 8 != 0) return bid;
+    return (bid % 8) * (n / 8) + bid / 8;
+}
+
 // Fragment loads: eight consecutive floats from a row of an fp32 buffer.
 __device__ __forceinline__ void load_frag_f32(Frag &f, const float *p) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
@@ -116,6 +211,9 @@ template <>
 __device__ __forceinline__ float load1<float>(const float *p) { return *p; }
 template <>
 __device__ __forceinline__ float load1<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 
 template <typename T>
 __device__ __forceinline__ void store1(T *p, float x);

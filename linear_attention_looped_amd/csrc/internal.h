@@ -20,11 +20,15 @@ struct GdnArgs {
 
 // Each launcher returns hipSuccess or the launch error; shapes are already
 // validated by the caller.
+// Prefill phases: the chunk-parallel prepare phase writes the per-chunk
+// factors into the workspace, the scan phase carries the state across chunks.
+enum { PHASE_PREPARE = 1, PHASE_SCAN = 2, PHASE_ALL = 3 };
+
 hipError_t launch_decode(const GdnArgs &a, hipStream_t s);
 size_t prefill_head_ws_bytes(int B, int L, int H, int C);
-hipError_t launch_prefill_head(const GdnArgs &a, hipStream_t s);
+hipError_t launch_prefill_head(const GdnArgs &a, int phase, hipStream_t s);
 size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C);
-hipError_t launch_prefill_channel(const GdnArgs &a, hipStream_t s);
+hipError_t launch_prefill_channel(const GdnArgs &a, int phase, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t s);
 

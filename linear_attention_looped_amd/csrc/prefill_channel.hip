@@ -6,6 +6,6 @@ namespace lt2 {
 
 size_t prefill_channel_ws_bytes(int, int, int, int, int) { return 0; }
 
-hipError_t launch_prefill_channel(const GdnArgs &, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_prefill_channel(const GdnArgs &, int, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace lt2

@@ -9,9 +9,11 @@
 //   U = Tm (V - diag(e^g) K S),                Tm = (I + A)^{-1} diag(b)
 //   O = diag(e^g) Q S + P U,                   P_ti = Gamma_ti q_t.k_i      (i <= t)
 //   S <- e^{g_C} S + K^T diag(e^{g_C - g}) U
-// Tm and P do not depend on the state: kernel 1 forms them for every chunk in
-// parallel; kernel 2 carries the fp32 state across the chunks of one unit in
-// order, for one block of BV state columns (columns evolve independently).
+// Tm and P do not depend on the state: the prepare kernel forms them for every
+// chunk in parallel; the scan kernel carries the fp32 state across the chunks
+// of one unit in order, for one block of BV state columns (columns evolve
+// independently), with the next chunk's inputs in flight while the current
+// chunk computes.
 //
 // Gate exponents are masked before exp, so every exponent is <= 0.
 #include "common.h"
@@ -20,7 +22,7 @@
 namespace lt2 {
 
 // ---------------------------------------------------------------------------
-// Kernel 1: per chunk, Tm = (I + A)^{-1} diag(beta), P, and g.  Workspace per
+// Prepare: per chunk, Tm = (I + A)^{-1} diag(beta), P and g.  Workspace per
 // (b, h, chunk): Tm [C][C], P [C][C], g [C], fp32, zero above the diagonal.
 // ---------------------------------------------------------------------------
 template <int DK, int C, int PREC, typename TI>
@@ -28,47 +30,42 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
                                                         const float *__restrict__ alpha,
                                                         const float *__restrict__ beta, float *__restrict__ ws,
                                                         int L, int H, int NC) {
-    constexpr int KP = DK + 4;
+    constexpr int KP = DK + 16 / (int)sizeof(TI);   // row pitch (elements), rows stay 16-byte aligned
     constexpr int CP = C + 4;
     constexpr int NT = C / 16;
-    __shared__ __attribute__((aligned(16))) float Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) float Qs[C * KP];
+    constexpr int K_BYTES = C * KP * (int)sizeof(TI);
+    constexpr int T_BYTES = C * CP * 4;
+    // K is dead once the gated Gram tiles are formed; the inverse reuses its space.
+    __shared__ __attribute__((aligned(16))) unsigned char kt_raw[K_BYTES > T_BYTES ? K_BYTES : T_BYTES];
     __shared__ float Am[C * CP];
-    __shared__ float Ti[C * CP];
     __shared__ float Xs[4][16 * 17];
     __shared__ float gs[C], bs[C];
+    TI *Ks = reinterpret_cast<TI *>(kt_raw);
+    float *Ti = reinterpret_cast<float *>(kt_raw);
 
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int n = blockIdx.x % NC;
+    const int unit = blockIdx.x / NC;
+    const int h = unit % H, b = unit / H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
     const int t0 = n * C;
     const int Lc = min(C, L - t0);
-    float *wsu = ws + (((size_t)b * H + h) * NC + n) * (size_t)(2 * C * C + C);
+    float *wsu = ws + ((size_t)unit * NC + n) * (size_t)(2 * C * C + C);
     float *Tg = wsu, *Pg = wsu + C * C, *gg = wsu + 2 * C * C;
 
     for (int idx = tid; idx < C * (DK / 8); idx += 256) {
         const int t = idx / (DK / 8), c8 = idx % (DK / 8);
-        Frag fk, fq;
-        if (t < Lc) {
-            const size_t off = ((size_t)(b * (size_t)L + t0 + t) * H + h) * DK + 8 * c8;
-            load_row8<TI>(fk, k + off);
-            load_row8<TI>(fq, q + off);
-        } else {
-            zero_frag(fk);
-            zero_frag(fq);
-        }
-        float *pk = Ks + t * KP + 8 * c8, *pq = Qs + t * KP + 8 * c8;
-        *reinterpret_cast<float4 *>(pk) = make_float4(fk.x[0], fk.x[1], fk.x[2], fk.x[3]);
-        *reinterpret_cast<float4 *>(pk + 4) = make_float4(fk.x[4], fk.x[5], fk.x[6], fk.x[7]);
-        *reinterpret_cast<float4 *>(pq) = make_float4(fq.x[0], fq.x[1], fq.x[2], fq.x[3]);
-        *reinterpret_cast<float4 *>(pq + 4) = make_float4(fq.x[4], fq.x[5], fq.x[6], fq.x[7]);
+        Raw8<TI> r;
+        load_raw8<TI>(r, k + ((size_t)(b * (size_t)L + t0 + min(t, Lc - 1)) * H + h) * DK + 8 * c8);
+        if (t >= Lc) zero_raw8<TI>(r);
+        *reinterpret_cast<Raw8<TI> *>(Ks + t * KP + 8 * c8) = r;
     }
     if (wave == 0) {
-        float lg = 0.f, bt = 0.f;
-        if (lane < Lc) {
-            const size_t tok = (size_t)(b * (size_t)L + t0 + lane) * H + h;
-            lg = log_gate(alpha[tok]);
-            bt = beta[tok];
-        }
+        const size_t tok = (size_t)(b * (size_t)L + t0 + min(lane, Lc - 1)) * H + h;
+        const float a_raw = alpha[tok], b_raw = beta[tok];
+        const float lg0 = log_gate(a_raw);
+        float lg = (lane < Lc) ? lg0 : 0.f;
+        const float bt = (lane < Lc) ? b_raw : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(lg, off);
@@ -83,27 +80,34 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     for (int tt = wave; tt < 2 * NT * NT; tt += 4) {
         const int which = tt / (NT * NT);  // 0: KK^T, 1: QK^T
         const int I = (tt % (NT * NT)) / NT, J = tt % NT;
-        const int row = 4 * (lane >> 4), col = lane & 15;
         if (J > I) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if (which == 0) Am[(16 * I + row + r) * CP + 16 * J + col] = 0.f;
-                else Pg[(16 * I + row + r) * C + 16 * J + col] = 0.f;
+                if (which == 0) Am[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = 0.f;
+                else Pg[(16 * I + 4 * lq + r) * C + 16 * J + lr] = 0.f;
             }
             continue;
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const float *Asrc = which == 0 ? Ks : Qs;
+        const int arow = 16 * I + lr;
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
+            Raw8<TI> ra, rb;
+            if (which == 0) {
+                ra = *reinterpret_cast<const Raw8<TI> *>(Ks + arow * KP + 32 * kb + 8 * lq);
+            } else {
+                load_raw8<TI>(ra, q + ((size_t)(b * (size_t)L + t0 + min(arow, Lc - 1)) * H + h) * DK + 32 * kb + 8 * lq);
+                if (arow >= Lc) zero_raw8<TI>(ra);
+            }
+            rb = *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq);
             Frag fa, fb;
-            load_frag_f32(fa, Asrc + (16 * I + (lane & 15)) * KP + 32 * kb + 8 * (lane >> 4));
-            load_frag_f32(fb, Ks + (16 * J + (lane & 15)) * KP + 32 * kb + 8 * (lane >> 4));
+            raw_to_frag(fa, ra);
+            raw_to_frag(fb, rb);
             mma<PREC, true, true>(acc, fa, fb);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * I + row + r, i = 16 * J + col;
+            const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
             if (which == 0) {
                 Am[t * CP + i] = (i < t) ? bs[t] * expf(gs[t] - gs[i]) * acc[r] : 0.f;
             } else {
@@ -134,56 +138,81 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     for (int dist = 1; dist < NT; ++dist) {
         if (wave < NT - dist) {
             const int J = wave, I = wave + dist;
-            const int lr = lane & 15, lk = lane >> 4;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int Kb = J; Kb < I; ++Kb) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const float a = Am[(16 * I + lr) * CP + 16 * Kb + 4 * kk + lk];
-                    const float bb = Ti[(16 * Kb + 4 * kk + lk) * CP + 16 * J + lr];
+                    const float a = Am[(16 * I + lr) * CP + 16 * Kb + 4 * kk + lq];
+                    const float bb = Ti[(16 * Kb + 4 * kk + lq) * CP + 16 * J + lr];
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0);
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Xs[wave][(4 * lk + r) * 17 + lr] = acc[r];
+            for (int r = 0; r < 4; ++r) Xs[wave][(4 * lq + r) * 17 + lr] = acc[r];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const float a = Ti[(16 * I + lr) * CP + 16 * I + 4 * kk + lk];
-                const float bb = Xs[wave][(4 * kk + lk) * 17 + lr];
+                const float a = Ti[(16 * I + lr) * CP + 16 * I + 4 * kk + lq];
+                const float bb = Xs[wave][(4 * kk + lq) * 17 + lr];
                 y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Ti[(16 * I + 4 * lk + r) * CP + 16 * J + lr] = -y[r];
+            for (int r = 0; r < 4; ++r) Ti[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = -y[r];
         }
         __syncthreads();
     }
 
-    // Tm = T diag(beta), zero above the diagonal.
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int t = idx / C, i = idx % C;
-        Tg[idx] = (i <= t) ? Ti[t * CP + i] * bs[i] : 0.f;
+    // Tm = T diag(beta), zero above the diagonal; four consecutive floats per store.
+    for (int idx = tid; idx < C * C / 4; idx += 256) {
+        const int t = idx / (C / 4), i0 = 4 * (idx % (C / 4));
+        float4 w;
+        w.x = (i0 + 0 <= t) ? Ti[t * CP + i0 + 0] * bs[i0 + 0] : 0.f;
+        w.y = (i0 + 1 <= t) ? Ti[t * CP + i0 + 1] * bs[i0 + 1] : 0.f;
+        w.z = (i0 + 2 <= t) ? Ti[t * CP + i0 + 2] * bs[i0 + 2] : 0.f;
+        w.w = (i0 + 3 <= t) ? Ti[t * CP + i0 + 3] * bs[i0 + 3] : 0.f;
+        *reinterpret_cast<float4 *>(Tg + t * C + i0) = w;
     }
     if (tid < C) gg[tid] = gs[tid];
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: state scan over the chunks of one (b, h) unit for BV columns.
+// Scan: state carried across the chunks of one (b, h) unit for BV columns.
+// Workgroup layout: 4 waves; wave w owns output row tile I = w % (C/16) and the
+// column tiles J of the output tiles o = w + 4m (o = I + (C/16) J); the state
+// tiles s = w + 4m (s = (dk tile) * (BV/16) + J) share one column tile.
 // ---------------------------------------------------------------------------
+template <int DK, int C, int BV, int PREC, typename TI>
+struct ScanPrefetch {
+    static constexpr int NTR = C / 16;
+    static constexpr int NT_O = NTR * (BV / 16);
+    static constexpr int MAXO = (NT_O + 3) / 4;
+    static constexpr int NKB_C = (C + 31) / 32;
+    static constexpr int KL = (C * (DK / 8) + 255) / 256;
+    Raw8<TI> k[KL];            // K rows for the LDS copy
+    Raw8<TI> qf[DK / 32];      // Q fragments of the wave's row tile
+    Frag tf[NKB_C], pf[NKB_C]; // Tm and P fragments of the wave's row tile
+    TI v[MAXO][4];             // V entries of the wave's output tiles (raw)
+    float g;                   // g[tid] (tid < C)
+};
+
 template <int DK, int DV, int BV, int C, int PREC, typename TI, typename TO>
 __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                         const TI *__restrict__ v, const float *__restrict__ ws,
                                                         const float *__restrict__ state_in, TO *__restrict__ out,
                                                         float *__restrict__ state_out, int L, int H, int NC) {
+    using PF = ScanPrefetch<DK, C, BV, PREC, TI>;
     constexpr int KP = DK + 4;
     constexpr int CP = C + 4;
     constexpr int NTR = C / 16, NTV = BV / 16, NTK = DK / 16;
     constexpr int NT_O = NTR * NTV, NT_S = NTK * NTV;
     constexpr int MAXO = (NT_O + 3) / 4, MAXS = (NT_S + 3) / 4;
     constexpr int NKB_C = (C + 31) / 32;
+    constexpr int NV = DV / BV;
+    static_assert(4 % NTR == 0, "a wave's output tiles share one row tile");
+    static_assert(4 % NTV == 0 && NT_S % 4 == 0, "a wave's state tiles share one column tile");
 
     __shared__ __attribute__((aligned(16))) float Ks[C * KP];
     __shared__ __attribute__((aligned(16))) float St[BV * KP];
@@ -192,164 +221,260 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
     __shared__ __attribute__((aligned(16))) float U2t[BV * CP];
     __shared__ float gs[C];
 
-    const int vb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    const int vb = logical % NV;
+    const size_t unit = logical / NV;
+    const int h = (int)(unit % H), b = (int)(unit / H);
     const int v0 = vb * BV;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
-    const size_t unit = (size_t)b * H + h;
+    const int I = wave % NTR;                       // this wave's output row tile
+    const bool has_o = wave < NT_O;
+    const int nkb = (16 * I + 16 + 31) / 32;        // K-blocks at or below the diagonal of row tile I
+    const size_t tok_stride = (size_t)H;            // tokens are [B, L, H, d]
+    const size_t base_tok = (size_t)b * L * tok_stride + h;
 
+    // Every load below is unconditional and unmasked: row indices past the
+    // ragged end are clamped to the last valid row, and the values are zeroed
+    // where they are consumed (one chunk later).  A select or a branch next to
+    // the load would make the wave wait for it here and defeat the prefetch.
+    auto fetch = [&](int n, PF &p) {
+        const int t0 = n * C;
+        const int Lc = min(C, L - t0);
+#pragma unroll
+        for (int i = 0; i < PF::KL; ++i) {
+            const int idx = min(tid + 256 * i, C * (DK / 8) - 1);
+            const int t = idx / (DK / 8), c8 = idx % (DK / 8);
+            load_raw8<TI>(p.k[i], k + (base_tok + (size_t)(t0 + min(t, Lc - 1)) * tok_stride) * DK + 8 * c8);
+        }
+        const int trow_c = min(16 * I + lr, Lc - 1);
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+            load_raw8<TI>(p.qf[kb], q + (base_tok + (size_t)(t0 + trow_c) * tok_stride) * DK + 32 * kb + 8 * lq);
+        const float *wsu = ws + (unit * NC + n) * (size_t)(2 * C * C + C);
+#pragma unroll
+        for (int kb = 0; kb < NKB_C; ++kb) {
+            const int kcc = min(32 * kb + 8 * lq, C - 8);
+            load_frag_f32(p.tf[kb], wsu + (16 * I + lr) * C + kcc);
+            load_frag_f32(p.pf[kb], wsu + C * C + (16 * I + lr) * C + kcc);
+        }
+#pragma unroll
+        for (int m = 0; m < MAXO; ++m) {
+            const int o = min(wave + 4 * m, NT_O - 1);
+            const int J = o / NTR;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * I + 4 * lq + r;
+                p.v[m][r] = v[(base_tok + (size_t)(t0 + min(t, Lc - 1)) * tok_stride) * DV + v0 + 16 * J + lr];
+            }
+        }
+        p.g = wsu[2 * C * C + min(tid, C - 1)];
+    };
+
+    // initial state -> registers (state tiles) and St (transposed)
     f32x4 Sacc[MAXS];
 #pragma unroll
     for (int m = 0; m < MAXS; ++m) {
         const int s = wave + 4 * m;
         Sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (s < NT_S && state_in) {
-            const int Ik = s / NTV, J = s % NTV;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Sacc[m][r] = state_in[(unit * DK + 16 * Ik + 4 * lq + r) * DV + v0 + 16 * J + lr];
-        }
         if (s < NT_S) {
             const int Ik = s / NTV, J = s % NTV;
+            if (state_in) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Sacc[m][r] = state_in[(unit * DK + 16 * Ik + 4 * lq + r) * DV + v0 + 16 * J + lr];
+            }
             *reinterpret_cast<float4 *>(St + (16 * J + lr) * KP + 16 * Ik + 4 * lq) =
                 make_float4(Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
         }
     }
 
+    // bf16: the next chunk's inputs are fetched while this chunk computes.
+    // fp32 (not pipelined): each chunk fetches its own inputs first.
+    constexpr bool PIPE = PREC == PREC_BF16;
+    PF cur, nxt;
+    if constexpr (PIPE) fetch(0, cur);
     for (int n = 0; n < NC; ++n) {
         const int t0 = n * C;
         const int Lc = min(C, L - t0);
-        const float *wsu = ws + (unit * NC + n) * (size_t)(2 * C * C + C);
-        const float *Tg = wsu, *Pg = wsu + C * C, *gg = wsu + 2 * C * C;
-        __syncthreads();
-        for (int idx = tid; idx < C * (DK / 8); idx += 256) {
-            const int t = idx / (DK / 8), c8 = idx % (DK / 8);
-            Frag fk;
-            if (t < Lc) load_row8<TI>(fk, k + ((size_t)(b * (size_t)L + t0 + t) * H + h) * DK + 8 * c8);
-            else zero_frag(fk);
-            float *pk = Ks + t * KP + 8 * c8;
-            *reinterpret_cast<float4 *>(pk) = make_float4(fk.x[0], fk.x[1], fk.x[2], fk.x[3]);
-            *reinterpret_cast<float4 *>(pk + 4) = make_float4(fk.x[4], fk.x[5], fk.x[6], fk.x[7]);
+        if constexpr (!PIPE) fetch(n, cur);
+        __syncthreads();   // the previous chunk is done with Ks and gs; St is complete
+#pragma unroll
+        for (int i = 0; i < PF::KL; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx < C * (DK / 8)) {
+                const int t = idx / (DK / 8), c8 = idx % (DK / 8);
+                Frag f;
+                raw_to_frag(f, cur.k[i]);
+                if (t >= Lc) zero_frag(f);
+                float *pk = Ks + t * KP + 8 * c8;
+                *reinterpret_cast<float4 *>(pk) = make_float4(f.x[0], f.x[1], f.x[2], f.x[3]);
+                *reinterpret_cast<float4 *>(pk + 4) = make_float4(f.x[4], f.x[5], f.x[6], f.x[7]);
+            }
         }
-        if (tid < C) gs[tid] = gg[tid];
+        if (tid < C) gs[tid] = cur.g;
         __syncthreads();
+        if constexpr (PIPE) {
+            if (n + 1 < NC) fetch(n + 1, nxt);   // in flight during this chunk
+        }
 
         // X_K = K S, X_Q = Q S;  R = V - e^g X_K (to LDS);  O = e^g X_Q (registers)
-        f32x4 Oacc[MAXO];
+        f32x4 xk[MAXO], xq[MAXO], Oacc[MAXO];
 #pragma unroll
         for (int m = 0; m < MAXO; ++m) {
-            const int o = wave + 4 * m;
-            Oacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (o >= NT_O) continue;
-            const int I = o / NTV, J = o % NTV;
-            f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = {0.f, 0.f, 0.f, 0.f};
-            const int trow = 16 * I + lr;
-            const TI *qrow = q + ((size_t)(b * (size_t)L + t0 + trow) * H + h) * DK;
+            xk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            xq[m] = xk[m];
+            Oacc[m] = xk[m];
+        }
+        if (has_o) {
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
-                Frag fk, fq, fs;
-                load_frag_f32(fk, Ks + trow * KP + 32 * kb + 8 * lq);
-                if (trow < Lc) load_row8<TI>(fq, qrow + 32 * kb + 8 * lq);
-                else zero_frag(fq);
-                load_frag_f32(fs, St + (16 * J + lr) * KP + 32 * kb + 8 * lq);
-                mma<PREC, true, false>(xk, fk, fs);
-                mma<PREC, true, false>(xq, fq, fs);
-            }
-            float rr[4];
+                Frag fk, fq;
+                load_frag_f32(fk, Ks + (16 * I + lr) * KP + 32 * kb + 8 * lq);
+                raw_to_frag(fq, cur.qf[kb]);
+                if (16 * I + lr >= Lc) zero_frag(fq);
+                const auto ak = make_op<PREC, true>(fk);
+                const auto aq = make_op<PREC, true>(fq);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * I + 4 * lq + r;
-                const float eg = expf(gs[t]);
-                const float vv = (t < Lc) ? load1<TI>(v + ((size_t)(b * (size_t)L + t0 + t) * H + h) * DV + v0 + 16 * J + lr) : 0.f;
-                rr[r] = vv - eg * xk[r];
-                Oacc[m][r] = eg * xq[r];
+                for (int m = 0; m < MAXO; ++m) {
+                    const int o = wave + 4 * m;
+                    if (o >= NT_O) continue;
+                    const int J = o / NTR;
+                    Frag fs;
+                    load_frag_f32(fs, St + (16 * J + lr) * KP + 32 * kb + 8 * lq);
+                    const auto bsop = make_op<PREC, false>(fs);
+                    mma_op<PREC, true, false>(xk[m], ak, bsop);
+                    mma_op<PREC, true, false>(xq[m], aq, bsop);
+                }
             }
-            *reinterpret_cast<float4 *>(Rt + (16 * J + lr) * CP + 16 * I + 4 * lq) = make_float4(rr[0], rr[1], rr[2], rr[3]);
+            float eg[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) eg[r] = expf(gs[16 * I + 4 * lq + r]);
+#pragma unroll
+            for (int m = 0; m < MAXO; ++m) {
+                const int o = wave + 4 * m;
+                if (o >= NT_O) continue;
+                const int J = o / NTR;
+                float rr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float vv = (16 * I + 4 * lq + r < Lc) ? to_f32(cur.v[m][r]) : 0.f;
+                    rr[r] = vv - eg[r] * xk[m][r];
+                    Oacc[m][r] = eg[r] * xq[m][r];
+                }
+                *reinterpret_cast<float4 *>(Rt + (16 * J + lr) * CP + 16 * I + 4 * lq) =
+                    make_float4(rr[0], rr[1], rr[2], rr[3]);
+            }
         }
         __syncthreads();
 
         // U = Tm R;  Ut = U, U2t = e^{g_C - g} U
         const float gC = gs[Lc - 1];
+        if (has_o) {
+            f32x4 ua[MAXO];
 #pragma unroll
-        for (int m = 0; m < MAXO; ++m) {
-            const int o = wave + 4 * m;
-            if (o >= NT_O) continue;
-            const int I = o / NTV, J = o % NTV;
-            f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
-            const int nkb = (16 * I + 16 + 31) / 32;
-            for (int kb = 0; kb < nkb; ++kb) {
+            for (int m = 0; m < MAXO; ++m) ua[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB_C; ++kb) {
+                if (kb >= nkb) continue;
                 const int kc = 32 * kb + 8 * lq;
-                Frag fa, fb;
-                if (kc < C) {
-                    load_frag_f32(fa, Tg + (16 * I + lr) * C + kc);
-                    load_frag_f32(fb, Rt + (16 * J + lr) * CP + kc);
-                } else {
-                    zero_frag(fa);
-                    zero_frag(fb);
-                }
-                mma<PREC, false, false>(uacc, fa, fb);
-            }
-            float w[4];
+                Frag ft = cur.tf[kb];
+                if (kc >= C) zero_frag(ft);
+                const auto at = make_op<PREC, false>(ft);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * I + 4 * lq + r;
-                w[r] = expf(gC - gs[t]) * uacc[r];
+                for (int m = 0; m < MAXO; ++m) {
+                    const int o = wave + 4 * m;
+                    if (o >= NT_O) continue;
+                    const int J = o / NTR;
+                    Frag fb;
+                    load_frag_f32(fb, Rt + (16 * J + lr) * CP + min(kc, C - 8));
+                    if (kc >= C) zero_frag(fb);
+                    mma_op<PREC, false, false>(ua[m], at, make_op<PREC, false>(fb));
+                }
             }
-            *reinterpret_cast<float4 *>(Ut + (16 * J + lr) * CP + 16 * I + 4 * lq) = make_float4(uacc[0], uacc[1], uacc[2], uacc[3]);
-            *reinterpret_cast<float4 *>(U2t + (16 * J + lr) * CP + 16 * I + 4 * lq) = make_float4(w[0], w[1], w[2], w[3]);
+            float w2[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w2[r] = expf(gC - gs[16 * I + 4 * lq + r]);
+#pragma unroll
+            for (int m = 0; m < MAXO; ++m) {
+                const int o = wave + 4 * m;
+                if (o >= NT_O) continue;
+                const int J = o / NTR;
+                *reinterpret_cast<float4 *>(Ut + (16 * J + lr) * CP + 16 * I + 4 * lq) =
+                    make_float4(ua[m][0], ua[m][1], ua[m][2], ua[m][3]);
+                *reinterpret_cast<float4 *>(U2t + (16 * J + lr) * CP + 16 * I + 4 * lq) =
+                    make_float4(w2[0] * ua[m][0], w2[1] * ua[m][1], w2[2] * ua[m][2], w2[3] * ua[m][3]);
+            }
         }
         __syncthreads();
 
         // O += P U, store
+        if (has_o) {
 #pragma unroll
-        for (int m = 0; m < MAXO; ++m) {
-            const int o = wave + 4 * m;
-            if (o >= NT_O) continue;
-            const int I = o / NTV, J = o % NTV;
-            const int nkb = (16 * I + 16 + 31) / 32;
-            for (int kb = 0; kb < nkb; ++kb) {
+            for (int kb = 0; kb < NKB_C; ++kb) {
+                if (kb >= nkb) continue;
                 const int kc = 32 * kb + 8 * lq;
-                Frag fa, fb;
-                if (kc < C) {
-                    load_frag_f32(fa, Pg + (16 * I + lr) * C + kc);
-                    load_frag_f32(fb, Ut + (16 * J + lr) * CP + kc);
-                } else {
-                    zero_frag(fa);
-                    zero_frag(fb);
+                Frag fp = cur.pf[kb];
+                if (kc >= C) zero_frag(fp);
+                const auto ap = make_op<PREC, false>(fp);
+#pragma unroll
+                for (int m = 0; m < MAXO; ++m) {
+                    const int o = wave + 4 * m;
+                    if (o >= NT_O) continue;
+                    const int J = o / NTR;
+                    Frag fb;
+                    load_frag_f32(fb, Ut + (16 * J + lr) * CP + min(kc, C - 8));
+                    if (kc >= C) zero_frag(fb);
+                    mma_op<PREC, false, false>(Oacc[m], ap, make_op<PREC, false>(fb));
                 }
-                mma<PREC, false, false>(Oacc[m], fa, fb);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * I + 4 * lq + r;
-                if (t < Lc) store1<TO>(out + ((size_t)(b * (size_t)L + t0 + t) * H + h) * DV + v0 + 16 * J + lr, Oacc[m][r]);
+            for (int m = 0; m < MAXO; ++m) {
+                const int o = wave + 4 * m;
+                if (o >= NT_O) continue;
+                const int J = o / NTR;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * I + 4 * lq + r;
+                    if (t < Lc) store1<TO>(out + (base_tok + (size_t)(t0 + t) * tok_stride) * DV + v0 + 16 * J + lr, Oacc[m][r]);
+                }
             }
         }
 
-        // S <- e^{g_C} S + K^T U2
+        // S <- e^{g_C} S + K^T U2   (the wave's state tiles share column tile J = wave % NTV)
         const float eC = expf(gC);
+        const int Js = wave % NTV;
+#pragma unroll
+        for (int m = 0; m < MAXS; ++m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[m][r] *= eC;
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB_C; ++kb) {
+            const int kc = 32 * kb + 8 * lq;
+            Frag fb;
+            load_frag_f32(fb, U2t + (16 * Js + lr) * CP + min(kc, C - 8));
+            if (kc >= C) zero_frag(fb);
+            const auto bu = make_op<PREC, false>(fb);
+#pragma unroll
+            for (int m = 0; m < MAXS; ++m) {
+                const int s = wave + 4 * m;
+                const int Ik = s / NTV;
+                Frag fa;
+                load_frag_strided(fa, Ks + min(kc, C - 8) * KP + 16 * Ik + lr, KP);
+                if (kc >= C) zero_frag(fa);
+                mma_op<PREC, true, false>(Sacc[m], make_op<PREC, true>(fa), bu);
+            }
+        }
 #pragma unroll
         for (int m = 0; m < MAXS; ++m) {
             const int s = wave + 4 * m;
-            if (s >= NT_S) continue;
-            const int Ik = s / NTV, J = s % NTV;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Sacc[m][r] *= eC;
-#pragma unroll
-            for (int kb = 0; kb < NKB_C; ++kb) {
-                const int kc = 32 * kb + 8 * lq;
-                Frag fa, fb;
-                if (kc < C) {
-                    load_frag_strided(fa, Ks + kc * KP + 16 * Ik + lr, KP);
-                    load_frag_f32(fb, U2t + (16 * J + lr) * CP + kc);
-                } else {
-                    zero_frag(fa);
-                    zero_frag(fb);
-                }
-                mma<PREC, true, false>(Sacc[m], fa, fb);
-            }
-            *reinterpret_cast<float4 *>(St + (16 * J + lr) * KP + 16 * Ik + 4 * lq) =
+            const int Ik = s / NTV;
+            *reinterpret_cast<float4 *>(St + (16 * Js + lr) * KP + 16 * Ik + 4 * lq) =
                 make_float4(Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+        }
+        if constexpr (PIPE) {
+            if (n + 1 < NC) cur = nxt;
         }
     }
 
@@ -357,7 +482,6 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
 #pragma unroll
         for (int m = 0; m < MAXS; ++m) {
             const int s = wave + 4 * m;
-            if (s >= NT_S) continue;
             const int Ik = s / NTV, J = s % NTV;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -372,37 +496,44 @@ size_t prefill_head_ws_bytes(int B, int L, int H, int C) {
 }
 
 template <int D, int C, int PREC, typename TI, typename TO>
-static hipError_t run(const GdnArgs &a, hipStream_t s) {
+static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
     constexpr int BV = 32;
     const int NC = (a.L + C - 1) / C;
-    hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI>), dim3(NC, a.H, a.B), dim3(256), 0, s,
-                       (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (float *)a.ws, a.L, a.H, NC);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_head_kernel<D, D, BV, C, PREC, TI, TO>), dim3(D / BV, a.H, a.B), dim3(256), 0, s,
-                       (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, (const float *)a.ws, a.state_in,
-                       (TO *)a.out, a.state_out, a.L, a.H, NC);
-    return hipGetLastError();
+    const unsigned units = (unsigned)a.B * (unsigned)a.H;
+    if (phase & PHASE_PREPARE) {
+        hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI>), dim3(units * NC), dim3(256), 0, s,
+                           (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (float *)a.ws, a.L, a.H, NC);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (phase & PHASE_SCAN) {
+        hipLaunchKernelGGL((scan_head_kernel<D, D, BV, C, PREC, TI, TO>), dim3(units * (D / BV)), dim3(256), 0, s,
+                           (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, (const float *)a.ws, a.state_in,
+                           (TO *)a.out, a.state_out, a.L, a.H, NC);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 template <int D, int C>
-static hipError_t run_t(const GdnArgs &a, hipStream_t s) {
+static hipError_t run_t(const GdnArgs &a, int phase, hipStream_t s) {
     if (a.qkv_bf16)
-        return a.out_bf16 ? run<D, C, PREC_BF16, uint16_t, uint16_t>(a, s) : run<D, C, PREC_BF16, uint16_t, float>(a, s);
-    return a.out_bf16 ? run<D, C, PREC_F32, float, uint16_t>(a, s) : run<D, C, PREC_F32, float, float>(a, s);
+        return a.out_bf16 ? run<D, C, PREC_BF16, uint16_t, uint16_t>(a, phase, s)
+                          : run<D, C, PREC_BF16, uint16_t, float>(a, phase, s);
+    return a.out_bf16 ? run<D, C, PREC_F32, float, uint16_t>(a, phase, s) : run<D, C, PREC_F32, float, float>(a, phase, s);
 }
 
 template <int D>
-static hipError_t run_c(const GdnArgs &a, hipStream_t s) {
+static hipError_t run_c(const GdnArgs &a, int phase, hipStream_t s) {
     switch (a.chunk) {
-        case 16: return run_t<D, 16>(a, s);
-        case 32: return run_t<D, 32>(a, s);
-        default: return run_t<D, 64>(a, s);
+        case 16: return run_t<D, 16>(a, phase, s);
+        case 32: return run_t<D, 32>(a, phase, s);
+        default: return run_t<D, 64>(a, phase, s);
     }
 }
 
-hipError_t launch_prefill_head(const GdnArgs &a, hipStream_t s) {
-    return a.dk == 64 ? run_c<64>(a, s) : run_c<128>(a, s);
+hipError_t launch_prefill_head(const GdnArgs &a, int phase, hipStream_t s) {
+    return a.dk == 64 ? run_c<64>(a, phase, s) : run_c<128>(a, phase, s);
 }
 
 }  // namespace lt2

@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.lt2_gdn_prefill_workspace_size.restype = Z
         L.lt2_gdn_prefill.argtypes = [GD, P, P, P, P, P, P, P, P, P, Z, P]
         L.lt2_gdn_prefill.restype = S
+        L.lt2_gdn_prefill_prepare.argtypes = [GD, P, P, P, P, P, Z, P]
+        L.lt2_gdn_prefill_prepare.restype = S
+        L.lt2_gdn_prefill_scan.argtypes = [GD, P, P, P, P, P, P, P, Z, P]
+        L.lt2_gdn_prefill_scan.restype = S
         L.lt2_gdn_decode_step.argtypes = [GD, P, P, P, P, P, P, P, P]
         L.lt2_gdn_decode_step.restype = S
         L.lt2_looped_mixer_workspace_size.argtypes = [LD]
