@@ -157,6 +157,13 @@ __device__ __forceinline__ void raw_to_frag(Frag &f, const Raw8<float> &r) {
     f.x[4] = r.b.x; f.x[5] = r.b.y; f.x[6] = r.b.z; f.x[7] = r.b.w;
 }
 
+// Wait until every outstanding vector-memory load of this wave has landed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt untouched).  Placed where prefetched
+// data is known to have had time to arrive, it also gives the compiler's
+// wait-count tracking a clean state across a loop back-edge, so later uses of
+// the prefetched registers do not wait on loads issued after them.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // The hardware hands out the workgroups of a launch to the 8 XCDs (each with
 // its own L2) round-robin by workgroup id.  This maps a 1-D id to a logical
 // index so that the ids one XCD receives get consecutive logical indices, i.e.
@@ -222,9 +229,37 @@ __device__ __forceinline__ void store1<float>(float *p, float x) { *p = x; }
 template <>
 __device__ __forceinline__ void store1<uint16_t>(uint16_t *p, float x) { *p = f32_to_bf16(x); }
 
-// log(alpha) with alpha = 0 mapped to a finite -80 (a factor below 2e-35).
-__device__ __forceinline__ float log_gate(float a) {
-    return fmaxf(logf(fmaxf(a, 1e-38f)), -80.f);
+// log2(alpha) with alpha = 0 mapped to a finite -116 (a factor below 2e-35).
+// Gates are carried in base 2 so that every decay factor is one v_exp_f32.
+__device__ __forceinline__ float log2_gate(float a) {
+    return fmaxf(__builtin_amdgcn_logf(fmaxf(a, 1e-38f)), -116.f);
 }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+// Four fp32 values -> bf16 hi and lo = bf16(x - hi), each packed in a uint2.
+__device__ __forceinline__ void split4(const float x[4], uint2 &hi, uint2 &lo) {
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const __bf16 hb = (__bf16)x[i];
+        h[i] = __builtin_bit_cast(uint16_t, hb);
+        l[i] = bf16_bits(x[i] - (float)hb);
+    }
+    hi = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+    lo = make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+}
+// Eight fp32 values -> bf16 hi and lo, each packed in a uint4.
+__device__ __forceinline__ void split8(const float x[8], uint4 &hi, uint4 &lo) {
+    uint2 h0, l0, h1, l1;
+    split4(x, h0, l0);
+    split4(x + 4, h1, l1);
+    hi = make_uint4(h0.x, h0.y, h1.x, h1.y);
+    lo = make_uint4(l0.x, l0.y, l1.x, l1.y);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 }  // namespace lt2

@@ -22,22 +22,28 @@
 namespace lt2 {
 
 // ---------------------------------------------------------------------------
-// Prepare: per chunk, Tm = (I + A)^{-1} diag(beta), P and g.  Workspace per
-// (b, h, chunk): Tm [C][C], P [C][C], g [C], fp32, zero above the diagonal.
+// Prepare: per chunk, Tm = (I + A)^{-1} diag(beta), P and the gate prefix g
+// (base 2).  Workspace per (b, h, chunk), (2*C*C + C) * 4 bytes:
+//   fp32 inputs: Tm [C][C] f32 | P [C][C] f32 | g [C] f32
+//   bf16 inputs: Tm hi, Tm lo, P hi, P lo [C][C] bf16 each | g [C] f32
+// (hi = bf16(x), lo = bf16(x - hi): the scan feeds them to bf16 matrix cores
+// without converting).  Tm and P are zero above the diagonal.
 // ---------------------------------------------------------------------------
 template <int DK, int C, int PREC, typename TI>
 __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                         const float *__restrict__ alpha,
-                                                        const float *__restrict__ beta, float *__restrict__ ws,
-                                                        int L, int H, int NC) {
+                                                        const float *__restrict__ beta,
+                                                        unsigned char *__restrict__ ws, int L, int H, int NC) {
     constexpr int KP = DK + 16 / (int)sizeof(TI);   // row pitch (elements), rows stay 16-byte aligned
     constexpr int CP = C + 4;
     constexpr int NT = C / 16;
+    constexpr int NLT = NT * (NT + 1) / 2;           // lower tiles (incl. diagonal)
+    constexpr int MAXP = (NLT + 3) / 4;              // Q K^T tiles per wave
     constexpr int K_BYTES = C * KP * (int)sizeof(TI);
     constexpr int T_BYTES = C * CP * 4;
-    // K is dead once the gated Gram tiles are formed; the inverse reuses its space.
+    // K is dead once the Gram tiles are formed; the inverse reuses its space.
     __shared__ __attribute__((aligned(16))) unsigned char kt_raw[K_BYTES > T_BYTES ? K_BYTES : T_BYTES];
-    __shared__ float Am[C * CP];
+    __shared__ float Am[C * CP];   // gated K K^T, then P
     __shared__ float Xs[4][16 * 17];
     __shared__ float gs[C], bs[C];
     TI *Ks = reinterpret_cast<TI *>(kt_raw);
@@ -50,8 +56,8 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     const int lr = lane & 15, lq = lane >> 4;
     const int t0 = n * C;
     const int Lc = min(C, L - t0);
-    float *wsu = ws + ((size_t)unit * NC + n) * (size_t)(2 * C * C + C);
-    float *Tg = wsu, *Pg = wsu + C * C, *gg = wsu + 2 * C * C;
+    unsigned char *wsu = ws + ((size_t)unit * NC + n) * (size_t)(8 * C * C + 4 * C);
+    float *gg = reinterpret_cast<float *>(wsu + 8 * C * C);
 
     for (int idx = tid; idx < C * (DK / 8); idx += 256) {
         const int t = idx / (DK / 8), c8 = idx % (DK / 8);
@@ -63,8 +69,7 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     if (wave == 0) {
         const size_t tok = (size_t)(b * (size_t)L + t0 + min(lane, Lc - 1)) * H + h;
         const float a_raw = alpha[tok], b_raw = beta[tok];
-        const float lg0 = log_gate(a_raw);
-        float lg = (lane < Lc) ? lg0 : 0.f;
+        float lg = (lane < Lc) ? log2_gate(a_raw) : 0.f;
         const float bt = (lane < Lc) ? b_raw : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -76,43 +81,47 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     __syncthreads();
 
     // Gated K K^T (strictly lower, rows scaled by beta) into Am; gated Q K^T
-    // (lower incl.) straight to the workspace.  Upper tiles are zero.
-    for (int tt = wave; tt < 2 * NT * NT; tt += 4) {
-        const int which = tt / (NT * NT);  // 0: KK^T, 1: QK^T
-        const int I = (tt % (NT * NT)) / NT, J = tt % NT;
+    // tiles (lower incl.) stay in registers until the inverse is done.
+    for (int tt = wave; tt < NT * NT; tt += 4) {
+        const int I = tt / NT, J = tt % NT;
         if (J > I) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (which == 0) Am[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = 0.f;
-                else Pg[(16 * I + 4 * lq + r) * C + 16 * J + lr] = 0.f;
-            }
+            for (int r = 0; r < 4; ++r) Am[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = 0.f;
             continue;
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int arow = 16 * I + lr;
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
-            Raw8<TI> ra, rb;
-            if (which == 0) {
-                ra = *reinterpret_cast<const Raw8<TI> *>(Ks + arow * KP + 32 * kb + 8 * lq);
-            } else {
-                load_raw8<TI>(ra, q + ((size_t)(b * (size_t)L + t0 + min(arow, Lc - 1)) * H + h) * DK + 32 * kb + 8 * lq);
-                if (arow >= Lc) zero_raw8<TI>(ra);
-            }
-            rb = *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq);
             Frag fa, fb;
-            raw_to_frag(fa, ra);
-            raw_to_frag(fb, rb);
+            raw_to_frag(fa, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * I + lr) * KP + 32 * kb + 8 * lq));
+            raw_to_frag(fb, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq));
             mma<PREC, true, true>(acc, fa, fb);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
-            if (which == 0) {
-                Am[t * CP + i] = (i < t) ? bs[t] * expf(gs[t] - gs[i]) * acc[r] : 0.f;
-            } else {
-                Pg[t * C + i] = (i <= t && t < Lc) ? expf(gs[t] - gs[i]) * acc[r] : 0.f;
-            }
+            Am[t * CP + i] = (i < t) ? bs[t] * exp2_fast(gs[t] - gs[i]) * acc[r] : 0.f;
+        }
+    }
+    f32x4 pacc[MAXP];
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+        pacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tt = wave + 4 * m;
+        if (tt >= NLT) continue;
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= tt) ++I;
+        const int J = tt - I * (I + 1) / 2;
+        const int arow = 16 * I + lr;
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            Raw8<TI> ra;
+            load_raw8<TI>(ra, q + ((size_t)(b * (size_t)L + t0 + min(arow, Lc - 1)) * H + h) * DK + 32 * kb + 8 * lq);
+            Frag fa, fb;
+            raw_to_frag(fa, ra);
+            if (arow >= Lc) zero_frag(fa);
+            raw_to_frag(fb, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq));
+            mma<PREC, true, true>(pacc[m], fa, fb);
         }
     }
     __syncthreads();
@@ -165,22 +174,60 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
         __syncthreads();
     }
 
-    // Tm = T diag(beta), zero above the diagonal; four consecutive floats per store.
-    for (int idx = tid; idx < C * C / 4; idx += 256) {
-        const int t = idx / (C / 4), i0 = 4 * (idx % (C / 4));
-        float4 w;
-        w.x = (i0 + 0 <= t) ? Ti[t * CP + i0 + 0] * bs[i0 + 0] : 0.f;
-        w.y = (i0 + 1 <= t) ? Ti[t * CP + i0 + 1] * bs[i0 + 1] : 0.f;
-        w.z = (i0 + 2 <= t) ? Ti[t * CP + i0 + 2] * bs[i0 + 2] : 0.f;
-        w.w = (i0 + 3 <= t) ? Ti[t * CP + i0 + 3] * bs[i0 + 3] : 0.f;
-        *reinterpret_cast<float4 *>(Tg + t * C + i0) = w;
+    // Gated P into Am's space (Am is dead after the inverse), zero above the diagonal.
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+        const int tt = wave + 4 * m;
+        if (tt >= NLT) continue;
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= tt) ++I;
+        const int J = tt - I * (I + 1) / 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
+            Am[t * CP + i] = (i <= t && t < Lc) ? exp2_fast(gs[t] - gs[i]) * pacc[m][r] : 0.f;
+        }
+    }
+    for (int tt = wave; tt < NT * NT; tt += 4) {
+        const int I = tt / NT, J = tt % NT;
+        if (J <= I) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Am[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = 0.f;
+    }
+    __syncthreads();
+
+    // Coalesced stores: eight consecutive entries per lane.  Tm = T diag(beta).
+    for (int idx = tid; idx < C * C / 8; idx += 256) {
+        const int t = idx / (C / 8), i0 = 8 * (idx % (C / 8));
+        float tv[8], pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            tv[e] = (i0 + e <= t) ? Ti[t * CP + i0 + e] * bs[i0 + e] : 0.f;
+            pv[e] = Am[t * CP + i0 + e];
+        }
+        if constexpr (PREC == PREC_F32) {
+            float *Tg = reinterpret_cast<float *>(wsu), *Pg = Tg + C * C;
+            *reinterpret_cast<float4 *>(Tg + t * C + i0) = make_float4(tv[0], tv[1], tv[2], tv[3]);
+            *reinterpret_cast<float4 *>(Tg + t * C + i0 + 4) = make_float4(tv[4], tv[5], tv[6], tv[7]);
+            *reinterpret_cast<float4 *>(Pg + t * C + i0) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+            *reinterpret_cast<float4 *>(Pg + t * C + i0 + 4) = make_float4(pv[4], pv[5], pv[6], pv[7]);
+        } else {
+            uint16_t *Th = reinterpret_cast<uint16_t *>(wsu);
+            uint4 hi, lo;
+            split8(tv, hi, lo);
+            *reinterpret_cast<uint4 *>(Th + t * C + i0) = hi;
+            *reinterpret_cast<uint4 *>(Th + C * C + t * C + i0) = lo;
+            split8(pv, hi, lo);
+            *reinterpret_cast<uint4 *>(Th + 2 * C * C + t * C + i0) = hi;
+            *reinterpret_cast<uint4 *>(Th + 3 * C * C + t * C + i0) = lo;
+        }
     }
     if (tid < C) gg[tid] = gs[tid];
 }
 
 // ---------------------------------------------------------------------------
-// Scan: state carried across the chunks of one (b, h) unit for BV columns.
-// Workgroup layout: 4 waves; wave w owns output row tile I = w % (C/16) and the
+// Scan, fp32 inputs (fp32 matrix cores): state carried across the chunks of
+// one (b, h) unit for BV columns.  Workgroup layout: 4 waves; wave w owns output row tile I = w % (C/16) and the
 // column tiles J of the output tiles o = w + 4m (o = I + (C/16) J); the state
 // tiles s = w + 4m (s = (dk tile) * (BV/16) + J) share one column tile.
 // ---------------------------------------------------------------------------
@@ -349,7 +396,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
             }
             float eg[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) eg[r] = expf(gs[16 * I + 4 * lq + r]);
+            for (int r = 0; r < 4; ++r) eg[r] = exp2_fast(gs[16 * I + 4 * lq + r]);
 #pragma unroll
             for (int m = 0; m < MAXO; ++m) {
                 const int o = wave + 4 * m;
@@ -394,7 +441,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
             }
             float w2[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w2[r] = expf(gC - gs[16 * I + 4 * lq + r]);
+            for (int r = 0; r < 4; ++r) w2[r] = exp2_fast(gC - gs[16 * I + 4 * lq + r]);
 #pragma unroll
             for (int m = 0; m < MAXO; ++m) {
                 const int o = wave + 4 * m;
@@ -442,7 +489,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
         }
 
         // S <- e^{g_C} S + K^T U2   (the wave's state tiles share column tile J = wave % NTV)
-        const float eC = expf(gC);
+        const float eC = exp2_fast(gC);
         const int Js = wave % NTV;
 #pragma unroll
         for (int m = 0; m < MAXS; ++m) {
@@ -490,6 +537,275 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Scan, bf16 inputs: 8 waves (two per SIMD) per (b, h, BV-column block).
+// Every LDS operand is stored as bf16 by the one wave that produces it: K raw
+// (row-major for K S, transposed for K^T U2), and the fp32 intermediates S, R,
+// U, U2 as hi/lo pairs, so the matrix cores read them without conversion.
+// fp32 x fp32 products take hi*hi + lo*hi + hi*lo; bf16-exact inputs (q, k)
+// take one or two products.  The next chunk's inputs are in flight in
+// registers while the current chunk computes.
+// ---------------------------------------------------------------------------
+template <int DK, int C>
+struct ScanPrefetchBf16 {
+    static constexpr int NKB_C = (C + 31) / 32;
+    static constexpr int KL = (C * (DK / 8) + 511) / 512;
+    uint4 k[KL];                                  // K rows (8 bf16 each)
+    uint4 q[DK / 32];                             // Q fragments of the wave's row tile
+    uint4 th[NKB_C], tl[NKB_C], ph[NKB_C], pl[NKB_C];  // Tm, P fragments (hi/lo)
+    uint16_t v[4];                                // V entries of the wave's tile
+    float g;                                      // g[tid] (tid < C)
+};
+
+template <int DK, int DV, int BV, int C, typename TO>
+__global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__restrict__ q,
+                                                             const uint16_t *__restrict__ k,
+                                                             const uint16_t *__restrict__ v,
+                                                             const unsigned char *__restrict__ ws,
+                                                             const float *__restrict__ state_in,
+                                                             TO *__restrict__ out, float *__restrict__ state_out,
+                                                             int L, int H, int NC) {
+    using PF = ScanPrefetchBf16<DK, C>;
+    constexpr int NW = 8;
+    constexpr int KP = DK + 8;   // bf16 pitch of Ks and S^T rows (16-byte aligned, staggered banks)
+    constexpr int CP = C + 8;    // bf16 pitch of K^T, R^T, U^T, U2^T rows
+    constexpr int NTR = C / 16, NTV = BV / 16, NTK = DK / 16;
+    constexpr int NT_O = NTR * NTV, NT_S = NTK * NTV;
+    constexpr int MAXS = NT_S / NW;
+    constexpr int NKB_C = (C + 31) / 32;
+    constexpr int NV = DV / BV;
+    constexpr int WSB = 8 * C * C + 4 * C;   // workspace bytes per chunk
+    static_assert(NT_O <= NW && NT_S % NW == 0 && NW % NTV == 0, "scan tiling");
+
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t KsT[DK * CP];
+    __shared__ __attribute__((aligned(16))) uint16_t Sth[BV * KP], Stl[BV * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t Rth[BV * CP], Rtl[BV * CP];
+    __shared__ __attribute__((aligned(16))) uint16_t Uth[BV * CP], Utl[BV * CP];
+    __shared__ __attribute__((aligned(16))) uint16_t U2h[BV * CP], U2l[BV * CP];
+    __shared__ float gs[C];
+
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    const int vb = logical % NV;
+    const size_t unit = logical / NV;
+    const int h = (int)(unit % H), b = (int)(unit / H);
+    const int v0 = vb * BV;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const bool has_o = wave < NT_O;
+    const int ot = has_o ? wave : NT_O - 1;
+    const int I = ot % NTR, J = ot / NTR;          // this wave's output tile
+    const int nkb = (16 * I + 16 + 31) / 32;       // K-blocks at or below the diagonal
+    const int Js = wave % NTV;                     // column tile of this wave's state tiles
+    const size_t base_tok = (size_t)b * L * H + h; // tokens are [B, L, H, d]
+
+    // Unconditional, unmasked loads with clamped rows; masking happens at use.
+    auto fetch = [&](int n, PF &p) {
+        const int t0 = n * C;
+        const int Lc = min(C, L - t0);
+#pragma unroll
+        for (int i = 0; i < PF::KL; ++i) {
+            const int idx = min(tid + 512 * i, C * (DK / 8) - 1);
+            const int t = idx % C, c8 = idx / C;   // a wave covers consecutive tokens
+            p.k[i] = *reinterpret_cast<const uint4 *>(k + (base_tok + (size_t)(t0 + min(t, Lc - 1)) * H) * DK + 8 * c8);
+        }
+        const int trow_c = min(16 * I + lr, Lc - 1);
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+            p.q[kb] = *reinterpret_cast<const uint4 *>(q + (base_tok + (size_t)(t0 + trow_c) * H) * DK + 32 * kb + 8 * lq);
+        const unsigned char *wsu = ws + (unit * NC + n) * (size_t)WSB;
+        const uint16_t *wt = reinterpret_cast<const uint16_t *>(wsu);
+#pragma unroll
+        for (int kb = 0; kb < NKB_C; ++kb) {
+            const int off = (16 * I + lr) * C + min(32 * kb + 8 * lq, C - 8);
+            p.th[kb] = *reinterpret_cast<const uint4 *>(wt + off);
+            p.tl[kb] = *reinterpret_cast<const uint4 *>(wt + C * C + off);
+            p.ph[kb] = *reinterpret_cast<const uint4 *>(wt + 2 * C * C + off);
+            p.pl[kb] = *reinterpret_cast<const uint4 *>(wt + 3 * C * C + off);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * I + 4 * lq + r;
+            p.v[r] = v[(base_tok + (size_t)(t0 + min(t, Lc - 1)) * H) * DV + v0 + 16 * J + lr];
+        }
+        p.g = reinterpret_cast<const float *>(wsu + 8 * C * C)[min(tid, C - 1)];
+    };
+
+    auto store_split = [&](uint16_t *hi, uint16_t *lo, int off, const float x[4]) {
+        uint2 h2, l2;
+        split4(x, h2, l2);
+        *reinterpret_cast<uint2 *>(hi + off) = h2;
+        *reinterpret_cast<uint2 *>(lo + off) = l2;
+    };
+
+    // initial state: registers (state tiles) and S^T (hi/lo) in LDS
+    f32x4 Sacc[MAXS];
+#pragma unroll
+    for (int m = 0; m < MAXS; ++m) {
+        const int Ik = (wave + NW * m) / NTV;
+        Sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (state_in) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Sacc[m][r] = state_in[(unit * DK + 16 * Ik + 4 * lq + r) * DV + v0 + 16 * Js + lr];
+        }
+        const float x[4] = {Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]};
+        store_split(Sth, Stl, (16 * Js + lr) * KP + 16 * Ik + 4 * lq, x);
+    }
+
+    PF cur, nxt;
+    fetch(0, cur);
+    for (int n = 0; n < NC; ++n) {
+        const int t0 = n * C;
+        const int Lc = min(C, L - t0);
+        wait_vmem_all();   // this chunk's prefetch was issued one chunk ago
+        __syncthreads();   // the previous chunk is done with Ks, K^T, U^T, U2^T and gs
+#pragma unroll
+        for (int i = 0; i < PF::KL; ++i) {
+            const int idx = tid + 512 * i;
+            if (idx < C * (DK / 8)) {
+                const int t = idx % C, c8 = idx / C;
+                const uint4 r = (t < Lc) ? cur.k[i] : make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4 *>(Ks + t * KP + 8 * c8) = r;
+                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    KsT[(8 * c8 + 2 * e) * CP + t] = (uint16_t)(w[e] & 0xFFFFu);
+                    KsT[(8 * c8 + 2 * e + 1) * CP + t] = (uint16_t)(w[e] >> 16);
+                }
+            }
+        }
+        if (tid < C) gs[tid] = cur.g;
+        __syncthreads();
+        if (n + 1 < NC) fetch(n + 1, nxt);   // in flight during this chunk
+
+        // X_K = K S, X_Q = Q S;  R = V - e^g X_K  (hi/lo to LDS);  O = e^g X_Q
+        f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+        if (has_o) {
+            f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = xk;
+            const bool qrow = 16 * I + lr < Lc;
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(Ks + (16 * I + lr) * KP + 32 * kb + 8 * lq);
+                const bf16x8 aq = as_bf16x8(qrow ? cur.q[kb] : make_uint4(0u, 0u, 0u, 0u));
+                const int so = (16 * J + lr) * KP + 32 * kb + 8 * lq;
+                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(Sth + so);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(Stl + so);
+                xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bh, xk, 0, 0, 0);
+                xq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bh, xq, 0, 0, 0);
+                xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bl, xk, 0, 0, 0);
+                xq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bl, xq, 0, 0, 0);
+            }
+            float rr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * I + 4 * lq + r;
+                const float eg = exp2_fast(gs[t]);
+                const float vv = (t < Lc) ? bf16_to_f32(cur.v[r]) : 0.f;
+                rr[r] = vv - eg * xk[r];
+                oacc[r] = eg * xq[r];
+            }
+            store_split(Rth, Rtl, (16 * J + lr) * CP + 16 * I + 4 * lq, rr);
+        }
+        __syncthreads();
+
+        // U = Tm R;  U^T and U2^T = (e^{g_C - g} U)^T as hi/lo
+        const float gC = gs[Lc - 1];
+        if (has_o) {
+            f32x4 ua = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB_C; ++kb) {
+                if (kb >= nkb) continue;
+                const int kc = 32 * kb + 8 * lq;
+                const bool kin = kc < C;
+                const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+                const bf16x8 th = as_bf16x8(kin ? cur.th[kb] : z), tl = as_bf16x8(kin ? cur.tl[kb] : z);
+                const int ro = (16 * J + lr) * CP + min(kc, C - 8);
+                const bf16x8 rh = *reinterpret_cast<const bf16x8 *>(Rth + ro);
+                const bf16x8 rl = *reinterpret_cast<const bf16x8 *>(Rtl + ro);
+                ua = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh, ua, 0, 0, 0);
+                ua = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh, ua, 0, 0, 0);
+                ua = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl, ua, 0, 0, 0);
+            }
+            float u[4], w2[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                u[r] = ua[r];
+                w2[r] = exp2_fast(gC - gs[16 * I + 4 * lq + r]) * ua[r];
+            }
+            const int uo = (16 * J + lr) * CP + 16 * I + 4 * lq;
+            store_split(Uth, Utl, uo, u);
+            store_split(U2h, U2l, uo, w2);
+        }
+        __syncthreads();
+
+        // O += P U, store
+        if (has_o) {
+#pragma unroll
+            for (int kb = 0; kb < NKB_C; ++kb) {
+                if (kb >= nkb) continue;
+                const int kc = 32 * kb + 8 * lq;
+                const bool kin = kc < C;
+                const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+                const bf16x8 ph = as_bf16x8(kin ? cur.ph[kb] : z), pl = as_bf16x8(kin ? cur.pl[kb] : z);
+                const int uo = (16 * J + lr) * CP + min(kc, C - 8);
+                const bf16x8 uh = *reinterpret_cast<const bf16x8 *>(Uth + uo);
+                const bf16x8 ul = *reinterpret_cast<const bf16x8 *>(Utl + uo);
+                oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, uh, oacc, 0, 0, 0);
+                oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, uh, oacc, 0, 0, 0);
+                oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ul, oacc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * I + 4 * lq + r;
+                if (t < Lc) store1<TO>(out + (base_tok + (size_t)(t0 + t) * H) * DV + v0 + 16 * J + lr, oacc[r]);
+            }
+        }
+
+        // S <- e^{g_C} S + K^T U2
+        const float eC = exp2_fast(gC);
+#pragma unroll
+        for (int m = 0; m < MAXS; ++m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[m][r] *= eC;
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB_C; ++kb) {
+            const int kc = 32 * kb + 8 * lq;
+            const bool kin = kc < C;
+            const int kcc = min(kc, C - 8);
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            const bf16x8 bh = as_bf16x8(kin ? *reinterpret_cast<const uint4 *>(U2h + (16 * Js + lr) * CP + kcc) : z);
+            const bf16x8 bl = as_bf16x8(kin ? *reinterpret_cast<const uint4 *>(U2l + (16 * Js + lr) * CP + kcc) : z);
+#pragma unroll
+            for (int m = 0; m < MAXS; ++m) {
+                const int Ik = (wave + NW * m) / NTV;
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(KsT + (16 * Ik + lr) * CP + kcc);
+                Sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, Sacc[m], 0, 0, 0);
+                Sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, Sacc[m], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MAXS; ++m) {
+            const int Ik = (wave + NW * m) / NTV;
+            const float x[4] = {Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]};
+            store_split(Sth, Stl, (16 * Js + lr) * KP + 16 * Ik + 4 * lq, x);
+        }
+        if (n + 1 < NC) cur = nxt;
+    }
+
+    if (state_out) {
+#pragma unroll
+        for (int m = 0; m < MAXS; ++m) {
+            const int Ik = (wave + NW * m) / NTV;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                state_out[(unit * DK + 16 * Ik + 4 * lq + r) * DV + v0 + 16 * Js + lr] = Sacc[m][r];
+        }
+    }
+}
+
 size_t prefill_head_ws_bytes(int B, int L, int H, int C) {
     const size_t NC = (size_t)((L + C - 1) / C);
     return (size_t)B * H * NC * (size_t)(2 * C * C + C) * sizeof(float);
@@ -502,14 +818,20 @@ static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
     const unsigned units = (unsigned)a.B * (unsigned)a.H;
     if (phase & PHASE_PREPARE) {
         hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI>), dim3(units * NC), dim3(256), 0, s,
-                           (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (float *)a.ws, a.L, a.H, NC);
+                           (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (unsigned char *)a.ws, a.L, a.H, NC);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (phase & PHASE_SCAN) {
-        hipLaunchKernelGGL((scan_head_kernel<D, D, BV, C, PREC, TI, TO>), dim3(units * (D / BV)), dim3(256), 0, s,
-                           (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, (const float *)a.ws, a.state_in,
-                           (TO *)a.out, a.state_out, a.L, a.H, NC);
+        if constexpr (PREC == PREC_BF16) {
+            hipLaunchKernelGGL((scan_head_bf16_kernel<D, D, BV, C, TO>), dim3(units * (D / BV)), dim3(512), 0, s,
+                               (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                               (const unsigned char *)a.ws, a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC);
+        } else {
+            hipLaunchKernelGGL((scan_head_kernel<D, D, BV, C, PREC, TI, TO>), dim3(units * (D / BV)), dim3(256), 0, s,
+                               (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, (const float *)a.ws, a.state_in,
+                               (TO *)a.out, a.state_out, a.L, a.H, NC);
+        }
         return hipGetLastError();
     }
     return hipSuccess;
