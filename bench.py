@@ -213,6 +213,41 @@ def bench_decode(args, torch, lt2, synth):
                 tokens_per_s_per_loop=B * steps * T / (span_ms / 1e3) / T)
 
 
+def bench_looped(args, torch, lt2, synth, reps=5):
+    """T=4 loops of the LT2-linear block, B=2 L=8192 d_model=2048 H=16 d=128."""
+    cfg = synth.CONFIGS[3]
+    sh = cfg["shape"]
+    log(f"looped inputs B={sh.B} L={sh.L} D={sh.d_model} H={sh.H} d={sh.d} T={sh.T}")
+    w = synth.loop_weights(sh, seed=0)
+    h0 = torch.from_numpy(synth.loop_h0(sh, seed=0)).to("cuda")
+    w_in = torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16)
+    w_o = torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)
+    h_out = torch.empty_like(h0)
+    desc = lt2.loop_desc(sh.B, sh.L, sh.d_model, sh.H, sh.d, sh.T, cfg["chunk"])
+    ws_bytes = lt2.lt2_looped_mixer_workspace_size(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        lt2.lt2_looped_mixer(h0, w_in, w_o, sh.H, sh.d, sh.T, chunk=cfg["chunk"], h_out=h_out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        lt2.lt2_looped_mixer(h0, w_in, w_o, sh.H, sh.d, sh.T, chunk=cfg["chunk"], h_out=h_out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    M, D, Hd, N_in = sh.B * sh.L, sh.d_model, sh.H * sh.d, 3 * sh.H * sh.d + 2 * sh.H
+    gemm_flops = sh.T * 2.0 * M * D * (N_in + Hd)
+    C = cfg["chunk"]
+    gdn_flops = sh.T * prefill_flops_bytes(sh.B, sh.L, sh.H, sh.d, C)["path_flops"]
+    log(f"looped {ms:.3f} ms per call ({sh.T} loops)")
+    return dict(B=sh.B, L=sh.L, d_model=D, H=sh.H, d=sh.d, T=sh.T, ms=ms,
+                tokens_per_s_per_loop=M * sh.T / (ms / 1e3) / sh.T,
+                gemm_flops=gemm_flops, gdn_flops=gdn_flops,
+                tflops=(gemm_flops + gdn_flops) / ms / 1e9,
+                mfma_frac=(gemm_flops + gdn_flops) / ms / 1e9 / BF16_PEAK_TFLOPS)
+
+
 def _slab_inputs(synth, shape, b0, nb):
     """Inputs of batch rows b0..b0+nb of the decode-seeding prefill (per-unit streams)."""
     L, H, d = shape.L, shape.H, shape.dk
@@ -254,6 +289,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-looped", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -272,6 +308,7 @@ def main():
     copy = bench_copy(torch, lt2)
     log(f"copy probe {copy['gbs']:.0f} GB/s")
     dec = None if args.no_decode else bench_decode(args, torch, lt2, synth)
+    loo = None if args.no_looped else bench_looped(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
     value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
@@ -291,6 +328,8 @@ def main():
         extra["decode"] = dict(dec, hbm_frac_kernel=dec["gbs_kernel"] / HBM_PEAK_GBS,
                                copy_frac_kernel=dec["gbs_kernel"] / copy["gbs"],
                                hbm_frac_span=dec["gbs_span"] / HBM_PEAK_GBS)
+    if loo:
+        extra["looped"] = loo
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",

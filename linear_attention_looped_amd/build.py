@@ -27,8 +27,10 @@ def hipcc() -> str:
 
 def cflags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
-            # packed fp32 VALU ops are left to nothing: they are kept out of every kernel
+            # no packed fp32 VALU instructions in any kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # private arrays stay in registers: never silently moved into LDS
+            "-mllvm", "-disable-promote-alloca-to-lds",
             "-I", INCLUDE, "-I", CSRC]
 
 

@@ -151,14 +151,46 @@ lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream) 
 
 }  // extern "C"
 
+namespace {
+
+lt2_status check_loop(const lt2_loop_desc *d) {
+    if (!d) return LT2_ERR_NULL;
+    if (d->B < 0 || d->L < 0 || d->T < 0 || d->d_model <= 0 || d->H <= 0 || d->d_head <= 0) return LT2_ERR_SHAPE;
+    if (d->d_head != 64 && d->d_head != 128) return LT2_ERR_UNSUPPORTED;
+    if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return LT2_ERR_UNSUPPORTED;
+    // GEMM tiles: K-tiles of 64, residual and head blocks whole 128-column tiles
+    if (d->d_model % 128 != 0 || ((int64_t)d->H * d->d_head) % 128 != 0) return LT2_ERR_UNSUPPORTED;
+    if ((int64_t)d->B * d->L > 0x7fffffffLL || (int64_t)d->H * d->d_head > 65536 || d->H > 65535 || d->B > 65535)
+        return LT2_ERR_SHAPE;
+    return LT2_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
-size_t lt2_looped_mixer_workspace_size(const lt2_loop_desc *) { return 0; }
+size_t lt2_looped_mixer_workspace_size(const lt2_loop_desc *desc) {
+    if (check_loop(desc) != LT2_OK) return 0;
+    if (desc->B == 0 || desc->L == 0) return 0;
+    return loop_layout(desc->B, desc->L, desc->d_model, desc->H, desc->d_head, desc->chunk).total;
+}
 
-lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *, float *, const void *, const void *, void *,
-                            size_t, void *) {
-    if (!desc) return LT2_ERR_NULL;
-    return LT2_ERR_UNSUPPORTED;
+lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *h_in, float *h_out, const void *W_in,
+                            const void *W_o, void *ws, size_t ws_bytes, void *stream) {
+    lt2_status st = check_loop(desc);
+    if (st != LT2_OK) return st;
+    const bool work = desc->B > 0 && desc->L > 0;
+    if (work && (!h_in || !h_out || !W_in || !W_o)) return LT2_ERR_NULL;
+    if (!aligned(h_in, 16) || !aligned(h_out, 16) || !aligned(W_in, 16) || !aligned(W_o, 16)) return LT2_ERR_ALIGN;
+    const size_t need = work ? loop_layout(desc->B, desc->L, desc->d_model, desc->H, desc->d_head, desc->chunk).total : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 256)) return LT2_ERR_ALIGN;
+    if (!work) return LT2_OK;
+    LoopArgs a;
+    a.B = desc->B; a.L = desc->L; a.D = desc->d_model; a.H = desc->H; a.d = desc->d_head; a.T = desc->T;
+    a.chunk = desc->chunk; a.h_in = h_in; a.h_out = h_out;
+    a.W_in = static_cast<const uint16_t *>(W_in); a.W_o = static_cast<const uint16_t *>(W_o); a.ws = ws;
+    return hip_status(launch_looped(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -30,6 +30,21 @@ hipError_t launch_prefill_head(const GdnArgs &a, int phase, hipStream_t s);
 size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C);
 hipError_t launch_prefill_channel(const GdnArgs &a, int phase, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+
+// Looped LT2-linear block.
+struct LoopArgs {
+    int B, L, D, H, d, T, chunk;
+    const float *h_in;
+    float *h_out;
+    const uint16_t *W_in, *W_o;
+    void *ws;
+};
+// Byte offsets of the looped block's buffers inside its workspace.
+struct LoopLayout {
+    size_t xb, q, k, v, beta, alpha, o, prefill, total;
+};
+LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk);
+hipError_t launch_looped(const LoopArgs &a, hipStream_t s);
 hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t s);
 
 }  // namespace lt2

@@ -1,0 +1,64 @@
+// looped.hip -- the looped LT2-linear block: T applications of one shared-weight
+// block (LT2 explainer, paithon.it, "Profondita presa in prestito", first
+// equation), each a gated-delta mixer with fresh zero state:
+//   xb = bf16(h)                                    (cast kernel, first loop only)
+//   [q|k|v|beta|alpha] = xb W_in^T  + per-head L2 norm and gate transforms (GEMM)
+//   o = gated-delta prefill(q, k, v, alpha, beta; S_0 = 0), bf16
+//   h += o W_o^T, xb = bf16(h)                      (GEMM with residual epilogue)
+// All launches are enqueued on one stream; nothing synchronises in between.
+#include "gemm.h"
+#include "internal.h"
+
+namespace lt2 {
+
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk) {
+    LoopLayout w{};
+    const size_t M = (size_t)B * L, Hd = (size_t)H * d;
+    size_t off = 0;
+    w.xb = off; off = align256(off + M * D * 2);
+    w.q = off; off = align256(off + M * Hd * 2);
+    w.k = off; off = align256(off + M * Hd * 2);
+    w.v = off; off = align256(off + M * Hd * 2);
+    w.beta = off; off = align256(off + M * H * 4);
+    w.alpha = off; off = align256(off + M * H * 4);
+    w.o = off; off = align256(off + M * Hd * 2);
+    w.prefill = off; off = align256(off + prefill_head_ws_bytes(B, L, H, chunk));
+    w.total = off;
+    return w;
+}
+
+hipError_t launch_looped(const LoopArgs &a, hipStream_t s) {
+    const int M = a.B * a.L, Hd = a.H * a.d, N_in = 3 * Hd + 2 * a.H;
+    unsigned char *ws = static_cast<unsigned char *>(a.ws);
+    const LoopLayout w = loop_layout(a.B, a.L, a.D, a.H, a.d, a.chunk);
+    uint16_t *xb = reinterpret_cast<uint16_t *>(ws + w.xb);
+    uint16_t *q = reinterpret_cast<uint16_t *>(ws + w.q);
+    uint16_t *k = reinterpret_cast<uint16_t *>(ws + w.k);
+    uint16_t *v = reinterpret_cast<uint16_t *>(ws + w.v);
+    float *beta = reinterpret_cast<float *>(ws + w.beta);
+    float *alpha = reinterpret_cast<float *>(ws + w.alpha);
+    uint16_t *o = reinterpret_cast<uint16_t *>(ws + w.o);
+
+    hipError_t e = launch_cast_residual(a.h_in, a.h_out, xb, (size_t)M * a.D, s);
+    if (e != hipSuccess) return e;
+    GdnArgs g{};
+    g.B = a.B; g.L = a.L; g.H = a.H; g.dk = a.d; g.dv = a.d; g.chunk = a.chunk;
+    g.qkv_bf16 = 1; g.out_bf16 = 1; g.channel = 0;
+    g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta;
+    g.state_in = nullptr; g.out = o; g.state_out = nullptr; g.ws = ws + w.prefill;
+    for (int t = 0; t < a.T; ++t) {
+        e = launch_gemm_proj(xb, a.W_in, M, N_in, a.D, q, k, v, beta, alpha, a.H, a.d, s);
+        if (e != hipSuccess) return e;
+        e = launch_prefill_head(g, PHASE_ALL, s);
+        if (e != hipSuccess) return e;
+        e = launch_gemm_resid(o, a.W_o, M, a.D, Hd, a.h_out, xb, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace lt2

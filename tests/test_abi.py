@@ -106,3 +106,34 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(lt2, "LIB_PATH", "/nonexistent/liblt2.so")
     with pytest.raises(RuntimeError):
         lt2.lib()
+
+
+def loop_call(desc, h_in=FAKE, h_out=FAKE, w_in=FAKE, w_o=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    P = ctypes.c_void_p
+    return lt2.lib().lt2_looped_mixer(ctypes.byref(desc), P(h_in), P(h_out), P(w_in), P(w_o), P(ws), ws_bytes, None)
+
+
+def good_loop(**kw):
+    d = dict(B=2, L=100, d_model=256, H=2, d_head=128, T=2, chunk=64)
+    d.update(kw)
+    return lt2.lt2_loop_desc(*[d[n] for n, _ in lt2.lt2_loop_desc._fields_])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), 2), (dict(T=-1), 2), (dict(H=0), 2), (dict(d_head=96), 4), (dict(chunk=8), 4),
+    (dict(d_model=192), 4), (dict(H=1, d_head=64), 4),
+])
+def test_looped_rejects_bad_descriptor(kw, code):
+    assert loop_call(good_loop(**kw)) == code
+
+
+def test_looped_null_align_workspace():
+    d = good_loop()
+    assert lt2.lib().lt2_looped_mixer(None, None, None, None, None, None, 0, None) == 1
+    assert loop_call(d, w_o=None) == 1
+    assert loop_call(d, h_in=FAKE + 4) == 6
+    need = lt2.lt2_looped_mixer_workspace_size(d)
+    assert need > 0
+    assert loop_call(d, ws_bytes=need - 1) == 5
+    assert loop_call(d, ws=FAKE + 16, ws_bytes=need) == 6
+    assert loop_call(good_loop(L=0), h_in=None, h_out=None, w_in=None, w_o=None, ws=None, ws_bytes=0) == 0
