@@ -99,7 +99,6 @@ lt2_status prefill_call(int phase, const lt2_gdn_desc *desc, const void *q, cons
         const size_t n = (size_t)desc->B * desc->H * desc->d_k * desc->d_v;
         return hip_status(launch_state_init(state_out, state_in, n, s));
     }
-    if (desc->gate == LT2_GATE_CHANNEL) return LT2_ERR_UNSUPPORTED;
     GdnArgs a = make_args(desc, q, k, v, alpha, beta, state_in, out, state_out, ws);
     return hip_status(a.channel ? launch_prefill_channel(a, phase, s) : launch_prefill_head(a, phase, s));
 }

@@ -225,3 +225,91 @@ def test_decode_full_size_sampled():
                                       S0[t, b, h][None, None])
         assert rel_err(outs[:, t, b, h], o_ref[0, :, 0]) <= TOL_F32, (b, h, t)
         assert rel_err(S_fin[t, b, h], S_ref[0, 0]) <= TOL_F32, (b, h, t)
+
+
+# ---- per-channel gate (KDA form) ------------------------------------------------
+
+@pytest.mark.parametrize("chunk", [64, 32, 16])
+@pytest.mark.parametrize("shift", [0.0, 2.0])
+def test_channel_gate_fp32(chunk, shift):
+    shape = synth.GDNShape(2, 200, 3, 64, 64, "channel", shift, "f32")
+    announce(f"channel fp32 chunk={chunk} shift={shift}")
+    x = synth.gdn_inputs(shape, seed=30)
+    S0 = np.random.default_rng(30).standard_normal((2, 3, 64, 64)).astype(np.float32)
+    o, S = run_prefill(x, shape, chunk, S0=S0)
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(o, o_ref) <= TOL_F32
+    assert rel_err(S, S_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_channel_gate_bf16(out_dtype):
+    shape = synth.GDNShape(1, 333, 2, 128, 128, "channel", 2.0, "bf16")
+    announce(f"channel bf16 out={out_dtype}")
+    x = synth.gdn_inputs(shape, seed=31)
+    o, S = run_prefill(x, shape, 64, out_dtype=out_dtype)
+    o_ref, S_ref = oracle_prefill(x)
+    assert rel_err(o, o_ref) <= TOL_BF16
+    assert rel_err(S, S_ref) <= TOL_BF16
+
+
+def test_channel_gate_slow_decay_d128_fp32():
+    shape = synth.GDNShape(1, 300, 2, 128, 128, "channel", 0.0, "f32")
+    announce("channel fp32 d128 slow decay")
+    x = synth.gdn_inputs(shape, seed=32)
+    o, S = run_prefill(x, shape, 64)
+    o_ref, S_ref = oracle_prefill(x)
+    assert rel_err(o, o_ref) <= TOL_F32
+    assert rel_err(S, S_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("case", ["zero", "some_channels_near_zero", "one"])
+def test_channel_gate_extreme_decays_fp32(case):
+    """alpha = 0 everywhere, a few channels with alpha ~ 1e-20 (gate spans far past
+    the matrix-core reference range inside a block), and alpha = 1."""
+    shape = synth.GDNShape(1, 150, 2, 64, 64, "channel", 0.0, "f32")
+    announce(f"channel extreme {case}")
+    x = synth.gdn_inputs(shape, seed=33)
+    a = x["alpha"].copy()
+    if case == "zero":
+        a[:] = 0.0
+    elif case == "one":
+        a[:] = 1.0
+    else:
+        a[..., ::7] = 1e-20
+    x["alpha"] = a
+    S0 = np.random.default_rng(33).standard_normal((1, 2, 64, 64)).astype(np.float32)
+    o, S = run_prefill(x, shape, 64, S0=S0)
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(o, o_ref) <= TOL_F32
+    assert rel_err(S, S_ref) <= TOL_F32
+
+
+def test_channel_state_passing_bf16():
+    shape = synth.GDNShape(1, 256, 2, 128, 128, "channel", 2.0, "bf16")
+    announce("channel state passing")
+    x = synth.gdn_inputs(shape, seed=34)
+    o_full, S_full = run_prefill(x, shape, 64, out_dtype=torch.float32)
+    L1 = 100
+    xa = {kk: vv[:, :L1] for kk, vv in x.items()}
+    xb = {kk: vv[:, L1:] for kk, vv in x.items()}
+    oa, Sa = run_prefill(xa, synth.GDNShape(1, L1, 2, 128, 128, "channel", 2.0, "bf16"), 64, out_dtype=torch.float32)
+    ob, Sb = run_prefill(xb, synth.GDNShape(1, 256 - L1, 2, 128, 128, "channel", 2.0, "bf16"), 64,
+                         out_dtype=torch.float32, S0=Sa.astype(np.float32))
+    assert rel_err(np.concatenate([oa, ob], axis=1), o_full) <= TOL_BF16
+    assert rel_err(Sb, S_full) <= TOL_BF16
+
+
+def test_channel_full_size_bf16_sampled():
+    """B=1 H=32 L=32768 d=128 bf16, per-channel gate (the benchmarked launch):
+    sampled heads against the oracle."""
+    shape = synth.CONFIGS[4]["shape"]
+    announce("channel full size")
+    x = synth.gdn_inputs(shape, seed=0)
+    o, S = run_prefill(x, shape, 64)
+    for h in (0, 31):
+        u = synth.gdn_unit(shape, 0, 0, h)
+        o_ref, S_ref = oracle.prefill(u["q"][None, :, None], u["k"][None, :, None], u["v"][None, :, None],
+                                      u["alpha"][None, :, None], u["beta"][None, :, None])
+        assert rel_err(o[0, :, h], o_ref[0, :, 0]) <= TOL_BF16, h
+        assert rel_err(S[0, h], S_ref[0, 0]) <= TOL_BF16, h
