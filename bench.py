@@ -213,6 +213,63 @@ def bench_decode(args, torch, lt2, synth):
                 tokens_per_s_per_loop=B * steps * T / (span_ms / 1e3) / T)
 
 
+def channel_flops_bytes(B, L, H, d, C):
+    """Algorithmic work of the per-channel-gate prefill (whole path, per launch pair):
+    per head-token 2*[C*(5d + 4d) + 4*d*d + C*C/6] flops (the pages' ordering makes
+    each step rank 2); bytes: q, k, v, o bf16, alpha fp32 per channel, beta fp32,
+    the final state."""
+    ht = B * L * H
+    flops = 2.0 * ht * (C * 9 * d + 4.0 * d * d + C * C / 6.0)
+    path_bytes = ht * (4 * d * 2 + 4 * d + 4) + B * H * d * d * 4.0
+    return flops, path_bytes
+
+
+def bench_channel(args, torch, lt2, synth, reps=3):
+    """Per-channel-gate prefill, B=1 H=32 L=32768 d=128, bf16 q/k/v, chunk 64."""
+    cfg = synth.CONFIGS[4]
+    sh, C = cfg["shape"], cfg["chunk"]
+    log(f"channel inputs B={sh.B} L={sh.L} H={sh.H} d={sh.dk}")
+    x = synth.gdn_inputs(sh, seed=0)
+    t = dict(q=torch.from_numpy(x["q"]).to("cuda").to(torch.bfloat16),
+             k=torch.from_numpy(x["k"]).to("cuda").to(torch.bfloat16),
+             v=torch.from_numpy(x["v"]).to("cuda").to(torch.bfloat16),
+             alpha=torch.from_numpy(x["alpha"]).to("cuda"), beta=torch.from_numpy(x["beta"]).to("cuda"))
+    del x
+    out = torch.empty((sh.B, sh.L, sh.H, sh.dv), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((sh.B, sh.H, sh.dk, sh.dv), dtype=torch.float32, device="cuda")
+    desc = lt2.gdn_desc(sh.B, sh.L, sh.H, sh.dk, sh.dv, C, lt2.LT2_BF16, lt2.LT2_BF16, lt2.LT2_GATE_CHANNEL)
+    ws_bytes = lt2.lt2_gdn_prefill_workspace_size(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    L_ = lt2.lib()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda a: ctypes.c_void_p(a.data_ptr())
+    prep = (ctypes.byref(desc), P(t["q"]), P(t["k"]), P(t["alpha"]), P(t["beta"]), P(ws), ws_bytes, sp)
+    scan = (ctypes.byref(desc), P(t["q"]), P(t["k"]), P(t["v"]), None, P(out), P(S), P(ws), ws_bytes, sp)
+    for _ in range(1):
+        L_.lt2_gdn_prefill_prepare(*prep)
+        L_.lt2_gdn_prefill_scan(*scan)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in evs:
+        e[0].record(stream)
+        if L_.lt2_gdn_prefill_prepare(*prep):
+            raise RuntimeError("channel prepare failed")
+        e[1].record(stream)
+        if L_.lt2_gdn_prefill_scan(*scan):
+            raise RuntimeError("channel scan failed")
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms = prep_ms + scan_ms
+    flops, pbytes = channel_flops_bytes(sh.B, sh.L, sh.H, sh.dk, C)
+    log(f"channel {ms:.3f} ms (prepare {prep_ms:.3f}, scan {scan_ms:.3f})")
+    return dict(B=sh.B, L=sh.L, H=sh.H, d=sh.dk, C=C, ms=ms, prepare_ms=prep_ms, scan_ms=scan_ms,
+                tokens_per_s_per_loop=sh.B * sh.L / (ms / 1e3), path_flops=flops, path_bytes=pbytes,
+                tflops=flops / ms / 1e9, gbs=pbytes / ms / 1e6, ws_bytes=ws_bytes)
+
+
 def bench_looped(args, torch, lt2, synth, reps=5):
     """T=4 loops of the LT2-linear block, B=2 L=8192 d_model=2048 H=16 d=128."""
     cfg = synth.CONFIGS[3]
@@ -290,6 +347,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-looped", action="store_true")
+    ap.add_argument("--no-channel", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -309,6 +367,7 @@ def main():
     log(f"copy probe {copy['gbs']:.0f} GB/s")
     dec = None if args.no_decode else bench_decode(args, torch, lt2, synth)
     loo = None if args.no_looped else bench_looped(args, torch, lt2, synth)
+    cha = None if args.no_channel else bench_channel(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
     value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
@@ -330,6 +389,8 @@ def main():
                                hbm_frac_span=dec["gbs_span"] / HBM_PEAK_GBS)
     if loo:
         extra["looped"] = loo
+    if cha:
+        extra["channel_prefill"] = cha
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",

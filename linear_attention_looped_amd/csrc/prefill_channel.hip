@@ -30,9 +30,10 @@ namespace {
 
 constexpr float DIAG_SPAN_MAX = 240.f;   // log2 span allowed for the midpoint reference
 
-// Workspace floats per chunk: Te, Nv, Pe, Pv [C][C] and G [C][DK].
+// Workspace floats per chunk: Te, Nv, Pe, Pv [C][C], G [C][DK] and beta [C]
+// (the scan phase takes its beta from here, not from the caller).
 template <int DK, int C>
-constexpr size_t chunk_floats() { return (size_t)4 * C * C + (size_t)C * DK; }
+constexpr size_t chunk_floats() { return (size_t)4 * C * C + (size_t)C * DK + C; }
 
 }  // namespace
 
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(256) void prep_channel_kernel(const TI *__restrict_
     const int Lc = min(C, L - t0);
     float *wsu = ws + ((size_t)unit * NC + n) * chunk_floats<DK, C>();
     float *Tg = wsu, *Ng = wsu + C * C, *Peg = wsu + 2 * C * C, *Pvg = wsu + 3 * C * C, *Gg = wsu + 4 * C * C;
+    float *Bg = Gg + C * DK;
     const size_t tok0 = (size_t)b * L * H + h;   // token index of (b, t = 0, h) is tok0 + t*H
 
     // ---- per-channel prefix sums of log2(alpha) ----
@@ -87,6 +89,7 @@ __global__ __launch_bounds__(256) void prep_channel_kernel(const TI *__restrict_
     if (tid < C) {
         const float bt = beta[tok0 + (size_t)(t0 + min(tid, Lc - 1)) * H];
         bs[tid] = (tid < Lc) ? bt : 0.f;
+        Bg[tid] = (tid < Lc) ? bt : 0.f;
     }
     __syncthreads();
     {
@@ -277,8 +280,7 @@ __global__ __launch_bounds__(256) void prep_channel_kernel(const TI *__restrict_
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int BV, int C, int PREC, typename TI, typename TO>
 __global__ __launch_bounds__(256) void scan_channel_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
-                                                           const TI *__restrict__ v, const float *__restrict__ beta,
-                                                           const float *__restrict__ ws,
+                                                           const TI *__restrict__ v, const float *__restrict__ ws,
                                                            const float *__restrict__ state_in, TO *__restrict__ out,
                                                            float *__restrict__ state_out, int L, int H, int NC) {
     constexpr int KP = DK + 4;
@@ -332,13 +334,14 @@ __global__ __launch_bounds__(256) void scan_channel_kernel(const TI *__restrict_
         const float *wsu = ws + (unit * NC + n) * chunk_floats<DK, C>();
         const float *Tg = wsu, *Ng = wsu + C * C, *Peg = wsu + 2 * C * C, *Pvg = wsu + 3 * C * C;
         const float *Gg = wsu + 4 * C * C;
+        const float *Bg = Gg + C * DK;
         __syncthreads();
         // gate-scaled copies of K: K*2^gh (rows), (K*2^(gC-gh))^T, (b K*2^(gC-g))^T
         for (int idx = tid; idx < C * DK; idx += 256) {
             const int t = idx / DK, c = idx % DK;
             const int tc = min(t, Lc - 1);
             const float kv = (t < Lc) ? load1<TI>(k + (tok0 + (size_t)(t0 + tc) * H) * DK + c) : 0.f;
-            const float bt = (t < Lc) ? beta[tok0 + (size_t)(t0 + tc) * H] : 0.f;
+            const float bt = Bg[t];   // zero past the ragged end
             const float g = Gg[t * DK + c];
             const float gh = t > 0 ? Gg[(t - 1) * DK + c] : 0.f;
             const float gc = Gg[(Lc - 1) * DK + c];
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(256) void scan_channel_kernel(const TI *__restrict_
 
 size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C) {
     const size_t NC = (size_t)((L + C - 1) / C);
-    return (size_t)B * H * NC * ((size_t)4 * C * C + (size_t)C * dk) * sizeof(float);
+    return (size_t)B * H * NC * ((size_t)4 * C * C + (size_t)C * dk + C) * sizeof(float);
 }
 
 namespace {
@@ -519,7 +522,7 @@ hipError_t run_channel(const GdnArgs &a, int phase, hipStream_t s) {
     }
     if (phase & PHASE_SCAN) {
         hipLaunchKernelGGL((scan_channel_kernel<D, D, BV, C, PREC, TI, TO>), dim3(units * (D / BV)), dim3(256), 0, s,
-                           (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, a.beta, (const float *)a.ws,
+                           (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, (const float *)a.ws,
                            a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC);
         return hipGetLastError();
     }

@@ -313,3 +313,30 @@ def test_channel_full_size_bf16_sampled():
                                       u["alpha"][None, :, None], u["beta"][None, :, None])
         assert rel_err(o[0, :, h], o_ref[0, :, 0]) <= TOL_BF16, h
         assert rel_err(S[0, h], S_ref[0, 0]) <= TOL_BF16, h
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_prepare_then_scan_equals_prefill(gate):
+    """lt2_gdn_prefill_prepare followed by lt2_gdn_prefill_scan (which receives no
+    alpha or beta) gives exactly what lt2_gdn_prefill gives."""
+    import ctypes
+    shape = synth.GDNShape(2, 150, 2, 128, 128, gate, 2.0, "bf16")
+    announce(f"phases {gate}")
+    x = synth.gdn_inputs(shape, seed=40)
+    q, k, v = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    a, b = dev(x["alpha"]), dev(x["beta"])
+    o_ref, S_ref = lt2.lt2_gdn_prefill(q, k, v, a, b, chunk=64, out_dtype=torch.float32)
+    desc = lt2.gdn_desc(2, 150, 2, 128, 128, 64, lt2.LT2_BF16, lt2.LT2_F32,
+                        lt2.LT2_GATE_CHANNEL if gate == "channel" else lt2.LT2_GATE_HEAD)
+    nbytes = lt2.lt2_gdn_prefill_workspace_size(desc)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(o_ref)
+    S = torch.empty_like(S_ref)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    L_ = lt2.lib()
+    assert L_.lt2_gdn_prefill_prepare(ctypes.byref(desc), P(q), P(k), P(a), P(b), P(ws), nbytes, sp) == 0
+    assert L_.lt2_gdn_prefill_scan(ctypes.byref(desc), P(q), P(k), P(v), None, P(o), P(S), P(ws), nbytes, sp) == 0
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(o), host(o_ref))
+    np.testing.assert_array_equal(host(S), host(S_ref))
