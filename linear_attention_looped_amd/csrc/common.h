@@ -22,6 +22,7 @@ namespace lt2 {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 enum Prec { PREC_F32 = 0, PREC_BF16 = 1 };
 

@@ -23,9 +23,9 @@ namespace lt2 {
 
 // ---------------------------------------------------------------------------
 // Prepare: per chunk, Tm = (I + A)^{-1} diag(beta), P and the gate prefix g
-// (base 2).  Workspace per (b, h, chunk), (2*C*C + C) * 4 bytes:
-//   fp32 inputs: Tm [C][C] f32 | P [C][C] f32 | g [C] f32
-//   bf16 inputs: Tm hi, Tm lo, P hi, P lo [C][C] bf16 each | g [C] f32
+// (base 2).  Workspace per (b, h, chunk), 8*C*C + 12*C bytes:
+//   fp32 inputs: Tm [C][C] f32 | P [C][C] f32 | g, 2^g, 2^(g_C - g) [C] f32
+//   bf16 inputs: Tm hi, Tm lo, P hi, P lo [C][C] bf16 | g, 2^g, 2^(g_C - g) [C] f32
 // (hi = bf16(x), lo = bf16(x - hi): the scan feeds them to bf16 matrix cores
 // without converting).  Tm and P are zero above the diagonal.
 // ---------------------------------------------------------------------------
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     const int lr = lane & 15, lq = lane >> 4;
     const int t0 = n * C;
     const int Lc = min(C, L - t0);
-    unsigned char *wsu = ws + ((size_t)unit * NC + n) * (size_t)(8 * C * C + 4 * C);
+    unsigned char *wsu = ws + ((size_t)unit * NC + n) * (size_t)(8 * C * C + 12 * C);
     float *gg = reinterpret_cast<float *>(wsu + 8 * C * C);
 
     for (int idx = tid; idx < C * (DK / 8); idx += 256) {
@@ -222,7 +222,11 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
             *reinterpret_cast<uint4 *>(Th + 3 * C * C + t * C + i0) = lo;
         }
     }
-    if (tid < C) gg[tid] = gs[tid];
+    if (tid < C) {
+        gg[tid] = gs[tid];
+        gg[C + tid] = exp2_fast(gs[tid]);
+        gg[2 * C + tid] = exp2_fast(gs[C - 1] - gs[tid]);   // rows past the ragged end keep g constant
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb)
             load_raw8<TI>(p.qf[kb], q + (base_tok + (size_t)(t0 + trow_c) * tok_stride) * DK + 32 * kb + 8 * lq);
-        const float *wsu = ws + (unit * NC + n) * (size_t)(2 * C * C + C);
+        const float *wsu = ws + (unit * NC + n) * (size_t)(2 * C * C + 3 * C);
 #pragma unroll
         for (int kb = 0; kb < NKB_C; ++kb) {
             const int kcc = min(32 * kb + 8 * lq, C - 8);
@@ -540,23 +544,36 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
 
 // ---------------------------------------------------------------------------
 // Scan, bf16 inputs: 8 waves (two per SIMD) per (b, h, BV-column block).
-// Every LDS operand is stored as bf16 by the one wave that produces it: K raw
-// (row-major for K S, transposed for K^T U2), and the fp32 intermediates S, R,
-// U, U2 as hi/lo pairs, so the matrix cores read them without conversion.
-// fp32 x fp32 products take hi*hi + lo*hi + hi*lo; bf16-exact inputs (q, k)
-// take one or two products.  The next chunk's inputs are in flight in
-// registers while the current chunk computes.
+//  * Every LDS operand is stored as bf16 by the one wave that produces it: K
+//    raw, and the fp32 intermediates S^T, R^T, U^T, U2^T as hi/lo pairs, so the
+//    matrix cores read them without conversion.  K^T fragments for the state
+//    update come straight from the row-major K tile through LDS transpose reads
+//    (ds_read_b64_tr_b16): within each 16-lane group, lane 4e+m points at
+//    K[t0 + e][c0 + 4m] and lane 4m+s receives K[t0 + 0..3][c0 + 4m + s].
+//  * fp32 x fp32 products take hi*hi + lo*hi + hi*lo; q, k are bf16-exact.
+//  * The next chunk's K, Q, V, Tm, P and decay factors are fetched into
+//    registers while the current chunk computes; K is double-buffered in LDS,
+//    so a chunk needs three workgroup barriers.
 // ---------------------------------------------------------------------------
 template <int DK, int C>
-struct ScanPrefetchBf16 {
-    static constexpr int NKB_C = (C + 31) / 32;
-    static constexpr int KL = (C * (DK / 8) + 511) / 512;
-    uint4 k[KL];                                  // K rows (8 bf16 each)
-    uint4 q[DK / 32];                             // Q fragments of the wave's row tile
-    uint4 th[NKB_C], tl[NKB_C], ph[NKB_C], pl[NKB_C];  // Tm, P fragments (hi/lo)
-    uint16_t v[4];                                // V entries of the wave's tile
-    float g;                                      // g[tid] (tid < C)
+struct ScanPrefetchBf16 {   // fetched one chunk ahead
+    static constexpr int KL = (C * (DK / 8) + 511) / 512;   // 1 or 2 (named: arrays would live in scratch)
+    static_assert(KL <= 2, "K tile rows per lane");
+    u32x4 k0, k1;           // K rows for the LDS tile (8 bf16 each)
+    uint4 ka[DK / 32];      // K fragments of the wave's row tile
+    uint4 q[DK / 32];       // Q fragments of the wave's row tile
+    uint16_t v[4];          // V entries of the wave's tile
 };
+template <int C>
+struct ScanFactorsBf16 {    // each group fetched right after its last use in the previous chunk
+    static constexpr int NKB_C = (C + 31) / 32;
+    uint4 th[NKB_C], tl[NKB_C], ph[NKB_C], pl[NKB_C];  // Tm, P fragments (hi/lo)
+    float eg[4], ew[4];                                // 2^g, 2^(gC - g) of the lane's rows
+    float ec;                                          // 2^gC
+};
+
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 template <int DK, int DV, int BV, int C, typename TO>
 __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__restrict__ q,
@@ -567,24 +584,23 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                                                              TO *__restrict__ out, float *__restrict__ state_out,
                                                              int L, int H, int NC) {
     using PF = ScanPrefetchBf16<DK, C>;
+    using FX = ScanFactorsBf16<C>;
     constexpr int NW = 8;
-    constexpr int KP = DK + 8;   // bf16 pitch of Ks and S^T rows (16-byte aligned, staggered banks)
-    constexpr int CP = C + 8;    // bf16 pitch of K^T, R^T, U^T, U2^T rows
+    constexpr int KP = DK + 8;   // bf16 pitch of K and S^T rows (16-byte aligned, staggered banks)
+    constexpr int CP = C + 8;    // bf16 pitch of R^T, U^T, U2^T rows
     constexpr int NTR = C / 16, NTV = BV / 16, NTK = DK / 16;
     constexpr int NT_O = NTR * NTV, NT_S = NTK * NTV;
     constexpr int MAXS = NT_S / NW;
     constexpr int NKB_C = (C + 31) / 32;
     constexpr int NV = DV / BV;
-    constexpr int WSB = 8 * C * C + 4 * C;   // workspace bytes per chunk
+    constexpr int WSB = 8 * C * C + 12 * C;   // workspace bytes per chunk
     static_assert(NT_O <= NW && NT_S % NW == 0 && NW % NTV == 0, "scan tiling");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t KsT[DK * CP];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C * KP];
     __shared__ __attribute__((aligned(16))) uint16_t Sth[BV * KP], Stl[BV * KP];
     __shared__ __attribute__((aligned(16))) uint16_t Rth[BV * CP], Rtl[BV * CP];
     __shared__ __attribute__((aligned(16))) uint16_t Uth[BV * CP], Utl[BV * CP];
     __shared__ __attribute__((aligned(16))) uint16_t U2h[BV * CP], U2l[BV * CP];
-    __shared__ float gs[C];
 
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int vb = logical % NV;
@@ -593,50 +609,96 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
     const int v0 = vb * BV;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
-    const bool has_o = wave < NT_O;
+    const bool has_o = NT_O == NW || wave < NT_O;
     const int ot = has_o ? wave : NT_O - 1;
     const int I = ot % NTR, J = ot / NTR;          // this wave's output tile
-    const int nkb = (16 * I + 16 + 31) / 32;       // K-blocks at or below the diagonal
     const int Js = wave % NTV;                     // column tile of this wave's state tiles
-    const size_t base_tok = (size_t)b * L * H + h; // tokens are [B, L, H, d]
+    const unsigned tok_stride = (unsigned)H * DK;  // elements between consecutive tokens (q, k)
+    const unsigned vtok_stride = (unsigned)H * DV;
+    const uint16_t *kb_ptr = k + ((size_t)b * L * H + h) * DK;   // token 0 of this unit
+    const uint16_t *qb_ptr = q + ((size_t)b * L * H + h) * DK;
+    const uint16_t *vb_ptr = v + ((size_t)b * L * H + h) * DV + v0;
+    // transpose-read lane roles: e = token offset, m = channel quad (see above)
+    const int tr_e = (lane & 15) >> 2, tr_m = lane & 3, tr_g = lane >> 4;
 
-    // Unconditional, unmasked loads with clamped rows; masking happens at use.
-    auto fetch = [&](int n, PF &p) {
+    // Per-lane token rows used by the fetches (fixed for the whole scan); the
+    // addresses are a uniform chunk base plus these 32-bit offsets.
+    const int kidx0 = min(tid, C * (DK / 8) - 1), kidx1 = min(tid + 512, C * (DK / 8) - 1);
+    const int krow0 = kidx0 / (DK / 8), kcol0 = 8 * (kidx0 % (DK / 8));   // 16 lanes cover one token row
+    const int krow1 = kidx1 / (DK / 8), kcol1 = 8 * (kidx1 % (DK / 8));
+    const int arow = 16 * I + lr;                  // A-fragment row of the wave's tile
+    const unsigned woff = (unsigned)(arow * C + 8 * lq);
+
+    // Unconditional, unmasked loads; only the last (ragged) chunk clamps rows to
+    // the last valid token.  Values of rows past the end never reach an output:
+    // beta is zero there, so Tm has zero rows and columns for them.
+    auto fetch = [&](int n, PF &p) __attribute__((always_inline)) {
         const int t0 = n * C;
-        const int Lc = min(C, L - t0);
+        const int last = min(C, L - t0) - 1;
+        const uint16_t *kc = kb_ptr + (size_t)t0 * tok_stride;
+        const uint16_t *qc = qb_ptr + (size_t)t0 * tok_stride;
+        const uint16_t *vc = vb_ptr + (size_t)t0 * vtok_stride;
+        p.k0 = *reinterpret_cast<const u32x4 *>(kc + (unsigned)min(krow0, last) * tok_stride + kcol0);
+        if constexpr (PF::KL > 1)
+            p.k1 = *reinterpret_cast<const u32x4 *>(kc + (unsigned)min(krow1, last) * tok_stride + kcol1);
+        const unsigned aoff = (unsigned)min(arow, last) * tok_stride + 8 * lq;
 #pragma unroll
-        for (int i = 0; i < PF::KL; ++i) {
-            const int idx = min(tid + 512 * i, C * (DK / 8) - 1);
-            const int t = idx % C, c8 = idx / C;   // a wave covers consecutive tokens
-            p.k[i] = *reinterpret_cast<const uint4 *>(k + (base_tok + (size_t)(t0 + min(t, Lc - 1)) * H) * DK + 8 * c8);
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            p.ka[kb] = *reinterpret_cast<const uint4 *>(kc + aoff + 32 * kb);
+            p.q[kb] = *reinterpret_cast<const uint4 *>(qc + aoff + 32 * kb);
         }
-        const int trow_c = min(16 * I + lr, Lc - 1);
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb)
-            p.q[kb] = *reinterpret_cast<const uint4 *>(q + (base_tok + (size_t)(t0 + trow_c) * H) * DK + 32 * kb + 8 * lq);
-        const unsigned char *wsu = ws + (unit * NC + n) * (size_t)WSB;
+        for (int r = 0; r < 4; ++r)
+            p.v[r] = vc[(unsigned)min(16 * I + 4 * lq + r, last) * vtok_stride + 16 * J + lr];
+    };
+    // Decay factors and Tm, P fragments of chunk n, in three groups ordered by
+    // first use; each group is fetched for chunk n + 1 as soon as chunk n has
+    // used it, so its latency hides behind the rest of chunk n.
+    auto ws_chunk = [&](int n) __attribute__((always_inline)) {
+        return ws + (unit * NC + (unsigned)n) * (size_t)WSB;
+    };
+    auto fetch_factors_a = [&](int n, FX &f) __attribute__((always_inline)) {   // 2^g, Tm, 2^(gC-g)
+        const unsigned char *wsu = ws_chunk(n);
         const uint16_t *wt = reinterpret_cast<const uint16_t *>(wsu);
+        const float *gf = reinterpret_cast<const float *>(wsu + 8 * C * C);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f.eg[r] = gf[C + 16 * I + 4 * lq + r];
 #pragma unroll
         for (int kb = 0; kb < NKB_C; ++kb) {
-            const int off = (16 * I + lr) * C + min(32 * kb + 8 * lq, C - 8);
-            p.th[kb] = *reinterpret_cast<const uint4 *>(wt + off);
-            p.tl[kb] = *reinterpret_cast<const uint4 *>(wt + C * C + off);
-            p.ph[kb] = *reinterpret_cast<const uint4 *>(wt + 2 * C * C + off);
-            p.pl[kb] = *reinterpret_cast<const uint4 *>(wt + 3 * C * C + off);
+            const unsigned off = woff + (unsigned)min(32 * kb, C - 8 - 8 * lq);
+            f.th[kb] = *reinterpret_cast<const uint4 *>(wt + off);
+            f.tl[kb] = *reinterpret_cast<const uint4 *>(wt + C * C + off);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * I + 4 * lq + r;
-            p.v[r] = v[(base_tok + (size_t)(t0 + min(t, Lc - 1)) * H) * DV + v0 + 16 * J + lr];
+        for (int r = 0; r < 4; ++r) f.ew[r] = gf[2 * C + 16 * I + 4 * lq + r];
+        asm volatile("" ::: "memory");   // keep the loads here, ahead of their uses
+    };
+    auto fetch_factors_b = [&](int n, FX &f) __attribute__((always_inline)) {   // P
+        const uint16_t *wt = reinterpret_cast<const uint16_t *>(ws_chunk(n));
+#pragma unroll
+        for (int kb = 0; kb < NKB_C; ++kb) {
+            const unsigned off = woff + (unsigned)min(32 * kb, C - 8 - 8 * lq);
+            f.ph[kb] = *reinterpret_cast<const uint4 *>(wt + 2 * C * C + off);
+            f.pl[kb] = *reinterpret_cast<const uint4 *>(wt + 3 * C * C + off);
         }
-        p.g = reinterpret_cast<const float *>(wsu + 8 * C * C)[min(tid, C - 1)];
+        asm volatile("" ::: "memory");
+    };
+    auto fetch_factors_c = [&](int n, FX &f) __attribute__((always_inline)) {   // 2^gC
+        f.ec = reinterpret_cast<const float *>(ws_chunk(n) + 8 * C * C)[C + C - 1];
+        asm volatile("" ::: "memory");
     };
 
-    auto store_split = [&](uint16_t *hi, uint16_t *lo, int off, const float x[4]) {
+    auto store_split = [&](uint16_t *hi, uint16_t *lo, int off, const float x[4]) __attribute__((always_inline)) {
         uint2 h2, l2;
         split4(x, h2, l2);
         *reinterpret_cast<uint2 *>(hi + off) = h2;
         *reinterpret_cast<uint2 *>(lo + off) = l2;
+    };
+    auto store_k = [&](const PF &p, int buf) __attribute__((always_inline)) {
+        if (tid < C * (DK / 8)) *reinterpret_cast<u32x4 *>(&Ks[buf][krow0 * KP + kcol0]) = p.k0;
+        if constexpr (PF::KL > 1) {
+            if (tid + 512 < C * (DK / 8)) *reinterpret_cast<u32x4 *>(&Ks[buf][krow1 * KP + kcol1]) = p.k1;
+        }
     };
 
     // initial state: registers (state tiles) and S^T (hi/lo) in LDS
@@ -654,41 +716,24 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
         store_split(Sth, Stl, (16 * Js + lr) * KP + 16 * Ik + 4 * lq, x);
     }
 
-    PF cur, nxt;
-    fetch(0, cur);
-    for (int n = 0; n < NC; ++n) {
+    // one chunk: `cur` holds its inputs, `nxt` receives the next chunk's
+    auto chunk = [&](int n, PF &cur, PF &nxt, FX &fx) __attribute__((always_inline)) {
         const int t0 = n * C;
         const int Lc = min(C, L - t0);
-        wait_vmem_all();   // this chunk's prefetch was issued one chunk ago
-        __syncthreads();   // the previous chunk is done with Ks, K^T, U^T, U2^T and gs
-#pragma unroll
-        for (int i = 0; i < PF::KL; ++i) {
-            const int idx = tid + 512 * i;
-            if (idx < C * (DK / 8)) {
-                const int t = idx % C, c8 = idx / C;
-                const uint4 r = (t < Lc) ? cur.k[i] : make_uint4(0u, 0u, 0u, 0u);
-                *reinterpret_cast<uint4 *>(Ks + t * KP + 8 * c8) = r;
-                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    KsT[(8 * c8 + 2 * e) * CP + t] = (uint16_t)(w[e] & 0xFFFFu);
-                    KsT[(8 * c8 + 2 * e + 1) * CP + t] = (uint16_t)(w[e] >> 16);
-                }
-            }
-        }
-        if (tid < C) gs[tid] = cur.g;
-        __syncthreads();
-        if (n + 1 < NC) fetch(n + 1, nxt);   // in flight during this chunk
+        const int buf = n & 1;
+        const int nn = min(n + 1, NC - 1);   // the last chunk re-fetches itself (unused)
+        __syncthreads();   // K[buf] and S^T complete; the previous chunk is done with R^T, U^T, U2^T
+        fetch(nn, nxt);    // in flight during this chunk
+        asm volatile("" ::: "memory");
 
-        // X_K = K S, X_Q = Q S;  R = V - e^g X_K  (hi/lo to LDS);  O = e^g X_Q
+        // X_K = K S, X_Q = Q S;  R = V - 2^g X_K (hi/lo to LDS);  O = 2^g X_Q
         f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
         if (has_o) {
             f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = xk;
-            const bool qrow = 16 * I + lr < Lc;
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
-                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(Ks + (16 * I + lr) * KP + 32 * kb + 8 * lq);
-                const bf16x8 aq = as_bf16x8(qrow ? cur.q[kb] : make_uint4(0u, 0u, 0u, 0u));
+                const bf16x8 ak = as_bf16x8(cur.ka[kb]);
+                const bf16x8 aq = as_bf16x8(cur.q[kb]);
                 const int so = (16 * J + lr) * KP + 32 * kb + 8 * lq;
                 const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(Sth + so);
                 const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(Stl + so);
@@ -700,27 +745,22 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
             float rr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * I + 4 * lq + r;
-                const float eg = exp2_fast(gs[t]);
-                const float vv = (t < Lc) ? bf16_to_f32(cur.v[r]) : 0.f;
-                rr[r] = vv - eg * xk[r];
-                oacc[r] = eg * xq[r];
+                rr[r] = bf16_to_f32(cur.v[r]) - fx.eg[r] * xk[r];
+                oacc[r] = fx.eg[r] * xq[r];
             }
             store_split(Rth, Rtl, (16 * J + lr) * CP + 16 * I + 4 * lq, rr);
         }
         __syncthreads();
 
-        // U = Tm R;  U^T and U2^T = (e^{g_C - g} U)^T as hi/lo
-        const float gC = gs[Lc - 1];
+        // U = Tm R;  U^T and U2^T = (2^(gC - g) U)^T as hi/lo
         if (has_o) {
             f32x4 ua = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKB_C; ++kb) {
-                if (kb >= nkb) continue;
+            for (int kb = 0; kb < NKB_C; ++kb) {   // blocks above the diagonal hold zeros
                 const int kc = 32 * kb + 8 * lq;
-                const bool kin = kc < C;
+                const bool kin = (C >= 32) || kc < C;
                 const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-                const bf16x8 th = as_bf16x8(kin ? cur.th[kb] : z), tl = as_bf16x8(kin ? cur.tl[kb] : z);
+                const bf16x8 th = as_bf16x8(kin ? fx.th[kb] : z), tl = as_bf16x8(kin ? fx.tl[kb] : z);
                 const int ro = (16 * J + lr) * CP + min(kc, C - 8);
                 const bf16x8 rh = *reinterpret_cast<const bf16x8 *>(Rth + ro);
                 const bf16x8 rl = *reinterpret_cast<const bf16x8 *>(Rtl + ro);
@@ -732,23 +772,23 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 u[r] = ua[r];
-                w2[r] = exp2_fast(gC - gs[16 * I + 4 * lq + r]) * ua[r];
+                w2[r] = fx.ew[r] * ua[r];
             }
             const int uo = (16 * J + lr) * CP + 16 * I + 4 * lq;
             store_split(Uth, Utl, uo, u);
             store_split(U2h, U2l, uo, w2);
         }
+        fetch_factors_a(nn, fx);
         __syncthreads();
 
         // O += P U, store
         if (has_o) {
 #pragma unroll
             for (int kb = 0; kb < NKB_C; ++kb) {
-                if (kb >= nkb) continue;
                 const int kc = 32 * kb + 8 * lq;
-                const bool kin = kc < C;
+                const bool kin = (C >= 32) || kc < C;
                 const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-                const bf16x8 ph = as_bf16x8(kin ? cur.ph[kb] : z), pl = as_bf16x8(kin ? cur.pl[kb] : z);
+                const bf16x8 ph = as_bf16x8(kin ? fx.ph[kb] : z), pl = as_bf16x8(kin ? fx.pl[kb] : z);
                 const int uo = (16 * J + lr) * CP + min(kc, C - 8);
                 const bf16x8 uh = *reinterpret_cast<const bf16x8 *>(Uth + uo);
                 const bf16x8 ul = *reinterpret_cast<const bf16x8 *>(Utl + uo);
@@ -756,32 +796,45 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                 oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, uh, oacc, 0, 0, 0);
                 oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ul, oacc, 0, 0, 0);
             }
+        }
+        fetch_factors_b(nn, fx);
+        if (has_o) {
+            TO *oc = out + ((size_t)b * L * H + h) * DV + (size_t)t0 * vtok_stride + v0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * I + 4 * lq + r;
-                if (t < Lc) store1<TO>(out + (base_tok + (size_t)(t0 + t) * H) * DV + v0 + 16 * J + lr, oacc[r]);
+                if (t < Lc) store1<TO>(oc + (unsigned)t * vtok_stride + 16 * J + lr, oacc[r]);
             }
         }
 
-        // S <- e^{g_C} S + K^T U2
-        const float eC = exp2_fast(gC);
+        // S <- 2^gC S + K^T U2  (K^T fragments by transpose reads of K[buf])
 #pragma unroll
         for (int m = 0; m < MAXS; ++m) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sacc[m][r] *= eC;
+            for (int r = 0; r < 4; ++r) Sacc[m][r] *= fx.ec;
         }
+        fetch_factors_c(nn, fx);
 #pragma unroll
         for (int kb = 0; kb < NKB_C; ++kb) {
             const int kc = 32 * kb + 8 * lq;
-            const bool kin = kc < C;
+            const bool kin = (C >= 32) || kc < C;
             const int kcc = min(kc, C - 8);
             const uint4 z = make_uint4(0u, 0u, 0u, 0u);
             const bf16x8 bh = as_bf16x8(kin ? *reinterpret_cast<const uint4 *>(U2h + (16 * Js + lr) * CP + kcc) : z);
             const bf16x8 bl = as_bf16x8(kin ? *reinterpret_cast<const uint4 *>(U2l + (16 * Js + lr) * CP + kcc) : z);
+            // tokens of this lane group's fragment: 32 kb + 8 g .. + 7 (clamped for C = 16)
+            const int tt = min(32 * kb + 8 * tr_g, C - 8);
 #pragma unroll
             for (int m = 0; m < MAXS; ++m) {
                 const int Ik = (wave + NW * m) / NTV;
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(KsT + (16 * Ik + lr) * CP + kcc);
+                const int col = 16 * Ik + 4 * tr_m;
+                const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4 *)(&Ks[buf][(tt + tr_e) * KP + col]));
+                const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4 *)(&Ks[buf][(tt + 4 + tr_e) * KP + col]));
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, (__attribute__((ext_vector_type(8))) short){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1],
+                                                                        hi4[2], hi4[3]});
                 Sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, Sacc[m], 0, 0, 0);
                 Sacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, Sacc[m], 0, 0, 0);
             }
@@ -792,8 +845,22 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
             const float x[4] = {Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]};
             store_split(Sth, Stl, (16 * Js + lr) * KP + 16 * Ik + 4 * lq, x);
         }
-        if (n + 1 < NC) cur = nxt;
+        store_k(nxt, buf ^ 1);   // K[buf ^ 1] was last read before this chunk's first barrier
+    };
+
+    PF pa, pb;
+    FX fx;
+    fetch(0, pa);
+    fetch_factors_a(0, fx);
+    fetch_factors_b(0, fx);
+    fetch_factors_c(0, fx);
+    store_k(pa, 0);
+    int n = 0;
+    for (; n + 1 < NC; n += 2) {
+        chunk(n, pa, pb, fx);
+        chunk(n + 1, pb, pa, fx);
     }
+    if (n < NC) chunk(n, pa, pb, fx);
 
     if (state_out) {
 #pragma unroll
@@ -808,7 +875,7 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
 
 size_t prefill_head_ws_bytes(int B, int L, int H, int C) {
     const size_t NC = (size_t)((L + C - 1) / C);
-    return (size_t)B * H * NC * (size_t)(2 * C * C + C) * sizeof(float);
+    return (size_t)B * H * NC * (size_t)(8 * C * C + 12 * C);
 }
 
 template <int D, int C, int PREC, typename TI, typename TO>
