@@ -544,34 +544,24 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
 
 // ---------------------------------------------------------------------------
 // Scan, bf16 inputs: 8 waves (two per SIMD) per (b, h, BV-column block).
-//  * Every LDS operand is stored as bf16 by the one wave that produces it: K
-//    raw, and the fp32 intermediates S^T, R^T, U^T, U2^T as hi/lo pairs, so the
-//    matrix cores read them without conversion.  K^T fragments for the state
-//    update come straight from the row-major K tile through LDS transpose reads
-//    (ds_read_b64_tr_b16): within each 16-lane group, lane 4e+m points at
-//    K[t0 + e][c0 + 4m] and lane 4m+s receives K[t0 + 0..3][c0 + 4m + s].
+//  * Every matrix-core operand is read from LDS as bf16: K, Q raw, and the fp32
+//    intermediates S^T, R^T, U^T, U2^T as hi/lo pairs written by the one wave
+//    that produces them.  K^T fragments for the state update come straight
+//    from the row-major K tile through LDS transpose reads (ds_read_b64_tr_b16):
+//    within each 16-lane group, lane 4e+m points at K[t0 + e][c0 + 4m] and lane
+//    4m+s receives K[t0 + 0..3][c0 + 4m + s].
 //  * fp32 x fp32 products take hi*hi + lo*hi + hi*lo; q, k are bf16-exact.
-//  * The next chunk's K, Q, V, Tm, P and decay factors are fetched into
-//    registers while the current chunk computes; K is double-buffered in LDS,
-//    so a chunk needs three workgroup barriers.
+//  * Staging: the next chunk's K, Q, V columns, Tm, P (hi/lo) and decay vectors
+//    are fetched while the current chunk computes, with coalesced 16-byte loads
+//    that fetch every byte once per block, and parked in registers.  K, Q, V and
+//    the decay vectors go to LDS at the end of the chunk (K double-buffered, as
+//    the state update still reads the current tile), Tm and P after the next
+//    chunk's first barrier, when the current ones have been read.
+//  * The output tile is staged in LDS and written with 16-byte stores after the
+//    next chunk's first barrier, behind that chunk's loads: vector-memory
+//    counters retire in issue order, so a store would otherwise hold up the
+//    wait for every load issued after it.
 // ---------------------------------------------------------------------------
-template <int DK, int C>
-struct ScanPrefetchBf16 {   // fetched one chunk ahead
-    static constexpr int KL = (C * (DK / 8) + 511) / 512;   // 1 or 2 (named: arrays would live in scratch)
-    static_assert(KL <= 2, "K tile rows per lane");
-    u32x4 k0, k1;           // K rows for the LDS tile (8 bf16 each)
-    uint4 ka[DK / 32];      // K fragments of the wave's row tile
-    uint4 q[DK / 32];       // Q fragments of the wave's row tile
-    uint16_t v[4];          // V entries of the wave's tile
-};
-template <int C>
-struct ScanFactorsBf16 {    // each group fetched right after its last use in the previous chunk
-    static constexpr int NKB_C = (C + 31) / 32;
-    uint4 th[NKB_C], tl[NKB_C], ph[NKB_C], pl[NKB_C];  // Tm, P fragments (hi/lo)
-    float eg[4], ew[4];                                // 2^g, 2^(gC - g) of the lane's rows
-    float ec;                                          // 2^gC
-};
-
 typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
@@ -583,31 +573,46 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                                                              const float *__restrict__ state_in,
                                                              TO *__restrict__ out, float *__restrict__ state_out,
                                                              int L, int H, int NC) {
-    using PF = ScanPrefetchBf16<DK, C>;
-    using FX = ScanFactorsBf16<C>;
-    constexpr int NW = 8;
-    constexpr int KP = DK + 8;   // bf16 pitch of K and S^T rows (16-byte aligned, staggered banks)
-    constexpr int CP = C + 8;    // bf16 pitch of R^T, U^T, U2^T rows
+    constexpr int NW = 8, NTH = 64 * NW;
+    constexpr int KP = DK + 8;   // bf16 pitch of K, Q and S^T rows (16-byte aligned, staggered banks)
+    constexpr int CP = C + 8;    // bf16 pitch of Tm, P, R^T, U^T, U2^T rows
+    constexpr int VP = BV + 8;   // bf16 pitch of V rows
+    constexpr int OV = 16 / (int)sizeof(TO);   // outputs per 16-byte store
+    constexpr int OP = BV + OV;                // pitch of the staged output rows
     constexpr int NTR = C / 16, NTV = BV / 16, NTK = DK / 16;
     constexpr int NT_O = NTR * NTV, NT_S = NTK * NTV;
     constexpr int MAXS = NT_S / NW;
     constexpr int NKB_C = (C + 31) / 32;
     constexpr int NV = DV / BV;
-    constexpr int WSB = 8 * C * C + 12 * C;   // workspace bytes per chunk
+    constexpr int WSB = 8 * C * C + 12 * C;    // workspace bytes per chunk
+    // 16-byte pieces per chunk: K (and Q), V columns, Tm/P hi/lo, decay vectors, outputs
+    constexpr int NK = C * DK / 8, KL = (NK + NTH - 1) / NTH;
+    constexpr int NVP = C * BV / 8;
+    constexpr int NF = C * C / 2, FL = (NF + NTH - 1) / NTH;
+    constexpr int NG = C / 2;
+    constexpr int NO = C * BV / OV;
     static_assert(NT_O <= NW && NT_S % NW == 0 && NW % NTV == 0, "scan tiling");
+    static_assert(KL <= 2 && FL <= 4 && NVP <= NTH && NO <= NTH && NG <= 64, "staging");
+    static_assert(NK % 64 == 0 && NVP % 64 == 0 && NF % 64 == 0 && NO % 64 == 0, "whole waves per piece set");
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[C * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[C * VP];
+    __shared__ __attribute__((aligned(16))) uint16_t Fs[4 * C * CP];   // Tm hi, Tm lo, P hi, P lo
+    __shared__ __attribute__((aligned(16))) float Gs[2 * C];           // 2^g, 2^(gC - g)
     __shared__ __attribute__((aligned(16))) uint16_t Sth[BV * KP], Stl[BV * KP];
     __shared__ __attribute__((aligned(16))) uint16_t Rth[BV * CP], Rtl[BV * CP];
     __shared__ __attribute__((aligned(16))) uint16_t Uth[BV * CP], Utl[BV * CP];
     __shared__ __attribute__((aligned(16))) uint16_t U2h[BV * CP], U2l[BV * CP];
+    __shared__ __attribute__((aligned(16))) TO Os[C * OP];
 
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int vb = logical % NV;
     const size_t unit = logical / NV;
     const int h = (int)(unit % H), b = (int)(unit / H);
     const int v0 = vb * BV;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;
     const bool has_o = NT_O == NW || wave < NT_O;
     const int ot = has_o ? wave : NT_O - 1;
@@ -618,87 +623,89 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
     const uint16_t *kb_ptr = k + ((size_t)b * L * H + h) * DK;   // token 0 of this unit
     const uint16_t *qb_ptr = q + ((size_t)b * L * H + h) * DK;
     const uint16_t *vb_ptr = v + ((size_t)b * L * H + h) * DV + v0;
+    TO *ob_ptr = out + ((size_t)b * L * H + h) * DV + v0;
     // transpose-read lane roles: e = token offset, m = channel quad (see above)
     const int tr_e = (lane & 15) >> 2, tr_m = lane & 3, tr_g = lane >> 4;
 
-    // Per-lane token rows used by the fetches (fixed for the whole scan); the
-    // addresses are a uniform chunk base plus these 32-bit offsets.
-    const int kidx0 = min(tid, C * (DK / 8) - 1), kidx1 = min(tid + 512, C * (DK / 8) - 1);
-    const int krow0 = kidx0 / (DK / 8), kcol0 = 8 * (kidx0 % (DK / 8));   // 16 lanes cover one token row
-    const int krow1 = kidx1 / (DK / 8), kcol1 = 8 * (kidx1 % (DK / 8));
-    const int arow = 16 * I + lr;                  // A-fragment row of the wave's tile
-    const unsigned woff = (unsigned)(arow * C + 8 * lq);
+    // Staging roles of this thread (fixed for the whole scan).
+    int krow[KL], kcol[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+        const int idx = min(tid + NTH * i, NK - 1);
+        krow[i] = idx / (DK / 8);
+        kcol[i] = 8 * (idx % (DK / 8));
+    }
+    const int vidx = min(tid, NVP - 1);
+    const int vrow = vidx / (BV / 8), vcol = 8 * (vidx % (BV / 8));
+    int fl[FL];   // LDS offsets of this thread's Tm/P pieces
+#pragma unroll
+    for (int i = 0; i < FL; ++i) {
+        const int idx = min(tid + NTH * i, NF - 1);
+        const int arr = idx / (C * C / 8), rem = idx % (C * C / 8);
+        fl[i] = arr * C * CP + (rem / (C / 8)) * CP + 8 * (rem % (C / 8));
+    }
+    const int gidx = min(lane, NG - 1);
+    const int orow = min(tid, NO - 1) / (BV / OV), ocol = OV * (min(tid, NO - 1) % (BV / OV));
 
-    // Unconditional, unmasked loads; only the last (ragged) chunk clamps rows to
-    // the last valid token.  Values of rows past the end never reach an output:
-    // beta is zero there, so Tm has zero rows and columns for them.
-    auto fetch = [&](int n, PF &p) __attribute__((always_inline)) {
+    u32x4 rk[KL], rq[KL], rv, rf[FL], rg;
+    // Loads of chunk n's inputs into the staging registers.  Rows past the end
+    // of a ragged last chunk repeat its last token: beta is zero there, so Tm
+    // has zero rows and columns for them and they never reach an output.
+    auto fetch = [&](int n) __attribute__((always_inline)) {
         const int t0 = n * C;
         const int last = min(C, L - t0) - 1;
         const uint16_t *kc = kb_ptr + (size_t)t0 * tok_stride;
         const uint16_t *qc = qb_ptr + (size_t)t0 * tok_stride;
         const uint16_t *vc = vb_ptr + (size_t)t0 * vtok_stride;
-        p.k0 = *reinterpret_cast<const u32x4 *>(kc + (unsigned)min(krow0, last) * tok_stride + kcol0);
-        if constexpr (PF::KL > 1)
-            p.k1 = *reinterpret_cast<const u32x4 *>(kc + (unsigned)min(krow1, last) * tok_stride + kcol1);
-        const unsigned aoff = (unsigned)min(arow, last) * tok_stride + 8 * lq;
+        const unsigned char *wsu = ws + (unit * NC + (unsigned)n) * (size_t)WSB;
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            p.ka[kb] = *reinterpret_cast<const uint4 *>(kc + aoff + 32 * kb);
-            p.q[kb] = *reinterpret_cast<const uint4 *>(qc + aoff + 32 * kb);
+        for (int i = 0; i < KL; ++i) {
+            if (NTH * (i + 1) <= NK || wave < (NK - NTH * i) / 64) {
+                const unsigned off = (unsigned)min(krow[i], last) * tok_stride + (unsigned)kcol[i];
+                rk[i] = *reinterpret_cast<const u32x4 *>(kc + off);
+                rq[i] = *reinterpret_cast<const u32x4 *>(qc + off);
+            }
         }
+        if (NVP == NTH || wave < NVP / 64)
+            rv = *reinterpret_cast<const u32x4 *>(vc + (unsigned)min(vrow, last) * vtok_stride + (unsigned)vcol);
+        if (wave == 0)
+            rg = *reinterpret_cast<const u32x4 *>(wsu + 8 * C * C + 4 * C + 16 * gidx);   // [2^g | 2^(gC-g)]
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            p.v[r] = vc[(unsigned)min(16 * I + 4 * lq + r, last) * vtok_stride + 16 * J + lr];
-    };
-    // Decay factors and Tm, P fragments of chunk n, in three groups ordered by
-    // first use; each group is fetched for chunk n + 1 as soon as chunk n has
-    // used it, so its latency hides behind the rest of chunk n.
-    auto ws_chunk = [&](int n) __attribute__((always_inline)) {
-        return ws + (unit * NC + (unsigned)n) * (size_t)WSB;
-    };
-    auto fetch_factors_a = [&](int n, FX &f) __attribute__((always_inline)) {   // 2^g, Tm, 2^(gC-g)
-        const unsigned char *wsu = ws_chunk(n);
-        const uint16_t *wt = reinterpret_cast<const uint16_t *>(wsu);
-        const float *gf = reinterpret_cast<const float *>(wsu + 8 * C * C);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) f.eg[r] = gf[C + 16 * I + 4 * lq + r];
-#pragma unroll
-        for (int kb = 0; kb < NKB_C; ++kb) {
-            const unsigned off = woff + (unsigned)min(32 * kb, C - 8 - 8 * lq);
-            f.th[kb] = *reinterpret_cast<const uint4 *>(wt + off);
-            f.tl[kb] = *reinterpret_cast<const uint4 *>(wt + C * C + off);
+        for (int i = 0; i < FL; ++i) {
+            if (NTH * (i + 1) <= NF || wave < (NF - NTH * i) / 64)
+                rf[i] = *reinterpret_cast<const u32x4 *>(wsu + 16 * (unsigned)(tid + NTH * i));
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) f.ew[r] = gf[2 * C + 16 * I + 4 * lq + r];
-        asm volatile("" ::: "memory");   // keep the loads here, ahead of their uses
     };
-    auto fetch_factors_b = [&](int n, FX &f) __attribute__((always_inline)) {   // P
-        const uint16_t *wt = reinterpret_cast<const uint16_t *>(ws_chunk(n));
+    auto stage_kqvg = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < NKB_C; ++kb) {
-            const unsigned off = woff + (unsigned)min(32 * kb, C - 8 - 8 * lq);
-            f.ph[kb] = *reinterpret_cast<const uint4 *>(wt + 2 * C * C + off);
-            f.pl[kb] = *reinterpret_cast<const uint4 *>(wt + 3 * C * C + off);
+        for (int i = 0; i < KL; ++i) {
+            if (NTH * (i + 1) <= NK || wave < (NK - NTH * i) / 64) {
+                *reinterpret_cast<u32x4 *>(&Ks[buf][krow[i] * KP + kcol[i]]) = rk[i];
+                *reinterpret_cast<u32x4 *>(&Qs[krow[i] * KP + kcol[i]]) = rq[i];
+            }
         }
-        asm volatile("" ::: "memory");
+        if (NVP == NTH || wave < NVP / 64) *reinterpret_cast<u32x4 *>(&Vs[vrow * VP + vcol]) = rv;
+        if (wave == 0) *reinterpret_cast<u32x4 *>(&Gs[4 * gidx]) = rg;
     };
-    auto fetch_factors_c = [&](int n, FX &f) __attribute__((always_inline)) {   // 2^gC
-        f.ec = reinterpret_cast<const float *>(ws_chunk(n) + 8 * C * C)[C + C - 1];
-        asm volatile("" ::: "memory");
+    auto stage_f = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < FL; ++i) {
+            if (NTH * (i + 1) <= NF || wave < (NF - NTH * i) / 64)
+                *reinterpret_cast<u32x4 *>(&Fs[fl[i]]) = rf[i];
+        }
     };
-
+    auto store_o = [&](int n, int rows) __attribute__((always_inline)) {   // staged outputs of chunk n
+        if ((NO == NTH || wave < NO / 64) && orow < rows) {
+            TO *oc = ob_ptr + (size_t)n * C * vtok_stride;
+            *reinterpret_cast<u32x4 *>(oc + (unsigned)orow * vtok_stride + (unsigned)ocol) =
+                *reinterpret_cast<const u32x4 *>(&Os[orow * OP + ocol]);
+        }
+    };
     auto store_split = [&](uint16_t *hi, uint16_t *lo, int off, const float x[4]) __attribute__((always_inline)) {
         uint2 h2, l2;
         split4(x, h2, l2);
         *reinterpret_cast<uint2 *>(hi + off) = h2;
         *reinterpret_cast<uint2 *>(lo + off) = l2;
-    };
-    auto store_k = [&](const PF &p, int buf) __attribute__((always_inline)) {
-        if (tid < C * (DK / 8)) *reinterpret_cast<u32x4 *>(&Ks[buf][krow0 * KP + kcol0]) = p.k0;
-        if constexpr (PF::KL > 1) {
-            if (tid + 512 < C * (DK / 8)) *reinterpret_cast<u32x4 *>(&Ks[buf][krow1 * KP + kcol1]) = p.k1;
-        }
     };
 
     // initial state: registers (state tiles) and S^T (hi/lo) in LDS
@@ -715,16 +722,15 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
         const float x[4] = {Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]};
         store_split(Sth, Stl, (16 * Js + lr) * KP + 16 * Ik + 4 * lq, x);
     }
+    fetch(0);
+    stage_kqvg(0);
 
-    // one chunk: `cur` holds its inputs, `nxt` receives the next chunk's
-    auto chunk = [&](int n, PF &cur, PF &nxt, FX &fx) __attribute__((always_inline)) {
-        const int t0 = n * C;
-        const int Lc = min(C, L - t0);
+    for (int n = 0; n < NC; ++n) {
         const int buf = n & 1;
-        const int nn = min(n + 1, NC - 1);   // the last chunk re-fetches itself (unused)
-        __syncthreads();   // K[buf] and S^T complete; the previous chunk is done with R^T, U^T, U2^T
-        fetch(nn, nxt);    // in flight during this chunk
-        asm volatile("" ::: "memory");
+        __syncthreads();   // chunk n's K, Q, V, decay vectors and S^T are in LDS; Tm, P and outputs of n - 1 are read
+        stage_f();                     // Tm, P of chunk n (first read after the next barrier)
+        fetch(min(n + 1, NC - 1));     // the last chunk re-fetches itself (unused)
+        if (n > 0) store_o(n - 1, C);  // only the last chunk can be ragged
 
         // X_K = K S, X_Q = Q S;  R = V - 2^g X_K (hi/lo to LDS);  O = 2^g X_Q
         f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
@@ -732,8 +738,9 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
             f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = xk;
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
-                const bf16x8 ak = as_bf16x8(cur.ka[kb]);
-                const bf16x8 aq = as_bf16x8(cur.q[kb]);
+                const int ao = (16 * I + lr) * KP + 32 * kb + 8 * lq;
+                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(&Ks[buf][ao]);
+                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(&Qs[ao]);
                 const int so = (16 * J + lr) * KP + 32 * kb + 8 * lq;
                 const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(Sth + so);
                 const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(Stl + so);
@@ -742,25 +749,29 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                 xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bl, xk, 0, 0, 0);
                 xq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bl, xq, 0, 0, 0);
             }
+            const f32x4 eg = *reinterpret_cast<const f32x4 *>(&Gs[16 * I + 4 * lq]);
             float rr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                rr[r] = bf16_to_f32(cur.v[r]) - fx.eg[r] * xk[r];
-                oacc[r] = fx.eg[r] * xq[r];
+                rr[r] = bf16_to_f32(Vs[(16 * I + 4 * lq + r) * VP + 16 * J + lr]) - eg[r] * xk[r];
+                oacc[r] = eg[r] * xq[r];
             }
             store_split(Rth, Rtl, (16 * J + lr) * CP + 16 * I + 4 * lq, rr);
         }
         __syncthreads();
 
         // U = Tm R;  U^T and U2^T = (2^(gC - g) U)^T as hi/lo
+        const float ec = Gs[C - 1];   // 2^gC, read before the decay vectors are restaged
         if (has_o) {
             f32x4 ua = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKB_C; ++kb) {   // blocks above the diagonal hold zeros
                 const int kc = 32 * kb + 8 * lq;
                 const bool kin = (C >= 32) || kc < C;
-                const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-                const bf16x8 th = as_bf16x8(kin ? fx.th[kb] : z), tl = as_bf16x8(kin ? fx.tl[kb] : z);
+                const bf16x8 z = {};
+                const int fo = (16 * I + lr) * CP + min(kc, C - 8);
+                const bf16x8 th = kin ? *reinterpret_cast<const bf16x8 *>(&Fs[fo]) : z;
+                const bf16x8 tl = kin ? *reinterpret_cast<const bf16x8 *>(&Fs[C * CP + fo]) : z;
                 const int ro = (16 * J + lr) * CP + min(kc, C - 8);
                 const bf16x8 rh = *reinterpret_cast<const bf16x8 *>(Rth + ro);
                 const bf16x8 rl = *reinterpret_cast<const bf16x8 *>(Rtl + ro);
@@ -768,27 +779,29 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                 ua = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh, ua, 0, 0, 0);
                 ua = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl, ua, 0, 0, 0);
             }
+            const f32x4 ew = *reinterpret_cast<const f32x4 *>(&Gs[C + 16 * I + 4 * lq]);
             float u[4], w2[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 u[r] = ua[r];
-                w2[r] = fx.ew[r] * ua[r];
+                w2[r] = ew[r] * ua[r];
             }
             const int uo = (16 * J + lr) * CP + 16 * I + 4 * lq;
             store_split(Uth, Utl, uo, u);
             store_split(U2h, U2l, uo, w2);
         }
-        fetch_factors_a(nn, fx);
         __syncthreads();
 
-        // O += P U, store
+        // O += P U, staged in LDS
         if (has_o) {
 #pragma unroll
             for (int kb = 0; kb < NKB_C; ++kb) {
                 const int kc = 32 * kb + 8 * lq;
                 const bool kin = (C >= 32) || kc < C;
-                const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-                const bf16x8 ph = as_bf16x8(kin ? fx.ph[kb] : z), pl = as_bf16x8(kin ? fx.pl[kb] : z);
+                const bf16x8 z = {};
+                const int fo = (16 * I + lr) * CP + min(kc, C - 8);
+                const bf16x8 ph = kin ? *reinterpret_cast<const bf16x8 *>(&Fs[2 * C * CP + fo]) : z;
+                const bf16x8 pl = kin ? *reinterpret_cast<const bf16x8 *>(&Fs[3 * C * CP + fo]) : z;
                 const int uo = (16 * J + lr) * CP + min(kc, C - 8);
                 const bf16x8 uh = *reinterpret_cast<const bf16x8 *>(Uth + uo);
                 const bf16x8 ul = *reinterpret_cast<const bf16x8 *>(Utl + uo);
@@ -796,32 +809,24 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                 oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, uh, oacc, 0, 0, 0);
                 oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ul, oacc, 0, 0, 0);
             }
-        }
-        fetch_factors_b(nn, fx);
-        if (has_o) {
-            TO *oc = out + ((size_t)b * L * H + h) * DV + (size_t)t0 * vtok_stride + v0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * I + 4 * lq + r;
-                if (t < Lc) store1<TO>(oc + (unsigned)t * vtok_stride + 16 * J + lr, oacc[r]);
-            }
+            for (int r = 0; r < 4; ++r) store1<TO>(&Os[(16 * I + 4 * lq + r) * OP + 16 * J + lr], oacc[r]);
         }
 
         // S <- 2^gC S + K^T U2  (K^T fragments by transpose reads of K[buf])
 #pragma unroll
         for (int m = 0; m < MAXS; ++m) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sacc[m][r] *= fx.ec;
+            for (int r = 0; r < 4; ++r) Sacc[m][r] *= ec;
         }
-        fetch_factors_c(nn, fx);
 #pragma unroll
         for (int kb = 0; kb < NKB_C; ++kb) {
             const int kc = 32 * kb + 8 * lq;
             const bool kin = (C >= 32) || kc < C;
             const int kcc = min(kc, C - 8);
-            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-            const bf16x8 bh = as_bf16x8(kin ? *reinterpret_cast<const uint4 *>(U2h + (16 * Js + lr) * CP + kcc) : z);
-            const bf16x8 bl = as_bf16x8(kin ? *reinterpret_cast<const uint4 *>(U2l + (16 * Js + lr) * CP + kcc) : z);
+            const bf16x8 z = {};
+            const bf16x8 bh = kin ? *reinterpret_cast<const bf16x8 *>(U2h + (16 * Js + lr) * CP + kcc) : z;
+            const bf16x8 bl = kin ? *reinterpret_cast<const bf16x8 *>(U2l + (16 * Js + lr) * CP + kcc) : z;
             // tokens of this lane group's fragment: 32 kb + 8 g .. + 7 (clamped for C = 16)
             const int tt = min(32 * kb + 8 * tr_g, C - 8);
 #pragma unroll
@@ -845,22 +850,10 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
             const float x[4] = {Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]};
             store_split(Sth, Stl, (16 * Js + lr) * KP + 16 * Ik + 4 * lq, x);
         }
-        store_k(nxt, buf ^ 1);   // K[buf ^ 1] was last read before this chunk's first barrier
-    };
-
-    PF pa, pb;
-    FX fx;
-    fetch(0, pa);
-    fetch_factors_a(0, fx);
-    fetch_factors_b(0, fx);
-    fetch_factors_c(0, fx);
-    store_k(pa, 0);
-    int n = 0;
-    for (; n + 1 < NC; n += 2) {
-        chunk(n, pa, pb, fx);
-        chunk(n + 1, pb, pa, fx);
+        stage_kqvg(buf ^ 1);   // chunk n + 1's inputs; their current copies were last read before the second barrier
     }
-    if (n < NC) chunk(n, pa, pb, fx);
+    __syncthreads();
+    store_o(NC - 1, L - (NC - 1) * C);
 
     if (state_out) {
 #pragma unroll
