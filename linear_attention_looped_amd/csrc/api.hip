@@ -42,7 +42,8 @@ GdnArgs make_args(const lt2_gdn_desc *d, const void *q, const void *k, const voi
 }
 
 size_t prefill_ws(const lt2_gdn_desc *d) {
-    if (d->gate == LT2_GATE_CHANNEL) return prefill_channel_ws_bytes(d->B, d->L, d->H, d->d_k, d->chunk);
+    if (d->gate == LT2_GATE_CHANNEL)
+        return prefill_channel_ws_bytes(d->B, d->L, d->H, d->d_k, d->chunk, d->qkv_dtype == LT2_BF16);
     return prefill_head_ws_bytes(d->B, d->L, d->H, d->chunk);
 }
 

@@ -27,7 +27,7 @@ enum { PHASE_PREPARE = 1, PHASE_SCAN = 2, PHASE_ALL = 3 };
 hipError_t launch_decode(const GdnArgs &a, hipStream_t s);
 size_t prefill_head_ws_bytes(int B, int L, int H, int C);
 hipError_t launch_prefill_head(const GdnArgs &a, int phase, hipStream_t s);
-size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C);
+size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C, bool bf16);
 hipError_t launch_prefill_channel(const GdnArgs &a, int phase, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 

@@ -502,8 +502,622 @@ __global__ __launch_bounds__(256) void scan_channel_kernel(const TI *__restrict_
     }
 }
 
-size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C) {
+// ---------------------------------------------------------------------------
+// bf16 inputs: transition form of a chunk.
+// Substituting E into the output and state updates above gives, for the state
+// S entering a chunk,
+//   O  = Qt S + Pt V,   Qt = Q * 2^g - Pe Te (K * 2^gh),   Pt = Pv - Pe Nv
+//   S' = M S  + N V,    M  = diag(2^gC) - K1^T Te (K * 2^gh),  N = K2^T - K1^T Nv
+// with K1 = K * 2^(gC - gh), K2 = b K * 2^(gC - g) and Nv = Te Av diag(b).  With
+// Z = K1^T Te and PT = Pe Te the whole (DK + C) x (DK + CK) matrix is
+//   W = [[M, N], [Qt, Pt]] = [[diag(2^gC), K2^T], [Q * 2^g, Pv]] - [Z; PT] [K * 2^gh | Av diag(b)]
+// (CK = C rounded up to a whole K-block of 32, the extra columns zero).  The
+// prepare phase forms W per chunk; the scan then does one product per chunk,
+// [S'; O] = W [S; V], with no dependency chain inside the chunk.
+//
+// W is stored as MFMA A-fragments in bf16 hi/lo: 16-row tile R, K-block kb,
+// hi then lo, 64 lanes x 16 bytes.  Lane (r, q) (r = lane % 16, q = lane / 16)
+// holds W[16R + r][32kb + 4q + s] in slot s < 4 and W[16R + r][32kb + 16 + 4q + s - 4]
+// in slots 4..7: the column order of two accumulator tiles of W^T, which the
+// scan matches by reading its B operand in the same order.
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int DK, int C>
+struct TmShape {
+    static constexpr int CK = C < 32 ? 32 : C;       // token extent in whole K-blocks
+    static constexpr int NRR = (DK + C) / 16;        // 16-row tiles of W
+    static constexpr int NKW = (DK + CK) / 32;       // K-blocks of W
+    static constexpr size_t BYTES = (size_t)NRR * NKW * 2048;   // per chunk
+};
+
+}  // namespace
+
+template <int DK, int C>
+__global__ __launch_bounds__(512) void prep_channel_tm_kernel(const uint16_t *__restrict__ q,
+                                                              const uint16_t *__restrict__ k,
+                                                              const float *__restrict__ alpha,
+                                                              const float *__restrict__ beta,
+                                                              unsigned char *__restrict__ ws, int L, int H, int NC) {
+    using SH = TmShape<DK, C>;
+    constexpr int NTH = 512, NW = 8;
+    constexpr int GP = DK + 4;    // fp32 pitch of G rows
+    constexpr int CP = C + 4;     // fp32 pitch of C-wide matrices
+    constexpr int KTP = C + 8;    // bf16 pitch of K^T rows
+    constexpr int NT = C / 16;
+    constexpr int NLT = NT * (NT + 1) / 2;
+    constexpr int PARTS = NTH / DK;
+    constexpr int SEG = C / PARTS;
+    constexpr int CK = SH::CK, NKW = SH::NKW, NRR = SH::NRR;
+    constexpr int NKT = CK / 32;                      // K-blocks over tokens
+    constexpr int ZR = DK > C ? DK : C;               // rows of the inverse / Z buffer
+    constexpr bool XS_IN_TZ = (DK - C) * CP >= 4 * 16 * 17;   // distance-loop scratch fits above the inverse
+    static_assert(NTH % DK == 0 && C % PARTS == 0 && SEG >= 1, "prefix layout");
+
+    __shared__ __attribute__((aligned(16))) float G[C * GP];          // g (base 2, chunk-relative)
+    __shared__ __attribute__((aligned(16))) uint16_t KT[DK * KTP];     // K^T, zero past the ragged end
+    __shared__ __attribute__((aligned(16))) float Am[C * CP];         // b-scaled Ae, then Te
+    __shared__ __attribute__((aligned(16))) float Avm[C * CP];        // Av diag(b)
+    __shared__ __attribute__((aligned(16))) float Pem[C * CP];        // Pe, then PT = Pe Te
+    __shared__ __attribute__((aligned(16))) float Pvm[C * CP];        // Pv (b-scaled columns)
+    __shared__ __attribute__((aligned(16))) float TZ[ZR * CP];        // inverse T, then Z = K1^T Te
+    __shared__ float Xs_own[XS_IN_TZ ? 1 : 4 * 16 * 17];
+    __shared__ float bs[C];
+    __shared__ float seg_tot[PARTS][DK];
+    float *Xs = XS_IN_TZ ? TZ + C * CP : Xs_own;
+
+    const int n = blockIdx.x % NC;
+    const int unit = blockIdx.x / NC;
+    const int h = unit % H, b = unit / H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int t0 = n * C;
+    const int Lc = min(C, L - t0);
+    const size_t tok0 = (size_t)b * L * H + h;   // token index of (b, t = 0, h) is tok0 + t*H
+    unsigned char *wsu = ws + ((size_t)unit * NC + n) * SH::BYTES;
+
+    // ---- K^T (bf16), beta, per-channel prefix sums of log2(alpha) ----
+    for (int idx = tid; idx < C * DK / 8; idx += NTH) {
+        const int t = idx / (DK / 8), c0 = 8 * (idx % (DK / 8));
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (t < Lc) u = *reinterpret_cast<const uint4 *>(k + (tok0 + (size_t)(t0 + t) * H) * DK + c0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            KT[(c0 + 2 * e) * KTP + t] = (uint16_t)(w[e] & 0xFFFFu);
+            KT[(c0 + 2 * e + 1) * KTP + t] = (uint16_t)(w[e] >> 16);
+        }
+    }
+    {
+        const int c = tid % DK, p = tid / DK;
+        float run = 0.f;
+        for (int s2 = 0; s2 < SEG; ++s2) {
+            const int t = p * SEG + s2;
+            const float a = alpha[(tok0 + (size_t)(t0 + min(t, Lc - 1)) * H) * DK + c];
+            run += (t < Lc) ? log2_gate(a) : 0.f;
+            G[t * GP + c] = run;
+        }
+        seg_tot[p][c] = run;
+    }
+    if (tid < C) {
+        const float bt = beta[tok0 + (size_t)(t0 + min(tid, Lc - 1)) * H];
+        bs[tid] = (tid < Lc) ? bt : 0.f;
+    }
+    __syncthreads();
+    {
+        const int c = tid % DK, p = tid / DK;
+        float off = 0.f;
+        for (int pp = 0; pp < p; ++pp) off += seg_tot[pp][c];
+        if (p > 0)
+            for (int s2 = 0; s2 < SEG; ++s2) G[(p * SEG + s2) * GP + c] += off;
+    }
+    __syncthreads();
+
+    // ---- pairwise gated sums, one 16x16 tile (I, J <= I) at a time per wave ----
+    auto ghat = [&](int t, int c) { return t > 0 ? G[(t - 1) * GP + c] : 0.f; };
+    for (int tt = wave; tt < NLT; tt += NW) {
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= tt) ++I;
+        const int J = tt - I * (I + 1) / 2;
+        const int trow = 16 * I + lr;
+        const int icol = 16 * J + lr;
+        const uint16_t *krow = k + (tok0 + (size_t)(t0 + min(trow, Lc - 1)) * H) * DK;
+        const uint16_t *qrow = q + (tok0 + (size_t)(t0 + min(trow, Lc - 1)) * H) * DK;
+        const uint16_t *kcol = k + (tok0 + (size_t)(t0 + min(icol, Lc - 1)) * H) * DK;
+        const bool trow_ok = trow < Lc, icol_ok = icol < Lc;
+        bool use_mfma = true;
+        if (I == J) {
+            bool ok = true;
+            for (int kb = 0; kb < DK / 32; ++kb)
+                for (int e = 0; e < 8; ++e) {
+                    const int c = 32 * kb + 8 * lq + e;
+                    ok = ok && (ghat(16 * I, c) - G[(16 * I + 15) * GP + c] <= DIAG_SPAN_MAX);
+                }
+            use_mfma = __all(ok);
+        }
+        f32x4 ae = {0.f, 0.f, 0.f, 0.f}, av = ae, pe = ae, pv = ae;
+        if (use_mfma) {
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                Frag rk, rq, ck1, ck2, fk, fq, fkc;
+                load_row8<uint16_t>(fk, krow + 32 * kb + 8 * lq);
+                load_row8<uint16_t>(fq, qrow + 32 * kb + 8 * lq);
+                load_row8<uint16_t>(fkc, kcol + 32 * kb + 8 * lq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = 32 * kb + 8 * lq + e;
+                    const float ref = (I == J) ? 0.5f * (ghat(16 * I, c) + G[(16 * I + 15) * GP + c])
+                                               : G[(16 * J + 15) * GP + c];
+                    rk.x[e] = trow_ok ? fk.x[e] * exp2_fast(ghat(trow, c) - ref) : 0.f;
+                    rq.x[e] = trow_ok ? fq.x[e] * exp2_fast(G[trow * GP + c] - ref) : 0.f;
+                    ck1.x[e] = icol_ok ? fkc.x[e] * exp2_fast(ref - ghat(icol, c)) : 0.f;
+                    ck2.x[e] = icol_ok ? fkc.x[e] * exp2_fast(ref - G[icol * GP + c]) : 0.f;
+                }
+                const auto ork = make_op<PREC_BF16, false>(rk), orq = make_op<PREC_BF16, false>(rq);
+                const auto oc1 = make_op<PREC_BF16, false>(ck1), oc2 = make_op<PREC_BF16, false>(ck2);
+                mma_op<PREC_BF16, false, false>(ae, ork, oc1);
+                mma_op<PREC_BF16, false, false>(av, ork, oc2);
+                mma_op<PREC_BF16, false, false>(pe, orq, oc1);
+                mma_op<PREC_BF16, false, false>(pv, orq, oc2);
+            }
+        } else {
+            // exact pairwise sums (diagonal block whose gate span is too large)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
+                if (i > t || t >= Lc) continue;
+                const uint16_t *kt = k + (tok0 + (size_t)(t0 + t) * H) * DK;
+                const uint16_t *qt = q + (tok0 + (size_t)(t0 + t) * H) * DK;
+                const uint16_t *ki = k + (tok0 + (size_t)(t0 + i) * H) * DK;
+                float s1 = 0.f, s2 = 0.f, s3 = 0.f, s4 = 0.f;
+                for (int c = 0; c < DK; ++c) {
+                    const float kk = bf16_to_f32(kt[c]) * bf16_to_f32(ki[c]);
+                    const float qk = bf16_to_f32(qt[c]) * bf16_to_f32(ki[c]);
+                    const float gt = G[t * GP + c], gi = G[i * GP + c];
+                    const float ght = ghat(t, c), ghi = ghat(i, c);
+                    if (i < t) {
+                        s1 += kk * exp2_fast(ght - ghi);
+                        s2 += kk * exp2_fast(ght - gi);
+                    }
+                    s3 += qk * exp2_fast(gt - ghi);
+                    s4 += qk * exp2_fast(gt - gi);
+                }
+                ae[r] = s1; av[r] = s2; pe[r] = s3; pv[r] = s4;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
+            Am[t * CP + i] = (i < t) ? bs[t] * ae[r] : 0.f;
+            Avm[t * CP + i] = (i < t) ? av[r] * bs[i] : 0.f;
+            Pem[t * CP + i] = (i <= t && t < Lc) ? pe[r] : 0.f;
+            Pvm[t * CP + i] = (i <= t && t < Lc) ? pv[r] * bs[i] : 0.f;
+        }
+    }
+    for (int tt = wave; tt < NT * NT; tt += NW) {   // upper tiles
+        const int I = tt / NT, J = tt % NT;
+        if (J <= I) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
+            Am[t * CP + i] = 0.f;
+            Avm[t * CP + i] = 0.f;
+            Pem[t * CP + i] = 0.f;
+            Pvm[t * CP + i] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- T = (I + Ae)^{-1}: diagonal blocks by forward substitution, then by distance ----
+    float *Ti = TZ;
+    if (wave < NT && lane < 16) {
+        const int base = 16 * wave;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float s2 = (t == lane) ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < t; ++j) s2 -= Am[(base + t) * CP + base + j] * x[j];
+            x[t] = s2;
+        }
+        for (int t = 0; t < C; ++t) Ti[t * CP + base + lane] = (t >= base && t < base + 16) ? x[t - base] : 0.f;
+    }
+    __syncthreads();
+    for (int dist = 1; dist < NT; ++dist) {
+        if (wave < NT - dist) {
+            const int J = wave, I = wave + dist;
+            float *X = Xs + wave * 16 * 17;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int Kb = J; Kb < I; ++Kb) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const float a = Am[(16 * I + lr) * CP + 16 * Kb + 4 * kk + lq];
+                    const float bb = Ti[(16 * Kb + 4 * kk + lq) * CP + 16 * J + lr];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X[(4 * lq + r) * 17 + lr] = acc[r];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const float a = Ti[(16 * I + lr) * CP + 16 * I + 4 * kk + lq];
+                const float bb = X[(4 * kk + lq) * 17 + lr];
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ti[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = -y[r];
+        }
+        __syncthreads();
+    }
+    // Te = T diag(b), into Am
+    for (int idx = tid; idx < C * C; idx += NTH) {
+        const int t = idx / C, i = idx % C;
+        Am[t * CP + i] = (i <= t) ? Ti[t * CP + i] * bs[i] : 0.f;
+    }
+    __syncthreads();
+
+    // Fragments over a token K-block kt: Te (B operand, rows = tokens) and the
+    // gate-scaled K^T rows (A operand).  Tokens past C (C < 32) are zero.
+    auto te_frag = [&](Frag &f, int kt, int col) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 32 * kt + 8 * lq + e;
+            f.x[e] = (i < C) ? Am[i * CP + col] : 0.f;
+        }
+    };
+
+    // ---- Z = K1^T Te (DK x C, into TZ) and PT = Pe Te (C x C, in place of Pe) ----
+    constexpr int ZT = (DK / 16) * NT;
+    for (int tt = wave; tt < ZT + NT; tt += NW) {
+        if (tt < ZT) {
+            const int Rz = tt / NT, Jz = tt % NT;
+            const int c = 16 * Rz + lr;
+            const float gc = G[(C - 1) * GP + c];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                Frag a, bfr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = 32 * kt + 8 * lq + e;
+                    a.x[e] = (i < C) ? bf16_to_f32(KT[c * KTP + i]) * exp2_fast(gc - ghat(i, c)) : 0.f;
+                }
+                te_frag(bfr, kt, 16 * Jz + lr);
+                mma<PREC_BF16, false, false>(acc, a, bfr);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) TZ[(16 * Rz + 4 * lq + r) * CP + 16 * Jz + lr] = acc[r];
+        } else {
+            const int I = tt - ZT;   // this wave alone reads and rewrites rows I of Pe
+            f32x4 acc[NT];
+#pragma unroll
+            for (int J = 0; J < NT; ++J) {
+                acc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) {
+                    Frag a, bfr;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int i = 32 * kt + 8 * lq + e;
+                        a.x[e] = (i < C) ? Pem[(16 * I + lr) * CP + i] : 0.f;
+                    }
+                    te_frag(bfr, kt, 16 * J + lr);
+                    mma<PREC_BF16, false, false>(acc[J], a, bfr);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int J = 0; J < NT; ++J) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Pem[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = acc[J][r];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- W^T tiles -> A-fragments of W, hi/lo ----
+    const uint16_t *qbase = q + (tok0 + (size_t)t0 * H) * DK;
+    for (int pr = wave; pr < NRR * NKW; pr += NW) {
+        const int R = pr / NKW, kb = pr % NKW;
+        const int r = 16 * R + lr;   // this lane's W row
+        float vals[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int T = 2 * kb + half;   // 16-column tile of W
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (16 * T < DK + C) {
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) {
+                    Frag a, bfr;
+                    const int w = 16 * T + lr;   // A row: a W column
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 32 * kt + 8 * lq + e;
+                        float x = 0.f;
+                        if (j < C) {
+                            if (w < DK) x = bf16_to_f32(KT[w * KTP + j]) * exp2_fast(ghat(j, w));
+                            else x = Avm[j * CP + (w - DK)];
+                        }
+                        a.x[e] = x;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 32 * kt + 8 * lq + e;
+                        float x = 0.f;
+                        if (j < C) x = (r < DK) ? TZ[r * CP + j] : Pem[(r - DK) * CP + j];
+                        bfr.x[e] = x;
+                    }
+                    mma<PREC_BF16, false, false>(acc, a, bfr);
+                }
+            }
+            // base - [Z; PT][K * 2^gh | Av diag(b)] at W[r][w], w = 16T + 4lq + e
+            float qv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (r >= DK && 16 * T < DK) {
+                const int t = r - DK;
+                if (t < Lc) {
+                    const uint2 u = *reinterpret_cast<const uint2 *>(qbase + (size_t)t * H * DK + 16 * T + 4 * lq);
+                    qv[0] = __uint_as_float(u.x << 16); qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
+                    qv[2] = __uint_as_float(u.y << 16); qv[3] = __uint_as_float(u.y & 0xFFFF0000u);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int w = 16 * T + 4 * lq + e;
+                float base = 0.f;
+                if (r < DK) {
+                    if (w < DK) {
+                        base = (w == r) ? exp2_fast(G[(C - 1) * GP + r]) : 0.f;
+                    } else if (w < DK + C) {
+                        const int i = w - DK;
+                        base = bs[i] * bf16_to_f32(KT[r * KTP + i]) * exp2_fast(G[(C - 1) * GP + r] - G[i * GP + r]);
+                    }
+                } else {
+                    const int t = r - DK;
+                    if (w < DK) base = qv[e] * exp2_fast(G[t * GP + w]);
+                    else if (w < DK + C) base = Pvm[t * CP + (w - DK)];
+                }
+                vals[4 * half + e] = base - acc[e];
+            }
+        }
+        uint4 hi, lo;
+        split8(vals, hi, lo);
+        unsigned char *dst = wsu + (size_t)(R * NKW + kb) * 2048 + 16 * lane;
+        *reinterpret_cast<uint4 *>(dst) = hi;
+        *reinterpret_cast<uint4 *>(dst + 1024) = lo;
+    }
+}
+
+// Scan in transition form for one (b, h, 16-column block of V), 8 waves:
+// [S'; O] = W [S; V] per chunk.  Wave w owns state rows 16w..16w+15 (w < DK/16)
+// and one half of the K-blocks of output row tile w % 4 (first half for
+// w < 4); the two halves are summed when the staged outputs are stored.
+// A-fragments of W go from the workspace straight into registers, one chunk
+// ahead, the same number of loads in every wave (a wave without a role loads a
+// valid tile and skips its products); S^T (hi/lo) and V^T are read from LDS in
+// the fragments' permuted column order.
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+template <int DK, int C>
+struct TmFrags {   // one chunk's A-fragments of this wave (hi, lo per K-block)
+    static constexpr int NKW = TmShape<DK, C>::NKW;
+    static constexpr int NKH = (NKW + 1) / 2;
+    u32x4 s[NKW][2];   // state rows: all K-blocks (S part, then V part)
+    u32x4 o[NKH][2];   // output rows: this wave's half of the K-blocks
+};
+
+template <int DK, int DV, int C, typename TO>
+__global__ __launch_bounds__(512) void scan_channel_tm_kernel(const uint16_t *__restrict__ v,
+                                                              const unsigned char *__restrict__ ws,
+                                                              const float *__restrict__ state_in,
+                                                              TO *__restrict__ out, float *__restrict__ state_out,
+                                                              int L, int H, int NC) {
+    using SH = TmShape<DK, C>;
+    using FR = TmFrags<DK, C>;
+    constexpr int NW = 8, BV = 16;
+    constexpr int CK = SH::CK, NKW = SH::NKW;
+    constexpr int NKS = DK / 32, NKV = CK / 32;
+    constexpr int SP = DK + 8;              // bf16 pitch of S^T rows
+    constexpr int VP = CK + 8;              // bf16 pitch of V^T rows
+    constexpr int OP = BV + 4;              // fp32 pitch of the output halves
+    constexpr int NTR = C / 16;
+    constexpr int OV = 16 / (int)sizeof(TO);
+    constexpr int NO = C * BV / OV;         // 16-byte output pieces per chunk
+    constexpr int NVP = C * BV / 8;         // 16-byte V pieces per chunk
+    constexpr int NV = DV / BV;
+    static_assert(NTR <= 4 && DK / 16 <= NW && NO <= 512 && NVP <= 512, "scan roles");
+
+    __shared__ __attribute__((aligned(16))) uint16_t Sth[2][BV * SP], Stl[2][BV * SP];
+    __shared__ __attribute__((aligned(16))) uint16_t VT[2][BV * VP];
+    __shared__ __attribute__((aligned(16))) float Oh[2][2][C * OP];
+
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    const int vb = logical % NV;
+    const size_t unit = logical / NV;
+    const int h = (int)(unit % H), b = (int)(unit / H);
+    const int v0 = vb * BV;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lq = lane >> 4;
+    constexpr int NKH = FR::NKH;
+    const bool has_s = DK / 16 == NW || wave < DK / 16;
+    const int oI = wave & 3, oh = wave >> 2;               // output row tile, K-block half
+    const bool has_o = NTR == 4 || oI < NTR;
+    const unsigned vtok_stride = (unsigned)H * DV;
+    const uint16_t *vb_ptr = v + ((size_t)b * L * H + h) * DV + v0;
+    TO *ob_ptr = out + ((size_t)b * L * H + h) * DV + v0;
+    const size_t lane_off = 16 * (size_t)lane;
+
+    auto frag_addr = [&](int n, int R, int kb) __attribute__((always_inline)) {
+        return ws + (unit * NC + (unsigned)n) * SH::BYTES + (size_t)(R * NKW + kb) * 2048 + lane_off;
+    };
+    const int Rs = min(wave, DK / 16 - 1);           // state row tile (valid for every wave)
+    const int Ro = DK / 16 + min(oI, NTR - 1);        // output row tile of W
+    auto fetch = [&](int n, FR &f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < NKW; ++kb) {
+            const unsigned char *p = frag_addr(n, Rs, kb);
+            f.s[kb][0] = *reinterpret_cast<const u32x4 *>(p);
+            f.s[kb][1] = *reinterpret_cast<const u32x4 *>(p + 1024);
+        }
+#pragma unroll
+        for (int j = 0; j < NKH; ++j) {
+            const unsigned char *p = frag_addr(n, Ro, min(oh * NKH + j, NKW - 1));
+            f.o[j][0] = *reinterpret_cast<const u32x4 *>(p);
+            f.o[j][1] = *reinterpret_cast<const u32x4 *>(p + 1024);
+        }
+    };
+    // V pieces: token row vrow, columns vcol..vcol+7 of this block
+    const int vidx = min(tid, NVP - 1);
+    const int vrow = vidx / (BV / 8), vcol = 8 * (vidx % (BV / 8));
+    auto fetch_v = [&](int n) __attribute__((always_inline)) {
+        u32x4 r = {0u, 0u, 0u, 0u};
+        const int last = min(C, L - n * C) - 1;
+        if (NVP % 64 == 0 ? wave < NVP / 64 : tid < NVP)
+            r = *reinterpret_cast<const u32x4 *>(vb_ptr + (size_t)n * C * vtok_stride +
+                                                 (unsigned)min(vrow, last) * vtok_stride + (unsigned)vcol);
+        return r;
+    };
+    auto stage_v = [&](const u32x4 &r, int buf) __attribute__((always_inline)) {
+        if (NVP % 64 == 0 ? wave < NVP / 64 : tid < NVP) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                VT[buf][(vcol + 2 * e) * VP + vrow] = (uint16_t)(r[e] & 0xFFFFu);
+                VT[buf][(vcol + 2 * e + 1) * VP + vrow] = (uint16_t)(r[e] >> 16);
+            }
+        }
+    };
+    // B fragments in the permuted column order: slots 0..3 = rows 32kb + 4lq + 0..3,
+    // slots 4..7 = rows 32kb + 16 + 4lq + 0..3 of S (resp. V)
+    auto bfrag = [&](const uint16_t *rowp, int kb) __attribute__((always_inline)) {
+        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(rowp + 32 * kb + 4 * lq);
+        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(rowp + 32 * kb + 16 + 4 * lq);
+        return __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+    };
+    auto store_o = [&](int n, int rows, int buf) __attribute__((always_inline)) {   // outputs of chunk n
+        const int oidx = min(tid, NO - 1);
+        const int orow = oidx / (BV / OV), ocol = OV * (oidx % (BV / OV));
+        if ((NO % 64 == 0 ? wave < NO / 64 : tid < NO) && orow < rows) {
+            float x[OV];
+#pragma unroll
+            for (int e = 0; e < OV; ++e) x[e] = Oh[buf][0][orow * OP + ocol + e] + Oh[buf][1][orow * OP + ocol + e];
+            TO *dst = ob_ptr + ((size_t)n * C + orow) * vtok_stride + ocol;
+            if constexpr (sizeof(TO) == 2) {
+                uint4 hi, lo;
+                split8(x, hi, lo);
+                *reinterpret_cast<uint4 *>(dst) = hi;
+            } else {
+                *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+            }
+        }
+    };
+
+    // initial state -> S^T[0]; chunk 0's fragments and V
+    f32x4 Sacc = {0.f, 0.f, 0.f, 0.f};
+    if (has_s) {
+        if (state_in) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[r] = state_in[(unit * DK + 16 * wave + 4 * lq + r) * DV + v0 + lr];
+        }
+        const float x[4] = {Sacc[0], Sacc[1], Sacc[2], Sacc[3]};
+        uint2 h2, l2;
+        split4(x, h2, l2);
+        *reinterpret_cast<uint2 *>(&Sth[0][lr * SP + 16 * wave + 4 * lq]) = h2;
+        *reinterpret_cast<uint2 *>(&Stl[0][lr * SP + 16 * wave + 4 * lq]) = l2;
+    }
+    if (CK > C) {   // V^T columns past the chunk stay zero
+        for (int idx = tid; idx < 2 * BV * VP; idx += 512) (&VT[0][0])[idx] = 0;
+        __syncthreads();
+    }
+    stage_v(fetch_v(0), 0);
+    FR pa, pb;
+    fetch(0, pa);
+
+    auto chunk = [&](int n, FR &cur, FR &nxt) __attribute__((always_inline)) {
+        const int buf = n & 1;
+        __syncthreads();   // S^T, V^T of chunk n and the outputs of chunk n - 1 are in LDS
+        const int nn = min(n + 1, NC - 1);   // the last chunk re-fetches itself (unused)
+        fetch(nn, nxt);
+        const u32x4 vn = fetch_v(nn);
+        if (n > 0) store_o(n - 1, C, buf ^ 1);
+
+        const uint16_t *sh = &Sth[buf][lr * SP], *sl = &Stl[buf][lr * SP], *vt = &VT[buf][lr * VP];
+        if (has_s) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKS; ++kb) {
+                const bf16x8 ah = __builtin_bit_cast(bf16x8, cur.s[kb][0]);
+                const bf16x8 al = __builtin_bit_cast(bf16x8, cur.s[kb][1]);
+                const bf16x8 bh = bfrag(sh, kb), bl = bfrag(sl, kb);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKV; ++kb) {
+                const bf16x8 ah = __builtin_bit_cast(bf16x8, cur.s[NKS + kb][0]);
+                const bf16x8 al = __builtin_bit_cast(bf16x8, cur.s[NKS + kb][1]);
+                const bf16x8 bv = bfrag(vt, kb);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc, 0, 0, 0);
+            }
+            Sacc = acc;
+        }
+        if (has_o) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NKH; ++j) {
+                const int kb = oh * NKH + j;   // wave-uniform
+                const bf16x8 ah = __builtin_bit_cast(bf16x8, cur.o[j][0]);
+                const bf16x8 al = __builtin_bit_cast(bf16x8, cur.o[j][1]);
+                if (kb < NKS) {
+                    const bf16x8 bh = bfrag(sh, kb), bl = bfrag(sl, kb);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+                } else if (kb < NKW) {
+                    const bf16x8 bv = bfrag(vt, kb - NKS);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Oh[buf][oh][(16 * oI + 4 * lq + r) * OP + lr] = acc[r];
+        }
+        if (has_s) {
+            const float x[4] = {Sacc[0], Sacc[1], Sacc[2], Sacc[3]};
+            uint2 h2, l2;
+            split4(x, h2, l2);
+            *reinterpret_cast<uint2 *>(&Sth[buf ^ 1][lr * SP + 16 * wave + 4 * lq]) = h2;
+            *reinterpret_cast<uint2 *>(&Stl[buf ^ 1][lr * SP + 16 * wave + 4 * lq]) = l2;
+        }
+        stage_v(vn, buf ^ 1);
+    };
+    int n = 0;
+    for (; n + 1 < NC; n += 2) {
+        chunk(n, pa, pb);
+        chunk(n + 1, pb, pa);
+    }
+    if (n < NC) chunk(n, pa, pb);
+    __syncthreads();
+    store_o(NC - 1, L - (NC - 1) * C, (NC - 1) & 1);
+
+    if (state_out && has_s) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) state_out[(unit * DK + 16 * wave + 4 * lq + r) * DV + v0 + lr] = Sacc[r];
+    }
+}
+
+size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C, bool bf16) {
     const size_t NC = (size_t)((L + C - 1) / C);
+    if (bf16) {
+        const size_t CK = C < 32 ? 32 : C;
+        return (size_t)B * H * NC * (size_t)(dk + C) * (dk + CK) * 4;
+    }
     return (size_t)B * H * NC * ((size_t)4 * C * C + (size_t)C * dk + C) * sizeof(float);
 }
 
@@ -515,15 +1129,25 @@ hipError_t run_channel(const GdnArgs &a, int phase, hipStream_t s) {
     const int NC = (a.L + C - 1) / C;
     const unsigned units = (unsigned)a.B * (unsigned)a.H;
     if (phase & PHASE_PREPARE) {
-        hipLaunchKernelGGL((prep_channel_kernel<D, C, PREC, TI>), dim3(units * NC), dim3(256), 0, s,
-                           (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (float *)a.ws, a.L, a.H, NC);
+        if constexpr (PREC == PREC_BF16)
+            hipLaunchKernelGGL((prep_channel_tm_kernel<D, C>), dim3(units * NC), dim3(512), 0, s,
+                               (const uint16_t *)a.q, (const uint16_t *)a.k, a.alpha, a.beta,
+                               (unsigned char *)a.ws, a.L, a.H, NC);
+        else
+            hipLaunchKernelGGL((prep_channel_kernel<D, C, PREC, TI>), dim3(units * NC), dim3(256), 0, s,
+                               (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (float *)a.ws, a.L, a.H, NC);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (phase & PHASE_SCAN) {
-        hipLaunchKernelGGL((scan_channel_kernel<D, D, BV, C, PREC, TI, TO>), dim3(units * (D / BV)), dim3(256), 0, s,
-                           (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, (const float *)a.ws,
-                           a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC);
+        if constexpr (PREC == PREC_BF16)
+            hipLaunchKernelGGL((scan_channel_tm_kernel<D, D, C, TO>), dim3(units * (D / BV)), dim3(512), 0, s,
+                               (const uint16_t *)a.v, (const unsigned char *)a.ws, a.state_in, (TO *)a.out,
+                               a.state_out, a.L, a.H, NC);
+        else
+            hipLaunchKernelGGL((scan_channel_kernel<D, D, BV, C, PREC, TI, TO>), dim3(units * (D / BV)), dim3(256), 0,
+                               s, (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, (const float *)a.ws,
+                               a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC);
         return hipGetLastError();
     }
     return hipSuccess;

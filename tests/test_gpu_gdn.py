@@ -253,6 +253,43 @@ def test_channel_gate_bf16(out_dtype):
     assert rel_err(S, S_ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("chunk", [64, 32, 16])
+def test_channel_gate_bf16_chunks(d, chunk):
+    """bf16 per-channel path at every chunk size and head width, ragged length,
+    nonzero initial state."""
+    shape = synth.GDNShape(2, 200, 2, d, d, "channel", 2.0, "bf16")
+    announce(f"channel bf16 d={d} chunk={chunk}")
+    x = synth.gdn_inputs(shape, seed=35 + d + chunk)
+    S0 = np.random.default_rng(35).standard_normal((2, 2, d, d)).astype(np.float32)
+    o, S = run_prefill(x, shape, chunk, out_dtype=torch.float32, S0=S0)
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(o, o_ref) <= TOL_BF16
+    assert rel_err(S, S_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("case", ["zero", "some_channels_near_zero", "one"])
+def test_channel_gate_extreme_decays_bf16(case):
+    """bf16 inputs with the gate extremes of the fp32 case (a block whose gate span
+    exceeds the matrix-core reference range is summed pair by pair)."""
+    shape = synth.GDNShape(1, 150, 2, 128, 128, "channel", 0.0, "bf16")
+    announce(f"channel bf16 extreme {case}")
+    x = synth.gdn_inputs(shape, seed=36)
+    a = x["alpha"].copy()
+    if case == "zero":
+        a[:] = 0.0
+    elif case == "one":
+        a[:] = 1.0
+    else:
+        a[..., ::7] = 1e-20
+    x["alpha"] = a
+    S0 = np.random.default_rng(36).standard_normal((1, 2, 128, 128)).astype(np.float32)
+    o, S = run_prefill(x, shape, 64, out_dtype=torch.float32, S0=S0)
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(o, o_ref) <= TOL_BF16
+    assert rel_err(S, S_ref) <= TOL_BF16
+
+
 def test_channel_gate_slow_decay_d128_fp32():
     shape = synth.GDNShape(1, 300, 2, 128, 128, "channel", 0.0, "f32")
     announce("channel fp32 d128 slow decay")
