@@ -562,6 +562,9 @@ __global__ __launch_bounds__(512) void prep_channel_tm_kernel(const uint16_t *__
     __shared__ __attribute__((aligned(16))) float Pvm[C * CP];        // Pv (b-scaled columns)
     __shared__ __attribute__((aligned(16))) float TZ[ZR * CP];        // inverse T, then Z = K1^T Te
     __shared__ float Xs_own[XS_IN_TZ ? 1 : 4 * 16 * 17];
+    constexpr int QP = DK + 8;                        // bf16 pitch of the staged Q rows
+    constexpr bool QS_IN_AM = DK <= 2 * C;            // Q fits where Te was once Te is no longer read
+    __shared__ __attribute__((aligned(16))) uint16_t Qs_own[QS_IN_AM ? 8 : C * QP];
     __shared__ float bs[C];
     __shared__ float seg_tot[PARTS][DK];
     float *Xs = XS_IN_TZ ? TZ + C * CP : Xs_own;
@@ -578,27 +581,45 @@ __global__ __launch_bounds__(512) void prep_channel_tm_kernel(const uint16_t *__
     unsigned char *wsu = ws + ((size_t)unit * NC + n) * SH::BYTES;
 
     // ---- K^T (bf16), beta, per-channel prefix sums of log2(alpha) ----
-    for (int idx = tid; idx < C * DK / 8; idx += NTH) {
-        const int t = idx / (DK / 8), c0 = 8 * (idx % (DK / 8));
-        uint4 u = make_uint4(0u, 0u, 0u, 0u);
-        if (t < Lc) u = *reinterpret_cast<const uint4 *>(k + (tok0 + (size_t)(t0 + t) * H) * DK + c0);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    // (all global loads of this step are issued before any of them is used)
+    // K pieces are token-major across lanes, so the transposed LDS writes of a
+    // wave land in consecutive banks.
+    constexpr int KPT = (C * DK / 8 + NTH - 1) / NTH;
+    uint4 kraw[KPT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            KT[(c0 + 2 * e) * KTP + t] = (uint16_t)(w[e] & 0xFFFFu);
-            KT[(c0 + 2 * e + 1) * KTP + t] = (uint16_t)(w[e] >> 16);
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = min(tid + NTH * i, C * DK / 8 - 1);
+        const int t = idx % C, c0 = 8 * (idx / C);
+        kraw[i] = *reinterpret_cast<const uint4 *>(k + (tok0 + (size_t)(t0 + min(t, Lc - 1)) * H) * DK + c0);
+    }
+    const int pc = tid % DK, pp0 = tid / DK;   // prefix-sum roles: channel, token segment
+    float alph[SEG];
+#pragma unroll
+    for (int s2 = 0; s2 < SEG; ++s2)
+        alph[s2] = alpha[(tok0 + (size_t)(t0 + min(pp0 * SEG + s2, Lc - 1)) * H) * DK + pc];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = tid + NTH * i;
+        if (idx < C * DK / 8) {
+            const int t = idx % C, c0 = 8 * (idx / C);
+            const uint4 u = (t < Lc) ? kraw[i] : make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                KT[(c0 + 2 * e) * KTP + t] = (uint16_t)(w[e] & 0xFFFFu);
+                KT[(c0 + 2 * e + 1) * KTP + t] = (uint16_t)(w[e] >> 16);
+            }
         }
     }
     {
-        const int c = tid % DK, p = tid / DK;
         float run = 0.f;
+#pragma unroll
         for (int s2 = 0; s2 < SEG; ++s2) {
-            const int t = p * SEG + s2;
-            const float a = alpha[(tok0 + (size_t)(t0 + min(t, Lc - 1)) * H) * DK + c];
-            run += (t < Lc) ? log2_gate(a) : 0.f;
-            G[t * GP + c] = run;
+            const int t = pp0 * SEG + s2;
+            run += (t < Lc) ? log2_gate(alph[s2]) : 0.f;
+            G[t * GP + pc] = run;
         }
-        seg_tot[p][c] = run;
+        seg_tot[pp0][pc] = run;
     }
     if (tid < C) {
         const float bt = beta[tok0 + (size_t)(t0 + min(tid, Lc - 1)) * H];
@@ -626,33 +647,59 @@ __global__ __launch_bounds__(512) void prep_channel_tm_kernel(const uint16_t *__
         const uint16_t *qrow = q + (tok0 + (size_t)(t0 + min(trow, Lc - 1)) * H) * DK;
         const uint16_t *kcol = k + (tok0 + (size_t)(t0 + min(icol, Lc - 1)) * H) * DK;
         const bool trow_ok = trow < Lc, icol_ok = icol < Lc;
+        // eight consecutive channels of a G row (row -1 reads as zeros)
+        auto grow8 = [&](Frag &f, int row, int c0) {
+            if (row >= 0) load_frag_f32(f, G + row * GP + c0);
+            else zero_frag(f);
+        };
         bool use_mfma = true;
         if (I == J) {
             bool ok = true;
-            for (int kb = 0; kb < DK / 32; ++kb)
-                for (int e = 0; e < 8; ++e) {
-                    const int c = 32 * kb + 8 * lq + e;
-                    ok = ok && (ghat(16 * I, c) - G[(16 * I + 15) * GP + c] <= DIAG_SPAN_MAX);
-                }
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                Frag a, z;
+                grow8(a, 16 * I - 1, 32 * kb + 8 * lq);
+                grow8(z, 16 * I + 15, 32 * kb + 8 * lq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ok = ok && (a.x[e] - z.x[e] <= DIAG_SPAN_MAX);
+            }
             use_mfma = __all(ok);
         }
         f32x4 ae = {0.f, 0.f, 0.f, 0.f}, av = ae, pe = ae, pv = ae;
         if (use_mfma) {
+            Raw8<uint16_t> rk8[DK / 32], rq8[DK / 32], rc8[DK / 32];
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
-                Frag rk, rq, ck1, ck2, fk, fq, fkc;
-                load_row8<uint16_t>(fk, krow + 32 * kb + 8 * lq);
-                load_row8<uint16_t>(fq, qrow + 32 * kb + 8 * lq);
-                load_row8<uint16_t>(fkc, kcol + 32 * kb + 8 * lq);
+                load_raw8<uint16_t>(rk8[kb], krow + 32 * kb + 8 * lq);
+                load_raw8<uint16_t>(rq8[kb], qrow + 32 * kb + 8 * lq);
+                load_raw8<uint16_t>(rc8[kb], kcol + 32 * kb + 8 * lq);
+            }
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                const int c0 = 32 * kb + 8 * lq;
+                Frag rk, rq, ck1, ck2, fk, fq, fkc, gt, ght, gi, ghi, ref;
+                raw_to_frag(fk, rk8[kb]);
+                raw_to_frag(fq, rq8[kb]);
+                raw_to_frag(fkc, rc8[kb]);
+                grow8(gt, trow, c0);
+                grow8(ght, trow - 1, c0);
+                grow8(gi, icol, c0);
+                grow8(ghi, icol - 1, c0);
+                if (I == J) {
+                    Frag a, z;
+                    grow8(a, 16 * I - 1, c0);
+                    grow8(z, 16 * I + 15, c0);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ref.x[e] = 0.5f * (a.x[e] + z.x[e]);
+                } else {
+                    grow8(ref, 16 * J + 15, c0);
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int c = 32 * kb + 8 * lq + e;
-                    const float ref = (I == J) ? 0.5f * (ghat(16 * I, c) + G[(16 * I + 15) * GP + c])
-                                               : G[(16 * J + 15) * GP + c];
-                    rk.x[e] = trow_ok ? fk.x[e] * exp2_fast(ghat(trow, c) - ref) : 0.f;
-                    rq.x[e] = trow_ok ? fq.x[e] * exp2_fast(G[trow * GP + c] - ref) : 0.f;
-                    ck1.x[e] = icol_ok ? fkc.x[e] * exp2_fast(ref - ghat(icol, c)) : 0.f;
-                    ck2.x[e] = icol_ok ? fkc.x[e] * exp2_fast(ref - G[icol * GP + c]) : 0.f;
+                    rk.x[e] = trow_ok ? fk.x[e] * exp2_fast(ght.x[e] - ref.x[e]) : 0.f;
+                    rq.x[e] = trow_ok ? fq.x[e] * exp2_fast(gt.x[e] - ref.x[e]) : 0.f;
+                    ck1.x[e] = icol_ok ? fkc.x[e] * exp2_fast(ref.x[e] - ghi.x[e]) : 0.f;
+                    ck2.x[e] = icol_ok ? fkc.x[e] * exp2_fast(ref.x[e] - gi.x[e]) : 0.f;
                 }
                 const auto ork = make_op<PREC_BF16, false>(rk), orq = make_op<PREC_BF16, false>(rq);
                 const auto oc1 = make_op<PREC_BF16, false>(ck1), oc2 = make_op<PREC_BF16, false>(ck2);
@@ -771,6 +818,16 @@ __global__ __launch_bounds__(512) void prep_channel_tm_kernel(const uint16_t *__
         }
     };
 
+    // Q rows for the W^T step, loaded now and staged once Te is no longer read
+    constexpr int QPT = (C * DK / 8 + NTH - 1) / NTH;
+    uint4 qraw[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int idx = min(tid + NTH * i, C * DK / 8 - 1);
+        const int t = idx / (DK / 8), c0 = 8 * (idx % (DK / 8));
+        qraw[i] = *reinterpret_cast<const uint4 *>(q + (tok0 + (size_t)(t0 + min(t, Lc - 1)) * H) * DK + c0);
+    }
+
     // ---- Z = K1^T Te (DK x C, into TZ) and PT = Pe Te (C x C, in place of Pe) ----
     constexpr int ZT = (DK / 16) * NT;
     for (int tt = wave; tt < ZT + NT; tt += NW) {
@@ -820,75 +877,115 @@ __global__ __launch_bounds__(512) void prep_channel_tm_kernel(const uint16_t *__
     }
     __syncthreads();
 
+    uint16_t *Qs = QS_IN_AM ? reinterpret_cast<uint16_t *>(Am) : Qs_own;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int idx = tid + NTH * i;
+        if (idx < C * DK / 8) {
+            const int t = idx / (DK / 8), c0 = 8 * (idx % (DK / 8));
+            *reinterpret_cast<uint4 *>(&Qs[t * QP + c0]) = (t < Lc) ? qraw[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    __syncthreads();
+
     // ---- W^T tiles -> A-fragments of W, hi/lo ----
-    const uint16_t *qbase = q + (tok0 + (size_t)t0 * H) * DK;
-    for (int pr = wave; pr < NRR * NKW; pr += NW) {
-        const int R = pr / NKW, kb = pr % NKW;
-        const int r = 16 * R + lr;   // this lane's W row
-        float vals[8];
+    // Task = (K-block kb of W, group of row tiles R): the A operand of W^T for
+    // the two 16-column tiles 2kb, 2kb + 1 ([K * 2^gh | Av diag(b)]^T rows) is
+    // built once and reused for every R of the group.
+    constexpr int RG = 4, RPG = (NRR + RG - 1) / RG;
+    for (int task = wave; task < NKW * RG; task += NW) {
+        const int kb = task % NKW, rg = task / NKW;
+        bf16x8 ah[2][NKT], al[2][NKT];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const int T = 2 * kb + half;   // 16-column tile of W
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (16 * T < DK + C) {
+            const int T = 2 * kb + half;   // 16-column tile of W (uniform)
+            const int w = 16 * T + lr;     // A row: a W column
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt) {
-                    Frag a, bfr;
-                    const int w = 16 * T + lr;   // A row: a W column
+            for (int kt = 0; kt < NKT; ++kt) {
+                const int j0 = 32 * kt + 8 * lq;   // first of this lane's eight tokens
+                Frag a;
+                zero_frag(a);
+                if (j0 < C) {
+                    if (16 * T < DK) {          // (K * 2^gh)^T
+                        const uint4 u = *reinterpret_cast<const uint4 *>(&KT[w * KTP + j0]);
+                        Raw8<uint16_t> r8;
+                        r8.u = u;
+                        raw_to_frag(a, r8);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = 32 * kt + 8 * lq + e;
-                        float x = 0.f;
-                        if (j < C) {
-                            if (w < DK) x = bf16_to_f32(KT[w * KTP + j]) * exp2_fast(ghat(j, w));
-                            else x = Avm[j * CP + (w - DK)];
-                        }
-                        a.x[e] = x;
+                        for (int e = 0; e < 8; ++e) a.x[e] *= exp2_fast(ghat(j0 + e, w));
+                    } else if (16 * T < DK + C) {   // (Av diag(b))^T
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) a.x[e] = Avm[(j0 + e) * CP + (w - DK)];
                     }
+                }
+                split_bf16(a, ah[half][kt], al[half][kt]);
+            }
+        }
+        for (int R = rg * RPG; R < min(NRR, (rg + 1) * RPG); ++R) {
+            const int r = 16 * R + lr;     // this lane's W row (B column)
+            const bool srow = R < DK / 16; // state rows (M, N) or output rows (Qt, Pt); uniform
+            const float *brow = srow ? TZ + r * CP : Pem + (r - DK) * CP;
+            bf16x8 bh[NKT], bl[NKT];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = 32 * kt + 8 * lq + e;
-                        float x = 0.f;
-                        if (j < C) x = (r < DK) ? TZ[r * CP + j] : Pem[(r - DK) * CP + j];
-                        bfr.x[e] = x;
+            for (int kt = 0; kt < NKT; ++kt) {
+                Frag bfr;
+                if (32 * kt + 8 * lq + 8 <= C) load_frag_f32(bfr, brow + 32 * kt + 8 * lq);
+                else zero_frag(bfr);
+                split_bf16(bfr, bh[kt], bl[kt]);
+            }
+            const float gcr = srow ? G[(C - 1) * GP + r] : 0.f;
+            float vals[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int T = 2 * kb + half;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (16 * T < DK + C) {
+#pragma unroll
+                    for (int kt = 0; kt < NKT; ++kt) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[half][kt], bh[kt], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[half][kt], bh[kt], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[half][kt], bl[kt], acc, 0, 0, 0);
                     }
-                    mma<PREC_BF16, false, false>(acc, a, bfr);
                 }
-            }
-            // base - [Z; PT][K * 2^gh | Av diag(b)] at W[r][w], w = 16T + 4lq + e
-            float qv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (r >= DK && 16 * T < DK) {
-                const int t = r - DK;
-                if (t < Lc) {
-                    const uint2 u = *reinterpret_cast<const uint2 *>(qbase + (size_t)t * H * DK + 16 * T + 4 * lq);
-                    qv[0] = __uint_as_float(u.x << 16); qv[1] = __uint_as_float(u.x & 0xFFFF0000u);
-                    qv[2] = __uint_as_float(u.y << 16); qv[3] = __uint_as_float(u.y & 0xFFFF0000u);
-                }
-            }
+                // base at W[r][w], w = 16T + 4lq + e (the block is uniform per (R, T))
+                const int w0 = 16 * T + 4 * lq;
+                float base[4] = {0.f, 0.f, 0.f, 0.f};
+                if (srow) {
+                    if (16 * T < DK) {                    // diag(2^gC)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int w = 16 * T + 4 * lq + e;
-                float base = 0.f;
-                if (r < DK) {
-                    if (w < DK) {
-                        base = (w == r) ? exp2_fast(G[(C - 1) * GP + r]) : 0.f;
-                    } else if (w < DK + C) {
-                        const int i = w - DK;
-                        base = bs[i] * bf16_to_f32(KT[r * KTP + i]) * exp2_fast(G[(C - 1) * GP + r] - G[i * GP + r]);
+                        for (int e = 0; e < 4; ++e) base[e] = (w0 + e == r) ? exp2_fast(gcr) : 0.f;
+                    } else if (16 * T < DK + C) {         // K2^T = (b K * 2^(gC - g))^T
+                        const int i0 = w0 - DK;
+                        const uint2 u = *reinterpret_cast<const uint2 *>(&KT[r * KTP + i0]);
+                        const float kk[4] = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                                             __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            base[e] = bs[i0 + e] * kk[e] * exp2_fast(gcr - G[(i0 + e) * GP + r]);
                     }
                 } else {
                     const int t = r - DK;
-                    if (w < DK) base = qv[e] * exp2_fast(G[t * GP + w]);
-                    else if (w < DK + C) base = Pvm[t * CP + (w - DK)];
+                    if (16 * T < DK) {                    // Q * 2^g
+                        const uint2 u = *reinterpret_cast<const uint2 *>(&Qs[t * QP + w0]);
+                        const float4 g4 = *reinterpret_cast<const float4 *>(&G[t * GP + w0]);
+                        base[0] = __uint_as_float(u.x << 16) * exp2_fast(g4.x);
+                        base[1] = __uint_as_float(u.x & 0xFFFF0000u) * exp2_fast(g4.y);
+                        base[2] = __uint_as_float(u.y << 16) * exp2_fast(g4.z);
+                        base[3] = __uint_as_float(u.y & 0xFFFF0000u) * exp2_fast(g4.w);
+                    } else if (16 * T < DK + C) {         // Pv
+                        const float4 p4 = *reinterpret_cast<const float4 *>(&Pvm[t * CP + (w0 - DK)]);
+                        base[0] = p4.x; base[1] = p4.y; base[2] = p4.z; base[3] = p4.w;
+                    }
                 }
-                vals[4 * half + e] = base - acc[e];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vals[4 * half + e] = base[e] - acc[e];
             }
+            uint4 hi, lo;
+            split8(vals, hi, lo);
+            unsigned char *dst = wsu + (size_t)(R * NKW + kb) * 2048 + 16 * lane;
+            *reinterpret_cast<uint4 *>(dst) = hi;
+            *reinterpret_cast<uint4 *>(dst + 1024) = lo;
         }
-        uint4 hi, lo;
-        split8(vals, hi, lo);
-        unsigned char *dst = wsu + (size_t)(R * NKW + kb) * 2048 + 16 * lane;
-        *reinterpret_cast<uint4 *>(dst) = hi;
-        *reinterpret_cast<uint4 *>(dst + 1024) = lo;
     }
 }
 
