@@ -2,12 +2,21 @@
 //
 //   C[m][n] = sum_k A[m][k] * B[n][k]        (A: [M, K], B: [N, K], both K-contiguous)
 //
-// which is y = x W^T for weights stored [d_out, d_in].  Workgroup tile 256 x 128
-// x 64, four waves, each wave 64 rows x 128 columns (4 x 8 tiles of
-// v_mfma_f32_16x16x32_bf16).  A and B tiles are double-buffered in LDS; the
-// next K-tile's global loads are in flight while the current one computes.
+// which is y = x W^T for weights stored [d_out, d_in].  Workgroup tile 256 x 256
+// x 64, four waves, each wave 128 x 128 as 4 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16 (the accumulators, 256 floats per lane, live in the
+// accumulation registers: one wave per SIMD).  Per k-step of 16 a wave reads
+// four A and four B fragments for sixteen products, a third less LDS traffic
+// per multiply-add than 64 x 128 wave tiles.  A and B K-tiles are staged
+// through registers into double-buffered LDS (one coalesced 16-byte load per
+// piece); LDS rows are 128 bytes with the 16-byte segments XOR-swizzled by row,
+// so fragment reads of 8 or 16 consecutive rows hit distinct banks.
 //
-// Epilogues (one launch each, fused into the store):
+// 32x32x16 operand layout: A[i][k]: lane = i + 32*(k/8), slot k%8; B[k][j]:
+// lane = j + 32*(k/8), slot k%8; accumulator register r of lane l holds
+// D[8*(r/4) + 4*(l/32) + r%4][l%32].
+//
+// Epilogues (fused into the store):
 //   EPI_PROJ  input projection of the looped block: columns [0, H*d) -> q and
 //             [H*d, 2H*d) -> k, each L2-normalised per head (x / max(|x|, 1e-6))
 //             and stored bf16; [2H*d, 3H*d) -> v (bf16); [3H*d, 3H*d + H) ->
@@ -22,8 +31,9 @@ namespace lt2 {
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int PITCH = BK + 8;   // bf16 elements per LDS row (16-byte aligned, staggered banks)
+constexpr int BM = 256, BN = 256, BK = 64;
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 struct ProjOut {
     uint16_t *q, *k, *v;   // [M, H*d] bf16
@@ -38,54 +48,62 @@ struct ResidOut {
 
 __device__ __forceinline__ float sigmoidf_acc(float z) { return 1.f / (1.f + expf(-z)); }
 
-template <int EPI, int DH>
-__global__ __launch_bounds__(256) void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
-                                                           int M, int N, int K, int lda, int ldb, ProjOut po,
-                                                           ResidOut ro) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * PITCH];
+// Element offset of 16-byte segment `seg` of LDS row `r` (64 bf16 per row).
+__device__ __forceinline__ int swz(int r, int seg) {
+    return r * BK + 8 * (seg ^ (r & 7) ^ ((r >> 3) & 1));
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lq = lane >> 4;
+template <int EPI, int DH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int M, int N, int K,
+                         int lda, int ldb, ProjOut po, ResidOut ro) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, lh = lane >> 5;
     const int n_tiles = (N + BN - 1) / BN;
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int mt = logical / n_tiles, nt = logical % n_tiles;
     const int m0 = mt * BM, n0 = nt * BN;
 
-    // global -> register staging: A 8 x 16 bytes, B 4 x 16 bytes per lane
-    // (plain macros rather than lambdas: a captured array would be moved to LDS)
-    uint4 ra[8], rb[4];
-#define LT2_GEMM_LOAD(k0)                                                                        \
-    do {                                                                                         \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
-            const int c = tid + 256 * i;                                                         \
-            const int gm = min(m0 + (c >> 3), M - 1);                                            \
-            ra[i] = *reinterpret_cast<const uint4 *>(A + (size_t)gm * lda + (k0) + 8 * (c & 7)); \
-        }                                                                                        \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
-            const int c = tid + 256 * i;                                                         \
-            const int gn = min(n0 + (c >> 3), N - 1);                                            \
-            rb[i] = *reinterpret_cast<const uint4 *>(B + (size_t)gn * ldb + (k0) + 8 * (c & 7)); \
-        }                                                                                        \
+    // staging: 8 A and 8 B pieces of 16 bytes per thread; piece c covers row c/8,
+    // segment c%8 (eight consecutive threads read one 128-byte row)
+    const uint16_t *ag[8], *bg[8];
+    int ls[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = tid + 256 * i;
+        const int row = c >> 3, seg = c & 7;
+        ag[i] = A + (size_t)min(m0 + row, M - 1) * lda + 8 * seg;
+        bg[i] = B + (size_t)min(n0 + row, N - 1) * ldb + 8 * seg;
+        ls[i] = swz(row, seg);
+    }
+    u32x4 ra[8], rb[8];
+#define LT2_GEMM_LOAD(k0)                                                                   \
+    do {                                                                                    \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
+            ra[i] = *reinterpret_cast<const u32x4 *>(ag[i] + (k0));                         \
+            rb[i] = *reinterpret_cast<const u32x4 *>(bg[i] + (k0));                         \
+        }                                                                                   \
     } while (0)
-#define LT2_GEMM_STORE(buf)                                                                      \
-    do {                                                                                         \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
-            const int c = tid + 256 * i;                                                         \
-            *reinterpret_cast<uint4 *>(&As[buf][(c >> 3) * PITCH + 8 * (c & 7)]) = ra[i];         \
-        }                                                                                        \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
-            const int c = tid + 256 * i;                                                         \
-            *reinterpret_cast<uint4 *>(&Bs[buf][(c >> 3) * PITCH + 8 * (c & 7)]) = rb[i];         \
-        }                                                                                        \
+#define LT2_GEMM_STORE(buf)                                                                 \
+    do {                                                                                    \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
+            *reinterpret_cast<u32x4 *>(&As[buf][ls[i]]) = ra[i];                            \
+            *reinterpret_cast<u32x4 *>(&Bs[buf][ls[i]]) = rb[i];                            \
+        }                                                                                   \
     } while (0)
 
-    f32x4 acc[4][8];
+    f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+    // fragment rows of this lane: A rows 128 wm + 32 mi + l32, B rows 128 wn + 32 ni + l32
     const int KT = K / BK;
     LT2_GEMM_LOAD(0);
     LT2_GEMM_STORE(0);
@@ -94,51 +112,49 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_kernel(const uint16_t *__res
         const int buf = kt & 1;
         if (kt + 1 < KT) LT2_GEMM_LOAD((kt + 1) * BK);
 #pragma unroll
-        for (int s = 0; s < BK / 32; ++s) {
-            bf16x8 a[4], b[8];
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int seg = 2 * ks + lh;
+            bf16x8 a[4], b[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][(64 * wave + 16 * i + lr) * PITCH + 32 * s + 8 * lq]);
+                a[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][swz(128 * wm + 32 * i + l32, seg)]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(16 * j + lr) * PITCH + 32 * s + 8 * lq]);
+            for (int j = 0; j < 4; ++j)
+                b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][swz(128 * wn + 32 * j + l32, seg)]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < KT) {
-            wait_vmem_all();
-            LT2_GEMM_STORE(buf ^ 1);
-        }
+        if (kt + 1 < KT) LT2_GEMM_STORE(buf ^ 1);
         __syncthreads();
     }
 
 #undef LT2_GEMM_LOAD
 #undef LT2_GEMM_STORE
 
-    // ---- epilogue: lane holds C[m0 + 64 wave + 16 i + 4 lq + r][n0 + 16 j + lr] ----
+    // ---- epilogue: register r of tile (i, j) holds
+    //      C[m0 + 128 wm + 32 i + 8 (r/4) + 4 lh + r%4][n0 + 128 wn + 32 j + l32] ----
+    const int nw = n0 + 128 * wn;   // first column of this wave
     if constexpr (EPI == EPI_PROJ) {
         const int Hd = po.H * po.d;
-        if (n0 < 3 * Hd) {
-            // q, k or v block; a 128-column tile holds whole heads (Hd % 128 == 0)
-            const int region = n0 / Hd;             // 0 q, 1 k, 2 v
+        if (nw < 3 * Hd) {
+            // q, k or v columns; the wave's 128 columns hold whole heads (Hd % 128 == 0)
+            const int region = nw / Hd;             // 0 q, 1 k, 2 v
             uint16_t *dst = region == 0 ? po.q : (region == 1 ? po.k : po.v);
-            const int c0 = n0 - region * Hd;
-            constexpr int TPH = DH / 16;            // column tiles per head
+            const int c0 = nw - region * Hd;
+            constexpr int TPH = DH / 32;            // 32-column tiles per head
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + 64 * wave + 16 * i + 4 * lq + r;
-                    float scale[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) scale[j] = 1.f;
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    float scale[4] = {1.f, 1.f, 1.f, 1.f};
                     if (region < 2) {
-                        // per-head sum of squares: own tiles, then across the 16 lanes of the row
+                        // per-head sum of squares: own tiles, then across the 32 lanes of the row
 #pragma unroll
-                        for (int h0 = 0; h0 < 8; h0 += TPH) {
+                        for (int h0 = 0; h0 < 4; h0 += TPH) {
                             float ss = 0.f;
 #pragma unroll
                             for (int j = h0; j < h0 + TPH; ++j) ss += acc[i][j][r] * acc[i][j][r];
@@ -146,6 +162,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_kernel(const uint16_t *__res
                             ss += __shfl_xor(ss, 2);
                             ss += __shfl_xor(ss, 4);
                             ss += __shfl_xor(ss, 8);
+                            ss += __shfl_xor(ss, 16);
                             const float sc = 1.f / fmaxf(sqrtf(ss), 1e-6f);
 #pragma unroll
                             for (int j = h0; j < h0 + TPH; ++j) scale[j] = sc;
@@ -153,8 +170,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_kernel(const uint16_t *__res
                     }
                     if (m < M) {
 #pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            dst[(size_t)m * Hd + c0 + 16 * j + lr] = bf16_bits(acc[i][j][r] * scale[j]);
+                        for (int j = 0; j < 4; ++j)
+                            dst[(size_t)m * Hd + c0 + 32 * j + l32] = bf16_bits(acc[i][j][r] * scale[j]);
                     }
                 }
             }
@@ -163,32 +180,36 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_kernel(const uint16_t *__res
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < 4; ++j) {
+                    const int c = nw + 32 * j + l32 - 3 * Hd;
+                    if (c >= 2 * po.H) continue;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int m = m0 + 64 * wave + 16 * i + 4 * lq + r;
-                        const int c = n0 + 16 * j + lr - 3 * Hd;
-                        if (m >= M || c >= 2 * po.H) continue;
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        if (m >= M) continue;
                         const float z = acc[i][j][r];
                         if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoidf_acc(z);
                         else po.alpha[(size_t)m * po.H + c - po.H] = sigmoidf_acc(-z);  // exp(-softplus(z))
                     }
+                }
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j) {
+                const int n = nw + 32 * j + l32;
+                if (n >= N) continue;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + 64 * wave + 16 * i + 4 * lq + r;
-                    const int n = n0 + 16 * j + lr;
-                    if (m >= M || n >= N) continue;
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    if (m >= M) continue;
                     const size_t o = (size_t)m * N + n;
                     const float hn = ro.h[o] + acc[i][j][r];
                     ro.h[o] = hn;
                     ro.xb[o] = bf16_bits(hn);
                 }
+            }
     }
 }
 
