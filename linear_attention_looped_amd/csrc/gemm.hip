@@ -70,28 +70,30 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     const int m0 = mt * BM, n0 = nt * BN;
 
     // staging: 8 A and 8 B pieces of 16 bytes per thread; piece c covers row c/8,
-    // segment c%8 (eight consecutive threads read one 128-byte row)
-    const uint16_t *ag[8], *bg[8];
+    // segment c%8 (eight consecutive threads read one 128-byte row).  Addresses
+    // are a uniform base plus 32-bit offsets; rows past M or N repeat the last row.
+    const uint16_t *Ab = A + (size_t)m0 * lda, *Bb = B + (size_t)n0 * ldb;
+    unsigned ao[8], bo[8];
     int ls[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int c = tid + 256 * i;
         const int row = c >> 3, seg = c & 7;
-        ag[i] = A + (size_t)min(m0 + row, M - 1) * lda + 8 * seg;
-        bg[i] = B + (size_t)min(n0 + row, N - 1) * ldb + 8 * seg;
+        ao[i] = (unsigned)(min(m0 + row, M - 1) - m0) * (unsigned)lda + 8 * seg;
+        bo[i] = (unsigned)(min(n0 + row, N - 1) - n0) * (unsigned)ldb + 8 * seg;
         ls[i] = swz(row, seg);
     }
     u32x4 ra[8], rb[8];
 #define LT2_GEMM_LOAD(k0)                                                                   \
     do {                                                                                    \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
-            ra[i] = *reinterpret_cast<const u32x4 *>(ag[i] + (k0));                         \
-            rb[i] = *reinterpret_cast<const u32x4 *>(bg[i] + (k0));                         \
+            ra[i] = *reinterpret_cast<const u32x4 *>(Ab + ao[i] + (k0));                    \
+            rb[i] = *reinterpret_cast<const u32x4 *>(Bb + bo[i] + (k0));                    \
         }                                                                                   \
     } while (0)
-#define LT2_GEMM_STORE(buf)                                                                 \
+#define LT2_GEMM_STORE_HALF(buf, h)                                                         \
     do {                                                                                    \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
+        _Pragma("unroll") for (int i = 4 * (h); i < 4 * (h) + 4; ++i) {                     \
             *reinterpret_cast<u32x4 *>(&As[buf][ls[i]]) = ra[i];                            \
             *reinterpret_cast<u32x4 *>(&Bs[buf][ls[i]]) = rb[i];                            \
         }                                                                                   \
@@ -103,36 +105,50 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    // fragment rows of this lane: A rows 128 wm + 32 mi + l32, B rows 128 wn + 32 ni + l32
+    // fragment reads of k-step ks (K offset 16 ks) of LDS buffer buf
+    int arow[4], brow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        arow[i] = 128 * wm + 32 * i + l32;
+        brow[i] = 128 * wn + 32 * i + l32;
+    }
+    auto frags = [&](int buf, int ks, bf16x8 *a, bf16x8 *b) __attribute__((always_inline)) {
+        const int seg = 2 * ks + lh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][swz(arow[i], seg)]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][swz(brow[j], seg)]);
+    };
+
     const int KT = K / BK;
     LT2_GEMM_LOAD(0);
-    LT2_GEMM_STORE(0);
+    LT2_GEMM_STORE_HALF(0, 0);
+    LT2_GEMM_STORE_HALF(0, 1);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < KT) LT2_GEMM_LOAD((kt + 1) * BK);
+        const bool more = kt + 1 < KT;
+        if (more) LT2_GEMM_LOAD((kt + 1) * BK);
+        bf16x8 a[2][4], b[2][4];
+        frags(buf, 0, a[0], b[0]);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            const int seg = 2 * ks + lh;
-            bf16x8 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][swz(128 * wm + 32 * i + l32, seg)]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][swz(128 * wn + 32 * j + l32, seg)]);
+            const int cur = ks & 1;
+            if (ks + 1 < BK / 16) frags(buf, ks + 1, a[cur ^ 1], b[cur ^ 1]);
+            // the next K-tile goes to the other buffer in two halves, behind this tile's products
+            if (more && ks == 2) LT2_GEMM_STORE_HALF(buf ^ 1, 0);
+            if (more && ks == 3) LT2_GEMM_STORE_HALF(buf ^ 1, 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < KT) LT2_GEMM_STORE(buf ^ 1);
         __syncthreads();
     }
 
 #undef LT2_GEMM_LOAD
-#undef LT2_GEMM_STORE
+#undef LT2_GEMM_STORE_HALF
 
     // ---- epilogue: register r of tile (i, j) holds
     //      C[m0 + 128 wm + 32 i + 8 (r/4) + 4 lh + r%4][n0 + 128 wn + 32 j + l32] ----

@@ -649,8 +649,10 @@ __global__ __launch_bounds__(512) void prep_channel_tm_kernel(const uint16_t *__
         const bool trow_ok = trow < Lc, icol_ok = icol < Lc;
         // eight consecutive channels of a G row (row -1 reads as zeros)
         auto grow8 = [&](Frag &f, int row, int c0) {
-            if (row >= 0) load_frag_f32(f, G + row * GP + c0);
-            else zero_frag(f);
+            load_frag_f32(f, G + max(row, 0) * GP + c0);
+            const bool z = row < 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f.x[e] = z ? 0.f : f.x[e];
         };
         bool use_mfma = true;
         if (I == J) {
@@ -661,7 +663,7 @@ __global__ __launch_bounds__(512) void prep_channel_tm_kernel(const uint16_t *__
                 grow8(a, 16 * I - 1, 32 * kb + 8 * lq);
                 grow8(z, 16 * I + 15, 32 * kb + 8 * lq);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ok = ok && (a.x[e] - z.x[e] <= DIAG_SPAN_MAX);
+                for (int e = 0; e < 8; ++e) ok &= (a.x[e] - z.x[e] <= DIAG_SPAN_MAX);
             }
             use_mfma = __all(ok);
         }
