@@ -59,12 +59,35 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     unsigned char *wsu = ws + ((size_t)unit * NC + n) * (size_t)(8 * C * C + 12 * C);
     float *gg = reinterpret_cast<float *>(wsu + 8 * C * C);
 
-    for (int idx = tid; idx < C * (DK / 8); idx += 256) {
+    // Q fragments of this wave's Q K^T tiles, fetched together with K so that
+    // the global latency is paid once
+    Raw8<TI> qraw[MAXP][DK / 32];
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+        const int tt = min(wave + 4 * m, NLT - 1);
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= tt) ++I;
+        const int arow = 16 * I + lr;
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+            load_raw8<TI>(qraw[m][kb], q + ((size_t)(b * (size_t)L + t0 + min(arow, Lc - 1)) * H + h) * DK + 32 * kb + 8 * lq);
+    }
+    constexpr int KPT = (C * (DK / 8) + 255) / 256;
+    Raw8<TI> kraw[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = min(tid + 256 * i, C * (DK / 8) - 1);
         const int t = idx / (DK / 8), c8 = idx % (DK / 8);
-        Raw8<TI> r;
-        load_raw8<TI>(r, k + ((size_t)(b * (size_t)L + t0 + min(t, Lc - 1)) * H + h) * DK + 8 * c8);
-        if (t >= Lc) zero_raw8<TI>(r);
-        *reinterpret_cast<Raw8<TI> *>(Ks + t * KP + 8 * c8) = r;
+        load_raw8<TI>(kraw[i], k + ((size_t)(b * (size_t)L + t0 + min(t, Lc - 1)) * H + h) * DK + 8 * c8);
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx < C * (DK / 8)) {
+            const int t = idx / (DK / 8), c8 = idx % (DK / 8);
+            if (t >= Lc) zero_raw8<TI>(kraw[i]);
+            *reinterpret_cast<Raw8<TI> *>(Ks + t * KP + 8 * c8) = kraw[i];
+        }
     }
     if (wave == 0) {
         const size_t tok = (size_t)(b * (size_t)L + t0 + min(lane, Lc - 1)) * H + h;
@@ -115,10 +138,8 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
         const int arow = 16 * I + lr;
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
-            Raw8<TI> ra;
-            load_raw8<TI>(ra, q + ((size_t)(b * (size_t)L + t0 + min(arow, Lc - 1)) * H + h) * DK + 32 * kb + 8 * lq);
             Frag fa, fb;
-            raw_to_frag(fa, ra);
+            raw_to_frag(fa, qraw[m][kb]);
             if (arow >= Lc) zero_frag(fa);
             raw_to_frag(fb, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq));
             mma<PREC, true, true>(pacc[m], fa, fb);
@@ -574,8 +595,8 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                                                              TO *__restrict__ out, float *__restrict__ state_out,
                                                              int L, int H, int NC) {
     constexpr int NW = 8, NTH = 64 * NW;
-    constexpr int KP = DK + 8;   // bf16 pitch of K, Q and S^T rows (16-byte aligned, staggered banks)
-    constexpr int CP = C + 8;    // bf16 pitch of Tm, P, R^T, U^T, U2^T rows
+    constexpr int KP = DK + 16;  // bf16 pitch of K, Q and S^T rows (16-byte aligned, staggered banks)
+    constexpr int CP = C + 16;   // bf16 pitch of Tm, P, R^T, U^T, U2^T rows
     constexpr int VP = BV + 8;   // bf16 pitch of V rows
     constexpr int OV = 16 / (int)sizeof(TO);   // outputs per 16-byte store
     constexpr int OP = BV + OV;                // pitch of the staged output rows
