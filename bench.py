@@ -348,6 +348,45 @@ def _slab_inputs(synth, shape, b0, nb):
     return out
 
 
+def bench_looped_decode(args, torch, lt2, synth, tokens=16, warm=3):
+    """Looped decode chain: 256 sequences, d_model 2048, H=16, d=128, T=4 loop
+    states carried in place, one token per step (fresh seeded h rows)."""
+    B, D, H, d, T = 256, 2048, 16, 128, 4
+    sh = synth.LoopShape(B, 1, D, H, d, T)
+    log(f"looped decode B={B} D={D} H={H} d={d} T={T}, {tokens} tokens")
+    w = synth.loop_weights(sh, seed=0)
+    w_in = torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16)
+    w_o = torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)
+    states = torch.zeros((T, B, H, d, d), dtype=torch.float32, device="cuda")
+    rows = [torch.from_numpy(synth.loop_h0(synth.LoopShape(B, 1, D, H, d, T), seed=100 + i)[:, 0]).to("cuda")
+            for i in range(tokens + warm)]
+    hbuf = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    desc = lt2.loop_desc(B, 1, D, H, d, T, 64)
+    ws = torch.empty(lt2.lt2_looped_decode_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        hbuf.copy_(rows[i])
+        lt2.lt2_looped_decode_step(hbuf, w_in, w_o, states, H, d, T, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(tokens)]
+    for i in range(tokens):
+        hbuf.copy_(rows[warm + i])
+        ev[i][0].record(stream)
+        lt2.lt2_looped_decode_step(hbuf, w_in, w_o, states, H, d, T, workspace=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    state_bytes = 2.0 * T * B * H * d * d * 4
+    weight_bytes = T * ((3 * H * d + 2 * H) * D + D * H * d) * 2.0
+    step_bytes = state_bytes + weight_bytes + T * B * (2 * D * 4 + D * 2)
+    flops = T * 2.0 * B * D * (3 * H * d + 2 * H + H * d) + T * B * H * 8.0 * d * d
+    log(f"looped decode {ms:.3f} ms per token step ({step_bytes / ms / 1e6:.0f} GB/s)")
+    return dict(B=B, d_model=D, H=H, d=d, T=T, tokens=tokens, ms_per_token=ms,
+                tokens_per_s=B / (ms / 1e3), tokens_per_s_per_loop=B * T / (ms / 1e3),
+                bytes_per_token=step_bytes, gbs=step_bytes / ms / 1e6, hbm_frac=step_bytes / ms / 1e6 / HBM_PEAK_GBS,
+                flops_per_token=flops, tflops=flops / ms / 1e9)
+
+
 def cpu_baseline(synth):
     """The fp64 oracle on the whole headline workload (4 sequences x 4096 tokens x
     16 heads, seed 0); tokens/s per loop = B*L / t."""
@@ -372,6 +411,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-looped", action="store_true")
     ap.add_argument("--no-channel", action="store_true")
+    ap.add_argument("--no-looped-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -392,6 +432,7 @@ def main():
     dec = None if args.no_decode else bench_decode(args, torch, lt2, synth)
     loo = None if args.no_looped else bench_looped(args, torch, lt2, synth)
     cha = None if args.no_channel else bench_channel(args, torch, lt2, synth)
+    lde = None if args.no_looped_decode else bench_looped_decode(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
     value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
@@ -416,6 +457,8 @@ def main():
         extra["looped"] = loo
     if cha:
         extra["channel_prefill"] = cha
+    if lde:
+        extra["looped_decode"] = lde
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",

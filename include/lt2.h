@@ -166,6 +166,33 @@ lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *h_in, float 
                             void *stream);
 
 /*
+ * Workspace bytes lt2_looped_decode_step needs (0 for an invalid descriptor,
+ * which includes desc->L != 1).
+ */
+size_t lt2_looped_decode_workspace_size(const lt2_loop_desc *desc);
+
+/*
+ * One decode token of the looped LT2-linear block for each of B sequences
+ * (the loop equation of the LT2 explainer, paithon.it, "Profondita presa in
+ * prestito", with the mixer in its recurrent form of "Sostituire il motore"):
+ * the T loops of lt2_looped_mixer applied to the new token, loop t carrying
+ * its own state across calls.  desc->L must be 1.
+ *   h        [B, d_model] fp32, the token's residual stream, updated in place
+ *   W_in     [3*H*d + 2*H, d_model] bf16, as for lt2_looped_mixer
+ *   W_o      [d_model, H*d] bf16
+ *   states   [T, B, H, d_head, d_head] fp32, loop t's state of every (b, h),
+ *            updated in place; zero before a sequence's first token
+ *   ws       at least lt2_looped_decode_workspace_size(desc) bytes, 256-aligned
+ * Each state is read once and written once per loop.  Because every loop's
+ * mixer is causal, calling this on tokens 1..L of a sequence from zero states
+ * yields, token by token, the h that lt2_looped_mixer gives for the sequence.
+ * Errors: LT2_ERR_SHAPE for L != 1; otherwise as lt2_looped_mixer.
+ */
+lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const void *W_in,
+                                  const void *W_o, float *states, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/*
  * Bandwidth probe: copy `bytes` (a multiple of 16) from src to dst with one
  * streaming kernel.  Used to measure the achievable HBM bandwidth.
  */

@@ -193,4 +193,29 @@ lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *h_in, float 
     return hip_status(launch_looped(a, (hipStream_t)stream));
 }
 
+size_t lt2_looped_decode_workspace_size(const lt2_loop_desc *desc) {
+    if (check_loop(desc) != LT2_OK || desc->L != 1) return 0;
+    if (desc->B == 0) return 0;
+    return loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head).total;
+}
+
+lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const void *W_in, const void *W_o,
+                                  float *states, void *ws, size_t ws_bytes, void *stream) {
+    lt2_status st = check_loop(desc);
+    if (st != LT2_OK) return st;
+    if (desc->L != 1) return LT2_ERR_SHAPE;
+    const bool work = desc->B > 0 && desc->T > 0;
+    if (work && (!h || !W_in || !W_o || !states)) return LT2_ERR_NULL;
+    if (!aligned(h, 16) || !aligned(W_in, 16) || !aligned(W_o, 16) || !aligned(states, 16)) return LT2_ERR_ALIGN;
+    const size_t need = work ? loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head).total : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 256)) return LT2_ERR_ALIGN;
+    if (!work) return LT2_OK;
+    LoopDecodeArgs a;
+    a.B = desc->B; a.D = desc->d_model; a.H = desc->H; a.d = desc->d_head; a.T = desc->T;
+    a.h = h; a.W_in = static_cast<const uint16_t *>(W_in); a.W_o = static_cast<const uint16_t *>(W_o);
+    a.states = states; a.ws = ws;
+    return hip_status(launch_looped_decode(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

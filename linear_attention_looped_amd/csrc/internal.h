@@ -45,6 +45,17 @@ struct LoopLayout {
 };
 LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk);
 hipError_t launch_looped(const LoopArgs &a, hipStream_t s);
+
+// Looped decode: one token per sequence, T loop states carried in place.
+struct LoopDecodeArgs {
+    int B, D, H, d, T;
+    float *h;                // [B, D] fp32, in place
+    const uint16_t *W_in, *W_o;
+    float *states;           // [T, B, H, d, d] fp32, in place
+    void *ws;
+};
+LoopLayout loop_decode_layout(int B, int D, int H, int d);
+hipError_t launch_looped_decode(const LoopDecodeArgs &a, hipStream_t s);
 hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t s);
 
 }  // namespace lt2

@@ -6,6 +6,12 @@
 //   o = gated-delta prefill(q, k, v, alpha, beta; S_0 = 0), bf16
 //   h += o W_o^T, xb = bf16(h)                      (GEMM with residual epilogue)
 // All launches are enqueued on one stream; nothing synchronises in between.
+//
+// Looped decode: one new token per sequence through the same T loops, loop t
+// carrying its own recurrent state across calls (the decode form of the mixer,
+// state update equation of "Sostituire il motore"):
+//   xb = bf16(h); for t: [q|k|v|beta|alpha] = xb W_in^T (as above);
+//   o = decode step on state t; h += o W_o^T, xb = bf16(h)
 #include "gemm.h"
 #include "internal.h"
 
@@ -29,6 +35,54 @@ LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk) {
     w.prefill = off; off = align256(off + prefill_head_ws_bytes(B, L, H, chunk));
     w.total = off;
     return w;
+}
+
+LoopLayout loop_decode_layout(int B, int D, int H, int d) {
+    LoopLayout w{};
+    const size_t M = (size_t)B, Hd = (size_t)H * d;
+    size_t off = 0;
+    w.xb = off; off = align256(off + M * D * 2);
+    w.q = off; off = align256(off + M * Hd * 2);
+    w.k = off; off = align256(off + M * Hd * 2);
+    w.v = off; off = align256(off + M * Hd * 2);
+    w.beta = off; off = align256(off + M * H * 4);
+    w.alpha = off; off = align256(off + M * H * 4);
+    w.o = off; off = align256(off + M * Hd * 2);
+    w.prefill = off;
+    w.total = off;
+    return w;
+}
+
+hipError_t launch_looped_decode(const LoopDecodeArgs &a, hipStream_t s) {
+    const int M = a.B, Hd = a.H * a.d, N_in = 3 * Hd + 2 * a.H;
+    unsigned char *ws = static_cast<unsigned char *>(a.ws);
+    const LoopLayout w = loop_decode_layout(a.B, a.D, a.H, a.d);
+    uint16_t *xb = reinterpret_cast<uint16_t *>(ws + w.xb);
+    uint16_t *q = reinterpret_cast<uint16_t *>(ws + w.q);
+    uint16_t *k = reinterpret_cast<uint16_t *>(ws + w.k);
+    uint16_t *v = reinterpret_cast<uint16_t *>(ws + w.v);
+    float *beta = reinterpret_cast<float *>(ws + w.beta);
+    float *alpha = reinterpret_cast<float *>(ws + w.alpha);
+    uint16_t *o = reinterpret_cast<uint16_t *>(ws + w.o);
+
+    hipError_t e = launch_cast_residual(a.h, a.h, xb, (size_t)M * a.D, s);
+    if (e != hipSuccess) return e;
+    GdnArgs g{};
+    g.B = a.B; g.L = 1; g.H = a.H; g.dk = a.d; g.dv = a.d; g.chunk = 64;
+    g.qkv_bf16 = 1; g.out_bf16 = 1; g.channel = 0;
+    g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta; g.out = o;
+    const size_t state_elems = (size_t)a.B * a.H * a.d * a.d;
+    for (int t = 0; t < a.T; ++t) {
+        e = launch_gemm_proj(xb, a.W_in, M, N_in, a.D, q, k, v, beta, alpha, a.H, a.d, s);
+        if (e != hipSuccess) return e;
+        g.state_in = a.states + (size_t)t * state_elems;
+        g.state_out = a.states + (size_t)t * state_elems;
+        e = launch_decode(g, s);
+        if (e != hipSuccess) return e;
+        e = launch_gemm_resid(o, a.W_o, M, a.D, Hd, a.h, xb, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_looped(const LoopArgs &a, hipStream_t s) {

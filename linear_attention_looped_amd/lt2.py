@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.lt2_looped_mixer_workspace_size.restype = Z
         L.lt2_looped_mixer.argtypes = [LD, P, P, P, P, P, Z, P]
         L.lt2_looped_mixer.restype = S
+        L.lt2_looped_decode_workspace_size.argtypes = [LD]
+        L.lt2_looped_decode_workspace_size.restype = Z
+        L.lt2_looped_decode_step.argtypes = [LD, P, P, P, P, P, Z, P]
+        L.lt2_looped_decode_step.restype = S
         L.lt2_hbm_copy.argtypes = [P, P, Z, P]
         L.lt2_hbm_copy.restype = S
         _lib = L
@@ -193,6 +197,32 @@ def lt2_looped_mixer(h_in, W_in, W_o, H: int, d_head: int, T: int, chunk: int = 
                                   _stream(stream))
     _check("lt2_looped_mixer", code)
     return h_out
+
+
+def lt2_looped_decode_workspace_size(desc: lt2_loop_desc) -> int:
+    return int(lib().lt2_looped_decode_workspace_size(ctypes.byref(desc)))
+
+
+def lt2_looped_decode_step(h, W_in, W_o, states, H: int, d_head: int, T: int, workspace=None, stream=None):
+    """One decode token of the looped block for each of B sequences.  h [B,D]
+    fp32 and states [T,B,H,d,d] fp32 are updated in place; W_in, W_o as for
+    lt2_looped_mixer.  Returns h."""
+    B, D = h.shape
+    _need(h, "h", torch.float32)
+    _need(states, "states", torch.float32)
+    _need(W_in, "W_in", torch.bfloat16)
+    _need(W_o, "W_o", torch.bfloat16)
+    assert tuple(states.shape) == (T, B, H, d_head, d_head), states.shape
+    desc = loop_desc(B, 1, D, H, d_head, T, 64)
+    ws_bytes = lt2_looped_decode_workspace_size(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=h.device)
+    code = lib().lt2_looped_decode_step(ctypes.byref(desc), _ptr(h), _ptr(W_in), _ptr(W_o), _ptr(states),
+                                        _ptr(workspace),
+                                        0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                        _stream(stream))
+    _check("lt2_looped_decode_step", code)
+    return h
 
 
 def lt2_hbm_copy(dst, src, stream=None):

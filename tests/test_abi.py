@@ -137,3 +137,26 @@ def test_looped_null_align_workspace():
     assert loop_call(d, ws_bytes=need - 1) == 5
     assert loop_call(d, ws=FAKE + 16, ws_bytes=need) == 6
     assert loop_call(good_loop(L=0), h_in=None, h_out=None, w_in=None, w_o=None, ws=None, ws_bytes=0) == 0
+
+
+def loop_decode_call(desc, h=FAKE, w_in=FAKE, w_o=FAKE, states=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    P = ctypes.c_void_p
+    return lt2.lib().lt2_looped_decode_step(ctypes.byref(desc), P(h), P(w_in), P(w_o), P(states), P(ws),
+                                            ws_bytes, None)
+
+
+def test_looped_decode_validation():
+    d = good_loop(L=1)
+    assert lt2.lib().lt2_looped_decode_step(None, None, None, None, None, None, 0, None) == 1
+    assert loop_decode_call(good_loop(L=2)) == 2                 # one token per call
+    assert lt2.lt2_looped_decode_workspace_size(good_loop(L=2)) == 0
+    assert loop_decode_call(good_loop(L=1, d_head=96)) == 4
+    assert loop_decode_call(d, states=None) == 1
+    assert loop_decode_call(d, h=FAKE + 4) == 6
+    need = lt2.lt2_looped_decode_workspace_size(d)
+    assert need > 0
+    assert loop_decode_call(d, ws_bytes=need - 1) == 5
+    assert loop_decode_call(d, ws=FAKE + 16, ws_bytes=need) == 6
+    # nothing to do: no sequences or no loops
+    assert loop_decode_call(good_loop(L=1, B=0), h=None, w_in=None, w_o=None, states=None, ws=None, ws_bytes=0) == 0
+    assert loop_decode_call(good_loop(L=1, T=0), h=None, w_in=None, w_o=None, states=None, ws=None, ws_bytes=0) == 0

@@ -70,3 +70,43 @@ def test_looped_full_size_prefix():
     ref = oracle.looped_mixer(h0[1:2, :P], w["w_in"], w["w_o"], shape.H, shape.d, shape.T)
     assert rel_err(got[1:2, :P], ref) <= TOL_BF16
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("B,L,D,H,d,T", [(2, 40, 256, 2, 128, 2), (3, 17, 128, 2, 64, 3)])
+def test_looped_decode_chain_matches_mixer(B, L, D, H, d, T):
+    """Token-by-token looped decode from zero states gives, for every token, the
+    h of the oracle's looped block on the whole sequence (each loop's mixer is
+    causal, so its state after token t is the prefill state after token t)."""
+    shape = synth.LoopShape(B, L, D, H, d, T)
+    announce(f"looped decode chain B={B} L={L} D={D} H={H} d={d} T={T}")
+    w = synth.loop_weights(shape, seed=4)
+    h0 = synth.loop_h0(shape, seed=4)
+    ref = oracle.looped_mixer(h0, w["w_in"], w["w_o"], H, d, T)
+    w_in = torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16)
+    w_o = torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)
+    states = torch.zeros((T, B, H, d, d), dtype=torch.float32, device="cuda")
+    got = np.empty_like(h0)
+    for t in range(L):
+        h = torch.from_numpy(np.ascontiguousarray(h0[:, t], np.float32)).to("cuda")
+        lt2.lt2_looped_decode_step(h, w_in, w_o, states, H, d, T)
+        got[:, t] = host(h)
+    torch.cuda.synchronize()
+    assert rel_err(got, ref) <= TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16
+
+
+def test_looped_decode_equals_mixer_on_gpu():
+    """Decode chain vs the GPU looped block on the same sequence (both bf16
+    GEMM inputs, fp32 state): agreement far inside the oracle bar."""
+    shape = synth.LoopShape(2, 24, 256, 2, 128, 2)
+    announce("looped decode vs GPU mixer")
+    w = synth.loop_weights(shape, seed=5)
+    h0 = synth.loop_h0(shape, seed=5)
+    full = run_looped(h0, w, shape)
+    w_in = torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16)
+    w_o = torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)
+    states = torch.zeros((2, 2, 2, 128, 128), dtype=torch.float32, device="cuda")
+    for t in range(shape.L):
+        h = torch.from_numpy(np.ascontiguousarray(h0[:, t], np.float32)).to("cuda")
+        lt2.lt2_looped_decode_step(h, w_in, w_o, states, 2, 128, 2)
+        assert rel_err(host(h), full[:, t]) <= TOL_BF16, t
