@@ -294,36 +294,40 @@ def bench_channel(args, torch, lt2, synth, reps=3):
                 tflops=flops / ms / 1e9, gbs=pbytes / ms / 1e6, ws_bytes=ws_bytes)
 
 
-def bench_looped(args, torch, lt2, synth, reps=5):
-    """T=4 loops of the LT2-linear block, B=2 L=8192 d_model=2048 H=16 d=128."""
+def bench_looped(args, torch, lt2, synth, reps=5, gate=False):
+    """T=4 loops of the LT2-linear block, B=2 L=8192 d_model=2048 H=16 d=128
+    (with ``gate``: the sigmoid output gate inside the loop)."""
     cfg = synth.CONFIGS[3]
     sh = cfg["shape"]
-    log(f"looped inputs B={sh.B} L={sh.L} D={sh.d_model} H={sh.H} d={sh.d} T={sh.T}")
-    w = synth.loop_weights(sh, seed=0)
+    log(f"looped inputs B={sh.B} L={sh.L} D={sh.d_model} H={sh.H} d={sh.d} T={sh.T} gate={gate}")
+    w = synth.loop_weights(sh, seed=0, gate=gate)
     h0 = torch.from_numpy(synth.loop_h0(sh, seed=0)).to("cuda")
     w_in = torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16)
     w_o = torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)
     h_out = torch.empty_like(h0)
-    desc = lt2.loop_desc(sh.B, sh.L, sh.d_model, sh.H, sh.d, sh.T, cfg["chunk"])
+    desc = lt2.loop_desc(sh.B, sh.L, sh.d_model, sh.H, sh.d, sh.T, cfg["chunk"], int(gate))
     ws_bytes = lt2.lt2_looped_mixer_workspace_size(desc)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    run = lambda: lt2.lt2_looped_mixer(h0, w_in, w_o, sh.H, sh.d, sh.T, chunk=cfg["chunk"], h_out=h_out,
+                                       workspace=ws, out_gate=gate)
     for _ in range(2):
-        lt2.lt2_looped_mixer(h0, w_in, w_o, sh.H, sh.d, sh.T, chunk=cfg["chunk"], h_out=h_out, workspace=ws)
+        run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        lt2.lt2_looped_mixer(h0, w_in, w_o, sh.H, sh.d, sh.T, chunk=cfg["chunk"], h_out=h_out, workspace=ws)
+        run()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    M, D, Hd, N_in = sh.B * sh.L, sh.d_model, sh.H * sh.d, 3 * sh.H * sh.d + 2 * sh.H
+    M, D, Hd = sh.B * sh.L, sh.d_model, sh.H * sh.d
+    N_in = (4 if gate else 3) * Hd + 2 * sh.H
     gemm_flops = sh.T * 2.0 * M * D * (N_in + Hd)
     C = cfg["chunk"]
     gdn_flops = sh.T * prefill_flops_bytes(sh.B, sh.L, sh.H, sh.d, C)["path_flops"]
     log(f"looped {ms:.3f} ms per call ({sh.T} loops)")
-    return dict(B=sh.B, L=sh.L, d_model=D, H=sh.H, d=sh.d, T=sh.T, ms=ms,
-                tokens_per_s_per_loop=M * sh.T / (ms / 1e3) / sh.T,
+    return dict(B=sh.B, L=sh.L, d_model=D, H=sh.H, d=sh.d, T=sh.T, out_gate=gate, ms=ms,
+                tokens_per_s_per_loop=M * sh.T / (ms / 1e3),
                 gemm_flops=gemm_flops, gdn_flops=gdn_flops,
                 tflops=(gemm_flops + gdn_flops) / ms / 1e9,
                 mfma_frac=(gemm_flops + gdn_flops) / ms / 1e9 / BF16_PEAK_TFLOPS)
@@ -431,6 +435,7 @@ def main():
     log(f"copy probe {copy['gbs']:.0f} GB/s")
     dec = None if args.no_decode else bench_decode(args, torch, lt2, synth)
     loo = None if args.no_looped else bench_looped(args, torch, lt2, synth)
+    loo_g = None if args.no_looped else bench_looped(args, torch, lt2, synth, gate=True)
     cha = None if args.no_channel else bench_channel(args, torch, lt2, synth)
     lde = None if args.no_looped_decode else bench_looped_decode(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
@@ -455,6 +460,8 @@ def main():
                                hbm_frac_span=dec["gbs_span"] / HBM_PEAK_GBS)
     if loo:
         extra["looped"] = loo
+    if loo_g:
+        extra["looped_output_gate"] = loo_g
     if cha:
         extra["channel_prefill"] = cha
     if lde:

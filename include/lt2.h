@@ -83,6 +83,7 @@ typedef struct lt2_loop_desc {
     int32_t H, d_head;   /* heads and head size (d_k = d_v = d_head) */
     int32_t T;           /* loops with shared weights */
     int32_t chunk;       /* prefill chunk length of the mixer */
+    int32_t out_gate;    /* 1: sigmoid output gate inside the loop (W_g rows in W_in), 0: none */
 } lt2_loop_desc;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -150,14 +151,18 @@ size_t lt2_looped_mixer_workspace_size(const lt2_loop_desc *desc);
 /*
  * T loops of the LT2-linear block with shared weights, fresh zero state in
  * every loop:
- *     z = bf16(h) W_in^T                      [B*L, 3*H*d + 2*H]
+ *     z = bf16(h) W_in^T                      [B*L, 3*H*d + 2*H] (+ H*d gated)
  *     q, k = per-head L2 normalisation of z's first two H*d blocks
  *            (x / max(||x||_2, 1e-6)), v = third block
  *     beta = sigmoid(z_beta), alpha = exp(-softplus(z_alpha))  (one per head)
  *     o = gated-delta prefill(q, k, v, alpha, beta; S_0 = 0)    bf16
+ *     desc->out_gate: o = o * sigmoid(z_g), z_g the fourth H*d block (the
+ *            sigmoid output gate the LT2 explainer places inside the loop)
  *     h = h + o W_o^T                          fp32 residual stream
  *   h_in, h_out   [B, L, d_model] fp32 (may be the same buffer)
- *   W_in          [3*H*d + 2*H, d_model] bf16, rows W_q, W_k, W_v, W_beta, W_alpha
+ *   W_in          [3*H*d + 2*H, d_model] bf16, rows W_q, W_k, W_v, W_beta, W_alpha;
+ *                 with out_gate [4*H*d + 2*H, d_model], rows W_q, W_k, W_v, W_g,
+ *                 W_beta, W_alpha
  *   W_o           [d_model, H*d] bf16
  * Requirements: d_model % 128 == 0, H*d % 128 == 0, d in {64, 128}.
  */
@@ -178,7 +183,7 @@ size_t lt2_looped_decode_workspace_size(const lt2_loop_desc *desc);
  * the T loops of lt2_looped_mixer applied to the new token, loop t carrying
  * its own state across calls.  desc->L must be 1.
  *   h        [B, d_model] fp32, the token's residual stream, updated in place
- *   W_in     [3*H*d + 2*H, d_model] bf16, as for lt2_looped_mixer
+ *   W_in     as for lt2_looped_mixer (with W_g rows when desc->out_gate)
  *   W_o      [d_model, H*d] bf16
  *   states   [T, B, H, d_head, d_head] fp32, loop t's state of every (b, h),
  *            updated in place; zero before a sequence's first token

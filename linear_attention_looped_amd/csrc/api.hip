@@ -158,6 +158,7 @@ lt2_status check_loop(const lt2_loop_desc *d) {
     if (d->B < 0 || d->L < 0 || d->T < 0 || d->d_model <= 0 || d->H <= 0 || d->d_head <= 0) return LT2_ERR_SHAPE;
     if (d->d_head != 64 && d->d_head != 128) return LT2_ERR_UNSUPPORTED;
     if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return LT2_ERR_UNSUPPORTED;
+    if (d->out_gate != 0 && d->out_gate != 1) return LT2_ERR_UNSUPPORTED;
     // GEMM tiles: K-tiles of 64, residual and head blocks whole 128-column tiles
     if (d->d_model % 128 != 0 || ((int64_t)d->H * d->d_head) % 128 != 0) return LT2_ERR_UNSUPPORTED;
     if ((int64_t)d->B * d->L > 0x7fffffffLL || (int64_t)d->H * d->d_head > 65536 || d->H > 65535 || d->B > 65535)
@@ -172,7 +173,7 @@ extern "C" {
 size_t lt2_looped_mixer_workspace_size(const lt2_loop_desc *desc) {
     if (check_loop(desc) != LT2_OK) return 0;
     if (desc->B == 0 || desc->L == 0) return 0;
-    return loop_layout(desc->B, desc->L, desc->d_model, desc->H, desc->d_head, desc->chunk).total;
+    return loop_layout(desc->B, desc->L, desc->d_model, desc->H, desc->d_head, desc->chunk, desc->out_gate).total;
 }
 
 lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *h_in, float *h_out, const void *W_in,
@@ -182,13 +183,14 @@ lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *h_in, float 
     const bool work = desc->B > 0 && desc->L > 0;
     if (work && (!h_in || !h_out || !W_in || !W_o)) return LT2_ERR_NULL;
     if (!aligned(h_in, 16) || !aligned(h_out, 16) || !aligned(W_in, 16) || !aligned(W_o, 16)) return LT2_ERR_ALIGN;
-    const size_t need = work ? loop_layout(desc->B, desc->L, desc->d_model, desc->H, desc->d_head, desc->chunk).total : 0;
+    const size_t need =
+        work ? loop_layout(desc->B, desc->L, desc->d_model, desc->H, desc->d_head, desc->chunk, desc->out_gate).total : 0;
     if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
     if (need > 0 && !aligned(ws, 256)) return LT2_ERR_ALIGN;
     if (!work) return LT2_OK;
     LoopArgs a;
     a.B = desc->B; a.L = desc->L; a.D = desc->d_model; a.H = desc->H; a.d = desc->d_head; a.T = desc->T;
-    a.chunk = desc->chunk; a.h_in = h_in; a.h_out = h_out;
+    a.chunk = desc->chunk; a.gated = desc->out_gate; a.h_in = h_in; a.h_out = h_out;
     a.W_in = static_cast<const uint16_t *>(W_in); a.W_o = static_cast<const uint16_t *>(W_o); a.ws = ws;
     return hip_status(launch_looped(a, (hipStream_t)stream));
 }
@@ -196,7 +198,7 @@ lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *h_in, float 
 size_t lt2_looped_decode_workspace_size(const lt2_loop_desc *desc) {
     if (check_loop(desc) != LT2_OK || desc->L != 1) return 0;
     if (desc->B == 0) return 0;
-    return loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head).total;
+    return loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head, desc->out_gate).total;
 }
 
 lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const void *W_in, const void *W_o,
@@ -207,13 +209,13 @@ lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const voi
     const bool work = desc->B > 0 && desc->T > 0;
     if (work && (!h || !W_in || !W_o || !states)) return LT2_ERR_NULL;
     if (!aligned(h, 16) || !aligned(W_in, 16) || !aligned(W_o, 16) || !aligned(states, 16)) return LT2_ERR_ALIGN;
-    const size_t need = work ? loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head).total : 0;
+    const size_t need = work ? loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head, desc->out_gate).total : 0;
     if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
     if (need > 0 && !aligned(ws, 256)) return LT2_ERR_ALIGN;
     if (!work) return LT2_OK;
     LoopDecodeArgs a;
     a.B = desc->B; a.D = desc->d_model; a.H = desc->H; a.d = desc->d_head; a.T = desc->T;
-    a.h = h; a.W_in = static_cast<const uint16_t *>(W_in); a.W_o = static_cast<const uint16_t *>(W_o);
+    a.gated = desc->out_gate; a.h = h; a.W_in = static_cast<const uint16_t *>(W_in); a.W_o = static_cast<const uint16_t *>(W_o);
     a.states = states; a.ws = ws;
     return hip_status(launch_looped_decode(a, (hipStream_t)stream));
 }

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const TI *__restrict__ 
                                                          const TI *__restrict__ v,
                                                          const float *__restrict__ alpha,
                                                          const float *__restrict__ beta,
-                                                         float *__restrict__ state, TO *__restrict__ out) {
+                                                         float *__restrict__ state, TO *__restrict__ out,
+                                                         const uint16_t *__restrict__ gate) {
     constexpr int CG = DV / 4;     // float4 column groups per row
     constexpr int RG = 256 / CG;   // row groups
     constexpr int RPT = DK / RG;   // rows per lane
@@ -118,6 +119,10 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const TI *__restrict__ 
         o.y = qS.y - cq * kS.y + cv * vv.y;
         o.z = qS.z - cq * kS.z + cv * vv.z;
         o.w = qS.w - cq * kS.w + cv * vv.w;
+        if (gate) {   // output gate of the looped block: o * sigmoid(z_g), bf16 gate values
+            const float4 gv = load4<uint16_t>(gate + u * DV + 4 * cg);
+            o.x *= gv.x; o.y *= gv.y; o.z *= gv.z; o.w *= gv.w;
+        }
         store4<TO>(out + u * DV + 4 * cg, o);
     }
 #pragma unroll
@@ -138,7 +143,7 @@ static hipError_t dec(const GdnArgs &a, hipStream_t s) {
     const unsigned units = (unsigned)a.B * (unsigned)a.H;
     hipLaunchKernelGGL((gdn_decode_kernel<D, D, CH, TI, TO>), dim3(units), dim3(256), 0, s,
                        (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, a.alpha, a.beta, a.state_out,
-                       (TO *)a.out);
+                       (TO *)a.out, a.gate);
     return hipGetLastError();
 }
 

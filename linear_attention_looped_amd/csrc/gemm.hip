@@ -19,8 +19,9 @@
 // Epilogues (fused into the store):
 //   EPI_PROJ  input projection of the looped block: columns [0, H*d) -> q and
 //             [H*d, 2H*d) -> k, each L2-normalised per head (x / max(|x|, 1e-6))
-//             and stored bf16; [2H*d, 3H*d) -> v (bf16); [3H*d, 3H*d + H) ->
-//             beta = sigmoid(z); [3H*d + H, 3H*d + 2H) -> alpha = exp(-softplus(z))
+//             and stored bf16; [2H*d, 3H*d) -> v (bf16); with the output gate
+//             [3H*d, 4H*d) -> g = sigmoid(z) (bf16); the next H columns ->
+//             beta = sigmoid(z), the H after them -> alpha = exp(-softplus(z))
 //             (both fp32, one per head).
 //   EPI_RESID residual update h[m][n] += C[m][n] (fp32), and xb[m][n] = bf16(h),
 //             the next loop's GEMM input.
@@ -37,6 +38,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 struct ProjOut {
     uint16_t *q, *k, *v;   // [M, H*d] bf16
+    uint16_t *g;           // [M, H*d] bf16 output gate, or nullptr
     float *beta, *alpha;   // [M, H]
     int H, d;
 };
@@ -155,10 +157,11 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     const int nw = n0 + 128 * wn;   // first column of this wave
     if constexpr (EPI == EPI_PROJ) {
         const int Hd = po.H * po.d;
-        if (nw < 3 * Hd) {
-            // q, k or v columns; the wave's 128 columns hold whole heads (Hd % 128 == 0)
-            const int region = nw / Hd;             // 0 q, 1 k, 2 v
-            uint16_t *dst = region == 0 ? po.q : (region == 1 ? po.k : po.v);
+        const int NR = po.g ? 4 : 3;                // head-width column blocks before the gates
+        if (nw < NR * Hd) {
+            // q, k, v or g columns; the wave's 128 columns hold whole heads (Hd % 128 == 0)
+            const int region = nw / Hd;             // 0 q, 1 k, 2 v, 3 g
+            uint16_t *dst = region == 0 ? po.q : (region == 1 ? po.k : (region == 2 ? po.v : po.g));
             const int c0 = nw - region * Hd;
             constexpr int TPH = DH / 32;            // 32-column tiles per head
 #pragma unroll
@@ -186,8 +189,10 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
                     }
                     if (m < M) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            dst[(size_t)m * Hd + c0 + 32 * j + l32] = bf16_bits(acc[i][j][r] * scale[j]);
+                        for (int j = 0; j < 4; ++j) {
+                            const float x = acc[i][j][r] * scale[j];
+                            dst[(size_t)m * Hd + c0 + 32 * j + l32] = bf16_bits(region == 3 ? sigmoidf_acc(x) : x);
+                        }
                     }
                 }
             }
@@ -197,7 +202,7 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int c = nw + 32 * j + l32 - 3 * Hd;
+                    const int c = nw + 32 * j + l32 - NR * Hd;
                     if (c >= 2 * po.H) continue;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -232,8 +237,8 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 }  // namespace
 
 hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, int K, uint16_t *q, uint16_t *k,
-                            uint16_t *v, float *beta, float *alpha, int H, int d, hipStream_t s) {
-    ProjOut po{q, k, v, beta, alpha, H, d};
+                            uint16_t *v, uint16_t *g, float *beta, float *alpha, int H, int d, hipStream_t s) {
+    ProjOut po{q, k, v, g, beta, alpha, H, d};
     ResidOut ro{nullptr, nullptr};
     const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
     if (d == 64)

@@ -16,6 +16,9 @@ struct GdnArgs {
     void *out;
     float *state_out;
     void *ws;
+    // Looped block only: bf16 output gate (same layout as out), multiplied into
+    // the output by the scalar-gate bf16 scan and the decode step; nullptr = none.
+    const uint16_t *gate = nullptr;
 };
 
 // Each launcher returns hipSuccess or the launch error; shapes are already
@@ -33,7 +36,7 @@ hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 
 // Looped LT2-linear block.
 struct LoopArgs {
-    int B, L, D, H, d, T, chunk;
+    int B, L, D, H, d, T, chunk, gated;
     const float *h_in;
     float *h_out;
     const uint16_t *W_in, *W_o;
@@ -41,20 +44,20 @@ struct LoopArgs {
 };
 // Byte offsets of the looped block's buffers inside its workspace.
 struct LoopLayout {
-    size_t xb, q, k, v, beta, alpha, o, prefill, total;
+    size_t xb, q, k, v, g, beta, alpha, o, prefill, total;
 };
-LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk);
+LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk, bool gated);
 hipError_t launch_looped(const LoopArgs &a, hipStream_t s);
 
 // Looped decode: one token per sequence, T loop states carried in place.
 struct LoopDecodeArgs {
-    int B, D, H, d, T;
+    int B, D, H, d, T, gated;
     float *h;                // [B, D] fp32, in place
     const uint16_t *W_in, *W_o;
     float *states;           // [T, B, H, d, d] fp32, in place
     void *ws;
 };
-LoopLayout loop_decode_layout(int B, int D, int H, int d);
+LoopLayout loop_decode_layout(int B, int D, int H, int d, bool gated);
 hipError_t launch_looped_decode(const LoopDecodeArgs &a, hipStream_t s);
 hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t s);
 

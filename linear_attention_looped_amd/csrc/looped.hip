@@ -4,6 +4,8 @@
 //   xb = bf16(h)                                    (cast kernel, first loop only)
 //   [q|k|v|beta|alpha] = xb W_in^T  + per-head L2 norm and gate transforms (GEMM)
 //   o = gated-delta prefill(q, k, v, alpha, beta; S_0 = 0), bf16
+//   optional output gate (the explainer's sigmoid gate inside the loop):
+//   o = o * sigmoid(xb W_g^T), one gate per channel, applied where o is stored
 //   h += o W_o^T, xb = bf16(h)                      (GEMM with residual epilogue)
 // All launches are enqueued on one stream; nothing synchronises in between.
 //
@@ -21,7 +23,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
-LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk) {
+LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk, bool gated) {
     LoopLayout w{};
     const size_t M = (size_t)B * L, Hd = (size_t)H * d;
     size_t off = 0;
@@ -29,6 +31,7 @@ LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk) {
     w.q = off; off = align256(off + M * Hd * 2);
     w.k = off; off = align256(off + M * Hd * 2);
     w.v = off; off = align256(off + M * Hd * 2);
+    w.g = off; off = align256(off + (gated ? M * Hd * 2 : 0));
     w.beta = off; off = align256(off + M * H * 4);
     w.alpha = off; off = align256(off + M * H * 4);
     w.o = off; off = align256(off + M * Hd * 2);
@@ -37,7 +40,7 @@ LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk) {
     return w;
 }
 
-LoopLayout loop_decode_layout(int B, int D, int H, int d) {
+LoopLayout loop_decode_layout(int B, int D, int H, int d, bool gated) {
     LoopLayout w{};
     const size_t M = (size_t)B, Hd = (size_t)H * d;
     size_t off = 0;
@@ -45,6 +48,7 @@ LoopLayout loop_decode_layout(int B, int D, int H, int d) {
     w.q = off; off = align256(off + M * Hd * 2);
     w.k = off; off = align256(off + M * Hd * 2);
     w.v = off; off = align256(off + M * Hd * 2);
+    w.g = off; off = align256(off + (gated ? M * Hd * 2 : 0));
     w.beta = off; off = align256(off + M * H * 4);
     w.alpha = off; off = align256(off + M * H * 4);
     w.o = off; off = align256(off + M * Hd * 2);
@@ -54,9 +58,10 @@ LoopLayout loop_decode_layout(int B, int D, int H, int d) {
 }
 
 hipError_t launch_looped_decode(const LoopDecodeArgs &a, hipStream_t s) {
-    const int M = a.B, Hd = a.H * a.d, N_in = 3 * Hd + 2 * a.H;
+    const int M = a.B, Hd = a.H * a.d, N_in = (a.gated ? 4 : 3) * Hd + 2 * a.H;
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
-    const LoopLayout w = loop_decode_layout(a.B, a.D, a.H, a.d);
+    const LoopLayout w = loop_decode_layout(a.B, a.D, a.H, a.d, a.gated);
+    uint16_t *gt = a.gated ? reinterpret_cast<uint16_t *>(ws + w.g) : nullptr;
     uint16_t *xb = reinterpret_cast<uint16_t *>(ws + w.xb);
     uint16_t *q = reinterpret_cast<uint16_t *>(ws + w.q);
     uint16_t *k = reinterpret_cast<uint16_t *>(ws + w.k);
@@ -70,10 +75,10 @@ hipError_t launch_looped_decode(const LoopDecodeArgs &a, hipStream_t s) {
     GdnArgs g{};
     g.B = a.B; g.L = 1; g.H = a.H; g.dk = a.d; g.dv = a.d; g.chunk = 64;
     g.qkv_bf16 = 1; g.out_bf16 = 1; g.channel = 0;
-    g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta; g.out = o;
+    g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta; g.out = o; g.gate = gt;
     const size_t state_elems = (size_t)a.B * a.H * a.d * a.d;
     for (int t = 0; t < a.T; ++t) {
-        e = launch_gemm_proj(xb, a.W_in, M, N_in, a.D, q, k, v, beta, alpha, a.H, a.d, s);
+        e = launch_gemm_proj(xb, a.W_in, M, N_in, a.D, q, k, v, gt, beta, alpha, a.H, a.d, s);
         if (e != hipSuccess) return e;
         g.state_in = a.states + (size_t)t * state_elems;
         g.state_out = a.states + (size_t)t * state_elems;
@@ -86,9 +91,10 @@ hipError_t launch_looped_decode(const LoopDecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_looped(const LoopArgs &a, hipStream_t s) {
-    const int M = a.B * a.L, Hd = a.H * a.d, N_in = 3 * Hd + 2 * a.H;
+    const int M = a.B * a.L, Hd = a.H * a.d, N_in = (a.gated ? 4 : 3) * Hd + 2 * a.H;
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
-    const LoopLayout w = loop_layout(a.B, a.L, a.D, a.H, a.d, a.chunk);
+    const LoopLayout w = loop_layout(a.B, a.L, a.D, a.H, a.d, a.chunk, a.gated);
+    uint16_t *gt = a.gated ? reinterpret_cast<uint16_t *>(ws + w.g) : nullptr;
     uint16_t *xb = reinterpret_cast<uint16_t *>(ws + w.xb);
     uint16_t *q = reinterpret_cast<uint16_t *>(ws + w.q);
     uint16_t *k = reinterpret_cast<uint16_t *>(ws + w.k);
@@ -103,9 +109,9 @@ hipError_t launch_looped(const LoopArgs &a, hipStream_t s) {
     g.B = a.B; g.L = a.L; g.H = a.H; g.dk = a.d; g.dv = a.d; g.chunk = a.chunk;
     g.qkv_bf16 = 1; g.out_bf16 = 1; g.channel = 0;
     g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta;
-    g.state_in = nullptr; g.out = o; g.state_out = nullptr; g.ws = ws + w.prefill;
+    g.state_in = nullptr; g.out = o; g.state_out = nullptr; g.ws = ws + w.prefill; g.gate = gt;
     for (int t = 0; t < a.T; ++t) {
-        e = launch_gemm_proj(xb, a.W_in, M, N_in, a.D, q, k, v, beta, alpha, a.H, a.d, s);
+        e = launch_gemm_proj(xb, a.W_in, M, N_in, a.D, q, k, v, gt, beta, alpha, a.H, a.d, s);
         if (e != hipSuccess) return e;
         e = launch_prefill_head(g, PHASE_ALL, s);
         if (e != hipSuccess) return e;

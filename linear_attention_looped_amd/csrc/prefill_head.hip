@@ -586,6 +586,33 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
 typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
+// 16 bytes of staged outputs times their gate values: 8 bf16 outputs times 8
+// bf16 gates, or 4 fp32 outputs times the 4 bf16 gates in the first 8 bytes.
+template <typename TO>
+__device__ __forceinline__ u32x4 gate_outputs(u32x4 x, u32x4 g);
+template <>
+__device__ __forceinline__ u32x4 gate_outputs<uint16_t>(u32x4 x, u32x4 g) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(x[i] << 16) * __uint_as_float(g[i] << 16);
+        const float hi = __uint_as_float(x[i] & 0xFFFF0000u) * __uint_as_float(g[i] & 0xFFFF0000u);
+        r[i] = (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+    }
+    return r;
+}
+template <>
+__device__ __forceinline__ u32x4 gate_outputs<float>(u32x4 x, u32x4 g) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t gw = g[i / 2];
+        const float gv = __uint_as_float((i & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
+        r[i] = __float_as_uint(__uint_as_float(x[i]) * gv);
+    }
+    return r;
+}
+
 template <int DK, int DV, int BV, int C, typename TO>
 __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__restrict__ q,
                                                              const uint16_t *__restrict__ k,
@@ -593,7 +620,8 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                                                              const unsigned char *__restrict__ ws,
                                                              const float *__restrict__ state_in,
                                                              TO *__restrict__ out, float *__restrict__ state_out,
-                                                             int L, int H, int NC) {
+                                                             int L, int H, int NC,
+                                                             const uint16_t *__restrict__ gate) {
     constexpr int NW = 8, NTH = 64 * NW;
     constexpr int KP = DK + 16;  // bf16 pitch of K, Q and S^T rows (16-byte aligned, staggered banks)
     constexpr int CP = C + 16;   // bf16 pitch of Tm, P, R^T, U^T, U2^T rows
@@ -645,6 +673,7 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
     const uint16_t *qb_ptr = q + ((size_t)b * L * H + h) * DK;
     const uint16_t *vb_ptr = v + ((size_t)b * L * H + h) * DV + v0;
     TO *ob_ptr = out + ((size_t)b * L * H + h) * DV + v0;
+    const uint16_t *gb_ptr = gate ? gate + ((size_t)b * L * H + h) * DV + v0 : nullptr;
     // transpose-read lane roles: e = token offset, m = channel quad (see above)
     const int tr_e = (lane & 15) >> 2, tr_m = lane & 3, tr_g = lane >> 4;
 
@@ -717,9 +746,22 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
     };
     auto store_o = [&](int n, int rows) __attribute__((always_inline)) {   // staged outputs of chunk n
         if ((NO == NTH || wave < NO / 64) && orow < rows) {
+            const unsigned off = (unsigned)orow * vtok_stride + (unsigned)ocol;
             TO *oc = ob_ptr + (size_t)n * C * vtok_stride;
-            *reinterpret_cast<u32x4 *>(oc + (unsigned)orow * vtok_stride + (unsigned)ocol) =
-                *reinterpret_cast<const u32x4 *>(&Os[orow * OP + ocol]);
+            u32x4 x = *reinterpret_cast<const u32x4 *>(&Os[orow * OP + ocol]);
+            if (gb_ptr) {   // output gate of the looped block: o * sigmoid(z_g), bf16 gate values
+                const uint16_t *gp = gb_ptr + (size_t)n * C * vtok_stride + off;   // OV gate values
+                u32x4 gu = {0u, 0u, 0u, 0u};
+                if constexpr (OV == 8) {
+                    gu = *reinterpret_cast<const u32x4 *>(gp);
+                } else {
+                    const uint2 g2 = *reinterpret_cast<const uint2 *>(gp);
+                    gu[0] = g2.x;
+                    gu[1] = g2.y;
+                }
+                x = gate_outputs<TO>(x, gu);
+            }
+            *reinterpret_cast<u32x4 *>(oc + off) = x;
         }
     };
     auto store_split = [&](uint16_t *hi, uint16_t *lo, int off, const float x[4]) __attribute__((always_inline)) {
@@ -907,7 +949,8 @@ static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
         if constexpr (PREC == PREC_BF16) {
             hipLaunchKernelGGL((scan_head_bf16_kernel<D, D, BV, C, TO>), dim3(units * (D / BV)), dim3(512), 0, s,
                                (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                               (const unsigned char *)a.ws, a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC);
+                               (const unsigned char *)a.ws, a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC,
+                               a.gate);
         } else {
             hipLaunchKernelGGL((scan_head_kernel<D, D, BV, C, PREC, TI, TO>), dim3(units * (D / BV)), dim3(256), 0, s,
                                (const TI *)a.q, (const TI *)a.k, (const TI *)a.v, (const float *)a.ws, a.state_in,

@@ -27,7 +27,7 @@ class lt2_gdn_desc(ctypes.Structure):
 
 
 class lt2_loop_desc(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "d_model", "H", "d_head", "T", "chunk")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "d_model", "H", "d_head", "T", "chunk", "out_gate")]
 
 
 class Lt2Error(RuntimeError):
@@ -169,8 +169,8 @@ def lt2_gdn_decode_step(q, k, v, alpha, beta, state, out=None, stream=None):
     return out
 
 
-def loop_desc(B, L, d_model, H, d_head, T, chunk=64):
-    return lt2_loop_desc(B, L, d_model, H, d_head, T, chunk)
+def loop_desc(B, L, d_model, H, d_head, T, chunk=64, out_gate=0):
+    return lt2_loop_desc(B, L, d_model, H, d_head, T, chunk, out_gate)
 
 
 def lt2_looped_mixer_workspace_size(desc: lt2_loop_desc) -> int:
@@ -178,16 +178,18 @@ def lt2_looped_mixer_workspace_size(desc: lt2_loop_desc) -> int:
 
 
 def lt2_looped_mixer(h_in, W_in, W_o, H: int, d_head: int, T: int, chunk: int = 64, h_out=None,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, out_gate: bool = False):
     """T shared-weight loops of the LT2-linear block.  h_in [B,L,D] fp32,
-    W_in [3*H*d + 2*H, D] bf16, W_o [D, H*d] bf16.  Returns h_out [B,L,D] fp32."""
+    W_in [3*H*d + 2*H, D] bf16 ([4*H*d + 2*H, D] with the output gate),
+    W_o [D, H*d] bf16.  Returns h_out [B,L,D] fp32."""
     B, L, D = h_in.shape
     _need(h_in, "h_in", torch.float32)
     _need(W_in, "W_in", torch.bfloat16)
     _need(W_o, "W_o", torch.bfloat16)
     if h_out is None:
         h_out = torch.empty_like(h_in)
-    desc = loop_desc(B, L, D, H, d_head, T, chunk)
+    assert W_in.shape[0] == (4 if out_gate else 3) * H * d_head + 2 * H, W_in.shape
+    desc = loop_desc(B, L, D, H, d_head, T, chunk, int(out_gate))
     ws_bytes = lt2_looped_mixer_workspace_size(desc)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=h_in.device)
@@ -203,7 +205,8 @@ def lt2_looped_decode_workspace_size(desc: lt2_loop_desc) -> int:
     return int(lib().lt2_looped_decode_workspace_size(ctypes.byref(desc)))
 
 
-def lt2_looped_decode_step(h, W_in, W_o, states, H: int, d_head: int, T: int, workspace=None, stream=None):
+def lt2_looped_decode_step(h, W_in, W_o, states, H: int, d_head: int, T: int, workspace=None, stream=None,
+                           out_gate: bool = False):
     """One decode token of the looped block for each of B sequences.  h [B,D]
     fp32 and states [T,B,H,d,d] fp32 are updated in place; W_in, W_o as for
     lt2_looped_mixer.  Returns h."""
@@ -213,7 +216,8 @@ def lt2_looped_decode_step(h, W_in, W_o, states, H: int, d_head: int, T: int, wo
     _need(W_in, "W_in", torch.bfloat16)
     _need(W_o, "W_o", torch.bfloat16)
     assert tuple(states.shape) == (T, B, H, d_head, d_head), states.shape
-    desc = loop_desc(B, 1, D, H, d_head, T, 64)
+    assert W_in.shape[0] == (4 if out_gate else 3) * H * d_head + 2 * H, W_in.shape
+    desc = loop_desc(B, 1, D, H, d_head, T, 64, int(out_gate))
     ws_bytes = lt2_looped_decode_workspace_size(desc)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=h.device)

@@ -28,7 +28,7 @@ import numpy as np
 
 # stream tags
 T_Q, T_K, T_V, T_BETA, T_ALPHA = 1, 2, 3, 4, 5
-T_H0, T_WIN, T_WO = 6, 7, 8
+T_H0, T_WIN, T_WO, T_WG = 6, 7, 8, 9
 T_DQ, T_DK, T_DV, T_DBETA, T_DALPHA = 11, 12, 13, 14, 15
 
 
@@ -168,15 +168,19 @@ class LoopShape:
     T: int
 
 
-def loop_weights(shape: LoopShape, seed: int = 0) -> dict:
+def loop_weights(shape: LoopShape, seed: int = 0, gate: bool = False) -> dict:
     """bf16-valued weights in the [d_out, d_in] convention (y = x W^T):
-    W_in [3*H*d + 2*H, d_model] = rows of W_q, W_k, W_v, W_beta, W_alpha;
-    W_o [d_model, H*d].  Entries N(0, 1/d_model)."""
+    W_in [3*H*d + 2*H, d_model] = rows of W_q, W_k, W_v, W_beta, W_alpha, or with
+    ``gate`` [4*H*d + 2*H, d_model] with W_g (its own stream) after W_v; the other
+    rows are the same draws either way.  W_o [d_model, H*d].  Entries N(0, 1/d_in)."""
     D, H, d = shape.d_model, shape.H, shape.d
     n_in = 3 * H * d + 2 * H
     s = 1.0 / np.sqrt(D)
     w_in = rng(seed, T_WIN).standard_normal((n_in, D), dtype=np.float32) * np.float32(s)
     w_o = rng(seed, T_WO).standard_normal((D, H * d), dtype=np.float32) * np.float32(1.0 / np.sqrt(H * d))
+    if gate:
+        w_g = rng(seed, T_WG).standard_normal((H * d, D), dtype=np.float32) * np.float32(s)
+        w_in = np.concatenate([w_in[:3 * H * d], w_g, w_in[3 * H * d:]], axis=0)
     return dict(w_in=bf16_round(w_in), w_o=bf16_round(w_o))
 
 

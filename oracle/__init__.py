@@ -127,16 +127,18 @@ def _softplus(z):
     return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
 
 
-def looped_layer(h, w_in, w_o, H: int, d: int, threads: int = 0):
+def looped_layer(h, w_in, w_o, H: int, d: int, threads: int = 0, gate: bool = False):
     """One loop iteration of the LT2-linear block on a residual stream h [B,L,D]:
 
-        z = h W_in^T;  q,k,v,z_beta,z_alpha = split(z)
+        z = h W_in^T;  q,k,v(,z_g),z_beta,z_alpha = split(z)
         q, k <- per-head L2 normalisation;  beta = sigmoid(z_beta);
         alpha = exp(-softplus(z_alpha));  o = GDN(q,k,v,alpha,beta; S_0 = 0)
+        gate (LT2 explainer, the sigmoid output gate inside the loop):
+            o <- o * sigmoid(z_g), elementwise, one gate per channel of each head
         h <- h + o W_o^T
 
-    W_in is [3*H*d + 2*H, D] (rows of W_q, W_k, W_v, W_beta, W_alpha), W_o is
-    [D, H*d].  Everything in fp64."""
+    W_in is [3*H*d + 2*H, D] (rows of W_q, W_k, W_v, W_beta, W_alpha) or, with
+    the gate, [4*H*d + 2*H, D] (W_g after W_v); W_o is [D, H*d].  fp64."""
     h = _f64(h)
     B, L, D = h.shape
     hd = H * d
@@ -145,16 +147,20 @@ def looped_layer(h, w_in, w_o, H: int, d: int, threads: int = 0):
     q = _l2norm_heads(z[:, 0:hd], H, d)
     k = _l2norm_heads(z[:, hd:2 * hd], H, d)
     v = z[:, 2 * hd:3 * hd]
-    beta = _sigmoid(z[:, 3 * hd:3 * hd + H])
-    alpha = np.exp(-_softplus(z[:, 3 * hd + H:3 * hd + 2 * H]))
+    gb = 4 * hd if gate else 3 * hd   # first gate-transform column
+    beta = _sigmoid(z[:, gb:gb + H])
+    alpha = np.exp(-_softplus(z[:, gb + H:gb + 2 * H]))
     o, _ = prefill(q.reshape(B, L, H, d), k.reshape(B, L, H, d), v.reshape(B, L, H, d),
                    alpha.reshape(B, L, H), beta.reshape(B, L, H), None, threads)
-    return h + (o.reshape(B * L, hd) @ _f64(w_o).T).reshape(B, L, D)
+    o = o.reshape(B * L, hd)
+    if gate:
+        o = o * _sigmoid(z[:, 3 * hd:4 * hd])
+    return h + (o @ _f64(w_o).T).reshape(B, L, D)
 
 
-def looped_mixer(h0, w_in, w_o, H: int, d: int, T: int, threads: int = 0):
+def looped_mixer(h0, w_in, w_o, H: int, d: int, T: int, threads: int = 0, gate: bool = False):
     """T loops of ``looped_layer`` with the same weights, h^(tau) = F(h^(tau-1))."""
     h = _f64(h0)
     for _ in range(T):
-        h = looped_layer(h, w_in, w_o, H, d, threads)
+        h = looped_layer(h, w_in, w_o, H, d, threads, gate)
     return h

@@ -114,14 +114,14 @@ def loop_call(desc, h_in=FAKE, h_out=FAKE, w_in=FAKE, w_o=FAKE, ws=FAKE, ws_byte
 
 
 def good_loop(**kw):
-    d = dict(B=2, L=100, d_model=256, H=2, d_head=128, T=2, chunk=64)
+    d = dict(B=2, L=100, d_model=256, H=2, d_head=128, T=2, chunk=64, out_gate=0)
     d.update(kw)
     return lt2.lt2_loop_desc(*[d[n] for n, _ in lt2.lt2_loop_desc._fields_])
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), 2), (dict(T=-1), 2), (dict(H=0), 2), (dict(d_head=96), 4), (dict(chunk=8), 4),
-    (dict(d_model=192), 4), (dict(H=1, d_head=64), 4),
+    (dict(d_model=192), 4), (dict(H=1, d_head=64), 4), (dict(out_gate=2), 4),
 ])
 def test_looped_rejects_bad_descriptor(kw, code):
     assert loop_call(good_loop(**kw)) == code
@@ -160,3 +160,9 @@ def test_looped_decode_validation():
     # nothing to do: no sequences or no loops
     assert loop_decode_call(good_loop(L=1, B=0), h=None, w_in=None, w_o=None, states=None, ws=None, ws_bytes=0) == 0
     assert loop_decode_call(good_loop(L=1, T=0), h=None, w_in=None, w_o=None, states=None, ws=None, ws_bytes=0) == 0
+
+
+def test_looped_gate_adds_workspace():
+    assert lt2.lt2_looped_mixer_workspace_size(good_loop(out_gate=1)) > lt2.lt2_looped_mixer_workspace_size(good_loop())
+    assert (lt2.lt2_looped_decode_workspace_size(good_loop(L=1, out_gate=1)) >
+            lt2.lt2_looped_decode_workspace_size(good_loop(L=1)))

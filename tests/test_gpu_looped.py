@@ -15,11 +15,11 @@ from gpu_util import TOL_BF16, announce, host, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def run_looped(h0, w, shape, chunk=64):
+def run_looped(h0, w, shape, chunk=64, gate=False):
     h = torch.from_numpy(np.ascontiguousarray(h0, np.float32)).to("cuda")
     w_in = torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16)
     w_o = torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)
-    out = lt2.lt2_looped_mixer(h, w_in, w_o, shape.H, shape.d, shape.T, chunk=chunk)
+    out = lt2.lt2_looped_mixer(h, w_in, w_o, shape.H, shape.d, shape.T, chunk=chunk, out_gate=gate)
     torch.cuda.synchronize()
     return host(out)
 
@@ -110,3 +110,34 @@ def test_looped_decode_equals_mixer_on_gpu():
         h = torch.from_numpy(np.ascontiguousarray(h0[:, t], np.float32)).to("cuda")
         lt2.lt2_looped_decode_step(h, w_in, w_o, states, 2, 128, 2)
         assert rel_err(host(h), full[:, t]) <= TOL_BF16, t
+
+
+@pytest.mark.parametrize("B,L,D,H,d,T", [(2, 200, 256, 2, 128, 2), (1, 150, 128, 2, 64, 3)])
+def test_looped_output_gate(B, L, D, H, d, T):
+    """Looped block with the sigmoid output gate inside the loop."""
+    shape = synth.LoopShape(B, L, D, H, d, T)
+    announce(f"gated looped B={B} L={L} D={D} H={H} d={d} T={T}")
+    w = synth.loop_weights(shape, seed=6, gate=True)
+    h0 = synth.loop_h0(shape, seed=6)
+    got = run_looped(h0, w, shape, gate=True)
+    ref = oracle.looped_mixer(h0, w["w_in"], w["w_o"], H, d, T, gate=True)
+    assert rel_err(got, ref) <= TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16
+
+
+def test_gated_looped_decode_chain_matches_mixer():
+    shape = synth.LoopShape(2, 20, 256, 2, 128, 2)
+    announce("gated looped decode chain")
+    w = synth.loop_weights(shape, seed=7, gate=True)
+    h0 = synth.loop_h0(shape, seed=7)
+    ref = oracle.looped_mixer(h0, w["w_in"], w["w_o"], 2, 128, 2, gate=True)
+    w_in = torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16)
+    w_o = torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)
+    states = torch.zeros((2, 2, 2, 128, 128), dtype=torch.float32, device="cuda")
+    got = np.empty_like(h0)
+    for t in range(shape.L):
+        h = torch.from_numpy(np.ascontiguousarray(h0[:, t], np.float32)).to("cuda")
+        lt2.lt2_looped_decode_step(h, w_in, w_o, states, 2, 128, 2, out_gate=True)
+        got[:, t] = host(h)
+    assert rel_err(got, ref) <= TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16

@@ -261,12 +261,13 @@ def test_empty_sequence_returns_initial_state():
 
 # ---- looped driver -------------------------------------------------------------
 
-def brute_layer(h, w_in, w_o, H, d):
+def brute_layer(h, w_in, w_o, H, d, gate=False):
     """Independent loop iteration: einsum projections, scipy gates, dense-A recurrence."""
     from scipy.special import expit
     B, L, D = h.shape
     hd = H * d
     z = np.einsum("bld,nd->bln", h, w_in)
+    gb = 4 * hd if gate else 3 * hd
     out = h.copy()
     for b in range(B):
         o_all = np.zeros((L, hd))
@@ -276,18 +277,20 @@ def brute_layer(h, w_in, w_o, H, d):
             v = z[b, :, 2 * hd + hh * d:2 * hd + (hh + 1) * d]
             q = q / np.linalg.norm(q, axis=1, keepdims=True)
             k = k / np.linalg.norm(k, axis=1, keepdims=True)
-            beta = expit(z[b, :, 3 * hd + hh])
-            alpha = expit(-z[b, :, 3 * hd + H + hh])  # exp(-softplus(z)) = sigmoid(-z)
+            beta = expit(z[b, :, gb + hh])
+            alpha = expit(-z[b, :, gb + H + hh])  # exp(-softplus(z)) = sigmoid(-z)
             o, _ = brute_force(q, k, v, alpha, beta, np.zeros((d, d)))
+            if gate:
+                o = o * expit(z[b, :, 3 * hd + hh * d:3 * hd + (hh + 1) * d])
             o_all[:, hh * d:(hh + 1) * d] = o
         out[b] = h[b] + np.einsum("lk,dk->ld", o_all, w_o)
     return out
 
 
-def small_loop_case(seed=12, B=2, L=6, D=8, H=2, d=3):
+def small_loop_case(seed=12, B=2, L=6, D=8, H=2, d=3, gate=False):
     rng = np.random.default_rng(seed)
     h = rng.standard_normal((B, L, D))
-    w_in = rng.standard_normal((3 * H * d + 2 * H, D)) / np.sqrt(D)
+    w_in = rng.standard_normal(((4 if gate else 3) * H * d + 2 * H, D)) / np.sqrt(D)
     w_o = rng.standard_normal((D, H * d)) / np.sqrt(H * d)
     return h, w_in, w_o, H, d
 
@@ -319,6 +322,31 @@ def test_looped_layer_causal():
     full = oracle.looped_mixer(h, w_in, w_o, H, d, 2)
     pre = oracle.looped_mixer(h[:, :5], w_in, w_o, H, d, 2)
     np.testing.assert_allclose(pre, full[:, :5], atol=1e-13)
+
+
+def test_gated_looped_layer_matches_brute_force():
+    h, w_in, w_o, H, d = small_loop_case(17, gate=True)
+    np.testing.assert_allclose(oracle.looped_layer(h, w_in, w_o, H, d, gate=True),
+                               brute_layer(h, w_in, w_o, H, d, gate=True), atol=1e-12)
+
+
+def test_gate_with_zero_weights_halves_the_mixer_output():
+    """W_g = 0 gives sigmoid(0) = 1/2 on every channel: the gated block equals the
+    ungated block with W_o halved (exact scaling by a power of two)."""
+    h, w_in, w_o, H, d = small_loop_case(18)
+    hd = H * d
+    w_gated = np.concatenate([w_in[:3 * hd], np.zeros((hd, w_in.shape[1])), w_in[3 * hd:]])
+    np.testing.assert_allclose(oracle.looped_mixer(h, w_gated, w_o, H, d, 3, gate=True),
+                               oracle.looped_mixer(h, w_in, w_o / 2, H, d, 3), atol=1e-13)
+
+
+def test_gated_loop_weights_share_the_ungated_draws():
+    shape = synth.LoopShape(1, 4, 128, 2, 64, 1)
+    a, g = synth.loop_weights(shape, seed=3), synth.loop_weights(shape, seed=3, gate=True)
+    hd = 2 * 64
+    np.testing.assert_array_equal(g["w_in"][:3 * hd], a["w_in"][:3 * hd])
+    np.testing.assert_array_equal(g["w_in"][4 * hd:], a["w_in"][3 * hd:])
+    np.testing.assert_array_equal(g["w_o"], a["w_o"])
 
 
 # ---- input generators (not the method, but both sides read them) --------------
