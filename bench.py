@@ -352,6 +352,51 @@ def _slab_inputs(synth, shape, b0, nb):
     return out
 
 
+def bench_decode_flat(args, torch, lt2, launches=64):
+    """Decode-step time against the context length behind the state (the pages'
+    flat decode throughput): the 4096-unit state of the decode workload (256
+    sequences x 16 heads, d=128) is seeded by a 2048-token and by a 32768-token
+    bf16 prefill of 16 sequences (tiled to 256), then the same fp32 decode step
+    is timed on each, rotating over four copies of the state.  Inputs are drawn
+    on the device with a fixed generator."""
+    B, H, d, Bs = 256, 16, 128, 16
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    res = {}
+    for L in (2048, 32768):
+        qk = [torch.nn.functional.normalize(torch.randn((Bs, L, H, d), device="cuda", generator=g), dim=-1)
+              .to(torch.bfloat16) for _ in range(2)]
+        vv = torch.randn((Bs, L, H, d), device="cuda", generator=g).to(torch.bfloat16)
+        a = torch.sigmoid(-torch.randn((Bs, L, H), device="cuda", generator=g))
+        bt = torch.sigmoid(torch.randn((Bs, L, H), device="cuda", generator=g))
+        S = torch.empty((Bs, H, d, d), dtype=torch.float32, device="cuda")
+        lt2.lt2_gdn_prefill(qk[0], qk[1], vv, a, bt, state_out=S, out=torch.empty_like(vv))
+        del qk, vv, a, bt
+        # four copies rotated per launch, as the loops of the decode workload do, so the
+        # 1 GiB of state is streamed from HBM rather than re-hit in the last-level cache
+        state = S.repeat(B // Bs, 1, 1, 1).unsqueeze(0).repeat(4, 1, 1, 1, 1).contiguous()
+        q = torch.nn.functional.normalize(torch.randn((B, H, d), device="cuda", generator=g), dim=-1)
+        k = torch.nn.functional.normalize(torch.randn((B, H, d), device="cuda", generator=g), dim=-1)
+        v = torch.randn((B, H, d), device="cuda", generator=g)
+        al = torch.sigmoid(-torch.randn((B, H), device="cuda", generator=g))
+        be = torch.sigmoid(torch.randn((B, H), device="cuda", generator=g))
+        out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+        for i in range(4):
+            lt2.lt2_gdn_decode_step(q, k, v, al, be, state[i], out=out)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for i, (e0, e1) in enumerate(ev):
+            e0.record()
+            lt2.lt2_gdn_decode_step(q, k, v, al, be, state[i % 4], out=out)
+            e1.record()
+        torch.cuda.synchronize()
+        res[L] = float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]))
+        del state, S
+        torch.cuda.empty_cache()
+    log(f"decode flat: {res[2048]:.1f} us/launch after 2048 tokens, {res[32768]:.1f} us after 32768")
+    return dict(units=B * H, d=d, us_per_launch_after_2048=res[2048], us_per_launch_after_32768=res[32768],
+                ratio=res[32768] / res[2048])
+
+
 def bench_looped_decode(args, torch, lt2, synth, tokens=16, warm=3):
     """Looped decode chain: 256 sequences, d_model 2048, H=16, d=128, T=4 loop
     states carried in place, one token per step (fresh seeded h rows)."""
@@ -416,6 +461,7 @@ def main():
     ap.add_argument("--no-looped", action="store_true")
     ap.add_argument("--no-channel", action="store_true")
     ap.add_argument("--no-looped-decode", action="store_true")
+    ap.add_argument("--no-decode-flat", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -438,6 +484,7 @@ def main():
     loo_g = None if args.no_looped else bench_looped(args, torch, lt2, synth, gate=True)
     cha = None if args.no_channel else bench_channel(args, torch, lt2, synth)
     lde = None if args.no_looped_decode else bench_looped_decode(args, torch, lt2, synth)
+    flat = None if (args.no_decode or args.no_decode_flat) else bench_decode_flat(args, torch, lt2)
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
     value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
@@ -466,6 +513,8 @@ def main():
         extra["channel_prefill"] = cha
     if lde:
         extra["looped_decode"] = lde
+    if flat:
+        extra["decode_flat"] = flat
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",
