@@ -30,6 +30,7 @@ import numpy as np
 T_Q, T_K, T_V, T_BETA, T_ALPHA = 1, 2, 3, 4, 5
 T_H0, T_WIN, T_WO, T_WG = 6, 7, 8, 9
 T_DQ, T_DK, T_DV, T_DBETA, T_DALPHA = 11, 12, 13, 14, 15
+T_SQ, T_SK, T_SV = 16, 17, 18
 
 
 def _threads() -> int:
@@ -168,18 +169,26 @@ class LoopShape:
     T: int
 
 
-def loop_weights(shape: LoopShape, seed: int = 0, gate: bool = False) -> dict:
+def loop_weights(shape: LoopShape, seed: int = 0, gate: bool = False, kind: str = "gdn",
+                 layer: int | None = None) -> dict:
     """bf16-valued weights in the [d_out, d_in] convention (y = x W^T):
     W_in [3*H*d + 2*H, d_model] = rows of W_q, W_k, W_v, W_beta, W_alpha, or with
     ``gate`` [4*H*d + 2*H, d_model] with W_g (its own stream) after W_v; the other
-    rows are the same draws either way.  W_o [d_model, H*d].  Entries N(0, 1/d_in)."""
+    rows are the same draws either way.  W_o [d_model, H*d].  Entries N(0, 1/d_in).
+    A window-attention layer (``kind="swa"``) takes the W_q, W_k, W_v (and W_g)
+    rows only.  ``layer`` keys the streams of one layer of a multi-layer block."""
     D, H, d = shape.d_model, shape.H, shape.d
     n_in = 3 * H * d + 2 * H
     s = 1.0 / np.sqrt(D)
-    w_in = rng(seed, T_WIN).standard_normal((n_in, D), dtype=np.float32) * np.float32(s)
-    w_o = rng(seed, T_WO).standard_normal((D, H * d), dtype=np.float32) * np.float32(1.0 / np.sqrt(H * d))
+    unit = () if layer is None else (layer,)
+    w_in = rng(seed, T_WIN, *unit).standard_normal((n_in, D), dtype=np.float32) * np.float32(s)
+    w_o = rng(seed, T_WO, *unit).standard_normal((D, H * d), dtype=np.float32) * np.float32(1.0 / np.sqrt(H * d))
+    if kind == "swa":
+        w_in = w_in[:3 * H * d]
+    elif kind != "gdn":
+        raise ValueError(kind)
     if gate:
-        w_g = rng(seed, T_WG).standard_normal((H * d, D), dtype=np.float32) * np.float32(s)
+        w_g = rng(seed, T_WG, *unit).standard_normal((H * d, D), dtype=np.float32) * np.float32(s)
         w_in = np.concatenate([w_in[:3 * H * d], w_g, w_in[3 * H * d:]], axis=0)
     return dict(w_in=bf16_round(w_in), w_o=bf16_round(w_o))
 
@@ -195,6 +204,43 @@ def loop_h0(shape: LoopShape, seed: int = 0, b: int | None = None, rows: int | N
     for bb in range(shape.B):
         out[bb] = bf16_round(rng(seed, T_H0, bb).standard_normal((shape.L, shape.d_model), dtype=np.float32)[:L])
     return out
+
+
+@dataclass(frozen=True)
+class SWAShape:
+    B: int
+    L: int
+    H: int
+    d: int
+    window: int
+
+
+def swa_unit(shape: SWAShape, seed: int, b: int, h: int) -> dict:
+    """q, k, v [L, d] of one (batch, head) unit of a window-attention layer:
+    N(0,1) entries (the scale of x W^T for x ~ N(0,1) and W ~ N(0, 1/d_in)),
+    rounded to bf16, float32 arrays."""
+    L, d = shape.L, shape.d
+    return {n: bf16_round(rng(seed, t, b, h).standard_normal((L, d), dtype=np.float32))
+            for n, t in (("q", T_SQ), ("k", T_SK), ("v", T_SV))}
+
+
+def swa_inputs(shape: SWAShape, seed: int = 0) -> dict:
+    """q, k, v [B, L, H, d] bf16-valued float32 arrays, unit by unit as ``swa_unit``."""
+    B, L, H, d = shape.B, shape.L, shape.H, shape.d
+    out = {n: np.empty((B, L, H, d), np.float32) for n in ("q", "k", "v")}
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        for n, arr in swa_unit(shape, seed, b, h).items():
+            out[n][b, :, h] = arr
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(B * H)))
+    return out
+
+
+# Window-attention workload: the looped block's head shape at 8k context, window 512.
+SWA_WORKLOAD = SWAShape(2, 8192, 16, 128, 512)
 
 
 # The five workloads of the LT2 linear-mixer hot path.

@@ -164,3 +164,75 @@ def looped_mixer(h0, w_in, w_o, H: int, d: int, T: int, threads: int = 0, gate: 
     for _ in range(T):
         h = looped_layer(h, w_in, w_o, H, d, threads, gate)
     return h
+
+
+# ---- sliding-window attention and the GDN/SWA hybrid ------------------------
+#
+# Sources: the LT2 explainer (paithon.it), section "Sostituire il motore": the
+# second (sparse) family lets each token attend only to a window of the w most
+# recent positions; section "Il giro trasforma il calcolo in contesto": a window
+# of width w applied T times reaches O(T w) tokens back.  The LT2 summary page
+# (hybrid strategies figure) interleaves the two mixer kinds across depth and
+# iterations.  Readings where the pages are silent: softmax attention with the
+# 1/sqrt(d) scale over keys j in [t - w + 1, t] (the token itself included), no
+# normalisation of q and k in the window layer, and the shared block of the
+# hybrid being a fixed stack of mixer layers applied in order, each with its
+# own weights, repeated T times.
+
+def swa(q, k, v, window: int):
+    """Causal sliding-window softmax attention, one query row at a time.
+
+    q, k, v [B, L, H, d]; output o [B, L, H, d] in fp64 with
+        o_t = sum_{j=max(0,t-w+1)}^{t} softmax_j(q_t . k_j / sqrt(d)) v_j
+    for every batch entry and head."""
+    q, k, v = map(_f64, (q, k, v))
+    B, L, H, d = q.shape
+    assert k.shape == q.shape and v.shape[:3] == (B, L, H) and window >= 1
+    o = np.empty(v.shape, np.float64)
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        for t in range(L):
+            j0 = max(0, t - window + 1)
+            kw = k[b, j0:t + 1]                      # [n, H, d]
+            vw = v[b, j0:t + 1]                      # [n, H, dv]
+            s = np.einsum("hd,nhd->hn", q[b, t], kw) * scale
+            s = s - s.max(axis=1, keepdims=True)     # the softmax is shift invariant
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)
+            o[b, t] = np.einsum("hn,nhe->he", p, vw)
+    return o
+
+
+def swa_layer(h, w_in, w_o, H: int, d: int, window: int, gate: bool = False):
+    """One window-attention layer of the looped hybrid on h [B,L,D]:
+
+        z = h W_in^T;  q, k, v (, z_g) = split(z);  o = swa(q, k, v; w)
+        gate: o <- o * sigmoid(z_g);  h <- h + o W_o^T
+
+    W_in is [3*H*d, D] (rows of W_q, W_k, W_v) or [4*H*d, D] with the gate;
+    W_o is [D, H*d].  fp64."""
+    h = _f64(h)
+    B, L, D = h.shape
+    hd = H * d
+    z = h.reshape(B * L, D) @ _f64(w_in).T
+    q, k, v = (z[:, i * hd:(i + 1) * hd].reshape(B, L, H, d) for i in range(3))
+    o = swa(q, k, v, window).reshape(B * L, hd)
+    if gate:
+        o = o * _sigmoid(z[:, 3 * hd:4 * hd])
+    return h + (o @ _f64(w_o).T).reshape(B, L, D)
+
+
+def hybrid_mixer(h0, layers, H: int, d: int, T: int, window: int, threads: int = 0, gate: bool = False):
+    """T loops of a shared block whose layers run in order; ``layers`` is a list
+    of (kind, W_in, W_o) with kind "gdn" (``looped_layer``) or "swa"
+    (``swa_layer``)."""
+    h = _f64(h0)
+    for _ in range(T):
+        for kind, w_in, w_o in layers:
+            if kind == "gdn":
+                h = looped_layer(h, w_in, w_o, H, d, threads, gate)
+            elif kind == "swa":
+                h = swa_layer(h, w_in, w_o, H, d, window, gate)
+            else:
+                raise ValueError(kind)
+    return h
