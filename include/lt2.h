@@ -197,6 +197,31 @@ lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const voi
                                   const void *W_o, float *states, void *ws, size_t ws_bytes,
                                   void *stream);
 
+/* Shape and types of one sliding-window attention call. */
+typedef struct lt2_swa_desc {
+    int32_t B, L, H;     /* batch, tokens, heads */
+    int32_t d;           /* head size (q, k and v) */
+    int32_t window;      /* w >= 1: query t attends to keys t-w+1 .. t */
+    int32_t qkv_dtype;   /* lt2_dtype of q, k and v (LT2_BF16 is built) */
+    int32_t out_dtype;   /* lt2_dtype of out */
+} lt2_swa_desc;
+
+/*
+ * Causal sliding-window softmax attention, the sparse mixer family of LT2
+ * (LT2 explainer, paithon.it, section "Sostituire il motore": each token looks
+ * only at a window of the w most recent positions):
+ *     o_t = sum_{j=max(0,t-w+1)}^{t} softmax_j(q_t . k_j / sqrt(d)) v_j
+ * for every batch entry and head; w >= L gives causal full attention.
+ *   q, k, v   [B, L, H, d] bf16, 16-byte aligned, used as given
+ *   out       [B, L, H, d] bf16 or fp32 (desc->out_dtype), 16-byte aligned
+ * Scores and the softmax are fp32; the probabilities enter the value product
+ * as bf16 with fp32 accumulation.  No workspace.
+ * Errors: LT2_ERR_SHAPE for negative sizes or window < 1; LT2_ERR_UNSUPPORTED
+ * for fp32 q/k/v or d not in {64, 128}; LT2_ERR_NULL / LT2_ERR_ALIGN as usual.
+ */
+lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *k, const void *v,
+                           void *out, void *stream);
+
 /*
  * Bandwidth probe: copy `bytes` (a multiple of 16) from src to dst with one
  * streaming kernel.  Used to measure the achievable HBM bandwidth.

@@ -141,6 +141,27 @@ lt2_status lt2_gdn_decode_step(const lt2_gdn_desc *desc, const void *q, const vo
     return hip_status(launch_decode(a, (hipStream_t)stream));
 }
 
+lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *k, const void *v, void *out,
+                           void *stream) {
+    if (!desc) return LT2_ERR_NULL;
+    if (desc->B < 0 || desc->L < 0 || desc->H <= 0 || desc->d <= 0 || desc->window < 1) return LT2_ERR_SHAPE;
+    if ((desc->qkv_dtype != LT2_F32 && desc->qkv_dtype != LT2_BF16) ||
+        (desc->out_dtype != LT2_F32 && desc->out_dtype != LT2_BF16))
+        return LT2_ERR_DTYPE;
+    if (desc->qkv_dtype != LT2_BF16 || (desc->d != 64 && desc->d != 128)) return LT2_ERR_UNSUPPORTED;
+    // one workgroup per (b, h, 128 queries): the grid must fit its 31-bit limit
+    if ((int64_t)desc->B * desc->H * (((int64_t)desc->L + 127) / 128) > 0x7fffffffLL) return LT2_ERR_SHAPE;
+    const bool work = desc->B > 0 && desc->L > 0;
+    if (work && (!q || !k || !v || !out)) return LT2_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return LT2_ERR_ALIGN;
+    if (!work) return LT2_OK;
+    SwaArgs a;
+    a.B = desc->B; a.L = desc->L; a.H = desc->H; a.d = desc->d; a.window = desc->window;
+    a.out_bf16 = desc->out_dtype == LT2_BF16;
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    return hip_status(launch_swa(a, (hipStream_t)stream));
+}
+
 lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream) {
     if (bytes == 0) return LT2_OK;
     if (!dst || !src) return LT2_ERR_NULL;

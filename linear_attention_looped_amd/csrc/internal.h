@@ -34,6 +34,17 @@ size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C, bool bf16);
 hipError_t launch_prefill_channel(const GdnArgs &a, int phase, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 
+// Causal sliding-window softmax attention: q, k, v bf16 [B, L, H, d], out bf16
+// or fp32 [B, L, H, d], keys t-window+1 .. t for query t, scale 1/sqrt(d);
+// gate (bf16, out's layout, or nullptr) multiplies the output where it is stored.
+struct SwaArgs {
+    int B, L, H, d, window, out_bf16;
+    const void *q, *k, *v;
+    void *out;
+    const uint16_t *gate = nullptr;
+};
+hipError_t launch_swa(const SwaArgs &a, hipStream_t s);
+
 // Looped LT2-linear block.
 struct LoopArgs {
     int B, L, D, H, d, T, chunk, gated;

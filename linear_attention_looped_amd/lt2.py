@@ -30,6 +30,10 @@ class lt2_loop_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "d_model", "H", "d_head", "T", "chunk", "out_gate")]
 
 
+class lt2_swa_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "H", "d", "window", "qkv_dtype", "out_dtype")]
+
+
 class Lt2Error(RuntimeError):
     def __init__(self, fn: str, code: int):
         self.code = code
@@ -68,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.lt2_looped_decode_workspace_size.restype = Z
         L.lt2_looped_decode_step.argtypes = [LD, P, P, P, P, P, Z, P]
         L.lt2_looped_decode_step.restype = S
+        L.lt2_swa_prefill.argtypes = [ctypes.POINTER(lt2_swa_desc), P, P, P, P, P]
+        L.lt2_swa_prefill.restype = S
         L.lt2_hbm_copy.argtypes = [P, P, Z, P]
         L.lt2_hbm_copy.restype = S
         _lib = L
@@ -227,6 +233,28 @@ def lt2_looped_decode_step(h, W_in, W_o, states, H: int, d_head: int, T: int, wo
                                         _stream(stream))
     _check("lt2_looped_decode_step", code)
     return h
+
+
+def swa_desc(B, L, H, d, window, qkv_dtype=LT2_BF16, out_dtype=LT2_BF16):
+    return lt2_swa_desc(B, L, H, d, window, qkv_dtype, out_dtype)
+
+
+def lt2_swa_prefill(q, k, v, window: int, out=None, out_dtype=None, stream=None):
+    """Causal sliding-window attention.  q, k, v [B,L,H,d] bf16; keys
+    t-window+1 .. t for query t, scale 1/sqrt(d).  Returns out [B,L,H,d]
+    (bf16, or ``out_dtype`` / the dtype of ``out``)."""
+    B, L, H, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+        assert tuple(t.shape) == (B, L, H, d), (n, t.shape)
+    if out is None:
+        out = torch.empty((B, L, H, d), dtype=out_dtype or torch.bfloat16, device=q.device)
+    _need(out, "out")
+    assert tuple(out.shape) == (B, L, H, d), out.shape
+    desc = swa_desc(B, L, H, d, int(window), _dt(q), _dt(out))
+    code = lib().lt2_swa_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream))
+    _check("lt2_swa_prefill", code)
+    return out
 
 
 def lt2_hbm_copy(dst, src, stream=None):

@@ -166,3 +166,34 @@ def test_looped_gate_adds_workspace():
     assert lt2.lt2_looped_mixer_workspace_size(good_loop(out_gate=1)) > lt2.lt2_looped_mixer_workspace_size(good_loop())
     assert (lt2.lt2_looped_decode_workspace_size(good_loop(L=1, out_gate=1)) >
             lt2.lt2_looped_decode_workspace_size(good_loop(L=1)))
+
+
+def swa_call(desc, q=FAKE, k=FAKE, v=FAKE, out=FAKE):
+    P = ctypes.c_void_p
+    return lt2.lib().lt2_swa_prefill(ctypes.byref(desc), P(q), P(k), P(v), P(out), None)
+
+
+def good_swa(**kw):
+    d = dict(B=2, L=300, H=3, d=128, window=64, qkv_dtype=1, out_dtype=1)
+    d.update(kw)
+    return lt2.lt2_swa_desc(*[d[n] for n, _ in lt2.lt2_swa_desc._fields_])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), 2), (dict(L=-1), 2), (dict(H=0), 2), (dict(d=0), 2), (dict(window=0), 2), (dict(window=-3), 2),
+    (dict(qkv_dtype=5), 3), (dict(out_dtype=2), 3),
+    (dict(qkv_dtype=0), 4), (dict(d=96), 4), (dict(d=256), 4),
+    (dict(B=65536, H=65536), 2),
+])
+def test_swa_rejects_bad_descriptor(kw, code):
+    assert swa_call(good_swa(**kw)) == code
+
+
+def test_swa_null_and_alignment():
+    assert lt2.lib().lt2_swa_prefill(None, None, None, None, None, None) == 1
+    assert swa_call(good_swa(), k=None) == 1
+    assert swa_call(good_swa(), out=FAKE + 8) == 6
+    assert swa_call(good_swa(), v=FAKE + 2) == 6
+    # empty inputs: nothing is read or written
+    assert swa_call(good_swa(L=0), q=None, k=None, v=None, out=None) == 0
+    assert swa_call(good_swa(B=0), q=None, k=None, v=None, out=None) == 0
