@@ -333,6 +333,42 @@ def bench_looped(args, torch, lt2, synth, reps=5, gate=False):
                 mfma_frac=(gemm_flops + gdn_flops) / ms / 1e9 / BF16_PEAK_TFLOPS)
 
 
+def swa_flops_bytes(B, L, H, d, w, out_bytes=2):
+    """Algorithmic work of causal window attention: query t scores and weights
+    min(t+1, w) keys, 2 d flop each for q.k and for p v; bytes are q, k, v read
+    and o written once (bf16 in)."""
+    keys = sum(min(t + 1, w) for t in range(L)) if L <= 1 << 16 else (
+        w * (w + 1) // 2 + (L - w) * w if L >= w else L * (L + 1) // 2)
+    flops = 4.0 * d * keys * B * H
+    nbytes = float(B * L * H * d * (3 * 2 + out_bytes))
+    return flops, nbytes
+
+
+def bench_swa(args, torch, lt2, synth, reps=20):
+    """Sliding-window attention B=2 L=8192 H=16 d=128, window 512, bf16 in and out."""
+    sh = synth.SWA_WORKLOAD
+    log(f"swa inputs B={sh.B} L={sh.L} H={sh.H} d={sh.d} window={sh.window}")
+    x = synth.swa_inputs(sh, seed=0)
+    q, k, v = (torch.from_numpy(x[n]).to("cuda").to(torch.bfloat16) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    for _ in range(3):
+        lt2.lt2_swa_prefill(q, k, v, sh.window, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        lt2.lt2_swa_prefill(q, k, v, sh.window, out=out)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    flops, nbytes = swa_flops_bytes(sh.B, sh.L, sh.H, sh.d, sh.window)
+    log(f"swa {ms * 1e3:.1f} us, {flops / ms / 1e9:.0f} TFLOP/s, {nbytes / ms / 1e6:.0f} GB/s")
+    return dict(B=sh.B, L=sh.L, H=sh.H, d=sh.d, window=sh.window, ms=ms,
+                tokens_per_s=sh.B * sh.L / (ms / 1e3), flops=flops, bytes=nbytes,
+                tflops=flops / ms / 1e9, mfma_frac=flops / ms / 1e9 / BF16_PEAK_TFLOPS,
+                gbs=nbytes / ms / 1e6, hbm_frac=nbytes / ms / 1e6 / HBM_PEAK_GBS)
+
+
 def _slab_inputs(synth, shape, b0, nb):
     """Inputs of batch rows b0..b0+nb of the decode-seeding prefill (per-unit streams)."""
     L, H, d = shape.L, shape.H, shape.dk
@@ -462,6 +498,7 @@ def main():
     ap.add_argument("--no-channel", action="store_true")
     ap.add_argument("--no-looped-decode", action="store_true")
     ap.add_argument("--no-decode-flat", action="store_true")
+    ap.add_argument("--no-swa", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -485,6 +522,7 @@ def main():
     cha = None if args.no_channel else bench_channel(args, torch, lt2, synth)
     lde = None if args.no_looped_decode else bench_looped_decode(args, torch, lt2, synth)
     flat = None if (args.no_decode or args.no_decode_flat) else bench_decode_flat(args, torch, lt2)
+    swa = None if args.no_swa else bench_swa(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
     value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
@@ -515,6 +553,8 @@ def main():
         extra["looped_decode"] = lde
     if flat:
         extra["decode_flat"] = flat
+    if swa:
+        extra["swa_prefill"] = swa
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",

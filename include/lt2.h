@@ -216,7 +216,9 @@ typedef struct lt2_swa_desc {
  *   out       [B, L, H, d] bf16 or fp32 (desc->out_dtype), 16-byte aligned
  * Scores and the softmax are fp32; the probabilities enter the value product
  * as bf16 with fp32 accumulation.  No workspace.
- * Errors: LT2_ERR_SHAPE for negative sizes or window < 1; LT2_ERR_UNSUPPORTED
+ * Limits: one sequence's q (L * H * d bf16) below 2 GiB.
+ * Errors: LT2_ERR_SHAPE for negative sizes, window < 1 or sizes beyond the
+ * limits; LT2_ERR_UNSUPPORTED
  * for fp32 q/k/v or d not in {64, 128}; LT2_ERR_NULL / LT2_ERR_ALIGN as usual.
  */
 lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *k, const void *v,

@@ -151,6 +151,8 @@ lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *
     if (desc->qkv_dtype != LT2_BF16 || (desc->d != 64 && desc->d != 128)) return LT2_ERR_UNSUPPORTED;
     // one workgroup per (b, h, 128 queries): the grid must fit its 31-bit limit
     if ((int64_t)desc->B * desc->H * (((int64_t)desc->L + 127) / 128) > 0x7fffffffLL) return LT2_ERR_SHAPE;
+    // key and value tiles are addressed with 32-bit byte offsets within one sequence
+    if ((int64_t)desc->L * desc->H * desc->d * 2 > 0x7fffffffLL) return LT2_ERR_SHAPE;
     const bool work = desc->B > 0 && desc->L > 0;
     if (work && (!q || !k || !v || !out)) return LT2_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return LT2_ERR_ALIGN;

@@ -8,9 +8,9 @@
 //
 // One workgroup = one (b, h) and 128 consecutive queries; four waves of 32
 // queries each.  Keys and values stream through LDS in tiles of 64 tokens,
-// double-buffered: the next tile is fetched into registers (coalesced 16-byte
-// loads) while the current one is used, and written to the other buffer at the
-// end of the tile, so one barrier per tile suffices.
+// double-buffered: the next tile is loaded straight into the other LDS buffer
+// (buffer loads with the LDS-DMA bit, 16 bytes per lane, no staging registers)
+// while the current one is used, so one barrier per tile suffices.
 //
 // Per wave and tile the scores are computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16: the A operand is a K row fragment read from LDS,
@@ -26,9 +26,19 @@
 //
 // Softmax in base 2: scores are scaled by log2(e)/sqrt(d) and exponentiated
 // with exp2; the running maximum starts at a large finite negative value so a
-// fully masked tile contributes exp2(-inf) = 0 without producing NaN.  Masking
-// is applied only on tiles that cross the causal diagonal or the window's start;
-// tiles wholly outside a wave's range are skipped by that wave.
+// fully masked tile contributes exp2(-inf) = 0 without producing NaN.  The
+// accumulated output is rescaled only when some lane's maximum has grown by
+// more than 8 (a factor 256): otherwise the stale maximum is kept, which bounds
+// the probabilities by 256 -- harmless in bf16 and fp32 -- and skips the
+// rescale on most tiles.  Masking is applied only on tiles that cross the
+// causal diagonal or the window's start; tiles wholly outside a wave's range
+// are skipped by that wave.
+//
+// K and V tiles are read through buffer descriptors whose range ends at the
+// sequence's last token, so rows past the end read as zero (and are masked)
+// without clamping, and each thread's offset inside a tile stays constant.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -44,6 +54,28 @@ constexpr int SWA_QT = 128;   // queries per workgroup
 constexpr int SWA_KT = 64;    // keys per LDS tile
 constexpr int SWA_NTH = 256;  // four waves
 
+// max (or sum) of a value over lanes l and l ^ 32
+__device__ __forceinline__ float halves_max(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// Buffer descriptor over bytes [p, p + n): loads at offsets >= n return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+
+// 16 bytes per lane from the buffer at byte offset voff into LDS at dst + 16 lane
+// (dst wave-uniform).  Kept out of the kernel's generic lambdas: instantiated
+// there by the host pass, the builtin would invalidate the kernel template.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t *dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
+}
+
 template <typename TO>
 __device__ __forceinline__ void store4(TO *p, float a, float b, float c, float d);
 template <>
@@ -58,20 +90,30 @@ __device__ __forceinline__ void store4<float>(float *p, float a, float b, float 
     *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
 }
 
+// LDS tiles hold 64 rows of d bf16 without padding; the 16-byte segment sigma
+// of row r sits at segment sigma ^ swz(r), which keeps both the 16-row fragment
+// reads of K and the 4-row transpose reads of V free of bank conflicts.
+template <int SPR>
+__device__ __forceinline__ int swz(int r) {
+    return (4 * (r & 3) + ((r >> 2) & 3)) & (SPR - 1);
+}
+
 template <int D, typename TO>
 __global__ __launch_bounds__(SWA_NTH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void swa_fwd_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
                     TO *__restrict__ out, const uint16_t *__restrict__ gate, int L, int H, int window, int nqt,
                     float sl2) {
     constexpr int KT = SWA_KT;
-    constexpr int KP = D + 8;          // K row pitch: 16-byte reads of 16 consecutive rows hit distinct banks
-    constexpr int VP = D + 32;         // V row pitch: rows 16 banks apart for the transpose reads
+    constexpr int SPR = D / 8;         // 16-byte segments per row
+    constexpr int RPC = 64 / SPR;      // rows per 1 KiB chunk (one wave's LDS-DMA load)
+    constexpr int CPW = KT / RPC / 4;  // chunks per wave per tile
+    constexpr int TILE = KT * D;       // bf16 per tile
     constexpr int NKS = D / 16;        // k-steps of the score product
     constexpr int NDT = D / 32;        // 32-wide value tiles
-    constexpr int PPT = KT * D / 8 / SWA_NTH;   // 16-byte pieces per thread per K (or V) tile
-    static_assert(PPT * SWA_NTH * 8 == KT * D, "tile pieces");
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * VP];
+    // four distinct arrays (not one [2][...] array): the compiler then knows that
+    // a DMA into one buffer does not alias reads of the other, and does not make
+    // those reads wait for the DMA
+    __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE], V0[TILE], V1[TILE];
 
     const int lid = xcd_logical(blockIdx.x, gridDim.x);
     const int qt = lid % nqt;
@@ -91,6 +133,31 @@ void swa_fwd_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     const int kend = min(L, t0 + SWA_QT);                  // exclusive
     const int kt0 = kbeg / KT, kt1 = (kend - 1) / KT;
 
+    // LDS-DMA roles: chunk wave + 4 n of a tile is 1 KiB of LDS; lane i fills its
+    // bytes 16 i .. 16 i + 15, i.e. row RPC c + i / SPR, physical segment i % SPR,
+    // from the global segment that the swizzle maps there
+    int voff[CPW];
+#pragma unroll
+    for (int n = 0; n < CPW; ++n) {
+        const int row = RPC * (wave + 4 * n) + lane / SPR;
+        const int sg = (lane % SPR) ^ swz<SPR>(row);
+        voff[n] = 2 * (row * (int)tok + 8 * sg);
+    }
+    auto fetch = [&](int kt, auto bufc) {
+        uint16_t *Kd = decltype(bufc)::value ? K1 : K0;
+        uint16_t *Vd = decltype(bufc)::value ? V1 : V0;
+        // bytes from the tile's first row to the end of the sequence's last row
+        const int n = 2 * ((L - 1 - kt * KT) * (int)tok + D);
+        const size_t t0b = base + (size_t)kt * KT * tok;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + t0b, n), vr = make_rsrc(v + t0b, n);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int ch = 512 * (wave + 4 * c);
+            dma16(kr, &Kd[ch], voff[c]);
+            dma16(vr, &Vd[ch], voff[c]);
+        }
+    };
+
     // Q^T fragments: B operand of S^T = K Q^T, query l32, channels 16 ks + 8 hh .. + 7
     bf16x8 qf[NKS];
     {
@@ -98,35 +165,29 @@ void swa_fwd_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
     }
-
-    // staging roles: piece p = tid + 256 i is row p / (D/8), 8 channels at 8 (p % (D/8))
-    int srow[PPT], scol[PPT];
+    fetch(kt0, std::integral_constant<int, 0>{});
+    // the Q fragments must have landed before the tile loop: left to itself the
+    // compiler sinks their loads into the loop preheader, and the loop's static
+    // wait counts then also hold every tile's MFMAs on that tile's prefetch
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-        const int p = tid + SWA_NTH * i;
-        srow[i] = p / (D / 8);
-        scol[i] = 8 * (p % (D / 8));
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(qf[ks]));
+
+    // per-lane LDS element offsets: K fragment (row l32, channels 16 ks + 8 hh) and
+    // the V^T transpose reads (rows 4 hh + e (+ 8), channels 32 dt + 16 (g&1) + 4 c)
+    int koff[NKS], vo[2][NDT];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * D + 8 * ((2 * ks + hh) ^ swz<SPR>(l32));
+    {
+        const int e = (lane & 15) >> 2, c4 = lane & 3, g1 = (lane >> 4) & 1;
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const int row = 4 * hh + e + 8 * hi;
+                const int sg = 4 * dt + 2 * g1 + (c4 >> 1);
+                vo[hi][dt] = row * D + 8 * (sg ^ swz<SPR>(row)) + 4 * (c4 & 1);
+            }
     }
-    u32x4 rk[PPT], rv[PPT];
-    auto fetch = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const size_t row = (size_t)min(kt * KT + srow[i], L - 1);
-            rk[i] = *reinterpret_cast<const u32x4 *>(k + base + row * tok + scol[i]);
-            rv[i] = *reinterpret_cast<const u32x4 *>(v + base + row * tok + scol[i]);
-        }
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            *reinterpret_cast<u32x4 *>(&Ks[buf][srow[i] * KP + scol[i]]) = rk[i];
-            *reinterpret_cast<u32x4 *>(&Vs[buf][srow[i] * VP + scol[i]]) = rv[i];
-        }
-    };
-
-    fetch(kt0);
-    stage(0);
-    __syncthreads();
 
     f32x16 oacc[NDT];
 #pragma unroll
@@ -134,53 +195,71 @@ void swa_fwd_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
     float m = -1e30f, lsum = 0.f;
-    // transpose-read roles: within each 16-lane group, lane 4e + c addresses row
-    // e of a 4-row block at channel 4c; the group's second bit picks the 16-channel half
-    const int tr_e = (lane & 15) >> 2;
-    const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    for (int kt = kt0; kt <= kt1; ++kt) {
-        const int buf = (kt - kt0) & 1;
-        if (kt < kt1) fetch(kt + 1);
+    wait_vmem_all();
+    __syncthreads();
+
+    auto tile = [&](int kt, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        const uint16_t *Kb = buf ? K1 : K0;
+        const uint16_t *Vb = buf ? V1 : V0;
+        if (kt < kt1) fetch(kt + 1, std::integral_constant<int, buf ^ 1>{});
         const int ka = kt * KT;
         const bool active = wave_live && ka <= qlast && ka + KT - 1 >= qa - window + 1;
         if (active) {
+            __builtin_amdgcn_s_setprio(1);
             f32x16 s[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-                const uint16_t *kr = &Ks[buf][(32 * kb + l32) * KP + 8 * hh];
+            // K fragments two k-steps (eight reads) ahead of their products, so that LDS
+            // latency hides behind four MFMAs; the order is pinned by group barriers
+            bf16x8 kf[NKS][2];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kr + 16 * ks);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-                }
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    kf[ks][kb] = *reinterpret_cast<const bf16x8 *>(&Kb[32 * kb * D + koff[ks]]);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kb], qf[ks], s[kb], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);          // k-steps 0, 1
+#pragma unroll
+            for (int p2 = 0; p2 < NKS / 2; ++p2) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);      // products of step pair p2
+                if (p2 + 2 < NKS / 2)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of pair p2 + 2
             }
-            // every key of the tile inside every live query's window?
-            const bool full = ka + KT - 1 <= qa && ka >= qlast - window + 1;
+            // keys outside a query's window: only on tiles that cross the diagonal
+            // or the window's start for some live query of the wave
+            if (!(ka + KT - 1 <= qa && ka >= qlast - window + 1)) {
+                const int jd = ka + 4 * hh - tq;          // key - query of register 0
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int dj = jd + 32 * kb + 8 * (r >> 2) + (r & 3);
+                        s[kb][r] = (dj > 0 || dj <= -window) ? -INFINITY : s[kb][r];
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = s[kb][r];
-                    if (!full) {
-                        const int j = ka + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        if (j > tq || j <= tq - window) x = -INFINITY;
-                    }
-                    s[kb][r] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m, mx * sl2);
-            const float f = __builtin_amdgcn_exp2f(m - mnew);
-            m = mnew;
-            lsum *= f;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            const float mnew = fmaxf(m, halves_max(mx) * sl2);
+            if (__builtin_amdgcn_ballot_w64(mnew > m + 8.f)) {
+                const float f = __builtin_amdgcn_exp2f(m - mnew);
+                m = mnew;
+                lsum *= f;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+                for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= f;
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= f;
+            }
             // probabilities as the B operand of O^T += V^T P^T: 16-key step (kb, half)
             // takes registers 8 half .. 8 half + 7 of s[kb]
             bf16x8 pf[2][2];
@@ -194,55 +273,74 @@ void swa_fwd_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
                         lsum += p;
                         pf[kb][hf][e] = (__bf16)p;
                     }
+            // V^T fragments of 16-key step st = 2 kb + hf (keys 32 kb + 16 hf + 4 hh + 0..3
+            // in slots 0-3, + 8 in slots 4-7), read two steps ahead of their products
+            bf16x8 vf[4][NDT];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int st = 0; st < 4; ++st) {
+                const uint16_t *vb = &Vb[16 * st * D];
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    // keys 32 kb + 16 hf + 4 hh + 0..3 (slots 0-3) and + 8 (slots 4-7)
-                    const int r0 = 32 * kb + 16 * hf + 4 * hh + tr_e;
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_short4 *)(&Vs[buf][r0 * VP + 32 * dt + tr_c]));
-                        const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_short4 *)(&Vs[buf][(r0 + 8) * VP + 32 * dt + tr_c]));
-                        const bf16x8 a = __builtin_bit_cast(
-                            bf16x8, (__attribute__((ext_vector_type(8))) short){lo4[0], lo4[1], lo4[2], lo4[3],
-                                                                                hi4[0], hi4[1], hi4[2], hi4[3]});
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][hf], oacc[dt], 0, 0, 0);
-                    }
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(vb + vo[0][dt]));
+                    const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(vb + vo[1][dt]));
+                    vf[st][dt] = __builtin_bit_cast(
+                        bf16x8, (__attribute__((ext_vector_type(8))) short){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0],
+                                                                            hi4[1], hi4[2], hi4[3]});
                 }
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st][dt], pf[st >> 1][st & 1], oacc[dt],
+                                                                       0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDT, 0);    // steps 0, 1
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NDT, 0);    // products of step st
+                if (st + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 0);   // reads of st + 2
+            }
+            __builtin_amdgcn_s_setprio(0);
         }
-        if (kt < kt1) {
-            wait_vmem_all();
-            stage(buf ^ 1);
-        }
+        wait_vmem_all();
         __syncthreads();
+    };
+    for (int kt = kt0; kt <= kt1; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 <= kt1) tile(kt + 1, std::integral_constant<int, 1>{});
     }
 
     if (!wave_live) return;
-    const float lt = lsum + __shfl_xor(lsum, 32);
+    const float lt = halves_sum(lsum);
     const int t = qa + l32;
     if (t >= L) return;
     const float inv = 1.f / lt;
     TO *op = out + base + (size_t)t * tok;
-    const uint16_t *gp = gate ? gate + base + (size_t)t * tok : nullptr;
+    // gate values of this lane's outputs (1.0 without a gate), all loads issued first
+    uint2 gv[NDT][4];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) gv[dt][g4] = make_uint2(0x3F803F80u, 0x3F803F80u);
+    if (gate) {
+        const uint16_t *gp = gate + base + (size_t)t * tok;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                gv[dt][g4] = *reinterpret_cast<const uint2 *>(gp + 32 * dt + 8 * g4 + 4 * hh);
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             // rows 8 g4 + 4 hh + 0..3 of value tile dt
             const int c = 32 * dt + 8 * g4 + 4 * hh;
-            float o0 = oacc[dt][4 * g4 + 0] * inv, o1 = oacc[dt][4 * g4 + 1] * inv;
-            float o2 = oacc[dt][4 * g4 + 2] * inv, o3 = oacc[dt][4 * g4 + 3] * inv;
-            if (gp) {
-                const uint2 g = *reinterpret_cast<const uint2 *>(gp + c);
-                o0 *= __uint_as_float(g.x << 16);
-                o1 *= __uint_as_float(g.x & 0xFFFF0000u);
-                o2 *= __uint_as_float(g.y << 16);
-                o3 *= __uint_as_float(g.y & 0xFFFF0000u);
-            }
-            store4<TO>(op + c, o0, o1, o2, o3);
+            const uint2 g = gv[dt][g4];
+            store4<TO>(op + c, oacc[dt][4 * g4 + 0] * inv * __uint_as_float(g.x << 16),
+                       oacc[dt][4 * g4 + 1] * inv * __uint_as_float(g.x & 0xFFFF0000u),
+                       oacc[dt][4 * g4 + 2] * inv * __uint_as_float(g.y << 16),
+                       oacc[dt][4 * g4 + 3] * inv * __uint_as_float(g.y & 0xFFFF0000u));
         }
 }
 

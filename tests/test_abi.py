@@ -183,7 +183,7 @@ def good_swa(**kw):
     (dict(B=-1), 2), (dict(L=-1), 2), (dict(H=0), 2), (dict(d=0), 2), (dict(window=0), 2), (dict(window=-3), 2),
     (dict(qkv_dtype=5), 3), (dict(out_dtype=2), 3),
     (dict(qkv_dtype=0), 4), (dict(d=96), 4), (dict(d=256), 4),
-    (dict(B=65536, H=65536), 2),
+    (dict(B=65536, H=65536), 2), (dict(L=1 << 20, H=16), 2),
 ])
 def test_swa_rejects_bad_descriptor(kw, code):
     assert swa_call(good_swa(**kw)) == code
