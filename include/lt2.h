@@ -224,6 +224,52 @@ typedef struct lt2_swa_desc {
 lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *k, const void *v,
                            void *out, void *stream);
 
+/* Layer kinds of the looped hybrid block. */
+#define LT2_MAX_LAYERS 8
+typedef enum lt2_mixer_kind {
+    LT2_MIXER_GDN = 0,   /* gated-delta layer, as in lt2_looped_mixer */
+    LT2_MIXER_SWA = 1    /* sliding-window attention layer */
+} lt2_mixer_kind;
+
+/* Shape of the looped hybrid block: n_layers layers applied in order, T times. */
+typedef struct lt2_hybrid_desc {
+    int32_t B, L, d_model, H, d_head, T, chunk, out_gate;   /* as lt2_loop_desc */
+    int32_t window;                      /* window w of the SWA layers (>= 1) */
+    int32_t n_layers;                    /* 1 .. LT2_MAX_LAYERS */
+    int32_t kinds[LT2_MAX_LAYERS];       /* lt2_mixer_kind of each layer */
+} lt2_hybrid_desc;
+
+/*
+ * Workspace bytes lt2_hybrid_mixer needs (0 for an invalid descriptor); the
+ * same as lt2_looped_mixer's for the same sizes (layers share the buffers).
+ */
+size_t lt2_hybrid_mixer_workspace_size(const lt2_hybrid_desc *desc);
+
+/*
+ * The looped hybrid block: the LT2 summary page's hybrid strategies interleave
+ * linear (gated-delta) and sparse (window) mixers across depth and loops; here
+ * the shared block is a stack of desc->n_layers layers run in order, each with
+ * its own weights, and the block is applied T times with the same weights.
+ *   gated-delta layer i: exactly one loop of lt2_looped_mixer with W_in[i], W_o[i]
+ *   window layer i:      z = bf16(h) W_in[i]^T, q, k, v = z's first three H*d
+ *                        blocks (no normalisation), o = lt2_swa_prefill(q, k, v;
+ *                        desc->window) in bf16, with out_gate o = o * sigmoid(z_g)
+ *                        (z_g the fourth block), h = h + o W_o[i]^T
+ *   W_in, W_o  host arrays of n_layers device pointers (bf16):
+ *              gated-delta layer: W_in [3*H*d + 2*H (+ H*d), d_model] as for
+ *              lt2_looped_mixer; window layer: W_in [3*H*d (+ H*d), d_model],
+ *              rows W_q, W_k, W_v (, W_g); W_o [d_model, H*d] for both
+ *   h_in, h_out [B, L, d_model] fp32 (may be the same buffer)
+ * A block of one gated-delta layer is lt2_looped_mixer.  Requirements as for
+ * lt2_looped_mixer, and for window layers those of lt2_swa_prefill.
+ * Errors: LT2_ERR_SHAPE for n_layers outside 1..LT2_MAX_LAYERS or window < 1
+ * with a window layer; LT2_ERR_UNSUPPORTED for an unknown layer kind; otherwise
+ * as lt2_looped_mixer.
+ */
+lt2_status lt2_hybrid_mixer(const lt2_hybrid_desc *desc, const float *h_in, float *h_out,
+                            const void *const *W_in, const void *const *W_o, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /*
  * Bandwidth probe: copy `bytes` (a multiple of 16) from src to dst with one
  * streaming kernel.  Used to measure the achievable HBM bandwidth.

@@ -244,3 +244,66 @@ lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const voi
 }
 
 }  // extern "C"
+
+namespace {
+
+lt2_status check_hybrid(const lt2_hybrid_desc *d) {
+    if (!d) return LT2_ERR_NULL;
+    lt2_loop_desc ld{d->B, d->L, d->d_model, d->H, d->d_head, d->T, d->chunk, d->out_gate};
+    const lt2_status st = check_loop(&ld);
+    if (st != LT2_OK) return st;
+    if (d->n_layers < 1 || d->n_layers > LT2_MAX_LAYERS) return LT2_ERR_SHAPE;
+    bool any_swa = false;
+    for (int i = 0; i < d->n_layers; ++i) {
+        if (d->kinds[i] != LT2_MIXER_GDN && d->kinds[i] != LT2_MIXER_SWA) return LT2_ERR_UNSUPPORTED;
+        any_swa = any_swa || d->kinds[i] == LT2_MIXER_SWA;
+    }
+    if (any_swa) {
+        if (d->window < 1) return LT2_ERR_SHAPE;
+        if ((int64_t)d->L * d->H * d->d_head * 2 > 0x7fffffffLL ||
+            (int64_t)d->B * d->H * (((int64_t)d->L + 127) / 128) > 0x7fffffffLL)
+            return LT2_ERR_SHAPE;
+    }
+    return LT2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lt2_hybrid_mixer_workspace_size(const lt2_hybrid_desc *desc) {
+    if (check_hybrid(desc) != LT2_OK) return 0;
+    if (desc->B == 0 || desc->L == 0) return 0;
+    return loop_layout(desc->B, desc->L, desc->d_model, desc->H, desc->d_head, desc->chunk, desc->out_gate).total;
+}
+
+lt2_status lt2_hybrid_mixer(const lt2_hybrid_desc *desc, const float *h_in, float *h_out, const void *const *W_in,
+                            const void *const *W_o, void *ws, size_t ws_bytes, void *stream) {
+    lt2_status st = check_hybrid(desc);
+    if (st != LT2_OK) return st;
+    const bool work = desc->B > 0 && desc->L > 0;
+    if (work && (!h_in || !h_out || !W_in || !W_o)) return LT2_ERR_NULL;
+    if (!aligned(h_in, 16) || !aligned(h_out, 16)) return LT2_ERR_ALIGN;
+    if (work)
+        for (int i = 0; i < desc->n_layers; ++i) {
+            if (!W_in[i] || !W_o[i]) return LT2_ERR_NULL;
+            if (!aligned(W_in[i], 16) || !aligned(W_o[i], 16)) return LT2_ERR_ALIGN;
+        }
+    const size_t need =
+        work ? loop_layout(desc->B, desc->L, desc->d_model, desc->H, desc->d_head, desc->chunk, desc->out_gate).total : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 256)) return LT2_ERR_ALIGN;
+    if (!work) return LT2_OK;
+    HybridArgs a{};
+    a.B = desc->B; a.L = desc->L; a.D = desc->d_model; a.H = desc->H; a.d = desc->d_head; a.T = desc->T;
+    a.chunk = desc->chunk; a.gated = desc->out_gate; a.window = desc->window; a.n_layers = desc->n_layers;
+    for (int i = 0; i < desc->n_layers; ++i) {
+        a.kinds[i] = desc->kinds[i];
+        a.W_in[i] = static_cast<const uint16_t *>(W_in[i]);
+        a.W_o[i] = static_cast<const uint16_t *>(W_o[i]);
+    }
+    a.h_in = h_in; a.h_out = h_out; a.ws = ws;
+    return hip_status(launch_hybrid(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

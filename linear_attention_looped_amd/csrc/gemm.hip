@@ -17,12 +17,12 @@
 // D[8*(r/4) + 4*(l/32) + r%4][l%32].
 //
 // Epilogues (fused into the store):
-//   EPI_PROJ  input projection of the looped block: columns [0, H*d) -> q and
-//             [H*d, 2H*d) -> k, each L2-normalised per head (x / max(|x|, 1e-6))
-//             and stored bf16; [2H*d, 3H*d) -> v (bf16); with the output gate
-//             [3H*d, 4H*d) -> g = sigmoid(z) (bf16); the next H columns ->
-//             beta = sigmoid(z), the H after them -> alpha = exp(-softplus(z))
-//             (both fp32, one per head).
+//   EPI_PROJ  input projection of a looped layer: columns [0, H*d) -> q and
+//             [H*d, 2H*d) -> k, for a gated-delta layer each L2-normalised per
+//             head (x / max(|x|, 1e-6)), stored bf16; [2H*d, 3H*d) -> v (bf16);
+//             with the output gate [3H*d, 4H*d) -> g = sigmoid(z) (bf16); for a
+//             gated-delta layer the next H columns -> beta = sigmoid(z), the H
+//             after them -> alpha = exp(-softplus(z)) (both fp32, one per head).
 //   EPI_RESID residual update h[m][n] += C[m][n] (fp32), and xb[m][n] = bf16(h),
 //             the next loop's GEMM input.
 #include "common.h"
@@ -39,8 +39,9 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 struct ProjOut {
     uint16_t *q, *k, *v;   // [M, H*d] bf16
     uint16_t *g;           // [M, H*d] bf16 output gate, or nullptr
-    float *beta, *alpha;   // [M, H]
+    float *beta, *alpha;   // [M, H], or nullptr (no gate-transform columns)
     int H, d;
+    int norm;              // L2-normalise q and k per head
 };
 
 struct ResidOut {
@@ -170,7 +171,7 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
                 for (int r = 0; r < 16; ++r) {
                     const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
                     float scale[4] = {1.f, 1.f, 1.f, 1.f};
-                    if (region < 2) {
+                    if (region < 2 && po.norm) {
                         // per-head sum of squares: own tiles, then across the 32 lanes of the row
 #pragma unroll
                         for (int h0 = 0; h0 < 4; h0 += TPH) {
@@ -203,7 +204,7 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int c = nw + 32 * j + l32 - NR * Hd;
-                    if (c >= 2 * po.H) continue;
+                    if (!po.beta || c >= 2 * po.H) continue;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -237,8 +238,9 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 }  // namespace
 
 hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, int K, uint16_t *q, uint16_t *k,
-                            uint16_t *v, uint16_t *g, float *beta, float *alpha, int H, int d, hipStream_t s) {
-    ProjOut po{q, k, v, g, beta, alpha, H, d};
+                            uint16_t *v, uint16_t *g, float *beta, float *alpha, int H, int d, hipStream_t s,
+                            bool norm_qk) {
+    ProjOut po{q, k, v, g, beta, alpha, H, d, norm_qk ? 1 : 0};
     ResidOut ro{nullptr, nullptr};
     const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
     if (d == 64)

@@ -60,6 +60,19 @@ struct LoopLayout {
 LoopLayout loop_layout(int B, int L, int D, int H, int d, int chunk, bool gated);
 hipError_t launch_looped(const LoopArgs &a, hipStream_t s);
 
+// Looped hybrid block: a shared stack of layers (gated-delta or window
+// attention), applied in order, T times.
+constexpr int HYBRID_MAX_LAYERS = 8;
+struct HybridArgs {
+    int B, L, D, H, d, T, chunk, gated, window, n_layers;
+    int kinds[HYBRID_MAX_LAYERS];                 // 0 gated delta, 1 window attention
+    const float *h_in;
+    float *h_out;
+    const uint16_t *W_in[HYBRID_MAX_LAYERS], *W_o[HYBRID_MAX_LAYERS];
+    void *ws;
+};
+hipError_t launch_hybrid(const HybridArgs &a, hipStream_t s);
+
 // Looped decode: one token per sequence, T loop states carried in place.
 struct LoopDecodeArgs {
     int B, D, H, d, T, gated;

@@ -9,6 +9,11 @@
 //   h += o W_o^T, xb = bf16(h)                      (GEMM with residual epilogue)
 // All launches are enqueued on one stream; nothing synchronises in between.
 //
+// Looped hybrid: the shared block is a fixed stack of layers, each a
+// gated-delta mixer as above or a sliding-window attention mixer (the LT2
+// summary page's hybrids interleave the two kinds across depth); a window layer
+// projects q, k, v (and g) without normalisation and has no gate transforms.
+//
 // Looped decode: one new token per sequence through the same T loops, loop t
 // carrying its own recurrent state across calls (the decode form of the mixer,
 // state update equation of "Sostituire il motore"):
@@ -118,6 +123,45 @@ hipError_t launch_looped(const LoopArgs &a, hipStream_t s) {
         e = launch_gemm_resid(o, a.W_o, M, a.D, Hd, a.h_out, xb, s);
         if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+hipError_t launch_hybrid(const HybridArgs &a, hipStream_t s) {
+    const int M = a.B * a.L, Hd = a.H * a.d, NR = a.gated ? 4 : 3;
+    unsigned char *ws = static_cast<unsigned char *>(a.ws);
+    const LoopLayout w = loop_layout(a.B, a.L, a.D, a.H, a.d, a.chunk, a.gated);
+    uint16_t *gt = a.gated ? reinterpret_cast<uint16_t *>(ws + w.g) : nullptr;
+    uint16_t *xb = reinterpret_cast<uint16_t *>(ws + w.xb);
+    uint16_t *q = reinterpret_cast<uint16_t *>(ws + w.q);
+    uint16_t *k = reinterpret_cast<uint16_t *>(ws + w.k);
+    uint16_t *v = reinterpret_cast<uint16_t *>(ws + w.v);
+    float *beta = reinterpret_cast<float *>(ws + w.beta);
+    float *alpha = reinterpret_cast<float *>(ws + w.alpha);
+    uint16_t *o = reinterpret_cast<uint16_t *>(ws + w.o);
+
+    hipError_t e = launch_cast_residual(a.h_in, a.h_out, xb, (size_t)M * a.D, s);
+    if (e != hipSuccess) return e;
+    GdnArgs g{};
+    g.B = a.B; g.L = a.L; g.H = a.H; g.dk = a.d; g.dv = a.d; g.chunk = a.chunk;
+    g.qkv_bf16 = 1; g.out_bf16 = 1; g.channel = 0;
+    g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta;
+    g.state_in = nullptr; g.out = o; g.state_out = nullptr; g.ws = ws + w.prefill; g.gate = gt;
+    SwaArgs sw{};
+    sw.B = a.B; sw.L = a.L; sw.H = a.H; sw.d = a.d; sw.window = a.window; sw.out_bf16 = 1;
+    sw.q = q; sw.k = k; sw.v = v; sw.out = o; sw.gate = gt;
+    for (int t = 0; t < a.T; ++t)
+        for (int i = 0; i < a.n_layers; ++i) {
+            if (a.kinds[i] == 0) {
+                e = launch_gemm_proj(xb, a.W_in[i], M, NR * Hd + 2 * a.H, a.D, q, k, v, gt, beta, alpha, a.H, a.d, s);
+                if (e == hipSuccess) e = launch_prefill_head(g, PHASE_ALL, s);
+            } else {
+                e = launch_gemm_proj(xb, a.W_in[i], M, NR * Hd, a.D, q, k, v, gt, nullptr, nullptr, a.H, a.d, s,
+                                     false);
+                if (e == hipSuccess) e = launch_swa(sw, s);
+            }
+            if (e == hipSuccess) e = launch_gemm_resid(o, a.W_o[i], M, a.D, Hd, a.h_out, xb, s);
+            if (e != hipSuccess) return e;
+        }
     return hipSuccess;
 }
 

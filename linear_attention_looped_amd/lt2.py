@@ -34,6 +34,16 @@ class lt2_swa_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "H", "d", "window", "qkv_dtype", "out_dtype")]
 
 
+LT2_MAX_LAYERS = 8
+LT2_MIXER_GDN, LT2_MIXER_SWA = 0, 1
+_KINDS = {"gdn": LT2_MIXER_GDN, "swa": LT2_MIXER_SWA}
+
+
+class lt2_hybrid_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "d_model", "H", "d_head", "T", "chunk", "out_gate",
+                                               "window", "n_layers")] + [("kinds", ctypes.c_int32 * LT2_MAX_LAYERS)]
+
+
 class Lt2Error(RuntimeError):
     def __init__(self, fn: str, code: int):
         self.code = code
@@ -74,6 +84,11 @@ def lib() -> ctypes.CDLL:
         L.lt2_looped_decode_step.restype = S
         L.lt2_swa_prefill.argtypes = [ctypes.POINTER(lt2_swa_desc), P, P, P, P, P]
         L.lt2_swa_prefill.restype = S
+        HD = ctypes.POINTER(lt2_hybrid_desc)
+        L.lt2_hybrid_mixer_workspace_size.argtypes = [HD]
+        L.lt2_hybrid_mixer_workspace_size.restype = Z
+        L.lt2_hybrid_mixer.argtypes = [HD, P, P, P, P, P, Z, P]
+        L.lt2_hybrid_mixer.restype = S
         L.lt2_hbm_copy.argtypes = [P, P, Z, P]
         L.lt2_hbm_copy.restype = S
         _lib = L
@@ -255,6 +270,44 @@ def lt2_swa_prefill(q, k, v, window: int, out=None, out_dtype=None, stream=None)
     code = lib().lt2_swa_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream))
     _check("lt2_swa_prefill", code)
     return out
+
+
+def hybrid_desc(B, L, D, H, d_head, T, kinds, window, chunk=64, out_gate=0):
+    kk = (ctypes.c_int32 * LT2_MAX_LAYERS)(*[_KINDS.get(x, x) if isinstance(x, str) else x for x in kinds])
+    return lt2_hybrid_desc(B, L, D, H, d_head, T, chunk, int(out_gate), window, len(kinds), kk)
+
+
+def lt2_hybrid_mixer_workspace_size(desc: lt2_hybrid_desc) -> int:
+    return int(lib().lt2_hybrid_mixer_workspace_size(ctypes.byref(desc)))
+
+
+def lt2_hybrid_mixer(h_in, layers, H: int, d_head: int, T: int, window: int, chunk: int = 64, h_out=None,
+                     workspace=None, stream=None, out_gate: bool = False):
+    """T loops of a shared stack of layers; ``layers`` is a list of (kind, W_in,
+    W_o) with kind "gdn" or "swa" (bf16 weights as in include/lt2.h).
+    h_in [B,L,D] fp32.  Returns h_out [B,L,D] fp32."""
+    B, L, D = h_in.shape
+    _need(h_in, "h_in", torch.float32)
+    for kind, w_in, w_o in layers:
+        _need(w_in, "W_in", torch.bfloat16)
+        _need(w_o, "W_o", torch.bfloat16)
+        n_in = (4 if out_gate else 3) * H * d_head + (2 * H if kind == "gdn" else 0)
+        assert w_in.shape[0] == n_in, (kind, w_in.shape)
+    if h_out is None:
+        h_out = torch.empty_like(h_in)
+    desc = hybrid_desc(B, L, D, H, d_head, T, [k for k, _, _ in layers], window, chunk, out_gate)
+    ws_bytes = lt2_hybrid_mixer_workspace_size(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=h_in.device)
+    n = len(layers)
+    w_in = (ctypes.c_void_p * n)(*[w.data_ptr() for _, w, _ in layers])
+    w_o = (ctypes.c_void_p * n)(*[w.data_ptr() for _, _, w in layers])
+    code = lib().lt2_hybrid_mixer(ctypes.byref(desc), _ptr(h_in), _ptr(h_out), ctypes.cast(w_in, ctypes.c_void_p),
+                                  ctypes.cast(w_o, ctypes.c_void_p), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    _check("lt2_hybrid_mixer", code)
+    return h_out
 
 
 def lt2_hbm_copy(dst, src, stream=None):

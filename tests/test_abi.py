@@ -197,3 +197,41 @@ def test_swa_null_and_alignment():
     # empty inputs: nothing is read or written
     assert swa_call(good_swa(L=0), q=None, k=None, v=None, out=None) == 0
     assert swa_call(good_swa(B=0), q=None, k=None, v=None, out=None) == 0
+
+
+def hybrid_call(desc, h=FAKE, w_in=(FAKE,), w_o=(FAKE,), ws=FAKE, ws_bytes=1 << 40, arrays=True):
+    P = ctypes.c_void_p
+    wi = (P * len(w_in))(*w_in) if arrays else None
+    wo = (P * len(w_o))(*w_o) if arrays else None
+    return lt2.lib().lt2_hybrid_mixer(ctypes.byref(desc), P(h), P(h), ctypes.cast(wi, P) if wi else None,
+                                      ctypes.cast(wo, P) if wo else None, P(ws), ws_bytes, None)
+
+
+def good_hybrid(kinds=("gdn", "swa"), **kw):
+    d = dict(B=1, L=300, D=256, H=2, d_head=128, T=2, window=64, chunk=64, out_gate=0)
+    d.update(kw)
+    return lt2.hybrid_desc(d["B"], d["L"], d["D"], d["H"], d["d_head"], d["T"], list(kinds), d["window"],
+                           d["chunk"], d["out_gate"])
+
+
+def test_hybrid_validation():
+    assert lt2.lib().lt2_hybrid_mixer(None, None, None, None, None, None, 0, None) == 1
+    two = dict(w_in=(FAKE, FAKE), w_o=(FAKE, FAKE))
+    assert hybrid_call(good_hybrid(kinds=()), **two) == 2                       # no layers
+    d9 = good_hybrid(kinds=["gdn"] * 8)
+    d9.n_layers = 9
+    assert hybrid_call(d9, **two) == 2                                          # too many layers
+    assert hybrid_call(good_hybrid(kinds=("gdn", 7)), **two) == 4               # unknown kind
+    assert hybrid_call(good_hybrid(window=0), **two) == 2                       # window layer needs w >= 1
+    assert hybrid_call(good_hybrid(d_head=96), **two) == 4
+    assert hybrid_call(good_hybrid(D=200), **two) == 4
+    assert hybrid_call(good_hybrid(), arrays=False) == 1
+    assert hybrid_call(good_hybrid(), w_in=(FAKE, 0), w_o=(FAKE, FAKE)) == 1
+    assert hybrid_call(good_hybrid(), w_in=(FAKE, FAKE + 8), w_o=(FAKE, FAKE)) == 6
+    need = lt2.lt2_hybrid_mixer_workspace_size(good_hybrid())
+    assert need == lt2.lt2_looped_mixer_workspace_size(good_loop(B=1, L=300, d_model=256, H=2, d_head=128, T=2))
+    assert hybrid_call(good_hybrid(), ws_bytes=need - 1, **two) == 5
+    assert hybrid_call(good_hybrid(), ws=FAKE + 16, ws_bytes=need, **two) == 6
+    assert lt2.lt2_hybrid_mixer_workspace_size(good_hybrid(kinds=())) == 0
+    # a block of gated-delta layers needs no window; nothing to do for an empty batch
+    assert hybrid_call(good_hybrid(kinds=("gdn",), window=0, B=0), h=0, w_in=(0,), w_o=(0,), ws=0, ws_bytes=0) == 0
