@@ -369,6 +369,43 @@ def bench_swa(args, torch, lt2, synth, reps=20):
                 gbs=nbytes / ms / 1e6, hbm_frac=nbytes / ms / 1e6 / HBM_PEAK_GBS)
 
 
+def bench_hybrid(args, torch, lt2, synth, reps=5):
+    """Looped hybrid block, B=2 L=8192 d_model=2048 H=16 d=128, shared stack
+    (gated-delta layer, window-512 attention layer), T=4."""
+    sh = synth.CONFIGS[3]["shape"]
+    kinds, window, C = ("gdn", "swa"), 512, 64
+    log(f"hybrid inputs B={sh.B} L={sh.L} D={sh.d_model} H={sh.H} d={sh.d} T={sh.T} layers={kinds} w={window}")
+    layers = []
+    for i, kind in enumerate(kinds):
+        w = synth.loop_weights(sh, seed=0, kind=kind, layer=i)
+        layers.append((kind, torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16),
+                       torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)))
+    h0 = torch.from_numpy(synth.loop_h0(sh, seed=0)).to("cuda")
+    h_out = torch.empty_like(h0)
+    desc = lt2.hybrid_desc(sh.B, sh.L, sh.d_model, sh.H, sh.d, sh.T, list(kinds), window, C)
+    ws = torch.empty(lt2.lt2_hybrid_mixer_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    run = lambda: lt2.lt2_hybrid_mixer(h0, layers, sh.H, sh.d, sh.T, window, chunk=C, h_out=h_out, workspace=ws)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    M, D, Hd = sh.B * sh.L, sh.d_model, sh.H * sh.d
+    gemm_flops = sh.T * 2.0 * M * D * ((3 * Hd + 2 * sh.H + Hd) + (3 * Hd + Hd))
+    mixer_flops = sh.T * (prefill_flops_bytes(sh.B, sh.L, sh.H, sh.d, C)["path_flops"] +
+                          swa_flops_bytes(sh.B, sh.L, sh.H, sh.d, window)[0])
+    log(f"hybrid {ms:.3f} ms per call ({sh.T} loops of {len(kinds)} layers)")
+    return dict(B=sh.B, L=sh.L, d_model=D, H=sh.H, d=sh.d, T=sh.T, layers=list(kinds), window=window, ms=ms,
+                tokens_per_s_per_loop=M * sh.T / (ms / 1e3), gemm_flops=gemm_flops, mixer_flops=mixer_flops,
+                tflops=(gemm_flops + mixer_flops) / ms / 1e9,
+                mfma_frac=(gemm_flops + mixer_flops) / ms / 1e9 / BF16_PEAK_TFLOPS)
+
+
 def _slab_inputs(synth, shape, b0, nb):
     """Inputs of batch rows b0..b0+nb of the decode-seeding prefill (per-unit streams)."""
     L, H, d = shape.L, shape.H, shape.dk
@@ -499,6 +536,7 @@ def main():
     ap.add_argument("--no-looped-decode", action="store_true")
     ap.add_argument("--no-decode-flat", action="store_true")
     ap.add_argument("--no-swa", action="store_true")
+    ap.add_argument("--no-hybrid", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -523,6 +561,7 @@ def main():
     lde = None if args.no_looped_decode else bench_looped_decode(args, torch, lt2, synth)
     flat = None if (args.no_decode or args.no_decode_flat) else bench_decode_flat(args, torch, lt2)
     swa = None if args.no_swa else bench_swa(args, torch, lt2, synth)
+    hyb = None if args.no_hybrid else bench_hybrid(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
     value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
@@ -555,6 +594,8 @@ def main():
         extra["decode_flat"] = flat
     if swa:
         extra["swa_prefill"] = swa
+    if hyb:
+        extra["hybrid"] = hyb
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",
