@@ -53,6 +53,8 @@ def _load():
         lib.lt2o_prefill.restype = I
         lib.lt2o_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, I]
         lib.lt2o_decode_step.restype = I
+        lib.lt2o_backward.argtypes = [I, I, I, I, I, I] + [P] * 14 + [I]
+        lib.lt2o_backward.restype = I
         lib.lt2o_max_threads.restype = I
         _lib = lib
     return _lib
@@ -107,6 +109,29 @@ def decode_step(q, k, v, alpha, beta, S, threads: int = 0):
     if rc != 0:
         raise RuntimeError("lt2o_decode_step failed")
     return o, S
+
+
+def backward(q, k, v, alpha, beta, dO, S0=None, dSL=None, threads: int = 0):
+    """Gradients of loss = sum <dO, o> + <dS_L, S_L> through the token recurrence
+    (the state-update equation of "Sostituire il motore", read out o_t = S_t^T q_t).
+
+    Returns dict(dq, dk, dv, dlog_alpha, dbeta, dS0) in fp64; dlog_alpha is the
+    gradient with respect to log alpha (alpha's shape)."""
+    q, k, v, alpha, beta, dO = map(_f64, (q, k, v, alpha, beta, dO))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    channel = 1 if alpha.ndim == 4 else 0
+    S0 = None if S0 is None else _f64(S0)
+    dSL = None if dSL is None else _f64(dSL)
+    out = dict(dq=np.empty_like(q), dk=np.empty_like(k), dv=np.empty_like(v),
+               dlog_alpha=np.empty_like(alpha), dbeta=np.empty_like(beta),
+               dS0=np.empty((B, H, dk, dv), np.float64))
+    rc = _load().lt2o_backward(B, L, H, dk, dv, channel, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(S0), _ptr(dO), _ptr(dSL), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                               _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dS0"]), int(threads))
+    if rc != 0:
+        raise RuntimeError("lt2o_backward failed")
+    return out
 
 
 # ---- looped LT2-linear mixer ------------------------------------------------
