@@ -197,6 +197,37 @@ lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const voi
                                   const void *W_o, float *states, void *ws, size_t ws_bytes,
                                   void *stream);
 
+/*
+ * Workspace bytes lt2_gdn_backward needs (0 for an invalid descriptor or a
+ * per-channel gate).
+ */
+size_t lt2_gdn_backward_workspace_size(const lt2_gdn_desc *desc);
+
+/*
+ * Backward pass of lt2_gdn_prefill, scalar gate (desc->gate == LT2_GATE_HEAD):
+ * the gradients of a loss whose cotangents are d_out for the outputs o and
+ * d_state_out for the final state, through the state-update equation of the
+ * LT2 explainer (paithon.it, "Sostituire il motore") with o_t = S_t^T q_t.
+ *   q, k, v, alpha, beta, state_in   the forward call's inputs (state_in NULL = 0)
+ *   d_out        [B, L, H, d_v] of desc->out_dtype
+ *   d_state_out  [B, H, d_k, d_v] fp32, or NULL (= 0)
+ *   dq, dk       [B, L, H, d_k] fp32      dv  [B, L, H, d_v] fp32
+ *   dlog_alpha   [B, L, H] fp32, the gradient with respect to log alpha_t
+ *                (finite at alpha = 0; divide by alpha for d/d alpha)
+ *   dbeta        [B, L, H] fp32
+ *   d_state_in   [B, H, d_k, d_v] fp32, or NULL when not wanted
+ *   ws           at least lt2_gdn_backward_workspace_size(desc) bytes, 16-aligned
+ * Arithmetic is fp32 throughout (bf16 inputs are widened exactly); the chunk
+ * length used internally is 64 whatever desc->chunk holds (the result does not
+ * depend on it).  Errors: LT2_ERR_UNSUPPORTED for the channel gate; otherwise
+ * as lt2_gdn_prefill.
+ */
+lt2_status lt2_gdn_backward(const lt2_gdn_desc *desc, const void *q, const void *k,
+                            const void *v, const float *alpha, const float *beta,
+                            const float *state_in, const void *d_out, const float *d_state_out,
+                            float *dq, float *dk, float *dv, float *dlog_alpha, float *dbeta,
+                            float *d_state_in, void *ws, size_t ws_bytes, void *stream);
+
 /* Shape and types of one sliding-window attention call. */
 typedef struct lt2_swa_desc {
     int32_t B, L, H;     /* batch, tokens, heads */

@@ -141,6 +141,47 @@ lt2_status lt2_gdn_decode_step(const lt2_gdn_desc *desc, const void *q, const vo
     return hip_status(launch_decode(a, (hipStream_t)stream));
 }
 
+size_t lt2_gdn_backward_workspace_size(const lt2_gdn_desc *desc) {
+    if (check_desc(desc, false) != LT2_OK || desc->gate != LT2_GATE_HEAD) return 0;
+    if (desc->B == 0 || desc->L == 0) return 0;
+    return gdn_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k);
+}
+
+lt2_status lt2_gdn_backward(const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,
+                            const float *alpha, const float *beta, const float *state_in, const void *d_out,
+                            const float *d_state_out, float *dq, float *dk, float *dv, float *dlog_alpha,
+                            float *dbeta, float *d_state_in, void *ws, size_t ws_bytes, void *stream) {
+    lt2_status st = check_desc(desc, false);
+    if (st != LT2_OK) return st;
+    if (desc->gate != LT2_GATE_HEAD) return LT2_ERR_UNSUPPORTED;
+    const bool work = desc->B > 0 && desc->L > 0;
+    if (work && (!q || !k || !v || !alpha || !beta || !d_out || !dq || !dk || !dv || !dlog_alpha || !dbeta))
+        return LT2_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_out, 16) || !aligned(dq, 16) ||
+        !aligned(dk, 16) || !aligned(dv, 16) || !aligned(state_in, 16) || !aligned(d_state_out, 16) ||
+        !aligned(d_state_in, 16) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(dlog_alpha, 4) ||
+        !aligned(dbeta, 4))
+        return LT2_ERR_ALIGN;
+    const size_t need = work ? gdn_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k) : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 16)) return LT2_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (desc->B == 0) return LT2_OK;
+    if (desc->L == 0) {
+        // no tokens: the state passes through unchanged
+        if (!d_state_in) return LT2_OK;
+        const size_t n = (size_t)desc->B * desc->H * desc->d_k * desc->d_v;
+        return hip_status(launch_state_init(d_state_in, d_state_out, n, s));
+    }
+    GdnBwdArgs a{};
+    a.B = desc->B; a.L = desc->L; a.H = desc->H; a.d = desc->d_k;
+    a.qkv_bf16 = desc->qkv_dtype == LT2_BF16; a.dout_bf16 = desc->out_dtype == LT2_BF16;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state_in = state_in; a.dout = d_out;
+    a.dstate_out = d_state_out; a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta;
+    a.dstate_in = d_state_in; a.ws = ws;
+    return hip_status(launch_gdn_bwd(a, s));
+}
+
 lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *k, const void *v, void *out,
                            void *stream) {
     if (!desc) return LT2_ERR_NULL;

@@ -1,0 +1,715 @@
+// bwd.hip -- backward pass of the chunked gated delta rule, scalar gate.
+//
+// The forward recurrence (LT2 explainer, paithon.it, section "Sostituire il
+// motore", the state-update equation, read out o_t = S_t^T q_t) in its chunk
+// form, for one chunk of C tokens with S the state entering it:
+//   g_t  = sum_{j<=t} log2 alpha_j (chunk-relative), gamma_t = 2^g_t,
+//   Gam_ti = 2^(g_t - g_i) (i <= t), gamma_C = gamma of the chunk's last token
+//   A = strict_lower(beta_t (k_t . k_i) Gam_ti),  N = (I + A)^-1,  Tm = N diag(beta)
+//   P = lower_incl((q_t . k_i) Gam_ti)
+//   R = V - diag(gamma) K S,   U = Tm R
+//   O = diag(gamma) Q S + P U,   S' = gamma_C S + K^T diag(gamma_C / gamma) U
+// Its reverse-mode derivative for a loss with output cotangent dO and cotangent
+// dS' of the state leaving the chunk:
+//   dU = P^T dO + diag(gamma_C / gamma) K dS'      dR = diag(beta) N^T dU = dV
+//   dS = Q^T diag(gamma) dO + gamma_C dS' - K^T diag(gamma) dR      (to the previous chunk)
+//   dP = (dO U^T) o lower_incl,  dTm = dU R^T,  dA = -N^T (dTm diag(beta)) N^T  (strict lower)
+//   dQ = diag(gamma) dO S^T + (dP o Gam) K
+//   dK = (dP o Gam)^T Q + diag(gamma_C/gamma) U dS'^T - diag(gamma) dR S^T + E K + E^T K,
+//        E_ti = dA_ti beta_t Gam_ti
+//   dbeta_t = sum_s dTm_st N_st + sum_i dA_ti (k_t . k_i) Gam_ti
+// and, for the natural-log cumulative gate Gn_t (gamma_t = e^Gn_t):
+//   d(log alpha_j) = sum_{t >= j} (gq_t + gk_t) + sum_{t < j} gd_t
+//                    + sum_{t >= j} sum_{i < j} X_ti + gamma_C <dS', S>
+// with gq_t = gamma_t <dO_t, (Q S)_t>, gk_t = -gamma_t <dR_t, (K S)_t>,
+// gd_t = (gamma_C/gamma_t) <U_t, (K dS')_t> and X = dP o P + dA o A: gamma_t
+// depends on the gates up to t, gamma_C/gamma_t on those after t, and Gam_ti on
+// those in (i, t].  (Summing per-token derivatives and then a suffix sum would
+// add and cancel the pairs with i >= j, which loses the small gradient of a
+// fast-decaying gate in fp32.)
+//
+// The chunk-relative cumulative log2 gates are kept in fp64: with a fast decay
+// they reach hundreds of octaves inside a chunk, where an fp32 sum would leave
+// every decay 2^(g_t - g_i) between nearby tokens with a relative error of
+// |g| 2^-24; each decay is formed from an fp64 difference and then
+// exponentiated in fp32.
+//
+// Four launches, all fp32 arithmetic apart from those sums (bf16 inputs are
+// widened exactly):
+//   bwd_prep_kernel    one workgroup per (b, h, chunk): g, N, P into the workspace
+//   bwd_states_kernel  one per (b, h, 32-column block): the state entering every chunk
+//   bwd_dstate_kernel  one per (b, h, 32-column block), chunks in reverse: the
+//                      cotangent of the state leaving every chunk, and dS_0
+//   bwd_grads_kernel   one per (b, h, chunk): dv, dq, dk, dbeta, d(log alpha)
+// Products are LDS-tiled: each thread accumulates a TM x TN micro-tile.
+#include "common.h"
+#include "internal.h"
+
+namespace lt2 {
+
+namespace {
+
+constexpr int BC = 64;        // chunk length of the backward pass
+constexpr int BNT = 256;      // threads per workgroup
+constexpr int CPp = BC + 1;   // pitch of C x C matrices (odd: conflict-free column reads)
+
+struct BwdLayout {
+    size_t gnp, s, ds, total;   // byte offsets of the g/N/P, state and state-cotangent regions
+};
+
+// per (unit, chunk): g [C] fp64, then N, P [C][C] fp32
+constexpr size_t G_FLOATS = 2 * BC;
+constexpr size_t GNP_FLOATS = G_FLOATS + 2 * BC * BC;
+
+BwdLayout bwd_layout(int B, int L, int H, int d) {
+    const size_t units = (size_t)B * H, NC = (size_t)(L + BC - 1) / BC;
+    BwdLayout w{};
+    w.gnp = 0;
+    w.s = w.gnp + units * NC * GNP_FLOATS * 4;
+    w.ds = w.s + units * NC * (size_t)d * d * 4;
+    w.total = w.ds + units * NC * (size_t)d * d * 4;
+    return w;
+}
+
+// acc[i][j] += sum_k opA(i0 + i, k) * opB(k, j0 + j), k = 0 .. KK-1, with
+// opA(i, k) = TA ? A[k * lda + i] : A[i * lda + k] and
+// opB(k, j) = TB ? B[j * ldb + k] : B[k * ldb + j].
+template <int TM, int TN, int KK, bool TA, bool TB>
+__device__ __forceinline__ void mmt(float (&acc)[TM][TN], const float *A, int lda, const float *B, int ldb, int i0,
+                                    int j0) {
+#pragma unroll 4
+    for (int k = 0; k < KK; ++k) {
+        float a[TM], b[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = TA ? A[k * lda + i0 + i] : A[(i0 + i) * lda + k];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = TB ? B[(j0 + j) * ldb + k] : B[k * ldb + j0 + j];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
+}
+
+// Rows [t0, t0 + n) of a [.., H, width] tensor (token stride tok, element offset
+// col0) into LDS dst [BC][pitch] as fp32; rows >= n are zero.
+template <typename T>
+__device__ __forceinline__ void load_rows(float *dst, int pitch, const T *src, size_t tok, int n, int width) {
+    for (int idx = threadIdx.x; idx < BC * width; idx += BNT) {
+        const int r = idx / width, c = idx % width;
+        dst[r * pitch + c] = r < n ? to_f32(src[(size_t)r * tok + c]) : 0.f;
+    }
+}
+
+// Chunk-relative inclusive prefix sums (fp64) of log2 alpha for tokens
+// [t0, t0 + n); entries >= n repeat the last sum.  Computed by wave 0.
+__device__ __forceinline__ void gate_prefix(double *g, const float *alpha, size_t gstride, int n) {
+    if (threadIdx.x < 64) {
+        const int l = threadIdx.x;
+        double x = l < n ? (double)log2_gate(alpha[(size_t)l * gstride]) : 0.0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(x, o);
+            if (l >= o) x += y;
+        }
+        g[l] = x;
+    }
+}
+
+// 2^(a - b) from fp64 exponents
+__device__ __forceinline__ float dexp2(double a, double b) { return exp2_fast((float)(a - b)); }
+
+// ---------------------------------------------------------------------------
+// g, N = (I + A)^-1 and P of one chunk.
+template <int D, typename TI>
+__global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
+                                                       const float *__restrict__ alpha,
+                                                       const float *__restrict__ beta, float *__restrict__ gnp,
+                                                       int L, int H, int NC) {
+    constexpr int DP = D + 1;
+    __shared__ float Ks[BC * DP], Qs[BC * DP], As[BC * CPp], Ns[BC * CPp], bt[BC];
+    __shared__ double g[BC];
+    const int c = blockIdx.x % NC;
+    const size_t unit = blockIdx.x / NC;
+    const int h = (int)(unit % H), b = (int)(unit / H);
+    const int t0 = c * BC, n = min(BC, L - t0);
+    const size_t tok = (size_t)H * D;
+    const size_t row0 = ((size_t)b * L + t0) * H + h;   // (b, t0, h) in [B, L, H]
+    load_rows(Ks, DP, k + row0 * D, tok, n, D);
+    load_rows(Qs, DP, q + row0 * D, tok, n, D);
+    gate_prefix(g, alpha + row0, H, n);
+    if (threadIdx.x < BC) bt[threadIdx.x] = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+    __syncthreads();
+    const int i0 = 4 * (threadIdx.x / 16), j0 = 4 * (threadIdx.x % 16);
+    float kk[4][4], qk[4][4];
+    zero(kk);
+    zero(qk);
+    mmt<4, 4, D, false, true>(kk, Ks, DP, Ks, DP, i0, j0);
+    mmt<4, 4, D, false, true>(qk, Qs, DP, Ks, DP, i0, j0);
+    float *out = gnp + (unit * NC + c) * GNP_FLOATS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = i0 + i, s = j0 + j;
+            const float gam = dexp2(g[t], g[min(s, t)]);
+            As[t * CPp + s] = s < t ? bt[t] * kk[i][j] * gam : 0.f;
+            out[G_FLOATS + BC * BC + t * BC + s] = (s <= t && t < n) ? qk[i][j] * gam : 0.f;   // P
+        }
+    if (threadIdx.x < BC) reinterpret_cast<double *>(out)[threadIdx.x] = g[threadIdx.x];
+    __syncthreads();
+    // N = (I + A)^-1 by rows: N_t = e_t - sum_{i<t} A_ti N_i
+    for (int t = 0; t < BC; ++t) {
+        if (threadIdx.x < BC) {
+            const int j = threadIdx.x;
+            float x = t == j ? 1.f : 0.f;
+            for (int i = j; i < t; ++i) x = fmaf(-As[t * CPp + i], Ns[i * CPp + j], x);
+            Ns[t * CPp + j] = j <= t ? x : 0.f;
+        }
+        __syncthreads();
+    }
+    for (int idx = threadIdx.x; idx < BC * BC; idx += BNT)
+        out[G_FLOATS + idx] = Ns[(idx / BC) * CPp + idx % BC];
+}
+
+// ---------------------------------------------------------------------------
+// The state entering every chunk, per 32-column block of the value dimension.
+template <int D, typename TI>
+__global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ k, const TI *__restrict__ v,
+                                                         const float *__restrict__ beta,
+                                                         const float *__restrict__ state_in,
+                                                         const float *__restrict__ gnp, float *__restrict__ sws,
+                                                         int L, int H, int NC) {
+    constexpr int BV = 32, DP = D + 1, VP = BV + 1;
+    __shared__ float Ss[D * VP], Ks[BC * DP], Vs[BC * VP], Ns[BC * CPp], Rs[BC * VP], Us[BC * VP], bt[BC];
+    __shared__ double g[BC];
+    constexpr int NB = D / BV;
+    const int vb = blockIdx.x % NB;
+    const size_t unit = blockIdx.x / NB;
+    const int h = (int)(unit % H), b = (int)(unit / H);
+    const size_t tok = (size_t)H * D;
+    for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
+        const int r = idx / BV, cc = idx % BV;
+        Ss[r * VP + cc] = state_in ? state_in[(unit * D + r) * D + vb * BV + cc] : 0.f;
+    }
+    for (int c = 0; c < NC; ++c) {
+        const int t0 = c * BC, n = min(BC, L - t0);
+        const size_t row0 = ((size_t)b * L + t0) * H + h;
+        const float *gc = gnp + (unit * NC + c) * GNP_FLOATS;
+        __syncthreads();
+        // the state entering chunk c
+        float *so = sws + (unit * NC + c) * (size_t)D * D;
+        for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
+            const int r = idx / BV, cc = idx % BV;
+            so[r * D + vb * BV + cc] = Ss[r * VP + cc];
+        }
+        load_rows(Ks, DP, k + row0 * D, tok, n, D);
+        load_rows(Vs, VP, v + row0 * D + vb * BV, tok, n, BV);
+        for (int idx = threadIdx.x; idx < BC * BC; idx += BNT) Ns[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + idx];
+        if (threadIdx.x < BC) {
+            g[threadIdx.x] = reinterpret_cast<const double *>(gc)[threadIdx.x];
+            bt[threadIdx.x] = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+        }
+        __syncthreads();
+        const double gC = g[n - 1];
+        {   // R' = diag(beta) (V - diag(gamma) K S)
+            const int i0 = 4 * (threadIdx.x / 16), j0 = 2 * (threadIdx.x % 16);
+            float ks[4][2];
+            zero(ks);
+            mmt<4, 2, D, false, false>(ks, Ks, DP, Ss, VP, i0, j0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = i0 + i;
+                    Rs[t * VP + j0 + j] = bt[t] * (Vs[t * VP + j0 + j] - dexp2(g[t], 0.0) * ks[i][j]);
+                }
+        }
+        __syncthreads();
+        {   // U' = diag(gamma_C / gamma) N R'
+            const int i0 = 4 * (threadIdx.x / 16), j0 = 2 * (threadIdx.x % 16);
+            float u[4][2];
+            zero(u);
+            mmt<4, 2, BC, false, false>(u, Ns, CPp, Rs, VP, i0, j0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) Us[(i0 + i) * VP + j0 + j] = dexp2(gC, g[i0 + i]) * u[i][j];
+        }
+        __syncthreads();
+        {   // S = gamma_C S + K^T U'  (D x 32: D / 32 rows x 4 columns per thread)
+            constexpr int TM = D / 32;
+            const int i0 = TM * (threadIdx.x / 8), j0 = 4 * (threadIdx.x % 8);
+            float s[TM][4];
+            zero(s);
+            mmt<TM, 4, BC, true, false>(s, Ks, DP, Us, VP, i0, j0);
+            const float gam = dexp2(gC, 0.0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Ss[(i0 + i) * VP + j0 + j] = fmaf(gam, Ss[(i0 + i) * VP + j0 + j], s[i][j]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chunks in reverse: the cotangent of the state leaving every chunk (stored) and
+// finally that of S_0.
+template <int D, typename TI, typename TO>
+__global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
+                                                         const TO *__restrict__ dout, const float *__restrict__ beta,
+                                                         const float *__restrict__ dstate_out,
+                                                         const float *__restrict__ gnp, float *__restrict__ dsws,
+                                                         float *__restrict__ dstate_in, int L, int H, int NC) {
+    constexpr int BV = 32, DP = D + 1, VP = BV + 1;
+    __shared__ float dS[D * VP], Ks[BC * DP], Qs[BC * DP], dOs[BC * VP], Ns[BC * CPp], Ps[BC * CPp], dUs[BC * VP],
+        dRs[BC * VP], bt[BC];
+    __shared__ double g[BC];
+    constexpr int NB = D / BV;
+    const int vb = blockIdx.x % NB;
+    const size_t unit = blockIdx.x / NB;
+    const int h = (int)(unit % H), b = (int)(unit / H);
+    const size_t tok = (size_t)H * D;
+    for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
+        const int r = idx / BV, cc = idx % BV;
+        dS[r * VP + cc] = dstate_out ? dstate_out[(unit * D + r) * D + vb * BV + cc] : 0.f;
+    }
+    for (int c = NC - 1; c >= 0; --c) {
+        const int t0 = c * BC, n = min(BC, L - t0);
+        const size_t row0 = ((size_t)b * L + t0) * H + h;
+        const float *gc = gnp + (unit * NC + c) * GNP_FLOATS;
+        __syncthreads();
+        float *dso = dsws + (unit * NC + c) * (size_t)D * D;
+        for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
+            const int r = idx / BV, cc = idx % BV;
+            dso[r * D + vb * BV + cc] = dS[r * VP + cc];
+        }
+        load_rows(Ks, DP, k + row0 * D, tok, n, D);
+        load_rows(Qs, DP, q + row0 * D, tok, n, D);
+        load_rows(dOs, VP, dout + row0 * D + vb * BV, tok, n, BV);
+        for (int idx = threadIdx.x; idx < BC * BC; idx += BNT) {
+            Ns[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + idx];
+            Ps[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + BC * BC + idx];
+        }
+        if (threadIdx.x < BC) {
+            g[threadIdx.x] = reinterpret_cast<const double *>(gc)[threadIdx.x];
+            bt[threadIdx.x] = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+        }
+        __syncthreads();
+        const double gC = g[n - 1];
+        {   // dU = P^T dO + diag(gamma_C / gamma) K dS'
+            const int i0 = 4 * (threadIdx.x / 16), j0 = 2 * (threadIdx.x % 16);
+            float a1[4][2], a2[4][2];
+            zero(a1);
+            zero(a2);
+            mmt<4, 2, BC, true, false>(a1, Ps, CPp, dOs, VP, i0, j0);
+            mmt<4, 2, D, false, false>(a2, Ks, DP, dS, VP, i0, j0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    dUs[(i0 + i) * VP + j0 + j] = fmaf(dexp2(gC, g[i0 + i]), a2[i][j], a1[i][j]);
+        }
+        __syncthreads();
+        {   // dR = diag(beta) N^T dU, kept as diag(gamma) dR for the state update
+            const int i0 = 4 * (threadIdx.x / 16), j0 = 2 * (threadIdx.x % 16);
+            float a[4][2];
+            zero(a);
+            mmt<4, 2, BC, true, false>(a, Ns, CPp, dUs, VP, i0, j0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = i0 + i;
+                    dRs[t * VP + j0 + j] = dexp2(g[t], 0.0) * bt[t] * a[i][j];
+                    dOs[t * VP + j0 + j] *= dexp2(g[t], 0.0);   // diag(gamma) dO
+                }
+        }
+        __syncthreads();
+        {   // dS = Q^T diag(gamma) dO + gamma_C dS' - K^T diag(gamma) dR  (D / 32 rows x 4 per thread)
+            constexpr int TM = D / 32;
+            const int i0 = TM * (threadIdx.x / 8), j0 = 4 * (threadIdx.x % 8);
+            float a1[TM][4], a2[TM][4];
+            zero(a1);
+            zero(a2);
+            mmt<TM, 4, BC, true, false>(a1, Qs, DP, dOs, VP, i0, j0);
+            mmt<TM, 4, BC, true, false>(a2, Ks, DP, dRs, VP, i0, j0);
+            const float gam = dexp2(gC, 0.0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float &x = dS[(i0 + i) * VP + j0 + j];
+                    x = fmaf(gam, x, a1[i][j] - a2[i][j]);
+                }
+        }
+    }
+    __syncthreads();
+    if (dstate_in)
+        for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
+            const int r = idx / BV, cc = idx % BV;
+            dstate_in[(unit * D + r) * D + vb * BV + cc] = dS[r * VP + cc];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk gradients.  The value dimension is walked in blocks of 16 columns;
+// dQ, dK (C x D) and dP, dTm (C x C) accumulate in registers across blocks.
+template <int D, typename TI, typename TO>
+__global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
+                                                        const TI *__restrict__ v, const TO *__restrict__ dout,
+                                                        const float *__restrict__ beta,
+                                                        const float *__restrict__ gnp,
+                                                        const float *__restrict__ sws,
+                                                        const float *__restrict__ dsws, float *__restrict__ dq,
+                                                        float *__restrict__ dk, float *__restrict__ dv,
+                                                        float *__restrict__ dlog_alpha, float *__restrict__ dbeta,
+                                                        int L, int H, int NC) {
+    constexpr int BV = 16, DP = D + 1, VP = BV + 1;
+    // phase-1 buffers (per value block) and phase-2 buffers (C x C) share one region
+    constexpr int P1 = 2 * D * VP + 9 * BC * VP;
+    constexpr int P2 = 3 * BC * CPp;
+    constexpr int UN = P1 > P2 ? P1 : P2;
+    __shared__ float Qs[BC * DP], Ks[BC * DP], Ns[BC * CPp], Ps[BC * CPp], un[UN];
+    __shared__ float bt[BC], gq[BC], gk[BC], gd[BC], red[BNT];
+    __shared__ double g[BC];
+    float *Sb = un, *dSb = Sb + D * VP, *Vb = dSb + D * VP, *dOb = Vb + BC * VP, *KS = dOb + BC * VP,
+          *QS = KS + BC * VP, *KdS = QS + BC * VP, *Rb = KdS + BC * VP, *Ub = Rb + BC * VP, *dUb = Ub + BC * VP,
+          *dRb = dUb + BC * VP;
+    float *X1 = un, *X2 = un + BC * CPp, *X3 = un + 2 * BC * CPp;
+
+    const int c = blockIdx.x % NC;
+    const size_t unit = blockIdx.x / NC;
+    const int h = (int)(unit % H), b = (int)(unit / H);
+    const int t0 = c * BC, n = min(BC, L - t0);
+    const size_t tok = (size_t)H * D;
+    const size_t row0 = ((size_t)b * L + t0) * H + h;
+    const float *gc = gnp + (unit * NC + c) * GNP_FLOATS;
+    const float *Sc = sws + (unit * NC + c) * (size_t)D * D;
+    const float *dSc = dsws + (unit * NC + c) * (size_t)D * D;
+    const int tid = threadIdx.x;
+
+    load_rows(Ks, DP, k + row0 * D, tok, n, D);
+    load_rows(Qs, DP, q + row0 * D, tok, n, D);
+    for (int idx = tid; idx < BC * BC; idx += BNT) {
+        Ns[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + idx];
+        Ps[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + BC * BC + idx];
+    }
+    if (tid < BC) {
+        g[tid] = reinterpret_cast<const double *>(gc)[tid];
+        bt[tid] = tid < n ? beta[row0 + (size_t)tid * H] : 0.f;
+        gq[tid] = gk[tid] = gd[tid] = 0.f;
+    }
+    float sdot = 0.f;
+    // register accumulators: dQ, dK rows 4 (tid / 16) .., columns QTN (tid % 16) ..;
+    // dP, dTm 4 x 4
+    constexpr int QTN = D / 16;
+    const int qi0 = 4 * (tid / 16), qj0 = QTN * (tid % 16);
+    const int pi0 = 4 * (tid / 16), pj0 = 4 * (tid % 16);
+    float aq[4][QTN], ak[4][QTN], ap[4][4], at[4][4];
+    zero(aq);
+    zero(ak);
+    zero(ap);
+    zero(at);
+    __syncthreads();
+    const double gC = g[n - 1];
+
+    for (int vb = 0; vb < D / BV; ++vb) {
+        for (int idx = tid; idx < D * BV; idx += BNT) {
+            const int r = idx / BV, cc = idx % BV;
+            Sb[r * VP + cc] = Sc[r * D + vb * BV + cc];
+            dSb[r * VP + cc] = dSc[r * D + vb * BV + cc];
+            sdot = fmaf(Sb[r * VP + cc], dSb[r * VP + cc], sdot);
+        }
+        load_rows(Vb, VP, v + row0 * D + vb * BV, tok, n, BV);
+        load_rows(dOb, VP, dout + row0 * D + vb * BV, tok, n, BV);
+        __syncthreads();
+        // KS = K S, QS = Q S, KdS = K dS' (C x BV)
+        const int i0 = 2 * (tid / 8), j0 = 2 * (tid % 8);
+        {
+            float a1[2][2], a2[2][2], a3[2][2];
+            zero(a1);
+            zero(a2);
+            zero(a3);
+            mmt<2, 2, D, false, false>(a1, Ks, DP, Sb, VP, i0, j0);
+            mmt<2, 2, D, false, false>(a2, Qs, DP, Sb, VP, i0, j0);
+            mmt<2, 2, D, false, false>(a3, Ks, DP, dSb, VP, i0, j0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = i0 + i, s = j0 + j;
+                    KS[t * VP + s] = a1[i][j];
+                    QS[t * VP + s] = a2[i][j];
+                    KdS[t * VP + s] = a3[i][j];
+                    Rb[t * VP + s] = Vb[t * VP + s] - dexp2(g[t], 0.0) * a1[i][j];   // R
+                }
+        }
+        __syncthreads();
+        {   // U = N diag(beta) R ; dU = P^T dO + diag(gamma_C/gamma) K dS'
+            float a1[2][2], a2[2][2];
+            zero(a1);
+            zero(a2);
+#pragma unroll 4
+            for (int kk = 0; kk < BC; ++kk) {
+                const float w = bt[kk];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        a1[i][j] = fmaf(Ns[(i0 + i) * CPp + kk] * w, Rb[kk * VP + j0 + j], a1[i][j]);
+                        a2[i][j] = fmaf(Ps[kk * CPp + i0 + i], dOb[kk * VP + j0 + j], a2[i][j]);
+                    }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = i0 + i, s = j0 + j;
+                    Ub[t * VP + s] = a1[i][j];
+                    dUb[t * VP + s] = fmaf(dexp2(gC, g[t]), KdS[t * VP + s], a2[i][j]);
+                }
+        }
+        __syncthreads();
+        {   // dR = diag(beta) N^T dU  (= dV)
+            float a1[2][2];
+            zero(a1);
+            mmt<2, 2, BC, true, false>(a1, Ns, CPp, dUb, VP, i0, j0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int t = i0 + i, s = j0 + j;
+                    const float r = bt[t] * a1[i][j];
+                    dRb[t * VP + s] = r;
+                    if (t < n) dv[(row0 + (size_t)t * H) * D + vb * BV + s] = r;
+                }
+        }
+        __syncthreads();
+        // gate row terms (wave 0): gamma <dO, QS>, -gamma <dR, KS>, (gamma_C/gamma) <U, KdS>
+        if (tid < BC) {
+            const int t = tid;
+            float x1 = 0.f, x2 = 0.f, x3 = 0.f;
+#pragma unroll
+            for (int s = 0; s < BV; ++s) {
+                x1 = fmaf(dOb[t * VP + s], QS[t * VP + s], x1);
+                x2 = fmaf(dRb[t * VP + s], KS[t * VP + s], x2);
+                x3 = fmaf(Ub[t * VP + s], KdS[t * VP + s], x3);
+            }
+            gq[t] += dexp2(g[t], 0.0) * x1;
+            gk[t] -= dexp2(g[t], 0.0) * x2;
+            gd[t] += dexp2(gC, g[t]) * x3;
+        }
+        // register accumulations over this value block
+        //   dQ += diag(gamma) dO S^T ; dK += diag(gamma_C/gamma) U dS'^T - diag(gamma) dR S^T
+        //   dP += dO U^T ; dTm += dU R^T
+#pragma unroll 2
+        for (int s = 0; s < BV; ++s) {
+            float sq[QTN], sd[QTN];
+#pragma unroll
+            for (int j = 0; j < QTN; ++j) {
+                sq[j] = Sb[(qj0 + j) * VP + s];
+                sd[j] = dSb[(qj0 + j) * VP + s];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = qi0 + i;
+                const float e = dexp2(g[t], 0.0);
+                const float o = e * dOb[t * VP + s];
+                const float u = dexp2(gC, g[t]) * Ub[t * VP + s];
+                const float r = e * dRb[t * VP + s];
+#pragma unroll
+                for (int j = 0; j < QTN; ++j) {
+                    aq[i][j] = fmaf(o, sq[j], aq[i][j]);
+                    ak[i][j] = fmaf(u, sd[j], fmaf(-r, sq[j], ak[i][j]));
+                }
+            }
+            float uu[4], rr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uu[j] = Ub[(pj0 + j) * VP + s];
+                rr[j] = Rb[(pj0 + j) * VP + s];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float o = dOb[(pi0 + i) * VP + s], du = dUb[(pi0 + i) * VP + s];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    ap[i][j] = fmaf(o, uu[j], ap[i][j]);
+                    at[i][j] = fmaf(du, rr[j], at[i][j]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 2: C x C algebra (buffers X1..X3 replace the value-block buffers) ----
+    // (a) X1 = dP o Gam (lower incl, rows < n), X2 = dTm, X3 = Q K^T
+    {
+        float qk[4][4];
+        zero(qk);
+        mmt<4, 4, D, false, true>(qk, Qs, DP, Ks, DP, pi0, pj0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = pi0 + i, s = pj0 + j;
+                const float gam = dexp2(g[t], g[min(s, t)]);
+                X1[t * CPp + s] = (s <= t && t < n) ? ap[i][j] * gam : 0.f;
+                X2[t * CPp + s] = at[i][j];
+                X3[t * CPp + s] = qk[i][j];
+            }
+    }
+    __syncthreads();
+    // (b) dQ += (dP o Gam) K ; dK += (dP o Gam)^T Q ; X = dP o P = X1 o QK^T into Ps
+    //     (P is no longer needed) ; dbeta from Tm = N diag(beta): sum_s dTm_st N_st
+    mmt<4, QTN, BC, false, false>(aq, X1, CPp, Ks, DP, qi0, qj0);
+    mmt<4, QTN, BC, true, false>(ak, X1, CPp, Qs, DP, qi0, qj0);
+    for (int idx = tid; idx < BC * BC; idx += BNT) {
+        const int t = idx / BC, s = idx % BC;
+        Ps[t * CPp + s] = X1[t * CPp + s] * X3[t * CPp + s];
+    }
+    float dbt = 0.f;
+    if (tid < BC) {
+        const int t = tid;
+        for (int s = 0; s < BC; ++s) dbt = fmaf(X2[s * CPp + t], Ns[s * CPp + t], dbt);
+    }
+    __syncthreads();
+    // (c) T1 = N^T dTm diag(beta) into X1 ; X3 = K K^T
+    {
+        float a[4][4], kk[4][4];
+        zero(a);
+        zero(kk);
+        mmt<4, 4, BC, true, false>(a, Ns, CPp, X2, CPp, pi0, pj0);
+        mmt<4, 4, D, false, true>(kk, Ks, DP, Ks, DP, pi0, pj0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                X1[(pi0 + i) * CPp + pj0 + j] = a[i][j] * bt[pj0 + j];
+                X3[(pi0 + i) * CPp + pj0 + j] = kk[i][j];
+            }
+    }
+    __syncthreads();
+    // (d) dA = -T1 N^T, strict lower part, into X2
+    {
+        float a[4][4];
+        zero(a);
+        mmt<4, 4, BC, false, true>(a, X1, CPp, Ns, CPp, pi0, pj0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = pi0 + i, s = pj0 + j;
+                X2[t * CPp + s] = s < t ? -a[i][j] : 0.f;
+            }
+    }
+    __syncthreads();
+    // (e) E = dA beta_t Gam into X1 ; X += dA o A (A = beta_t K K^T Gam) ;
+    //     dbeta from A: sum_s dA_ts (k_t . k_s) Gam_ts
+    for (int idx = tid; idx < BC * BC; idx += BNT) {
+        const int t = idx / BC, s = idx % BC;
+        const float gts = s < t ? dexp2(g[t], g[s]) : 0.f;
+        const float kg = X3[t * CPp + s] * gts;
+        X1[t * CPp + s] = X2[t * CPp + s] * bt[t] * gts;
+        Ps[t * CPp + s] = fmaf(X2[t * CPp + s], bt[t] * kg, Ps[t * CPp + s]);
+    }
+    if (tid < BC) {
+        const int t = tid;
+        for (int s = 0; s < t; ++s) dbt = fmaf(X2[t * CPp + s], X3[t * CPp + s] * dexp2(g[t], g[s]), dbt);
+    }
+    __syncthreads();
+    // (f) dK += E K + E^T K
+    mmt<4, QTN, BC, false, false>(ak, X1, CPp, Ks, DP, qi0, qj0);
+    mmt<4, QTN, BC, true, false>(ak, X1, CPp, Ks, DP, qi0, qj0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = qi0 + i;
+        if (t < n)
+#pragma unroll
+            for (int j = 0; j < QTN; ++j) {
+                dq[(row0 + (size_t)t * H) * D + qj0 + j] = aq[i][j];
+                dk[(row0 + (size_t)t * H) * D + qj0 + j] = ak[i][j];
+            }
+    }
+    // gate (wave 0, thread j = token j of the chunk)
+    red[tid] = sdot;
+    __syncthreads();
+    if (tid < 64) {
+        float x = red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+        const int j = tid;
+        // suffix sums of gq + gk over t >= j, exclusive prefix sums of gd over t < j
+        float suf = j < n ? gq[j] + gk[j] : 0.f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float z = __shfl_down(suf, o);
+            if (j + o < 64) suf += z;
+        }
+        float pre = j < n ? gd[j] : 0.f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float z = __shfl_up(pre, o);
+            if (j >= o) pre += z;
+        }
+        pre -= j < n ? gd[j] : 0.f;
+        // pairs i < j <= t of X (lower triangular, rows < n)
+        float cross = 0.f;
+        for (int t = j; t < n; ++t)
+            for (int i = 0; i < j; ++i) cross += Ps[t * CPp + i];
+        if (j < n) {
+            dlog_alpha[row0 + (size_t)j * H] = suf + pre + cross + dexp2(gC, 0.0) * x;
+            dbeta[row0 + (size_t)j * H] = dbt;
+        }
+    }
+}
+
+template <int D, typename TI, typename TO>
+hipError_t launch_bwd_d(const GdnBwdArgs &a, hipStream_t s) {
+    const int NC = (a.L + BC - 1) / BC;
+    const BwdLayout w = bwd_layout(a.B, a.L, a.H, D);
+    unsigned char *ws = static_cast<unsigned char *>(a.ws);
+    float *gnp = reinterpret_cast<float *>(ws + w.gnp);
+    float *sws = reinterpret_cast<float *>(ws + w.s);
+    float *dsws = reinterpret_cast<float *>(ws + w.ds);
+    const TI *q = static_cast<const TI *>(a.q), *k = static_cast<const TI *>(a.k), *v = static_cast<const TI *>(a.v);
+    const TO *dout = static_cast<const TO *>(a.dout);
+    const unsigned units = (unsigned)((size_t)a.B * a.H);
+    hipLaunchKernelGGL((bwd_prep_kernel<D, TI>), dim3(units * NC), dim3(BNT), 0, s, q, k, a.alpha, a.beta, gnp, a.L,
+                       a.H, NC);
+    hipLaunchKernelGGL((bwd_states_kernel<D, TI>), dim3(units * (D / 32)), dim3(BNT), 0, s, k, v, a.beta,
+                       a.state_in, gnp, sws, a.L, a.H, NC);
+    hipLaunchKernelGGL((bwd_dstate_kernel<D, TI, TO>), dim3(units * (D / 32)), dim3(BNT), 0, s, q, k, dout, a.beta,
+                       a.dstate_out, gnp, dsws, a.dstate_in, a.L, a.H, NC);
+    hipLaunchKernelGGL((bwd_grads_kernel<D, TI, TO>), dim3(units * NC), dim3(BNT), 0, s, q, k, v, dout, a.beta, gnp,
+                       sws, dsws, a.dq, a.dk, a.dv, a.dlog_alpha, a.dbeta, a.L, a.H, NC);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_dt(const GdnBwdArgs &a, hipStream_t s) {
+    if (a.qkv_bf16)
+        return a.dout_bf16 ? launch_bwd_d<D, uint16_t, uint16_t>(a, s) : launch_bwd_d<D, uint16_t, float>(a, s);
+    return a.dout_bf16 ? launch_bwd_d<D, float, uint16_t>(a, s) : launch_bwd_d<D, float, float>(a, s);
+}
+
+}  // namespace
+
+size_t gdn_bwd_ws_bytes(int B, int L, int H, int d) { return bwd_layout(B, L, H, d).total; }
+
+hipError_t launch_gdn_bwd(const GdnBwdArgs &a, hipStream_t s) {
+    if (a.B == 0 || a.L == 0) return hipSuccess;
+    return a.d == 64 ? launch_bwd_dt<64>(a, s) : launch_bwd_dt<128>(a, s);
+}
+
+}  // namespace lt2

@@ -45,6 +45,22 @@ struct SwaArgs {
 };
 hipError_t launch_swa(const SwaArgs &a, hipStream_t s);
 
+// Backward pass of the gated-delta prefill, scalar gate; gradients fp32.
+struct GdnBwdArgs {
+    int B, L, H, d, qkv_bf16, dout_bf16;
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    const float *state_in;      // [B, H, d, d] or nullptr (zero)
+    const void *dout;           // [B, L, H, d], bf16 or fp32
+    const float *dstate_out;    // [B, H, d, d] or nullptr (zero)
+    float *dq, *dk, *dv;        // [B, L, H, d]
+    float *dlog_alpha, *dbeta;  // [B, L, H]
+    float *dstate_in;           // [B, H, d, d] or nullptr
+    void *ws;
+};
+size_t gdn_bwd_ws_bytes(int B, int L, int H, int d);
+hipError_t launch_gdn_bwd(const GdnBwdArgs &a, hipStream_t s);
+
 // Looped LT2-linear block.
 struct LoopArgs {
     int B, L, D, H, d, T, chunk, gated;

@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
         L.lt2_looped_decode_workspace_size.restype = Z
         L.lt2_looped_decode_step.argtypes = [LD, P, P, P, P, P, Z, P]
         L.lt2_looped_decode_step.restype = S
+        L.lt2_gdn_backward_workspace_size.argtypes = [GD]
+        L.lt2_gdn_backward_workspace_size.restype = Z
+        L.lt2_gdn_backward.argtypes = [GD] + [P] * 15 + [Z, P]
+        L.lt2_gdn_backward.restype = S
         L.lt2_swa_prefill.argtypes = [ctypes.POINTER(lt2_swa_desc), P, P, P, P, P]
         L.lt2_swa_prefill.restype = S
         HD = ctypes.POINTER(lt2_hybrid_desc)
@@ -248,6 +252,43 @@ def lt2_looped_decode_step(h, W_in, W_o, states, H: int, d_head: int, T: int, wo
                                         _stream(stream))
     _check("lt2_looped_decode_step", code)
     return h
+
+
+def lt2_gdn_backward_workspace_size(desc: lt2_gdn_desc) -> int:
+    return int(lib().lt2_gdn_backward_workspace_size(ctypes.byref(desc)))
+
+
+def lt2_gdn_backward(q, k, v, alpha, beta, d_out, state_in=None, d_state_out=None, want_state_grad=True,
+                     workspace=None, stream=None):
+    """Gradients of the gated-delta prefill (scalar gate) for the output
+    cotangent d_out [B,L,H,d_v] and final-state cotangent d_state_out (or None).
+    Returns dict(dq, dk, dv, dlog_alpha, dbeta, d_state_in) of fp32 tensors."""
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(alpha, "alpha", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(d_out, "d_out")
+    assert alpha.dim() == 3, "the backward pass is built for the scalar gate"
+    dev = q.device
+    desc = gdn_desc(B, L, H, dk, dv, 64, _dt(q), _dt(d_out), LT2_GATE_HEAD)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, L, H, dk), **f32), dk=torch.empty((B, L, H, dk), **f32),
+               dv=torch.empty((B, L, H, dv), **f32), dlog_alpha=torch.empty((B, L, H), **f32),
+               dbeta=torch.empty((B, L, H), **f32),
+               d_state_in=torch.empty((B, H, dk, dv), **f32) if want_state_grad else None)
+    ws_bytes = lt2_gdn_backward_workspace_size(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    code = lib().lt2_gdn_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(state_in), _ptr(d_out), _ptr(d_state_out), _ptr(out["dq"]),
+                                  _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
+                                  _ptr(out["d_state_in"]), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    _check("lt2_gdn_backward", code)
+    return out
 
 
 def swa_desc(B, L, H, d, window, qkv_dtype=LT2_BF16, out_dtype=LT2_BF16):

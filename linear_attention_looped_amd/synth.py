@@ -31,6 +31,7 @@ T_Q, T_K, T_V, T_BETA, T_ALPHA = 1, 2, 3, 4, 5
 T_H0, T_WIN, T_WO, T_WG = 6, 7, 8, 9
 T_DQ, T_DK, T_DV, T_DBETA, T_DALPHA = 11, 12, 13, 14, 15
 T_SQ, T_SK, T_SV = 16, 17, 18
+T_GO = 19
 
 
 def _threads() -> int:
@@ -100,6 +101,26 @@ def gdn_unit(shape: GDNShape, seed: int, b: int, h: int) -> dict:
     if shape.dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     return dict(q=q, k=k, v=v, alpha=alpha, beta=beta)
+
+
+def grad_out_unit(shape: GDNShape, seed: int, b: int, h: int) -> np.ndarray:
+    """Output cotangent dO [L, dv] of one unit for the backward pass: N(0,1),
+    rounded to bf16 for bf16 workloads."""
+    x = rng(seed, T_GO, b, h).standard_normal((shape.L, shape.dv), dtype=np.float32)
+    return bf16_round(x) if shape.dtype == "bf16" else x
+
+
+def grad_out(shape: GDNShape, seed: int = 0) -> np.ndarray:
+    """dO [B, L, H, dv], unit by unit as ``grad_out_unit``."""
+    out = np.empty((shape.B, shape.L, shape.H, shape.dv), np.float32)
+
+    def fill(bh):
+        b, h = divmod(bh, shape.H)
+        out[b, :, h] = grad_out_unit(shape, seed, b, h)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(shape.B * shape.H)))
+    return out
 
 
 def gdn_inputs(shape: GDNShape, seed: int = 0) -> dict:

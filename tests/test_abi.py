@@ -235,3 +235,33 @@ def test_hybrid_validation():
     assert lt2.lt2_hybrid_mixer_workspace_size(good_hybrid(kinds=())) == 0
     # a block of gated-delta layers needs no window; nothing to do for an empty batch
     assert hybrid_call(good_hybrid(kinds=("gdn",), window=0, B=0), h=0, w_in=(0,), w_o=(0,), ws=0, ws_bytes=0) == 0
+
+
+def bwd_call(desc, ws_bytes=1 << 40, **kw):
+    P = ctypes.c_void_p
+    a = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, s_in=None, d_out=FAKE, ds_out=None, dq=FAKE, dk=FAKE,
+             dv=FAKE, dla=FAKE, db=FAKE, ds_in=None, ws=FAKE)
+    a.update(kw)
+    return lt2.lib().lt2_gdn_backward(ctypes.byref(desc), *[P(a[n]) for n in (
+        "q", "k", "v", "alpha", "beta", "s_in", "d_out", "ds_out", "dq", "dk", "dv", "dla", "db", "ds_in", "ws")],
+        ws_bytes, None)
+
+
+def test_backward_validation():
+    assert bwd_call(good_desc(gate=1)) == 4                  # channel gate not built
+    assert lt2.lt2_gdn_backward_workspace_size(good_desc(gate=1)) == 0
+    assert bwd_call(good_desc(d_k=96, d_v=96)) == 4
+    assert bwd_call(good_desc(B=-1)) == 2
+    assert bwd_call(good_desc(), db=None) == 1
+    assert bwd_call(good_desc(), d_out=None) == 1
+    assert bwd_call(good_desc(), dq=FAKE + 4) == 6
+    assert bwd_call(good_desc(), dla=FAKE + 2) == 6
+    need = lt2.lt2_gdn_backward_workspace_size(good_desc())
+    assert need > 0
+    assert bwd_call(good_desc(), ws_bytes=need - 1) == 5
+    assert bwd_call(good_desc(), ws=FAKE + 8, ws_bytes=need) == 6
+    # the internal chunk is fixed: the workspace does not depend on desc->chunk
+    assert lt2.lt2_gdn_backward_workspace_size(good_desc(chunk=16)) == need
+    # nothing to do for an empty batch
+    assert bwd_call(good_desc(B=0), q=None, k=None, v=None, alpha=None, beta=None, d_out=None, dq=None, dk=None,
+                    dv=None, dla=None, db=None, ws=None, ws_bytes=0) == 0
