@@ -406,6 +406,50 @@ def bench_hybrid(args, torch, lt2, synth, reps=5):
                 mfma_frac=(gemm_flops + mixer_flops) / ms / 1e9 / BF16_PEAK_TFLOPS)
 
 
+def bwd_flops_bytes(B, L, H, d, C=64):
+    """Work of the backward pass as built (scalar gate, chunk C): multiply-adds
+    per chunk of the prepare (K K^T, Q K^T, inverse), chunk-state (K S, N R,
+    K^T U), state-cotangent (P^T dO, K dS, N^T dU, Q^T dO, K^T dR) and gradient
+    kernels (K S, Q S, K dS, N R, P^T dO, N^T dU, three C x d x d accumulations,
+    dO U^T, dU R^T, Q K^T, K K^T, (dP o Gam) K and its transpose, two C^3
+    products, E K and E^T K); bytes are the inputs q, k, v, dO (bf16), alpha,
+    beta and the fp32 gradients, each once."""
+    NC = (L + C - 1) // C
+    cdd, ccd, ccc = C * d * d, C * C * d, C * C * C
+    macs = (2 * ccd + ccc / 6) + (2 * cdd + ccd) + (3 * cdd + 2 * ccd) + (6 * cdd + 8 * ccd + 2 * ccc)
+    flops = 2.0 * macs * NC * B * H
+    nbytes = float(B * L * H * (4 * d * 2 + 8 + 3 * d * 4 + 8))
+    return flops, nbytes
+
+
+def bench_backward(args, torch, lt2, synth, reps=5):
+    """Backward pass of the headline prefill workload (B4 H16 L4096 d128 bf16)."""
+    sh = synth.CONFIGS[2]["shape"]
+    log(f"backward inputs B={sh.B} L={sh.L} H={sh.H} d={sh.dk} bf16")
+    x = synth.gdn_inputs(sh, seed=0)
+    t = {kk: torch.from_numpy(vv).to("cuda") for kk, vv in x.items()}
+    q, k, v = (t[n].to(torch.bfloat16) for n in ("q", "k", "v"))
+    dO = torch.from_numpy(synth.grad_out(sh, seed=0)).to("cuda").to(torch.bfloat16)
+    desc = lt2.gdn_desc(sh.B, sh.L, sh.H, sh.dk, sh.dv, 64, lt2.LT2_BF16, lt2.LT2_BF16, lt2.LT2_GATE_HEAD)
+    ws = torch.empty(lt2.lt2_gdn_backward_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    run = lambda: lt2.lt2_gdn_backward(q, k, v, t["alpha"], t["beta"], dO, workspace=ws)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    flops, nbytes = bwd_flops_bytes(sh.B, sh.L, sh.H, sh.dk)
+    log(f"backward {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s fp32")
+    return dict(B=sh.B, L=sh.L, H=sh.H, d=sh.dk, ms=ms, tokens_per_s=sh.B * sh.L / (ms / 1e3),
+                flops=flops, bytes=nbytes, tflops=flops / ms / 1e9, fp32_vector_frac=flops / ms / 1e9 / 157.3,
+                gbs=nbytes / ms / 1e6, ws_bytes=ws.numel())
+
+
 def _slab_inputs(synth, shape, b0, nb):
     """Inputs of batch rows b0..b0+nb of the decode-seeding prefill (per-unit streams)."""
     L, H, d = shape.L, shape.H, shape.dk
@@ -537,6 +581,7 @@ def main():
     ap.add_argument("--no-decode-flat", action="store_true")
     ap.add_argument("--no-swa", action="store_true")
     ap.add_argument("--no-hybrid", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -562,6 +607,7 @@ def main():
     flat = None if (args.no_decode or args.no_decode_flat) else bench_decode_flat(args, torch, lt2)
     swa = None if args.no_swa else bench_swa(args, torch, lt2, synth)
     hyb = None if args.no_hybrid else bench_hybrid(args, torch, lt2, synth)
+    bwd = None if args.no_backward else bench_backward(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
     value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
@@ -596,6 +642,8 @@ def main():
         extra["swa_prefill"] = swa
     if hyb:
         extra["hybrid"] = hyb
+    if bwd:
+        extra["backward"] = bwd
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",
