@@ -99,13 +99,29 @@ __device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
         for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
 }
 
-// Rows [t0, t0 + n) of a [.., H, width] tensor (token stride tok, element offset
-// col0) into LDS dst [BC][pitch] as fp32; rows >= n are zero.
+// Rows [t0, t0 + n) of a [.., H, width] tensor (token stride tok) into LDS
+// dst [BC][pitch] as fp32, 16 bytes per load; rows >= n are zero.  Rows start
+// 16-byte aligned (aligned base, width a multiple of 16 bytes).
+__device__ __forceinline__ void widen16(float *d, u32x4 x, const uint16_t *) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        d[2 * i] = __uint_as_float(x[i] << 16);
+        d[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void widen16(float *d, u32x4 x, const float *) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = __uint_as_float(x[i]);
+}
 template <typename T>
 __device__ __forceinline__ void load_rows(float *dst, int pitch, const T *src, size_t tok, int n, int width) {
-    for (int idx = threadIdx.x; idx < BC * width; idx += BNT) {
-        const int r = idx / width, c = idx % width;
-        dst[r * pitch + c] = r < n ? to_f32(src[(size_t)r * tok + c]) : 0.f;
+    constexpr int VEC = 16 / (int)sizeof(T);
+    const int per_row = width / VEC;
+    for (int idx = threadIdx.x; idx < BC * per_row; idx += BNT) {
+        const int r = idx / per_row, c = VEC * (idx % per_row);
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (r < n) x = *reinterpret_cast<const u32x4 *>(src + (size_t)r * tok + c);
+        widen16(dst + r * pitch + c, x, src);
     }
 }
 
@@ -166,13 +182,43 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q,
         }
     if (threadIdx.x < BC) reinterpret_cast<double *>(out)[threadIdx.x] = g[threadIdx.x];
     __syncthreads();
-    // N = (I + A)^-1 by rows: N_t = e_t - sum_{i<t} A_ti N_i
-    for (int t = 0; t < BC; ++t) {
-        if (threadIdx.x < BC) {
-            const int j = threadIdx.x;
+    // N = (I + A)^-1, blocked by 16: the four diagonal blocks by row substitution
+    // in wave 0 (lane j owns column j and reads only that column's earlier rows,
+    // so no barrier is needed between rows), then the off-diagonal blocks one
+    // block-distance at a time:
+    //   N_ij = -N_ii sum_{k=j}^{i-1} A_ik N_kj   (i > j)
+    for (int idx = threadIdx.x; idx < BC * BC; idx += BNT) Ns[(idx / BC) * CPp + idx % BC] = 0.f;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int bb = threadIdx.x / 16, j = threadIdx.x;   // column j of diagonal block bb
+        for (int r = 0; r < 16; ++r) {
+            const int t = 16 * bb + r;
             float x = t == j ? 1.f : 0.f;
             for (int i = j; i < t; ++i) x = fmaf(-As[t * CPp + i], Ns[i * CPp + j], x);
-            Ns[t * CPp + j] = j <= t ? x : 0.f;
+            if (j <= t) Ns[t * CPp + j] = x;
+        }
+    }
+    __syncthreads();
+    __shared__ float Ws[BC * CPp];   // W_ij = sum_k A_ik N_kj for the current distance
+    for (int dist = 1; dist < 4; ++dist) {
+        // W blocks (i, j = i - dist): 16 x 16 each, (4 - dist) of them
+        const int nb = 4 - dist;
+        for (int idx = threadIdx.x; idx < nb * 256; idx += BNT) {
+            const int blk = idx / 256, e = idx % 256, r = e / 16, cc = e % 16;
+            const int bi = blk + dist, bj = blk;
+            const int t = 16 * bi + r, jj = 16 * bj + cc;
+            float x = 0.f;
+            for (int kk = 16 * bj; kk < 16 * bi; ++kk) x = fmaf(As[t * CPp + kk], Ns[kk * CPp + jj], x);
+            Ws[t * CPp + jj] = x;
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nb * 256; idx += BNT) {
+            const int blk = idx / 256, e = idx % 256, r = e / 16, cc = e % 16;
+            const int bi = blk + dist, bj = blk;
+            const int t = 16 * bi + r, jj = 16 * bj + cc;
+            float x = 0.f;
+            for (int kk = 16 * bi; kk <= t; ++kk) x = fmaf(Ns[t * CPp + kk], Ws[kk * CPp + jj], x);
+            Ns[t * CPp + jj] = -x;
         }
         __syncthreads();
     }
