@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     __shared__ __attribute__((aligned(16))) unsigned char kt_raw[K_BYTES > T_BYTES ? K_BYTES : T_BYTES];
     __shared__ float Am[C * CP];   // gated K K^T, then P
     __shared__ float Xs[4][16 * 17];
-    __shared__ float gs[C], bs[C];
+    __shared__ float bs[C];
+    __shared__ double gs[C];   // fp64: see the gate-prefix comment below
     TI *Ks = reinterpret_cast<TI *>(kt_raw);
     float *Ti = reinterpret_cast<float *>(kt_raw);
 
@@ -92,11 +93,14 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     if (wave == 0) {
         const size_t tok = (size_t)(b * (size_t)L + t0 + min(lane, Lc - 1)) * H + h;
         const float a_raw = alpha[tok], b_raw = beta[tok];
-        float lg = (lane < Lc) ? log2_gate(a_raw) : 0.f;
+        // chunk-relative prefix of log2 alpha in fp64: a fast decay reaches hundreds
+        // of octaves within a chunk, where an fp32 sum would give every decay
+        // 2^(g_t - g_i) between nearby tokens a relative error of |g| 2^-24
+        double lg = (lane < Lc) ? (double)log2_gate(a_raw) : 0.0;
         const float bt = (lane < Lc) ? b_raw : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(lg, off);
+            const double y = __shfl_up(lg, off);
             if (lane >= off) lg += y;
         }
         if (lane < C) { gs[lane] = lg; bs[lane] = bt; }
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
-            Am[t * CP + i] = (i < t) ? bs[t] * exp2_fast(gs[t] - gs[i]) * acc[r] : 0.f;
+            Am[t * CP + i] = (i < t) ? bs[t] * exp2_fast((float)(gs[t] - gs[i])) * acc[r] : 0.f;
         }
     }
     f32x4 pacc[MAXP];
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
-            Am[t * CP + i] = (i <= t && t < Lc) ? exp2_fast(gs[t] - gs[i]) * pacc[m][r] : 0.f;
+            Am[t * CP + i] = (i <= t && t < Lc) ? exp2_fast((float)(gs[t] - gs[i])) * pacc[m][r] : 0.f;
         }
     }
     for (int tt = wave; tt < NT * NT; tt += 4) {
@@ -244,9 +248,9 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
         }
     }
     if (tid < C) {
-        gg[tid] = gs[tid];
-        gg[C + tid] = exp2_fast(gs[tid]);
-        gg[2 * C + tid] = exp2_fast(gs[C - 1] - gs[tid]);   // rows past the ragged end keep g constant
+        gg[tid] = (float)gs[tid];
+        gg[C + tid] = exp2_fast((float)gs[tid]);
+        gg[2 * C + tid] = exp2_fast((float)(gs[C - 1] - gs[tid]));   // rows past the ragged end keep g constant
     }
 }
 
@@ -267,7 +271,7 @@ struct ScanPrefetch {
     Raw8<TI> qf[DK / 32];      // Q fragments of the wave's row tile
     Frag tf[NKB_C], pf[NKB_C]; // Tm and P fragments of the wave's row tile
     TI v[MAXO][4];             // V entries of the wave's output tiles (raw)
-    float g;                   // g[tid] (tid < C)
+    float e, w;                // 2^g[tid], 2^(gC - g[tid]) (tid < C)
 };
 
 template <int DK, int DV, int BV, int C, int PREC, typename TI, typename TO>
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
     __shared__ __attribute__((aligned(16))) float Rt[BV * CP];
     __shared__ __attribute__((aligned(16))) float Ut[BV * CP];
     __shared__ __attribute__((aligned(16))) float U2t[BV * CP];
-    __shared__ float gs[C];
+    __shared__ float es[C], ws2[C];   // 2^g and 2^(gC - g) of the current chunk
 
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int vb = logical % NV;
@@ -340,7 +344,8 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
                 p.v[m][r] = v[(base_tok + (size_t)(t0 + min(t, Lc - 1)) * tok_stride) * DV + v0 + 16 * J + lr];
             }
         }
-        p.g = wsu[2 * C * C + min(tid, C - 1)];
+        p.e = wsu[2 * C * C + C + min(tid, C - 1)];
+        p.w = wsu[2 * C * C + 2 * C + min(tid, C - 1)];
     };
 
     // initial state -> registers (state tiles) and St (transposed)
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
                 *reinterpret_cast<float4 *>(pk + 4) = make_float4(f.x[4], f.x[5], f.x[6], f.x[7]);
             }
         }
-        if (tid < C) gs[tid] = cur.g;
+        if (tid < C) { es[tid] = cur.e; ws2[tid] = cur.w; }
         __syncthreads();
         if constexpr (PIPE) {
             if (n + 1 < NC) fetch(n + 1, nxt);   // in flight during this chunk
@@ -421,7 +426,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
             }
             float eg[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) eg[r] = exp2_fast(gs[16 * I + 4 * lq + r]);
+            for (int r = 0; r < 4; ++r) eg[r] = es[16 * I + 4 * lq + r];
 #pragma unroll
             for (int m = 0; m < MAXO; ++m) {
                 const int o = wave + 4 * m;
@@ -441,7 +446,6 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
         __syncthreads();
 
         // U = Tm R;  Ut = U, U2t = e^{g_C - g} U
-        const float gC = gs[Lc - 1];
         if (has_o) {
             f32x4 ua[MAXO];
 #pragma unroll
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
             }
             float w2[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w2[r] = exp2_fast(gC - gs[16 * I + 4 * lq + r]);
+            for (int r = 0; r < 4; ++r) w2[r] = ws2[16 * I + 4 * lq + r];
 #pragma unroll
             for (int m = 0; m < MAXO; ++m) {
                 const int o = wave + 4 * m;
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q
         }
 
         // S <- e^{g_C} S + K^T U2   (the wave's state tiles share column tile J = wave % NTV)
-        const float eC = exp2_fast(gC);
+        const float eC = es[Lc - 1];
         const int Js = wave % NTV;
 #pragma unroll
         for (int m = 0; m < MAXS; ++m) {

@@ -123,6 +123,22 @@ def test_gate_special_cases_fp32():
         assert rel_err(S, S_ref) <= TOL_F32, name
 
 
+@pytest.mark.parametrize("shift", [6.0, -6.0])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_fast_and_slow_scalar_gates_fp32(shift, chunk):
+    """alpha = exp(-softplus(N(0,1) + 6)) (about e^-6: the state forgets almost
+    every token, cumulative log2 gates reach hundreds of octaves inside a chunk)
+    and shift -6 (alpha close to 1), fp32 inputs, to the fp32 bar."""
+    shape = synth.GDNShape(2, 300, 2, 128, 128, "head", shift, "f32")
+    announce(f"scalar gate shift={shift} chunk={chunk}")
+    x = synth.gdn_inputs(shape, seed=41)
+    S0 = np.random.default_rng(41).standard_normal((2, 2, 128, 128)).astype(np.float32)
+    o, S = run_prefill(x, shape, chunk, S0=S0)
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(o, o_ref) <= TOL_F32
+    assert rel_err(S, S_ref) <= TOL_F32
+
+
 def test_empty_and_determinism():
     announce("empty + determinism")
     shape = synth.GDNShape(1, 0, 2, 64, 64, "head", 0.0, "f32")
