@@ -235,6 +235,171 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M variant (the decode chain's M = batch of sequences): 64 x 128 tiles
+// so that a few hundred rows still give ~200 workgroups.  Four waves, wave w
+// owning columns 32w .. 32w+31 of the tile for all 64 rows (two 32x32 MFMA
+// accumulators).  K-tiles of 64 are staged through registers into double-
+// buffered, swizzled LDS as in the large kernel.  The accumulators then go to
+// LDS and the epilogue works row by row: four threads per row, 32 columns each,
+// so the per-head L2 norm is a two-step shuffle reduction and every global
+// access is a 16-byte vector.
+constexpr int SBM = 64, SBN = 128;
+
+template <int EPI, int DH>
+__global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restrict__ A,
+                                                         const uint16_t *__restrict__ B, int M, int N, int K,
+                                                         ProjOut po, ResidOut ro) {
+    constexpr int A_EL = SBM * BK, B_EL = SBN * BK, CP = SBN + 4;
+    constexpr int STAGE_BYTES = 2 * 2 * (A_EL + B_EL), EPI_BYTES = SBM * CP * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[STAGE_BYTES > EPI_BYTES ? STAGE_BYTES : EPI_BYTES];
+    uint16_t *As = reinterpret_cast<uint16_t *>(smem);          // [2][SBM * BK]
+    uint16_t *Bs = As + 2 * A_EL;                                // [2][SBN * BK]
+    float *Cs = reinterpret_cast<float *>(smem);                 // [SBM][CP], after the main loop
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int n_tiles = (N + SBN - 1) / SBN;
+    const int mt = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
+    const int m0 = mt * SBM, n0 = nt * SBN;
+
+    // staging: A 512 pieces (2 per thread), B 1024 pieces (4 per thread); rows past
+    // M or N repeat the last row
+    const uint16_t *Ab = A + (size_t)m0 * K, *Bb = B + (size_t)n0 * K;
+    unsigned ao[2], bo[4];
+    int la[2], lb[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
+        ao[i] = (unsigned)(min(m0 + row, M - 1) - m0) * (unsigned)K + 8 * seg;
+        la[i] = swz(row, seg);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
+        bo[i] = (unsigned)(min(n0 + row, N - 1) - n0) * (unsigned)K + 8 * seg;
+        lb[i] = swz(row, seg);
+    }
+    u32x4 ra[2], rb[4];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(Ab + ao[i] + k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(Bb + bo[i] + k0);
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4 *>(&As[buf * A_EL + la[i]]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(&Bs[buf * B_EL + lb[i]]) = rb[i];
+    };
+
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    const int KT = K / BK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < KT;
+        if (more) load((kt + 1) * BK);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int seg = 2 * ks + lh;
+            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Bs[buf * B_EL + swz(32 * wave + l32, seg)]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[buf * A_EL + swz(32 * i + l32, seg)]);
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+            }
+        }
+        if (more) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // accumulators -> LDS: register r of tile i holds row 32 i + 8 (r/4) + 4 lh + r%4,
+    // column 32 wave + l32
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Cs[(32 * i + 8 * (r >> 2) + 4 * lh + (r & 3)) * CP + 32 * wave + l32] = acc[i][r];
+    __syncthreads();
+
+    // epilogue: thread (row, quarter): row = tid / 4, columns 32 (tid % 4) .. + 31
+    const int row = tid >> 2, q4 = tid & 3;
+    const int m = m0 + row;
+    const int c0 = 32 * q4;
+    const float *cr = Cs + row * CP + c0;
+    if constexpr (EPI == EPI_RESID) {
+        if (m < M) {
+#pragma unroll
+            for (int j = 0; j < 32; j += 8) {
+                const int n = n0 + c0 + j;
+                if (n >= N) break;
+                float *hp = ro.h + (size_t)m * N + n;
+                float4 h0 = *reinterpret_cast<float4 *>(hp), h1 = *reinterpret_cast<float4 *>(hp + 4);
+                h0.x += cr[j + 0]; h0.y += cr[j + 1]; h0.z += cr[j + 2]; h0.w += cr[j + 3];
+                h1.x += cr[j + 4]; h1.y += cr[j + 5]; h1.z += cr[j + 6]; h1.w += cr[j + 7];
+                *reinterpret_cast<float4 *>(hp) = h0;
+                *reinterpret_cast<float4 *>(hp + 4) = h1;
+                u32x4 xb;
+                xb[0] = (uint32_t)bf16_bits(h0.x) | ((uint32_t)bf16_bits(h0.y) << 16);
+                xb[1] = (uint32_t)bf16_bits(h0.z) | ((uint32_t)bf16_bits(h0.w) << 16);
+                xb[2] = (uint32_t)bf16_bits(h1.x) | ((uint32_t)bf16_bits(h1.y) << 16);
+                xb[3] = (uint32_t)bf16_bits(h1.z) | ((uint32_t)bf16_bits(h1.w) << 16);
+                *reinterpret_cast<u32x4 *>(ro.xb + (size_t)m * N + n) = xb;
+            }
+        }
+    } else {
+        const int Hd = po.H * po.d;
+        const int NR = po.g ? 4 : 3;
+        if (n0 < NR * Hd) {
+            // the tile lies in one region (Hd is a multiple of 128); heads of DH columns
+            const int region = n0 / Hd;
+            uint16_t *dst = region == 0 ? po.q : (region == 1 ? po.k : (region == 2 ? po.v : po.g));
+            float scale = 1.f;
+            if (region < 2 && po.norm) {
+                float ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) ss += cr[j] * cr[j];
+                ss += __shfl_xor(ss, 1);                      // 64 columns
+                if constexpr (DH == 128) ss += __shfl_xor(ss, 2);   // 128 columns
+                scale = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+            }
+            if (m < M) {
+                const int c = n0 - region * Hd + c0;
+#pragma unroll
+                for (int j = 0; j < 32; j += 8) {
+                    u32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float x0 = cr[j + 2 * e] * scale, x1 = cr[j + 2 * e + 1] * scale;
+                        if (region == 3) {
+                            x0 = sigmoidf_acc(x0);
+                            x1 = sigmoidf_acc(x1);
+                        }
+                        o[e] = (uint32_t)bf16_bits(x0) | ((uint32_t)bf16_bits(x1) << 16);
+                    }
+                    *reinterpret_cast<u32x4 *>(dst + (size_t)m * Hd + c + j) = o;
+                }
+            }
+        } else if (po.beta && m < M) {
+            // gate columns: beta (first H) and alpha (next H)
+            for (int j = 0; j < 32; ++j) {
+                const int c = n0 + c0 + j - NR * Hd;
+                if (c >= 2 * po.H) break;
+                const float z = cr[j];
+                if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoidf_acc(z);
+                else po.alpha[(size_t)m * po.H + c - po.H] = sigmoidf_acc(-z);
+            }
+        }
+    }
+}
+
+// The 256 x 256 kernel unless it would launch fewer than 64 workgroups.
+bool use_small(int M, int N) { return (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN) < 64; }
+
 }  // namespace
 
 hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, int K, uint16_t *q, uint16_t *k,
@@ -242,6 +407,14 @@ hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, 
                             bool norm_qk) {
     ProjOut po{q, k, v, g, beta, alpha, H, d, norm_qk ? 1 : 0};
     ResidOut ro{nullptr, nullptr};
+    if (use_small(M, N)) {
+        const unsigned sg = (unsigned)((M + SBM - 1) / SBM) * (unsigned)((N + SBN - 1) / SBN);
+        if (d == 64)
+            hipLaunchKernelGGL((gemm_small_kernel<EPI_PROJ, 64>), dim3(sg), dim3(256), 0, s, X, W, M, N, K, po, ro);
+        else
+            hipLaunchKernelGGL((gemm_small_kernel<EPI_PROJ, 128>), dim3(sg), dim3(256), 0, s, X, W, M, N, K, po, ro);
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
     if (d == 64)
         hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_PROJ, 64>), dim3(grid), dim3(256), 0, s, X, W, M, N, K, K, K, po, ro);
@@ -254,6 +427,11 @@ hipError_t launch_gemm_resid(const uint16_t *O, const uint16_t *W, int M, int N,
                              hipStream_t s) {
     ProjOut po{};
     ResidOut ro{h, xb};
+    if (use_small(M, N)) {
+        const unsigned sg = (unsigned)((M + SBM - 1) / SBM) * (unsigned)((N + SBN - 1) / SBN);
+        hipLaunchKernelGGL((gemm_small_kernel<EPI_RESID, 128>), dim3(sg), dim3(256), 0, s, O, W, M, N, K, po, ro);
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
     hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_RESID, 128>), dim3(grid), dim3(256), 0, s, O, W, M, N, K, K, K, po, ro);
     return hipGetLastError();
