@@ -627,8 +627,12 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                                                              int L, int H, int NC,
                                                              const uint16_t *__restrict__ gate) {
     constexpr int NW = 8, NTH = 64 * NW;
-    constexpr int KP = DK + 16;  // bf16 pitch of K, Q and S^T rows (16-byte aligned, staggered banks)
-    constexpr int CP = C + 16;   // bf16 pitch of Tm, P, R^T, U^T, U2^T rows
+    // bf16 pitch of K, Q and S^T rows: DK + 8 puts consecutive rows 4 banks apart,
+    // so a 16-row fragment read (16 bytes per row) touches 64 distinct banks; it
+    // costs the 4-row transpose reads of K a 2-way overlap, which measured cheaper
+    // (scan 197 vs 210 us on the headline workload with rows 8 banks apart)
+    constexpr int KP = DK + 8;
+    constexpr int CP = C + 16;   // bf16 pitch of Tm, P, R^T, U^T, U2^T rows (measured best of C + 8/16/24)
     constexpr int VP = BV + 8;   // bf16 pitch of V rows
     constexpr int OV = 16 / (int)sizeof(TO);   // outputs per 16-byte store
     constexpr int OP = BV + OV;                // pitch of the staged output rows
