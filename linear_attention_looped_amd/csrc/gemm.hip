@@ -7,10 +7,10 @@
 // v_mfma_f32_32x32x16_bf16 (the accumulators, 256 floats per lane, live in the
 // accumulation registers: one wave per SIMD).  Per k-step of 16 a wave reads
 // four A and four B fragments for sixteen products, a third less LDS traffic
-// per multiply-add than 64 x 128 wave tiles.  A and B K-tiles are staged
-// through registers into double-buffered LDS (one coalesced 16-byte load per
-// piece); LDS rows are 128 bytes with the 16-byte segments XOR-swizzled by row,
-// so fragment reads of 8 or 16 consecutive rows hit distinct banks.
+// per multiply-add than 64 x 128 wave tiles.  A and B K-tiles are loaded
+// straight into double-buffered LDS by LDS-DMA buffer loads one tile ahead;
+// LDS rows are 128 bytes with the 16-byte segments XOR-swizzled by row, so
+// fragment reads of 8 or 16 consecutive rows hit distinct banks.
 //
 // 32x32x16 operand layout: A[i][k]: lane = i + 32*(k/8), slot k%8; B[k][j]:
 // lane = j + 32*(k/8), slot k%8; accumulator register r of lane l holds
@@ -25,6 +25,8 @@
 //             after them -> alpha = exp(-softplus(z)) (both fp32, one per head).
 //   EPI_RESID residual update h[m][n] += C[m][n] (fp32), and xb[m][n] = bf16(h),
 //             the next loop's GEMM input.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -56,12 +58,24 @@ __device__ __forceinline__ int swz(int r, int seg) {
     return r * BK + 8 * (seg ^ (r & 7) ^ ((r >> 3) & 1));
 }
 
+// Buffer descriptor over bytes [p, p + n): loads at offsets >= n return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void *p, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+// 16 bytes per lane from the buffer at byte offset voff into LDS at dst + 16 lane
+// (dst wave-uniform).  A plain function: the builtin must not sit in a generic
+// lambda of a kernel template (the host pass would drop the kernel's stub).
+__device__ __forceinline__ void gemm_dma16(__amdgpu_buffer_rsrc_t r, uint16_t *dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
+}
+
 template <int EPI, int DH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int M, int N, int K,
                          int lda, int ldb, ProjOut po, ResidOut ro) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+    // two buffers as four distinct arrays: the compiler can then tell that the DMA
+    // into one buffer does not alias the fragment reads of the other
+    __shared__ __attribute__((aligned(1024))) uint16_t A0[BM * BK], A1[BM * BK], B0[BN * BK], B1[BN * BK];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -72,35 +86,36 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     const int mt = logical / n_tiles, nt = logical % n_tiles;
     const int m0 = mt * BM, n0 = nt * BN;
 
-    // staging: 8 A and 8 B pieces of 16 bytes per thread; piece c covers row c/8,
-    // segment c%8 (eight consecutive threads read one 128-byte row).  Addresses
-    // are a uniform base plus 32-bit offsets; rows past M or N repeat the last row.
-    const uint16_t *Ab = A + (size_t)m0 * lda, *Bb = B + (size_t)n0 * ldb;
-    unsigned ao[8], bo[8];
-    int ls[8];
+    // K-tiles (256 rows x 64 bf16 of A and of B) go from memory straight into LDS
+    // by LDS-DMA buffer loads, 16 bytes per lane: wave w fills the 1 KiB chunks
+    // w, w + 4, ... (8 rows each); lane i of chunk c writes bytes 16 i of it, i.e.
+    // row 8 c + i / 8, physical segment i % 8, and fetches the logical segment the
+    // swizzle maps there.  The descriptors end at the tile's last row of A (B) in
+    // range, so rows past M (N) read as zero.  The next K-tile is requested into
+    // the other buffer at the top of a tile and waited for at its end, so a whole
+    // tile of products covers the load latency, with no staging registers.
+    int voa[8], vob[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = tid + 256 * i;
-        const int row = c >> 3, seg = c & 7;
-        ao[i] = (unsigned)(min(m0 + row, M - 1) - m0) * (unsigned)lda + 8 * seg;
-        bo[i] = (unsigned)(min(n0 + row, N - 1) - n0) * (unsigned)ldb + 8 * seg;
-        ls[i] = swz(row, seg);
+    for (int n = 0; n < 8; ++n) {
+        const int row = 8 * (wave + 4 * n) + (lane >> 3);
+        const int lseg = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+        voa[n] = 2 * (row * lda + 8 * lseg);
+        vob[n] = 2 * (row * ldb + 8 * lseg);
     }
-    u32x4 ra[8], rb[8];
-#define LT2_GEMM_LOAD(k0)                                                                   \
-    do {                                                                                    \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
-            ra[i] = *reinterpret_cast<const u32x4 *>(Ab + ao[i] + (k0));                    \
-            rb[i] = *reinterpret_cast<const u32x4 *>(Bb + bo[i] + (k0));                    \
-        }                                                                                   \
-    } while (0)
-#define LT2_GEMM_STORE_HALF(buf, h)                                                         \
-    do {                                                                                    \
-        _Pragma("unroll") for (int i = 4 * (h); i < 4 * (h) + 4; ++i) {                     \
-            *reinterpret_cast<u32x4 *>(&As[buf][ls[i]]) = ra[i];                            \
-            *reinterpret_cast<u32x4 *>(&Bs[buf][ls[i]]) = rb[i];                            \
-        }                                                                                   \
-    } while (0)
+    const int abytes = 2 * min(M - m0, BM) * lda, bbytes = 2 * min(N - n0, BN) * ldb;
+    const uint16_t *Ag = A + (size_t)m0 * lda, *Bg = B + (size_t)n0 * ldb;
+    auto dma_tile = [&](int kt, auto bufc) {
+        uint16_t *Ad = decltype(bufc)::value ? A1 : A0;
+        uint16_t *Bd = decltype(bufc)::value ? B1 : B0;
+        const int k0 = kt * BK;
+        const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(Ag + k0, abytes - 2 * k0);
+        const __amdgpu_buffer_rsrc_t rb = gemm_rsrc(Bg + k0, bbytes - 2 * k0);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            gemm_dma16(ra, Ad + 512 * (wave + 4 * n), voa[n]);
+            gemm_dma16(rb, Bd + 512 * (wave + 4 * n), vob[n]);
+        }
+    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -108,50 +123,58 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    // fragment reads of k-step ks (K offset 16 ks) of LDS buffer buf
+    // fragment reads of k-step ks (K offset 16 ks) of one LDS buffer
     int arow[4], brow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         arow[i] = 128 * wm + 32 * i + l32;
         brow[i] = 128 * wn + 32 * i + l32;
     }
-    auto frags = [&](int buf, int ks, bf16x8 *a, bf16x8 *b) __attribute__((always_inline)) {
-        const int seg = 2 * ks + lh;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][swz(arow[i], seg)]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][swz(brow[j], seg)]);
-    };
-
-    const int KT = K / BK;
-    LT2_GEMM_LOAD(0);
-    LT2_GEMM_STORE_HALF(0, 0);
-    LT2_GEMM_STORE_HALF(0, 1);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) LT2_GEMM_LOAD((kt + 1) * BK);
+    auto compute_tile = [&](auto bufc) {
+        const uint16_t *As = decltype(bufc)::value ? A1 : A0;
+        const uint16_t *Bs = decltype(bufc)::value ? B1 : B0;
         bf16x8 a[2][4], b[2][4];
-        frags(buf, 0, a[0], b[0]);
+        auto frags = [&](int ks, bf16x8 *fa, bf16x8 *fb) {
+            const int seg = 2 * ks + lh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(arow[i], seg)]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(brow[j], seg)]);
+        };
+        frags(0, a[0], b[0]);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int cur = ks & 1;
-            if (ks + 1 < BK / 16) frags(buf, ks + 1, a[cur ^ 1], b[cur ^ 1]);
-            // the next K-tile goes to the other buffer in two halves, behind this tile's products
-            if (more && ks == 2) LT2_GEMM_STORE_HALF(buf ^ 1, 0);
-            if (more && ks == 3) LT2_GEMM_STORE_HALF(buf ^ 1, 1);
+            if (ks + 1 < BK / 16) frags(ks + 1, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
         }
+    };
+
+    // K is a multiple of 128 (the looped drivers require d_model and H*d to be),
+    // so the K-tiles come in pairs, one per buffer
+    const int KT = K / BK;
+    const std::integral_constant<int, 0> c0{};
+    const std::integral_constant<int, 1> c1{};
+    dma_tile(0, c0);
+    wait_vmem_all();
+    __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+        // the scheduler would otherwise sink the DMA issue to the tile's last k-step
+        dma_tile(kt + 1, c1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile(c0);
+        wait_vmem_all();
+        __syncthreads();
+        if (kt + 2 < KT) dma_tile(kt + 2, c0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile(c1);
+        wait_vmem_all();
         __syncthreads();
     }
-
-#undef LT2_GEMM_LOAD
-#undef LT2_GEMM_STORE_HALF
 
     // ---- epilogue: register r of tile (i, j) holds
     //      C[m0 + 128 wm + 32 i + 8 (r/4) + 4 lh + r%4][n0 + 128 wn + 32 j + l32] ----
@@ -405,6 +428,7 @@ bool use_small(int M, int N) { return (long)((M + BM - 1) / BM) * ((N + BN - 1) 
 hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, int K, uint16_t *q, uint16_t *k,
                             uint16_t *v, uint16_t *g, float *beta, float *alpha, int H, int d, hipStream_t s,
                             bool norm_qk) {
+    if (K <= 0 || K % (2 * BK) != 0) return hipErrorInvalidValue;   // K-tiles are consumed in pairs
     ProjOut po{q, k, v, g, beta, alpha, H, d, norm_qk ? 1 : 0};
     ResidOut ro{nullptr, nullptr};
     if (use_small(M, N)) {
@@ -425,6 +449,7 @@ hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, 
 
 hipError_t launch_gemm_resid(const uint16_t *O, const uint16_t *W, int M, int N, int K, float *h, uint16_t *xb,
                              hipStream_t s) {
+    if (K <= 0 || K % (2 * BK) != 0) return hipErrorInvalidValue;
     ProjOut po{};
     ResidOut ro{h, xb};
     if (use_small(M, N)) {
