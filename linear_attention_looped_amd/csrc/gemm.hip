@@ -151,6 +151,17 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
+            // the next k-step's eight fragment reads go out one per product, so
+            // that they land while this k-step's sixteen products run
+            if (ks + 1 < BK / 16) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -239,22 +250,44 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
                 }
         }
     } else {
+        // Residual update, one 32-row block of the wave's 128 x 128 quadrant at a
+        // time: the block goes through LDS (the wave's own K-tile buffer, free since
+        // the loop's last barrier) so that h is read and written as whole 512-byte
+        // row pieces, 16 float4 per lane, all loads of a block in flight together.
+        // N is a multiple of 128, so a wave's columns are all in range or all out.
+        if (nw >= N) return;
+        constexpr int RP = 132;   // fp32 pitch of a staged row (16-byte rows, no 2-way conflict)
+        float *stage = reinterpret_cast<float *>(wave == 0 ? A0 : (wave == 1 ? A1 : (wave == 2 ? B0 : B1)));
+        const int n = nw + 4 * l32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = nw + 32 * j + l32;
-                if (n >= N) continue;
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    if (m >= M) continue;
+                for (int r = 0; r < 16; ++r)
+                    stage[(8 * (r >> 2) + 4 * lh + (r & 3)) * RP + 32 * j + l32] = acc[i][j][r];
+            const int mb = m0 + 128 * wm + 32 * i + lh;   // row of piece q is mb + 2 q
+            float4 hv[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int m = min(mb + 2 * q, M - 1);    // rows past M load row M - 1, store nothing
+                hv[q] = *reinterpret_cast<const float4 *>(&ro.h[(size_t)m * N + n]);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
+                const float4 hn = make_float4(hv[q].x + c.x, hv[q].y + c.y, hv[q].z + c.z, hv[q].w + c.w);
+                const int m = mb + 2 * q;
+                if (m < M) {
                     const size_t o = (size_t)m * N + n;
-                    const float hn = ro.h[o] + acc[i][j][r];
-                    ro.h[o] = hn;
-                    ro.xb[o] = bf16_bits(hn);
+                    *reinterpret_cast<float4 *>(&ro.h[o]) = hn;
+                    uint2 u;
+                    u.x = (uint32_t)bf16_bits(hn.x) | ((uint32_t)bf16_bits(hn.y) << 16);
+                    u.y = (uint32_t)bf16_bits(hn.z) | ((uint32_t)bf16_bits(hn.w) << 16);
+                    *reinterpret_cast<uint2 *>(&ro.xb[o]) = u;
                 }
             }
+        }
     }
 }
 
@@ -449,7 +482,7 @@ hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, 
 
 hipError_t launch_gemm_resid(const uint16_t *O, const uint16_t *W, int M, int N, int K, float *h, uint16_t *xb,
                              hipStream_t s) {
-    if (K <= 0 || K % (2 * BK) != 0) return hipErrorInvalidValue;
+    if (K <= 0 || K % (2 * BK) != 0 || N % 128 != 0) return hipErrorInvalidValue;
     ProjOut po{};
     ResidOut ro{h, xb};
     if (use_small(M, N)) {
