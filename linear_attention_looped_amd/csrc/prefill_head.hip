@@ -705,11 +705,24 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
     const int gidx = min(lane, NG - 1);
     const int orow = min(tid, NO - 1) / (BV / OV), ocol = OV * (min(tid, NO - 1) % (BV / OV));
 
-    u32x4 rk[KL], rq[KL], rv, rf[FL], rg;
+    u32x4 rk[KL], rq[KL], rv, rf[FL], rg, rgate = {0u, 0u, 0u, 0u};
     // Loads of chunk n's inputs into the staging registers.  Rows past the end
     // of a ragged last chunk repeat its last token: beta is zero there, so Tm
     // has zero rows and columns for them and they never reach an output.
-    auto fetch = [&](int n) __attribute__((always_inline)) {
+    // With an output gate, the gate values of chunk gn's outputs come first:
+    // they are stored at the top of chunk gn + 1, and by then every load of this
+    // fetch has been waited for (so the store waits for none of the later ones).
+    auto fetch = [&](int n, int gn) __attribute__((always_inline)) {
+        if (gb_ptr && gn >= 0 && (NO == NTH || wave < NO / 64) && orow < min(C, L - gn * C)) {
+            const uint16_t *gp = gb_ptr + ((size_t)gn * C + orow) * vtok_stride + ocol;   // OV gate values
+            if constexpr (OV == 8) {
+                rgate = *reinterpret_cast<const u32x4 *>(gp);
+            } else {
+                const uint2 g2 = *reinterpret_cast<const uint2 *>(gp);
+                rgate[0] = g2.x;
+                rgate[1] = g2.y;
+            }
+        }
         const int t0 = n * C;
         const int last = min(C, L - t0) - 1;
         const uint16_t *kc = kb_ptr + (size_t)t0 * tok_stride;
@@ -757,18 +770,8 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
             const unsigned off = (unsigned)orow * vtok_stride + (unsigned)ocol;
             TO *oc = ob_ptr + (size_t)n * C * vtok_stride;
             u32x4 x = *reinterpret_cast<const u32x4 *>(&Os[orow * OP + ocol]);
-            if (gb_ptr) {   // output gate of the looped block: o * sigmoid(z_g), bf16 gate values
-                const uint16_t *gp = gb_ptr + (size_t)n * C * vtok_stride + off;   // OV gate values
-                u32x4 gu = {0u, 0u, 0u, 0u};
-                if constexpr (OV == 8) {
-                    gu = *reinterpret_cast<const u32x4 *>(gp);
-                } else {
-                    const uint2 g2 = *reinterpret_cast<const uint2 *>(gp);
-                    gu[0] = g2.x;
-                    gu[1] = g2.y;
-                }
-                x = gate_outputs<TO>(x, gu);
-            }
+            // output gate of the looped block: o * sigmoid(z_g), bf16 gate values of chunk n
+            if (gb_ptr) x = gate_outputs<TO>(x, rgate);
             *reinterpret_cast<u32x4 *>(oc + off) = x;
         }
     };
@@ -793,15 +796,15 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
         const float x[4] = {Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]};
         store_split(Sth, Stl, (16 * Js + lr) * KP + 16 * Ik + 4 * lq, x);
     }
-    fetch(0);
+    fetch(0, -1);
     stage_kqvg(0);
 
     for (int n = 0; n < NC; ++n) {
         const int buf = n & 1;
         __syncthreads();   // chunk n's K, Q, V, decay vectors and S^T are in LDS; Tm, P and outputs of n - 1 are read
         stage_f();                     // Tm, P of chunk n (first read after the next barrier)
-        fetch(min(n + 1, NC - 1));     // the last chunk re-fetches itself (unused)
-        if (n > 0) store_o(n - 1, C);  // only the last chunk can be ragged
+        if (n > 0) store_o(n - 1, C);  // only the last chunk can be ragged; gate values of n - 1 in rgate
+        fetch(min(n + 1, NC - 1), n);  // the last chunk re-fetches itself (unused); gate values of chunk n
 
         // X_K = K S, X_Q = Q S;  R = V - 2^g X_K (hi/lo to LDS);  O = 2^g X_Q
         f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
