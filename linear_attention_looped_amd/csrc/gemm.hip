@@ -194,40 +194,46 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
         const int Hd = po.H * po.d;
         const int NR = po.g ? 4 : 3;                // head-width column blocks before the gates
         if (nw < NR * Hd) {
-            // q, k, v or g columns; the wave's 128 columns hold whole heads (Hd % 128 == 0)
+            // q, k, v or g columns; the wave's 128 columns hold whole heads (Hd % 128 == 0).
+            // One 32-row block at a time goes through LDS (the wave's own K-tile
+            // buffer, free since the loop's last barrier); a half-wave then holds a
+            // row, 4 columns per lane, so the per-head L2 norm is a reduction over
+            // the head's DH / 4 lanes and each lane stores 8 bytes.
             const int region = nw / Hd;             // 0 q, 1 k, 2 v, 3 g
             uint16_t *dst = region == 0 ? po.q : (region == 1 ? po.k : (region == 2 ? po.v : po.g));
-            const int c0 = nw - region * Hd;
-            constexpr int TPH = DH / 32;            // 32-column tiles per head
+            const int c0 = nw - region * Hd + 4 * l32;
+            const bool norm = region < 2 && po.norm;
+            constexpr int RP = 132;
+            float *stage = reinterpret_cast<float *>(wave == 0 ? A0 : (wave == 1 ? A1 : (wave == 2 ? B0 : B1)));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    float scale[4] = {1.f, 1.f, 1.f, 1.f};
-                    if (region < 2 && po.norm) {
-                        // per-head sum of squares: own tiles, then across the 32 lanes of the row
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int h0 = 0; h0 < 4; h0 += TPH) {
-                            float ss = 0.f;
+                    for (int r = 0; r < 16; ++r)
+                        stage[(8 * (r >> 2) + 4 * lh + (r & 3)) * RP + 32 * j + l32] = acc[i][j][r];
+                const int mb = m0 + 128 * wm + 32 * i + lh;   // row of piece q is mb + 2 q
 #pragma unroll
-                            for (int j = h0; j < h0 + TPH; ++j) ss += acc[i][j][r] * acc[i][j][r];
-                            ss += __shfl_xor(ss, 1);
-                            ss += __shfl_xor(ss, 2);
-                            ss += __shfl_xor(ss, 4);
-                            ss += __shfl_xor(ss, 8);
-                            ss += __shfl_xor(ss, 16);
-                            const float sc = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+                for (int q = 0; q < 16; ++q) {
+                    const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
+                    float x[4] = {c.x, c.y, c.z, c.w};
+                    if (norm) {
+                        float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
 #pragma unroll
-                            for (int j = h0; j < h0 + TPH; ++j) scale[j] = sc;
-                        }
+                        for (int o = 1; o < DH / 4; o <<= 1) ss += __shfl_xor(ss, o);
+                        const float sc = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] *= sc;
+                    } else if (region == 3) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = sigmoidf_acc(x[e]);
                     }
+                    const int m = mb + 2 * q;
                     if (m < M) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float x = acc[i][j][r] * scale[j];
-                            dst[(size_t)m * Hd + c0 + 32 * j + l32] = bf16_bits(region == 3 ? sigmoidf_acc(x) : x);
-                        }
+                        uint2 u;
+                        u.x = (uint32_t)bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
+                        u.y = (uint32_t)bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
+                        *reinterpret_cast<uint2 *>(&dst[(size_t)m * Hd + c0]) = u;
                     }
                 }
             }
