@@ -410,6 +410,11 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
 // ---------------------------------------------------------------------------
 // Per-chunk gradients.  The value dimension is walked in blocks of 16 columns;
 // dQ, dK (C x D) and dP, dTm (C x C) accumulate in registers across blocks.
+// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4f32: exact
+// fp32 products, fp32 sums), one 16 x 16 output tile per instruction chain.
+// Wave w owns rows 16w .. 16w + 15 (tokens) of every row-partitioned product;
+// in a tile, lane l holds rows 4 (l / 16) + r, r < 4, of column l % 16, and
+// reads A(row l % 16, k = l / 16) and B(k = l / 16, column l % 16) per k-step.
 template <int D, typename TI, typename TO>
 __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                         const TI *__restrict__ v, const TO *__restrict__ dout,
@@ -421,6 +426,8 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                                                         float *__restrict__ dlog_alpha, float *__restrict__ dbeta,
                                                         int L, int H, int NC) {
     constexpr int BV = 16, DP = D + 1, VP = BV + 1;
+    constexpr int NJ = D / 16, NP = BC / 16;   // 16-column tiles of dQ/dK and of dP/dTm
+    static_assert(BNT == 256 && BC == 64, "four waves of 16 token rows");
     // phase-1 buffers (per value block) and phase-2 buffers (C x C) share one region
     constexpr int P1 = 2 * D * VP + 9 * BC * VP;
     constexpr int P2 = 3 * BC * CPp;
@@ -442,7 +449,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     const float *gc = gnp + (unit * NC + c) * GNP_FLOATS;
     const float *Sc = sws + (unit * NC + c) * (size_t)D * D;
     const float *dSc = dsws + (unit * NC + c) * (size_t)D * D;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int R0 = 16 * __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ra = R0 + lr;   // this lane's A-operand row
 
     load_rows(Ks, DP, k + row0 * D, tok, n, D);
     load_rows(Qs, DP, q + row0 * D, tok, n, D);
@@ -456,18 +465,14 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         gq[tid] = gk[tid] = gd[tid] = 0.f;
     }
     float sdot = 0.f;
-    // register accumulators: dQ, dK rows 4 (tid / 16) .., columns QTN (tid % 16) ..;
-    // dP, dTm 4 x 4
-    constexpr int QTN = D / 16;
-    const int qi0 = 4 * (tid / 16), qj0 = QTN * (tid % 16);
-    const int pi0 = 4 * (tid / 16), pj0 = 4 * (tid % 16);
-    float aq[4][QTN], ak[4][QTN], ap[4][4], at[4][4];
-    zero(aq);
-    zero(ak);
-    zero(ap);
-    zero(at);
+    f32x4 aq[NJ], ak[NJ], ap[NP], at[NP];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) aq[j] = ak[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NP; ++j) ap[j] = at[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
     const double gC = g[n - 1];
+    const float ea = dexp2(g[ra], 0.0), eca = dexp2(gC, g[ra]);   // gamma, gamma_C / gamma of row ra
 
     for (int vb = 0; vb < D / BV; ++vb) {
         for (int idx = tid; idx < D * BV; idx += BNT) {
@@ -479,66 +484,57 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         load_rows(Vb, VP, v + row0 * D + vb * BV, tok, n, BV);
         load_rows(dOb, VP, dout + row0 * D + vb * BV, tok, n, BV);
         __syncthreads();
-        // KS = K S, QS = Q S, KdS = K dS' (C x BV)
-        const int i0 = 2 * (tid / 8), j0 = 2 * (tid % 8);
-        {
-            float a1[2][2], a2[2][2], a3[2][2];
-            zero(a1);
-            zero(a2);
-            zero(a3);
-            mmt<2, 2, D, false, false>(a1, Ks, DP, Sb, VP, i0, j0);
-            mmt<2, 2, D, false, false>(a2, Qs, DP, Sb, VP, i0, j0);
-            mmt<2, 2, D, false, false>(a3, Ks, DP, dSb, VP, i0, j0);
+        {   // KS = K S, QS = Q S, KdS = K dS' (C x BV);  R = V - diag(gamma) KS
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1;
+#pragma unroll 8
+            for (int k0 = 0; k0 < D; k0 += 4) {
+                const int kk = k0 + lq;
+                const float ka = Ks[ra * DP + kk], qa = Qs[ra * DP + kk];
+                const float sb = Sb[kk * VP + lr], dsb = dSb[kk * VP + lr];
+                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, sb, a1, 0, 0, 0);
+                a2 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa, sb, a2, 0, 0, 0);
+                a3 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, dsb, a3, 0, 0, 0);
+            }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int t = i0 + i, s = j0 + j;
-                    KS[t * VP + s] = a1[i][j];
-                    QS[t * VP + s] = a2[i][j];
-                    KdS[t * VP + s] = a3[i][j];
-                    Rb[t * VP + s] = Vb[t * VP + s] - dexp2(g[t], 0.0) * a1[i][j];   // R
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int t = R0 + 4 * lq + r, o = t * VP + lr;
+                KS[o] = a1[r];
+                QS[o] = a2[r];
+                KdS[o] = a3[r];
+                Rb[o] = Vb[o] - dexp2(g[t], 0.0) * a1[r];
+            }
         }
         __syncthreads();
         {   // U = N diag(beta) R ; dU = P^T dO + diag(gamma_C/gamma) K dS'
-            float a1[2][2], a2[2][2];
-            zero(a1);
-            zero(a2);
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
 #pragma unroll 4
-            for (int kk = 0; kk < BC; ++kk) {
-                const float w = bt[kk];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        a1[i][j] = fmaf(Ns[(i0 + i) * CPp + kk] * w, Rb[kk * VP + j0 + j], a1[i][j]);
-                        a2[i][j] = fmaf(Ps[kk * CPp + i0 + i], dOb[kk * VP + j0 + j], a2[i][j]);
-                    }
+            for (int k0 = 0; k0 < BC; k0 += 4) {
+                const int kk = k0 + lq;
+                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[ra * CPp + kk], bt[kk] * Rb[kk * VP + lr], a1, 0, 0, 0);
+                a2 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[kk * CPp + ra], dOb[kk * VP + lr], a2, 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int t = i0 + i, s = j0 + j;
-                    Ub[t * VP + s] = a1[i][j];
-                    dUb[t * VP + s] = fmaf(dexp2(gC, g[t]), KdS[t * VP + s], a2[i][j]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int t = R0 + 4 * lq + r, o = t * VP + lr;
+                Ub[o] = a1[r];
+                dUb[o] = fmaf(dexp2(gC, g[t]), KdS[o], a2[r]);
+            }
         }
         __syncthreads();
         {   // dR = diag(beta) N^T dU  (= dV)
-            float a1[2][2];
-            zero(a1);
-            mmt<2, 2, BC, true, false>(a1, Ns, CPp, dUb, VP, i0, j0);
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k0 = 0; k0 < BC; k0 += 4) {
+                const int kk = k0 + lq;
+                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[kk * CPp + ra], dUb[kk * VP + lr], a1, 0, 0, 0);
+            }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int t = i0 + i, s = j0 + j;
-                    const float r = bt[t] * a1[i][j];
-                    dRb[t * VP + s] = r;
-                    if (t < n) dv[(row0 + (size_t)t * H) * D + vb * BV + s] = r;
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int t = R0 + 4 * lq + r;
+                const float x = bt[t] * a1[r];
+                dRb[t * VP + lr] = x;
+                if (t < n) dv[(row0 + (size_t)t * H) * D + vb * BV + lr] = x;
+            }
         }
         __syncthreads();
         // gate row terms (wave 0): gamma <dO, QS>, -gamma <dR, KS>, (gamma_C/gamma) <U, KdS>
@@ -555,44 +551,27 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             gk[t] -= dexp2(g[t], 0.0) * x2;
             gd[t] += dexp2(gC, g[t]) * x3;
         }
-        // register accumulations over this value block
+        // register accumulations over this value block (k = value column s)
         //   dQ += diag(gamma) dO S^T ; dK += diag(gamma_C/gamma) U dS'^T - diag(gamma) dR S^T
         //   dP += dO U^T ; dTm += dU R^T
-#pragma unroll 2
-        for (int s = 0; s < BV; ++s) {
-            float sq[QTN], sd[QTN];
 #pragma unroll
-            for (int j = 0; j < QTN; ++j) {
-                sq[j] = Sb[(qj0 + j) * VP + s];
-                sd[j] = dSb[(qj0 + j) * VP + s];
+        for (int k0 = 0; k0 < BV; k0 += 4) {
+            const int s = k0 + lq;
+            const float o = dOb[ra * VP + s], du = dUb[ra * VP + s];
+            const float oe = ea * o, ue = eca * Ub[ra * VP + s], re = -ea * dRb[ra * VP + s];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int cc = 16 * j + lr;
+                const float sq = Sb[cc * VP + s], sd = dSb[cc * VP + s];
+                aq[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(oe, sq, aq[j], 0, 0, 0);
+                ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ue, sd, ak[j], 0, 0, 0);
+                ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(re, sq, ak[j], 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = qi0 + i;
-                const float e = dexp2(g[t], 0.0);
-                const float o = e * dOb[t * VP + s];
-                const float u = dexp2(gC, g[t]) * Ub[t * VP + s];
-                const float r = e * dRb[t * VP + s];
-#pragma unroll
-                for (int j = 0; j < QTN; ++j) {
-                    aq[i][j] = fmaf(o, sq[j], aq[i][j]);
-                    ak[i][j] = fmaf(u, sd[j], fmaf(-r, sq[j], ak[i][j]));
-                }
-            }
-            float uu[4], rr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uu[j] = Ub[(pj0 + j) * VP + s];
-                rr[j] = Rb[(pj0 + j) * VP + s];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float o = dOb[(pi0 + i) * VP + s], du = dUb[(pi0 + i) * VP + s];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    ap[i][j] = fmaf(o, uu[j], ap[i][j]);
-                    at[i][j] = fmaf(du, rr[j], at[i][j]);
-                }
+            for (int j = 0; j < NP; ++j) {
+                const int jj = 16 * j + lr;
+                ap[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(o, Ub[jj * VP + s], ap[j], 0, 0, 0);
+                at[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(du, Rb[jj * VP + s], at[j], 0, 0, 0);
             }
         }
         __syncthreads();
@@ -600,26 +579,35 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
 
     // ---- phase 2: C x C algebra (buffers X1..X3 replace the value-block buffers) ----
     // (a) X1 = dP o Gam (lower incl, rows < n), X2 = dTm, X3 = Q K^T
-    {
-        float qk[4][4];
-        zero(qk);
-        mmt<4, 4, D, false, true>(qk, Qs, DP, Ks, DP, pi0, pj0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < NP; ++j) {
+        f32x4 qk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int k0 = 0; k0 < D; k0 += 4)
+            qk = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[ra * DP + k0 + lq], Ks[(16 * j + lr) * DP + k0 + lq], qk,
+                                                     0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = pi0 + i, s = pj0 + j;
-                const float gam = dexp2(g[t], g[min(s, t)]);
-                X1[t * CPp + s] = (s <= t && t < n) ? ap[i][j] * gam : 0.f;
-                X2[t * CPp + s] = at[i][j];
-                X3[t * CPp + s] = qk[i][j];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int t = R0 + 4 * lq + r, s = 16 * j + lr;
+            const float gam = dexp2(g[t], g[min(s, t)]);
+            X1[t * CPp + s] = (s <= t && t < n) ? ap[j][r] * gam : 0.f;
+            X2[t * CPp + s] = at[j][r];
+            X3[t * CPp + s] = qk[r];
+        }
     }
     __syncthreads();
     // (b) dQ += (dP o Gam) K ; dK += (dP o Gam)^T Q ; X = dP o P = X1 o QK^T into Ps
     //     (P is no longer needed) ; dbeta from Tm = N diag(beta): sum_s dTm_st N_st
-    mmt<4, QTN, BC, false, false>(aq, X1, CPp, Ks, DP, qi0, qj0);
-    mmt<4, QTN, BC, true, false>(ak, X1, CPp, Qs, DP, qi0, qj0);
+#pragma unroll 4
+    for (int k0 = 0; k0 < BC; k0 += 4) {
+        const int kk = k0 + lq;
+        const float x = X1[ra * CPp + kk], xt = X1[kk * CPp + ra];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            aq[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, Ks[kk * DP + 16 * j + lr], aq[j], 0, 0, 0);
+            ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt, Qs[kk * DP + 16 * j + lr], ak[j], 0, 0, 0);
+        }
+    }
     for (int idx = tid; idx < BC * BC; idx += BNT) {
         const int t = idx / BC, s = idx % BC;
         Ps[t * CPp + s] = X1[t * CPp + s] * X3[t * CPp + s];
@@ -631,33 +619,38 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     }
     __syncthreads();
     // (c) T1 = N^T dTm diag(beta) into X1 ; X3 = K K^T
-    {
-        float a[4][4], kk[4][4];
-        zero(a);
-        zero(kk);
-        mmt<4, 4, BC, true, false>(a, Ns, CPp, X2, CPp, pi0, pj0);
-        mmt<4, 4, D, false, true>(kk, Ks, DP, Ks, DP, pi0, pj0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < NP; ++j) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f}, kk4 = a;
+#pragma unroll 4
+        for (int k0 = 0; k0 < BC; k0 += 4)
+            a = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[(k0 + lq) * CPp + ra], X2[(k0 + lq) * CPp + 16 * j + lr], a,
+                                                    0, 0, 0);
+#pragma unroll 8
+        for (int k0 = 0; k0 < D; k0 += 4)
+            kk4 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[ra * DP + k0 + lq], Ks[(16 * j + lr) * DP + k0 + lq], kk4,
+                                                      0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                X1[(pi0 + i) * CPp + pj0 + j] = a[i][j] * bt[pj0 + j];
-                X3[(pi0 + i) * CPp + pj0 + j] = kk[i][j];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int t = R0 + 4 * lq + r, s = 16 * j + lr;
+            X1[t * CPp + s] = a[r] * bt[s];
+            X3[t * CPp + s] = kk4[r];
+        }
     }
     __syncthreads();
     // (d) dA = -T1 N^T, strict lower part, into X2
-    {
-        float a[4][4];
-        zero(a);
-        mmt<4, 4, BC, false, true>(a, X1, CPp, Ns, CPp, pi0, pj0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < NP; ++j) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int k0 = 0; k0 < BC; k0 += 4)
+            a = __builtin_amdgcn_mfma_f32_16x16x4f32(X1[ra * CPp + k0 + lq], Ns[(16 * j + lr) * CPp + k0 + lq], a, 0,
+                                                    0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = pi0 + i, s = pj0 + j;
-                X2[t * CPp + s] = s < t ? -a[i][j] : 0.f;
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int t = R0 + 4 * lq + r, s = 16 * j + lr;
+            X2[t * CPp + s] = s < t ? -a[r] : 0.f;
+        }
     }
     __syncthreads();
     // (e) E = dA beta_t Gam into X1 ; X += dA o A (A = beta_t K K^T Gam) ;
@@ -675,16 +668,25 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     }
     __syncthreads();
     // (f) dK += E K + E^T K
-    mmt<4, QTN, BC, false, false>(ak, X1, CPp, Ks, DP, qi0, qj0);
-    mmt<4, QTN, BC, true, false>(ak, X1, CPp, Ks, DP, qi0, qj0);
+#pragma unroll 4
+    for (int k0 = 0; k0 < BC; k0 += 4) {
+        const int kk = k0 + lq;
+        const float x = X1[ra * CPp + kk], xt = X1[kk * CPp + ra];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = qi0 + i;
+        for (int j = 0; j < NJ; ++j) {
+            const float kb = Ks[kk * DP + 16 * j + lr];
+            ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, kb, ak[j], 0, 0, 0);
+            ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt, kb, ak[j], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = R0 + 4 * lq + r;
         if (t < n)
 #pragma unroll
-            for (int j = 0; j < QTN; ++j) {
-                dq[(row0 + (size_t)t * H) * D + qj0 + j] = aq[i][j];
-                dk[(row0 + (size_t)t * H) * D + qj0 + j] = ak[i][j];
+            for (int j = 0; j < NJ; ++j) {
+                dq[(row0 + (size_t)t * H) * D + 16 * j + lr] = aq[j][r];
+                dk[(row0 + (size_t)t * H) * D + 16 * j + lr] = ak[j][r];
             }
     }
     // gate (wave 0, thread j = token j of the chunk)
