@@ -238,6 +238,13 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
     __shared__ float Ss[D * VP], Ks[BC * DP], Vs[BC * VP], Ns[BC * CPp], Rs[BC * VP], Us[BC * VP], bt[BC];
     __shared__ double g[BC];
     constexpr int NB = D / BV;
+    // matrix-core roles (fp32 16 x 16 x 4 products): wave w owns token rows
+    // 16w .. 16w + 15 of the C x 32 products and state rows SR0 .. SR0 + 16 NR - 1
+    constexpr int NR = D / 64;
+    static_assert(BNT == 256 && BC == 64 && BV == 32, "four waves, two 16-column tiles");
+    const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int R0 = 16 * wv, ra = R0 + lr, SR0 = 16 * NR * wv;
     const int vb = blockIdx.x % NB;
     const size_t unit = blockIdx.x / NB;
     const int h = (int)(unit % H), b = (int)(unit / H);
@@ -267,42 +274,66 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
         __syncthreads();
         const double gC = g[n - 1];
         {   // R' = diag(beta) (V - diag(gamma) K S)
-            const int i0 = 4 * (threadIdx.x / 16), j0 = 2 * (threadIdx.x % 16);
-            float ks[4][2];
-            zero(ks);
-            mmt<4, 2, D, false, false>(ks, Ks, DP, Ss, VP, i0, j0);
+            f32x4 a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 8
+            for (int k0 = 0; k0 < D; k0 += 4) {
+                const float ka = Ks[ra * DP + k0 + lq];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 2; ++j)
+                    a[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, Ss[(k0 + lq) * VP + 16 * j + lr], a[j], 0, 0, 0);
+            }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int t = i0 + i;
-                    Rs[t * VP + j0 + j] = bt[t] * (Vs[t * VP + j0 + j] - dexp2(g[t], 0.0) * ks[i][j]);
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = R0 + 4 * lq + r, o = t * VP + 16 * j + lr;
+                    Rs[o] = bt[t] * (Vs[o] - dexp2(g[t], 0.0) * a[j][r]);
                 }
         }
         __syncthreads();
         {   // U' = diag(gamma_C / gamma) N R'
-            const int i0 = 4 * (threadIdx.x / 16), j0 = 2 * (threadIdx.x % 16);
-            float u[4][2];
-            zero(u);
-            mmt<4, 2, BC, false, false>(u, Ns, CPp, Rs, VP, i0, j0);
+            f32x4 a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+            for (int k0 = 0; k0 < BC; k0 += 4) {
+                const float na = Ns[ra * CPp + k0 + lq];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 2; ++j)
+                    a[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(na, Rs[(k0 + lq) * VP + 16 * j + lr], a[j], 0, 0, 0);
+            }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) Us[(i0 + i) * VP + j0 + j] = dexp2(gC, g[i0 + i]) * u[i][j];
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = R0 + 4 * lq + r;
+                    Us[t * VP + 16 * j + lr] = dexp2(gC, g[t]) * a[j][r];
+                }
         }
         __syncthreads();
-        {   // S = gamma_C S + K^T U'  (D x 32: D / 32 rows x 4 columns per thread)
-            constexpr int TM = D / 32;
-            const int i0 = TM * (threadIdx.x / 8), j0 = 4 * (threadIdx.x % 8);
-            float s[TM][4];
-            zero(s);
-            mmt<TM, 4, BC, true, false>(s, Ks, DP, Us, VP, i0, j0);
+        {   // S = gamma_C S + K^T U'  (wave w: state rows 16 (w NR + x) .., both column tiles)
+            f32x4 a[NR][2];
+#pragma unroll
+            for (int x = 0; x < NR; ++x) a[x][0] = a[x][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k0 = 0; k0 < BC; k0 += 4) {
+                const int kk = k0 + lq;
+                const float u0 = Us[kk * VP + lr], u1 = Us[kk * VP + 16 + lr];
+#pragma unroll
+                for (int x = 0; x < NR; ++x) {
+                    const float kt = Ks[kk * DP + SR0 + 16 * x + lr];
+                    a[x][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt, u0, a[x][0], 0, 0, 0);
+                    a[x][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt, u1, a[x][1], 0, 0, 0);
+                }
+            }
             const float gam = dexp2(gC, 0.0);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int x = 0; x < NR; ++x)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Ss[(i0 + i) * VP + j0 + j] = fmaf(gam, Ss[(i0 + i) * VP + j0 + j], s[i][j]);
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float &y = Ss[(SR0 + 16 * x + 4 * lq + r) * VP + 16 * j + lr];
+                        y = fmaf(gam, y, a[x][j][r]);
+                    }
         }
     }
 }
@@ -321,6 +352,12 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
         dRs[BC * VP], bt[BC];
     __shared__ double g[BC];
     constexpr int NB = D / BV;
+    // matrix-core roles as in the chunk-state kernel
+    constexpr int NR = D / 64;
+    static_assert(BNT == 256 && BC == 64 && BV == 32, "four waves, two 16-column tiles");
+    const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int R0 = 16 * wv, ra = R0 + lr, SR0 = 16 * NR * wv;
     const int vb = blockIdx.x % NB;
     const size_t unit = blockIdx.x / NB;
     const int h = (int)(unit % H), b = (int)(unit / H);
@@ -353,50 +390,77 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
         __syncthreads();
         const double gC = g[n - 1];
         {   // dU = P^T dO + diag(gamma_C / gamma) K dS'
-            const int i0 = 4 * (threadIdx.x / 16), j0 = 2 * (threadIdx.x % 16);
-            float a1[4][2], a2[4][2];
-            zero(a1);
-            zero(a2);
-            mmt<4, 2, BC, true, false>(a1, Ps, CPp, dOs, VP, i0, j0);
-            mmt<4, 2, D, false, false>(a2, Ks, DP, dS, VP, i0, j0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
+            f32x4 a1[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, a2[2] = {a1[0], a1[0]};
+#pragma unroll 4
+            for (int k0 = 0; k0 < BC; k0 += 4) {
+                const float pa = Ps[(k0 + lq) * CPp + ra];
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    dUs[(i0 + i) * VP + j0 + j] = fmaf(dexp2(gC, g[i0 + i]), a2[i][j], a1[i][j]);
+                    a1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, dOs[(k0 + lq) * VP + 16 * j + lr], a1[j], 0, 0, 0);
+            }
+#pragma unroll 8
+            for (int k0 = 0; k0 < D; k0 += 4) {
+                const float ka = Ks[ra * DP + k0 + lq];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    a2[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, dS[(k0 + lq) * VP + 16 * j + lr], a2[j], 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = R0 + 4 * lq + r;
+                    dUs[t * VP + 16 * j + lr] = fmaf(dexp2(gC, g[t]), a2[j][r], a1[j][r]);
+                }
         }
         __syncthreads();
         {   // dR = diag(beta) N^T dU, kept as diag(gamma) dR for the state update
-            const int i0 = 4 * (threadIdx.x / 16), j0 = 2 * (threadIdx.x % 16);
-            float a[4][2];
-            zero(a);
-            mmt<4, 2, BC, true, false>(a, Ns, CPp, dUs, VP, i0, j0);
+            f32x4 a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+            for (int k0 = 0; k0 < BC; k0 += 4) {
+                const float na = Ns[(k0 + lq) * CPp + ra];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 2; ++j)
+                    a[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(na, dUs[(k0 + lq) * VP + 16 * j + lr], a[j], 0, 0, 0);
+            }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int t = i0 + i;
-                    dRs[t * VP + j0 + j] = dexp2(g[t], 0.0) * bt[t] * a[i][j];
-                    dOs[t * VP + j0 + j] *= dexp2(g[t], 0.0);   // diag(gamma) dO
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = R0 + 4 * lq + r, o = t * VP + 16 * j + lr;
+                    dRs[o] = dexp2(g[t], 0.0) * bt[t] * a[j][r];
+                    dOs[o] *= dexp2(g[t], 0.0);   // diag(gamma) dO
                 }
         }
         __syncthreads();
-        {   // dS = Q^T diag(gamma) dO + gamma_C dS' - K^T diag(gamma) dR  (D / 32 rows x 4 per thread)
-            constexpr int TM = D / 32;
-            const int i0 = TM * (threadIdx.x / 8), j0 = 4 * (threadIdx.x % 8);
-            float a1[TM][4], a2[TM][4];
-            zero(a1);
-            zero(a2);
-            mmt<TM, 4, BC, true, false>(a1, Qs, DP, dOs, VP, i0, j0);
-            mmt<TM, 4, BC, true, false>(a2, Ks, DP, dRs, VP, i0, j0);
+        {   // dS = Q^T diag(gamma) dO + gamma_C dS' - K^T diag(gamma) dR  (wave w: state rows SR0 ..)
+            f32x4 a[NR][2];
+#pragma unroll
+            for (int x = 0; x < NR; ++x) a[x][0] = a[x][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k0 = 0; k0 < BC; k0 += 4) {
+                const int kk = k0 + lq;
+                const float o0 = dOs[kk * VP + lr], o1 = dOs[kk * VP + 16 + lr];
+                const float r0 = -dRs[kk * VP + lr], r1 = -dRs[kk * VP + 16 + lr];
+#pragma unroll
+                for (int x = 0; x < NR; ++x) {
+                    const float qt = Qs[kk * DP + SR0 + 16 * x + lr], kt = Ks[kk * DP + SR0 + 16 * x + lr];
+                    a[x][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt, o0, a[x][0], 0, 0, 0);
+                    a[x][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt, o1, a[x][1], 0, 0, 0);
+                    a[x][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt, r0, a[x][0], 0, 0, 0);
+                    a[x][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt, r1, a[x][1], 0, 0, 0);
+                }
+            }
             const float gam = dexp2(gC, 0.0);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int x = 0; x < NR; ++x)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float &x = dS[(i0 + i) * VP + j0 + j];
-                    x = fmaf(gam, x, a1[i][j] - a2[i][j]);
-                }
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float &y = dS[(SR0 + 16 * x + 4 * lq + r) * VP + 16 * j + lr];
+                        y = fmaf(gam, y, a[x][j][r]);
+                    }
         }
     }
     __syncthreads();
