@@ -99,9 +99,11 @@ __device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
         for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
 }
 
-// Rows [t0, t0 + n) of a [.., H, width] tensor (token stride tok) into LDS
-// dst [BC][pitch] as fp32, 16 bytes per load; rows >= n are zero.  Rows start
-// 16-byte aligned (aligned base, width a multiple of 16 bytes).
+// Rows [t0, t0 + n) of a [.., H, W] tensor (token stride tok) into LDS dst
+// [BC][pitch] as fp32, 16 bytes per load; rows >= n are zero.  Rows start
+// 16-byte aligned (aligned base, W a multiple of 16 bytes).  fetch() issues
+// every load of the tile into registers, put() widens and stores them, so a
+// caller can issue several tiles' loads before the first wait.
 __device__ __forceinline__ void widen16(float *d, u32x4 x, const uint16_t *) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -113,17 +115,44 @@ __device__ __forceinline__ void widen16(float *d, u32x4 x, const float *) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) d[i] = __uint_as_float(x[i]);
 }
-template <typename T>
-__device__ __forceinline__ void load_rows(float *dst, int pitch, const T *src, size_t tok, int n, int width) {
-    constexpr int VEC = 16 / (int)sizeof(T);
-    const int per_row = width / VEC;
-    for (int idx = threadIdx.x; idx < BC * per_row; idx += BNT) {
-        const int r = idx / per_row, c = VEC * (idx % per_row);
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (r < n) x = *reinterpret_cast<const u32x4 *>(src + (size_t)r * tok + c);
-        widen16(dst + r * pitch + c, x, src);
+template <int W, typename T>
+struct Rows {
+    static constexpr int VEC = 16 / (int)sizeof(T), PR = W / VEC, IT = (BC * PR + BNT - 1) / BNT;
+    u32x4 x[IT];
+    __device__ __forceinline__ void fetch(const T *src, size_t tok, int n) {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int idx = threadIdx.x + BNT * i, r = idx / PR, c = VEC * (idx % PR);
+            x[i] = u32x4{0u, 0u, 0u, 0u};
+            if (idx < BC * PR && r < n) x[i] = *reinterpret_cast<const u32x4 *>(src + (size_t)r * tok + c);
+        }
     }
-}
+    __device__ __forceinline__ void put(float *dst, int pitch) const {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int idx = threadIdx.x + BNT * i, r = idx / PR, c = VEC * (idx % PR);
+            if (idx < BC * PR) widen16(dst + r * pitch + c, x[i], static_cast<const T *>(nullptr));
+        }
+    }
+};
+// A C x C fp32 matrix of the workspace (16-byte aligned, row-major) into LDS
+// with pitch CPp, four 16-byte loads per thread.
+struct CCm {
+    static constexpr int IT = BC * BC / 4 / BNT;
+    u32x4 x[IT];
+    __device__ __forceinline__ void fetch(const float *src) {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) x[i] = reinterpret_cast<const u32x4 *>(src)[threadIdx.x + BNT * i];
+    }
+    __device__ __forceinline__ void put(float *dst) const {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = 4 * (threadIdx.x + BNT * i), r = e / BC, c = e % BC;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[r * CPp + c + j] = __uint_as_float(x[i][j]);
+        }
+    }
+};
 
 // Chunk-relative inclusive prefix sums (fp64) of log2 alpha for tokens
 // [t0, t0 + n); entries >= n repeat the last sum.  Computed by wave 0.
@@ -159,8 +188,13 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q,
     const int t0 = c * BC, n = min(BC, L - t0);
     const size_t tok = (size_t)H * D;
     const size_t row0 = ((size_t)b * L + t0) * H + h;   // (b, t0, h) in [B, L, H]
-    load_rows(Ks, DP, k + row0 * D, tok, n, D);
-    load_rows(Qs, DP, q + row0 * D, tok, n, D);
+    {
+        Rows<D, TI> rk, rq;
+        rk.fetch(k + row0 * D, tok, n);
+        rq.fetch(q + row0 * D, tok, n);
+        rk.put(Ks, DP);
+        rq.put(Qs, DP);
+    }
     gate_prefix(g, alpha + row0, H, n);
     if (threadIdx.x < BC) bt[threadIdx.x] = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
     __syncthreads();
@@ -264,12 +298,26 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
             const int r = idx / BV, cc = idx % BV;
             so[r * D + vb * BV + cc] = Ss[r * VP + cc];
         }
-        load_rows(Ks, DP, k + row0 * D, tok, n, D);
-        load_rows(Vs, VP, v + row0 * D + vb * BV, tok, n, BV);
-        for (int idx = threadIdx.x; idx < BC * BC; idx += BNT) Ns[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + idx];
-        if (threadIdx.x < BC) {
-            g[threadIdx.x] = reinterpret_cast<const double *>(gc)[threadIdx.x];
-            bt[threadIdx.x] = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+        {   // every load of the chunk in flight before the first is used
+            Rows<D, TI> rk;
+            Rows<BV, TI> rv;
+            CCm nm;
+            rk.fetch(k + row0 * D, tok, n);
+            rv.fetch(v + row0 * D + vb * BV, tok, n);
+            nm.fetch(gc + G_FLOATS);
+            double gv = 0.0;
+            float bv = 0.f;
+            if (threadIdx.x < BC) {
+                gv = reinterpret_cast<const double *>(gc)[threadIdx.x];
+                bv = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+            }
+            rk.put(Ks, DP);
+            rv.put(Vs, VP);
+            nm.put(Ns);
+            if (threadIdx.x < BC) {
+                g[threadIdx.x] = gv;
+                bt[threadIdx.x] = bv;
+            }
         }
         __syncthreads();
         const double gC = g[n - 1];
@@ -376,16 +424,30 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
             const int r = idx / BV, cc = idx % BV;
             dso[r * D + vb * BV + cc] = dS[r * VP + cc];
         }
-        load_rows(Ks, DP, k + row0 * D, tok, n, D);
-        load_rows(Qs, DP, q + row0 * D, tok, n, D);
-        load_rows(dOs, VP, dout + row0 * D + vb * BV, tok, n, BV);
-        for (int idx = threadIdx.x; idx < BC * BC; idx += BNT) {
-            Ns[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + idx];
-            Ps[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + BC * BC + idx];
-        }
-        if (threadIdx.x < BC) {
-            g[threadIdx.x] = reinterpret_cast<const double *>(gc)[threadIdx.x];
-            bt[threadIdx.x] = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+        {   // every load of the chunk in flight before the first is used
+            Rows<D, TI> rk, rq;
+            Rows<BV, TO> ro;
+            CCm nm, pm;
+            rk.fetch(k + row0 * D, tok, n);
+            rq.fetch(q + row0 * D, tok, n);
+            ro.fetch(dout + row0 * D + vb * BV, tok, n);
+            nm.fetch(gc + G_FLOATS);
+            pm.fetch(gc + G_FLOATS + BC * BC);
+            double gv = 0.0;
+            float bv = 0.f;
+            if (threadIdx.x < BC) {
+                gv = reinterpret_cast<const double *>(gc)[threadIdx.x];
+                bv = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+            }
+            rk.put(Ks, DP);
+            rq.put(Qs, DP);
+            ro.put(dOs, VP);
+            nm.put(Ns);
+            pm.put(Ps);
+            if (threadIdx.x < BC) {
+                g[threadIdx.x] = gv;
+                bt[threadIdx.x] = bv;
+            }
         }
         __syncthreads();
         const double gC = g[n - 1];
@@ -517,11 +579,17 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     const int R0 = 16 * __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ra = R0 + lr;   // this lane's A-operand row
 
-    load_rows(Ks, DP, k + row0 * D, tok, n, D);
-    load_rows(Qs, DP, q + row0 * D, tok, n, D);
-    for (int idx = tid; idx < BC * BC; idx += BNT) {
-        Ns[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + idx];
-        Ps[(idx / BC) * CPp + idx % BC] = gc[G_FLOATS + BC * BC + idx];
+    {
+        Rows<D, TI> rk, rq;
+        CCm nm, pm;
+        rk.fetch(k + row0 * D, tok, n);
+        rq.fetch(q + row0 * D, tok, n);
+        nm.fetch(gc + G_FLOATS);
+        pm.fetch(gc + G_FLOATS + BC * BC);
+        rk.put(Ks, DP);
+        rq.put(Qs, DP);
+        nm.put(Ns);
+        pm.put(Ps);
     }
     if (tid < BC) {
         g[tid] = reinterpret_cast<const double *>(gc)[tid];
@@ -539,14 +607,33 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     const float ea = dexp2(g[ra], 0.0), eca = dexp2(gC, g[ra]);   // gamma, gamma_C / gamma of row ra
 
     for (int vb = 0; vb < D / BV; ++vb) {
-        for (int idx = tid; idx < D * BV; idx += BNT) {
-            const int r = idx / BV, cc = idx % BV;
-            Sb[r * VP + cc] = Sc[r * D + vb * BV + cc];
-            dSb[r * VP + cc] = dSc[r * D + vb * BV + cc];
-            sdot = fmaf(Sb[r * VP + cc], dSb[r * VP + cc], sdot);
+        {   // the block's S and dS' columns (16-byte pieces), V and dO columns, all in flight together
+            constexpr int SP = D * BV / 4 / BNT;   // 16-byte pieces of S per thread
+            u32x4 xs[SP], xd[SP];
+#pragma unroll
+            for (int i = 0; i < SP; ++i) {
+                const int e = 4 * (tid + BNT * i), r = e / BV, cc = e % BV;
+                xs[i] = *reinterpret_cast<const u32x4 *>(Sc + r * D + vb * BV + cc);
+                xd[i] = *reinterpret_cast<const u32x4 *>(dSc + r * D + vb * BV + cc);
+            }
+            Rows<BV, TI> rv;
+            Rows<BV, TO> ro;
+            rv.fetch(v + row0 * D + vb * BV, tok, n);
+            ro.fetch(dout + row0 * D + vb * BV, tok, n);
+#pragma unroll
+            for (int i = 0; i < SP; ++i) {
+                const int e = 4 * (tid + BNT * i), r = e / BV, cc = e % BV;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float a = __uint_as_float(xs[i][j]), d2 = __uint_as_float(xd[i][j]);
+                    Sb[r * VP + cc + j] = a;
+                    dSb[r * VP + cc + j] = d2;
+                    sdot = fmaf(a, d2, sdot);
+                }
+            }
+            rv.put(Vb, VP);
+            ro.put(dOb, VP);
         }
-        load_rows(Vb, VP, v + row0 * D + vb * BV, tok, n, BV);
-        load_rows(dOb, VP, dout + row0 * D + vb * BV, tok, n, BV);
         __syncthreads();
         {   // KS = K S, QS = Q S, KdS = K dS' (C x BV);  R = V - diag(gamma) KS
             f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1;
