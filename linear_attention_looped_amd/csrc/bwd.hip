@@ -840,7 +840,17 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 dk[(row0 + (size_t)t * H) * D + 16 * j + lr] = ak[j][r];
             }
     }
-    // gate (wave 0, thread j = token j of the chunk)
+    // gate (wave 0, thread j = token j of the chunk).  The pairs i < j <= t of X
+    // (lower triangular, rows >= n zero): column suffix sums over t in place
+    // (lane i walks column i), then lane j adds row j over i < j.
+    if (tid < BC) {
+        float acc = 0.f;
+#pragma unroll 8
+        for (int t = BC - 1; t >= 0; --t) {
+            acc += Ps[t * CPp + tid];
+            Ps[t * CPp + tid] = acc;
+        }
+    }
     red[tid] = sdot;
     __syncthreads();
     if (tid < 64) {
@@ -862,10 +872,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             if (j >= o) pre += z;
         }
         pre -= j < n ? gd[j] : 0.f;
-        // pairs i < j <= t of X (lower triangular, rows < n)
         float cross = 0.f;
-        for (int t = j; t < n; ++t)
-            for (int i = 0; i < j; ++i) cross += Ps[t * CPp + i];
+#pragma unroll 8
+        for (int i = 0; i < BC; ++i) cross += i < j ? Ps[j * CPp + i] : 0.f;
         if (j < n) {
             dlog_alpha[row0 + (size_t)j * H] = suf + pre + cross + dexp2(gC, 0.0) * x;
             dbeta[row0 + (size_t)j * H] = dbt;
