@@ -41,7 +41,9 @@
 //   bwd_dstate_kernel  one per (b, h, 32-column block), chunks in reverse: the
 //                      cotangent of the state leaving every chunk, and dS_0
 //   bwd_grads_kernel   one per (b, h, chunk): dv, dq, dk, dbeta, d(log alpha)
-// Products are LDS-tiled: each thread accumulates a TM x TN micro-tile.
+// Products run on the fp32 matrix cores (v_mfma_f32_16x16x4f32: exact fp32
+// products, fp32 sums) from LDS operands; each wave owns 16-row output tiles.
+// Every load of a chunk is issued before the first of them is used.
 #include "common.h"
 #include "internal.h"
 
@@ -69,34 +71,6 @@ BwdLayout bwd_layout(int B, int L, int H, int d) {
     w.ds = w.s + units * NC * (size_t)d * d * 4;
     w.total = w.ds + units * NC * (size_t)d * d * 4;
     return w;
-}
-
-// acc[i][j] += sum_k opA(i0 + i, k) * opB(k, j0 + j), k = 0 .. KK-1, with
-// opA(i, k) = TA ? A[k * lda + i] : A[i * lda + k] and
-// opB(k, j) = TB ? B[j * ldb + k] : B[k * ldb + j].
-template <int TM, int TN, int KK, bool TA, bool TB>
-__device__ __forceinline__ void mmt(float (&acc)[TM][TN], const float *A, int lda, const float *B, int ldb, int i0,
-                                    int j0) {
-#pragma unroll 4
-    for (int k = 0; k < KK; ++k) {
-        float a[TM], b[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = TA ? A[k * lda + i0 + i] : A[(i0 + i) * lda + k];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = TB ? B[(j0 + j) * ldb + k] : B[k * ldb + j0 + j];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-}
-
-template <int TM, int TN>
-__device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
 }
 
 // Rows [t0, t0 + n) of a [.., H, W] tensor (token stride tok) into LDS dst
@@ -198,22 +172,27 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q,
     gate_prefix(g, alpha + row0, H, n);
     if (threadIdx.x < BC) bt[threadIdx.x] = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
     __syncthreads();
-    const int i0 = 4 * (threadIdx.x / 16), j0 = 4 * (threadIdx.x % 16);
-    float kk[4][4], qk[4][4];
-    zero(kk);
-    zero(qk);
-    mmt<4, 4, D, false, true>(kk, Ks, DP, Ks, DP, i0, j0);
-    mmt<4, 4, D, false, true>(qk, Qs, DP, Ks, DP, i0, j0);
+    // K K^T and Q K^T on the fp32 matrix cores: wave w owns rows 16w .. 16w + 15
+    const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+    const int R0 = 16 * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), ra = R0 + lr;
     float *out = gnp + (unit * NC + c) * GNP_FLOATS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = i0 + i, s = j0 + j;
-            const float gam = dexp2(g[t], g[min(s, t)]);
-            As[t * CPp + s] = s < t ? bt[t] * kk[i][j] * gam : 0.f;
-            out[G_FLOATS + BC * BC + t * BC + s] = (s <= t && t < n) ? qk[i][j] * gam : 0.f;   // P
+    for (int j = 0; j < BC / 16; ++j) {
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+#pragma unroll 8
+        for (int k0 = 0; k0 < D; k0 += 4) {
+            const float kb = Ks[(16 * j + lr) * DP + k0 + lq];
+            kk = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[ra * DP + k0 + lq], kb, kk, 0, 0, 0);
+            qk = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[ra * DP + k0 + lq], kb, qk, 0, 0, 0);
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = R0 + 4 * lq + r, s = 16 * j + lr;
+            const float gam = dexp2(g[t], g[min(s, t)]);
+            As[t * CPp + s] = s < t ? bt[t] * kk[r] * gam : 0.f;
+            out[G_FLOATS + BC * BC + t * BC + s] = (s <= t && t < n) ? qk[r] * gam : 0.f;   // P
+        }
+    }
     if (threadIdx.x < BC) reinterpret_cast<double *>(out)[threadIdx.x] = g[threadIdx.x];
     __syncthreads();
     // N = (I + A)^-1, blocked by 16: the four diagonal blocks by row substitution
@@ -287,10 +266,28 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
         const int r = idx / BV, cc = idx % BV;
         Ss[r * VP + cc] = state_in ? state_in[(unit * D + r) * D + vb * BV + cc] : 0.f;
     }
-    for (int c = 0; c < NC; ++c) {
+    // The loads of chunk c + 1 are issued once chunk c's inputs are in LDS and
+    // land while chunk c computes.
+    Rows<D, TI> rk;
+    Rows<BV, TI> rv;
+    CCm nm;
+    double gv = 0.0;
+    float bv = 0.f;
+    auto fetch = [&](int c) {
         const int t0 = c * BC, n = min(BC, L - t0);
         const size_t row0 = ((size_t)b * L + t0) * H + h;
         const float *gc = gnp + (unit * NC + c) * GNP_FLOATS;
+        rk.fetch(k + row0 * D, tok, n);
+        rv.fetch(v + row0 * D + vb * BV, tok, n);
+        nm.fetch(gc + G_FLOATS);
+        if (threadIdx.x < BC) {
+            gv = reinterpret_cast<const double *>(gc)[threadIdx.x];
+            bv = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+        }
+    };
+    fetch(0);
+    for (int c = 0; c < NC; ++c) {
+        const int t0 = c * BC, n = min(BC, L - t0);
         __syncthreads();
         // the state entering chunk c
         float *so = sws + (unit * NC + c) * (size_t)D * D;
@@ -298,27 +295,14 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
             const int r = idx / BV, cc = idx % BV;
             so[r * D + vb * BV + cc] = Ss[r * VP + cc];
         }
-        {   // every load of the chunk in flight before the first is used
-            Rows<D, TI> rk;
-            Rows<BV, TI> rv;
-            CCm nm;
-            rk.fetch(k + row0 * D, tok, n);
-            rv.fetch(v + row0 * D + vb * BV, tok, n);
-            nm.fetch(gc + G_FLOATS);
-            double gv = 0.0;
-            float bv = 0.f;
-            if (threadIdx.x < BC) {
-                gv = reinterpret_cast<const double *>(gc)[threadIdx.x];
-                bv = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
-            }
-            rk.put(Ks, DP);
-            rv.put(Vs, VP);
-            nm.put(Ns);
-            if (threadIdx.x < BC) {
-                g[threadIdx.x] = gv;
-                bt[threadIdx.x] = bv;
-            }
+        rk.put(Ks, DP);
+        rv.put(Vs, VP);
+        nm.put(Ns);
+        if (threadIdx.x < BC) {
+            g[threadIdx.x] = gv;
+            bt[threadIdx.x] = bv;
         }
+        if (c + 1 < NC) fetch(c + 1);
         __syncthreads();
         const double gC = g[n - 1];
         {   // R' = diag(beta) (V - diag(gamma) K S)
@@ -414,41 +398,46 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
         const int r = idx / BV, cc = idx % BV;
         dS[r * VP + cc] = dstate_out ? dstate_out[(unit * D + r) * D + vb * BV + cc] : 0.f;
     }
-    for (int c = NC - 1; c >= 0; --c) {
+    // The loads of chunk c - 1 are issued once chunk c's inputs are in LDS and
+    // land while chunk c computes.
+    Rows<D, TI> rk, rq;
+    Rows<BV, TO> ro;
+    CCm nm, pm;
+    double gv = 0.0;
+    float bv = 0.f;
+    auto fetch = [&](int c) {
         const int t0 = c * BC, n = min(BC, L - t0);
         const size_t row0 = ((size_t)b * L + t0) * H + h;
         const float *gc = gnp + (unit * NC + c) * GNP_FLOATS;
+        rk.fetch(k + row0 * D, tok, n);
+        rq.fetch(q + row0 * D, tok, n);
+        ro.fetch(dout + row0 * D + vb * BV, tok, n);
+        nm.fetch(gc + G_FLOATS);
+        pm.fetch(gc + G_FLOATS + BC * BC);
+        if (threadIdx.x < BC) {
+            gv = reinterpret_cast<const double *>(gc)[threadIdx.x];
+            bv = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+        }
+    };
+    fetch(NC - 1);
+    for (int c = NC - 1; c >= 0; --c) {
+        const int t0 = c * BC, n = min(BC, L - t0);
         __syncthreads();
         float *dso = dsws + (unit * NC + c) * (size_t)D * D;
         for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
             const int r = idx / BV, cc = idx % BV;
             dso[r * D + vb * BV + cc] = dS[r * VP + cc];
         }
-        {   // every load of the chunk in flight before the first is used
-            Rows<D, TI> rk, rq;
-            Rows<BV, TO> ro;
-            CCm nm, pm;
-            rk.fetch(k + row0 * D, tok, n);
-            rq.fetch(q + row0 * D, tok, n);
-            ro.fetch(dout + row0 * D + vb * BV, tok, n);
-            nm.fetch(gc + G_FLOATS);
-            pm.fetch(gc + G_FLOATS + BC * BC);
-            double gv = 0.0;
-            float bv = 0.f;
-            if (threadIdx.x < BC) {
-                gv = reinterpret_cast<const double *>(gc)[threadIdx.x];
-                bv = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
-            }
-            rk.put(Ks, DP);
-            rq.put(Qs, DP);
-            ro.put(dOs, VP);
-            nm.put(Ns);
-            pm.put(Ps);
-            if (threadIdx.x < BC) {
-                g[threadIdx.x] = gv;
-                bt[threadIdx.x] = bv;
-            }
+        rk.put(Ks, DP);
+        rq.put(Qs, DP);
+        ro.put(dOs, VP);
+        nm.put(Ns);
+        pm.put(Ps);
+        if (threadIdx.x < BC) {
+            g[threadIdx.x] = gv;
+            bt[threadIdx.x] = bv;
         }
+        if (c > 0) fetch(c - 1);
         __syncthreads();
         const double gC = g[n - 1];
         {   // dU = P^T dO + diag(gamma_C / gamma) K dS'
