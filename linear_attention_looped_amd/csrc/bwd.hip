@@ -595,34 +595,39 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     const double gC = g[n - 1];
     const float ea = dexp2(g[ra], 0.0), eca = dexp2(gC, g[ra]);   // gamma, gamma_C / gamma of row ra
 
-    for (int vb = 0; vb < D / BV; ++vb) {
-        {   // the block's S and dS' columns (16-byte pieces), V and dO columns, all in flight together
-            constexpr int SP = D * BV / 4 / BNT;   // 16-byte pieces of S per thread
-            u32x4 xs[SP], xd[SP];
+    // A value block's S and dS' columns (16-byte pieces), V and dO columns: the
+    // loads of block vb + 1 are issued once block vb is in LDS and land while it
+    // computes.
+    constexpr int SP = D * BV / 4 / BNT;   // 16-byte pieces of S per thread
+    u32x4 xs[SP], xd[SP];
+    Rows<BV, TI> rv;
+    Rows<BV, TO> ro;
+    auto fetch = [&](int vb) {
 #pragma unroll
-            for (int i = 0; i < SP; ++i) {
-                const int e = 4 * (tid + BNT * i), r = e / BV, cc = e % BV;
-                xs[i] = *reinterpret_cast<const u32x4 *>(Sc + r * D + vb * BV + cc);
-                xd[i] = *reinterpret_cast<const u32x4 *>(dSc + r * D + vb * BV + cc);
-            }
-            Rows<BV, TI> rv;
-            Rows<BV, TO> ro;
-            rv.fetch(v + row0 * D + vb * BV, tok, n);
-            ro.fetch(dout + row0 * D + vb * BV, tok, n);
-#pragma unroll
-            for (int i = 0; i < SP; ++i) {
-                const int e = 4 * (tid + BNT * i), r = e / BV, cc = e % BV;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float a = __uint_as_float(xs[i][j]), d2 = __uint_as_float(xd[i][j]);
-                    Sb[r * VP + cc + j] = a;
-                    dSb[r * VP + cc + j] = d2;
-                    sdot = fmaf(a, d2, sdot);
-                }
-            }
-            rv.put(Vb, VP);
-            ro.put(dOb, VP);
+        for (int i = 0; i < SP; ++i) {
+            const int e = 4 * (tid + BNT * i), r = e / BV, cc = e % BV;
+            xs[i] = *reinterpret_cast<const u32x4 *>(Sc + r * D + vb * BV + cc);
+            xd[i] = *reinterpret_cast<const u32x4 *>(dSc + r * D + vb * BV + cc);
         }
+        rv.fetch(v + row0 * D + vb * BV, tok, n);
+        ro.fetch(dout + row0 * D + vb * BV, tok, n);
+    };
+    fetch(0);
+    for (int vb = 0; vb < D / BV; ++vb) {
+#pragma unroll
+        for (int i = 0; i < SP; ++i) {
+            const int e = 4 * (tid + BNT * i), r = e / BV, cc = e % BV;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = __uint_as_float(xs[i][j]), d2 = __uint_as_float(xd[i][j]);
+                Sb[r * VP + cc + j] = a;
+                dSb[r * VP + cc + j] = d2;
+                sdot = fmaf(a, d2, sdot);
+            }
+        }
+        rv.put(Vb, VP);
+        ro.put(dOb, VP);
+        if (vb + 1 < D / BV) fetch(vb + 1);
         __syncthreads();
         {   // KS = K S, QS = Q S, KdS = K dS' (C x BV);  R = V - diag(gamma) KS
             f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1;
