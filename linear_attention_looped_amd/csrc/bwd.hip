@@ -651,13 +651,17 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         }
         __syncthreads();
         {   // U = N diag(beta) R ; dU = P^T dO + diag(gamma_C/gamma) K dS'
-            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
-#pragma unroll 4
+            // four partial sums per product (k-step mod 4): eight independent chains
+            f32x4 p1[4], p2[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) p1[x] = p2[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
             for (int k0 = 0; k0 < BC; k0 += 4) {
-                const int kk = k0 + lq;
-                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[ra * CPp + kk], bt[kk] * Rb[kk * VP + lr], a1, 0, 0, 0);
-                a2 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[kk * CPp + ra], dOb[kk * VP + lr], a2, 0, 0, 0);
+                const int kk = k0 + lq, h4 = (k0 >> 2) & 3;
+                p1[h4] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[ra * CPp + kk], bt[kk] * Rb[kk * VP + lr], p1[h4], 0, 0, 0);
+                p2[h4] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[kk * CPp + ra], dOb[kk * VP + lr], p2[h4], 0, 0, 0);
             }
+            const f32x4 a1 = (p1[0] + p1[1]) + (p1[2] + p1[3]), a2 = (p2[0] + p2[1]) + (p2[2] + p2[3]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = R0 + 4 * lq + r, o = t * VP + lr;
@@ -667,12 +671,15 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         }
         __syncthreads();
         {   // dR = diag(beta) N^T dU  (= dV)
-            f32x4 a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+            f32x4 p1[4];   // four partial sums (k-step mod 4)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) p1[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
             for (int k0 = 0; k0 < BC; k0 += 4) {
-                const int kk = k0 + lq;
-                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[kk * CPp + ra], dUb[kk * VP + lr], a1, 0, 0, 0);
+                const int kk = k0 + lq, h4 = (k0 >> 2) & 3;
+                p1[h4] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[kk * CPp + ra], dUb[kk * VP + lr], p1[h4], 0, 0, 0);
             }
+            const f32x4 a1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = R0 + 4 * lq + r;
