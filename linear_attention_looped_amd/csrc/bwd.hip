@@ -306,14 +306,16 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
         __syncthreads();
         const double gC = g[n - 1];
         {   // R' = diag(beta) (V - diag(gamma) K S)
-            f32x4 a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            f32x4 p[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll 8
-            for (int k0 = 0; k0 < D; k0 += 4) {
+            for (int k0 = 0; k0 < D; k0 += 4) {   // two partial sums per tile (even, odd k-steps)
+                const int h2 = (k0 >> 2) & 1;
                 const float ka = Ks[ra * DP + k0 + lq];
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    a[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, Ss[(k0 + lq) * VP + 16 * j + lr], a[j], 0, 0, 0);
+                    p[h2][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, Ss[(k0 + lq) * VP + 16 * j + lr], p[h2][j], 0, 0, 0);
             }
+            const f32x4 a[2] = {p[0][0] + p[1][0], p[0][1] + p[1][1]};
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -324,14 +326,16 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
         }
         __syncthreads();
         {   // U' = diag(gamma_C / gamma) N R'
-            f32x4 a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 4
-            for (int k0 = 0; k0 < BC; k0 += 4) {
+            f32x4 p[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 4) {   // two partial sums per tile
+                const int h2 = (k0 >> 2) & 1;
                 const float na = Ns[ra * CPp + k0 + lq];
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    a[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(na, Rs[(k0 + lq) * VP + 16 * j + lr], a[j], 0, 0, 0);
+                    p[h2][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(na, Rs[(k0 + lq) * VP + 16 * j + lr], p[h2][j], 0, 0, 0);
             }
+            const f32x4 a[2] = {p[0][0] + p[1][0], p[0][1] + p[1][1]};
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -441,20 +445,31 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
         __syncthreads();
         const double gC = g[n - 1];
         {   // dU = P^T dO + diag(gamma_C / gamma) K dS'
+            // two partial sums per tile and product (even, odd k-steps)
             f32x4 a1[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, a2[2] = {a1[0], a1[0]};
-#pragma unroll 4
-            for (int k0 = 0; k0 < BC; k0 += 4) {
-                const float pa = Ps[(k0 + lq) * CPp + ra];
+            f32x4 b1[2] = {a1[0], a1[0]}, b2[2] = {a1[0], a1[0]};
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+            for (int k0 = 0; k0 < BC; k0 += 8) {
+                const float pa = Ps[(k0 + lq) * CPp + ra], pb = Ps[(k0 + 4 + lq) * CPp + ra];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
                     a1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, dOs[(k0 + lq) * VP + 16 * j + lr], a1[j], 0, 0, 0);
+                    b1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pb, dOs[(k0 + 4 + lq) * VP + 16 * j + lr], b1[j], 0, 0, 0);
+                }
             }
-#pragma unroll 8
-            for (int k0 = 0; k0 < D; k0 += 4) {
-                const float ka = Ks[ra * DP + k0 + lq];
+#pragma unroll 4
+            for (int k0 = 0; k0 < D; k0 += 8) {
+                const float ka = Ks[ra * DP + k0 + lq], kb = Ks[ra * DP + k0 + 4 + lq];
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j) {
                     a2[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, dS[(k0 + lq) * VP + 16 * j + lr], a2[j], 0, 0, 0);
+                    b2[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kb, dS[(k0 + 4 + lq) * VP + 16 * j + lr], b2[j], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                a1[j] += b1[j];
+                a2[j] += b2[j];
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
@@ -466,14 +481,16 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
         }
         __syncthreads();
         {   // dR = diag(beta) N^T dU, kept as diag(gamma) dR for the state update
-            f32x4 a[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 4
-            for (int k0 = 0; k0 < BC; k0 += 4) {
+            f32x4 p[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 4) {   // two partial sums per tile
+                const int h2 = (k0 >> 2) & 1;
                 const float na = Ns[(k0 + lq) * CPp + ra];
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    a[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(na, dUs[(k0 + lq) * VP + 16 * j + lr], a[j], 0, 0, 0);
+                    p[h2][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(na, dUs[(k0 + lq) * VP + 16 * j + lr], p[h2][j], 0, 0, 0);
             }
+            const f32x4 a[2] = {p[0][0] + p[1][0], p[0][1] + p[1][1]};
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
