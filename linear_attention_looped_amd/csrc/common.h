@@ -164,6 +164,13 @@ __device__ __forceinline__ void raw_to_frag(Frag &f, const Raw8<float> &r) {
 // wait-count tracking a clean state across a loop back-edge, so later uses of
 // the prefetched registers do not wait on loads issued after them.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations still
+// outstanding (they retire in issue order); expcnt and lgkmcnt untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+}
 
 // The hardware hands out the workgroups of a launch to the 8 XCDs (each with
 // its own L2) round-robin by workgroup id.  This maps a 1-D id to a logical

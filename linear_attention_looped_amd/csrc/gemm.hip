@@ -301,23 +301,30 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 // Small-M variant (the decode chain's M = batch of sequences): 64 x 128 tiles
 // so that a few hundred rows still give ~200 workgroups.  Four waves, wave w
 // owning columns 32w .. 32w+31 of the tile for all 64 rows (two 32x32 MFMA
-// accumulators).  K-tiles of 64 are staged through registers into double-
-// buffered, swizzled LDS as in the large kernel.  The accumulators then go to
-// LDS and the epilogue works row by row: four threads per row, 32 columns each,
-// so the per-head L2 norm is a two-step shuffle reduction and every global
-// access is a 16-byte vector.
-constexpr int SBM = 64, SBN = 128;
+// accumulators).  With M this small the products are cheap and the kernel
+// streams B: K-tiles of 64 go from memory into LDS by LDS-DMA buffer loads
+// through five stages (swizzled as in the large kernel), four K-tiles in flight
+// per workgroup.  Each stage is its own pair of __shared__ arrays, selected at
+// compile time (the K loop is unrolled by the stage count), so that the
+// compiler can tell a DMA into one stage from the fragment reads of another.
+// The accumulators then go to LDS and the epilogue works row by row: four
+// threads per row, 32 columns each, so the per-head L2 norm is a two-step
+// shuffle reduction and every global access is a 16-byte vector.
+constexpr int SBM = 64, SBN = 128, SNS = 5;   // rows, columns, LDS stages
 
 template <int EPI, int DH>
 __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, int M, int N, int K,
                                                          ProjOut po, ResidOut ro) {
     constexpr int A_EL = SBM * BK, B_EL = SBN * BK, CP = SBN + 4;
-    constexpr int STAGE_BYTES = 2 * 2 * (A_EL + B_EL), EPI_BYTES = SBM * CP * 4;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[STAGE_BYTES > EPI_BYTES ? STAGE_BYTES : EPI_BYTES];
-    uint16_t *As = reinterpret_cast<uint16_t *>(smem);          // [2][SBM * BK]
-    uint16_t *Bs = As + 2 * A_EL;                                // [2][SBN * BK]
-    float *Cs = reinterpret_cast<float *>(smem);                 // [SBM][CP], after the main loop
+    // 1 KiB DMA chunks per stage: A 8, B 16; wave w takes A chunks w, w + 4 and B chunks w + 4 j
+    constexpr int DMA_PER_WAVE = 6;
+    // one array per stage (A tile, then B tile): the compiler tracks only a few
+    // distinct LDS-DMA targets, and ten would make every fragment read wait for
+    // every DMA in flight
+    __shared__ __attribute__((aligned(1024))) uint16_t S0[A_EL + B_EL], S1[A_EL + B_EL], S2[A_EL + B_EL],
+        S3[A_EL + B_EL], S4[A_EL + B_EL];
+    __shared__ __attribute__((aligned(16))) float Cs[SBM * CP];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,58 +333,91 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
     const int mt = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
     const int m0 = mt * SBM, n0 = nt * SBN;
 
-    // staging: A 512 pieces (2 per thread), B 1024 pieces (4 per thread); rows past
-    // M or N repeat the last row
-    const uint16_t *Ab = A + (size_t)m0 * K, *Bb = B + (size_t)n0 * K;
-    unsigned ao[2], bo[4];
-    int la[2], lb[4];
+    // lane i of a chunk writes bytes 16 i of it: row 8 c + i / 8, physical
+    // segment i % 8, holding the logical segment the swizzle maps there
+    int voa[2], vob[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
-        ao[i] = (unsigned)(min(m0 + row, M - 1) - m0) * (unsigned)K + 8 * seg;
-        la[i] = swz(row, seg);
+    for (int j = 0; j < 2; ++j) {
+        const int row = 8 * (wave + 4 * j) + (lane >> 3);
+        voa[j] = 2 * (row * K + 8 * ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
-        bo[i] = (unsigned)(min(n0 + row, N - 1) - n0) * (unsigned)K + 8 * seg;
-        lb[i] = swz(row, seg);
+    for (int j = 0; j < 4; ++j) {
+        const int row = 8 * (wave + 4 * j) + (lane >> 3);
+        vob[j] = 2 * (row * K + 8 * ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)));
     }
-    u32x4 ra[2], rb[4];
-    auto load = [&](int k0) {
+    // descriptors end at the tile's last row in range: rows past M (N) read zero
+    const int abytes = 2 * min(M - m0, SBM) * K, bbytes = 2 * min(N - n0, SBN) * K;
+    const uint16_t *Ag = A + (size_t)m0 * K, *Bg = B + (size_t)n0 * K;
+    auto dma = [&](int kt, uint16_t *Ad, uint16_t *Bd) {
+        const int k0 = kt * BK;
+        const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(Ag + k0, abytes - 2 * k0);
+        const __amdgpu_buffer_rsrc_t rb = gemm_rsrc(Bg + k0, bbytes - 2 * k0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(Ab + ao[i] + k0);
+        for (int j = 0; j < 2; ++j) gemm_dma16(ra, Ad + 512 * (wave + 4 * j), voa[j]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(Bb + bo[i] + k0);
+        for (int j = 0; j < 4; ++j) gemm_dma16(rb, Bd + 512 * (wave + 4 * j), vob[j]);
     };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4 *>(&As[buf * A_EL + la[i]]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(&Bs[buf * B_EL + lb[i]]) = rb[i];
-    };
-
     f32x16 acc[2] = {f32x16{}, f32x16{}};
-    const int KT = K / BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) load((kt + 1) * BK);
+    auto compute = [&](const uint16_t *As, const uint16_t *Bs) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int seg = 2 * ks + lh;
-            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Bs[buf * B_EL + swz(32 * wave + l32, seg)]);
+            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Bs[swz(32 * wave + l32, seg)]);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[buf * A_EL + swz(32 * i + l32, seg)]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[swz(32 * i + l32, seg)]);
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
             }
         }
-        if (more) store(buf ^ 1);
-        __syncthreads();
+    };
+    // K-tile kt sits in stage kt % SNS.  Step kt: wait for this wave's DMAs of
+    // K-tile kt (those of the SNS - 2 later K-tiles may still be in flight),
+    // barrier (every wave's share has landed, and every wave has finished
+    // reading the stage that K-tile kt + SNS - 1 is about to overwrite), issue
+    // that K-tile, multiply K-tile kt.
+    const int KT = K / BK;
+    // stage arrays by compile-time index (so each access names its own array)
+    auto stA = [&](auto sc) -> uint16_t * {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S == 0) return S0; else if constexpr (S == 1) return S1;
+        else if constexpr (S == 2) return S2; else if constexpr (S == 3) return S3; else return S4;
+    };
+    auto stB = [&](auto sc) -> uint16_t * { return stA(sc) + A_EL; };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // every step issues one K-tile (past the last, the last again, into the
+    // stage being retired, which is never read again), so the DMAs in flight
+    // behind K-tile kt are always SNS - 2 K-tiles' worth and the wait is constant
+    dma(0, stA(I0{}), stB(I0{}));
+    dma(min(1, KT - 1), stA(I1{}), stB(I1{}));
+    dma(min(2, KT - 1), stA(I2{}), stB(I2{}));
+    dma(min(3, KT - 1), stA(I3{}), stB(I3{}));
+    auto step = [&](int kt, auto sc) {
+        constexpr int S = decltype(sc)::value, SN = (S + SNS - 1) % SNS;
+        const std::integral_constant<int, S> cs{};
+        const std::integral_constant<int, SN> cn{};
+        wait_vmem_le<(SNS - 2) * DMA_PER_WAVE>();
+        // A bare hardware barrier: __syncthreads (a release fence, which counts
+        // the LDS-DMA writes still in flight) would wait for every later
+        // K-tile too.  What it would order is covered otherwise: this wave's
+        // share of K-tile kt has landed (the wait above), and every fragment
+        // read of the stage about to be overwritten was consumed by the
+        // previous step's products before this wave reached the barrier.
+        __builtin_amdgcn_s_barrier();
+        dma(min(kt + SNS - 1, KT - 1), stA(cn), stB(cn));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stA(cs), stB(cs));
+    };
+    static_assert(SNS == 5, "the step sequence below names five stages");
+    for (int kt = 0; kt < KT; kt += SNS) {
+        step(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < KT) step(kt + 1, std::integral_constant<int, 1>{});
+        if (kt + 2 < KT) step(kt + 2, std::integral_constant<int, 2>{});
+        if (kt + 3 < KT) step(kt + 3, std::integral_constant<int, 3>{});
+        if (kt + 4 < KT) step(kt + 4, std::integral_constant<int, 4>{});
     }
 
     // accumulators -> LDS: register r of tile i holds row 32 i + 8 (r/4) + 4 lh + r%4,
