@@ -95,6 +95,31 @@ def test_looped_decode_chain_matches_mixer(B, L, D, H, d, T):
     assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16
 
 
+def test_looped_decode_chain_full_width_sampled():
+    """The decode chain at its benchmarked width (256 sequences, d_model 2048,
+    H16 d128, T4: projection M 256 x N 6176 x K 2048 on the small-M GEMM, 32
+    K-tiles through its LDS stages): two tokens for all sequences; the oracle
+    recomputes the first and the last sequence on their own."""
+    B, L, D, H, d, T = 256, 2, 2048, 16, 128, 4
+    shape = synth.LoopShape(B, L, D, H, d, T)
+    announce("looped decode chain full width")
+    w = synth.loop_weights(shape, seed=3)
+    h0 = synth.loop_h0(shape, seed=3)
+    w_in = torch.from_numpy(w["w_in"]).to("cuda").to(torch.bfloat16)
+    w_o = torch.from_numpy(w["w_o"]).to("cuda").to(torch.bfloat16)
+    states = torch.zeros((T, B, H, d, d), dtype=torch.float32, device="cuda")
+    got = np.empty_like(h0)
+    for t in range(L):
+        h = torch.from_numpy(np.ascontiguousarray(h0[:, t], np.float32)).to("cuda")
+        lt2.lt2_looped_decode_step(h, w_in, w_o, states, H, d, T)
+        got[:, t] = host(h)
+    torch.cuda.synchronize()
+    for b in (0, B - 1):
+        ref = oracle.looped_mixer(h0[b:b + 1], w["w_in"], w["w_o"], H, d, T)
+        assert rel_err(got[b:b + 1], ref) <= TOL_BF16, b
+        assert rel_err(got[b:b + 1] - h0[b:b + 1], ref - h0[b:b + 1]) <= 4 * TOL_BF16, b
+
+
 def test_looped_decode_equals_mixer_on_gpu():
     """Decode chain vs the GPU looped block on the same sequence (both bf16
     GEMM inputs, fp32 state): agreement far inside the oracle bar."""
