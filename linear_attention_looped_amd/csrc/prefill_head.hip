@@ -945,6 +945,18 @@ size_t prefill_head_ws_bytes(int B, int L, int H, int C) {
     return (size_t)B * H * NC * (size_t)(8 * C * C + 12 * C);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    }
+    return cus[dev];
+}
+
 template <int D, int C, int PREC, typename TI, typename TO>
 static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
     constexpr int BV = 32;
@@ -958,6 +970,19 @@ static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
     }
     if (phase & PHASE_SCAN) {
         if constexpr (PREC == PREC_BF16) {
+            // 32-column blocks, or (d = 128, C = 64) 16-column blocks when 32
+            // would leave compute units idle: each block walks every chunk of its
+            // unit and loads the chunk's K, Q, Tm and P either way, but twice the
+            // blocks run at once
+            if constexpr (D == 128 && C == 64) {
+                if ((long)units * (D / BV) < device_cus()) {
+                    hipLaunchKernelGGL((scan_head_bf16_kernel<D, D, BV / 2, C, TO>), dim3(units * (D / (BV / 2))),
+                                       dim3(512), 0, s, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                                       (const uint16_t *)a.v, (const unsigned char *)a.ws, a.state_in, (TO *)a.out,
+                                       a.state_out, a.L, a.H, NC, a.gate);
+                    return hipGetLastError();
+                }
+            }
             hipLaunchKernelGGL((scan_head_bf16_kernel<D, D, BV, C, TO>), dim3(units * (D / BV)), dim3(512), 0, s,
                                (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                                (const unsigned char *)a.ws, a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC,

@@ -78,6 +78,26 @@ def test_bf16_prefill_small(out_dtype):
     assert rel_err(S, S_ref) <= TOL_BF16
 
 
+def test_bf16_wide_and_narrow_column_blocks():
+    """d128, chunk 64, bf16: 64 (b, h) units run the scan in 32-column blocks
+    (256 workgroups); fewer units (here the first two batch rows alone, 32
+    units) run it in 16-column blocks so that twice the workgroups fill the
+    GPU.  Ragged L, initial state; both against the oracle."""
+    shape = synth.GDNShape(4, 333, 16, 128, 128, "head", 2.0, "bf16")
+    announce("bf16 wide and narrow column blocks")
+    x = synth.gdn_inputs(shape, seed=21)
+    S0 = np.random.default_rng(21).standard_normal((4, 16, 128, 128)).astype(np.float32) * 0.1
+    o_ref, S_ref = oracle_prefill(x, S0)
+    o, S = run_prefill(x, shape, 64, out_dtype=torch.float32, S0=S0)
+    assert rel_err(o, o_ref) <= TOL_BF16
+    assert rel_err(S, S_ref) <= TOL_BF16
+    x2 = {kk: vv[:2] for kk, vv in x.items()}
+    o2, S2 = run_prefill(x2, synth.GDNShape(2, 333, 16, 128, 128, "head", 2.0, "bf16"), 64,
+                         out_dtype=torch.float32, S0=S0[:2])
+    assert rel_err(o2, o_ref[:2]) <= TOL_BF16
+    assert rel_err(S2, S_ref[:2]) <= TOL_BF16
+
+
 def test_bf16_slow_decay_long():
     """bf16 with slow decay (shift 0), where the state carries over many chunks."""
     shape = synth.GDNShape(1, 1024, 2, 128, 128, "head", 0.0, "bf16")
