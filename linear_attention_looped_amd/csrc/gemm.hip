@@ -130,39 +130,47 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
         arow[i] = 128 * wm + 32 * i + l32;
         brow[i] = 128 * wn + 32 * i + l32;
     }
-    auto compute_tile = [&](auto bufc) {
+    // Fragments by k-step parity.  A K-tile's k-steps 0..2 run with the reads of
+    // k-steps 1..3; then this wave waits for the next K-tile's DMA, the
+    // workgroup meets (every read of this tile's buffer is done, so the DMA two
+    // K-tiles ahead can go into it), and k-step 3 runs with the reads of the
+    // next tile's k-step 0, so no tile starts on an LDS round trip.
+    bf16x8 fa[2][4], fb[2][4];
+    auto frags = [&](auto bufc, int ks, bf16x8 *xa, bf16x8 *xb) {
         const uint16_t *As = decltype(bufc)::value ? A1 : A0;
         const uint16_t *Bs = decltype(bufc)::value ? B1 : B0;
-        bf16x8 a[2][4], b[2][4];
-        auto frags = [&](int ks, bf16x8 *fa, bf16x8 *fb) {
-            const int seg = 2 * ks + lh;
+        const int seg = 2 * ks + lh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(arow[i], seg)]);
+        for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(arow[i], seg)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(brow[j], seg)]);
-        };
-        frags(0, a[0], b[0]);
+        for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(brow[j], seg)]);
+    };
+    // sixteen products; the eight fragment reads issued just before go out one per product
+    auto products = [&](const bf16x8 *xa, const bf16x8 *xb) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int cur = ks & 1;
-            if (ks + 1 < BK / 16) frags(ks + 1, a[cur ^ 1], b[cur ^ 1]);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
-            // the next k-step's eight fragment reads go out one per product, so
-            // that they land while this k-step's sixteen products run
-            if (ks + 1 < BK / 16) {
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int n = 0; n < 8; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto head = [&](auto bufc) {   // k-steps 0 .. 2 of the tile in bufc
+#pragma unroll
+        for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+            frags(bufc, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            products(fa[ks & 1], fb[ks & 1]);
+        }
+    };
+    auto tail = [&](auto nextc) {   // k-step 3, with k-step 0 of the tile in nextc
+        static_assert(BK / 16 == 4, "k-step 3 uses the odd fragment set");
+        frags(nextc, 0, fa[0], fb[0]);
+        products(fa[1], fb[1]);
     };
 
     // K is a multiple of 128 (the looped drivers require d_model and H*d to be),
@@ -171,21 +179,25 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     const std::integral_constant<int, 0> c0{};
     const std::integral_constant<int, 1> c1{};
     dma_tile(0, c0);
+    dma_tile(1, c1);
     wait_vmem_all();
     __syncthreads();
+    frags(c0, 0, fa[0], fb[0]);
     for (int kt = 0; kt < KT; kt += 2) {
-        // the scheduler would otherwise sink the DMA issue to the tile's last k-step
-        dma_tile(kt + 1, c1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_tile(c0);
-        wait_vmem_all();
+        head(c0);                         // K-tile kt
+        wait_vmem_all();                  // K-tile kt + 1 (buffer 1) has landed
         __syncthreads();
         if (kt + 2 < KT) dma_tile(kt + 2, c0);
         __builtin_amdgcn_sched_barrier(0);
-        compute_tile(c1);
-        wait_vmem_all();
+        tail(c1);
+        head(c1);                         // K-tile kt + 1
+        wait_vmem_all();                  // K-tile kt + 2 (buffer 0) has landed
         __syncthreads();
+        if (kt + 3 < KT) dma_tile(kt + 3, c1);
+        __builtin_amdgcn_sched_barrier(0);
+        tail(c0);                         // past the last tile its reads are stale and unused
     }
+    __syncthreads();   // the epilogue stages through the K-tile buffers
 
     // ---- epilogue: register r of tile (i, j) holds
     //      C[m0 + 128 wm + 32 i + 8 (r/4) + 4 lh + r%4][n0 + 128 wn + 32 j + l32] ----
