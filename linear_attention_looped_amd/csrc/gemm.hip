@@ -324,7 +324,7 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 // shuffle reduction and every global access is a 16-byte vector.
 constexpr int SBM = 64, SBN = 128, SNS = 5;   // rows, columns, LDS stages
 
-template <int EPI, int DH>
+template <int EPI, int DH, int KTC>   // KTC: K-tiles known at compile time (0: K at run time)
 __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, int M, int N, int K,
                                                          ProjOut po, ResidOut ro) {
@@ -388,7 +388,11 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
     // barrier (every wave's share has landed, and every wave has finished
     // reading the stage that K-tile kt + SNS - 1 is about to overwrite), issue
     // that K-tile, multiply K-tile kt.
-    const int KT = K / BK;
+    // With the K-tile count known at compile time the K loop unrolls completely;
+    // the compiler's wait counts are then exact and the DMAs of the later
+    // stages stay in flight while a stage is read (in a loop they are merged at
+    // the back-edge into a wait for all but the newest stage).
+    const int KT = KTC > 0 ? KTC : K / BK;
     // stage arrays by compile-time index (so each access names its own array)
     auto stA = [&](auto sc) -> uint16_t * {
         constexpr int S = decltype(sc)::value;
@@ -424,12 +428,18 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
         compute(stA(cs), stB(cs));
     };
     static_assert(SNS == 5, "the step sequence below names five stages");
-    for (int kt = 0; kt < KT; kt += SNS) {
+    auto five = [&](int kt) {
         step(kt, std::integral_constant<int, 0>{});
         if (kt + 1 < KT) step(kt + 1, std::integral_constant<int, 1>{});
         if (kt + 2 < KT) step(kt + 2, std::integral_constant<int, 2>{});
         if (kt + 3 < KT) step(kt + 3, std::integral_constant<int, 3>{});
         if (kt + 4 < KT) step(kt + 4, std::integral_constant<int, 4>{});
+    };
+    if constexpr (KTC > 0) {
+#pragma unroll
+        for (int kt = 0; kt < KTC; kt += SNS) five(kt);
+    } else {
+        for (int kt = 0; kt < KT; kt += SNS) five(kt);
     }
 
     // accumulators -> LDS: register r of tile i holds row 32 i + 8 (r/4) + 4 lh + r%4,
@@ -525,9 +535,14 @@ hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, 
     if (use_small(M, N)) {
         const unsigned sg = (unsigned)((M + SBM - 1) / SBM) * (unsigned)((N + SBN - 1) / SBN);
         if (d == 64)
-            hipLaunchKernelGGL((gemm_small_kernel<EPI_PROJ, 64>), dim3(sg), dim3(256), 0, s, X, W, M, N, K, po, ro);
+            hipLaunchKernelGGL((gemm_small_kernel<EPI_PROJ, 64, 0>), dim3(sg), dim3(256), 0, s, X, W, M, N, K, po, ro);
         else
-            hipLaunchKernelGGL((gemm_small_kernel<EPI_PROJ, 128>), dim3(sg), dim3(256), 0, s, X, W, M, N, K, po, ro);
+            if (K == 32 * BK)
+                hipLaunchKernelGGL((gemm_small_kernel<EPI_PROJ, 128, 32>), dim3(sg), dim3(256), 0, s, X, W, M, N, K, po,
+                                   ro);
+            else
+                hipLaunchKernelGGL((gemm_small_kernel<EPI_PROJ, 128, 0>), dim3(sg), dim3(256), 0, s, X, W, M, N, K, po,
+                                   ro);
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
@@ -545,7 +560,10 @@ hipError_t launch_gemm_resid(const uint16_t *O, const uint16_t *W, int M, int N,
     ResidOut ro{h, xb};
     if (use_small(M, N)) {
         const unsigned sg = (unsigned)((M + SBM - 1) / SBM) * (unsigned)((N + SBN - 1) / SBN);
-        hipLaunchKernelGGL((gemm_small_kernel<EPI_RESID, 128>), dim3(sg), dim3(256), 0, s, O, W, M, N, K, po, ro);
+        if (K == 32 * BK)
+            hipLaunchKernelGGL((gemm_small_kernel<EPI_RESID, 128, 32>), dim3(sg), dim3(256), 0, s, O, W, M, N, K, po, ro);
+        else
+            hipLaunchKernelGGL((gemm_small_kernel<EPI_RESID, 128, 0>), dim3(sg), dim3(256), 0, s, O, W, M, N, K, po, ro);
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
