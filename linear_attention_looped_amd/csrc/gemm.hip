@@ -8,9 +8,15 @@
 // accumulation registers: one wave per SIMD).  Per k-step of 16 a wave reads
 // four A and four B fragments for sixteen products, a third less LDS traffic
 // per multiply-add than 64 x 128 wave tiles.  A and B K-tiles are loaded
-// straight into double-buffered LDS by LDS-DMA buffer loads one tile ahead;
-// LDS rows are 128 bytes with the 16-byte segments XOR-swizzled by row, so
-// fragment reads of 8 or 16 consecutive rows hit distinct banks.
+// straight into double-buffered LDS by LDS-DMA buffer loads; the workgroup
+// meets once per K-tile, before its last k-step, so that k-step's products
+// cover the next tile's first fragment reads.  LDS rows are 128 bytes with the
+// 16-byte segments XOR-swizzled by row, so fragment reads of 8 or 16
+// consecutive rows hit distinct banks.  The epilogues stage 32-row blocks of
+// the accumulators through the idle K-tile buffers and work row by row.
+//
+// For the few rows of a decode step (M of a few hundred) a 64 x 128 variant
+// streams its K-tiles through five LDS stages instead (gemm_small_kernel).
 //
 // 32x32x16 operand layout: A[i][k]: lane = i + 32*(k/8), slot k%8; B[k][j]:
 // lane = j + 32*(k/8), slot k%8; accumulator register r of lane l holds
@@ -91,9 +97,9 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     // w, w + 4, ... (8 rows each); lane i of chunk c writes bytes 16 i of it, i.e.
     // row 8 c + i / 8, physical segment i % 8, and fetches the logical segment the
     // swizzle maps there.  The descriptors end at the tile's last row of A (B) in
-    // range, so rows past M (N) read as zero.  The next K-tile is requested into
-    // the other buffer at the top of a tile and waited for at its end, so a whole
-    // tile of products covers the load latency, with no staging registers.
+    // range, so rows past M (N) read as zero.  K-tile kt + 2 is requested into
+    // K-tile kt's buffer at kt's barrier and waited for at kt + 1's, so a tile of
+    // products covers the load latency, with no staging registers.
     int voa[8], vob[8];
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
