@@ -557,19 +557,24 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                                                         float *__restrict__ dk, float *__restrict__ dv,
                                                         float *__restrict__ dlog_alpha, float *__restrict__ dbeta,
                                                         int L, int H, int NC) {
-    constexpr int BV = 16, DP = D + 1, VP = BV + 1;
+    // Row pitches are multiples of four floats: where a product's operand row is
+    // contiguous in k, a lane reads its four k values with one 16-byte load (in
+    // a 16-wide k block, product m takes k = 4 (l / 16) + m from lane l, which
+    // covers each k once), and the K, Q rows and the 16-column value blocks are
+    // read that way.
+    constexpr int BV = 16, DP = D + 4, VP = BV + 4;
     constexpr int NJ = D / 16, NP = BC / 16;   // 16-column tiles of dQ/dK and of dP/dTm
     static_assert(BNT == 256 && BC == 64, "four waves of 16 token rows");
     // phase-1 buffers (per value block) and phase-2 buffers (C x C) share one region
-    constexpr int P1 = 2 * D * VP + 9 * BC * VP;
+    constexpr int P1 = 2 * D * VP + 6 * BC * VP;
     constexpr int P2 = 3 * BC * CPp;
     constexpr int UN = P1 > P2 ? P1 : P2;
-    __shared__ float Qs[BC * DP], Ks[BC * DP], Ns[BC * CPp], Ps[BC * CPp], un[UN];
+    __shared__ __attribute__((aligned(16))) float Qs[BC * DP], Ks[BC * DP], un[UN];
+    __shared__ float Ns[BC * CPp], Ps[BC * CPp];
     __shared__ float bt[BC], gq[BC], gk[BC], gd[BC], red[BNT];
     __shared__ double g[BC];
-    float *Sb = un, *dSb = Sb + D * VP, *Vb = dSb + D * VP, *dOb = Vb + BC * VP, *KS = dOb + BC * VP,
-          *QS = KS + BC * VP, *KdS = QS + BC * VP, *Rb = KdS + BC * VP, *Ub = Rb + BC * VP, *dUb = Ub + BC * VP,
-          *dRb = dUb + BC * VP;
+    float *Sb = un, *dSb = Sb + D * VP, *Vb = dSb + D * VP, *dOb = Vb + BC * VP, *Rb = dOb + BC * VP,
+          *Ub = Rb + BC * VP, *dUb = Ub + BC * VP, *dRb = dUb + BC * VP;
     float *X1 = un, *X2 = un + BC * CPp, *X3 = un + 2 * BC * CPp;
 
     const int c = blockIdx.x % NC;
@@ -600,7 +605,6 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     if (tid < BC) {
         g[tid] = reinterpret_cast<const double *>(gc)[tid];
         bt[tid] = tid < n ? beta[row0 + (size_t)tid * H] : 0.f;
-        gq[tid] = gk[tid] = gd[tid] = 0.f;
     }
     float sdot = 0.f;
     f32x4 aq[NJ], ak[NJ], ap[NP], at[NP];
@@ -611,6 +615,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     __syncthreads();
     const double gC = g[n - 1];
     const float ea = dexp2(g[ra], 0.0), eca = dexp2(gC, g[ra]);   // gamma, gamma_C / gamma of row ra
+    // gate row terms of this lane's accumulator rows t = R0 + 4 (lane / 16) + r,
+    // summed over the value blocks: gamma <dO, QS>, -gamma <dR, KS>, (gamma_C/gamma) <U, KdS>
+    float gqr[4] = {0.f, 0.f, 0.f, 0.f}, gkr[4] = {0.f, 0.f, 0.f, 0.f}, gdr[4] = {0.f, 0.f, 0.f, 0.f};
 
     // A value block's S and dS' columns (16-byte pieces), V and dO columns: the
     // loads of block vb + 1 are issued once block vb is in LDS and land while it
@@ -634,39 +641,41 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
 #pragma unroll
         for (int i = 0; i < SP; ++i) {
             const int e = 4 * (tid + BNT * i), r = e / BV, cc = e % BV;
+            const f32x4 a = {__uint_as_float(xs[i][0]), __uint_as_float(xs[i][1]), __uint_as_float(xs[i][2]),
+                             __uint_as_float(xs[i][3])};
+            const f32x4 d2 = {__uint_as_float(xd[i][0]), __uint_as_float(xd[i][1]), __uint_as_float(xd[i][2]),
+                              __uint_as_float(xd[i][3])};
+            *reinterpret_cast<f32x4 *>(&Sb[r * VP + cc]) = a;
+            *reinterpret_cast<f32x4 *>(&dSb[r * VP + cc]) = d2;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float a = __uint_as_float(xs[i][j]), d2 = __uint_as_float(xd[i][j]);
-                Sb[r * VP + cc + j] = a;
-                dSb[r * VP + cc + j] = d2;
-                sdot = fmaf(a, d2, sdot);
-            }
+            for (int j = 0; j < 4; ++j) sdot = fmaf(a[j], d2[j], sdot);
         }
         rv.put(Vb, VP);
         ro.put(dOb, VP);
         if (vb + 1 < D / BV) fetch(vb + 1);
         __syncthreads();
-        {   // KS = K S, QS = Q S, KdS = K dS' (C x BV);  R = V - diag(gamma) KS
-            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1;
-#pragma unroll 8
-            for (int k0 = 0; k0 < D; k0 += 4) {
-                const int kk = k0 + lq;
-                const float ka = Ks[ra * DP + kk], qa = Qs[ra * DP + kk];
-                const float sb = Sb[kk * VP + lr], dsb = dSb[kk * VP + lr];
-                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, sb, a1, 0, 0, 0);
-                a2 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa, sb, a2, 0, 0, 0);
-                a3 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, dsb, a3, 0, 0, 0);
-            }
+        // KS = K S, QS = Q S, KdS = K dS' (C x BV), kept in registers;  R = V - diag(gamma) KS
+        f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = ks, kds = ks;
+#pragma unroll 2
+        for (int kb = 0; kb < D; kb += 16) {
+            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&Ks[ra * DP + kb + 4 * lq]);
+            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&Qs[ra * DP + kb + 4 * lq]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = R0 + 4 * lq + r, o = t * VP + lr;
-                KS[o] = a1[r];
-                QS[o] = a2[r];
-                KdS[o] = a3[r];
-                Rb[o] = Vb[o] - dexp2(g[t], 0.0) * a1[r];
+            for (int m = 0; m < 4; ++m) {
+                const int kk = kb + 4 * lq + m;
+                const float sb = Sb[kk * VP + lr], dsb = dSb[kk * VP + lr];
+                ks = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], sb, ks, 0, 0, 0);
+                qs = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[m], sb, qs, 0, 0, 0);
+                kds = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], dsb, kds, 0, 0, 0);
             }
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = (R0 + 4 * lq + r) * VP + lr;
+            Rb[o] = Vb[o] - dexp2(g[R0 + 4 * lq + r], 0.0) * ks[r];
+        }
         __syncthreads();
+        f32x4 u4;   // U, this lane's accumulator rows
         {   // U = N diag(beta) R ; dU = P^T dO + diag(gamma_C/gamma) K dS'
             // four partial sums per product (k-step mod 4): eight independent chains
             f32x4 p1[4], p2[4];
@@ -678,12 +687,13 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 p1[h4] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[ra * CPp + kk], bt[kk] * Rb[kk * VP + lr], p1[h4], 0, 0, 0);
                 p2[h4] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[kk * CPp + ra], dOb[kk * VP + lr], p2[h4], 0, 0, 0);
             }
-            const f32x4 a1 = (p1[0] + p1[1]) + (p1[2] + p1[3]), a2 = (p2[0] + p2[1]) + (p2[2] + p2[3]);
+            u4 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
+            const f32x4 a2 = (p2[0] + p2[1]) + (p2[2] + p2[3]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = R0 + 4 * lq + r, o = t * VP + lr;
-                Ub[o] = a1[r];
-                dUb[o] = fmaf(dexp2(gC, g[t]), KdS[o], a2[r]);
+                Ub[o] = u4[r];
+                dUb[o] = fmaf(dexp2(gC, g[t]), kds[r], a2[r]);
             }
         }
         __syncthreads();
@@ -703,44 +713,50 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 const float x = bt[t] * a1[r];
                 dRb[t * VP + lr] = x;
                 if (t < n) dv[(row0 + (size_t)t * H) * D + vb * BV + lr] = x;
+                // gate row terms: this block's 16 columns of row t sit in the 16
+                // lanes of this lane's group; reduce across them
+                float x1 = dOb[t * VP + lr] * qs[r], x2 = x * ks[r], x3 = u4[r] * kds[r];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    x1 += __shfl_xor(x1, o);
+                    x2 += __shfl_xor(x2, o);
+                    x3 += __shfl_xor(x3, o);
+                }
+                const float e = dexp2(g[t], 0.0);
+                gqr[r] += e * x1;
+                gkr[r] -= e * x2;
+                gdr[r] += dexp2(gC, g[t]) * x3;
             }
         }
         __syncthreads();
-        // gate row terms (wave 0): gamma <dO, QS>, -gamma <dR, KS>, (gamma_C/gamma) <U, KdS>
-        if (tid < BC) {
-            const int t = tid;
-            float x1 = 0.f, x2 = 0.f, x3 = 0.f;
-#pragma unroll
-            for (int s = 0; s < BV; ++s) {
-                x1 = fmaf(dOb[t * VP + s], QS[t * VP + s], x1);
-                x2 = fmaf(dRb[t * VP + s], KS[t * VP + s], x2);
-                x3 = fmaf(Ub[t * VP + s], KdS[t * VP + s], x3);
-            }
-            gq[t] += dexp2(g[t], 0.0) * x1;
-            gk[t] -= dexp2(g[t], 0.0) * x2;
-            gd[t] += dexp2(gC, g[t]) * x3;
-        }
         // register accumulations over this value block (k = value column s)
         //   dQ += diag(gamma) dO S^T ; dK += diag(gamma_C/gamma) U dS'^T - diag(gamma) dR S^T
         //   dP += dO U^T ; dTm += dU R^T
-#pragma unroll
-        for (int k0 = 0; k0 < BV; k0 += 4) {
-            const int s = k0 + lq;
-            const float o = dOb[ra * VP + s], du = dUb[ra * VP + s];
-            const float oe = ea * o, ue = eca * Ub[ra * VP + s], re = -ea * dRb[ra * VP + s];
+        {   // value column s = 4 (lane / 16) + m in product m
+            const f32x4 o4 = *reinterpret_cast<const f32x4 *>(&dOb[ra * VP + 4 * lq]);
+            const f32x4 du4 = *reinterpret_cast<const f32x4 *>(&dUb[ra * VP + 4 * lq]);
+            const f32x4 ua4 = *reinterpret_cast<const f32x4 *>(&Ub[ra * VP + 4 * lq]);
+            const f32x4 ra4 = *reinterpret_cast<const f32x4 *>(&dRb[ra * VP + 4 * lq]);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int cc = 16 * j + lr;
-                const float sq = Sb[cc * VP + s], sd = dSb[cc * VP + s];
-                aq[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(oe, sq, aq[j], 0, 0, 0);
-                ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ue, sd, ak[j], 0, 0, 0);
-                ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(re, sq, ak[j], 0, 0, 0);
+                const f32x4 sq = *reinterpret_cast<const f32x4 *>(&Sb[(16 * j + lr) * VP + 4 * lq]);
+                const f32x4 sd = *reinterpret_cast<const f32x4 *>(&dSb[(16 * j + lr) * VP + 4 * lq]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    aq[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ea * o4[m], sq[m], aq[j], 0, 0, 0);
+                    ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(eca * ua4[m], sd[m], ak[j], 0, 0, 0);
+                    ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(-ea * ra4[m], sq[m], ak[j], 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
-                const int jj = 16 * j + lr;
-                ap[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(o, Ub[jj * VP + s], ap[j], 0, 0, 0);
-                at[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(du, Rb[jj * VP + s], at[j], 0, 0, 0);
+                const f32x4 ub = *reinterpret_cast<const f32x4 *>(&Ub[(16 * j + lr) * VP + 4 * lq]);
+                const f32x4 rb = *reinterpret_cast<const f32x4 *>(&Rb[(16 * j + lr) * VP + 4 * lq]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    ap[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[m], ub[m], ap[j], 0, 0, 0);
+                    at[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(du4[m], rb[m], at[j], 0, 0, 0);
+                }
             }
         }
         __syncthreads();
@@ -751,10 +767,13 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
         f32x4 qk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int k0 = 0; k0 < D; k0 += 4)
-            qk = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[ra * DP + k0 + lq], Ks[(16 * j + lr) * DP + k0 + lq], qk,
-                                                     0, 0, 0);
+#pragma unroll 4
+        for (int kb = 0; kb < D; kb += 16) {
+            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&Qs[ra * DP + kb + 4 * lq]);
+            const f32x4 kb4 = *reinterpret_cast<const f32x4 *>(&Ks[(16 * j + lr) * DP + kb + 4 * lq]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) qk = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[m], kb4[m], qk, 0, 0, 0);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = R0 + 4 * lq + r, s = 16 * j + lr;
@@ -795,10 +814,13 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         for (int k0 = 0; k0 < BC; k0 += 4)
             a = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[(k0 + lq) * CPp + ra], X2[(k0 + lq) * CPp + 16 * j + lr], a,
                                                     0, 0, 0);
-#pragma unroll 8
-        for (int k0 = 0; k0 < D; k0 += 4)
-            kk4 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[ra * DP + k0 + lq], Ks[(16 * j + lr) * DP + k0 + lq], kk4,
-                                                      0, 0, 0);
+#pragma unroll 4
+        for (int kb = 0; kb < D; kb += 16) {
+            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&Ks[ra * DP + kb + 4 * lq]);
+            const f32x4 kb4 = *reinterpret_cast<const f32x4 *>(&Ks[(16 * j + lr) * DP + kb + 4 * lq]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) kk4 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], kb4[m], kk4, 0, 0, 0);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = R0 + 4 * lq + r, s = 16 * j + lr;
@@ -857,6 +879,14 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 dq[(row0 + (size_t)t * H) * D + 16 * j + lr] = aq[j][r];
                 dk[(row0 + (size_t)t * H) * D + 16 * j + lr] = ak[j][r];
             }
+    }
+    if (lr == 0) {   // each accumulator row belongs to one lane group
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            gq[R0 + 4 * lq + r] = gqr[r];
+            gk[R0 + 4 * lq + r] = gkr[r];
+            gd[R0 + 4 * lq + r] = gdr[r];
+        }
     }
     // gate (wave 0, thread j = token j of the chunk).  The pairs i < j <= t of X
     // (lower triangular, rows >= n zero): column suffix sums over t in place
