@@ -110,7 +110,7 @@ struct Rows {
     }
 };
 // A C x C fp32 matrix of the workspace (16-byte aligned, row-major) into LDS
-// with pitch CPp, four 16-byte loads per thread.
+// (pitch CPp unless given), four 16-byte loads per thread.
 struct CCm {
     static constexpr int IT = BC * BC / 4 / BNT;
     u32x4 x[IT];
@@ -118,12 +118,21 @@ struct CCm {
 #pragma unroll
         for (int i = 0; i < IT; ++i) x[i] = reinterpret_cast<const u32x4 *>(src)[threadIdx.x + BNT * i];
     }
-    __device__ __forceinline__ void put(float *dst) const {
+    __device__ __forceinline__ void put(float *dst, int pitch = CPp) const {
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
             const int e = 4 * (threadIdx.x + BNT * i), r = e / BC, c = e % BC;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[r * CPp + c + j] = __uint_as_float(x[i][j]);
+            for (int j = 0; j < 4; ++j) dst[r * pitch + c + j] = __uint_as_float(x[i][j]);
+        }
+    }
+    // transposed: dst[c * pitch + r] = M[r][c]
+    __device__ __forceinline__ void put_t(float *dst, int pitch) const {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = 4 * (threadIdx.x + BNT * i), r = e / BC, c = e % BC;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[(c + j) * pitch + r] = __uint_as_float(x[i][j]);
         }
     }
 };
@@ -145,98 +154,187 @@ __device__ __forceinline__ void gate_prefix(double *g, const float *alpha, size_
 
 // 2^(a - b) from fp64 exponents
 __device__ __forceinline__ float dexp2(double a, double b) { return exp2_fast((float)(a - b)); }
+// Sum over each 16-lane row of the wave (lanes 16 i .. 16 i + 15), result in
+// every lane of the row: rotations by 8 and 4 within the row, then swaps of
+// lane pairs 2 apart and 1 apart within each quad (all DPP moves).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));   // row_ror:8
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));   // row_ror:4
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));    // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));    // quad_perm 1,0,3,2
+    return x;
+}
 
 // ---------------------------------------------------------------------------
-// g, N = (I + A)^-1 and P of one chunk.
+// g, N = (I + A)^-1 and P of one chunk.  K K^T and Q K^T run on the matrix
+// cores in 32-wide k blocks (bf16 inputs: one bf16 instruction per block, whose
+// products are exact, with fp32 sums; fp32 inputs: eight fp32 instructions).
+// In a block, lane l reads eight consecutive k values 32 kb + 8 (l / 16) ..
+// of row l % 16 of both operands.  The inverse takes its 16 x 16 diagonal
+// blocks by forward substitution in registers and the blocks below them by
+// block distance on the fp32 matrix cores:
+//   N_IJ = -N_II sum_{K=J}^{I-1} A_IK N_KJ   (I > J).
+template <typename TI>
+__device__ __forceinline__ f32x4 gram_block(f32x4 acc, const TI *a, const TI *b);
+template <>
+__device__ __forceinline__ f32x4 gram_block<uint16_t>(f32x4 acc, const uint16_t *a, const uint16_t *b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(a),
+                                                   *reinterpret_cast<const bf16x8 *>(b), acc, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 gram_block<float>(f32x4 acc, const float *a, const float *b) {
+    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(a), a1 = *reinterpret_cast<const f32x4 *>(a + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(b), b1 = *reinterpret_cast<const f32x4 *>(b + 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[s], b0[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[s], b1[s], acc, 0, 0, 0);
+    return acc;
+}
+// (I, J) of lower tile number tl (row-major over I >= J)
+__device__ __forceinline__ void lower_tile(int tl, int &I, int &J) {
+    I = 0;
+    while ((I + 1) * (I + 2) / 2 <= tl) ++I;
+    J = tl - I * (I + 1) / 2;
+}
+
 template <int D, typename TI>
 __global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                        const float *__restrict__ alpha,
                                                        const float *__restrict__ beta, float *__restrict__ gnp,
                                                        int L, int H, int NC) {
-    constexpr int DP = D + 1;
-    __shared__ float Ks[BC * DP], Qs[BC * DP], As[BC * CPp], Ns[BC * CPp], bt[BC];
+    constexpr int KP = D + 16 / (int)sizeof(TI);   // row pitch (elements): rows stay 16-byte aligned
+    constexpr int CQ = BC + 4, NT = BC / 16, NLT = NT * (NT + 1) / 2, MP = (NLT + 3) / 4;
+    constexpr int VE = 16 / (int)sizeof(TI), PPR = D / VE, PCS = BC * PPR / BNT;   // 16-byte pieces
+    static_assert(BC * PPR % BNT == 0 && 2 * BC * KP * (int)sizeof(TI) >= BC * CQ * 4, "layout");
+    __shared__ __attribute__((aligned(16))) TI KQ[2 * BC * KP];   // K, Q; then P
+    __shared__ __attribute__((aligned(16))) float As[BC * CQ], Ns[BC * CQ];
+    __shared__ float Xs[NT][16 * 17], bt[BC];
     __shared__ double g[BC];
+    TI *Ks = KQ, *Qs = KQ + BC * KP;
+    float *Ps = reinterpret_cast<float *>(KQ);
     const int c = blockIdx.x % NC;
     const size_t unit = blockIdx.x / NC;
     const int h = (int)(unit % H), b = (int)(unit / H);
     const int t0 = c * BC, n = min(BC, L - t0);
-    const size_t tok = (size_t)H * D;
     const size_t row0 = ((size_t)b * L + t0) * H + h;   // (b, t0, h) in [B, L, H]
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     {
-        Rows<D, TI> rk, rq;
-        rk.fetch(k + row0 * D, tok, n);
-        rq.fetch(q + row0 * D, tok, n);
-        rk.put(Ks, DP);
-        rq.put(Qs, DP);
+        u32x4 kr[PCS], qr[PCS];
+#pragma unroll
+        for (int i = 0; i < PCS; ++i) {
+            const int idx = tid + BNT * i, r = idx / PPR, cc = VE * (idx % PPR);
+            const size_t o = (row0 + (size_t)min(r, n - 1) * H) * D + cc;
+            kr[i] = *reinterpret_cast<const u32x4 *>(k + o);
+            qr[i] = *reinterpret_cast<const u32x4 *>(q + o);
+        }
+#pragma unroll
+        for (int i = 0; i < PCS; ++i) {
+            const int idx = tid + BNT * i, r = idx / PPR, cc = VE * (idx % PPR);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(Ks + r * KP + cc) = r < n ? kr[i] : z;
+            *reinterpret_cast<u32x4 *>(Qs + r * KP + cc) = r < n ? qr[i] : z;
+        }
     }
     gate_prefix(g, alpha + row0, H, n);
-    if (threadIdx.x < BC) bt[threadIdx.x] = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
+    if (tid < BC) bt[tid] = tid < n ? beta[row0 + (size_t)tid * H] : 0.f;
+    // N starts as zero (its blocks above the diagonal stay zero)
+    for (int idx = tid; idx < BC * BC; idx += BNT) Ns[(idx / BC) * CQ + idx % BC] = 0.f;
     __syncthreads();
-    // K K^T and Q K^T on the fp32 matrix cores: wave w owns rows 16w .. 16w + 15
-    const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
-    const int R0 = 16 * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), ra = R0 + lr;
-    float *out = gnp + (unit * NC + c) * GNP_FLOATS;
+    // A = strict_lower(beta_t Gam_ts k_t . k_s): the lower tiles of K K^T (wave w
+    // takes tiles w, w + 4, ...); tiles above the diagonal are never read
+    for (int tl = wave; tl < NLT; tl += 4) {
+        int I, J;
+        lower_tile(tl, I, J);
+        const TI *ar = Ks + (16 * I + lr) * KP + 8 * lq, *br = Ks + (16 * J + lr) * KP + 8 * lq;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < BC / 16; ++j) {
-        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
-#pragma unroll 8
-        for (int k0 = 0; k0 < D; k0 += 4) {
-            const float kb = Ks[(16 * j + lr) * DP + k0 + lq];
-            kk = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[ra * DP + k0 + lq], kb, kk, 0, 0, 0);
-            qk = __builtin_amdgcn_mfma_f32_16x16x4f32(Qs[ra * DP + k0 + lq], kb, qk, 0, 0, 0);
-        }
+        for (int kb = 0; kb < D / 32; ++kb) acc = gram_block<TI>(acc, ar + 32 * kb, br + 32 * kb);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = R0 + 4 * lq + r, s = 16 * j + lr;
-            const float gam = dexp2(g[t], g[min(s, t)]);
-            As[t * CPp + s] = s < t ? bt[t] * kk[r] * gam : 0.f;
-            out[G_FLOATS + BC * BC + t * BC + s] = (s <= t && t < n) ? qk[r] * gam : 0.f;   // P
+            const int t = 16 * I + 4 * lq + r, s = 16 * J + lr;
+            As[t * CQ + s] = s < t ? bt[t] * dexp2(g[t], g[s]) * acc[r] : 0.f;
         }
     }
-    if (threadIdx.x < BC) reinterpret_cast<double *>(out)[threadIdx.x] = g[threadIdx.x];
-    __syncthreads();
-    // N = (I + A)^-1, blocked by 16: the four diagonal blocks by row substitution
-    // in wave 0 (lane j owns column j and reads only that column's earlier rows,
-    // so no barrier is needed between rows), then the off-diagonal blocks one
-    // block-distance at a time:
-    //   N_ij = -N_ii sum_{k=j}^{i-1} A_ik N_kj   (i > j)
-    for (int idx = threadIdx.x; idx < BC * BC; idx += BNT) Ns[(idx / BC) * CPp + idx % BC] = 0.f;
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int bb = threadIdx.x / 16, j = threadIdx.x;   // column j of diagonal block bb
-        for (int r = 0; r < 16; ++r) {
-            const int t = 16 * bb + r;
-            float x = t == j ? 1.f : 0.f;
-            for (int i = j; i < t; ++i) x = fmaf(-As[t * CPp + i], Ns[i * CPp + j], x);
-            if (j <= t) Ns[t * CPp + j] = x;
-        }
+    // the lower tiles of Q K^T stay in registers until K and Q are dead
+    f32x4 pacc[MP];
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+        pacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tl = wave + 4 * m;
+        if (tl >= NLT) continue;
+        int I, J;
+        lower_tile(tl, I, J);
+        const TI *ar = Qs + (16 * I + lr) * KP + 8 * lq, *br = Ks + (16 * J + lr) * KP + 8 * lq;
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) pacc[m] = gram_block<TI>(pacc[m], ar + 32 * kb, br + 32 * kb);
     }
     __syncthreads();
-    __shared__ float Ws[BC * CPp];   // W_ij = sum_k A_ik N_kj for the current distance
-    for (int dist = 1; dist < 4; ++dist) {
-        // W blocks (i, j = i - dist): 16 x 16 each, (4 - dist) of them
-        const int nb = 4 - dist;
-        for (int idx = threadIdx.x; idx < nb * 256; idx += BNT) {
-            const int blk = idx / 256, e = idx % 256, r = e / 16, cc = e % 16;
-            const int bi = blk + dist, bj = blk;
-            const int t = 16 * bi + r, jj = 16 * bj + cc;
-            float x = 0.f;
-            for (int kk = 16 * bj; kk < 16 * bi; ++kk) x = fmaf(As[t * CPp + kk], Ns[kk * CPp + jj], x);
-            Ws[t * CPp + jj] = x;
+    // diagonal blocks: wave w solves block w, lane j < 16 its column j
+    if (wave < NT && lane < 16) {
+        const int o = 16 * wave;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float y = t == lane ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < t; ++s2) y = fmaf(-As[(o + t) * CQ + o + s2], x[s2], y);
+            x[t] = y;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Ns[(o + t) * CQ + o + lane] = x[t];
+    }
+    __syncthreads();
+    // blocks below the diagonal, one block distance at a time (wave w: J = w)
+    for (int dist = 1; dist < NT; ++dist) {
+        if (wave < NT - dist) {
+            const int J = wave, I = wave + dist;
+            f32x4 w4 = {0.f, 0.f, 0.f, 0.f};   // W = sum_K A_IK N_KJ
+            for (int kb = 16 * J; kb < 16 * I; kb += 4)
+                w4 = __builtin_amdgcn_mfma_f32_16x16x4f32(As[(16 * I + lr) * CQ + kb + lq],
+                                                         Ns[(kb + lq) * CQ + 16 * J + lr], w4, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xs[wave][(4 * lq + r) * 17 + lr] = w4[r];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};   // N_II W
+#pragma unroll
+            for (int k4 = 0; k4 < 16; k4 += 4)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[(16 * I + lr) * CQ + 16 * I + k4 + lq],
+                                                        Xs[wave][(k4 + lq) * 17 + lr], y, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ns[(16 * I + 4 * lq + r) * CQ + 16 * J + lr] = -y[r];
         }
         __syncthreads();
-        for (int idx = threadIdx.x; idx < nb * 256; idx += BNT) {
-            const int blk = idx / 256, e = idx % 256, r = e / 16, cc = e % 16;
-            const int bi = blk + dist, bj = blk;
-            const int t = 16 * bi + r, jj = 16 * bj + cc;
-            float x = 0.f;
-            for (int kk = 16 * bi; kk <= t; ++kk) x = fmaf(Ns[t * CPp + kk], Ws[kk * CPp + jj], x);
-            Ns[t * CPp + jj] = -x;
-        }
-        __syncthreads();
     }
-    for (int idx = threadIdx.x; idx < BC * BC; idx += BNT)
-        out[G_FLOATS + idx] = Ns[(idx / BC) * CPp + idx % BC];
+    // P = (Q K^T o Gam) on s <= t, rows < n, into K's space
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+        const int tl = wave + 4 * m;
+        if (tl >= NLT) continue;
+        int I, J;
+        lower_tile(tl, I, J);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * I + 4 * lq + r, s = 16 * J + lr;
+            Ps[t * CQ + s] = (s <= t && t < n) ? dexp2(g[t], g[s]) * pacc[m][r] : 0.f;
+        }
+    }
+    __syncthreads();
+    float *out = gnp + (unit * NC + c) * GNP_FLOATS;
+    if (tid < BC) reinterpret_cast<double *>(out)[tid] = g[tid];
+    for (int idx = tid; idx < BC * BC / 4; idx += BNT) {
+        const int t = idx / (BC / 4), s = 4 * (idx % (BC / 4));
+        f32x4 nv = *reinterpret_cast<const f32x4 *>(&Ns[t * CQ + s]);
+        f32x4 pv = *reinterpret_cast<const f32x4 *>(&Ps[t * CQ + s]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (s + e > t) pv[e] = 0.f;   // tiles above the diagonal hold K, Q bytes
+        *reinterpret_cast<f32x4 *>(out + G_FLOATS + t * BC + s) = nv;
+        *reinterpret_cast<f32x4 *>(out + G_FLOATS + BC * BC + t * BC + s) = pv;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -545,8 +643,15 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
 // Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4f32: exact
 // fp32 products, fp32 sums), one 16 x 16 output tile per instruction chain.
 // Wave w owns rows 16w .. 16w + 15 (tokens) of every row-partitioned product;
-// in a tile, lane l holds rows 4 (l / 16) + r, r < 4, of column l % 16, and
-// reads A(row l % 16, k = l / 16) and B(k = l / 16, column l % 16) per k-step.
+// in a tile, lane l holds rows 4 (l / 16) + r, r < 4, of column l % 16.  The
+// contraction runs in 16-wide k blocks: in product m of a block, lane l reads
+// A(row l % 16, k = 4 (l / 16) + m) and B(k = 4 (l / 16) + m, column l % 16),
+// so an operand row contiguous in k is one 16-byte read per block, and a
+// column read touches rows 4 apart.  Row pitches: D + 4 for K and Q, 20 for
+// value blocks, C + 4 for C x C matrices (four rows apart is 16 banks apart:
+// column reads are conflict-free; 16-byte row reads are too).  The loads of a
+// block are issued before the products of the previous one
+// (sched_barrier keeps the compiler from sinking them to their use).
 template <int D, typename TI, typename TO>
 __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                         const TI *__restrict__ v, const TO *__restrict__ dout,
@@ -557,25 +662,21 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                                                         float *__restrict__ dk, float *__restrict__ dv,
                                                         float *__restrict__ dlog_alpha, float *__restrict__ dbeta,
                                                         int L, int H, int NC) {
-    // Row pitches are multiples of four floats: where a product's operand row is
-    // contiguous in k, a lane reads its four k values with one 16-byte load (in
-    // a 16-wide k block, product m takes k = 4 (l / 16) + m from lane l, which
-    // covers each k once), and the K, Q rows and the 16-column value blocks are
-    // read that way.
-    constexpr int BV = 16, DP = D + 4, VP = BV + 4;
+    constexpr int BV = 16, DP = D + 4, VP = BV + 4, CQ = BC + 4;
     constexpr int NJ = D / 16, NP = BC / 16;   // 16-column tiles of dQ/dK and of dP/dTm
+    constexpr int KD = D / 16, KC = BC / 16;   // 16-wide k blocks over D and over C
     static_assert(BNT == 256 && BC == 64, "four waves of 16 token rows");
     // phase-1 buffers (per value block) and phase-2 buffers (C x C) share one region
     constexpr int P1 = 2 * D * VP + 6 * BC * VP;
-    constexpr int P2 = 3 * BC * CPp;
+    constexpr int P2 = 3 * BC * CQ;
     constexpr int UN = P1 > P2 ? P1 : P2;
-    __shared__ __attribute__((aligned(16))) float Qs[BC * DP], Ks[BC * DP], un[UN];
-    __shared__ float Ns[BC * CPp], Ps[BC * CPp];
-    __shared__ float bt[BC], gq[BC], gk[BC], gd[BC], red[BNT];
+    // Pt holds P transposed (P is only read as P^T), then X = dP o P
+    __shared__ __attribute__((aligned(16))) float Qs[BC * DP], Ks[BC * DP], un[UN], Ns[BC * CQ], Pt[BC * CQ], bt[BC];
+    __shared__ float gq[BC], gk[BC], gd[BC], red[BNT], redb[BNT];
     __shared__ double g[BC];
     float *Sb = un, *dSb = Sb + D * VP, *Vb = dSb + D * VP, *dOb = Vb + BC * VP, *Rb = dOb + BC * VP,
           *Ub = Rb + BC * VP, *dUb = Ub + BC * VP, *dRb = dUb + BC * VP;
-    float *X1 = un, *X2 = un + BC * CPp, *X3 = un + 2 * BC * CPp;
+    float *X1 = un, *X2 = un + BC * CQ, *X3 = un + 2 * BC * CQ;
 
     const int c = blockIdx.x % NC;
     const size_t unit = blockIdx.x / NC;
@@ -589,6 +690,17 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int R0 = 16 * __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ra = R0 + lr;   // this lane's A-operand row
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // 16-byte row read and column read of a k block (k0 + 4 (lane / 16) + m)
+    auto row4 = [&](const float *m, int pitch, int r, int k0) {
+        return *reinterpret_cast<const f32x4 *>(&m[r * pitch + k0 + 4 * lq]);
+    };
+    auto col4 = [&](const float *m, int pitch, int col, int k0) {
+        const float *p = &m[(k0 + 4 * lq) * pitch + col];
+        return f32x4{p[0], p[pitch], p[2 * pitch], p[3 * pitch]};
+    };
+    auto mfma = [](float a, float b2, f32x4 acc) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b2, acc, 0, 0, 0); };
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
     {
         Rows<D, TI> rk, rq;
@@ -599,8 +711,8 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         pm.fetch(gc + G_FLOATS + BC * BC);
         rk.put(Ks, DP);
         rq.put(Qs, DP);
-        nm.put(Ns);
-        pm.put(Ps);
+        nm.put(Ns, CQ);
+        pm.put_t(Pt, CQ);
     }
     if (tid < BC) {
         g[tid] = reinterpret_cast<const double *>(gc)[tid];
@@ -609,14 +721,24 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     float sdot = 0.f;
     f32x4 aq[NJ], ak[NJ], ap[NP], at[NP];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) aq[j] = ak[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) aq[j] = ak[j] = z4;
 #pragma unroll
-    for (int j = 0; j < NP; ++j) ap[j] = at[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NP; ++j) ap[j] = at[j] = z4;
     __syncthreads();
     const double gC = g[n - 1];
     const float ea = dexp2(g[ra], 0.0), eca = dexp2(gC, g[ra]);   // gamma, gamma_C / gamma of row ra
-    // gate row terms of this lane's accumulator rows t = R0 + 4 (lane / 16) + r,
-    // summed over the value blocks: gamma <dO, QS>, -gamma <dR, KS>, (gamma_C/gamma) <U, KdS>
+    // the same and beta for this lane's accumulator rows R0 + 4 (lane / 16) + r
+    float er[4], ecr[4], br[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = R0 + 4 * lq + r;
+        er[r] = dexp2(g[t], 0.0);
+        ecr[r] = dexp2(gC, g[t]);
+        br[r] = bt[t];
+    }
+    // gate row terms <dO, QS>, <dR, KS>, <U, KdS> of this lane's accumulator rows
+    // t = R0 + 4 (lane / 16) + r: each lane sums its own column's products over
+    // the value blocks; the 16 lanes of a row are reduced once at the end
     float gqr[4] = {0.f, 0.f, 0.f, 0.f}, gkr[4] = {0.f, 0.f, 0.f, 0.f}, gdr[4] = {0.f, 0.f, 0.f, 0.f};
 
     // A value block's S and dS' columns (16-byte pieces), V and dO columns: the
@@ -655,107 +777,124 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         if (vb + 1 < D / BV) fetch(vb + 1);
         __syncthreads();
         // KS = K S, QS = Q S, KdS = K dS' (C x BV), kept in registers;  R = V - diag(gamma) KS
-        f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = ks, kds = ks;
-#pragma unroll 2
-        for (int kb = 0; kb < D; kb += 16) {
-            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&Ks[ra * DP + kb + 4 * lq]);
-            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&Qs[ra * DP + kb + 4 * lq]);
+        f32x4 ks = z4, qs = z4, kds = z4;
+        {
+            f32x4 ka[2], qa[2], sb[2], sd[2];
+            auto ld = [&](int u, int kb) {
+                ka[u] = row4(Ks, DP, ra, kb);
+                qa[u] = row4(Qs, DP, ra, kb);
+                sb[u] = col4(Sb, VP, lr, kb);
+                sd[u] = col4(dSb, VP, lr, kb);
+            };
+            ld(0, 0);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int kk = kb + 4 * lq + m;
-                const float sb = Sb[kk * VP + lr], dsb = dSb[kk * VP + lr];
-                ks = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], sb, ks, 0, 0, 0);
-                qs = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[m], sb, qs, 0, 0, 0);
-                kds = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], dsb, kds, 0, 0, 0);
+            for (int i = 0; i < KD; ++i) {
+                const int u = i & 1;
+                if (i + 1 < KD) ld(u ^ 1, 16 * (i + 1));
+                fence();
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    ks = mfma(ka[u][m], sb[u][m], ks);
+                    qs = mfma(qa[u][m], sb[u][m], qs);
+                    kds = mfma(ka[u][m], sd[u][m], kds);
+                }
+                fence();
             }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int o = (R0 + 4 * lq + r) * VP + lr;
-            Rb[o] = Vb[o] - dexp2(g[R0 + 4 * lq + r], 0.0) * ks[r];
+            const int t = R0 + 4 * lq + r, o = t * VP + lr;
+            Rb[o] = Vb[o] - er[r] * ks[r];
         }
         __syncthreads();
+        // U = N diag(beta) R ; dU = P^T dO + diag(gamma_C/gamma) K dS'
         f32x4 u4;   // U, this lane's accumulator rows
-        {   // U = N diag(beta) R ; dU = P^T dO + diag(gamma_C/gamma) K dS'
-            // four partial sums per product (k-step mod 4): eight independent chains
-            f32x4 p1[4], p2[4];
+        {
+            f32x4 p1[2] = {z4, z4}, p2[2] = {z4, z4};   // two partial sums per product (m even, odd)
+            f32x4 na[2], pa[2], ba[2], rb[2], ob[2];
+            auto ld = [&](int u, int kb) {
+                na[u] = row4(Ns, CQ, ra, kb);
+                pa[u] = row4(Pt, CQ, ra, kb);
+                ba[u] = *reinterpret_cast<const f32x4 *>(&bt[kb + 4 * lq]);
+                rb[u] = col4(Rb, VP, lr, kb);
+                ob[u] = col4(dOb, VP, lr, kb);
+            };
+            ld(0, 0);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) p1[x] = p2[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < KC; ++i) {
+                const int u = i & 1;
+                if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
+                fence();
 #pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 4) {
-                const int kk = k0 + lq, h4 = (k0 >> 2) & 3;
-                p1[h4] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[ra * CPp + kk], bt[kk] * Rb[kk * VP + lr], p1[h4], 0, 0, 0);
-                p2[h4] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[kk * CPp + ra], dOb[kk * VP + lr], p2[h4], 0, 0, 0);
+                for (int m = 0; m < 4; ++m) {
+                    p1[m & 1] = mfma(na[u][m], ba[u][m] * rb[u][m], p1[m & 1]);
+                    p2[m & 1] = mfma(pa[u][m], ob[u][m], p2[m & 1]);
+                }
+                fence();
             }
-            u4 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
-            const f32x4 a2 = (p2[0] + p2[1]) + (p2[2] + p2[3]);
+            u4 = p1[0] + p1[1];
+            const f32x4 a2 = p2[0] + p2[1];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = R0 + 4 * lq + r, o = t * VP + lr;
                 Ub[o] = u4[r];
-                dUb[o] = fmaf(dexp2(gC, g[t]), kds[r], a2[r]);
+                dUb[o] = fmaf(ecr[r], kds[r], a2[r]);
             }
         }
         __syncthreads();
         {   // dR = diag(beta) N^T dU  (= dV)
-            f32x4 p1[4];   // four partial sums (k-step mod 4)
+            f32x4 p1[2] = {z4, z4};
+            f32x4 na[2], db[2];
+            auto ld = [&](int u, int kb) {
+                na[u] = col4(Ns, CQ, ra, kb);
+                db[u] = col4(dUb, VP, lr, kb);
+            };
+            ld(0, 0);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) p1[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < KC; ++i) {
+                const int u = i & 1;
+                if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
+                fence();
 #pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 4) {
-                const int kk = k0 + lq, h4 = (k0 >> 2) & 3;
-                p1[h4] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[kk * CPp + ra], dUb[kk * VP + lr], p1[h4], 0, 0, 0);
+                for (int m = 0; m < 4; ++m) p1[m & 1] = mfma(na[u][m], db[u][m], p1[m & 1]);
+                fence();
             }
-            const f32x4 a1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
+            const f32x4 a1 = p1[0] + p1[1];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = R0 + 4 * lq + r;
-                const float x = bt[t] * a1[r];
+                const float x = br[r] * a1[r];
                 dRb[t * VP + lr] = x;
                 if (t < n) dv[(row0 + (size_t)t * H) * D + vb * BV + lr] = x;
-                // gate row terms: this block's 16 columns of row t sit in the 16
-                // lanes of this lane's group; reduce across them
-                float x1 = dOb[t * VP + lr] * qs[r], x2 = x * ks[r], x3 = u4[r] * kds[r];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    x1 += __shfl_xor(x1, o);
-                    x2 += __shfl_xor(x2, o);
-                    x3 += __shfl_xor(x3, o);
-                }
-                const float e = dexp2(g[t], 0.0);
-                gqr[r] += e * x1;
-                gkr[r] -= e * x2;
-                gdr[r] += dexp2(gC, g[t]) * x3;
+                gqr[r] = fmaf(dOb[t * VP + lr], qs[r], gqr[r]);
+                gkr[r] = fmaf(x, ks[r], gkr[r]);
+                gdr[r] = fmaf(u4[r], kds[r], gdr[r]);
             }
         }
         __syncthreads();
         // register accumulations over this value block (k = value column s)
         //   dQ += diag(gamma) dO S^T ; dK += diag(gamma_C/gamma) U dS'^T - diag(gamma) dR S^T
         //   dP += dO U^T ; dTm += dU R^T
-        {   // value column s = 4 (lane / 16) + m in product m
-            const f32x4 o4 = *reinterpret_cast<const f32x4 *>(&dOb[ra * VP + 4 * lq]);
-            const f32x4 du4 = *reinterpret_cast<const f32x4 *>(&dUb[ra * VP + 4 * lq]);
-            const f32x4 ua4 = *reinterpret_cast<const f32x4 *>(&Ub[ra * VP + 4 * lq]);
-            const f32x4 ra4 = *reinterpret_cast<const f32x4 *>(&dRb[ra * VP + 4 * lq]);
+        {
+            const f32x4 o4 = row4(dOb, VP, ra, 0), du4 = row4(dUb, VP, ra, 0);
+            const f32x4 ua4 = row4(Ub, VP, ra, 0), ra4 = row4(dRb, VP, ra, 0);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const f32x4 sq = *reinterpret_cast<const f32x4 *>(&Sb[(16 * j + lr) * VP + 4 * lq]);
-                const f32x4 sd = *reinterpret_cast<const f32x4 *>(&dSb[(16 * j + lr) * VP + 4 * lq]);
+                const f32x4 sq = row4(Sb, VP, 16 * j + lr, 0), sd = row4(dSb, VP, 16 * j + lr, 0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    aq[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ea * o4[m], sq[m], aq[j], 0, 0, 0);
-                    ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(eca * ua4[m], sd[m], ak[j], 0, 0, 0);
-                    ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(-ea * ra4[m], sq[m], ak[j], 0, 0, 0);
+                    aq[j] = mfma(ea * o4[m], sq[m], aq[j]);
+                    ak[j] = mfma(eca * ua4[m], sd[m], ak[j]);
+                    ak[j] = mfma(-ea * ra4[m], sq[m], ak[j]);
                 }
             }
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
-                const f32x4 ub = *reinterpret_cast<const f32x4 *>(&Ub[(16 * j + lr) * VP + 4 * lq]);
-                const f32x4 rb = *reinterpret_cast<const f32x4 *>(&Rb[(16 * j + lr) * VP + 4 * lq]);
+                const f32x4 ub = row4(Ub, VP, 16 * j + lr, 0), rb = row4(Rb, VP, 16 * j + lr, 0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    ap[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(o4[m], ub[m], ap[j], 0, 0, 0);
-                    at[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(du4[m], rb[m], at[j], 0, 0, 0);
+                    ap[j] = mfma(o4[m], ub[m], ap[j]);
+                    at[j] = mfma(du4[m], rb[m], at[j]);
                 }
             }
         }
@@ -764,110 +903,191 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
 
     // ---- phase 2: C x C algebra (buffers X1..X3 replace the value-block buffers) ----
     // (a) X1 = dP o Gam (lower incl, rows < n), X2 = dTm, X3 = Q K^T
+    {
+        f32x4 qk[NP];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-        f32x4 qk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int kb = 0; kb < D; kb += 16) {
-            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&Qs[ra * DP + kb + 4 * lq]);
-            const f32x4 kb4 = *reinterpret_cast<const f32x4 *>(&Ks[(16 * j + lr) * DP + kb + 4 * lq]);
+        for (int j = 0; j < NP; ++j) qk[j] = z4;
+        f32x4 qa[2], kb4[2][NP];
+        auto ld = [&](int u, int kb) {
+            qa[u] = row4(Qs, DP, ra, kb);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) qk = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[m], kb4[m], qk, 0, 0, 0);
+            for (int j = 0; j < NP; ++j) kb4[u][j] = row4(Ks, DP, 16 * j + lr, kb);
+        };
+        ld(0, 0);
+#pragma unroll
+        for (int i = 0; i < KD; ++i) {
+            const int u = i & 1;
+            if (i + 1 < KD) ld(u ^ 1, 16 * (i + 1));
+            fence();
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < NP; ++j) qk[j] = mfma(qa[u][m], kb4[u][j][m], qk[j]);
+            fence();
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = R0 + 4 * lq + r, s = 16 * j + lr;
-            const float gam = dexp2(g[t], g[min(s, t)]);
-            X1[t * CPp + s] = (s <= t && t < n) ? ap[j][r] * gam : 0.f;
-            X2[t * CPp + s] = at[j][r];
-            X3[t * CPp + s] = qk[r];
-        }
+        for (int j = 0; j < NP; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = R0 + 4 * lq + r, s = 16 * j + lr;
+                const float gam = dexp2(g[t], g[min(s, t)]);
+                X1[t * CQ + s] = (s <= t && t < n) ? ap[j][r] * gam : 0.f;
+                X2[t * CQ + s] = at[j][r];
+                X3[t * CQ + s] = qk[j][r];
+            }
     }
     __syncthreads();
-    // (b) dQ += (dP o Gam) K ; dK += (dP o Gam)^T Q ; X = dP o P = X1 o QK^T into Ps
+    // (b) dQ += (dP o Gam) K ; dK += (dP o Gam)^T Q ; X = dP o P = X1 o QK^T into Pt
     //     (P is no longer needed) ; dbeta from Tm = N diag(beta): sum_s dTm_st N_st
-#pragma unroll 4
-    for (int k0 = 0; k0 < BC; k0 += 4) {
-        const int kk = k0 + lq;
-        const float x = X1[ra * CPp + kk], xt = X1[kk * CPp + ra];
+    {
+        // steps (k block, tile j); the operands of step i + 1 load during step i
+        f32x4 xa[2], xt[2], kv[2], qv[2];
+        auto ld = [&](int u, int i) {
+            const int kb = 16 * (i / NJ), j = i % NJ;
+            if (j == 0) {
+                xa[(i / NJ) & 1] = row4(X1, CQ, ra, kb);
+                xt[(i / NJ) & 1] = col4(X1, CQ, ra, kb);
+            }
+            kv[u] = col4(Ks, DP, 16 * j + lr, kb);
+            qv[u] = col4(Qs, DP, 16 * j + lr, kb);
+        };
+        ld(0, 0);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            aq[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, Ks[kk * DP + 16 * j + lr], aq[j], 0, 0, 0);
-            ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt, Qs[kk * DP + 16 * j + lr], ak[j], 0, 0, 0);
+        for (int i = 0; i < KC * NJ; ++i) {
+            const int u = i & 1, w = (i / NJ) & 1, j = i % NJ;
+            if (i + 1 < KC * NJ) ld(u ^ 1, i + 1);
+            fence();
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                aq[j] = mfma(xa[w][m], kv[u][m], aq[j]);
+                ak[j] = mfma(xt[w][m], qv[u][m], ak[j]);
+            }
+            fence();
         }
     }
     for (int idx = tid; idx < BC * BC; idx += BNT) {
         const int t = idx / BC, s = idx % BC;
-        Ps[t * CPp + s] = X1[t * CPp + s] * X3[t * CPp + s];
+        Pt[t * CQ + s] = X1[t * CQ + s] * X3[t * CQ + s];
     }
+    // dbeta of token t = lane: wave w sums s = w (mod 4); the four are added at the end
+    const int wv = tid >> 6;
     float dbt = 0.f;
-    if (tid < BC) {
-        const int t = tid;
-        for (int s = 0; s < BC; ++s) dbt = fmaf(X2[s * CPp + t], Ns[s * CPp + t], dbt);
-    }
+#pragma unroll 4
+    for (int s = wv; s < BC; s += 4) dbt = fmaf(X2[s * CQ + lane], Ns[s * CQ + lane], dbt);
     __syncthreads();
     // (c) T1 = N^T dTm diag(beta) into X1 ; X3 = K K^T
+    {
+        f32x4 a[NP], kk4[NP];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f}, kk4 = a;
-#pragma unroll 4
-        for (int k0 = 0; k0 < BC; k0 += 4)
-            a = __builtin_amdgcn_mfma_f32_16x16x4f32(Ns[(k0 + lq) * CPp + ra], X2[(k0 + lq) * CPp + 16 * j + lr], a,
-                                                    0, 0, 0);
-#pragma unroll 4
-        for (int kb = 0; kb < D; kb += 16) {
-            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&Ks[ra * DP + kb + 4 * lq]);
-            const f32x4 kb4 = *reinterpret_cast<const f32x4 *>(&Ks[(16 * j + lr) * DP + kb + 4 * lq]);
+        for (int j = 0; j < NP; ++j) a[j] = kk4[j] = z4;
+        f32x4 na[2], xb[2][NP];
+        auto ld = [&](int u, int kb) {
+            na[u] = col4(Ns, CQ, ra, kb);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) kk4 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], kb4[m], kk4, 0, 0, 0);
+            for (int j = 0; j < NP; ++j) xb[u][j] = col4(X2, CQ, 16 * j + lr, kb);
+        };
+        ld(0, 0);
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const int u = i & 1;
+            if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
+            fence();
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < NP; ++j) a[j] = mfma(na[u][m], xb[u][j][m], a[j]);
+            fence();
+        }
+        f32x4 ka[2], kb4[2][NP];
+        auto ldk = [&](int u, int kb) {
+            ka[u] = row4(Ks, DP, ra, kb);
+#pragma unroll
+            for (int j = 0; j < NP; ++j) kb4[u][j] = row4(Ks, DP, 16 * j + lr, kb);
+        };
+        ldk(0, 0);
+#pragma unroll
+        for (int i = 0; i < KD; ++i) {
+            const int u = i & 1;
+            if (i + 1 < KD) ldk(u ^ 1, 16 * (i + 1));
+            fence();
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < NP; ++j) kk4[j] = mfma(ka[u][m], kb4[u][j][m], kk4[j]);
+            fence();
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = R0 + 4 * lq + r, s = 16 * j + lr;
-            X1[t * CPp + s] = a[r] * bt[s];
-            X3[t * CPp + s] = kk4[r];
-        }
+        for (int j = 0; j < NP; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = R0 + 4 * lq + r, s = 16 * j + lr;
+                X1[t * CQ + s] = a[j][r] * bt[s];
+                X3[t * CQ + s] = kk4[j][r];
+            }
     }
     __syncthreads();
     // (d) dA = -T1 N^T, strict lower part, into X2
+    {
+        f32x4 a[NP];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int k0 = 0; k0 < BC; k0 += 4)
-            a = __builtin_amdgcn_mfma_f32_16x16x4f32(X1[ra * CPp + k0 + lq], Ns[(16 * j + lr) * CPp + k0 + lq], a, 0,
-                                                    0, 0);
+        for (int j = 0; j < NP; ++j) a[j] = z4;
+        f32x4 xa[2], nb[2][NP];
+        auto ld = [&](int u, int kb) {
+            xa[u] = row4(X1, CQ, ra, kb);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = R0 + 4 * lq + r, s = 16 * j + lr;
-            X2[t * CPp + s] = s < t ? -a[r] : 0.f;
+            for (int j = 0; j < NP; ++j) nb[u][j] = row4(Ns, CQ, 16 * j + lr, kb);
+        };
+        ld(0, 0);
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const int u = i & 1;
+            if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
+            fence();
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < NP; ++j) a[j] = mfma(xa[u][m], nb[u][j][m], a[j]);
+            fence();
         }
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = R0 + 4 * lq + r, s = 16 * j + lr;
+                X2[t * CQ + s] = s < t ? -a[j][r] : 0.f;
+            }
     }
     __syncthreads();
-    // (e) E = dA beta_t Gam into X1 ; X += dA o A (A = beta_t K K^T Gam) ;
-    //     dbeta from A: sum_s dA_ts (k_t . k_s) Gam_ts
+    // (e) E = dA beta_t Gam (strict lower); X1 = E + E^T ; X += dA o A
+    //     (A = beta_t K K^T Gam) ; dbeta from A: sum_s dA_ts (k_t . k_s) Gam_ts
     for (int idx = tid; idx < BC * BC; idx += BNT) {
         const int t = idx / BC, s = idx % BC;
         const float gts = s < t ? dexp2(g[t], g[s]) : 0.f;
-        const float kg = X3[t * CPp + s] * gts;
-        X1[t * CPp + s] = X2[t * CPp + s] * bt[t] * gts;
-        Ps[t * CPp + s] = fmaf(X2[t * CPp + s], bt[t] * kg, Ps[t * CPp + s]);
+        const float kg = X3[t * CQ + s] * gts;
+        const float e = X2[t * CQ + s] * bt[t] * gts;
+        if (s < t) X1[s * CQ + t] = e;
+        if (s <= t) X1[t * CQ + s] = e;
+        Pt[t * CQ + s] = fmaf(X2[t * CQ + s], bt[t] * kg, Pt[t * CQ + s]);
     }
-    if (tid < BC) {
-        const int t = tid;
-        for (int s = 0; s < t; ++s) dbt = fmaf(X2[t * CPp + s], X3[t * CPp + s] * dexp2(g[t], g[s]), dbt);
-    }
+    for (int s = wv; s < lane; s += 4) dbt = fmaf(X2[lane * CQ + s], X3[lane * CQ + s] * dexp2(g[lane], g[s]), dbt);
     __syncthreads();
-    // (f) dK += E K + E^T K
-#pragma unroll 4
-    for (int k0 = 0; k0 < BC; k0 += 4) {
-        const int kk = k0 + lq;
-        const float x = X1[ra * CPp + kk], xt = X1[kk * CPp + ra];
+    // (f) dK += (E + E^T) K
+    {
+        f32x4 xa[2], kv[2];
+        auto ld = [&](int u, int i) {
+            const int kb = 16 * (i / NJ), j = i % NJ;
+            if (j == 0) xa[(i / NJ) & 1] = row4(X1, CQ, ra, kb);
+            kv[u] = col4(Ks, DP, 16 * j + lr, kb);
+        };
+        ld(0, 0);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const float kb = Ks[kk * DP + 16 * j + lr];
-            ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, kb, ak[j], 0, 0, 0);
-            ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt, kb, ak[j], 0, 0, 0);
+        for (int i = 0; i < KC * NJ; ++i) {
+            const int u = i & 1, w = (i / NJ) & 1, j = i % NJ;
+            if (i + 1 < KC * NJ) ld(u ^ 1, i + 1);
+            fence();
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ak[j] = mfma(xa[w][m], kv[u][m], ak[j]);
+            fence();
         }
     }
 #pragma unroll
@@ -880,12 +1100,14 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 dk[(row0 + (size_t)t * H) * D + 16 * j + lr] = ak[j][r];
             }
     }
-    if (lr == 0) {   // each accumulator row belongs to one lane group
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            gq[R0 + 4 * lq + r] = gqr[r];
-            gk[R0 + 4 * lq + r] = gkr[r];
-            gd[R0 + 4 * lq + r] = gdr[r];
+    for (int r = 0; r < 4; ++r) {   // gamma <dO, QS>, -gamma <dR, KS>, (gamma_C/gamma) <U, KdS>
+        const int t = R0 + 4 * lq + r;
+        const float x1 = row16_sum(gqr[r]), x2 = row16_sum(gkr[r]), x3 = row16_sum(gdr[r]);
+        if (lr == 0) {
+            gq[t] = er[r] * x1;
+            gk[t] = -er[r] * x2;
+            gd[t] = ecr[r] * x3;
         }
     }
     // gate (wave 0, thread j = token j of the chunk).  The pairs i < j <= t of X
@@ -895,11 +1117,12 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         float acc = 0.f;
 #pragma unroll 8
         for (int t = BC - 1; t >= 0; --t) {
-            acc += Ps[t * CPp + tid];
-            Ps[t * CPp + tid] = acc;
+            acc += Pt[t * CQ + tid];
+            Pt[t * CQ + tid] = acc;
         }
     }
     red[tid] = sdot;
+    redb[tid] = dbt;
     __syncthreads();
     if (tid < 64) {
         float x = red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192];
@@ -922,10 +1145,10 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         pre -= j < n ? gd[j] : 0.f;
         float cross = 0.f;
 #pragma unroll 8
-        for (int i = 0; i < BC; ++i) cross += i < j ? Ps[j * CPp + i] : 0.f;
+        for (int i = 0; i < BC; ++i) cross += i < j ? Pt[j * CQ + i] : 0.f;
         if (j < n) {
             dlog_alpha[row0 + (size_t)j * H] = suf + pre + cross + dexp2(gC, 0.0) * x;
-            dbeta[row0 + (size_t)j * H] = dbt;
+            dbeta[row0 + (size_t)j * H] = (redb[j] + redb[j + 64]) + (redb[j + 128] + redb[j + 192]);
         }
     }
 }
