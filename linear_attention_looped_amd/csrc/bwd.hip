@@ -338,17 +338,69 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
+// fp32 matrix-core helpers of the chunk-state kernels.  A contraction runs in
+// 16-wide k blocks: in product m of a block, lane l reads A(row l % 16,
+// k = k0 + 4 (l / 16) + m) and B(k = k0 + 4 (l / 16) + m, column l % 16).
+// krow4 reads the four k values of a row that is contiguous in k (one 16-byte
+// read), kcol4 those of a column (rows 4 apart: with a row pitch of 4 (mod 16)
+// words the four lane groups fall on disjoint banks).
+__device__ __forceinline__ f32x4 krow4(const float *m, int pitch, int r, int k0, int lq) {
+    return *reinterpret_cast<const f32x4 *>(&m[r * pitch + k0 + 4 * lq]);
+}
+__device__ __forceinline__ f32x4 kcol4(const float *m, int pitch, int col, int k0, int lq) {
+    const float *p = &m[(k0 + 4 * lq) * pitch + col];
+    return f32x4{p[0], p[pitch], p[2 * pitch], p[3 * pitch]};
+}
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+// A k loop of NK blocks, software-pipelined over two register buffers:
+// ld(buf, i) issues block i's operand loads, mm(buf, i) runs its products.
+// Block i + 1's loads are issued before block i's products (the scheduling
+// barriers keep the compiler from sinking them to their first use).
+template <int NK, class LD, class MM>
+__device__ __forceinline__ void kpipe(LD &&ld, MM &&mm) {
+    ld(0, 0);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        if (i + 1 < NK) ld((i + 1) & 1, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(i & 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+// D x BV fp32 state block: global (row pitch D, columns c0 ..) <-> LDS (pitch VP)
+template <int D, int BV, int VP>
+__device__ __forceinline__ void state_to_lds(float *dst, const float *src, int c0) {
+    for (int idx = threadIdx.x; idx < D * BV / 4; idx += BNT) {
+        const int r = idx / (BV / 4), cc = 4 * (idx % (BV / 4));
+        *reinterpret_cast<f32x4 *>(&dst[r * VP + cc]) =
+            src ? *reinterpret_cast<const f32x4 *>(&src[(size_t)r * D + c0 + cc]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+template <int D, int BV, int VP>
+__device__ __forceinline__ void state_from_lds(float *dst, const float *src, int c0) {
+    for (int idx = threadIdx.x; idx < D * BV / 4; idx += BNT) {
+        const int r = idx / (BV / 4), cc = 4 * (idx % (BV / 4));
+        *reinterpret_cast<f32x4 *>(&dst[(size_t)r * D + c0 + cc]) = *reinterpret_cast<const f32x4 *>(&src[r * VP + cc]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // The state entering every chunk, per 32-column block of the value dimension.
+// Row pitches: D + 4 (K), 36 (32-column blocks), C + 4 (N).
 template <int D, typename TI>
 __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ k, const TI *__restrict__ v,
                                                          const float *__restrict__ beta,
                                                          const float *__restrict__ state_in,
                                                          const float *__restrict__ gnp, float *__restrict__ sws,
                                                          int L, int H, int NC) {
-    constexpr int BV = 32, DP = D + 1, VP = BV + 1;
-    __shared__ float Ss[D * VP], Ks[BC * DP], Vs[BC * VP], Ns[BC * CPp], Rs[BC * VP], Us[BC * VP], bt[BC];
+    constexpr int BV = 32, DP = D + 4, VP = BV + 4, CQ = BC + 4;
+    constexpr int NB = D / BV, KD = D / 16, KC = BC / 16;
+    __shared__ __attribute__((aligned(16))) float Ss[D * VP], Ks[BC * DP], Vs[BC * VP], Ns[BC * CQ], Rs[BC * VP],
+        Us[BC * VP];
+    __shared__ float bt[BC];
     __shared__ double g[BC];
-    constexpr int NB = D / BV;
     // matrix-core roles (fp32 16 x 16 x 4 products): wave w owns token rows
     // 16w .. 16w + 15 of the C x 32 products and state rows SR0 .. SR0 + 16 NR - 1
     constexpr int NR = D / 64;
@@ -360,10 +412,8 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
     const size_t unit = blockIdx.x / NB;
     const int h = (int)(unit % H), b = (int)(unit / H);
     const size_t tok = (size_t)H * D;
-    for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
-        const int r = idx / BV, cc = idx % BV;
-        Ss[r * VP + cc] = state_in ? state_in[(unit * D + r) * D + vb * BV + cc] : 0.f;
-    }
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    state_to_lds<D, BV, VP>(Ss, state_in ? state_in + unit * D * D : nullptr, vb * BV);
     // The loads of chunk c + 1 are issued once chunk c's inputs are in LDS and
     // land while chunk c computes.
     Rows<D, TI> rk;
@@ -388,14 +438,10 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
         const int t0 = c * BC, n = min(BC, L - t0);
         __syncthreads();
         // the state entering chunk c
-        float *so = sws + (unit * NC + c) * (size_t)D * D;
-        for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
-            const int r = idx / BV, cc = idx % BV;
-            so[r * D + vb * BV + cc] = Ss[r * VP + cc];
-        }
+        state_from_lds<D, BV, VP>(sws + (unit * NC + c) * (size_t)D * D, Ss, vb * BV);
         rk.put(Ks, DP);
         rv.put(Vs, VP);
-        nm.put(Ns);
+        nm.put(Ns, CQ);
         if (threadIdx.x < BC) {
             g[threadIdx.x] = gv;
             bt[threadIdx.x] = bv;
@@ -403,61 +449,77 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
         if (c + 1 < NC) fetch(c + 1);
         __syncthreads();
         const double gC = g[n - 1];
-        {   // R' = diag(beta) (V - diag(gamma) K S)
-            f32x4 p[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
-#pragma unroll 8
-            for (int k0 = 0; k0 < D; k0 += 4) {   // two partial sums per tile (even, odd k-steps)
-                const int h2 = (k0 >> 2) & 1;
-                const float ka = Ks[ra * DP + k0 + lq];
+        float er[4], ecr[4], br[4];   // gamma, gamma_C / gamma, beta of rows R0 + 4 (lane / 16) + r
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    p[h2][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, Ss[(k0 + lq) * VP + 16 * j + lr], p[h2][j], 0, 0, 0);
-            }
-            const f32x4 a[2] = {p[0][0] + p[1][0], p[0][1] + p[1][1]};
+        for (int r = 0; r < 4; ++r) {
+            const int t = R0 + 4 * lq + r;
+            er[r] = dexp2(g[t], 0.0);
+            ecr[r] = dexp2(gC, g[t]);
+            br[r] = bt[t];
+        }
+        {   // R' = diag(beta) (V - diag(gamma) K S); two partial sums per tile (m even, odd)
+            f32x4 p[2][2] = {{z4, z4}, {z4, z4}}, ka[2], sb[2][2];
+            kpipe<KD>(
+                [&](int u, int i) {
+                    ka[u] = krow4(Ks, DP, ra, 16 * i, lq);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) sb[u][j] = kcol4(Ss, VP, 16 * j + lr, 16 * i, lq);
+                },
+                [&](int u, int) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) p[m & 1][j] = mfma4(ka[u][m], sb[u][j][m], p[m & 1][j]);
+                });
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = R0 + 4 * lq + r, o = t * VP + 16 * j + lr;
-                    Rs[o] = bt[t] * (Vs[o] - dexp2(g[t], 0.0) * a[j][r]);
+                    const int o = (R0 + 4 * lq + r) * VP + 16 * j + lr;
+                    Rs[o] = br[r] * (Vs[o] - er[r] * (p[0][j][r] + p[1][j][r]));
                 }
         }
         __syncthreads();
         {   // U' = diag(gamma_C / gamma) N R'
-            f32x4 p[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+            f32x4 p[2][2] = {{z4, z4}, {z4, z4}}, na[2], rb[2][2];
+            kpipe<KC>(
+                [&](int u, int i) {
+                    na[u] = krow4(Ns, CQ, ra, 16 * i, lq);
 #pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 4) {   // two partial sums per tile
-                const int h2 = (k0 >> 2) & 1;
-                const float na = Ns[ra * CPp + k0 + lq];
+                    for (int j = 0; j < 2; ++j) rb[u][j] = kcol4(Rs, VP, 16 * j + lr, 16 * i, lq);
+                },
+                [&](int u, int) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    p[h2][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(na, Rs[(k0 + lq) * VP + 16 * j + lr], p[h2][j], 0, 0, 0);
-            }
-            const f32x4 a[2] = {p[0][0] + p[1][0], p[0][1] + p[1][1]};
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) p[m & 1][j] = mfma4(na[u][m], rb[u][j][m], p[m & 1][j]);
+                });
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = R0 + 4 * lq + r;
-                    Us[t * VP + 16 * j + lr] = dexp2(gC, g[t]) * a[j][r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    Us[(R0 + 4 * lq + r) * VP + 16 * j + lr] = ecr[r] * (p[0][j][r] + p[1][j][r]);
         }
         __syncthreads();
         {   // S = gamma_C S + K^T U'  (wave w: state rows 16 (w NR + x) .., both column tiles)
-            f32x4 a[NR][2];
+            f32x4 a[NR][2], kt[2][NR], ub[2][2];
 #pragma unroll
-            for (int x = 0; x < NR; ++x) a[x][0] = a[x][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int k0 = 0; k0 < BC; k0 += 4) {
-                const int kk = k0 + lq;
-                const float u0 = Us[kk * VP + lr], u1 = Us[kk * VP + 16 + lr];
+            for (int x = 0; x < NR; ++x) a[x][0] = a[x][1] = z4;
+            kpipe<KC>(
+                [&](int u, int i) {
 #pragma unroll
-                for (int x = 0; x < NR; ++x) {
-                    const float kt = Ks[kk * DP + SR0 + 16 * x + lr];
-                    a[x][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt, u0, a[x][0], 0, 0, 0);
-                    a[x][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt, u1, a[x][1], 0, 0, 0);
-                }
-            }
+                    for (int x = 0; x < NR; ++x) kt[u][x] = kcol4(Ks, DP, SR0 + 16 * x + lr, 16 * i, lq);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) ub[u][j] = kcol4(Us, VP, 16 * j + lr, 16 * i, lq);
+                },
+                [&](int u, int) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int x = 0; x < NR; ++x)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) a[x][j] = mfma4(kt[u][x][m], ub[u][j][m], a[x][j]);
+                });
             const float gam = dexp2(gC, 0.0);
 #pragma unroll
             for (int x = 0; x < NR; ++x)
@@ -473,19 +535,21 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Chunks in reverse: the cotangent of the state leaving every chunk (stored) and
-// finally that of S_0.
+// dS' entering every chunk from the right (the cotangent of the state leaving
+// it), per 32-column block, chunks in reverse; the final one is d state_in.
+// Pitches as in the chunk-state kernel; P is held transposed (read as P^T).
 template <int D, typename TI, typename TO>
 __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                          const TO *__restrict__ dout, const float *__restrict__ beta,
                                                          const float *__restrict__ dstate_out,
                                                          const float *__restrict__ gnp, float *__restrict__ dsws,
                                                          float *__restrict__ dstate_in, int L, int H, int NC) {
-    constexpr int BV = 32, DP = D + 1, VP = BV + 1;
-    __shared__ float dS[D * VP], Ks[BC * DP], Qs[BC * DP], dOs[BC * VP], Ns[BC * CPp], Ps[BC * CPp], dUs[BC * VP],
-        dRs[BC * VP], bt[BC];
+    constexpr int BV = 32, DP = D + 4, VP = BV + 4, CQ = BC + 4;
+    constexpr int NB = D / BV, KD = D / 16, KC = BC / 16;
+    __shared__ __attribute__((aligned(16))) float dS[D * VP], Ks[BC * DP], Qs[BC * DP], dOs[BC * VP], Ns[BC * CQ],
+        Pt[BC * CQ], dUs[BC * VP], dRs[BC * VP];
+    __shared__ float bt[BC];
     __shared__ double g[BC];
-    constexpr int NB = D / BV;
     // matrix-core roles as in the chunk-state kernel
     constexpr int NR = D / 64;
     static_assert(BNT == 256 && BC == 64 && BV == 32, "four waves, two 16-column tiles");
@@ -496,10 +560,8 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
     const size_t unit = blockIdx.x / NB;
     const int h = (int)(unit % H), b = (int)(unit / H);
     const size_t tok = (size_t)H * D;
-    for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
-        const int r = idx / BV, cc = idx % BV;
-        dS[r * VP + cc] = dstate_out ? dstate_out[(unit * D + r) * D + vb * BV + cc] : 0.f;
-    }
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    state_to_lds<D, BV, VP>(dS, dstate_out ? dstate_out + unit * D * D : nullptr, vb * BV);
     // The loads of chunk c - 1 are issued once chunk c's inputs are in LDS and
     // land while chunk c computes.
     Rows<D, TI> rk, rq;
@@ -525,16 +587,12 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
     for (int c = NC - 1; c >= 0; --c) {
         const int t0 = c * BC, n = min(BC, L - t0);
         __syncthreads();
-        float *dso = dsws + (unit * NC + c) * (size_t)D * D;
-        for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
-            const int r = idx / BV, cc = idx % BV;
-            dso[r * D + vb * BV + cc] = dS[r * VP + cc];
-        }
+        state_from_lds<D, BV, VP>(dsws + (unit * NC + c) * (size_t)D * D, dS, vb * BV);
         rk.put(Ks, DP);
         rq.put(Qs, DP);
         ro.put(dOs, VP);
-        nm.put(Ns);
-        pm.put(Ps);
+        nm.put(Ns, CQ);
+        pm.put_t(Pt, CQ);
         if (threadIdx.x < BC) {
             g[threadIdx.x] = gv;
             bt[threadIdx.x] = bv;
@@ -542,81 +600,102 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
         if (c > 0) fetch(c - 1);
         __syncthreads();
         const double gC = g[n - 1];
+        float er[4], ecr[4], br[4];   // gamma, gamma_C / gamma, beta of rows R0 + 4 (lane / 16) + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = R0 + 4 * lq + r;
+            er[r] = dexp2(g[t], 0.0);
+            ecr[r] = dexp2(gC, g[t]);
+            br[r] = bt[t];
+        }
         {   // dU = P^T dO + diag(gamma_C / gamma) K dS'
-            // two partial sums per tile and product (even, odd k-steps)
-            f32x4 a1[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, a2[2] = {a1[0], a1[0]};
-            f32x4 b1[2] = {a1[0], a1[0]}, b2[2] = {a1[0], a1[0]};
+            f32x4 a1[2][2] = {{z4, z4}, {z4, z4}}, a2[2][2] = {{z4, z4}, {z4, z4}};
+            f32x4 pa[2], ob[2][2];
+            kpipe<KC>(
+                [&](int u, int i) {
+                    pa[u] = krow4(Pt, CQ, ra, 16 * i, lq);
 #pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 8) {
-                const float pa = Ps[(k0 + lq) * CPp + ra], pb = Ps[(k0 + 4 + lq) * CPp + ra];
+                    for (int j = 0; j < 2; ++j) ob[u][j] = kcol4(dOs, VP, 16 * j + lr, 16 * i, lq);
+                },
+                [&](int u, int) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    a1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, dOs[(k0 + lq) * VP + 16 * j + lr], a1[j], 0, 0, 0);
-                    b1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pb, dOs[(k0 + 4 + lq) * VP + 16 * j + lr], b1[j], 0, 0, 0);
-                }
-            }
-#pragma unroll 4
-            for (int k0 = 0; k0 < D; k0 += 8) {
-                const float ka = Ks[ra * DP + k0 + lq], kb = Ks[ra * DP + k0 + 4 + lq];
+                    for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    a2[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, dS[(k0 + lq) * VP + 16 * j + lr], a2[j], 0, 0, 0);
-                    b2[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kb, dS[(k0 + 4 + lq) * VP + 16 * j + lr], b2[j], 0, 0, 0);
-                }
-            }
+                        for (int j = 0; j < 2; ++j) a1[m & 1][j] = mfma4(pa[u][m], ob[u][j][m], a1[m & 1][j]);
+                });
+            f32x4 ka[2], sb[2][2];
+            kpipe<KD>(
+                [&](int u, int i) {
+                    ka[u] = krow4(Ks, DP, ra, 16 * i, lq);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                a1[j] += b1[j];
-                a2[j] += b2[j];
-            }
+                    for (int j = 0; j < 2; ++j) sb[u][j] = kcol4(dS, VP, 16 * j + lr, 16 * i, lq);
+                },
+                [&](int u, int) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) a2[m & 1][j] = mfma4(ka[u][m], sb[u][j][m], a2[m & 1][j]);
+                });
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = R0 + 4 * lq + r;
-                    dUs[t * VP + 16 * j + lr] = fmaf(dexp2(gC, g[t]), a2[j][r], a1[j][r]);
-                }
+                for (int r = 0; r < 4; ++r)
+                    dUs[(R0 + 4 * lq + r) * VP + 16 * j + lr] =
+                        fmaf(ecr[r], a2[0][j][r] + a2[1][j][r], a1[0][j][r] + a1[1][j][r]);
         }
         __syncthreads();
         {   // dR = diag(beta) N^T dU, kept as diag(gamma) dR for the state update
-            f32x4 p[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+            f32x4 p[2][2] = {{z4, z4}, {z4, z4}}, na[2], ub[2][2];
+            kpipe<KC>(
+                [&](int u, int i) {
+                    na[u] = kcol4(Ns, CQ, ra, 16 * i, lq);
 #pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 4) {   // two partial sums per tile
-                const int h2 = (k0 >> 2) & 1;
-                const float na = Ns[(k0 + lq) * CPp + ra];
+                    for (int j = 0; j < 2; ++j) ub[u][j] = kcol4(dUs, VP, 16 * j + lr, 16 * i, lq);
+                },
+                [&](int u, int) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    p[h2][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(na, dUs[(k0 + lq) * VP + 16 * j + lr], p[h2][j], 0, 0, 0);
-            }
-            const f32x4 a[2] = {p[0][0] + p[1][0], p[0][1] + p[1][1]};
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) p[m & 1][j] = mfma4(na[u][m], ub[u][j][m], p[m & 1][j]);
+                });
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = R0 + 4 * lq + r, o = t * VP + 16 * j + lr;
-                    dRs[o] = dexp2(g[t], 0.0) * bt[t] * a[j][r];
-                    dOs[o] *= dexp2(g[t], 0.0);   // diag(gamma) dO
+                    const int o = (R0 + 4 * lq + r) * VP + 16 * j + lr;
+                    dRs[o] = er[r] * br[r] * (p[0][j][r] + p[1][j][r]);
+                    dOs[o] *= er[r];   // diag(gamma) dO
                 }
         }
         __syncthreads();
         {   // dS = Q^T diag(gamma) dO + gamma_C dS' - K^T diag(gamma) dR  (wave w: state rows SR0 ..)
-            f32x4 a[NR][2];
+            f32x4 a[NR][2], qt[2][NR], kt[2][NR], ob[2][2], rb[2][2];
 #pragma unroll
-            for (int x = 0; x < NR; ++x) a[x][0] = a[x][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int k0 = 0; k0 < BC; k0 += 4) {
-                const int kk = k0 + lq;
-                const float o0 = dOs[kk * VP + lr], o1 = dOs[kk * VP + 16 + lr];
-                const float r0 = -dRs[kk * VP + lr], r1 = -dRs[kk * VP + 16 + lr];
+            for (int x = 0; x < NR; ++x) a[x][0] = a[x][1] = z4;
+            kpipe<KC>(
+                [&](int u, int i) {
 #pragma unroll
-                for (int x = 0; x < NR; ++x) {
-                    const float qt = Qs[kk * DP + SR0 + 16 * x + lr], kt = Ks[kk * DP + SR0 + 16 * x + lr];
-                    a[x][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt, o0, a[x][0], 0, 0, 0);
-                    a[x][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt, o1, a[x][1], 0, 0, 0);
-                    a[x][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt, r0, a[x][0], 0, 0, 0);
-                    a[x][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt, r1, a[x][1], 0, 0, 0);
-                }
-            }
+                    for (int x = 0; x < NR; ++x) {
+                        qt[u][x] = kcol4(Qs, DP, SR0 + 16 * x + lr, 16 * i, lq);
+                        kt[u][x] = kcol4(Ks, DP, SR0 + 16 * x + lr, 16 * i, lq);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        ob[u][j] = kcol4(dOs, VP, 16 * j + lr, 16 * i, lq);
+                        rb[u][j] = -kcol4(dRs, VP, 16 * j + lr, 16 * i, lq);
+                    }
+                },
+                [&](int u, int) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int x = 0; x < NR; ++x)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                a[x][j] = mfma4(qt[u][x][m], ob[u][j][m], a[x][j]);
+                                a[x][j] = mfma4(kt[u][x][m], rb[u][j][m], a[x][j]);
+                            }
+                });
             const float gam = dexp2(gC, 0.0);
 #pragma unroll
             for (int x = 0; x < NR; ++x)
@@ -630,11 +709,7 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
         }
     }
     __syncthreads();
-    if (dstate_in)
-        for (int idx = threadIdx.x; idx < D * BV; idx += BNT) {
-            const int r = idx / BV, cc = idx % BV;
-            dstate_in[(unit * D + r) * D + vb * BV + cc] = dS[r * VP + cc];
-        }
+    if (dstate_in) state_from_lds<D, BV, VP>(dstate_in + unit * D * D, dS, vb * BV);
 }
 
 // ---------------------------------------------------------------------------
