@@ -408,8 +408,11 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
     const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R0 = 16 * wv, ra = R0 + lr, SR0 = 16 * NR * wv;
-    const int vb = blockIdx.x % NB;
-    const size_t unit = blockIdx.x / NB;
+    // the NB column blocks of a (b, h) read the same K, N (and Q, P) rows: give
+    // them one XCD, so that one L2 serves all of them
+    const int bid = xcd_logical(blockIdx.x, gridDim.x);
+    const int vb = bid % NB;
+    const size_t unit = bid / NB;
     const int h = (int)(unit % H), b = (int)(unit / H);
     const size_t tok = (size_t)H * D;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -556,8 +559,11 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
     const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int R0 = 16 * wv, ra = R0 + lr, SR0 = 16 * NR * wv;
-    const int vb = blockIdx.x % NB;
-    const size_t unit = blockIdx.x / NB;
+    // the NB column blocks of a (b, h) read the same K, N (and Q, P) rows: give
+    // them one XCD, so that one L2 serves all of them
+    const int bid = xcd_logical(blockIdx.x, gridDim.x);
+    const int vb = bid % NB;
+    const size_t unit = bid / NB;
     const int h = (int)(unit % H), b = (int)(unit / H);
     const size_t tok = (size_t)H * D;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
