@@ -41,8 +41,10 @@
 //   bwd_dstate_kernel  one per (b, h, 32-column block), chunks in reverse: the
 //                      cotangent of the state leaving every chunk, and dS_0
 //   bwd_grads_kernel   one per (b, h, chunk): dv, dq, dk, dbeta, d(log alpha)
-// Products run on the fp32 matrix cores (v_mfma_f32_16x16x4f32: exact fp32
-// products, fp32 sums) from LDS operands; each wave owns 16-row output tiles.
+// Products run on the matrix cores from LDS operands: the fp32 instruction
+// (v_mfma_f32_16x16x4f32: exact fp32 products, fp32 sums), except K K^T and
+// Q K^T of bf16 inputs, which take the bf16 one (products of bf16 values are
+// exact in fp32; the sums are fp32).  Each wave owns 16-row output tiles.
 // Every load of a chunk is issued before the first of them is used.
 #include "common.h"
 #include "internal.h"
@@ -440,8 +442,6 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
     for (int c = 0; c < NC; ++c) {
         const int t0 = c * BC, n = min(BC, L - t0);
         __syncthreads();
-        // the state entering chunk c
-        state_from_lds<D, BV, VP>(sws + (unit * NC + c) * (size_t)D * D, Ss, vb * BV);
         rk.put(Ks, DP);
         rv.put(Vs, VP);
         nm.put(Ns, CQ);
@@ -449,6 +449,9 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
             g[threadIdx.x] = gv;
             bt[threadIdx.x] = bv;
         }
+        // the state entering chunk c (stored after the puts: their waits then
+        // cover only loads, not these stores)
+        state_from_lds<D, BV, VP>(sws + (unit * NC + c) * (size_t)D * D, Ss, vb * BV);
         if (c + 1 < NC) fetch(c + 1);
         __syncthreads();
         const double gC = g[n - 1];
@@ -593,7 +596,6 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
     for (int c = NC - 1; c >= 0; --c) {
         const int t0 = c * BC, n = min(BC, L - t0);
         __syncthreads();
-        state_from_lds<D, BV, VP>(dsws + (unit * NC + c) * (size_t)D * D, dS, vb * BV);
         rk.put(Ks, DP);
         rq.put(Qs, DP);
         ro.put(dOs, VP);
@@ -603,6 +605,8 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
             g[threadIdx.x] = gv;
             bt[threadIdx.x] = bv;
         }
+        // dS' entering chunk c (stored after the puts, as in the chunk-state kernel)
+        state_from_lds<D, BV, VP>(dsws + (unit * NC + c) * (size_t)D * D, dS, vb * BV);
         if (c > 0) fetch(c - 1);
         __syncthreads();
         const double gC = g[n - 1];
@@ -817,10 +821,10 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         ecr[r] = dexp2(gC, g[t]);
         br[r] = bt[t];
     }
-    // gate row terms <dO, QS>, <dR, KS>, <U, KdS> of this lane's accumulator rows
+    // gate row terms <dR, KS>, <U, KdS> of this lane's accumulator rows
     // t = R0 + 4 (lane / 16) + r: each lane sums its own column's products over
     // the value blocks; the 16 lanes of a row are reduced once at the end
-    float gqr[4] = {0.f, 0.f, 0.f, 0.f}, gkr[4] = {0.f, 0.f, 0.f, 0.f}, gdr[4] = {0.f, 0.f, 0.f, 0.f};
+    float gkr[4] = {0.f, 0.f, 0.f, 0.f}, gdr[4] = {0.f, 0.f, 0.f, 0.f};
 
     // A value block's S and dS' columns (16-byte pieces), V and dO columns: the
     // loads of block vb + 1 are issued once block vb is in LDS and land while it
@@ -857,13 +861,14 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         ro.put(dOb, VP);
         if (vb + 1 < D / BV) fetch(vb + 1);
         __syncthreads();
-        // KS = K S, QS = Q S, KdS = K dS' (C x BV), kept in registers;  R = V - diag(gamma) KS
-        f32x4 ks = z4, qs = z4, kds = z4;
+        // KS = K S, KdS = K dS' (C x BV), kept in registers;  R = V - diag(gamma) KS
+        // (two partial sums each, m even and odd)
+        f32x4 ks, kds;
         {
-            f32x4 ka[2], qa[2], sb[2], sd[2];
+            f32x4 ks2[2] = {z4, z4}, kds2[2] = {z4, z4};
+            f32x4 ka[2], sb[2], sd[2];
             auto ld = [&](int u, int kb) {
                 ka[u] = row4(Ks, DP, ra, kb);
-                qa[u] = row4(Qs, DP, ra, kb);
                 sb[u] = col4(Sb, VP, lr, kb);
                 sd[u] = col4(dSb, VP, lr, kb);
             };
@@ -875,12 +880,13 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 fence();
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    ks = mfma(ka[u][m], sb[u][m], ks);
-                    qs = mfma(qa[u][m], sb[u][m], qs);
-                    kds = mfma(ka[u][m], sd[u][m], kds);
+                    ks2[m & 1] = mfma(ka[u][m], sb[u][m], ks2[m & 1]);
+                    kds2[m & 1] = mfma(ka[u][m], sd[u][m], kds2[m & 1]);
                 }
                 fence();
             }
+            ks = ks2[0] + ks2[1];
+            kds = kds2[0] + kds2[1];
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -947,7 +953,6 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 const float x = br[r] * a1[r];
                 dRb[t * VP + lr] = x;
                 if (t < n) dv[(row0 + (size_t)t * H) * D + vb * BV + lr] = x;
-                gqr[r] = fmaf(dOb[t * VP + lr], qs[r], gqr[r]);
                 gkr[r] = fmaf(x, ks[r], gkr[r]);
                 gdr[r] = fmaf(u4[r], kds[r], gdr[r]);
             }
@@ -980,6 +985,18 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             }
         }
         __syncthreads();
+    }
+
+    // gamma <dO, Q S> of row t is <Q_t, (diag(gamma) dO S^T)_t>, and the second
+    // factor is what dQ holds after the value blocks
+    float gqv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = R0 + 4 * lq + r;
+        float x = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) x = fmaf(Qs[t * DP + 16 * j + lr], aq[j][r], x);
+        gqv[r] = row16_sum(x);
     }
 
     // ---- phase 2: C x C algebra (buffers X1..X3 replace the value-block buffers) ----
@@ -1184,9 +1201,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
 #pragma unroll
     for (int r = 0; r < 4; ++r) {   // gamma <dO, QS>, -gamma <dR, KS>, (gamma_C/gamma) <U, KdS>
         const int t = R0 + 4 * lq + r;
-        const float x1 = row16_sum(gqr[r]), x2 = row16_sum(gkr[r]), x3 = row16_sum(gdr[r]);
+        const float x2 = row16_sum(gkr[r]), x3 = row16_sum(gdr[r]);
         if (lr == 0) {
-            gq[t] = er[r] * x1;
+            gq[t] = gqv[r];
             gk[t] = -er[r] * x2;
             gd[t] = ecr[r] * x3;
         }
