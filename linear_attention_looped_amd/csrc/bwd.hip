@@ -356,6 +356,64 @@ __device__ __forceinline__ f32x4 kcol4(const float *m, int pitch, int col, int k
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
+// The operands of one 16-wide k block in the precision of the inputs.  fp32
+// inputs: the four fp32 values feed four v_mfma_f32_16x16x4f32 (exact
+// products).  bf16 inputs: v_mfma_f32_16x16x16_bf16 takes the same four k
+// values per lane as bf16.  Values known to be bf16 (the widened inputs) go in
+// as they are (EX); others are split into hi = bf16(x) and lo = bf16(x - hi),
+// and a product sums hi*hi + lo*hi + hi*lo (about 16 significant bits of each
+// operand; fp32 sums).
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// bf16(a) in the low half, bf16(b) in the high half (round to nearest even)
+__device__ __forceinline__ unsigned bf16_pair(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+template <bool BF, bool EX>
+struct Op4 {
+    f32x4 f;
+};
+template <>
+struct Op4<true, true> {
+    s16x4 hi;
+};
+template <>
+struct Op4<true, false> {
+    s16x4 hi, lo;
+};
+template <bool BF, bool EX>
+__device__ __forceinline__ Op4<BF, EX> op4(f32x4 x) {
+    Op4<BF, EX> o;
+    if constexpr (!BF) {
+        o.f = x;
+    } else if constexpr (EX) {   // the high halves are the bf16 values
+        const u32x2 h = {__builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u),
+                         __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u)};
+        o.hi = __builtin_bit_cast(s16x4, h);
+    } else {
+        const unsigned h0 = bf16_pair(x[0], x[1]), h1 = bf16_pair(x[2], x[3]);
+        const unsigned l0 = bf16_pair(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xFFFF0000u));
+        const unsigned l1 = bf16_pair(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xFFFF0000u));
+        o.hi = __builtin_bit_cast(s16x4, u32x2{h0, h1});
+        o.lo = __builtin_bit_cast(s16x4, u32x2{l0, l1});
+    }
+    return o;
+}
+// acc += (A block) (B block) for one 16-wide k block
+template <bool BF, bool AE, bool BE>
+__device__ __forceinline__ f32x4 mm4(f32x4 acc, const Op4<BF, AE> &a, const Op4<BF, BE> &b) {
+    if constexpr (!BF) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mfma4(a.f[m], b.f[m], acc);
+    } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+        if constexpr (!AE) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
+        if constexpr (!BE) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
+    }
+    return acc;
+}
 // A k loop of NK blocks, software-pipelined over two register buffers:
 // ld(buf, i) issues block i's operand loads, mm(buf, i) runs its products.
 // Block i + 1's loads are issued before block i's products (the scheduling
@@ -399,6 +457,7 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
                                                          int L, int H, int NC) {
     constexpr int BV = 32, DP = D + 4, VP = BV + 4, CQ = BC + 4;
     constexpr int NB = D / BV, KD = D / 16, KC = BC / 16;
+    constexpr bool BF = sizeof(TI) == 2;   // bf16 inputs: bf16 matrix cores (K exact, the rest split)
     __shared__ __attribute__((aligned(16))) float Ss[D * VP], Ks[BC * DP], Vs[BC * VP], Ns[BC * CQ], Rs[BC * VP],
         Us[BC * VP];
     __shared__ float bt[BC];
@@ -463,7 +522,7 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
             ecr[r] = dexp2(gC, g[t]);
             br[r] = bt[t];
         }
-        {   // R' = diag(beta) (V - diag(gamma) K S); two partial sums per tile (m even, odd)
+        {   // R' = diag(beta) (V - diag(gamma) K S); two partial sums per tile (even, odd k blocks)
             f32x4 p[2][2] = {{z4, z4}, {z4, z4}}, ka[2], sb[2][2];
             kpipe<KD>(
                 [&](int u, int i) {
@@ -471,11 +530,10 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
 #pragma unroll
                     for (int j = 0; j < 2; ++j) sb[u][j] = kcol4(Ss, VP, 16 * j + lr, 16 * i, lq);
                 },
-                [&](int u, int) {
+                [&](int u, int i) {
+                    const auto a = op4<BF, BF>(ka[u]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) p[m & 1][j] = mfma4(ka[u][m], sb[u][j][m], p[m & 1][j]);
+                    for (int j = 0; j < 2; ++j) p[i & 1][j] = mm4(p[i & 1][j], a, op4<BF, false>(sb[u][j]));
                 });
 #pragma unroll
             for (int j = 0; j < 2; ++j)
@@ -494,11 +552,10 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
 #pragma unroll
                     for (int j = 0; j < 2; ++j) rb[u][j] = kcol4(Rs, VP, 16 * j + lr, 16 * i, lq);
                 },
-                [&](int u, int) {
+                [&](int u, int i) {
+                    const auto a = op4<BF, false>(na[u]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) p[m & 1][j] = mfma4(na[u][m], rb[u][j][m], p[m & 1][j]);
+                    for (int j = 0; j < 2; ++j) p[i & 1][j] = mm4(p[i & 1][j], a, op4<BF, false>(rb[u][j]));
                 });
 #pragma unroll
             for (int j = 0; j < 2; ++j)
@@ -519,12 +576,13 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
                     for (int j = 0; j < 2; ++j) ub[u][j] = kcol4(Us, VP, 16 * j + lr, 16 * i, lq);
                 },
                 [&](int u, int) {
+                    const Op4<BF, false> b0 = op4<BF, false>(ub[u][0]), b1 = op4<BF, false>(ub[u][1]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int x = 0; x < NR; ++x)
-#pragma unroll
-                            for (int j = 0; j < 2; ++j) a[x][j] = mfma4(kt[u][x][m], ub[u][j][m], a[x][j]);
+                    for (int x = 0; x < NR; ++x) {
+                        const auto a2 = op4<BF, BF>(kt[u][x]);
+                        a[x][0] = mm4(a[x][0], a2, b0);
+                        a[x][1] = mm4(a[x][1], a2, b1);
+                    }
                 });
             const float gam = dexp2(gC, 0.0);
 #pragma unroll
@@ -552,6 +610,8 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
                                                          float *__restrict__ dstate_in, int L, int H, int NC) {
     constexpr int BV = 32, DP = D + 4, VP = BV + 4, CQ = BC + 4;
     constexpr int NB = D / BV, KD = D / 16, KC = BC / 16;
+    // bf16 inputs: bf16 matrix cores (K, Q exact; dO exact when it is bf16; the rest split)
+    constexpr bool BF = sizeof(TI) == 2, OX = BF && sizeof(TO) == 2;
     __shared__ __attribute__((aligned(16))) float dS[D * VP], Ks[BC * DP], Qs[BC * DP], dOs[BC * VP], Ns[BC * CQ],
         Pt[BC * CQ], dUs[BC * VP], dRs[BC * VP];
     __shared__ float bt[BC];
@@ -627,11 +687,10 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
 #pragma unroll
                     for (int j = 0; j < 2; ++j) ob[u][j] = kcol4(dOs, VP, 16 * j + lr, 16 * i, lq);
                 },
-                [&](int u, int) {
+                [&](int u, int i) {
+                    const auto a = op4<BF, false>(pa[u]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) a1[m & 1][j] = mfma4(pa[u][m], ob[u][j][m], a1[m & 1][j]);
+                    for (int j = 0; j < 2; ++j) a1[i & 1][j] = mm4(a1[i & 1][j], a, op4<BF, OX>(ob[u][j]));
                 });
             f32x4 ka[2], sb[2][2];
             kpipe<KD>(
@@ -640,11 +699,10 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
 #pragma unroll
                     for (int j = 0; j < 2; ++j) sb[u][j] = kcol4(dS, VP, 16 * j + lr, 16 * i, lq);
                 },
-                [&](int u, int) {
+                [&](int u, int i) {
+                    const auto a = op4<BF, BF>(ka[u]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) a2[m & 1][j] = mfma4(ka[u][m], sb[u][j][m], a2[m & 1][j]);
+                    for (int j = 0; j < 2; ++j) a2[i & 1][j] = mm4(a2[i & 1][j], a, op4<BF, false>(sb[u][j]));
                 });
 #pragma unroll
             for (int j = 0; j < 2; ++j)
@@ -662,11 +720,10 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
 #pragma unroll
                     for (int j = 0; j < 2; ++j) ub[u][j] = kcol4(dUs, VP, 16 * j + lr, 16 * i, lq);
                 },
-                [&](int u, int) {
+                [&](int u, int i) {
+                    const auto a = op4<BF, false>(na[u]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) p[m & 1][j] = mfma4(na[u][m], ub[u][j][m], p[m & 1][j]);
+                    for (int j = 0; j < 2; ++j) p[i & 1][j] = mm4(p[i & 1][j], a, op4<BF, false>(ub[u][j]));
                 });
 #pragma unroll
             for (int j = 0; j < 2; ++j)
@@ -696,15 +753,15 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
                     }
                 },
                 [&](int u, int) {
+                    // diag(gamma) dO and dR are not bf16 values
+                    const Op4<BF, false> o0 = op4<BF, false>(ob[u][0]), o1 = op4<BF, false>(ob[u][1]);
+                    const Op4<BF, false> r0 = op4<BF, false>(rb[u][0]), r1 = op4<BF, false>(rb[u][1]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int x = 0; x < NR; ++x)
-#pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                a[x][j] = mfma4(qt[u][x][m], ob[u][j][m], a[x][j]);
-                                a[x][j] = mfma4(kt[u][x][m], rb[u][j][m], a[x][j]);
-                            }
+                    for (int x = 0; x < NR; ++x) {
+                        const auto qx = op4<BF, BF>(qt[u][x]), kx = op4<BF, BF>(kt[u][x]);
+                        a[x][0] = mm4(mm4(a[x][0], qx, o0), kx, r0);
+                        a[x][1] = mm4(mm4(a[x][1], qx, o1), kx, r1);
+                    }
                 });
             const float gam = dexp2(gC, 0.0);
 #pragma unroll
@@ -750,6 +807,8 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     constexpr int BV = 16, DP = D + 4, VP = BV + 4, CQ = BC + 4;
     constexpr int NJ = D / 16, NP = BC / 16;   // 16-column tiles of dQ/dK and of dP/dTm
     constexpr int KD = D / 16, KC = BC / 16;   // 16-wide k blocks over D and over C
+    // bf16 inputs: bf16 matrix cores (K, Q exact; dO exact when it is bf16; the rest split)
+    constexpr bool BF = sizeof(TI) == 2, OX = BF && sizeof(TO) == 2;
     static_assert(BNT == 256 && BC == 64, "four waves of 16 token rows");
     // phase-1 buffers (per value block) and phase-2 buffers (C x C) share one region
     constexpr int P1 = 2 * D * VP + 6 * BC * VP;
@@ -784,7 +843,6 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         const float *p = &m[(k0 + 4 * lq) * pitch + col];
         return f32x4{p[0], p[pitch], p[2 * pitch], p[3 * pitch]};
     };
-    auto mfma = [](float a, float b2, f32x4 acc) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b2, acc, 0, 0, 0); };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
     {
@@ -862,7 +920,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         if (vb + 1 < D / BV) fetch(vb + 1);
         __syncthreads();
         // KS = K S, KdS = K dS' (C x BV), kept in registers;  R = V - diag(gamma) KS
-        // (two partial sums each, m even and odd)
+        // (two partial sums each, even and odd k blocks)
         f32x4 ks, kds;
         {
             f32x4 ks2[2] = {z4, z4}, kds2[2] = {z4, z4};
@@ -878,11 +936,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 const int u = i & 1;
                 if (i + 1 < KD) ld(u ^ 1, 16 * (i + 1));
                 fence();
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    ks2[m & 1] = mfma(ka[u][m], sb[u][m], ks2[m & 1]);
-                    kds2[m & 1] = mfma(ka[u][m], sd[u][m], kds2[m & 1]);
-                }
+                const auto a = op4<BF, BF>(ka[u]);
+                ks2[i & 1] = mm4(ks2[i & 1], a, op4<BF, false>(sb[u]));
+                kds2[i & 1] = mm4(kds2[i & 1], a, op4<BF, false>(sd[u]));
                 fence();
             }
             ks = ks2[0] + ks2[1];
@@ -897,7 +953,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         // U = N diag(beta) R ; dU = P^T dO + diag(gamma_C/gamma) K dS'
         f32x4 u4;   // U, this lane's accumulator rows
         {
-            f32x4 p1[2] = {z4, z4}, p2[2] = {z4, z4};   // two partial sums per product (m even, odd)
+            f32x4 p1[2] = {z4, z4}, p2[2] = {z4, z4};   // two partial sums per product (k block even, odd)
             f32x4 na[2], pa[2], ba[2], rb[2], ob[2];
             auto ld = [&](int u, int kb) {
                 na[u] = row4(Ns, CQ, ra, kb);
@@ -912,11 +968,8 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 const int u = i & 1;
                 if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
                 fence();
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    p1[m & 1] = mfma(na[u][m], ba[u][m] * rb[u][m], p1[m & 1]);
-                    p2[m & 1] = mfma(pa[u][m], ob[u][m], p2[m & 1]);
-                }
+                p1[i & 1] = mm4(p1[i & 1], op4<BF, false>(na[u]), op4<BF, false>(ba[u] * rb[u]));
+                p2[i & 1] = mm4(p2[i & 1], op4<BF, false>(pa[u]), op4<BF, OX>(ob[u]));
                 fence();
             }
             u4 = p1[0] + p1[1];
@@ -942,8 +995,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 const int u = i & 1;
                 if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
                 fence();
-#pragma unroll
-                for (int m = 0; m < 4; ++m) p1[m & 1] = mfma(na[u][m], db[u][m], p1[m & 1]);
+                p1[i & 1] = mm4(p1[i & 1], op4<BF, false>(na[u]), op4<BF, false>(db[u]));
                 fence();
             }
             const f32x4 a1 = p1[0] + p1[1];
@@ -959,40 +1011,37 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         }
         __syncthreads();
         // register accumulations over this value block (k = value column s)
-        //   dQ += diag(gamma) dO S^T ; dK += diag(gamma_C/gamma) U dS'^T - diag(gamma) dR S^T
-        //   dP += dO U^T ; dTm += dU R^T
+        //   dQ += dO S^T (rows scaled by gamma after the last block) ;
+        //   dK += diag(gamma_C/gamma) U dS'^T - diag(gamma) dR S^T ; dP += dO U^T ; dTm += dU R^T
         {
-            const f32x4 o4 = row4(dOb, VP, ra, 0), du4 = row4(dUb, VP, ra, 0);
-            const f32x4 ua4 = row4(Ub, VP, ra, 0), ra4 = row4(dRb, VP, ra, 0);
+            const auto o4 = op4<BF, OX>(row4(dOb, VP, ra, 0));
+            const auto du4 = op4<BF, false>(row4(dUb, VP, ra, 0));
+            const auto ua4 = op4<BF, false>(eca * row4(Ub, VP, ra, 0));
+            const auto ra4 = op4<BF, false>(-ea * row4(dRb, VP, ra, 0));
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const f32x4 sq = row4(Sb, VP, 16 * j + lr, 0), sd = row4(dSb, VP, 16 * j + lr, 0);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    aq[j] = mfma(ea * o4[m], sq[m], aq[j]);
-                    ak[j] = mfma(eca * ua4[m], sd[m], ak[j]);
-                    ak[j] = mfma(-ea * ra4[m], sq[m], ak[j]);
-                }
+                const auto sq = op4<BF, false>(row4(Sb, VP, 16 * j + lr, 0));
+                const auto sd = op4<BF, false>(row4(dSb, VP, 16 * j + lr, 0));
+                aq[j] = mm4(aq[j], o4, sq);
+                ak[j] = mm4(mm4(ak[j], ua4, sd), ra4, sq);
             }
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
-                const f32x4 ub = row4(Ub, VP, 16 * j + lr, 0), rb = row4(Rb, VP, 16 * j + lr, 0);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    ap[j] = mfma(o4[m], ub[m], ap[j]);
-                    at[j] = mfma(du4[m], rb[m], at[j]);
-                }
+                ap[j] = mm4(ap[j], o4, op4<BF, false>(row4(Ub, VP, 16 * j + lr, 0)));
+                at[j] = mm4(at[j], du4, op4<BF, false>(row4(Rb, VP, 16 * j + lr, 0)));
             }
         }
         __syncthreads();
     }
 
     // gamma <dO, Q S> of row t is <Q_t, (diag(gamma) dO S^T)_t>, and the second
-    // factor is what dQ holds after the value blocks
+    // factor is what dQ holds after the value blocks and the row scaling
     float gqv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int t = R0 + 4 * lq + r;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) aq[j][r] *= er[r];
         float x = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) x = fmaf(Qs[t * DP + 16 * j + lr], aq[j][r], x);
@@ -1017,10 +1066,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             const int u = i & 1;
             if (i + 1 < KD) ld(u ^ 1, 16 * (i + 1));
             fence();
+            const auto a = op4<BF, BF>(qa[u]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j = 0; j < NP; ++j) qk[j] = mfma(qa[u][m], kb4[u][j][m], qk[j]);
+            for (int j = 0; j < NP; ++j) qk[j] = mm4(qk[j], a, op4<BF, BF>(kb4[u][j]));
             fence();
         }
 #pragma unroll
@@ -1040,6 +1088,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     {
         // steps (k block, tile j); the operands of step i + 1 load during step i
         f32x4 xa[2], xt[2], kv[2], qv[2];
+        Op4<BF, false> xo, xto;   // the current k block's X1 operands, converted once
         auto ld = [&](int u, int i) {
             const int kb = 16 * (i / NJ), j = i % NJ;
             if (j == 0) {
@@ -1055,11 +1104,12 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             const int u = i & 1, w = (i / NJ) & 1, j = i % NJ;
             if (i + 1 < KC * NJ) ld(u ^ 1, i + 1);
             fence();
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                aq[j] = mfma(xa[w][m], kv[u][m], aq[j]);
-                ak[j] = mfma(xt[w][m], qv[u][m], ak[j]);
+            if (j == 0) {
+                xo = op4<BF, false>(xa[w]);
+                xto = op4<BF, false>(xt[w]);
             }
+            aq[j] = mm4(aq[j], xo, op4<BF, BF>(kv[u]));
+            ak[j] = mm4(ak[j], xto, op4<BF, BF>(qv[u]));
             fence();
         }
     }
@@ -1090,10 +1140,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             const int u = i & 1;
             if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
             fence();
+            const auto a0 = op4<BF, false>(na[u]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j = 0; j < NP; ++j) a[j] = mfma(na[u][m], xb[u][j][m], a[j]);
+            for (int j = 0; j < NP; ++j) a[j] = mm4(a[j], a0, op4<BF, false>(xb[u][j]));
             fence();
         }
         f32x4 ka[2], kb4[2][NP];
@@ -1108,10 +1157,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             const int u = i & 1;
             if (i + 1 < KD) ldk(u ^ 1, 16 * (i + 1));
             fence();
+            const auto a0 = op4<BF, BF>(ka[u]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j = 0; j < NP; ++j) kk4[j] = mfma(ka[u][m], kb4[u][j][m], kk4[j]);
+            for (int j = 0; j < NP; ++j) kk4[j] = mm4(kk4[j], a0, op4<BF, BF>(kb4[u][j]));
             fence();
         }
 #pragma unroll
@@ -1141,10 +1189,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             const int u = i & 1;
             if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
             fence();
+            const auto a0 = op4<BF, false>(xa[u]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int j = 0; j < NP; ++j) a[j] = mfma(xa[u][m], nb[u][j][m], a[j]);
+            for (int j = 0; j < NP; ++j) a[j] = mm4(a[j], a0, op4<BF, false>(nb[u][j]));
             fence();
         }
 #pragma unroll
@@ -1172,6 +1219,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     // (f) dK += (E + E^T) K
     {
         f32x4 xa[2], kv[2];
+        Op4<BF, false> xo;
         auto ld = [&](int u, int i) {
             const int kb = 16 * (i / NJ), j = i % NJ;
             if (j == 0) xa[(i / NJ) & 1] = row4(X1, CQ, ra, kb);
@@ -1183,8 +1231,8 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             const int u = i & 1, w = (i / NJ) & 1, j = i % NJ;
             if (i + 1 < KC * NJ) ld(u ^ 1, i + 1);
             fence();
-#pragma unroll
-            for (int m = 0; m < 4; ++m) ak[j] = mfma(xa[w][m], kv[u][m], ak[j]);
+            if (j == 0) xo = op4<BF, false>(xa[w]);
+            ak[j] = mm4(ak[j], xo, op4<BF, BF>(kv[u]));
             fence();
         }
     }
