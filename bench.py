@@ -423,8 +423,10 @@ def bwd_flops_bytes(B, L, H, d, C=64):
 
 
 def bench_backward(args, torch, lt2, synth, reps=5):
-    """Backward pass of the headline prefill workload (B4 H16 L4096 d128 bf16);
-    its products run on the fp32 matrix cores (157.3 TFLOP/s peak)."""
+    """Backward pass of the headline prefill workload (B4 H16 L4096 d128 bf16).
+    With bf16 inputs its products run on the bf16 matrix cores, the fp32
+    intermediates as hi + lo bf16 pairs (up to three instructions per product),
+    so the algorithmic rate is reported without a peak fraction."""
     sh = synth.CONFIGS[2]["shape"]
     log(f"backward inputs B={sh.B} L={sh.L} H={sh.H} d={sh.dk} bf16")
     x = synth.gdn_inputs(sh, seed=0)
@@ -445,9 +447,9 @@ def bench_backward(args, torch, lt2, synth, reps=5):
     torch.cuda.synchronize()
     ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
     flops, nbytes = bwd_flops_bytes(sh.B, sh.L, sh.H, sh.dk)
-    log(f"backward {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s fp32")
+    log(f"backward {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s (algorithmic)")
     return dict(B=sh.B, L=sh.L, H=sh.H, d=sh.dk, ms=ms, tokens_per_s=sh.B * sh.L / (ms / 1e3),
-                flops=flops, bytes=nbytes, tflops=flops / ms / 1e9, fp32_mfma_frac=flops / ms / 1e9 / 157.3,
+                flops=flops, bytes=nbytes, tflops=flops / ms / 1e9, matrix_path="bf16, fp32 intermediates as hi+lo",
                 gbs=nbytes / ms / 1e6, ws_bytes=ws.numel())
 
 

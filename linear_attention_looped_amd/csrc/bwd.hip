@@ -34,18 +34,20 @@
 // |g| 2^-24; each decay is formed from an fp64 difference and then
 // exponentiated in fp32.
 //
-// Four launches, all fp32 arithmetic apart from those sums (bf16 inputs are
-// widened exactly):
+// Four launches; values are held and summed in fp32 apart from those sums
+// (bf16 inputs are widened exactly):
 //   bwd_prep_kernel    one workgroup per (b, h, chunk): g, N, P into the workspace
 //   bwd_states_kernel  one per (b, h, 32-column block): the state entering every chunk
 //   bwd_dstate_kernel  one per (b, h, 32-column block), chunks in reverse: the
 //                      cotangent of the state leaving every chunk, and dS_0
 //   bwd_grads_kernel   one per (b, h, chunk): dv, dq, dk, dbeta, d(log alpha)
-// Products run on the matrix cores from LDS operands: the fp32 instruction
-// (v_mfma_f32_16x16x4f32: exact fp32 products, fp32 sums), except K K^T and
-// Q K^T of bf16 inputs, which take the bf16 one (products of bf16 values are
-// exact in fp32; the sums are fp32).  Each wave owns 16-row output tiles.
-// Every load of a chunk is issued before the first of them is used.
+// Products run on the matrix cores from LDS operands.  fp32 inputs: the fp32
+// instruction (v_mfma_f32_16x16x4f32: exact fp32 products, fp32 sums).  bf16
+// inputs: the bf16 instructions, the inputs as they are and every fp32
+// intermediate split into hi + lo bf16 halves (about 16 significant bits per
+// operand, fp32 sums; K K^T and Q K^T of the inputs are exact).  Each wave owns
+// 16-row output tiles.  Every load of a chunk is issued before the first of
+// them is used.
 #include "common.h"
 #include "internal.h"
 

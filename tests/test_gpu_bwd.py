@@ -35,8 +35,9 @@ def run_bwd(x, dO, shape, S0=None, dSL=None):
 
 def check(got, ref, tol):
     for n in NAMES:
-        print(f"  {n}:", end="")
-        assert rel_err(got[n], ref[n]) <= tol, n
+        e = rel_err(got[n], ref[n])
+        print(f"  {n}: {e:.2e}", end="")
+        assert e <= tol, n
 
 
 @pytest.mark.parametrize("d", [64, 128])
