@@ -21,11 +21,11 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0")
 
 
-def run_bwd(x, dO, shape, S0=None, dSL=None):
+def run_bwd(x, dO, shape, S0=None, dSL=None, dO_dtype=None):
     qdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
     q, k, v = dev(x["q"], qdt), dev(x["k"], qdt), dev(x["v"], qdt)
     a, b = dev(x["alpha"]), dev(x["beta"])
-    g = lt2.lt2_gdn_backward(q, k, v, a, b, dev(dO, qdt), state_in=None if S0 is None else dev(S0),
+    g = lt2.lt2_gdn_backward(q, k, v, a, b, dev(dO, dO_dtype or qdt), state_in=None if S0 is None else dev(S0),
                              d_state_out=None if dSL is None else dev(dSL))
     torch.cuda.synchronize()
     out = {n: host(g[n]) for n in ("dq", "dk", "dv", "dlog_alpha", "dbeta")}
@@ -74,6 +74,26 @@ def test_backward_bf16():
     got = run_bwd(x, dO, shape)
     ref = oracle.backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO)
     check(got, ref, TOL_BF16)
+
+
+def test_backward_mixed_dtypes():
+    """bf16 q, k, v with an fp32 output cotangent (bf16 matrix cores, dO split
+    into hi + lo), and fp32 q, k, v with a bf16 cotangent (fp32 matrix cores)."""
+    shape = synth.GDNShape(1, 150, 2, 128, 128, "head", 2.0, "bf16")
+    announce("bwd bf16 inputs, fp32 dO")
+    x = synth.gdn_inputs(shape, seed=15)
+    dO = synth.grad_out(shape, seed=15)
+    dO32 = np.random.default_rng(15).standard_normal(dO.shape).astype(np.float32)   # not bf16-valued
+    got = run_bwd(x, dO32, shape, dO_dtype=torch.float32)
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO32)
+    check(got, ref, TOL_BF16)
+    shape32 = synth.GDNShape(1, 150, 2, 64, 64, "head", 2.0, "f32")
+    announce("bwd fp32 inputs, bf16 dO")
+    x = synth.gdn_inputs(shape32, seed=16)
+    dO = torch.from_numpy(synth.grad_out(shape32, seed=16)).to(torch.bfloat16).double().numpy()   # bf16-valued
+    got = run_bwd(x, dO, shape32, dO_dtype=torch.bfloat16)
+    ref = oracle.backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO)
+    check(got, ref, TOL_F32)
 
 
 def test_backward_extreme_gates():
