@@ -837,14 +837,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     const int R0 = 16 * __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ra = R0 + lr;   // this lane's A-operand row
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    // 16-byte row read and column read of a k block (k0 + 4 (lane / 16) + m)
-    auto row4 = [&](const float *m, int pitch, int r, int k0) {
-        return *reinterpret_cast<const f32x4 *>(&m[r * pitch + k0 + 4 * lq]);
-    };
-    auto col4 = [&](const float *m, int pitch, int col, int k0) {
-        const float *p = &m[(k0 + 4 * lq) * pitch + col];
-        return f32x4{p[0], p[pitch], p[2 * pitch], p[3 * pitch]};
-    };
+    // row and column reads of a 16-wide k block (krow4, kcol4)
+    auto row4 = [&](const float *m, int pitch, int r, int k0) { return krow4(m, pitch, r, k0, lq); };
+    auto col4 = [&](const float *m, int pitch, int col, int k0) { return kcol4(m, pitch, col, k0, lq); };
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
     {
