@@ -65,9 +65,10 @@ def test_backward_fp32_no_state():
     check(got, ref, TOL_F32)
 
 
-def test_backward_bf16():
-    shape = synth.GDNShape(2, 333, 2, 128, 128, "head", 2.0, "bf16")
-    announce("bwd bf16")
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_bf16(d):
+    shape = synth.GDNShape(2, 333, 2, d, d, "head", 2.0, "bf16")
+    announce(f"bwd bf16 d={d}")
     x = synth.gdn_inputs(shape, seed=13)
     dO = synth.grad_out(shape, seed=13)
     got = run_bwd(x, dO, shape)
