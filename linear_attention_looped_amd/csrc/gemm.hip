@@ -35,6 +35,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "internal.h"
 
 namespace lt2 {
 
@@ -327,16 +328,22 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 // compiler can tell a DMA into one stage from the fragment reads of another.
 // The accumulators then go to LDS and the epilogue works row by row: four
 // threads per row, 32 columns each, so the per-head L2 norm is a two-step
-// shuffle reduction and every global access is a 16-byte vector.
-constexpr int SBM = 64, SBN = 128, SNS = 5;   // rows, columns, LDS stages
+// shuffle reduction and every global access is a 16-byte vector.  The residual
+// product also has a 32-row form (one accumulator per wave, eight threads per
+// row in the epilogue) for shapes with too few 64-row tiles to fill the GPU.
+constexpr int SBN = 128, SNS = 5;   // columns, LDS stages
 
-template <int EPI, int DH, int KTC>   // KTC: K-tiles known at compile time (0: K at run time)
+// SBM: tile rows (64; 32 for the residual product only); KTC: K-tiles known at
+// compile time (0: K at run time)
+template <int EPI, int DH, int KTC, int SBM = 64>
 __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, int M, int N, int K,
                                                          ProjOut po, ResidOut ro) {
+    static_assert(SBM == 64 || (SBM == 32 && EPI == EPI_RESID), "tile rows");
     constexpr int A_EL = SBM * BK, B_EL = SBN * BK, CP = SBN + 4;
-    // 1 KiB DMA chunks per stage: A 8, B 16; wave w takes A chunks w, w + 4 and B chunks w + 4 j
-    constexpr int DMA_PER_WAVE = 6;
+    constexpr int NA = SBM / 32;   // A chunks per wave, accumulators per wave
+    // 1 KiB DMA chunks per stage: A SBM / 8, B 16; wave w takes A chunks w + 4 j and B chunks w + 4 j
+    constexpr int DMA_PER_WAVE = NA + 4;
     // one array per stage (A tile, then B tile): the compiler tracks only a few
     // distinct LDS-DMA targets, and ten would make every fragment read wait for
     // every DMA in flight
@@ -353,9 +360,9 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
 
     // lane i of a chunk writes bytes 16 i of it: row 8 c + i / 8, physical
     // segment i % 8, holding the logical segment the swizzle maps there
-    int voa[2], vob[4];
+    int voa[NA], vob[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NA; ++j) {
         const int row = 8 * (wave + 4 * j) + (lane >> 3);
         voa[j] = 2 * (row * K + 8 * ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)));
     }
@@ -372,18 +379,20 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
         const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(Ag + k0, abytes - 2 * k0);
         const __amdgpu_buffer_rsrc_t rb = gemm_rsrc(Bg + k0, bbytes - 2 * k0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) gemm_dma16(ra, Ad + 512 * (wave + 4 * j), voa[j]);
+        for (int j = 0; j < NA; ++j) gemm_dma16(ra, Ad + 512 * (wave + 4 * j), voa[j]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) gemm_dma16(rb, Bd + 512 * (wave + 4 * j), vob[j]);
     };
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    f32x16 acc[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) acc[i] = f32x16{};
     auto compute = [&](const uint16_t *As, const uint16_t *Bs) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int seg = 2 * ks + lh;
             const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Bs[swz(32 * wave + l32, seg)]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < NA; ++i) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[swz(32 * i + l32, seg)]);
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
             }
@@ -451,20 +460,22 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
     // accumulators -> LDS: register r of tile i holds row 32 i + 8 (r/4) + 4 lh + r%4,
     // column 32 wave + l32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) Cs[(32 * i + 8 * (r >> 2) + 4 * lh + (r & 3)) * CP + 32 * wave + l32] = acc[i][r];
     __syncthreads();
 
-    // epilogue: thread (row, quarter): row = tid / 4, columns 32 (tid % 4) .. + 31
-    const int row = tid >> 2, q4 = tid & 3;
+    // epilogue: thread (row, part): TPR = 256 / SBM threads per row, each CPT
+    // columns (64 rows: four threads of 32 columns)
+    constexpr int TPR = 256 / SBM, CPT = SBN / TPR;
+    const int row = tid / TPR, q4 = tid % TPR;
     const int m = m0 + row;
-    const int c0 = 32 * q4;
+    const int c0 = CPT * q4;
     const float *cr = Cs + row * CP + c0;
     if constexpr (EPI == EPI_RESID) {
         if (m < M) {
 #pragma unroll
-            for (int j = 0; j < 32; j += 8) {
+            for (int j = 0; j < CPT; j += 8) {
                 const int n = n0 + c0 + j;
                 if (n >= N) break;
                 float *hp = ro.h + (size_t)m * N + n;
@@ -539,7 +550,7 @@ hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, 
     ProjOut po{q, k, v, g, beta, alpha, H, d, norm_qk ? 1 : 0};
     ResidOut ro{nullptr, nullptr};
     if (use_small(M, N)) {
-        const unsigned sg = (unsigned)((M + SBM - 1) / SBM) * (unsigned)((N + SBN - 1) / SBN);
+        const unsigned sg = (unsigned)((M + 63) / 64) * (unsigned)((N + SBN - 1) / SBN);
         if (d == 64)
             hipLaunchKernelGGL((gemm_small_kernel<EPI_PROJ, 64, 0>), dim3(sg), dim3(256), 0, s, X, W, M, N, K, po, ro);
         else
@@ -565,8 +576,12 @@ hipError_t launch_gemm_resid(const uint16_t *O, const uint16_t *W, int M, int N,
     ProjOut po{};
     ResidOut ro{h, xb};
     if (use_small(M, N)) {
-        const unsigned sg = (unsigned)((M + SBM - 1) / SBM) * (unsigned)((N + SBN - 1) / SBN);
-        if (K == 32 * BK)
+        const unsigned sg = (unsigned)((M + 63) / 64) * (unsigned)((N + SBN - 1) / SBN);
+        const unsigned sg32 = (unsigned)((M + 31) / 32) * (unsigned)((N + SBN - 1) / SBN);
+        if (K == 32 * BK && 2 * sg < (unsigned)device_cus())   // few 64-row tiles: 32-row tiles, twice as many
+            hipLaunchKernelGGL((gemm_small_kernel<EPI_RESID, 128, 32, 32>), dim3(sg32), dim3(256), 0, s, O, W, M, N, K,
+                               po, ro);
+        else if (K == 32 * BK)
             hipLaunchKernelGGL((gemm_small_kernel<EPI_RESID, 128, 32>), dim3(sg), dim3(256), 0, s, O, W, M, N, K, po, ro);
         else
             hipLaunchKernelGGL((gemm_small_kernel<EPI_RESID, 128, 0>), dim3(sg), dim3(256), 0, s, O, W, M, N, K, po, ro);

@@ -7,6 +7,18 @@
 
 namespace lt2 {
 
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    }
+    return cus[dev];
+}
+
 struct GdnArgs {
     int B, L, H, dk, dv, chunk;
     int qkv_bf16, out_bf16, channel;

@@ -945,18 +945,6 @@ size_t prefill_head_ws_bytes(int B, int L, int H, int C) {
     return (size_t)B * H * NC * (size_t)(8 * C * C + 12 * C);
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
-    }
-    return cus[dev];
-}
-
 template <int D, int C, int PREC, typename TI, typename TO>
 static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
     constexpr int BV = 32;
