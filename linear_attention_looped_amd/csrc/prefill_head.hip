@@ -29,6 +29,22 @@ namespace lt2 {
 // (hi = bf16(x), lo = bf16(x - hi): the scan feeds them to bf16 matrix cores
 // without converting).  Tm and P are zero above the diagonal.
 // ---------------------------------------------------------------------------
+// One 32-wide k block of a product of two input fragments (eight consecutive
+// elements per lane, the common.h fragment layout).  bf16 inputs on the bf16
+// path go to the matrix core as they are; otherwise through fp32 fragments.
+template <int PREC, typename TI>
+__device__ __forceinline__ void gram_mma(f32x4 &acc, const Raw8<TI> &a, const Raw8<TI> &b) {
+    if constexpr (PREC == PREC_BF16 && sizeof(TI) == 2) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                      0, 0, 0);
+    } else {
+        Frag fa, fb;
+        raw_to_frag(fa, a);
+        raw_to_frag(fb, b);
+        mma<PREC, true, true>(acc, fa, fb);
+    }
+}
+
 template <int DK, int C, int PREC, typename TI>
 __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                         const float *__restrict__ alpha,
@@ -118,12 +134,9 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            Frag fa, fb;
-            raw_to_frag(fa, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * I + lr) * KP + 32 * kb + 8 * lq));
-            raw_to_frag(fb, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq));
-            mma<PREC, true, true>(acc, fa, fb);
-        }
+        for (int kb = 0; kb < DK / 32; ++kb)
+            gram_mma<PREC>(acc, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * I + lr) * KP + 32 * kb + 8 * lq),
+                           *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
@@ -142,11 +155,9 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
         const int arow = 16 * I + lr;
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
-            Frag fa, fb;
-            raw_to_frag(fa, qraw[m][kb]);
-            if (arow >= Lc) zero_frag(fa);
-            raw_to_frag(fb, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq));
-            mma<PREC, true, true>(pacc[m], fa, fb);
+            Raw8<TI> qa = qraw[m][kb];
+            if (arow >= Lc) zero_raw8<TI>(qa);
+            gram_mma<PREC>(pacc[m], qa, *reinterpret_cast<const Raw8<TI> *>(Ks + (16 * J + lr) * KP + 32 * kb + 8 * lq));
         }
     }
     __syncthreads();
