@@ -45,7 +45,8 @@
 // instruction (v_mfma_f32_16x16x4f32: exact fp32 products, fp32 sums).  bf16
 // inputs: the bf16 instructions, the inputs as they are and every fp32
 // intermediate split into hi + lo bf16 halves (about 16 significant bits per
-// operand, fp32 sums; K K^T and Q K^T of the inputs are exact).  Each wave owns
+// operand, fp32 sums; K K^T and Q K^T of the inputs are exact); operands that
+// all waves read (N, P^T, the S and dS' blocks) are stored split.  Each wave owns
 // 16-row output tiles.  Every load of a chunk is issued before the first of
 // them is used.
 #include "common.h"
@@ -130,6 +131,9 @@ struct CCm {
             for (int j = 0; j < 4; ++j) dst[r * pitch + c + j] = __uint_as_float(x[i][j]);
         }
     }
+    // as put and put_t, each value stored as a packed hi/lo word (pack_hilo4)
+    __device__ __forceinline__ void put_packed(float *dst, int pitch) const;
+    __device__ __forceinline__ void put_t_packed(float *dst, int pitch) const;
     // transposed: dst[c * pitch + r] = M[r][c]
     __device__ __forceinline__ void put_t(float *dst, int pitch) const {
 #pragma unroll
@@ -403,6 +407,55 @@ __device__ __forceinline__ Op4<BF, EX> op4(f32x4 x) {
     }
     return o;
 }
+// Operands that several waves read are split once, where they are written to
+// LDS, into one 32-bit word per value: hi in the low half, lo in the high half.
+__device__ __forceinline__ f32x4 pack_hilo4(f32x4 x) {
+    const unsigned h0 = bf16_pair(x[0], x[1]), h1 = bf16_pair(x[2], x[3]);
+    const unsigned l0 = bf16_pair(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xFFFF0000u));
+    const unsigned l1 = bf16_pair(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xFFFF0000u));
+    return f32x4{__uint_as_float(__builtin_amdgcn_perm(l0, h0, 0x05040100u)),
+                 __uint_as_float(__builtin_amdgcn_perm(l0, h0, 0x07060302u)),
+                 __uint_as_float(__builtin_amdgcn_perm(l1, h1, 0x05040100u)),
+                 __uint_as_float(__builtin_amdgcn_perm(l1, h1, 0x07060302u))};
+}
+__device__ __forceinline__ Op4<true, false> op4_packed(f32x4 w) {
+    const unsigned w0 = __float_as_uint(w[0]), w1 = __float_as_uint(w[1]), w2 = __float_as_uint(w[2]),
+                   w3 = __float_as_uint(w[3]);
+    Op4<true, false> o;
+    o.hi = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(w1, w0, 0x05040100u),
+                                           __builtin_amdgcn_perm(w3, w2, 0x05040100u)});
+    o.lo = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(w1, w0, 0x07060302u),
+                                           __builtin_amdgcn_perm(w3, w2, 0x07060302u)});
+    return o;
+}
+__device__ __forceinline__ float unpack_hilo(float w) {   // hi + lo
+    const unsigned u = __float_as_uint(w);
+    return __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
+}
+__device__ __forceinline__ void CCm::put_packed(float *dst, int pitch) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int e = 4 * (threadIdx.x + BNT * i), r = e / BC, c = e % BC;
+        const f32x4 w = pack_hilo4(__builtin_bit_cast(f32x4, x[i]));
+        *reinterpret_cast<f32x4 *>(&dst[r * pitch + c]) = w;
+    }
+}
+__device__ __forceinline__ void CCm::put_t_packed(float *dst, int pitch) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int e = 4 * (threadIdx.x + BNT * i), r = e / BC, c = e % BC;
+        const f32x4 w = pack_hilo4(__builtin_bit_cast(f32x4, x[i]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[(c + j) * pitch + r] = w[j];
+    }
+}
+// an operand block of a stored matrix: packed words (bf16 inputs) or fp32 values
+template <bool BF>
+__device__ __forceinline__ Op4<BF, false> op4_stored(f32x4 x) {
+    if constexpr (BF) return op4_packed(x);
+    else return op4<false, false>(x);
+}
+
 // acc += (A block) (B block) for one 16-wide k block
 template <bool BF, bool AE, bool BE>
 __device__ __forceinline__ f32x4 mm4(f32x4 acc, const Op4<BF, AE> &a, const Op4<BF, BE> &b) {
@@ -851,8 +904,14 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         pm.fetch(gc + G_FLOATS + BC * BC);
         rk.put(Ks, DP);
         rq.put(Qs, DP);
-        nm.put(Ns, CQ);
-        pm.put_t(Pt, CQ);
+        // bf16 inputs: N and P^T as packed hi/lo words (split once for all waves and blocks)
+        if constexpr (BF) {
+            nm.put_packed(Ns, CQ);
+            pm.put_t_packed(Pt, CQ);
+        } else {
+            nm.put(Ns, CQ);
+            pm.put_t(Pt, CQ);
+        }
     }
     if (tid < BC) {
         g[tid] = reinterpret_cast<const double *>(gc)[tid];
@@ -907,8 +966,9 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                              __uint_as_float(xs[i][3])};
             const f32x4 d2 = {__uint_as_float(xd[i][0]), __uint_as_float(xd[i][1]), __uint_as_float(xd[i][2]),
                               __uint_as_float(xd[i][3])};
-            *reinterpret_cast<f32x4 *>(&Sb[r * VP + cc]) = a;
-            *reinterpret_cast<f32x4 *>(&dSb[r * VP + cc]) = d2;
+            // bf16 inputs: S and dS' as packed hi/lo words
+            *reinterpret_cast<f32x4 *>(&Sb[r * VP + cc]) = BF ? pack_hilo4(a) : a;
+            *reinterpret_cast<f32x4 *>(&dSb[r * VP + cc]) = BF ? pack_hilo4(d2) : d2;
 #pragma unroll
             for (int j = 0; j < 4; ++j) sdot = fmaf(a[j], d2[j], sdot);
         }
@@ -934,8 +994,8 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 if (i + 1 < KD) ld(u ^ 1, 16 * (i + 1));
                 fence();
                 const auto a = op4<BF, BF>(ka[u]);
-                ks2[i & 1] = mm4(ks2[i & 1], a, op4<BF, false>(sb[u]));
-                kds2[i & 1] = mm4(kds2[i & 1], a, op4<BF, false>(sd[u]));
+                ks2[i & 1] = mm4(ks2[i & 1], a, op4_stored<BF>(sb[u]));
+                kds2[i & 1] = mm4(kds2[i & 1], a, op4_stored<BF>(sd[u]));
                 fence();
             }
             ks = ks2[0] + ks2[1];
@@ -965,8 +1025,8 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 const int u = i & 1;
                 if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
                 fence();
-                p1[i & 1] = mm4(p1[i & 1], op4<BF, false>(na[u]), op4<BF, false>(ba[u] * rb[u]));
-                p2[i & 1] = mm4(p2[i & 1], op4<BF, false>(pa[u]), op4<BF, OX>(ob[u]));
+                p1[i & 1] = mm4(p1[i & 1], op4_stored<BF>(na[u]), op4<BF, false>(ba[u] * rb[u]));
+                p2[i & 1] = mm4(p2[i & 1], op4_stored<BF>(pa[u]), op4<BF, OX>(ob[u]));
                 fence();
             }
             u4 = p1[0] + p1[1];
@@ -992,7 +1052,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
                 const int u = i & 1;
                 if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
                 fence();
-                p1[i & 1] = mm4(p1[i & 1], op4<BF, false>(na[u]), op4<BF, false>(db[u]));
+                p1[i & 1] = mm4(p1[i & 1], op4_stored<BF>(na[u]), op4<BF, false>(db[u]));
                 fence();
             }
             const f32x4 a1 = p1[0] + p1[1];
@@ -1017,8 +1077,8 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             const auto ra4 = op4<BF, false>(-ea * row4(dRb, VP, ra, 0));
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const auto sq = op4<BF, false>(row4(Sb, VP, 16 * j + lr, 0));
-                const auto sd = op4<BF, false>(row4(dSb, VP, 16 * j + lr, 0));
+                const auto sq = op4_stored<BF>(row4(Sb, VP, 16 * j + lr, 0));
+                const auto sd = op4_stored<BF>(row4(dSb, VP, 16 * j + lr, 0));
                 aq[j] = mm4(aq[j], o4, sq);
                 ak[j] = mm4(mm4(ak[j], ua4, sd), ra4, sq);
             }
@@ -1118,7 +1178,10 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     const int wv = tid >> 6;
     float dbt = 0.f;
 #pragma unroll 4
-    for (int s = wv; s < BC; s += 4) dbt = fmaf(X2[s * CQ + lane], Ns[s * CQ + lane], dbt);
+    for (int s = wv; s < BC; s += 4) {
+        const float nv = BF ? unpack_hilo(Ns[s * CQ + lane]) : Ns[s * CQ + lane];
+        dbt = fmaf(X2[s * CQ + lane], nv, dbt);
+    }
     __syncthreads();
     // (c) T1 = N^T dTm diag(beta) into X1 ; X3 = K K^T
     {
@@ -1137,7 +1200,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             const int u = i & 1;
             if (i + 1 < KC) ld(u ^ 1, 16 * (i + 1));
             fence();
-            const auto a0 = op4<BF, false>(na[u]);
+            const auto a0 = op4_stored<BF>(na[u]);
 #pragma unroll
             for (int j = 0; j < NP; ++j) a[j] = mm4(a[j], a0, op4<BF, false>(xb[u][j]));
             fence();
@@ -1188,7 +1251,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
             fence();
             const auto a0 = op4<BF, false>(xa[u]);
 #pragma unroll
-            for (int j = 0; j < NP; ++j) a[j] = mm4(a[j], a0, op4<BF, false>(nb[u][j]));
+            for (int j = 0; j < NP; ++j) a[j] = mm4(a[j], a0, op4_stored<BF>(nb[u][j]));
             fence();
         }
 #pragma unroll
