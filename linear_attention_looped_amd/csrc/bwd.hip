@@ -45,10 +45,10 @@
 // instruction (v_mfma_f32_16x16x4f32: exact fp32 products, fp32 sums).  bf16
 // inputs: the bf16 instructions, the inputs as they are and every fp32
 // intermediate split into hi + lo bf16 halves (about 16 significant bits per
-// operand, fp32 sums; K K^T and Q K^T of the inputs are exact); operands that
-// all waves read (N, P^T, the S and dS' blocks) are stored split.  Each wave owns
-// 16-row output tiles.  Every load of a chunk is issued before the first of
-// them is used.
+// operand, fp32 sums; K K^T and Q K^T of the inputs are exact).  In the
+// gradients kernel the operands that all waves read (N, P^T, the S and dS'
+// blocks) are stored split.  Each wave owns 16-row output tiles.  Every load
+// of a chunk is issued before the first of them is used.
 #include "common.h"
 #include "internal.h"
 
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// fp32 matrix-core helpers of the chunk-state kernels.  A contraction runs in
-// 16-wide k blocks: in product m of a block, lane l reads A(row l % 16,
+// Matrix-core helpers of the chunk-state and gradients kernels.  A contraction
+// runs in 16-wide k blocks: in product m of a block, lane l reads A(row l % 16,
 // k = k0 + 4 (l / 16) + m) and B(k = k0 + 4 (l / 16) + m, column l % 16).
 // krow4 reads the four k values of a row that is contiguous in k (one 16-byte
 // read), kcol4 those of a column (rows 4 apart: with a row pitch of 4 (mod 16)
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(const TI *__restrict__ 
         Us[BC * VP];
     __shared__ float bt[BC];
     __shared__ double g[BC];
-    // matrix-core roles (fp32 16 x 16 x 4 products): wave w owns token rows
+    // matrix-core roles (16 x 16 output tiles): wave w owns token rows
     // 16w .. 16w + 15 of the C x 32 products and state rows SR0 .. SR0 + 16 NR - 1
     constexpr int NR = D / 64;
     static_assert(BNT == 256 && BC == 64 && BV == 32, "four waves, two 16-column tiles");
@@ -837,8 +837,9 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
 // ---------------------------------------------------------------------------
 // Per-chunk gradients.  The value dimension is walked in blocks of 16 columns;
 // dQ, dK (C x D) and dP, dTm (C x C) accumulate in registers across blocks.
-// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4f32: exact
-// fp32 products, fp32 sums), one 16 x 16 output tile per instruction chain.
+// Every product runs on the matrix cores in the inputs' precision (mm4: fp32
+// instructions, or bf16 ones with split operands), one 16 x 16 output tile per
+// instruction chain.
 // Wave w owns rows 16w .. 16w + 15 (tokens) of every row-partitioned product;
 // in a tile, lane l holds rows 4 (l / 16) + r, r < 4, of column l % 16.  The
 // contraction runs in 16-wide k blocks: in product m of a block, lane l reads
