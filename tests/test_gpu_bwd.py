@@ -96,17 +96,19 @@ def test_backward_mixed_dtypes():
     check(got, ref, TOL_F32)
 
 
-def test_backward_extreme_gates():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_extreme_gates(dtype):
     """alpha near 0 (shift 6: the state forgets every token) and near 1, beta in
-    (0, 1): chunk-relative decays span hundreds of octaves inside a chunk."""
+    (0, 1): chunk-relative decays span hundreds of octaves inside a chunk (bf16:
+    the split-operand matrix-core path over the same range)."""
     for shift in (6.0, -6.0):
-        shape = synth.GDNShape(1, 130, 2, 64, 64, "head", shift, "f32")
-        announce(f"bwd extreme gates shift={shift}")
+        shape = synth.GDNShape(1, 130, 2, 64, 64, "head", shift, dtype)
+        announce(f"bwd extreme gates {dtype} shift={shift}")
         x = synth.gdn_inputs(shape, seed=14)
         dO = synth.grad_out(shape, seed=14)
         got = run_bwd(x, dO, shape)
         ref = oracle.backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO)
-        check(got, ref, TOL_F32)
+        check(got, ref, TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
 def test_backward_full_workload_sampled_units():
