@@ -83,7 +83,7 @@ def prefill_flops_bytes(B, L, H, d, C, qkv_bytes=2, out_bytes=2):
 
 
 def bench_prefill(args, torch, lt2, synth):
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS["prefill_B4_H16_L4096_d128_bf16"]
     shape, C = cfg["shape"], cfg["chunk"]
     B, L, H, d = shape.B, shape.L, shape.H, shape.dk
     log(f"prefill inputs B={B} L={L} H={H} d={d} (2 seeded sets)")
@@ -167,7 +167,7 @@ def bench_copy(torch, lt2, nbytes=4 << 30, reps=20):
 
 
 def bench_decode(args, torch, lt2, synth):
-    cfg = synth.CONFIGS[5]
+    cfg = synth.WORKLOADS["decode_B256_H16_d128_T4"]
     B, H, d, T, steps = cfg["B"], cfg["H"], cfg["d"], cfg["T"], cfg["steps"]
     if args.decode_steps:
         steps = args.decode_steps
@@ -250,7 +250,7 @@ def channel_flops_bytes(B, L, H, d, C):
 
 def bench_channel(args, torch, lt2, synth, reps=3):
     """Per-channel-gate prefill, B=1 H=32 L=32768 d=128, bf16 q/k/v, chunk 64."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS["channel_B1_H32_L32768_d128_bf16"]
     sh, C = cfg["shape"], cfg["chunk"]
     log(f"channel inputs B={sh.B} L={sh.L} H={sh.H} d={sh.dk}")
     x = synth.gdn_inputs(sh, seed=0)
@@ -297,7 +297,7 @@ def bench_channel(args, torch, lt2, synth, reps=3):
 def bench_looped(args, torch, lt2, synth, reps=5, gate=False):
     """T=4 loops of the LT2-linear block, B=2 L=8192 d_model=2048 H=16 d=128
     (with ``gate``: the sigmoid output gate inside the loop)."""
-    cfg = synth.CONFIGS[3]
+    cfg = synth.WORKLOADS["looped_B2_L8192_D2048_T4"]
     sh = cfg["shape"]
     log(f"looped inputs B={sh.B} L={sh.L} D={sh.d_model} H={sh.H} d={sh.d} T={sh.T} gate={gate}")
     w = synth.loop_weights(sh, seed=0, gate=gate)
@@ -372,7 +372,7 @@ def bench_swa(args, torch, lt2, synth, reps=20):
 def bench_hybrid(args, torch, lt2, synth, reps=5):
     """Looped hybrid block, B=2 L=8192 d_model=2048 H=16 d=128, shared stack
     (gated-delta layer, window-512 attention layer), T=4."""
-    sh = synth.CONFIGS[3]["shape"]
+    sh = synth.WORKLOADS["looped_B2_L8192_D2048_T4"]["shape"]
     kinds, window, C = ("gdn", "swa"), 512, 64
     log(f"hybrid inputs B={sh.B} L={sh.L} D={sh.d_model} H={sh.H} d={sh.d} T={sh.T} layers={kinds} w={window}")
     layers = []
@@ -427,7 +427,7 @@ def bench_backward(args, torch, lt2, synth, reps=5):
     With bf16 inputs its products run on the bf16 matrix cores, the fp32
     intermediates as hi + lo bf16 pairs (up to three instructions per product),
     so the algorithmic rate is reported without a peak fraction."""
-    sh = synth.CONFIGS[2]["shape"]
+    sh = synth.WORKLOADS["prefill_B4_H16_L4096_d128_bf16"]["shape"]
     log(f"backward inputs B={sh.B} L={sh.L} H={sh.H} d={sh.dk} bf16")
     x = synth.gdn_inputs(sh, seed=0)
     t = {kk: torch.from_numpy(vv).to("cuda") for kk, vv in x.items()}
@@ -560,7 +560,7 @@ def cpu_baseline(synth):
     """The fp64 oracle on the whole headline workload (4 sequences x 4096 tokens x
     16 heads, seed 0); tokens/s per loop = B*L / t."""
     import oracle
-    shape = synth.CONFIGS[2]["shape"]
+    shape = synth.WORKLOADS["prefill_B4_H16_L4096_d128_bf16"]["shape"]
     x = synth.gdn_inputs(shape, seed=0)
     threads = oracle.max_threads()
     t0 = time.perf_counter()

@@ -264,12 +264,12 @@ def swa_inputs(shape: SWAShape, seed: int = 0) -> dict:
 SWA_WORKLOAD = SWAShape(2, 8192, 16, 128, 512)
 
 
-# The five workloads of the LT2 linear-mixer hot path.
-CONFIGS = {
-    1: dict(kind="prefill", shape=GDNShape(1, 256, 1, 64, 64, "head", 0.0, "f32"), chunk=64, T=1),
-    2: dict(kind="prefill", shape=GDNShape(4, 4096, 16, 128, 128, "head", 2.0, "bf16"), chunk=64, T=1),
-    3: dict(kind="looped", shape=LoopShape(2, 8192, 2048, 16, 128, 4), chunk=64),
-    4: dict(kind="prefill", shape=GDNShape(1, 32768, 32, 128, 128, "channel", 2.0, "bf16"), chunk=64, T=1),
-    5: dict(kind="decode", prefill=GDNShape(256, 2048, 16, 128, 128, "head", 0.0, "f32"),
+# The five workloads of the LT2 linear-mixer hot path, named by kind and sizes.
+WORKLOADS = {
+    "prefill_B1_L256_d64_f32": dict(kind="prefill", shape=GDNShape(1, 256, 1, 64, 64, "head", 0.0, "f32"), chunk=64, T=1),
+    "prefill_B4_H16_L4096_d128_bf16": dict(kind="prefill", shape=GDNShape(4, 4096, 16, 128, 128, "head", 2.0, "bf16"), chunk=64, T=1),
+    "looped_B2_L8192_D2048_T4": dict(kind="looped", shape=LoopShape(2, 8192, 2048, 16, 128, 4), chunk=64),
+    "channel_B1_H32_L32768_d128_bf16": dict(kind="prefill", shape=GDNShape(1, 32768, 32, 128, 128, "channel", 2.0, "bf16"), chunk=64, T=1),
+    "decode_B256_H16_d128_T4": dict(kind="decode", prefill=GDNShape(256, 2048, 16, 128, 128, "head", 0.0, "f32"),
             B=256, H=16, d=128, T=4, steps=1024, chunk=64),
 }

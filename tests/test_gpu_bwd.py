@@ -114,7 +114,7 @@ def test_backward_extreme_gates(dtype):
 def test_backward_full_workload_sampled_units():
     """B4 H16 L4096 d128 bf16 (the headline prefill workload): the GPU runs the
     whole batch; the oracle recomputes two (b, h) units from their own streams."""
-    shape = synth.CONFIGS[2]["shape"]
+    shape = synth.WORKLOADS["prefill_B4_H16_L4096_d128_bf16"]["shape"]
     announce("bwd full workload")
     x = synth.gdn_inputs(shape, seed=0)
     dO = synth.grad_out(shape, seed=0)

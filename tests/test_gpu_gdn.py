@@ -32,7 +32,7 @@ def oracle_prefill(x, S0=None):
 @pytest.mark.parametrize("chunk", [64, 32, 16])
 def test_tiny_gdn_fp32_chunks(chunk):
     """B=1 H=1 L=256 d=64 fp32, scalar gate, S0=0: every chunk size matches the oracle."""
-    shape = synth.CONFIGS[1]["shape"]
+    shape = synth.WORKLOADS["prefill_B1_L256_d64_f32"]["shape"]
     announce(f"tiny fp32 chunk={chunk}")
     x = synth.gdn_inputs(shape, seed=0)
     o, S = run_prefill(x, shape, chunk)
@@ -178,7 +178,7 @@ def test_empty_and_determinism():
 def test_prefill_full_size_bf16_sampled():
     """B=4 H=16 L=4096 d=128 bf16, chunk 64 (the benchmarked prefill launch):
     sampled (b, h) units against the oracle."""
-    shape = synth.CONFIGS[2]["shape"]
+    shape = synth.WORKLOADS["prefill_B4_H16_L4096_d128_bf16"]["shape"]
     announce("prefill full size bf16")
     x = synth.gdn_inputs(shape, seed=0)
     o, S = run_prefill(x, shape, 64)
@@ -376,7 +376,7 @@ def test_channel_state_passing_bf16():
 def test_channel_full_size_bf16_sampled():
     """B=1 H=32 L=32768 d=128 bf16, per-channel gate (the benchmarked launch):
     sampled heads against the oracle."""
-    shape = synth.CONFIGS[4]["shape"]
+    shape = synth.WORKLOADS["channel_B1_H32_L32768_d128_bf16"]["shape"]
     announce("channel full size")
     x = synth.gdn_inputs(shape, seed=0)
     o, S = run_prefill(x, shape, 64)

@@ -100,7 +100,7 @@ def test_hybrid_full_size_prefix():
     T=2 times (four layer applications), the benchmarked launch shape: every
     layer is causal, so the oracle's run on the first 384 tokens of sequence 0
     must match the GPU's full run there."""
-    s3 = synth.CONFIGS[3]["shape"]
+    s3 = synth.WORKLOADS["looped_B2_L8192_D2048_T4"]["shape"]
     shape = synth.LoopShape(s3.B, s3.L, s3.d_model, s3.H, s3.d, 2)
     announce("hybrid full size")
     hl, dl = make_layers(shape, ("gdn", "swa"), seed=0)

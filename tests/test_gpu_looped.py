@@ -61,7 +61,7 @@ def test_looped_full_size_prefix():
     """B=2 L=8192 d_model=2048 H=16 d=128 T=4 (the benchmarked launch): the output
     at token t depends only on tokens <= t, so the oracle's run on the first 512
     tokens of sequence 1 must match the GPU's full run there."""
-    shape = synth.CONFIGS[3]["shape"]
+    shape = synth.WORKLOADS["looped_B2_L8192_D2048_T4"]["shape"]
     announce("looped full size")
     w = synth.loop_weights(shape, seed=0)
     h0 = synth.loop_h0(shape, seed=0)
