@@ -72,7 +72,8 @@ def test_looped_full_size_prefix():
     assert np.all(np.isfinite(got))
 
 
-@pytest.mark.parametrize("B,L,D,H,d,T", [(2, 40, 256, 2, 128, 2), (3, 17, 128, 2, 64, 3)])
+@pytest.mark.parametrize("B,L,D,H,d,T", [(2, 40, 256, 2, 128, 2), (3, 17, 128, 2, 64, 3),
+                                          (130, 6, 128, 2, 64, 2)])
 def test_looped_decode_chain_matches_mixer(B, L, D, H, d, T):
     """Token-by-token looped decode from zero states gives, for every token, the
     h of the oracle's looped block on the whole sequence (each loop's mixer is
