@@ -164,6 +164,13 @@ size_t lt2_looped_mixer_workspace_size(const lt2_loop_desc *desc);
  *                 with out_gate [4*H*d + 2*H, d_model], rows W_q, W_k, W_v, W_g,
  *                 W_beta, W_alpha
  *   W_o           [d_model, H*d] bf16
+ * Weight layout: every weight is stored [d_out, d_in] (row i holds the
+ * weights of output feature i) and applied as x W^T, so both operands of each
+ * product run contiguously along the reduction dimension.  This departs from
+ * the row-vector convention x W with W stored [d_in, d_out]: a caller holding
+ * weights that way passes their transposes (W_in = [W_q W_k W_v W_beta
+ * W_alpha]^T).  The same layout holds for lt2_looped_decode_step and
+ * lt2_hybrid_mixer.
  * Requirements: d_model % 128 == 0, H*d % 128 == 0, d in {64, 128}.
  */
 lt2_status lt2_looped_mixer(const lt2_loop_desc *desc, const float *h_in, float *h_out,
@@ -306,6 +313,31 @@ lt2_status lt2_hybrid_mixer(const lt2_hybrid_desc *desc, const float *h_in, floa
  * streaming kernel.  Used to measure the achievable HBM bandwidth.
  */
 lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+/* Access patterns of lt2_hbm_probe. */
+typedef enum lt2_probe_mode {
+    LT2_PROBE_COPY = 0,   /* read src, write dst */
+    LT2_PROBE_READ = 1,   /* read src only (dst is not written in practice) */
+    LT2_PROBE_WRITE = 2   /* write dst only (src unused, may be NULL) */
+} lt2_probe_mode;
+
+/*
+ * Bandwidth probe with a chosen launch shape, for finding the achievable HBM
+ * bandwidth of each access pattern (the best over shapes is the measured
+ * ceiling the memory-bound kernels are compared with).  One grid-stride
+ * streaming kernel of `blocks` workgroups of 256 lanes (0 = the default of 16
+ * per compute unit of a 256-CU device), each lane keeping `unroll` 16-byte
+ * loads (or stores) in flight.
+ *   dst, src   device buffers of `bytes` bytes each (a multiple of 16),
+ *              16-byte aligned; src may be NULL for LT2_PROBE_WRITE
+ *   mode       lt2_probe_mode
+ *   blocks     0 .. 16777215     unroll  1, 2, 4, 8 or 16
+ * Errors: LT2_ERR_NULL, LT2_ERR_ALIGN as usual; LT2_ERR_SHAPE for a size not a
+ * multiple of 16 or blocks out of range; LT2_ERR_UNSUPPORTED for another mode
+ * or unroll.
+ */
+lt2_status lt2_hbm_probe(void *dst, const void *src, size_t bytes, int32_t mode, int32_t blocks,
+                         int32_t unroll, void *stream);
 
 #ifdef __cplusplus
 }

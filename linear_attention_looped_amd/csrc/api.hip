@@ -12,6 +12,19 @@ namespace {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Every launch of the gated-delta kernels has one workgroup per (unit, chunk)
+// (prepare, backward gradients), per (unit, column block of >= 16 columns)
+// (scans) or per unit (decode), of at most 512 threads; the runtime rejects a
+// launch of 2^32 threads or more.  Checked here in 64 bits, before anything is
+// enqueued, for `units` (b, h) units of L tokens in chunks of `chunk` (the
+// backward pass always uses 64, at least the smallest chunk, 16).
+bool launch_fits(int64_t units, int64_t L, int64_t chunk, bool column_blocks = true) {
+    const int64_t limit = 0xffffffffLL / 512;   // workgroups of 512 threads
+    const int64_t chunks = units * ((L + chunk - 1) / chunk);
+    const int64_t col_blocks = column_blocks ? units * (128 / 16) : units;
+    return chunks <= limit && col_blocks <= limit;
+}
+
 lt2_status check_desc(const lt2_gdn_desc *d, bool decode) {
     if (!d) return LT2_ERR_NULL;
     if (d->B < 0 || d->L < 0 || d->H <= 0 || d->d_k <= 0 || d->d_v <= 0) return LT2_ERR_SHAPE;
@@ -26,6 +39,7 @@ lt2_status check_desc(const lt2_gdn_desc *d, bool decode) {
     // grid dimensions must fit their 32-bit and 65535 limits
     if ((int64_t)d->B * d->H > 0x7fffffffLL) return LT2_ERR_SHAPE;
     if (!decode && (d->H > 65535 || d->B > 65535)) return LT2_ERR_SHAPE;
+    if (!launch_fits((int64_t)d->B * d->H, decode ? 1 : d->L, decode ? 1 : d->chunk, !decode)) return LT2_ERR_SHAPE;
     return LT2_OK;
 }
 
@@ -213,6 +227,17 @@ lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream) 
     return hip_status(launch_copy(dst, src, bytes, (hipStream_t)stream));
 }
 
+lt2_status lt2_hbm_probe(void *dst, const void *src, size_t bytes, int32_t mode, int32_t blocks, int32_t unroll,
+                         void *stream) {
+    if (mode != LT2_PROBE_COPY && mode != LT2_PROBE_READ && mode != LT2_PROBE_WRITE) return LT2_ERR_UNSUPPORTED;
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16) return LT2_ERR_UNSUPPORTED;
+    if (bytes % 16 != 0 || blocks < 0 || blocks > 16777215) return LT2_ERR_SHAPE;
+    if (bytes == 0) return LT2_OK;
+    if (!dst || (mode != LT2_PROBE_WRITE && !src)) return LT2_ERR_NULL;
+    if (!aligned(dst, 16) || !aligned(src, 16)) return LT2_ERR_ALIGN;
+    return hip_status(launch_probe(dst, src, bytes, mode, (unsigned)blocks, unroll, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {
@@ -227,6 +252,7 @@ lt2_status check_loop(const lt2_loop_desc *d) {
     if (d->d_model % 128 != 0 || ((int64_t)d->H * d->d_head) % 128 != 0) return LT2_ERR_UNSUPPORTED;
     if ((int64_t)d->B * d->L > 0x7fffffffLL || (int64_t)d->H * d->d_head > 65536 || d->H > 65535 || d->B > 65535)
         return LT2_ERR_SHAPE;
+    if (!launch_fits((int64_t)d->B * d->H, d->L, d->chunk)) return LT2_ERR_SHAPE;
     return LT2_OK;
 }
 

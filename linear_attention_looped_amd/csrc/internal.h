@@ -45,6 +45,8 @@ hipError_t launch_prefill_head(const GdnArgs &a, int phase, hipStream_t s);
 size_t prefill_channel_ws_bytes(int B, int L, int H, int dk, int C, bool bf16);
 hipError_t launch_prefill_channel(const GdnArgs &a, int phase, hipStream_t s);
 hipError_t launch_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+hipError_t launch_probe(void *dst, const void *src, size_t bytes, int mode, unsigned blocks, int unroll,
+                        hipStream_t s);
 
 // Causal sliding-window softmax attention: q, k, v bf16 [B, L, H, d], out bf16
 // or fp32 [B, L, H, d], keys t-window+1 .. t for query t, scale 1/sqrt(d);

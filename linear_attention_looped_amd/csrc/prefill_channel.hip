@@ -281,8 +281,8 @@ __global__ __launch_bounds__(256) void prep_channel_kernel(const TI *__restrict_
 template <int DK, int DV, int BV, int C, int PREC, typename TI, typename TO>
 __global__ __launch_bounds__(256) void scan_channel_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                            const TI *__restrict__ v, const float *__restrict__ ws,
-                                                           const float *__restrict__ state_in, TO *__restrict__ out,
-                                                           float *__restrict__ state_out, int L, int H, int NC) {
+                                                           const float *state_in, TO *__restrict__ out,
+                                                           float *state_out, int L, int H, int NC) {
     constexpr int KP = DK + 4;
     constexpr int CP = C + 4;
     constexpr int NTR = C / 16, NTK = DK / 16;
@@ -1012,8 +1012,8 @@ struct TmFrags {   // one chunk's A-fragments of this wave (hi, lo per K-block)
 template <int DK, int DV, int C, typename TO>
 __global__ __launch_bounds__(512) void scan_channel_tm_kernel(const uint16_t *__restrict__ v,
                                                               const unsigned char *__restrict__ ws,
-                                                              const float *__restrict__ state_in,
-                                                              TO *__restrict__ out, float *__restrict__ state_out,
+                                                              const float *state_in,
+                                                              TO *__restrict__ out, float *state_out,
                                                               int L, int H, int NC) {
     using SH = TmShape<DK, C>;
     using FR = TmFrags<DK, C>;

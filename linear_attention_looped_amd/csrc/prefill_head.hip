@@ -288,8 +288,8 @@ struct ScanPrefetch {
 template <int DK, int DV, int BV, int C, int PREC, typename TI, typename TO>
 __global__ __launch_bounds__(256) void scan_head_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                         const TI *__restrict__ v, const float *__restrict__ ws,
-                                                        const float *__restrict__ state_in, TO *__restrict__ out,
-                                                        float *__restrict__ state_out, int L, int H, int NC) {
+                                                        const float *state_in, TO *__restrict__ out,
+                                                        float *state_out, int L, int H, int NC) {
     using PF = ScanPrefetch<DK, C, BV, PREC, TI>;
     constexpr int KP = DK + 4;
     constexpr int CP = C + 4;
@@ -633,8 +633,8 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
                                                              const uint16_t *__restrict__ k,
                                                              const uint16_t *__restrict__ v,
                                                              const unsigned char *__restrict__ ws,
-                                                             const float *__restrict__ state_in,
-                                                             TO *__restrict__ out, float *__restrict__ state_out,
+                                                             const float *state_in,
+                                                             TO *__restrict__ out, float *state_out,
                                                              int L, int H, int NC,
                                                              const uint16_t *__restrict__ gate) {
     constexpr int NW = 8, NTH = 64 * NW;

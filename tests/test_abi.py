@@ -72,6 +72,18 @@ def test_prefill_rejects_null_misaligned_and_small_workspace():
     assert prefill(d, ws=FAKE + 4, ws_bytes=need) == 6
 
 
+def test_launch_size_limits_are_checked_before_enqueue():
+    # valid sizes whose grids would pass 2^32 threads: rejected on the host in
+    # 64-bit arithmetic, not at launch time with a HIP error
+    big = good_desc(B=1024, H=1024, L=1 << 20, chunk=16)
+    assert prefill(big) == 2
+    assert lt2.lt2_gdn_prefill_workspace_size(big) == 0
+    assert bwd_call(big) == 2
+    assert decode(good_desc(B=8192, H=1024, L=1)) == 2
+    assert decode(good_desc(B=8191, H=1024, L=1), s=None) == 1      # just inside: reaches the pointer checks
+    assert loop_call(good_loop(B=4096, L=1 << 19, H=2, chunk=16)) == 2
+
+
 def test_workspace_size_of_invalid_descriptor_is_zero():
     assert lt2.lt2_gdn_prefill_workspace_size(good_desc(chunk=7)) == 0
     assert lt2.lt2_gdn_prefill_workspace_size(good_desc(L=0)) == 0
@@ -99,6 +111,20 @@ def test_copy_validation():
     assert L.lt2_hbm_copy(None, P(FAKE), 16, None) == 1
     assert L.lt2_hbm_copy(P(FAKE), P(FAKE), 17, None) == 2
     assert L.lt2_hbm_copy(P(FAKE + 4), P(FAKE), 32, None) == 6
+
+
+def test_probe_validation():
+    L = lt2.lib()
+    P = ctypes.c_void_p
+    assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 0, 0, 0, 4, None) == 0
+    assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 32, 3, 0, 4, None) == 4       # unknown mode
+    assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 32, 0, 0, 3, None) == 4       # unroll not built
+    assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 40, 0, 0, 4, None) == 2
+    assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 32, 0, -1, 4, None) == 2
+    assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 32, 0, 1 << 24, 4, None) == 2
+    assert L.lt2_hbm_probe(P(FAKE), None, 32, 1, 0, 4, None) == 1         # reading needs src
+    assert L.lt2_hbm_probe(None, P(FAKE), 32, 2, 0, 4, None) == 1
+    assert L.lt2_hbm_probe(P(FAKE + 8), P(FAKE), 32, 0, 0, 4, None) == 6
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -413,3 +413,58 @@ def test_prepare_then_scan_equals_prefill(gate):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(o), host(o_ref))
     np.testing.assert_array_equal(host(S), host(S_ref))
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_state_in_place(gate, dtype):
+    """state_out may be the state_in buffer (the header allows it): with a ragged
+    L the in-place call gives, bit for bit, what separate buffers give, and both
+    match the oracle."""
+    shape = synth.GDNShape(2, 150, 2, 128, 128, gate, 0.0, dtype)
+    announce(f"in-place state {gate} {dtype}")
+    x = synth.gdn_inputs(shape, seed=41)
+    S0 = np.random.default_rng(41).standard_normal((2, 2, 128, 128)).astype(np.float32) * 0.1
+    qdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = (dev(x[n], qdt) for n in ("q", "k", "v"))
+    a, b = dev(x["alpha"]), dev(x["beta"])
+    o1, S1 = lt2.lt2_gdn_prefill(q, k, v, a, b, state_in=dev(S0), chunk=64, out_dtype=torch.float32)
+    st = dev(S0)
+    o2, S2 = lt2.lt2_gdn_prefill(q, k, v, a, b, state_in=st, state_out=st, chunk=64, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == st.data_ptr()
+    np.testing.assert_array_equal(host(o2), host(o1))
+    np.testing.assert_array_equal(host(st), host(S1))
+    o_ref, S_ref = oracle_prefill(x, S0)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert rel_err(host(o2), o_ref) <= tol
+    assert rel_err(host(st), S_ref) <= tol
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_workspace_nan_canary(gate, dtype, chunk):
+    """The scan reads only workspace bytes the prepare phase wrote: a workspace
+    filled with NaN beforehand gives finite outputs bit-identical to a
+    zero-filled one, on a ragged last chunk."""
+    L = 150 if chunk == 64 else 71
+    shape = synth.GDNShape(1, L, 3, 64, 64, gate, 0.0, dtype)
+    announce(f"nan canary {gate} {dtype} chunk={chunk}")
+    x = synth.gdn_inputs(shape, seed=42)
+    qdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = (dev(x[n], qdt) for n in ("q", "k", "v"))
+    a, b = dev(x["alpha"]), dev(x["beta"])
+    desc = lt2.gdn_desc(1, L, 3, 64, 64, chunk, lt2._dt(q), lt2.LT2_F32,
+                        lt2.LT2_GATE_CHANNEL if gate == "channel" else lt2.LT2_GATE_HEAD)
+    nbytes = lt2.lt2_gdn_prefill_workspace_size(desc)
+    res = []
+    for fill in (0x00, 0xFF):          # 0xFF bytes: NaN as fp32 and as bf16
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        o, S = lt2.lt2_gdn_prefill(q, k, v, a, b, chunk=chunk, out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        res.append((host(o), host(S)))
+    for arr in res[1]:
+        assert np.all(np.isfinite(arr))
+    np.testing.assert_array_equal(res[1][0], res[0][0])
+    np.testing.assert_array_equal(res[1][1], res[0][1])

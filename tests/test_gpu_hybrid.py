@@ -36,9 +36,13 @@ def run_hybrid(h0, dev_layers, shape, window, gate=False, chunk=64):
     return host(out)
 
 
-# At most four layer applications per case, as in the looped workload (T = 4 of
-# one layer): every application rounds its GEMM and mixer inputs to bf16, so the
-# error against the fp64 oracle grows with depth (six applications reach 5.1e-3).
+# At most four layer applications per case (the benchmarked hybrid is T = 2 of a
+# two-layer block).  Every application rounds its GEMM and mixer inputs to bf16;
+# a window layer's unnormalised q, k give large logits and its update roughly
+# doubles max|h|, so the error against the fp64 oracle grows with depth.  An fp64
+# emulation of these rounding points puts the full-size block at 2.2e-3 after
+# four applications and at 3.9e-3 .. 5.4e-3 (by seed) after eight, which the
+# 5e-3 bar does not hold reliably.
 @pytest.mark.parametrize("kinds,gate,w,T", [(("gdn", "swa"), False, 64, 2), (("swa", "gdn"), True, 100, 2),
                                             (("swa",), False, 37, 2), (("gdn", "swa", "swa"), False, 300, 1)])
 def test_hybrid_matches_oracle(kinds, gate, w, T):
@@ -49,17 +53,18 @@ def test_hybrid_matches_oracle(kinds, gate, w, T):
     got = run_hybrid(h0, dl, shape, w, gate)
     ref = oracle.hybrid_mixer(h0, hl, shape.H, shape.d, shape.T, w, gate=gate)
     assert rel_err(got, ref) <= TOL_BF16
-    assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
 
 
 def test_hybrid_d64():
-    shape = synth.LoopShape(1, 200, 128, 2, 64, 3)
+    shape = synth.LoopShape(1, 200, 128, 2, 64, 2)
     announce("hybrid d=64")
     hl, dl = make_layers(shape, ("gdn", "swa"), seed=5)
     h0 = synth.loop_h0(shape, seed=5)
     got = run_hybrid(h0, dl, shape, 50)
     ref = oracle.hybrid_mixer(h0, hl, shape.H, shape.d, shape.T, 50)
     assert rel_err(got, ref) <= TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
 
 
 def test_gdn_only_block_is_the_looped_mixer_bitwise():
@@ -109,3 +114,4 @@ def test_hybrid_full_size_prefix():
     P = 384
     ref = oracle.hybrid_mixer(h0[0:1, :P], hl, shape.H, shape.d, shape.T, 512)
     assert rel_err(got[0:1, :P], ref) <= TOL_BF16
+    assert rel_err(got[0:1, :P] - h0[0:1, :P], ref - h0[0:1, :P]) <= TOL_BF16

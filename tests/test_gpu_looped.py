@@ -33,8 +33,8 @@ def test_looped_small(B, L, D, H, d, T):
     got = run_looped(h0, w, shape)
     ref = oracle.looped_mixer(h0, w["w_in"], w["w_o"], H, d, T)
     assert rel_err(got, ref) <= TOL_BF16
-    # the mixer's own contribution, relative to its own scale (reported, looser)
-    assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16
+    # the mixer's own contribution h_T - h_0, relative to its own scale
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
 
 
 def test_looped_zero_loops_is_identity():
@@ -57,19 +57,20 @@ def test_looped_chunk_invariance():
     assert rel_err(b, ref) <= TOL_BF16
 
 
-def test_looped_full_size_prefix():
-    """B=2 L=8192 d_model=2048 H=16 d=128 T=4 (the benchmarked launch): the output
-    at token t depends only on tokens <= t, so the oracle's run on the first 512
-    tokens of sequence 1 must match the GPU's full run there."""
+def test_looped_full_size_whole_sequence():
+    """B=2 L=8192 d_model=2048 H=16 d=128 T=4 (the benchmarked launch, whose scan
+    runs in 16-column blocks): sequences are independent, so the oracle's run
+    on all 8192 tokens of sequence 1 alone must match the GPU's full run there,
+    on h_T and on the mixers' contribution h_T - h_0."""
     shape = synth.WORKLOADS["looped_B2_L8192_D2048_T4"]["shape"]
-    announce("looped full size")
+    announce("looped full size, whole sequence 1")
     w = synth.loop_weights(shape, seed=0)
     h0 = synth.loop_h0(shape, seed=0)
     got = run_looped(h0, w, shape)
-    P = 512
-    ref = oracle.looped_mixer(h0[1:2, :P], w["w_in"], w["w_o"], shape.H, shape.d, shape.T)
-    assert rel_err(got[1:2, :P], ref) <= TOL_BF16
     assert np.all(np.isfinite(got))
+    ref = oracle.looped_mixer(h0[1:2], w["w_in"], w["w_o"], shape.H, shape.d, shape.T)
+    assert rel_err(got[1:2], ref) <= TOL_BF16
+    assert rel_err(got[1:2] - h0[1:2], ref - h0[1:2]) <= TOL_BF16
 
 
 @pytest.mark.parametrize("B,L,D,H,d,T", [(2, 40, 256, 2, 128, 2), (3, 17, 128, 2, 64, 3),
@@ -93,7 +94,7 @@ def test_looped_decode_chain_matches_mixer(B, L, D, H, d, T):
         got[:, t] = host(h)
     torch.cuda.synchronize()
     assert rel_err(got, ref) <= TOL_BF16
-    assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
 
 
 def test_looped_decode_chain_full_width_sampled():
@@ -118,7 +119,7 @@ def test_looped_decode_chain_full_width_sampled():
     for b in (0, B - 1):
         ref = oracle.looped_mixer(h0[b:b + 1], w["w_in"], w["w_o"], H, d, T)
         assert rel_err(got[b:b + 1], ref) <= TOL_BF16, b
-        assert rel_err(got[b:b + 1] - h0[b:b + 1], ref - h0[b:b + 1]) <= 4 * TOL_BF16, b
+        assert rel_err(got[b:b + 1] - h0[b:b + 1], ref - h0[b:b + 1]) <= TOL_BF16, b
 
 
 def test_looped_decode_equals_mixer_on_gpu():
@@ -148,7 +149,7 @@ def test_looped_output_gate(B, L, D, H, d, T):
     got = run_looped(h0, w, shape, gate=True)
     ref = oracle.looped_mixer(h0, w["w_in"], w["w_o"], H, d, T, gate=True)
     assert rel_err(got, ref) <= TOL_BF16
-    assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
 
 
 def test_gated_looped_decode_chain_matches_mixer():
@@ -166,4 +167,19 @@ def test_gated_looped_decode_chain_matches_mixer():
         lt2.lt2_looped_decode_step(h, w_in, w_o, states, 2, 128, 2, out_gate=True)
         got[:, t] = host(h)
     assert rel_err(got, ref) <= TOL_BF16
-    assert rel_err(got - h0, ref - h0) <= 4 * TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
+
+
+def test_weight_layout_is_d_out_by_d_in():
+    """The C ABI takes weights stored [d_out, d_in] and applies x W^T: with a
+    square W_o (d_model = H*d = 256) the GPU block matches the oracle with that
+    layout and is far from the same weights read as [d_in, d_out] (x W)."""
+    shape = synth.LoopShape(1, 96, 256, 2, 128, 1)
+    announce("weight layout")
+    w = synth.loop_weights(shape, seed=8)
+    h0 = synth.loop_h0(shape, seed=8)
+    got = run_looped(h0, w, shape)
+    ref = oracle.looped_mixer(h0, w["w_in"], w["w_o"], 2, 128, 1)
+    ref_t = oracle.looped_mixer(h0, w["w_in"], np.ascontiguousarray(w["w_o"].T), 2, 128, 1)
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
+    assert rel_err(got - h0, ref_t - h0) > 0.1
