@@ -622,6 +622,7 @@ def main():
     ap.add_argument("--no-hybrid", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=0, help="decode tokens (default: the workload's 1024)")
+    ap.add_argument("--probe-reps", type=int, default=5, help="timed launches per HBM probe shape")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -636,7 +637,7 @@ def main():
         sys.exit(1)
     lt2.lib()
     pre = bench_prefill(args, torch, lt2, synth)
-    copy = bench_copy(torch, lt2)
+    copy = bench_copy(torch, lt2, reps=args.probe_reps)
     dec = None if args.no_decode else bench_decode(args, torch, lt2, synth)
     loo = None if args.no_looped else bench_looped(args, torch, lt2, synth)
     loo_g = None if args.no_looped else bench_looped(args, torch, lt2, synth, gate=True)
