@@ -205,6 +205,33 @@ lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const voi
                                   void *stream);
 
 /*
+ * Scratch capacity of lt2_looped_decode_step_noalloc: a fixed device array of
+ * this many bytes, one per GPU the library runs on, held until the process
+ * ends.
+ */
+#define LT2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * lt2_looped_decode_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * lt2_looped_decode_step with its workspace replaced by the library's
+ * fixed-size scratch array on the current device: the call allocates and frees
+ * nothing and uses no workspace argument.  Every buffer in the scratch array is
+ * written before it is read within one call, so nothing needs clearing.
+ * Limit: lt2_looped_decode_workspace_size(desc) <= LT2_NOALLOC_SCRATCH_BYTES
+ * (32 MiB: e.g. up to 1024 sequences at d_model 2048 with 16 heads of 128, with
+ * the output gate), else LT2_ERR_WORKSPACE and nothing is launched.
+ * Concurrency: all calls on one GPU share its scratch array, so calls that may
+ * overlap on one GPU (different streams, or host threads without ordering)
+ * race; serialise them (one stream) or use lt2_looped_decode_step.  The first
+ * call on a device looks up that device's copy of the array
+ * (LT2_ERR_HIP if the runtime cannot).
+ */
+lt2_status lt2_looped_decode_step_noalloc(const lt2_loop_desc *desc, float *h, const void *W_in,
+                                          const void *W_o, float *states, void *stream);
+
+/*
  * Workspace bytes lt2_gdn_backward needs (0 for an invalid descriptor or a
  * per-channel gate).
  */

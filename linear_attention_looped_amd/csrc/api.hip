@@ -4,6 +4,8 @@
 // enqueues anything, so an error leaves all outputs untouched.
 #include "lt2.h"
 
+#include <mutex>
+
 #include "internal.h"
 
 using namespace lt2;
@@ -289,6 +291,68 @@ size_t lt2_looped_decode_workspace_size(const lt2_loop_desc *desc) {
     if (check_loop(desc) != LT2_OK || desc->L != 1) return 0;
     if (desc->B == 0) return 0;
     return loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head, desc->out_gate).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch array of lt2_looped_decode_step_noalloc (its workspace).  In host code
+// `scratch` names a host-side stand-in, not device memory: kernels receive the
+// device address looked up per device below, never the array's name.
+static __device__ __align__(256) unsigned char scratch[LT2_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// Device address of the current device's copy of `scratch` (looked up on the
+// first call on each device), or nullptr with the runtime's error in *err.
+void *scratch_on_current_device(hipError_t *err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess || !p) {
+            if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        scratch_ptr[dev] = p;
+    }
+    *err = hipSuccess;
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+lt2_status lt2_looped_decode_step_noalloc(const lt2_loop_desc *desc, float *h, const void *W_in, const void *W_o,
+                                          float *states, void *stream) {
+    lt2_status st = check_loop(desc);
+    if (st != LT2_OK) return st;
+    if (desc->L != 1) return LT2_ERR_SHAPE;
+    const bool work = desc->B > 0 && desc->T > 0;
+    if (work && (!h || !W_in || !W_o || !states)) return LT2_ERR_NULL;
+    if (!aligned(h, 16) || !aligned(W_in, 16) || !aligned(W_o, 16) || !aligned(states, 16)) return LT2_ERR_ALIGN;
+    if (!work) return LT2_OK;
+    const size_t need = loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head, desc->out_gate).total;
+    if (need > LT2_NOALLOC_SCRATCH_BYTES) return LT2_ERR_WORKSPACE;
+    hipError_t err;
+    void *ws = scratch_on_current_device(&err);
+    if (!ws) return LT2_ERR_HIP;
+    LoopDecodeArgs a;
+    a.B = desc->B; a.D = desc->d_model; a.H = desc->H; a.d = desc->d_head; a.T = desc->T;
+    a.gated = desc->out_gate; a.h = h; a.W_in = static_cast<const uint16_t *>(W_in);
+    a.W_o = static_cast<const uint16_t *>(W_o); a.states = states; a.ws = ws;
+    return hip_status(launch_looped_decode(a, (hipStream_t)stream));
 }
 
 lt2_status lt2_looped_decode_step(const lt2_loop_desc *desc, float *h, const void *W_in, const void *W_o,

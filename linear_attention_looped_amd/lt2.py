@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.lt2_looped_decode_workspace_size.restype = Z
         L.lt2_looped_decode_step.argtypes = [LD, P, P, P, P, P, Z, P]
         L.lt2_looped_decode_step.restype = S
+        L.lt2_looped_decode_step_noalloc.argtypes = [LD, P, P, P, P, P]
+        L.lt2_looped_decode_step_noalloc.restype = S
         L.lt2_gdn_backward_workspace_size.argtypes = [GD]
         L.lt2_gdn_backward_workspace_size.restype = Z
         L.lt2_gdn_backward.argtypes = [GD] + [P] * 15 + [Z, P]
@@ -306,6 +308,28 @@ def lt2_looped_decode_step(h, W_in, W_o, states, H: int, d_head: int, T: int, wo
     code = lib().lt2_looped_decode_step(ctypes.byref(desc), _ptr(h), _ptr(W_in), _ptr(W_o), _ptr(states),
                                         _ptr(workspace), nbytes, _stream(stream))
     _check("lt2_looped_decode_step", code)
+    return h
+
+
+LT2_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def lt2_looped_decode_step_noalloc(h, W_in, W_o, states, H: int, d_head: int, T: int, stream=None,
+                                   out_gate: bool = False):
+    """lt2_looped_decode_step using the library's fixed device scratch array
+    instead of a workspace: neither this wrapper nor the library allocates.
+    h [B,D] fp32 and states [T,B,H,d,d] fp32 are updated in place.  Calls that
+    may overlap on one GPU share the scratch array and race.  Returns h."""
+    B, D = _dims(h, 2, "h")
+    _expect(h, "h", dtypes=torch.float32)
+    _expect(states, "states", (T, B, H, d_head, d_head), torch.float32)
+    _expect(W_in, "W_in", (_w_in_rows(H, d_head, out_gate), D), torch.bfloat16)
+    _expect(W_o, "W_o", (D, H * d_head), torch.bfloat16)
+    _on_device(h.device, h=h, W_in=W_in, W_o=W_o, states=states)
+    desc = loop_desc(B, 1, D, H, d_head, T, 64, int(out_gate))
+    code = lib().lt2_looped_decode_step_noalloc(ctypes.byref(desc), _ptr(h), _ptr(W_in), _ptr(W_o), _ptr(states),
+                                                _stream(stream))
+    _check("lt2_looped_decode_step_noalloc", code)
     return h
 
 

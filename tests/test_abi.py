@@ -188,6 +188,24 @@ def test_looped_decode_validation():
     assert loop_decode_call(good_loop(L=1, T=0), h=None, w_in=None, w_o=None, states=None, ws=None, ws_bytes=0) == 0
 
 
+def test_looped_decode_noalloc_validation():
+    P = ctypes.c_void_p
+    call = lambda d, h=FAKE, w_in=FAKE, w_o=FAKE, states=FAKE: lt2.lib().lt2_looped_decode_step_noalloc(
+        ctypes.byref(d), P(h), P(w_in), P(w_o), P(states), None)
+    assert lt2.lib().lt2_looped_decode_step_noalloc(None, None, None, None, None, None) == 1
+    assert call(good_loop(L=2)) == 2
+    assert call(good_loop(L=1, d_head=96)) == 4
+    assert call(good_loop(L=1), states=None) == 1
+    assert call(good_loop(L=1), w_o=FAKE + 8) == 6
+    # beyond the fixed scratch array: rejected before any device call
+    big = good_loop(L=1, B=2048, d_model=2048, H=16, d_head=128, out_gate=1)
+    assert lt2.lt2_looped_decode_workspace_size(big) > lt2.LT2_NOALLOC_SCRATCH_BYTES
+    assert call(big) == 5
+    # nothing to do
+    assert call(good_loop(L=1, B=0), h=None, w_in=None, w_o=None, states=None) == 0
+    assert call(good_loop(L=1, T=0), h=None, w_in=None, w_o=None, states=None) == 0
+
+
 def test_looped_gate_adds_workspace():
     assert lt2.lt2_looped_mixer_workspace_size(good_loop(out_gate=1)) > lt2.lt2_looped_mixer_workspace_size(good_loop())
     assert (lt2.lt2_looped_decode_workspace_size(good_loop(L=1, out_gate=1)) >
