@@ -51,6 +51,9 @@ KERNEL_SOURCES = {
 TRAFFIC_KEYS = {"prepare": "prep_head_kernel", "scan": "scan_head_bf16_kernel"}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+# fp32 FMA on the vector ALUs without packed-fp32 instructions: 256 CUs x 4 SIMDs
+# x 16 lanes x 2 flop x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 78.6
 
 
 def measured_traffic(kernel: str):
@@ -489,6 +492,49 @@ def bench_backward(args, torch, lt2, synth, reps=5):
                 gbs=nbytes / ms / 1e6, ws_bytes=ws.numel())
 
 
+def kda_bwd_flops_bytes(B, L, H, d):
+    """Work of the per-channel backward as built (token adjoint, fp32 vector
+    ALUs): per head-token and state element, the forward step (2 multiply-adds
+    for S^T k, 2 for the update) is run twice (checkpoint pass and segment
+    recompute) and the reverse step takes 10 multiply-adds (G += q dO^T, S_t dO,
+    G o E, D G, dE^T k, G^T k, G v, dE y, S_{t-1} z, the G update); bytes: q, k,
+    v, dO (bf16), alpha per channel and beta read, the fp32 gradients written,
+    each once."""
+    ht = B * L * H
+    flops = 2.0 * ht * d * d * (2 * 4 + 10)
+    nbytes = float(ht * (4 * d * 2 + 4 * d + 4 + 3 * d * 4 + d * 4 + 4))
+    return flops, nbytes
+
+
+def bench_backward_channel(args, torch, lt2, synth, reps=3):
+    """Backward pass of the per-channel prefill workload (B1 H32 L32768 d128
+    bf16, alpha per key channel): the token adjoint on the vector ALUs."""
+    sh = synth.WORKLOADS["channel_B1_H32_L32768_d128_bf16"]["shape"]
+    log(f"channel backward inputs B={sh.B} L={sh.L} H={sh.H} d={sh.dk} bf16")
+    x = synth.gdn_inputs(sh, seed=0)
+    t = {kk: torch.from_numpy(vv).to("cuda") for kk, vv in x.items()}
+    del x
+    q, k, v = (t[n].to(torch.bfloat16) for n in ("q", "k", "v"))
+    dO = torch.from_numpy(synth.grad_out(sh, seed=0)).to("cuda").to(torch.bfloat16)
+    desc = lt2.gdn_desc(sh.B, sh.L, sh.H, sh.dk, sh.dv, 64, lt2.LT2_BF16, lt2.LT2_BF16, lt2.LT2_GATE_CHANNEL)
+    ws = torch.empty(lt2.lt2_gdn_backward_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    run = lambda: lt2.lt2_gdn_backward(q, k, v, t["alpha"], t["beta"], dO, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    flops, nbytes = kda_bwd_flops_bytes(sh.B, sh.L, sh.H, sh.dk)
+    log(f"channel backward {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s (vector ALUs)")
+    return dict(B=sh.B, L=sh.L, H=sh.H, d=sh.dk, ms=ms, tokens_per_s=sh.B * sh.L / (ms / 1e3), flops=flops,
+                bytes=nbytes, tflops=flops / ms / 1e9, valu_frac=flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS,
+                path="token adjoint, fp32 vector ALUs", ws_bytes=ws.numel())
+
+
 def _slab_inputs(synth, shape, b0, nb):
     """Inputs of batch rows b0..b0+nb of the decode-seeding prefill (per-unit streams)."""
     L, H, d = shape.L, shape.H, shape.dk
@@ -647,6 +693,7 @@ def main():
     swa = None if args.no_swa else bench_swa(args, torch, lt2, synth)
     hyb = None if args.no_hybrid else bench_hybrid(args, torch, lt2, synth)
     bwd = None if args.no_backward else bench_backward(args, torch, lt2, synth)
+    bwc = None if (args.no_backward or args.no_channel) else bench_backward_channel(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
 
     value = pre["B"] * pre["L"] * 1 / (pre["ms_step"] / 1e3)
@@ -696,6 +743,8 @@ def main():
         extra["hybrid"] = hyb
     if bwd:
         extra["backward"] = bwd
+    if bwc:
+        extra["backward_channel"] = bwc
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pre["ms_step"], "higher_is_better": True, "scaling": "weak",

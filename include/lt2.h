@@ -232,29 +232,31 @@ lt2_status lt2_looped_decode_step_noalloc(const lt2_loop_desc *desc, float *h, c
                                           const void *W_o, float *states, void *stream);
 
 /*
- * Workspace bytes lt2_gdn_backward needs (0 for an invalid descriptor or a
- * per-channel gate).
+ * Workspace bytes lt2_gdn_backward needs (0 for an invalid descriptor).
  */
 size_t lt2_gdn_backward_workspace_size(const lt2_gdn_desc *desc);
 
 /*
- * Backward pass of lt2_gdn_prefill, scalar gate (desc->gate == LT2_GATE_HEAD):
- * the gradients of a loss whose cotangents are d_out for the outputs o and
- * d_state_out for the final state, through the state-update equation of the
- * LT2 explainer (paithon.it, "Sostituire il motore") with o_t = S_t^T q_t.
+ * Backward pass of lt2_gdn_prefill: the gradients of a loss whose cotangents
+ * are d_out for the outputs o and d_state_out for the final state, through the
+ * state-update equation of the LT2 explainer (paithon.it, "Sostituire il
+ * motore") with o_t = S_t^T q_t, for either gate.
  *   q, k, v, alpha, beta, state_in   the forward call's inputs (state_in NULL = 0)
  *   d_out        [B, L, H, d_v] of desc->out_dtype
  *   d_state_out  [B, H, d_k, d_v] fp32, or NULL (= 0)
  *   dq, dk       [B, L, H, d_k] fp32      dv  [B, L, H, d_v] fp32
- *   dlog_alpha   [B, L, H] fp32, the gradient with respect to log alpha_t
+ *   dlog_alpha   the gradient with respect to log alpha_t, alpha's shape:
+ *                [B, L, H] (scalar gate) or [B, L, H, d_k] (channel gate), fp32
  *                (finite at alpha = 0; divide by alpha for d/d alpha)
  *   dbeta        [B, L, H] fp32
  *   d_state_in   [B, H, d_k, d_v] fp32, or NULL when not wanted
  *   ws           at least lt2_gdn_backward_workspace_size(desc) bytes, 16-aligned
- * Arithmetic is fp32 throughout (bf16 inputs are widened exactly); the chunk
- * length used internally is 64 whatever desc->chunk holds (the result does not
- * depend on it).  Errors: LT2_ERR_UNSUPPORTED for the channel gate; otherwise
- * as lt2_gdn_prefill.
+ * Arithmetic is fp32 throughout (bf16 inputs are widened exactly).  Scalar
+ * gate: the chunk form on the matrix cores with chunk 64 whatever desc->chunk
+ * holds.  Channel gate: the token adjoint on the vector ALUs, with the state
+ * checkpointed every 16 tokens in the workspace (d_k^2 * 4 bytes per 16 tokens
+ * per unit, plus d_k/16 partial sums of the row gradients).  The result does
+ * not depend on desc->chunk.  Errors as for lt2_gdn_prefill.
  */
 lt2_status lt2_gdn_backward(const lt2_gdn_desc *desc, const void *q, const void *k,
                             const void *v, const float *alpha, const float *beta,

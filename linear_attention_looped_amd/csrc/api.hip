@@ -158,9 +158,10 @@ lt2_status lt2_gdn_decode_step(const lt2_gdn_desc *desc, const void *q, const vo
 }
 
 size_t lt2_gdn_backward_workspace_size(const lt2_gdn_desc *desc) {
-    if (check_desc(desc, false) != LT2_OK || desc->gate != LT2_GATE_HEAD) return 0;
+    if (check_desc(desc, false) != LT2_OK) return 0;
     if (desc->B == 0 || desc->L == 0) return 0;
-    return gdn_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k);
+    return desc->gate == LT2_GATE_CHANNEL ? kda_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k)
+                                          : gdn_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k);
 }
 
 lt2_status lt2_gdn_backward(const lt2_gdn_desc *desc, const void *q, const void *k, const void *v,
@@ -169,7 +170,7 @@ lt2_status lt2_gdn_backward(const lt2_gdn_desc *desc, const void *q, const void 
                             float *dbeta, float *d_state_in, void *ws, size_t ws_bytes, void *stream) {
     lt2_status st = check_desc(desc, false);
     if (st != LT2_OK) return st;
-    if (desc->gate != LT2_GATE_HEAD) return LT2_ERR_UNSUPPORTED;
+    const bool channel = desc->gate == LT2_GATE_CHANNEL;
     const bool work = desc->B > 0 && desc->L > 0;
     if (work && (!q || !k || !v || !alpha || !beta || !d_out || !dq || !dk || !dv || !dlog_alpha || !dbeta))
         return LT2_ERR_NULL;
@@ -178,7 +179,9 @@ lt2_status lt2_gdn_backward(const lt2_gdn_desc *desc, const void *q, const void 
         !aligned(d_state_in, 16) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(dlog_alpha, 4) ||
         !aligned(dbeta, 4))
         return LT2_ERR_ALIGN;
-    const size_t need = work ? gdn_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k) : 0;
+    const size_t need = !work ? 0
+                        : channel ? kda_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k)
+                                  : gdn_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k);
     if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
     if (need > 0 && !aligned(ws, 16)) return LT2_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
@@ -195,7 +198,7 @@ lt2_status lt2_gdn_backward(const lt2_gdn_desc *desc, const void *q, const void 
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state_in = state_in; a.dout = d_out;
     a.dstate_out = d_state_out; a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta;
     a.dstate_in = d_state_in; a.ws = ws;
-    return hip_status(launch_gdn_bwd(a, s));
+    return hip_status(channel ? launch_kda_bwd(a, s) : launch_gdn_bwd(a, s));
 }
 
 lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *k, const void *v, void *out,

@@ -74,6 +74,9 @@ struct GdnBwdArgs {
 };
 size_t gdn_bwd_ws_bytes(int B, int L, int H, int d);
 hipError_t launch_gdn_bwd(const GdnBwdArgs &a, hipStream_t s);
+// Per-channel gate: dlog_alpha is [B, L, H, d].
+size_t kda_bwd_ws_bytes(int B, int L, int H, int d);
+hipError_t launch_kda_bwd(const GdnBwdArgs &a, hipStream_t s);
 
 // Looped LT2-linear block.
 struct LoopArgs {
