@@ -86,8 +86,9 @@ typedef struct lt2_loop_desc {
     int32_t out_gate;    /* 1: sigmoid output gate inside the loop (W_g rows in W_in), 0: none */
 } lt2_loop_desc;
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char *lt2_status_string(lt2_status s);
+/* Human-readable name of a status code (static string, never NULL); any value
+ * outside lt2_status gives "unknown status". */
+const char *lt2_status_string(int32_t status);
 
 /*
  * Workspace bytes lt2_gdn_prefill needs for `desc` (0 if none).  Returns 0 for

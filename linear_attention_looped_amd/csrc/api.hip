@@ -69,8 +69,8 @@ lt2_status hip_status(hipError_t e) { return e == hipSuccess ? LT2_OK : LT2_ERR_
 
 extern "C" {
 
-const char *lt2_status_string(lt2_status s) {
-    switch (s) {
+const char *lt2_status_string(int32_t status) {
+    switch (status) {
         case LT2_OK: return "ok";
         case LT2_ERR_NULL: return "required pointer is NULL";
         case LT2_ERR_SHAPE: return "invalid or inconsistent shape";
