@@ -252,6 +252,7 @@ size_t lt2_gdn_backward_workspace_size(const lt2_gdn_desc *desc);
  *   dbeta        [B, L, H] fp32
  *   d_state_in   [B, H, d_k, d_v] fp32, or NULL when not wanted
  *   ws           at least lt2_gdn_backward_workspace_size(desc) bytes, 16-aligned
+ * With the channel gate alpha must be 16-byte aligned (read 16 bytes at a time).
  * Arithmetic is fp32 throughout (bf16 inputs are widened exactly).  Scalar
  * gate: the chunk form on the matrix cores with chunk 64 whatever desc->chunk
  * holds.  Channel gate: the token adjoint on the vector ALUs, with the state

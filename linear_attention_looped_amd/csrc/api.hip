@@ -15,16 +15,17 @@ namespace {
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Every launch of the gated-delta kernels has one workgroup per (unit, chunk)
-// (prepare, backward gradients), per (unit, column block of >= 16 columns)
-// (scans) or per unit (decode), of at most 512 threads; the runtime rejects a
-// launch of 2^32 threads or more.  Checked here in 64 bits, before anything is
-// enqueued, for `units` (b, h) units of L tokens in chunks of `chunk` (the
-// backward pass always uses 64, at least the smallest chunk, 16).
-bool launch_fits(int64_t units, int64_t L, int64_t chunk, bool column_blocks = true) {
-    const int64_t limit = 0xffffffffLL / 512;   // workgroups of 512 threads
+// (prepare, backward gradients: at most 512 threads), per (unit, column block
+// of >= 16 columns) (scans, the per-channel backward: at most 1024 threads) or
+// per unit (decode); the runtime rejects a launch of 2^32 threads or more.
+// Checked here in 64 bits, before anything is enqueued, for `units` (b, h)
+// units of L tokens in chunks of `chunk` (the backward pass always uses 64, at
+// least the smallest chunk, 16).
+bool launch_fits(int64_t units, int64_t L, int64_t chunk, bool decode = false) {
+    if (decode) return units <= 0xffffffffLL / 256;   // 256 threads per unit
     const int64_t chunks = units * ((L + chunk - 1) / chunk);
-    const int64_t col_blocks = column_blocks ? units * (128 / 16) : units;
-    return chunks <= limit && col_blocks <= limit;
+    const int64_t col_blocks = units * (128 / 16);
+    return chunks <= 0xffffffffLL / 512 && col_blocks <= 0xffffffffLL / 1024;
 }
 
 lt2_status check_desc(const lt2_gdn_desc *d, bool decode) {
@@ -41,7 +42,7 @@ lt2_status check_desc(const lt2_gdn_desc *d, bool decode) {
     // grid dimensions must fit their 32-bit and 65535 limits
     if ((int64_t)d->B * d->H > 0x7fffffffLL) return LT2_ERR_SHAPE;
     if (!decode && (d->H > 65535 || d->B > 65535)) return LT2_ERR_SHAPE;
-    if (!launch_fits((int64_t)d->B * d->H, decode ? 1 : d->L, decode ? 1 : d->chunk, !decode)) return LT2_ERR_SHAPE;
+    if (!launch_fits((int64_t)d->B * d->H, d->L, decode ? 1 : d->chunk, decode)) return LT2_ERR_SHAPE;
     return LT2_OK;
 }
 
@@ -176,8 +177,8 @@ lt2_status lt2_gdn_backward(const lt2_gdn_desc *desc, const void *q, const void 
         return LT2_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_out, 16) || !aligned(dq, 16) ||
         !aligned(dk, 16) || !aligned(dv, 16) || !aligned(state_in, 16) || !aligned(d_state_out, 16) ||
-        !aligned(d_state_in, 16) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(dlog_alpha, 4) ||
-        !aligned(dbeta, 4))
+        !aligned(d_state_in, 16) || !aligned(alpha, channel ? 16 : 4) || !aligned(beta, 4) ||
+        !aligned(dlog_alpha, 4) || !aligned(dbeta, 4))
         return LT2_ERR_ALIGN;
     const size_t need = !work ? 0
                         : channel ? kda_bwd_ws_bytes(desc->B, desc->L, desc->H, desc->d_k)

@@ -17,15 +17,19 @@
 // the work splits over column blocks; the row quantities dq, dk, d(log alpha)
 // and dbeta sum over all columns.
 //
-// One workgroup of 8 waves per (b, h, 16-column block); each wave owns 2 state
-// columns and every row (lane l: rows RPL l .. RPL l + RPL - 1, RPL = d/64), so
-// sums over rows are wave reductions.  The workgroup first runs the recurrence
-// forward and stores the state entering every segment of 16 tokens; then, for
-// the segments in reverse order, it recomputes the segment's 17 states into
-// registers and walks its tokens backwards.  Per token the row quantities of
-// the workgroup's 16 columns are summed in LDS (float atomics from the 8
-// waves) and written once per segment to a partial buffer per column block,
-// which a second kernel sums.  Inputs of a segment are staged in LDS as fp32.
+// One workgroup of 8 waves per (b, h, 16-column block); each wave owns two
+// state columns and every row (lane l: rows RPL l .. RPL l + RPL - 1, RPL =
+// d/64), so sums over rows are wave reductions in registers (DPP and row
+// swaps) and sums over the wave's columns stay in its lanes.  The workgroup
+// first runs the recurrence forward and stores the state entering every
+// segment of 16 tokens.  Then, for the segments in reverse order and each
+// segment's two halves of 8 tokens (second half first), it recomputes the
+// half's 9 states into registers from the segment's checkpoint and walks its
+// tokens backwards, keeping the row quantities of its columns in registers;
+// the eight waves' sums are then added through LDS (one write and one read per
+// value) and written to a partial buffer per column block, which a second
+// kernel sums.  Inputs of a segment are staged in LDS as fp32 with 16-byte
+// loads issued one segment ahead.
 #include "common.h"
 #include "internal.h"
 
@@ -34,6 +38,7 @@ namespace lt2 {
 namespace {
 
 constexpr int KS = 16;               // segment (checkpoint interval) in tokens
+constexpr int HS = KS / 2;           // tokens per backward half-segment
 constexpr int KCOL = 2;              // state columns per wave
 constexpr int KW = 8;                // waves per workgroup
 constexpr int KBV = KCOL * KW;       // columns per workgroup
@@ -53,18 +58,53 @@ KdaLayout kda_layout(int B, int L, int H, int d) {
     return w;
 }
 
+// Sum over the 64 lanes, in registers: DPP within rows of 16 lanes (pairs,
+// quads, mirrored half rows, mirrored rows), then the row-swap permutes.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    x += dppf<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dppf<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dppf<0x141>(x);   // row_half_mirror
+    x += dppf<0x140>(x);   // row_mirror
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
+// KCOL consecutive floats (8- or 16-byte aligned)
+__device__ __forceinline__ void ld_cols(const float *p, float (&x)[KCOL]) {
+#pragma unroll
+    for (int j = 0; j < KCOL; j += 2) {
+        const float2 t = *reinterpret_cast<const float2 *>(p + j);
+        x[j] = t.x;
+        x[j + 1] = t.y;
+    }
+}
+__device__ __forceinline__ void st_cols(float *p, const float (&x)[KCOL]) {
+#pragma unroll
+    for (int j = 0; j < KCOL; j += 2) *reinterpret_cast<float2 *>(p + j) = make_float2(x[j], x[j + 1]);
+}
+
+// 16 bytes of T -> fp32 values (8 bf16 or 4 fp32)
 template <typename T>
-__device__ __forceinline__ float ld1(const T *p);
-template <>
-__device__ __forceinline__ float ld1<float>(const float *p) { return *p; }
-template <>
-__device__ __forceinline__ float ld1<uint16_t>(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+struct Piece {
+    static constexpr int N = 16 / (int)sizeof(T);
+};
+__device__ __forceinline__ void widen(const u32x4 u, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void widen(const u32x4 u, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(u[i]);
+}
 
 template <int D, typename TI, typename TO>
 __global__ __launch_bounds__(KNT) void kda_bwd_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
@@ -74,54 +114,121 @@ __global__ __launch_bounds__(KNT) void kda_bwd_kernel(const TI *__restrict__ q, 
                                                        float *__restrict__ dv_out, float *dstate_in,
                                                        float *__restrict__ ck, float *__restrict__ part, int B, int L,
                                                        int H) {
-    constexpr int RPL = D / 64;      // rows per lane
+    constexpr int RPL = D / 64;                  // rows per lane
     constexpr int NCB = D / KBV;
-    __shared__ float sk[KS][D], sq[KS][D], sa[KS][D];
-    __shared__ float sv[KS][KBV], sd[KS][KBV], sb[KS];
-    __shared__ float acc[KS][3][D];  // per token of the segment: dq, dk, d(log alpha) row sums
-    __shared__ float accb[KS];
+    constexpr int EI = Piece<TI>::N, EO = Piece<TO>::N;
+    constexpr int PK = KS * D / EI;              // 16-byte pieces of a segment's k (and q)
+    constexpr int PA = KS * D / 4;               // ... of its alpha
+    constexpr int PV = KS * KBV / EI;            // ... of the block's v columns
+    constexpr int PD = KS * KBV / EO;            // ... of the block's dO columns
+    constexpr int NPK = (PK + KNT - 1) / KNT, NPA = (PA + KNT - 1) / KNT;
+    static_assert(PV + PD + KS / 4 <= KNT, "one small piece per thread");
+    __shared__ __attribute__((aligned(16))) float sk[2][KS][D], sq[2][KS][D], sa[2][KS][D];
+    __shared__ __attribute__((aligned(16))) float sv[2][KS][KBV], sd[2][KS][KBV], sb[2][KS];
+    __shared__ float red[KW][HS][3][D];          // each wave's row sums of a half-segment: dq, dk, d(log alpha)
+    __shared__ float redb[KW][HS];               // ... and its dbeta
 
     const int cb = blockIdx.x % NCB;
     const size_t unit = blockIdx.x / NCB;
     const int h = (int)(unit % H), b = (int)(unit / H);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cw = KCOL * wave;              // this wave's first column inside the block
-    const int c0 = cb * KBV + cw;            // ... in the state
-    const int r0 = RPL * lane;               // this lane's first row
+    const int cw = KCOL * wave;                  // this wave's first column inside the block
+    const int c0 = cb * KBV + cw;                // ... in the state
+    const int r0 = RPL * lane;                   // this lane's first row
     const int NS = (L + KS - 1) / KS;
     const size_t n_tok = (size_t)B * L * H;
     float *ckp = ck + unit * (size_t)NS * D * D;
 
     auto tok_of = [&](int t) __attribute__((always_inline)) { return ((size_t)b * L + t) * H + h; };
-    // Inputs of tokens t0 .. t0 + KS - 1 (rows past L: k = q = 0, alpha = 1, beta = 0, v = dO = 0).
-    auto stage = [&](int t0) __attribute__((always_inline)) {
-        for (int idx = tid; idx < KS * D; idx += KNT) {
-            const int tt = idx / D, c = idx % D, t = t0 + tt;
-            const bool ok = t < L;
-            const size_t o = tok_of(ok ? t : 0) * D + c;
-            sk[tt][c] = ok ? ld1<TI>(k + o) : 0.f;
-            sq[tt][c] = ok ? ld1<TI>(q + o) : 0.f;
-            sa[tt][c] = ok ? alpha[o] : 1.f;
+
+    // ---- segment inputs: 16-byte loads into registers, then fp32 into LDS ----
+    // (tokens past L: k = q = 0, alpha = 1, beta = 0, v = dO = 0)
+    u32x4 rk[NPK], rq[NPK], ra[NPA], rvd = {};
+    auto fetch = [&](int s) __attribute__((always_inline)) {
+        const int t0 = s * KS;
+#pragma unroll
+        for (int m = 0; m < NPK; ++m) {
+            const int p = min(tid + KNT * m, PK - 1);
+            const int tt = p / (D / EI), c = (p % (D / EI)) * EI;
+            const size_t o = tok_of(min(t0 + tt, L - 1)) * D + c;
+            rk[m] = *reinterpret_cast<const u32x4 *>(k + o);
+            rq[m] = *reinterpret_cast<const u32x4 *>(q + o);
         }
-        for (int idx = tid; idx < KS * KBV; idx += KNT) {
-            const int tt = idx / KBV, c = idx % KBV, t = t0 + tt;
-            const bool ok = t < L;
-            const size_t o = tok_of(ok ? t : 0) * D + cb * KBV + c;
-            sv[tt][c] = ok ? ld1<TI>(v + o) : 0.f;
-            sd[tt][c] = ok ? ld1<TO>(dout + o) : 0.f;
+#pragma unroll
+        for (int m = 0; m < NPA; ++m) {
+            const int p = min(tid + KNT * m, PA - 1);
+            const int tt = p / (D / 4), c = (p % (D / 4)) * 4;
+            ra[m] = *reinterpret_cast<const u32x4 *>(alpha + tok_of(min(t0 + tt, L - 1)) * D + c);
         }
-        if (tid < KS) {
-            const int t = t0 + tid;
-            sb[tid] = t < L ? beta[tok_of(t)] : 0.f;
+        if (tid < PV) {
+            const int tt = tid / (KBV / EI), c = (tid % (KBV / EI)) * EI;
+            rvd = *reinterpret_cast<const u32x4 *>(v + tok_of(min(t0 + tt, L - 1)) * D + cb * KBV + c);
+        } else if (tid < PV + PD) {
+            const int p = tid - PV, tt = p / (KBV / EO), c = (p % (KBV / EO)) * EO;
+            rvd = *reinterpret_cast<const u32x4 *>(dout + tok_of(min(t0 + tt, L - 1)) * D + cb * KBV + c);
+        } else if (tid < PV + PD + KS / 4) {
+            const int p = tid - PV - PD;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rvd[e] = __float_as_uint(beta[tok_of(min(t0 + 4 * p + e, L - 1))]);
         }
     };
-    // One forward token on the wave's state slice; returns y = S^T k (in y).
-    auto step = [&](float (&S)[RPL][KCOL], float (&y)[KCOL], int tt) __attribute__((always_inline)) {
+    auto stage = [&](int s, int buf) __attribute__((always_inline)) {
+        const int t0 = s * KS;
+#pragma unroll
+        for (int m = 0; m < NPK; ++m) {
+            const int p = tid + KNT * m;
+            if (p < PK) {
+                const int tt = p / (D / EI), c = (p % (D / EI)) * EI;
+                const bool ok = t0 + tt < L;
+                float fk[EI], fq[EI];
+                widen(rk[m], fk);
+                widen(rq[m], fq);
+#pragma unroll
+                for (int e = 0; e < EI; ++e) {
+                    sk[buf][tt][c + e] = ok ? fk[e] : 0.f;
+                    sq[buf][tt][c + e] = ok ? fq[e] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NPA; ++m) {
+            const int p = tid + KNT * m;
+            if (p < PA) {
+                const int tt = p / (D / 4), c = (p % (D / 4)) * 4;
+                const bool ok = t0 + tt < L;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sa[buf][tt][c + e] = ok ? __uint_as_float(ra[m][e]) : 1.f;
+            }
+        }
+        if (tid < PV) {
+            const int tt = tid / (KBV / EI), c = (tid % (KBV / EI)) * EI;
+            const bool ok = t0 + tt < L;
+            float f[EI];
+            widen(rvd, f);
+#pragma unroll
+            for (int e = 0; e < EI; ++e) sv[buf][tt][c + e] = ok ? f[e] : 0.f;
+        } else if (tid < PV + PD) {
+            const int p = tid - PV, tt = p / (KBV / EO), c = (p % (KBV / EO)) * EO;
+            const bool ok = t0 + tt < L;
+            float f[EO];
+            widen(rvd, f);
+#pragma unroll
+            for (int e = 0; e < EO; ++e) sd[buf][tt][c + e] = ok ? f[e] : 0.f;
+        } else if (tid < PV + PD + KS / 4) {
+            const int p = tid - PV - PD;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sb[buf][4 * p + e] = (t0 + 4 * p + e < L) ? __uint_as_float(rvd[e]) : 0.f;
+        }
+    };
+    // One forward token on the wave's state columns; y = S^T k of the old state.
+    auto step = [&](float (&S)[RPL][KCOL], float (&y)[KCOL], int buf, int tt) __attribute__((always_inline)) {
         float kr[RPL], ar[RPL];
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) { kr[i] = sk[tt][r0 + i]; ar[i] = sa[tt][r0 + i]; }
-        const float bt = sb[tt];
+        for (int i = 0; i < RPL; ++i) { kr[i] = sk[buf][tt][r0 + i]; ar[i] = sa[buf][tt][r0 + i]; }
+        const float bt = sb[buf][tt];
+        float v4[KCOL];
+        ld_cols(&sv[buf][tt][cw], v4);
 #pragma unroll
         for (int j = 0; j < KCOL; ++j) {
             float p = 0.f;
@@ -130,13 +237,10 @@ __global__ __launch_bounds__(KNT) void kda_bwd_kernel(const TI *__restrict__ q, 
             y[j] = wave_sum(p);
         }
 #pragma unroll
-        for (int j = 0; j < KCOL; ++j) {
-            const float vj = sv[tt][cw + j];
+        for (int i = 0; i < RPL; ++i) {
+            const float bk = bt * kr[i];
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                const float bk = bt * kr[i];
-                S[i][j] = ar[i] * (S[i][j] - bk * y[j]) + bk * vj;
-            }
+            for (int j = 0; j < KCOL; ++j) S[i][j] = ar[i] * (S[i][j] - bk * y[j]) + bk * v4[j];
         }
     };
 
@@ -146,115 +250,161 @@ __global__ __launch_bounds__(KNT) void kda_bwd_kernel(const TI *__restrict__ q, 
     for (int i = 0; i < RPL; ++i)
 #pragma unroll
         for (int j = 0; j < KCOL; ++j) S[i][j] = state_in ? state_in[(unit * D + r0 + i) * D + c0 + j] : 0.f;
+    fetch(0);
+    stage(0, 0);
+    __syncthreads();
     for (int s = 0; s < NS; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < NS) fetch(s + 1);
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
-#pragma unroll
-            for (int j = 0; j < KCOL; ++j) ckp[((size_t)s * D + r0 + i) * D + c0 + j] = S[i][j];
-        __syncthreads();   // the previous segment's inputs are no longer read
-        stage(s * KS);
-        __syncthreads();
+        for (int i = 0; i < RPL; ++i) st_cols(&ckp[((size_t)s * D + r0 + i) * D + c0], S[i]);
         const int n = min(KS, L - s * KS);
         for (int tt = 0; tt < n; ++tt) {
             float y[KCOL];
-            step(S, y, tt);
+            step(S, y, buf, tt);
         }
+        if (s + 1 < NS) stage(s + 1, buf ^ 1);
+        __syncthreads();
     }
 
-    // ---- backward, segments in reverse ----
+    // ---- backward, segments in reverse, each in two halves (second half first) ----
     float G[RPL][KCOL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
 #pragma unroll
         for (int j = 0; j < KCOL; ++j) G[i][j] = dstate_out ? dstate_out[(unit * D + r0 + i) * D + c0 + j] : 0.f;
-    for (int s = NS - 1; s >= 0; --s) {
+    fetch(NS - 1);
+    stage(NS - 1, 0);
+    __syncthreads();
+    float *pb = part + (size_t)cb * (3 * n_tok * D + n_tok);
+    for (int jseg = 0; jseg < NS; ++jseg) {
+        const int s = NS - 1 - jseg, buf = jseg & 1;
         const int t0 = s * KS;
         const int n = min(KS, L - t0);
-        __syncthreads();   // the previous segment's inputs and sums have been read
-        stage(t0);
-        for (int idx = tid; idx < KS * 3 * D; idx += KNT) (&acc[0][0][0])[idx] = 0.f;
-        if (tid < KS) accb[tid] = 0.f;
-        __syncthreads();
-        // states before each token of the segment and after its last: Sx[tt] = S_{t0+tt-1}
-        float Sx[KS + 1][RPL][KCOL], yy[KS][KCOL];
+        if (s > 0) fetch(s - 1);
+        for (int half = 1; half >= 0; --half) {
+            const int u0 = HS * half;             // first token of the half inside the segment
+            const int nh = min(HS, n - u0);       // its tokens (may be <= 0 for a ragged last segment)
+            if (nh > 0) {
+                // the state entering the half: the checkpoint advanced by u0 tokens
+                float Sx[HS + 1][RPL][KCOL], yy[HS][KCOL];
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
-#pragma unroll
-            for (int j = 0; j < KCOL; ++j) Sx[0][i][j] = ckp[((size_t)s * D + r0 + i) * D + c0 + j];
-#pragma unroll
-        for (int tt = 0; tt < KS; ++tt) {
-#pragma unroll
-            for (int i = 0; i < RPL; ++i)
-#pragma unroll
-                for (int j = 0; j < KCOL; ++j) Sx[tt + 1][i][j] = Sx[tt][i][j];
-            if (tt < n) step(Sx[tt + 1], yy[tt], tt);
-        }
-#pragma unroll
-        for (int tt = KS - 1; tt >= 0; --tt) {
-            if (tt >= n) continue;
-            float kr[RPL], qr[RPL], ar[RPL], vj[KCOL], dj[KCOL];
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) { kr[i] = sk[tt][r0 + i]; qr[i] = sq[tt][r0 + i]; ar[i] = sa[tt][r0 + i]; }
-#pragma unroll
-            for (int j = 0; j < KCOL; ++j) { vj[j] = sv[tt][cw + j]; dj[j] = sd[tt][cw + j]; }
-            const float bt = sb[tt];
-            float dE[RPL][KCOL], red[2 * KCOL + 1];
-            float dq_[RPL], dla[RPL], gv[RPL];
-#pragma unroll
-            for (int j = 0; j < 2 * KCOL + 1; ++j) red[j] = 0.f;
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                dq_[i] = 0.f; dla[i] = 0.f; gv[i] = 0.f;
-                const float bk = bt * kr[i];
-#pragma unroll
-                for (int j = 0; j < KCOL; ++j) {
-                    G[i][j] += qr[i] * dj[j];
-                    dq_[i] += Sx[tt + 1][i][j] * dj[j];
-                    // E = S_{t-1} - beta k y^T: exact zero gradient for alpha = 0 and no
-                    // cancellation for small alpha (unlike S_t - beta k v^T = alpha E)
-                    dla[i] += G[i][j] * (Sx[tt][i][j] - bk * yy[tt][j]);
-                    dE[i][j] = ar[i] * G[i][j];
-                    gv[i] += G[i][j] * vj[j];
-                    red[j] += dE[i][j] * kr[i];              // z_j
-                    red[KCOL + j] += G[i][j] * kr[i];        // dv_j / beta
-                    red[2 * KCOL] += kr[i] * (G[i][j] * vj[j] - dE[i][j] * yy[tt][j]);   // dbeta
+                for (int i = 0; i < RPL; ++i) ld_cols(&ckp[((size_t)s * D + r0 + i) * D + c0], Sx[0][i]);
+                for (int tt = 0; tt < u0; ++tt) {
+                    float y[KCOL];
+                    step(Sx[0], y, buf, tt);
                 }
-                dla[i] *= ar[i];
-            }
 #pragma unroll
-            for (int j = 0; j < 2 * KCOL + 1; ++j) red[j] = wave_sum(red[j]);
+                for (int u = 0; u < HS; ++u) {
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                float dk_ = gv[i];
+                    for (int i = 0; i < RPL; ++i)
 #pragma unroll
-                for (int j = 0; j < KCOL; ++j) {
-                    dk_ -= Sx[tt][i][j] * red[j] + dE[i][j] * yy[tt][j];
-                    G[i][j] = dE[i][j] - bt * kr[i] * red[j];
+                        for (int j = 0; j < KCOL; ++j) Sx[u + 1][i][j] = Sx[u][i][j];
+#pragma unroll
+                    for (int j = 0; j < KCOL; ++j) yy[u][j] = 0.f;
+                    if (u < nh) step(Sx[u + 1], yy[u], buf, u0 + u);
                 }
-                atomicAdd(&acc[tt][0][r0 + i], dq_[i]);
-                atomicAdd(&acc[tt][1][r0 + i], bt * dk_);
-                atomicAdd(&acc[tt][2][r0 + i], dla[i]);
+                float rq_[HS][RPL], rk_[HS][RPL], ra_[HS][RPL], rb_[HS];
+#pragma unroll
+                for (int u = HS - 1; u >= 0; --u) {
+                    if (u >= nh) {
+#pragma unroll
+                        for (int i = 0; i < RPL; ++i) { rq_[u][i] = 0.f; rk_[u][i] = 0.f; ra_[u][i] = 0.f; }
+                        rb_[u] = 0.f;
+                        continue;
+                    }
+                    const int tt = u0 + u;
+                    float kr[RPL], qr[RPL], ar[RPL];
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) {
+                        kr[i] = sk[buf][tt][r0 + i]; qr[i] = sq[buf][tt][r0 + i]; ar[i] = sa[buf][tt][r0 + i];
+                    }
+                    float v4[KCOL], d4[KCOL];
+                    ld_cols(&sv[buf][tt][cw], v4);
+                    ld_cols(&sd[buf][tt][cw], d4);
+                    const float bt = sb[buf][tt];
+                    float dE[RPL][KCOL], zp[KCOL], gkp[KCOL], dbp = 0.f;
+#pragma unroll
+                    for (int j = 0; j < KCOL; ++j) { zp[j] = 0.f; gkp[j] = 0.f; }
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) {
+                        float dq_ = 0.f, dla = 0.f, gv = 0.f, dey = 0.f;
+#pragma unroll
+                        for (int j = 0; j < KCOL; ++j) {
+                            G[i][j] += qr[i] * d4[j];
+                            dq_ += Sx[u + 1][i][j] * d4[j];
+                            // E = S_{t-1} - beta k y: exact zero gradient for alpha = 0 and
+                            // no cancellation for small alpha (unlike S_t - beta k v = alpha E)
+                            dla += G[i][j] * (Sx[u][i][j] - bt * kr[i] * yy[u][j]);
+                            dE[i][j] = ar[i] * G[i][j];
+                            gv += G[i][j] * v4[j];
+                            dey += dE[i][j] * yy[u][j];
+                            zp[j] += dE[i][j] * kr[i];
+                            gkp[j] += G[i][j] * kr[i];
+                        }
+                        rq_[u][i] = dq_;
+                        ra_[u][i] = ar[i] * dla;
+                        rk_[u][i] = gv - dey;             // the S_{t-1} z term is added below
+                        dbp += kr[i] * (gv - dey);
+                    }
+                    float z[KCOL], gk[KCOL];
+#pragma unroll
+                    for (int j = 0; j < KCOL; ++j) { z[j] = wave_sum(zp[j]); gk[j] = wave_sum(gkp[j]); }
+                    rb_[u] = wave_sum(dbp);
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) {
+                        float sz = 0.f;
+#pragma unroll
+                        for (int j = 0; j < KCOL; ++j) {
+                            sz += Sx[u][i][j] * z[j];
+                            G[i][j] = dE[i][j] - bt * kr[i] * z[j];
+                        }
+                        rk_[u][i] = bt * (rk_[u][i] - sz);
+                    }
+                    if (lane < KCOL) {
+                        float g = gk[0];
+#pragma unroll
+                        for (int j = 1; j < KCOL; ++j) g = lane == j ? gk[j] : g;
+                        dv_out[tok_of(t0 + tt) * D + c0 + lane] = bt * g;
+                    }
+                }
+                // this wave's row sums of the half -> LDS
+#pragma unroll
+                for (int u = 0; u < HS; ++u) {
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) {
+                        red[wave][u][0][r0 + i] = rq_[u][i];
+                        red[wave][u][1][r0 + i] = rk_[u][i];
+                        red[wave][u][2][r0 + i] = ra_[u][i];
+                    }
+                    if (lane == 0) redb[wave][u] = rb_[u];
+                }
             }
-            if (lane == 0) atomicAdd(&accb[tt], red[2 * KCOL]);
-            if (lane < KCOL) {
-                const float dvv = bt * (lane == 0 ? red[KCOL] : red[KCOL + 1]);
-                dv_out[tok_of(t0 + tt) * D + c0 + lane] = dvv;
+            __syncthreads();
+            // the waves' sums of the half -> this block's partial buffer
+            if (nh > 0) {
+                for (int idx = tid; idx < nh * 3 * D; idx += KNT) {
+                    const int u = idx / (3 * D), rem = idx % (3 * D), qd = rem / D, c = rem % D;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < KW; ++w) sum += red[w][u][qd][c];
+                    pb[(size_t)qd * n_tok * D + tok_of(t0 + u0 + u) * D + c] = sum;
+                }
+                if (tid < nh) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < KW; ++w) sum += redb[w][tid];
+                    pb[3 * n_tok * D + tok_of(t0 + u0 + tid)] = sum;
+                }
             }
+            __syncthreads();
         }
+        if (s > 0) stage(s - 1, buf ^ 1);
         __syncthreads();
-        // this block's partial row sums of the segment's tokens
-        float *pb = part + (size_t)cb * (3 * n_tok * D + n_tok);
-        for (int idx = tid; idx < n * 3 * D; idx += KNT) {
-            const int tt = idx / (3 * D), rem = idx % (3 * D), qd = rem / D, c = rem % D;
-            pb[(size_t)qd * n_tok * D + tok_of(t0 + tt) * D + c] = acc[tt][qd][c];
-        }
-        if (tid < n) pb[3 * n_tok * D + tok_of(t0 + tid)] = accb[tid];
     }
     if (dstate_in) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
-#pragma unroll
-            for (int j = 0; j < KCOL; ++j) dstate_in[(unit * D + r0 + i) * D + c0 + j] = G[i][j];
+        for (int i = 0; i < RPL; ++i) st_cols(&dstate_in[(unit * D + r0 + i) * D + c0], G[i]);
     }
 }
 

@@ -90,7 +90,7 @@ int main(void) {
         d.L = 1;
         EXPECT(lt2_gdn_decode_step(&d, F, F, F, F, F, NULL, F, NULL), LT2_ERR_NULL);
         EXPECT(lt2_gdn_decode_step(&d, F, F, F, F, F, F, FM, NULL), LT2_ERR_ALIGN);
-        d.B = 8192; d.H = 1024;
+        d.B = 16384; d.H = 1024;
         EXPECT(lt2_gdn_decode_step(&d, F, F, F, F, F, F, F, NULL), LT2_ERR_SHAPE);
         d.B = 0;
         EXPECT(lt2_gdn_decode_step(&d, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL), LT2_OK);

@@ -79,8 +79,8 @@ def test_launch_size_limits_are_checked_before_enqueue():
     assert prefill(big) == 2
     assert lt2.lt2_gdn_prefill_workspace_size(big) == 0
     assert bwd_call(big) == 2
-    assert decode(good_desc(B=8192, H=1024, L=1)) == 2
-    assert decode(good_desc(B=8191, H=1024, L=1), s=None) == 1      # just inside: reaches the pointer checks
+    assert decode(good_desc(B=16384, H=1024, L=1)) == 2
+    assert decode(good_desc(B=16383, H=1024, L=1), s=None) == 1     # just inside: reaches the pointer checks
     assert loop_call(good_loop(B=4096, L=1 << 19, H=2, chunk=16)) == 2
 
 
