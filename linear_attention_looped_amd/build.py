@@ -34,6 +34,13 @@ def cflags() -> list[str]:
             "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source extra flags.  prefill_head.hip: matrix-core accumulators in
+# ordinary VGPRs (its kernels fit in 256 of them): the column-tile scan feeds
+# every accumulator tile to vector ALU work, and AGPR accumulators cost a copy
+# instruction per register each way.
+FILE_FLAGS = {"prefill_head.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -45,7 +52,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-        cmd = [cc, *cflags(), "-c", src, "-o", obj]
+        cmd = [cc, *cflags(), *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -248,17 +248,20 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
+// Two fp32 values -> packed bf16 hi = bf16(x) and lo = bf16(x - hi), both
+// rounded to nearest even; one two-value conversion instruction per pair.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    typedef __attribute__((ext_vector_type(2))) float f2_t;
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2_t;
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
+    const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xFFFF0000u);
+    hi = h;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a - ha, b - hb}, b2_t));
+}
 // Four fp32 values -> bf16 hi and lo = bf16(x - hi), each packed in a uint2.
 __device__ __forceinline__ void split4(const float x[4], uint2 &hi, uint2 &lo) {
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 hb = (__bf16)x[i];
-        h[i] = __builtin_bit_cast(uint16_t, hb);
-        l[i] = bf16_bits(x[i] - (float)hb);
-    }
-    hi = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-    lo = make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
 }
 // Eight fp32 values -> bf16 hi and lo, each packed in a uint4.
 __device__ __forceinline__ void split8(const float x[8], uint4 &hi, uint4 &lo) {

@@ -27,7 +27,11 @@ namespace lt2 {
 //   fp32 inputs: Tm [C][C] f32 | P [C][C] f32 | g, 2^g, 2^(g_C - g) [C] f32
 //   bf16 inputs: Tm hi, Tm lo, P hi, P lo [C][C] bf16 | g, 2^g, 2^(g_C - g) [C] f32
 // (hi = bf16(x), lo = bf16(x - hi): the scan feeds them to bf16 matrix cores
-// without converting).  Tm and P are zero above the diagonal.
+// without converting).  Tm and P are zero above the diagonal.  With C = 64
+// the bf16 factors are stored in MFMA A-fragment order instead (FragLayout):
+// for matrix m (Tm, P), 16-row tile w, K-block kb of 32 and half (hi, lo), one
+// KiB holding lane l's eight bf16 A[16w + l%16][32kb + 8(l/16) + 0..7] at
+// 16 l, so a wave reads its fragments with one contiguous KiB load each.
 // ---------------------------------------------------------------------------
 // One 32-wide k block of a product of two input fragments (eight consecutive
 // elements per lane, the common.h fragment layout).  bf16 inputs on the bf16
@@ -44,6 +48,25 @@ __device__ __forceinline__ void gram_mma(f32x4 &acc, const Raw8<TI> &a, const Ra
         mma<PREC, true, true>(acc, fa, fb);
     }
 }
+
+// Fragment-ordered layout of a C = 64 chunk's Tm and P.  frag(m, hl, I, kb) is
+// the byte offset of the 1 KiB fragment of matrix m (0 Tm, 1 P), half hl (0 hi,
+// 1 lo), row tile I and K-block kb; off(m, hl, t, c0) that of the 16-byte piece
+// holding A[t][c0 .. c0+7].  Lane i + 16 g of a fragment holds row 16 I + i and
+// the eight columns 32 kb + 8 gperm(g) + 0..7, gperm(g) = (0, 2, 1, 3): the
+// token order of the B operands the scan regroups from accumulator tiles.
+template <int C>
+struct FragLayout {
+    static constexpr bool on = C == 64;
+    static constexpr int NKB = C / 32, NT = C / 16;
+    __host__ __device__ static constexpr int gperm(int x) { return ((x & 1) << 1) | (x >> 1); }
+    __host__ __device__ static constexpr int frag(int m, int hl, int I, int kb) {
+        return (((m * NT + I) * NKB + kb) * 2 + hl) << 10;
+    }
+    __host__ __device__ static constexpr int off(int m, int hl, int t, int c0) {
+        return frag(m, hl, t / 16, c0 / 32) + (16 * gperm((c0 % 32) / 8) + t % 16) * 16;
+    }
+};
 
 template <int DK, int C, int PREC, typename TI>
 __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
@@ -247,6 +270,15 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
             *reinterpret_cast<float4 *>(Tg + t * C + i0 + 4) = make_float4(tv[4], tv[5], tv[6], tv[7]);
             *reinterpret_cast<float4 *>(Pg + t * C + i0) = make_float4(pv[0], pv[1], pv[2], pv[3]);
             *reinterpret_cast<float4 *>(Pg + t * C + i0 + 4) = make_float4(pv[4], pv[5], pv[6], pv[7]);
+        } else if constexpr (FragLayout<C>::on) {
+            using FLY = FragLayout<C>;
+            uint4 hi, lo;
+            split8(tv, hi, lo);
+            *reinterpret_cast<uint4 *>(wsu + FLY::off(0, 0, t, i0)) = hi;
+            *reinterpret_cast<uint4 *>(wsu + FLY::off(0, 1, t, i0)) = lo;
+            split8(pv, hi, lo);
+            *reinterpret_cast<uint4 *>(wsu + FLY::off(1, 0, t, i0)) = hi;
+            *reinterpret_cast<uint4 *>(wsu + FLY::off(1, 1, t, i0)) = lo;
         } else {
             uint16_t *Th = reinterpret_cast<uint16_t *>(wsu);
             uint4 hi, lo;
@@ -710,8 +742,17 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
 #pragma unroll
     for (int i = 0; i < FL; ++i) {
         const int idx = min(tid + NTH * i, NF - 1);
-        const int arr = idx / (C * C / 8), rem = idx % (C * C / 8);
-        fl[i] = arr * C * CP + (rem / (C / 8)) * CP + 8 * (rem % (C / 8));
+        if constexpr (FragLayout<C>::on) {
+            // piece idx of the fragment-ordered layout: (matrix, tile, K-block, half), lane
+            using FLY = FragLayout<C>;
+            const int frag = idx / 64, l = idx % 64;
+            const int hl = frag % 2, kb = (frag / 2) % FLY::NKB, w = (frag / (2 * FLY::NKB)) % (C / 16);
+            const int m = frag / (2 * FLY::NKB * (C / 16));
+            fl[i] = (2 * m + hl) * C * CP + (16 * w + l % 16) * CP + 32 * kb + 8 * FLY::gperm(l / 16);
+        } else {
+            const int arr = idx / (C * C / 8), rem = idx % (C * C / 8);
+            fl[i] = arr * C * CP + (rem / (C / 8)) * CP + 8 * (rem % (C / 8));
+        }
     }
     const int gidx = min(lane, NG - 1);
     const int orow = min(tid, NO - 1) / (BV / OV), ocol = OV * (min(tid, NO - 1) % (BV / OV));
@@ -951,9 +992,366 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
     }
 }
 
+// ---------------------------------------------------------------------------
+// Scan, bf16 inputs, d = 128, C = 64: one wave per 16-column tile of the state.
+// A workgroup owns NWV adjacent column tiles of one (b, h) unit with NWV
+// compute waves and NWV loader waves (one wave per SIMD).  Each compute wave
+// keeps its 128 x 16 state slice in eight 16x16 accumulator tiles and carries
+// the whole chunk recurrence for its columns in registers:
+//   X_K = K S, X_Q = Q S       B = the state itself: accumulator tiles 2kb and
+//                              2kb + 1 exchanged by v_permlane16_swap give lane
+//                              group g the state rows 32kb + 8p(g) + 0..7, with
+//                              p(g) = (0, 2, 1, 3); the A operands (K, Q rows)
+//                              are read at the same columns.  S split hi/lo.
+//   R = V - 2^g X_K            the same exchange turns the four token tiles of R
+//   U = Tm R                   (and of U, U2) into B operands over the tokens;
+//   O = 2^g X_Q + P U          Tm and P come from the workspace as A fragments
+//   S = 2^gC S + K^T U2        whose K-columns follow the same order p(g);
+//                              K^T by LDS transpose reads of the K rows.
+// The compute waves exchange nothing through LDS and issue no loads: the
+// loader waves copy the chunk's read-only operands (K, Q, the lower Tm and P
+// fragments, the workgroup's V and gate columns, the decay vectors) from
+// global memory straight into LDS (buffer_load ... lds, no registers) one
+// chunk ahead into a second buffer, so the copies' issue cost and latency stay
+// off the recurrence.  Outputs are held in registers over the next chunk's
+// barrier and stored by bounds-checked buffer stores, so the rows of a ragged
+// last chunk past L are dropped by the hardware and every compute wave runs the
+// same straight-line code.
+// ---------------------------------------------------------------------------
+// 16-byte block swizzle of the K and Q rows in LDS (rows of 256 bytes, no
+// padding, so that a wave's 1 KiB LDS copy fills four whole rows): block b of
+// row r sits at block b ^ col_swz(r).  On the 16 rows of a fragment read (one
+// block per row) it is a bijection; on the transposed reads of K (rows
+// 8p + e and 16 + 8p + e, e < 4, two blocks each) the eight rows of a half-wave
+// get eight distinct block pairs.
+__device__ __forceinline__ int col_swz(int r) {
+    const int x = r & 15;
+    return ((x & 8) | ((x & 3) << 1) | ((x >> 2) & 1)) ^ (((r >> 4) & 1) << 3);
+}
+
+// One chunk's operands in LDS (16-bit elements unless stated).
+template <int NWV>
+struct ColChunk {
+    uint16_t K[64 * 128];       // swizzled rows
+    uint16_t Q[64 * 128];       // swizzled rows
+    uint16_t F[24 * 512];       // Tm, P lower-block fragments, 1 KiB each: ((m * 6 + pair) * 2 + hl)
+    uint16_t V[64 * 16 * NWV];  // the workgroup's V columns, row-major
+    uint16_t G[64 * 16 * NWV];  // output-gate values, same layout
+    float E[128];               // 2^g [64] | 2^(gC - g) [64]
+};
+
+// 16 bytes per lane from a buffer into LDS at lds + 16 * lane (lds is
+// wave-uniform), from byte voff + soff; lanes past the buffer's num_records
+// write zeros.  Counted by vmcnt like a load.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Output stores at byte voff + soff; stores past num_records are dropped.
+template <typename TO>
+__device__ __forceinline__ void store_buf(float x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff);
+template <>
+__device__ __forceinline__ void store_buf<uint16_t>(float x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(x), r, (int)voff, (int)soff, 0);
+}
+template <>
+__device__ __forceinline__ void store_buf<float>(float x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, (int)soff, 0);
+}
+
+// Eight fp32 values of two accumulator tiles (rows 4g + r of tile a and tile b)
+// regrouped so that lane group g holds rows 8p(g) + 0..7 of the 32-row pair.
+__device__ __forceinline__ void pair_rows(const f32x4 &a, const f32x4 &b, float x[8]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[r]), __float_as_uint(b[r]), false, false);
+        x[r] = __uint_as_float(sw[0]);
+        x[4 + r] = __uint_as_float(sw[1]);
+    }
+}
+__device__ __forceinline__ void pair_split(const f32x4 &a, const f32x4 &b, bf16x8 &hi, bf16x8 &lo) {
+    float x[8];
+    pair_rows(a, b, x);
+    uint4 h, l;
+    split8(x, h, l);
+    hi = as_bf16x8(h);
+    lo = as_bf16x8(l);
+}
+
+template <int NWV, bool GATE, typename TO>
+__global__ __launch_bounds__(128 * NWV) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                          const uint16_t *__restrict__ v, const unsigned char *__restrict__ ws,
+                          const float *state_in, TO *__restrict__ out, float *state_out, int L, int H, int NC,
+                          const uint16_t *__restrict__ gate) {
+    constexpr int D = 128, C = 64, NB = 8 / NWV;   // workgroups per unit
+    constexpr int WSB = 8 * C * C + 12 * C;
+    constexpr int VW = 16 * NWV;                    // V columns of the workgroup
+    using FLY = FragLayout<C>;
+    static_assert(FLY::on && (NWV == 1 || NWV == 2 || NWV == 4), "column scan layout");
+    __shared__ __attribute__((aligned(16))) ColChunk<NWV> lds0, lds1;
+
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    const int vb = logical % NB;
+    const unsigned unit = logical / NB;
+    const int h = (int)(unit % H), b = (int)(unit / H);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool loader = wave >= NWV;                // waves NWV .. 2 NWV - 1 copy, the others compute
+    const int li = wave - NWV;                      // loader index
+    const int c = lane & 15, g = lane >> 4;
+    const int gp = ((g & 1) << 1) | (g >> 1);       // lane group g holds K-block rows 8 gp .. 8 gp + 7
+    const int vw0 = VW * vb;                        // first V column of the workgroup
+    const int col = vw0 + 16 * wave + c;            // a compute lane's state and output column
+    const unsigned tok = (unsigned)H * D;           // elements between consecutive tokens
+    const size_t base = ((size_t)b * L * H + h) * D;
+    // Buffer views of this unit: rows t >= L lie past num_records, so copies
+    // of a ragged last chunk's missing rows read zeros and its stores there
+    // are dropped.  Zero K, Q, V rows leave the state and the stored outputs
+    // unchanged: Tm has zero rows and columns for them (beta is zero there).
+    const unsigned in_bytes = ((unsigned)(L - 1) * tok + D) * 2u;
+    const __amdgpu_buffer_rsrc_t krs = buf_rsrc(k + base, in_bytes), qrs = buf_rsrc(q + base, in_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(v + base, in_bytes);
+    const __amdgpu_buffer_rsrc_t grs = buf_rsrc(GATE ? gate + base : v + base, in_bytes);
+    const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(ws + (size_t)unit * NC * WSB, (unsigned)NC * WSB);
+    const __amdgpu_buffer_rsrc_t ors = buf_rsrc(out + base, ((unsigned)(L - 1) * tok + D) * (unsigned)sizeof(TO));
+
+    // A loader wave's share of chunk n's copies into cb: piece p = li + NWV i of
+    // each kind (K rows 4p .. 4p + 3 with swizzled blocks, the same Q rows, the
+    // Tm / P fragments of the six lower (tile, K-block) pairs, 1 KiB pieces of
+    // the row-major [64][VW] V and gate images) and, from loader 0, the decay
+    // vectors.
+    auto issue_all = [&](int n, ColChunk<NWV> &cb) __attribute__((always_inline)) {
+        const unsigned sk = (unsigned)(n * C) * tok * 2u;   // byte offset of the chunk's first token
+        const unsigned sw = (unsigned)n * WSB;
+#pragma unroll
+        for (int i = 0; i < 16 / NWV; ++i) {
+            const int p = li + NWV * i, r = 4 * p + g;
+            const unsigned off = (unsigned)r * tok * 2u + 16u * (unsigned)(c ^ col_swz(r));
+            dma16(krs, off, sk, &cb.K[512 * p]);
+            dma16(qrs, off, sk, &cb.Q[512 * p]);
+        }
+#pragma unroll
+        for (int i = 0; i < 24 / NWV; ++i) {
+            const int p = li + NWV * i;
+            const int hl = p & 1, pr = (p >> 1) % 6, m = p / 12;
+            const int I = pr < 2 ? pr : 2 + ((pr - 2) >> 1), kb = pr < 2 ? 0 : (pr & 1);
+            dma16(wrs, 16u * (unsigned)lane, sw + FLY::frag(m, hl, I, kb), &cb.F[512 * p]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int p = li + NWV * i;
+            const int idx = 64 * p + lane, r = idx / (2 * NWV), part = idx % (2 * NWV);
+            const unsigned off = (unsigned)r * tok * 2u + 2u * (unsigned)(vw0 + 8 * part);
+            dma16(vrs, off, sk, &cb.V[512 * p]);
+            if constexpr (GATE) dma16(grs, off, sk, &cb.G[512 * p]);
+        }
+        if (li == 0 && lane < 32) dma16(wrs, 16u * (unsigned)lane, sw + 8 * C * C + 4 * C, cb.E);
+    };
+
+    // Loader waves: chunk n + 1 into the free buffer while the compute waves
+    // work on chunk n (the last chunk copies itself again, unused).  A loader
+    // reaches barrier n only once its copies of chunk n have landed; barrier n
+    // also orders every compute wave's reads of chunk n - 1 before the copies
+    // into that buffer.  Both kinds of wave pass NC barriers.
+    if (loader) {
+        issue_all(0, lds0);
+        for (int n = 0; n < NC; n += 2) {
+            wait_vmem_all();
+            __syncthreads();
+            issue_all(min(n + 1, NC - 1), lds1);
+            if (n + 1 < NC) {
+                wait_vmem_all();
+                __syncthreads();
+                issue_all(min(n + 2, NC - 1), lds0);
+            }
+        }
+        wait_vmem_all();   // the spare copies land before the workgroup ends
+        return;
+    }
+
+    f32x4 S[8];   // S[16 m + 4 g + r][col]
+#pragma unroll
+    for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (state_in) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[m][r] = state_in[((size_t)unit * D + 16 * m + 4 * g + r) * D + col];
+    }
+
+    f32x4 Oh[4];   // gated outputs of the previous chunk, rows 16 I + 4 g + r
+    const unsigned ovo = ((unsigned)(4 * g) * tok + (unsigned)col) * (unsigned)sizeof(TO);
+    auto store_tile = [&](int n, int I) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            store_buf<TO>(Oh[I][r], ors, ovo, (unsigned)(n * C + 16 * I + r) * tok * (unsigned)sizeof(TO));
+    };
+
+    auto compute = [&](const ColChunk<NWV> &cb, auto &&hook) __attribute__((always_inline)) {
+        // X_K = K S, X_Q = Q S
+        f32x4 xk[4], xq[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) xk[I] = xq[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            hook(kb);
+            bf16x8 sh, sl;
+            pair_split(S[2 * kb], S[2 * kb + 1], sh, sl);
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int r = 16 * I + c;
+                const int o = r * 128 + 8 * ((4 * kb + gp) ^ col_swz(r));
+                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(&cb.K[o]);
+                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(&cb.Q[o]);
+                xk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sh, xk[I], 0, 0, 0);
+                xq[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sh, xq[I], 0, 0, 0);
+                xk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sl, xk[I], 0, 0, 0);
+                xq[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sl, xq[I], 0, 0, 0);
+            }
+        }
+        // R = V - 2^g X_K;  O = 2^g X_Q
+        f32x4 R[4], O[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const f32x4 ev = *reinterpret_cast<const f32x4 *>(&cb.E[16 * I + 4 * g]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float vv = bf16_to_f32(cb.V[(16 * I + 4 * g + r) * VW + 16 * wave + c]);
+                R[I][r] = vv - ev[r] * xk[I][r];
+                O[I][r] = ev[r] * xq[I][r];
+            }
+        }
+        // U = Tm R over the lower K-blocks (Tm is zero above the diagonal)
+        hook(4);
+        bf16x8 rh[2], rl[2];
+        pair_split(R[0], R[1], rh[0], rl[0]);
+        pair_split(R[2], R[3], rh[1], rl[1]);
+        f32x4 U[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            U[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb <= I / 2; ++kb) {
+                const int pr = I < 2 ? I : 2 + 2 * (I - 2) + kb;
+                const bf16x8 th = *reinterpret_cast<const bf16x8 *>(&cb.F[512 * (2 * pr) + 8 * lane]);
+                const bf16x8 tl = *reinterpret_cast<const bf16x8 *>(&cb.F[512 * (2 * pr + 1) + 8 * lane]);
+                U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh[kb], U[I], 0, 0, 0);
+                U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh[kb], U[I], 0, 0, 0);
+                U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl[kb], U[I], 0, 0, 0);
+            }
+        }
+        // U and U2 = 2^(gC - g) U as B operands over the tokens 32 kb + 8 gp + 0..7
+        hook(5);
+        bf16x8 uh[2], ul[2], u2h[2], u2l[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            float x[8], x2[8];
+            pair_rows(U[2 * kb], U[2 * kb + 1], x);
+            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&cb.E[64 + 32 * kb + 8 * gp]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&cb.E[64 + 32 * kb + 8 * gp + 4]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                x2[s] = w0[s] * x[s];
+                x2[4 + s] = w1[s] * x[4 + s];
+            }
+            uint4 hh, ll;
+            split8(x, hh, ll);
+            uh[kb] = as_bf16x8(hh);
+            ul[kb] = as_bf16x8(ll);
+            split8(x2, hh, ll);
+            u2h[kb] = as_bf16x8(hh);
+            u2l[kb] = as_bf16x8(ll);
+        }
+        // O += P U, gated, held for the store after the next barrier
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+#pragma unroll
+            for (int kb = 0; kb <= I / 2; ++kb) {
+                const int pr = 6 + (I < 2 ? I : 2 + 2 * (I - 2) + kb);
+                const bf16x8 ph = *reinterpret_cast<const bf16x8 *>(&cb.F[512 * (2 * pr) + 8 * lane]);
+                const bf16x8 pl = *reinterpret_cast<const bf16x8 *>(&cb.F[512 * (2 * pr + 1) + 8 * lane]);
+                O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, uh[kb], O[I], 0, 0, 0);
+                O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, uh[kb], O[I], 0, 0, 0);
+                O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ul[kb], O[I], 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float o = O[I][r];
+                // output gate of the looped block: o * sigmoid(z_g), bf16 gate values
+                if constexpr (GATE) o *= bf16_to_f32(cb.G[(16 * I + 4 * g + r) * VW + 16 * wave + c]);
+                Oh[I][r] = o;
+            }
+        }
+        // S = 2^gC S + K^T U2 (A = K^T tiles by transpose reads of the K rows)
+        hook(6);
+        const float ec = cb.E[C - 1];
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[m][r] *= ec;
+        const int te = c >> 2, tm = c & 3;   // transpose-read roles: row offset, column quad
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb == 1) hook(7);
+            const int r0 = 32 * kb + 8 * gp + te, r1 = r0 + 4;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int blk = 2 * m + (tm >> 1), sub = 4 * (tm & 1);
+                const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4 *)(&cb.K[r0 * 128 + 8 * (blk ^ col_swz(r0)) + sub]));
+                const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_short4 *)(&cb.K[r1 * 128 + 8 * (blk ^ col_swz(r1)) + sub]));
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, (__attribute__((ext_vector_type(8))) short){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1],
+                                                                        hi4[2], hi4[3]});
+                S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2h[kb], S[m], 0, 0, 0);
+                S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2l[kb], S[m], 0, 0, 0);
+            }
+        }
+    };
+
+    // Compute waves: chunk n from cur after barrier n; the stores of chunk
+    // n - 1 go out during the first two phases (before O overwrites Oh).
+    auto step = [&](int n, const ColChunk<NWV> &cur, bool store_prev) __attribute__((always_inline)) {
+        __syncthreads();
+        compute(cur, [&](int hk) __attribute__((always_inline)) {
+            if (store_prev && hk >= 4 && hk <= 5) {
+                store_tile(n - 1, 2 * (hk - 4));
+                store_tile(n - 1, 2 * (hk - 4) + 1);
+            }
+        });
+    };
+    step(0, lds0, false);
+    for (int n = 1; n < NC; n += 2) {
+        step(n, lds1, true);
+        if (n + 1 < NC) step(n + 1, lds0, true);
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) store_tile(NC - 1, I);
+
+    if (state_out) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) state_out[((size_t)unit * D + 16 * m + 4 * g + r) * D + col] = S[m][r];
+    }
+}
+
 size_t prefill_head_ws_bytes(int B, int L, int H, int C) {
     const size_t NC = (size_t)((L + C - 1) / C);
     return (size_t)B * H * NC * (size_t)(8 * C * C + 12 * C);
+}
+
+template <int NWV, bool GATE, typename TO>
+static void launch_col(const GdnArgs &a, int NC, hipStream_t s) {
+    const unsigned units = (unsigned)a.B * (unsigned)a.H;
+    hipLaunchKernelGGL((scan_head_col_kernel<NWV, GATE, TO>), dim3(units * (8 / NWV)), dim3(128 * NWV), 0, s,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const unsigned char *)a.ws,
+                       a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC, a.gate);
 }
 
 template <int D, int C, int PREC, typename TI, typename TO>
@@ -973,6 +1371,21 @@ static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
             // would leave compute units idle: each block walks every chunk of its
             // unit and loads the chunk's K, Q, Tm and P either way, but twice the
             // blocks run at once
+            if constexpr (D == 128 && C == 64) {
+                // one compute wave per 16-column state tile, two tiles (and two
+                // loader waves) per workgroup when that still gives every compute
+                // unit a workgroup.  Its buffer views address one unit's tokens and
+                // workspace in 31 bits.
+                const size_t lim = (size_t)1 << 31;
+                if ((size_t)(a.L + C) * a.H * D * 4 < lim && (size_t)NC * (8 * C * C + 12 * C) < lim) {
+                    const bool two = (long)units * 4 >= device_cus();
+                    if (two && a.gate) launch_col<2, true, TO>(a, NC, s);
+                    else if (two) launch_col<2, false, TO>(a, NC, s);
+                    else if (a.gate) launch_col<1, true, TO>(a, NC, s);
+                    else launch_col<1, false, TO>(a, NC, s);
+                    return hipGetLastError();
+                }
+            }
             if constexpr (D == 128 && C == 64) {
                 if ((long)units * (D / BV) < device_cus()) {
                     hipLaunchKernelGGL((scan_head_bf16_kernel<D, D, BV / 2, C, TO>), dim3(units * (D / (BV / 2))),
