@@ -1093,6 +1093,7 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     using FLY = FragLayout<C>;
     static_assert(FLY::on && (NWV == 1 || NWV == 2 || NWV == 4), "column scan layout");
     __shared__ __attribute__((aligned(16))) ColChunk<NWV> lds0, lds1;
+    __shared__ __attribute__((aligned(16))) TO osb0[64 * 16 * NWV], osb1[64 * 16 * NWV];   // staged outputs
 
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int vb = logical % NB;
@@ -1157,17 +1158,33 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     // reaches barrier n only once its copies of chunk n have landed; barrier n
     // also orders every compute wave's reads of chunk n - 1 before the copies
     // into that buffer.  Both kinds of wave pass NC barriers.
+    // Staged outputs of chunk n (row-major [64][VW] of TO) to global memory,
+    // 16 bytes per lane; rows past L are dropped by the buffer bounds.
+    constexpr int OPR = VW * (int)sizeof(TO) / 16;   // 16-byte pieces per output row
+    auto store_staged = [&](int n, const TO *ob) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < (int)sizeof(TO); ++i) {   // NWV sizeof(TO) KiB per chunk, sizeof(TO) per loader
+            const int p = li + NWV * i, idx = 64 * p + lane, r = idx / OPR, part = idx % OPR;
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(ob) + 16 * idx);
+            __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)((unsigned)r * tok * (unsigned)sizeof(TO) +
+                                                                 (unsigned)(vw0 * (int)sizeof(TO) + 16 * part)),
+                                                   (int)((unsigned)(n * C) * tok * (unsigned)sizeof(TO)), 0);
+        }
+    };
     if (loader) {
-        issue_all(0, lds0);
-        for (int n = 0; n < NC; n += 2) {
+        // barrier n (n = 0 .. NC): chunk n's copies have landed and chunk n - 1's
+        // outputs are staged; the copies of chunk n + 1 and the stores of chunk
+        // n - 1 follow it
+        auto lstep = [&](int n, ColChunk<NWV> &nxt, const TO *ob) __attribute__((always_inline)) {
             wait_vmem_all();
             __syncthreads();
-            issue_all(min(n + 1, NC - 1), lds1);
-            if (n + 1 < NC) {
-                wait_vmem_all();
-                __syncthreads();
-                issue_all(min(n + 2, NC - 1), lds0);
-            }
+            if (n < NC) issue_all(min(n + 1, NC - 1), nxt);
+            if (n > 0) store_staged(n - 1, ob);
+        };
+        issue_all(0, lds0);
+        for (int n = 0; n <= NC; n += 2) {
+            lstep(n, lds1, osb1);
+            if (n + 1 <= NC) lstep(n + 1, lds0, osb0);
         }
         wait_vmem_all();   // the spare copies land before the workgroup ends
         return;
@@ -1183,22 +1200,13 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
             for (int r = 0; r < 4; ++r) S[m][r] = state_in[((size_t)unit * D + 16 * m + 4 * g + r) * D + col];
     }
 
-    f32x4 Oh[4];   // gated outputs of the previous chunk, rows 16 I + 4 g + r
-    const unsigned ovo = ((unsigned)(4 * g) * tok + (unsigned)col) * (unsigned)sizeof(TO);
-    auto store_tile = [&](int n, int I) __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            store_buf<TO>(Oh[I][r], ors, ovo, (unsigned)(n * C + 16 * I + r) * tok * (unsigned)sizeof(TO));
-    };
-
-    auto compute = [&](const ColChunk<NWV> &cb, auto &&hook) __attribute__((always_inline)) {
+    auto compute = [&](const ColChunk<NWV> &cb, TO *ob) __attribute__((always_inline)) {
         // X_K = K S, X_Q = Q S
         f32x4 xk[4], xq[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) xk[I] = xq[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            hook(kb);
             bf16x8 sh, sl;
             pair_split(S[2 * kb], S[2 * kb + 1], sh, sl);
 #pragma unroll
@@ -1226,7 +1234,6 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
             }
         }
         // U = Tm R over the lower K-blocks (Tm is zero above the diagonal)
-        hook(4);
         bf16x8 rh[2], rl[2];
         pair_split(R[0], R[1], rh[0], rl[0]);
         pair_split(R[2], R[3], rh[1], rl[1]);
@@ -1245,7 +1252,6 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
             }
         }
         // U and U2 = 2^(gC - g) U as B operands over the tokens 32 kb + 8 gp + 0..7
-        hook(5);
         bf16x8 uh[2], ul[2], u2h[2], u2l[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -1283,11 +1289,10 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
                 float o = O[I][r];
                 // output gate of the looped block: o * sigmoid(z_g), bf16 gate values
                 if constexpr (GATE) o *= bf16_to_f32(cb.G[(16 * I + 4 * g + r) * VW + 16 * wave + c]);
-                Oh[I][r] = o;
+                store1<TO>(&ob[(16 * I + 4 * g + r) * VW + 16 * wave + c], o);
             }
         }
         // S = 2^gC S + K^T U2 (A = K^T tiles by transpose reads of the K rows)
-        hook(6);
         const float ec = cb.E[C - 1];
 #pragma unroll
         for (int m = 0; m < 8; ++m)
@@ -1296,7 +1301,6 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
         const int te = c >> 2, tm = c & 3;   // transpose-read roles: row offset, column quad
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            if (kb == 1) hook(7);
             const int r0 = 32 * kb + 8 * gp + te, r1 = r0 + 4;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -1314,24 +1318,18 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
         }
     };
 
-    // Compute waves: chunk n from cur after barrier n; the stores of chunk
-    // n - 1 go out during the first two phases (before O overwrites Oh).
-    auto step = [&](int n, const ColChunk<NWV> &cur, bool store_prev) __attribute__((always_inline)) {
+    // Compute waves: chunk n from lds(n & 1) after barrier n, outputs staged in
+    // osb(n & 1) for the loaders (which stored that buffer's previous contents
+    // before barrier n); barrier NC hands over the last chunk's outputs.
+    for (int n = 0; n < NC; n += 2) {
         __syncthreads();
-        compute(cur, [&](int hk) __attribute__((always_inline)) {
-            if (store_prev && hk >= 4 && hk <= 5) {
-                store_tile(n - 1, 2 * (hk - 4));
-                store_tile(n - 1, 2 * (hk - 4) + 1);
-            }
-        });
-    };
-    step(0, lds0, false);
-    for (int n = 1; n < NC; n += 2) {
-        step(n, lds1, true);
-        if (n + 1 < NC) step(n + 1, lds0, true);
+        compute(lds0, osb0);
+        if (n + 1 < NC) {
+            __syncthreads();
+            compute(lds1, osb1);
+        }
     }
-#pragma unroll
-    for (int I = 0; I < 4; ++I) store_tile(NC - 1, I);
+    __syncthreads();
 
     if (state_out) {
 #pragma unroll
