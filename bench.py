@@ -78,19 +78,22 @@ def log(msg: str):
 
 
 def prefill_flops_bytes(B, L, H, d, C, qkv_bytes=2, out_bytes=2):
-    """Algorithmic flops and bytes per kernel of the chunked prefill (per launch).
+    """Algorithmic flops and bytes per kernel of the chunked prefill (per launch),
+    as the two kernels of the d = 128, C = 64 bf16 path split the work.
 
-    prepare, per head-token: gated K K^T (strictly lower) and Q K^T (lower incl.)
-      C*d MACs, the unit-lower inverse C^2/6 MACs; reads q, k, alpha, beta;
-      writes Tm and P (2*C*C fp32 per chunk) and g (C fp32 per chunk).
-    scan, per head-token: K S, Q S and K^T U (3*d*d MACs), Tm R and P U (C*d MACs);
-      reads q, k, v, Tm, P, g; writes o; reads/writes the state once per unit.
+    prepare, per head-token: gated K K^T (strictly lower) C*d/2 MACs, the
+      unit-lower inverse C^2/6 MACs; reads k, alpha, beta; writes the chunk's
+      workspace (the lower Tm fragments as bf16 hi/lo pairs, 12 KiB, the fp64 gate
+      prefix and the two decay vectors, 1 KiB: 13,312 bytes per 64-token chunk).
+    scan, per head-token: K S, Q S and K^T U (3*d*d MACs), Tm R and P U (C*d MACs),
+      the gated Q K^T (lower incl., C*d/2 MACs); reads q, k, v and the workspace;
+      writes o; reads/writes the state once per unit.
     """
     ht = B * L * H
-    prep_flops = 2.0 * ht * (C * d + C * C / 6.0)
-    scan_flops = 2.0 * ht * (3.0 * d * d + C * d)
-    ws_per_ht = (2 * C * C + C) * 4.0 / C
-    prep_bytes = ht * (2 * d * qkv_bytes + 8 + ws_per_ht)
+    prep_flops = 2.0 * ht * (C * d / 2.0 + C * C / 6.0)
+    scan_flops = 2.0 * ht * (3.0 * d * d + C * d + C * d / 2.0)
+    ws_per_ht = 13312.0 / C
+    prep_bytes = ht * (d * qkv_bytes + 8 + ws_per_ht)
     scan_bytes = ht * (3 * d * qkv_bytes + ws_per_ht + d * out_bytes) + B * H * d * d * 4.0
     path_bytes = ht * (3 * d * qkv_bytes + 8 + d * out_bytes) + B * H * d * d * 4.0
     # the method's own flops per head-token of the chunk form: K K^T, Q K^T and

@@ -16,6 +16,8 @@
 // chunk computes.
 //
 // Gate exponents are masked before exp, so every exponent is <= 0.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -68,7 +70,16 @@ struct FragLayout {
     }
 };
 
-template <int DK, int C, int PREC, typename TI>
+// Workspace of a chunk on the column-tile path (d = 128, C = 64, bf16 inputs):
+// the twelve lower Tm fragments (pair pr, half hl at (2 pr + hl) KiB, the
+// ColChunk order), the fp64 gate prefix g and the decay vectors 2^g, 2^(gC - g).
+// P is formed by the scan itself.
+struct ColWs {
+    static constexpr int GS = 12 * 1024, E = GS + 64 * 8, BYTES = E + 128 * 4;
+};
+
+// COL: write the column-tile path's workspace (Tm only, see ColWs).
+template <int DK, int C, int PREC, typename TI, bool COL = false>
 __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                         const float *__restrict__ alpha,
                                                         const float *__restrict__ beta,
@@ -96,14 +107,15 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     const int lr = lane & 15, lq = lane >> 4;
     const int t0 = n * C;
     const int Lc = min(C, L - t0);
-    unsigned char *wsu = ws + ((size_t)unit * NC + n) * (size_t)(8 * C * C + 12 * C);
+    unsigned char *wsu = ws + ((size_t)unit * NC + n) * (size_t)(COL ? ColWs::BYTES : 8 * C * C + 12 * C);
     float *gg = reinterpret_cast<float *>(wsu + 8 * C * C);
+    static_assert(!COL || (DK == 128 && C == 64 && PREC == PREC_BF16), "column-tile workspace");
 
     // Q fragments of this wave's Q K^T tiles, fetched together with K so that
     // the global latency is paid once
     Raw8<TI> qraw[MAXP][DK / 32];
 #pragma unroll
-    for (int m = 0; m < MAXP; ++m) {
+    for (int m = 0; m < (COL ? 0 : MAXP); ++m) {
         const int tt = min(wave + 4 * m, NLT - 1);
         int I = 0;
         while ((I + 1) * (I + 2) / 2 <= tt) ++I;
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     }
     f32x4 pacc[MAXP];
 #pragma unroll
-    for (int m = 0; m < MAXP; ++m) {
+    for (int m = 0; m < (COL ? 0 : MAXP); ++m) {
         pacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int tt = wave + 4 * m;
         if (tt >= NLT) continue;
@@ -233,6 +245,30 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
         __syncthreads();
     }
 
+    if constexpr (COL) {
+        // Tm = T diag(beta): the twelve lower fragments, 16 bytes per lane; the
+        // fp64 gate prefix and the decay vectors beside them
+        using FLY = FragLayout<C>;
+        for (int idx = tid; idx < 6 * 64; idx += 256) {
+            const int pr = idx / 64, l = idx % 64;
+            const int I = pr < 2 ? pr : 2 + ((pr - 2) >> 1), kb = pr < 2 ? 0 : (pr & 1);
+            const int t = 16 * I + l % 16, i0 = 32 * kb + 8 * FLY::gperm(l / 16);
+            float tv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = (i0 + e <= t) ? Ti[t * CP + i0 + e] * bs[i0 + e] : 0.f;
+            uint4 hi, lo;
+            split8(tv, hi, lo);
+            *reinterpret_cast<uint4 *>(wsu + 1024 * (2 * pr) + 16 * l) = hi;
+            *reinterpret_cast<uint4 *>(wsu + 1024 * (2 * pr + 1) + 16 * l) = lo;
+        }
+        if (tid < C) {
+            reinterpret_cast<double *>(wsu + ColWs::GS)[tid] = gs[tid];
+            float *E = reinterpret_cast<float *>(wsu + ColWs::E);
+            E[tid] = exp2_fast((float)gs[tid]);
+            E[C + tid] = exp2_fast((float)(gs[C - 1] - gs[tid]));   // rows past the ragged end keep g constant
+        }
+        return;
+    }
     // Gated P into Am's space (Am is dead after the inverse), zero above the diagonal.
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
@@ -995,9 +1031,9 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
 // ---------------------------------------------------------------------------
 // Scan, bf16 inputs, d = 128, C = 64: one wave per 16-column tile of the state.
 // A workgroup owns NWV adjacent column tiles of one (b, h) unit with NWV
-// compute waves and NWV loader waves (one wave per SIMD).  Each compute wave
-// keeps its 128 x 16 state slice in eight 16x16 accumulator tiles and carries
-// the whole chunk recurrence for its columns in registers:
+// state waves, one P wave and one loader wave (one wave per SIMD for NWV = 2).
+// Each state wave keeps its 128 x 16 state slice in eight 16x16 accumulator
+// tiles and carries the whole chunk recurrence for its columns in registers:
 //   X_K = K S, X_Q = Q S       B = the state itself: accumulator tiles 2kb and
 //                              2kb + 1 exchanged by v_permlane16_swap give lane
 //                              group g the state rows 32kb + 8p(g) + 0..7, with
@@ -1005,18 +1041,22 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
 //                              are read at the same columns.  S split hi/lo.
 //   R = V - 2^g X_K            the same exchange turns the four token tiles of R
 //   U = Tm R                   (and of U, U2) into B operands over the tokens;
-//   O = 2^g X_Q + P U          Tm and P come from the workspace as A fragments
-//   S = 2^gC S + K^T U2        whose K-columns follow the same order p(g);
-//                              K^T by LDS transpose reads of the K rows.
-// The compute waves exchange nothing through LDS and issue no loads: the
-// loader waves copy the chunk's read-only operands (K, Q, the lower Tm and P
-// fragments, the workgroup's V and gate columns, the decay vectors) from
-// global memory straight into LDS (buffer_load ... lds, no registers) one
-// chunk ahead into a second buffer, so the copies' issue cost and latency stay
-// off the recurrence.  Outputs are held in registers over the next chunk's
-// barrier and stored by bounds-checked buffer stores, so the rows of a ragged
-// last chunk past L are dropped by the hardware and every compute wave runs the
-// same straight-line code.
+//   S = 2^gC S + K^T U2        K^T by LDS transpose reads of the K rows;
+//   O = 2^g X_Q + P U          Tm and P are A fragments whose K-columns follow
+//                              the same order p(g).
+// Tm (the inverse factor) and the gate prefix come from the prepare kernel's
+// workspace; P = exp2(g_t - g_i) q_t.k_i is formed in the workgroup by the P
+// wave from the chunk's K and Q rows already in LDS, while the state waves
+// take X, R, U and the state update; a second barrier per chunk hands P over
+// before the output product.  So Q K^T never travels through HBM.
+// The state waves issue no global loads or stores: the loader wave copies the
+// chunk's read-only operands (K, Q, the lower Tm fragments, the workgroup's V
+// and gate columns, the gate prefix and decay vectors) from global memory
+// straight into LDS (buffer_load ... lds, no registers) one chunk ahead into a
+// second buffer, so the copies' issue cost and latency stay off the
+// recurrence, and stores the outputs the state waves staged in LDS one chunk
+// later by bounds-checked buffer stores, so the rows of a ragged last chunk
+// past L are dropped by the hardware and every wave runs straight-line code.
 // ---------------------------------------------------------------------------
 // 16-byte block swizzle of the K and Q rows in LDS (rows of 256 bytes, no
 // padding, so that a wave's 1 KiB LDS copy fills four whole rows): block b of
@@ -1037,14 +1077,19 @@ struct ColChunk {
     uint16_t F[24 * 512];       // Tm, P lower-block fragments, 1 KiB each: ((m * 6 + pair) * 2 + hl)
     uint16_t V[64 * 16 * NWV];  // the workgroup's V columns, row-major
     uint16_t G[64 * 16 * NWV];  // output-gate values, same layout
-    float E[128];               // 2^g [64] | 2^(gC - g) [64]
+    double GS[64];              // g, the chunk-relative log2 gate prefix
+    float E[128];               // 2^g [64] | 2^(gC - g) [64] (follows GS, as in the workspace)
 };
 
 // 16 bytes per lane from a buffer into LDS at lds + 16 * lane (lds is
 // wave-uniform), from byte voff + soff; lanes past the buffer's num_records
 // write zeros.  Counted by vmcnt like a load.
+// The destination goes in as its LDS offset (the low 32 bits of a flat LDS
+// address), so no generic-to-LDS conversion with a null check is emitted.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, void *lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+    const unsigned off = (unsigned)(size_t)lds;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(size_t)off, 16, voff, soff,
+                                             0, 0);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, unsigned bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
@@ -1081,17 +1126,149 @@ __device__ __forceinline__ void pair_split(const f32x4 &a, const f32x4 &b, bf16x
     lo = as_bf16x8(l);
 }
 
-template <int NWV, bool GATE, typename TO>
-__global__ __launch_bounds__(128 * NWV) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// One chunk of a state wave (column tile `tile` of a workgroup holding VW V
+// columns): the chunk's K, Q (swizzled rows), Tm / P lower fragments, V (and
+// gate) images and decay vectors in LDS; the tile's state S in registers
+// (updated in place); the chunk's outputs written to the staging image ob
+// ([64][VW] of TO).  mid() runs before the first read of P, which comes last
+// (the state update does not need it).
+template <int VW, bool GATE, typename TO, typename MID>
+__device__ __forceinline__ void scan_chunk(const uint16_t *cK, const uint16_t *cQ, const uint16_t *cF,
+                                           const uint16_t *cV, const uint16_t *cG, const float *cE,
+                                           f32x4 (&S)[8], TO *ob, int tile, int lane, MID &&mid) {
+    constexpr int C = 64;
+    const int c = lane & 15, g = lane >> 4;
+    const int gp = ((g & 1) << 1) | (g >> 1);   // lane group g holds K-block rows 8 gp .. 8 gp + 7
+    // X_K = K S, X_Q = Q S
+    f32x4 xk[4], xq[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) xk[I] = xq[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        bf16x8 sh, sl;
+        pair_split(S[2 * kb], S[2 * kb + 1], sh, sl);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const int r = 16 * I + c;
+            const int o = r * 128 + 8 * ((4 * kb + gp) ^ col_swz(r));
+            const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(&cK[o]);
+            const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(&cQ[o]);
+            xk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sh, xk[I], 0, 0, 0);
+            xq[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sh, xq[I], 0, 0, 0);
+            xk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sl, xk[I], 0, 0, 0);
+            xq[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sl, xq[I], 0, 0, 0);
+        }
+    }
+    // R = V - 2^g X_K;  O = 2^g X_Q
+    f32x4 R[4], O[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const f32x4 ev = *reinterpret_cast<const f32x4 *>(&cE[16 * I + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float vv = bf16_to_f32(cV[(16 * I + 4 * g + r) * VW + 16 * tile + c]);
+            R[I][r] = vv - ev[r] * xk[I][r];
+            O[I][r] = ev[r] * xq[I][r];
+        }
+    }
+    // U = Tm R over the lower K-blocks (Tm is zero above the diagonal)
+    bf16x8 rh[2], rl[2];
+    pair_split(R[0], R[1], rh[0], rl[0]);
+    pair_split(R[2], R[3], rh[1], rl[1]);
+    f32x4 U[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        U[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb <= I / 2; ++kb) {
+            const int pr = I < 2 ? I : 2 + 2 * (I - 2) + kb;
+            const bf16x8 th = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr) + 8 * lane]);
+            const bf16x8 tl = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr + 1) + 8 * lane]);
+            U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh[kb], U[I], 0, 0, 0);
+            U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh[kb], U[I], 0, 0, 0);
+            U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl[kb], U[I], 0, 0, 0);
+        }
+    }
+    // U and U2 = 2^(gC - g) U as B operands over the tokens 32 kb + 8 gp + 0..7
+    bf16x8 uh[2], ul[2], u2h[2], u2l[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        float x[8], x2[8];
+        pair_rows(U[2 * kb], U[2 * kb + 1], x);
+        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&cE[64 + 32 * kb + 8 * gp]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&cE[64 + 32 * kb + 8 * gp + 4]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            x2[s] = w0[s] * x[s];
+            x2[4 + s] = w1[s] * x[4 + s];
+        }
+        uint4 hh, ll;
+        split8(x, hh, ll);
+        uh[kb] = as_bf16x8(hh);
+        ul[kb] = as_bf16x8(ll);
+        split8(x2, hh, ll);
+        u2h[kb] = as_bf16x8(hh);
+        u2l[kb] = as_bf16x8(ll);
+    }
+    // S = 2^gC S + K^T U2 (A = K^T tiles by transpose reads of the K rows)
+    const float ec = cE[C - 1];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[m][r] *= ec;
+    const int te = c >> 2, tm = c & 3;   // transpose-read roles: row offset, column quad
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int r0 = 32 * kb + 8 * gp + te, r1 = r0 + 4;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int blk = 2 * m + (tm >> 1), sub = 4 * (tm & 1);
+            const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4 *)(&cK[r0 * 128 + 8 * (blk ^ col_swz(r0)) + sub]));
+            const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4 *)(&cK[r1 * 128 + 8 * (blk ^ col_swz(r1)) + sub]));
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, (__attribute__((ext_vector_type(8))) short){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1],
+                                                                    hi4[2], hi4[3]});
+            S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2h[kb], S[m], 0, 0, 0);
+            S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2l[kb], S[m], 0, 0, 0);
+        }
+    }
+    mid();   // P's fragments are in cF past this point
+    // O += P U, gated, held for the store after the next barrier
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+#pragma unroll
+        for (int kb = 0; kb <= I / 2; ++kb) {
+            const int pr = 6 + (I < 2 ? I : 2 + 2 * (I - 2) + kb);
+            const bf16x8 ph = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr) + 8 * lane]);
+            const bf16x8 pl = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr + 1) + 8 * lane]);
+            O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, uh[kb], O[I], 0, 0, 0);
+            O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, uh[kb], O[I], 0, 0, 0);
+            O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ul[kb], O[I], 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float o = O[I][r];
+            // output gate of the looped block: o * sigmoid(z_g), bf16 gate values
+            if constexpr (GATE) o *= bf16_to_f32(cG[(16 * I + 4 * g + r) * VW + 16 * tile + c]);
+            store1<TO>(&ob[(16 * I + 4 * g + r) * VW + 16 * tile + c], o);
+        }
+    }
+}
+
+template <int NWV, int NLD, bool GATE, typename TO>
+__global__ __launch_bounds__(64 * (NWV + 1 + NLD))
 void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                           const uint16_t *__restrict__ v, const unsigned char *__restrict__ ws,
                           const float *state_in, TO *__restrict__ out, float *state_out, int L, int H, int NC,
                           const uint16_t *__restrict__ gate) {
     constexpr int D = 128, C = 64, NB = 8 / NWV;   // workgroups per unit
-    constexpr int WSB = 8 * C * C + 12 * C;
+    constexpr int WSB = ColWs::BYTES;
     constexpr int VW = 16 * NWV;                    // V columns of the workgroup
     using FLY = FragLayout<C>;
     static_assert(FLY::on && (NWV == 1 || NWV == 2 || NWV == 4), "column scan layout");
+    static_assert(NLD == 1 || NLD == 2, "loader waves split 16 K / Q pieces, 12 Tm fragments, 2 NWV V pieces");
     __shared__ __attribute__((aligned(16))) ColChunk<NWV> lds0, lds1;
     __shared__ __attribute__((aligned(16))) TO osb0[64 * 16 * NWV], osb1[64 * 16 * NWV];   // staged outputs
 
@@ -1101,10 +1278,10 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     const int h = (int)(unit % H), b = (int)(unit / H);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool loader = wave >= NWV;                // waves NWV .. 2 NWV - 1 copy, the others compute
-    const int li = wave - NWV;                      // loader index
+    // waves 0 .. NWV - 1: state (one column tile each); NWV: P; the rest: copies
+    const bool loader = wave > NWV;
+    const int li = wave - NWV - 1;                  // loader index
     const int c = lane & 15, g = lane >> 4;
-    const int gp = ((g & 1) << 1) | (g >> 1);       // lane group g holds K-block rows 8 gp .. 8 gp + 7
     const int vw0 = VW * vb;                        // first V column of the workgroup
     const int col = vw0 + 16 * wave + c;            // a compute lane's state and output column
     const unsigned tok = (unsigned)H * D;           // elements between consecutive tokens
@@ -1120,57 +1297,130 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(ws + (size_t)unit * NC * WSB, (unsigned)NC * WSB);
     const __amdgpu_buffer_rsrc_t ors = buf_rsrc(out + base, ((unsigned)(L - 1) * tok + D) * (unsigned)sizeof(TO));
 
-    // A loader wave's share of chunk n's copies into cb: piece p = li + NWV i of
+    // A loader wave's share of chunk n's copies into cb: piece p = li + NLD i of
     // each kind (K rows 4p .. 4p + 3 with swizzled blocks, the same Q rows, the
-    // Tm / P fragments of the six lower (tile, K-block) pairs, 1 KiB pieces of
-    // the row-major [64][VW] V and gate images) and, from loader 0, the decay
-    // vectors.
+    // Tm fragments of the six lower (tile, K-block) pairs, 1 KiB pieces of the
+    // row-major [64][VW] V and gate images) and, from loader 0, the gate prefix
+    // and decay vectors.
     auto issue_all = [&](int n, ColChunk<NWV> &cb) __attribute__((always_inline)) {
         const unsigned sk = (unsigned)(n * C) * tok * 2u;   // byte offset of the chunk's first token
         const unsigned sw = (unsigned)n * WSB;
 #pragma unroll
-        for (int i = 0; i < 16 / NWV; ++i) {
-            const int p = li + NWV * i, r = 4 * p + g;
+        for (int i = 0; i < 16 / NLD; ++i) {
+            const int p = li + NLD * i, r = 4 * p + g;
             const unsigned off = (unsigned)r * tok * 2u + 16u * (unsigned)(c ^ col_swz(r));
             dma16(krs, off, sk, &cb.K[512 * p]);
             dma16(qrs, off, sk, &cb.Q[512 * p]);
         }
 #pragma unroll
-        for (int i = 0; i < 24 / NWV; ++i) {
-            const int p = li + NWV * i;
-            const int hl = p & 1, pr = (p >> 1) % 6, m = p / 12;
-            const int I = pr < 2 ? pr : 2 + ((pr - 2) >> 1), kb = pr < 2 ? 0 : (pr & 1);
-            dma16(wrs, 16u * (unsigned)lane, sw + FLY::frag(m, hl, I, kb), &cb.F[512 * p]);
+        for (int i = 0; i < 12 / NLD; ++i) {
+            const int p = li + NLD * i;
+            dma16(wrs, 16u * (unsigned)lane, sw + 1024u * (unsigned)p, &cb.F[512 * p]);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int p = li + NWV * i;
+        for (int i = 0; i < 2 * NWV / NLD; ++i) {
+            const int p = li + NLD * i;
             const int idx = 64 * p + lane, r = idx / (2 * NWV), part = idx % (2 * NWV);
             const unsigned off = (unsigned)r * tok * 2u + 2u * (unsigned)(vw0 + 8 * part);
             dma16(vrs, off, sk, &cb.V[512 * p]);
             if constexpr (GATE) dma16(grs, off, sk, &cb.G[512 * p]);
         }
-        if (li == 0 && lane < 32) dma16(wrs, 16u * (unsigned)lane, sw + 8 * C * C + 4 * C, cb.E);
+        if (li == 0) dma16(wrs, 16u * (unsigned)lane, sw + ColWs::GS, cb.GS);   // GS then E, 1 KiB
     };
 
-    // Loader waves: chunk n + 1 into the free buffer while the compute waves
+    // Loader waves: chunk n + 1 into the free buffer while the other waves
     // work on chunk n (the last chunk copies itself again, unused).  A loader
     // reaches barrier n only once its copies of chunk n have landed; barrier n
-    // also orders every compute wave's reads of chunk n - 1 before the copies
-    // into that buffer.  Both kinds of wave pass NC barriers.
+    // also orders every wave's reads of chunk n - 1 before the copies into that
+    // buffer.  Every wave passes barriers 0 .. NC and the middle barrier of
+    // each chunk.
     // Staged outputs of chunk n (row-major [64][VW] of TO) to global memory,
     // 16 bytes per lane; rows past L are dropped by the buffer bounds.
     constexpr int OPR = VW * (int)sizeof(TO) / 16;   // 16-byte pieces per output row
     auto store_staged = [&](int n, const TO *ob) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < (int)sizeof(TO); ++i) {   // NWV sizeof(TO) KiB per chunk, sizeof(TO) per loader
-            const int p = li + NWV * i, idx = 64 * p + lane, r = idx / OPR, part = idx % OPR;
+        for (int i = 0; i < NWV * (int)sizeof(TO) / NLD; ++i) {   // NWV sizeof(TO) KiB per chunk
+            const int p = li + NLD * i, idx = 64 * p + lane, r = idx / OPR, part = idx % OPR;
             const u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(ob) + 16 * idx);
             __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)((unsigned)r * tok * (unsigned)sizeof(TO) +
                                                                  (unsigned)(vw0 * (int)sizeof(TO) + 16 * part)),
                                                    (int)((unsigned)(n * C) * tok * (unsigned)sizeof(TO)), 0);
         }
     };
+    // P wave: after barrier n, chunk n's P = exp2(g_t - g_i) q_t.k_i (i <= t < Lc)
+    // from its K and Q rows and gate prefix in lds(n & 1), as the lower A
+    // fragments F[12 ..] of that buffer; the chunk's middle barrier hands them
+    // to the state waves, which meanwhile form K S, Q S and U.  The products are
+    // taken transposed, P^T = K Q^T, so that a lane holds four tokens i of one
+    // row t per tile: the state's pair regrouping of two such tiles then gives
+    // the A fragment of a (row tile, K-block) pair in registers.
+    if (wave == NWV) {
+        auto pstep = [&](int j, ColChunk<NWV> &cb) __attribute__((always_inline)) {
+            const int Lc = min(C, L - j * C);
+            bf16x8 kf[4][4];   // K rows 16 J + c, columns 32 kb + 8 g .. + 7
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int r = 16 * J + c;
+                    kf[J][kb] = *reinterpret_cast<const bf16x8 *>(&cb.K[r * 128 + 8 * ((4 * kb + g) ^ col_swz(r))]);
+                }
+            double gi[4][4];   // g of the lane's tokens i = 16 J + 4 g + r
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; r += 2) {
+                    const double2 x = *reinterpret_cast<const double2 *>(&cb.GS[16 * J + 4 * g + r]);
+                    gi[J][r] = x.x;
+                    gi[J][r + 1] = x.y;
+                }
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int t = 16 * I + c;   // this lane's row of P
+                bf16x8 qf[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    qf[kb] = *reinterpret_cast<const bf16x8 *>(&cb.Q[t * 128 + 8 * ((4 * kb + g) ^ col_swz(t))]);
+                const double gt = cb.GS[t];
+                f32x4 pt[4];   // P^T tile (J, I): element r is P[t][16 J + 4 g + r]
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    pt[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (J > I) continue;
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+                        pt[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[J][kb], qf[kb], pt[J], 0, 0, 0);
+                    // computed for every element, then selected (no branch per element)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * J + 4 * g + r;
+                        const float v = exp2_fast((float)(gt - gi[J][r])) * pt[J][r];
+                        pt[J][r] = (i <= t && t < Lc) ? v : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int kb = 0; kb <= I / 2; ++kb) {
+                    const int pr = I < 2 ? I : 2 + 2 * (I - 2) + kb;
+                    bf16x8 hi, lo;
+                    pair_split(pt[2 * kb], pt[2 * kb + 1], hi, lo);
+                    *reinterpret_cast<bf16x8 *>(&cb.F[512 * (12 + 2 * pr) + 8 * lane]) = hi;
+                    *reinterpret_cast<bf16x8 *>(&cb.F[512 * (13 + 2 * pr) + 8 * lane]) = lo;
+                }
+            }
+        };
+        for (int n = 0; n < NC; n += 2) {
+            __syncthreads();
+            pstep(n, lds0);
+            __syncthreads();
+            if (n + 1 < NC) {
+                __syncthreads();
+                pstep(n + 1, lds1);
+                __syncthreads();
+            }
+        }
+        __syncthreads();
+        return;
+    }
     if (loader) {
         // barrier n (n = 0 .. NC): chunk n's copies have landed and chunk n - 1's
         // outputs are staged; the copies of chunk n + 1 and the stores of chunk
@@ -1180,6 +1430,9 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
             __syncthreads();
             if (n < NC) issue_all(min(n + 1, NC - 1), nxt);
             if (n > 0) store_staged(n - 1, ob);
+            // the chunk's middle barrier: nothing of a loader's to publish there, so
+            // no fence, which would wait for the copies just issued
+            if (n < NC) __builtin_amdgcn_s_barrier();
         };
         issue_all(0, lds0);
         for (int n = 0; n <= NC; n += 2) {
@@ -1201,126 +1454,14 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     }
 
     auto compute = [&](const ColChunk<NWV> &cb, TO *ob) __attribute__((always_inline)) {
-        // X_K = K S, X_Q = Q S
-        f32x4 xk[4], xq[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) xk[I] = xq[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            bf16x8 sh, sl;
-            pair_split(S[2 * kb], S[2 * kb + 1], sh, sl);
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const int r = 16 * I + c;
-                const int o = r * 128 + 8 * ((4 * kb + gp) ^ col_swz(r));
-                const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(&cb.K[o]);
-                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(&cb.Q[o]);
-                xk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sh, xk[I], 0, 0, 0);
-                xq[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sh, xq[I], 0, 0, 0);
-                xk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sl, xk[I], 0, 0, 0);
-                xq[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sl, xq[I], 0, 0, 0);
-            }
-        }
-        // R = V - 2^g X_K;  O = 2^g X_Q
-        f32x4 R[4], O[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const f32x4 ev = *reinterpret_cast<const f32x4 *>(&cb.E[16 * I + 4 * g]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float vv = bf16_to_f32(cb.V[(16 * I + 4 * g + r) * VW + 16 * wave + c]);
-                R[I][r] = vv - ev[r] * xk[I][r];
-                O[I][r] = ev[r] * xq[I][r];
-            }
-        }
-        // U = Tm R over the lower K-blocks (Tm is zero above the diagonal)
-        bf16x8 rh[2], rl[2];
-        pair_split(R[0], R[1], rh[0], rl[0]);
-        pair_split(R[2], R[3], rh[1], rl[1]);
-        f32x4 U[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            U[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb <= I / 2; ++kb) {
-                const int pr = I < 2 ? I : 2 + 2 * (I - 2) + kb;
-                const bf16x8 th = *reinterpret_cast<const bf16x8 *>(&cb.F[512 * (2 * pr) + 8 * lane]);
-                const bf16x8 tl = *reinterpret_cast<const bf16x8 *>(&cb.F[512 * (2 * pr + 1) + 8 * lane]);
-                U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh[kb], U[I], 0, 0, 0);
-                U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh[kb], U[I], 0, 0, 0);
-                U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl[kb], U[I], 0, 0, 0);
-            }
-        }
-        // U and U2 = 2^(gC - g) U as B operands over the tokens 32 kb + 8 gp + 0..7
-        bf16x8 uh[2], ul[2], u2h[2], u2l[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            float x[8], x2[8];
-            pair_rows(U[2 * kb], U[2 * kb + 1], x);
-            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&cb.E[64 + 32 * kb + 8 * gp]);
-            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&cb.E[64 + 32 * kb + 8 * gp + 4]);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                x2[s] = w0[s] * x[s];
-                x2[4 + s] = w1[s] * x[4 + s];
-            }
-            uint4 hh, ll;
-            split8(x, hh, ll);
-            uh[kb] = as_bf16x8(hh);
-            ul[kb] = as_bf16x8(ll);
-            split8(x2, hh, ll);
-            u2h[kb] = as_bf16x8(hh);
-            u2l[kb] = as_bf16x8(ll);
-        }
-        // O += P U, gated, held for the store after the next barrier
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-#pragma unroll
-            for (int kb = 0; kb <= I / 2; ++kb) {
-                const int pr = 6 + (I < 2 ? I : 2 + 2 * (I - 2) + kb);
-                const bf16x8 ph = *reinterpret_cast<const bf16x8 *>(&cb.F[512 * (2 * pr) + 8 * lane]);
-                const bf16x8 pl = *reinterpret_cast<const bf16x8 *>(&cb.F[512 * (2 * pr + 1) + 8 * lane]);
-                O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, uh[kb], O[I], 0, 0, 0);
-                O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, uh[kb], O[I], 0, 0, 0);
-                O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ul[kb], O[I], 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float o = O[I][r];
-                // output gate of the looped block: o * sigmoid(z_g), bf16 gate values
-                if constexpr (GATE) o *= bf16_to_f32(cb.G[(16 * I + 4 * g + r) * VW + 16 * wave + c]);
-                store1<TO>(&ob[(16 * I + 4 * g + r) * VW + 16 * wave + c], o);
-            }
-        }
-        // S = 2^gC S + K^T U2 (A = K^T tiles by transpose reads of the K rows)
-        const float ec = cb.E[C - 1];
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[m][r] *= ec;
-        const int te = c >> 2, tm = c & 3;   // transpose-read roles: row offset, column quad
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int r0 = 32 * kb + 8 * gp + te, r1 = r0 + 4;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int blk = 2 * m + (tm >> 1), sub = 4 * (tm & 1);
-                const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4 *)(&cb.K[r0 * 128 + 8 * (blk ^ col_swz(r0)) + sub]));
-                const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_short4 *)(&cb.K[r1 * 128 + 8 * (blk ^ col_swz(r1)) + sub]));
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, (__attribute__((ext_vector_type(8))) short){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1],
-                                                                        hi4[2], hi4[3]});
-                S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2h[kb], S[m], 0, 0, 0);
-                S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2l[kb], S[m], 0, 0, 0);
-            }
-        }
+        scan_chunk<VW, GATE, TO>(cb.K, cb.Q, cb.F, cb.V, cb.G, cb.E, S, ob, wave, lane,
+                                 []() __attribute__((always_inline)) { __syncthreads(); });
     };
 
-    // Compute waves: chunk n from lds(n & 1) after barrier n, outputs staged in
-    // osb(n & 1) for the loaders (which stored that buffer's previous contents
-    // before barrier n); barrier NC hands over the last chunk's outputs.
+    // State waves: chunk n from lds(n & 1) after barrier n (P after the chunk's
+    // middle barrier), outputs staged in osb(n & 1) for the loaders (which
+    // stored that buffer's previous contents before barrier n); barrier NC
+    // hands over the last chunk's outputs.
     for (int n = 0; n < NC; n += 2) {
         __syncthreads();
         compute(lds0, osb0);
@@ -1344,10 +1485,14 @@ size_t prefill_head_ws_bytes(int B, int L, int H, int C) {
     return (size_t)B * H * NC * (size_t)(8 * C * C + 12 * C);
 }
 
+// NWV state waves, the P wave and one loader wave: one wave per SIMD when NWV
+// is 2 (a loader's copies of a chunk take about half the chunk's time).
 template <int NWV, bool GATE, typename TO>
 static void launch_col(const GdnArgs &a, int NC, hipStream_t s) {
+    constexpr int NLD = 1;
     const unsigned units = (unsigned)a.B * (unsigned)a.H;
-    hipLaunchKernelGGL((scan_head_col_kernel<NWV, GATE, TO>), dim3(units * (8 / NWV)), dim3(128 * NWV), 0, s,
+    hipLaunchKernelGGL((scan_head_col_kernel<NWV, NLD, GATE, TO>), dim3(units * (8 / NWV)), dim3(64 * (NWV + 1 + NLD)),
+                       0, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const unsigned char *)a.ws,
                        a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC, a.gate);
 }
@@ -1357,9 +1502,26 @@ static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
     constexpr int BV = 32;
     const int NC = (a.L + C - 1) / C;
     const unsigned units = (unsigned)a.B * (unsigned)a.H;
+    // The column-tile scan (bf16 inputs, d = 128, C = 64) takes a workspace of
+    // Tm alone and forms P itself; the same test picks it in both phases.  Its
+    // buffer views address one unit's tokens and workspace in 31 bits.
+    const size_t lim = (size_t)1 << 31;
+    const bool col = PREC == PREC_BF16 && D == 128 && C == 64 && (size_t)(a.L + C) * a.H * D * 4 < lim &&
+                     (size_t)NC * ColWs::BYTES < lim;
     if (phase & PHASE_PREPARE) {
-        hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI>), dim3(units * NC), dim3(256), 0, s,
-                           (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (unsigned char *)a.ws, a.L, a.H, NC);
+        if constexpr (PREC == PREC_BF16 && D == 128 && C == 64) {
+            if (col)
+                hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI, true>), dim3(units * NC), dim3(256), 0, s,
+                                   (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (unsigned char *)a.ws, a.L,
+                                   a.H, NC);
+            else
+                hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI>), dim3(units * NC), dim3(256), 0, s,
+                                   (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (unsigned char *)a.ws, a.L,
+                                   a.H, NC);
+        } else {
+            hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI>), dim3(units * NC), dim3(256), 0, s,
+                               (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (unsigned char *)a.ws, a.L, a.H, NC);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1370,12 +1532,10 @@ static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
             // unit and loads the chunk's K, Q, Tm and P either way, but twice the
             // blocks run at once
             if constexpr (D == 128 && C == 64) {
-                // one compute wave per 16-column state tile, two tiles (and two
-                // loader waves) per workgroup when that still gives every compute
-                // unit a workgroup.  Its buffer views address one unit's tokens and
-                // workspace in 31 bits.
-                const size_t lim = (size_t)1 << 31;
-                if ((size_t)(a.L + C) * a.H * D * 4 < lim && (size_t)NC * (8 * C * C + 12 * C) < lim) {
+                // one state wave per 16-column state tile, two tiles (with a P wave
+                // and two loader waves) per workgroup when that still gives every
+                // compute unit a workgroup
+                if (col) {
                     const bool two = (long)units * 4 >= device_cus();
                     if (two && a.gate) launch_col<2, true, TO>(a, NC, s);
                     else if (two) launch_col<2, false, TO>(a, NC, s);

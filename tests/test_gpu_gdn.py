@@ -415,6 +415,45 @@ def test_prepare_then_scan_equals_prefill(gate):
     np.testing.assert_array_equal(host(S), host(S_ref))
 
 
+@pytest.mark.parametrize("L", [333, 64, 1])
+def test_column_scan_phases_bf16(L):
+    """d128, chunk 64, bf16 in and out, 64 (b, h) units: the column-tile path,
+    whose scan workgroups form each chunk's gated Q K^T themselves (the prepare
+    phase writes only the inverse factor and the gate prefix).  lt2_gdn_prefill
+    with the final state written in place over the initial one equals its two
+    phases called apart (lt2_gdn_prefill_prepare, then lt2_gdn_prefill_scan) bit
+    for bit, and the oracle within the bf16 bound.  Ragged, single-chunk and
+    single-token lengths."""
+    import ctypes
+    B, H = 4, 16
+    shape = synth.GDNShape(B, L, H, 128, 128, "head", 2.0, "bf16")
+    announce(f"column scan phases L={L}")
+    x = synth.gdn_inputs(shape, seed=23)
+    S0 = np.random.default_rng(23).standard_normal((B, H, 128, 128)).astype(np.float32) * 0.1
+    q, k, v = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    a, b = dev(x["alpha"]), dev(x["beta"])
+    st = dev(S0)
+    o1, _ = lt2.lt2_gdn_prefill(q, k, v, a, b, state_in=st, state_out=st, chunk=64, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    desc = lt2.gdn_desc(B, L, H, 128, 128, 64, lt2.LT2_BF16, lt2.LT2_BF16, lt2.LT2_GATE_HEAD)
+    nbytes = lt2.lt2_gdn_prefill_workspace_size(desc)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(o1)
+    S2 = torch.empty_like(st)
+    s0 = dev(S0)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    L_ = lt2.lib()
+    assert L_.lt2_gdn_prefill_prepare(ctypes.byref(desc), P(q), P(k), P(a), P(b), P(ws), nbytes, sp) == 0
+    assert L_.lt2_gdn_prefill_scan(ctypes.byref(desc), P(q), P(k), P(v), P(s0), P(o2), P(S2), P(ws), nbytes, sp) == 0
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(o1), host(o2))
+    np.testing.assert_array_equal(host(st), host(S2))
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(host(o1), o_ref) <= TOL_BF16
+    assert rel_err(host(st), S_ref) <= TOL_BF16
+
+
 @pytest.mark.parametrize("gate", ["head", "channel"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_state_in_place(gate, dtype):
