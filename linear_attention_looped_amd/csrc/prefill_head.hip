@@ -78,8 +78,64 @@ struct ColWs {
     static constexpr int GS = 12 * 1024, E = GS + 64 * 8, BYTES = E + 128 * 4;
 };
 
-// COL: write the column-tile path's workspace (Tm only, see ColWs).
-template <int DK, int C, int PREC, typename TI, bool COL = false>
+// (I + A)^{-1} of a chunk's strictly lower C x C matrix A (fp32 in LDS, row
+// pitch CP) into Ti (same pitch; blocks above the diagonal are not written).
+// Called by all 256 threads of the workgroup: it holds barriers.
+template <int C, int CP>
+__device__ __forceinline__ void unit_lower_inverse(const float *Am, float *Ti, float (*Xs)[16 * 17], int wave,
+                                                   int lane) {
+    constexpr int NT = C / 16;
+    const int lr = lane & 15, lq = lane >> 4;
+    // (I + A)^{-1}: 16x16 diagonal blocks by forward substitution (one wave per
+    // block, lane j < 16 solves column j) ...
+    if (wave < NT && lane < 16) {
+        const int base = 16 * wave;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float s = (t == lane) ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < t; ++s2) s -= Am[(base + t) * CP + base + s2] * x[s2];
+            x[t] = s;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Ti[(base + t) * CP + base + lane] = x[t];
+    }
+    __syncthreads();
+    // ... then the blocks below the diagonal by distance:
+    //   T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ   (fp32 matrix cores)
+    for (int dist = 1; dist < NT; ++dist) {
+        if (wave < NT - dist) {
+            const int J = wave, I = wave + dist;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int Kb = J; Kb < I; ++Kb) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const float a = Am[(16 * I + lr) * CP + 16 * Kb + 4 * kk + lq];
+                    const float bb = Ti[(16 * Kb + 4 * kk + lq) * CP + 16 * J + lr];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xs[wave][(4 * lq + r) * 17 + lr] = acc[r];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const float a = Ti[(16 * I + lr) * CP + 16 * I + 4 * kk + lq];
+                const float bb = Xs[wave][(4 * kk + lq) * 17 + lr];
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ti[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = -y[r];
+        }
+        __syncthreads();
+    }
+}
+
+template <int DK, int C, int PREC, typename TI>
 __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                                                         const float *__restrict__ alpha,
                                                         const float *__restrict__ beta,
@@ -107,15 +163,14 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     const int lr = lane & 15, lq = lane >> 4;
     const int t0 = n * C;
     const int Lc = min(C, L - t0);
-    unsigned char *wsu = ws + ((size_t)unit * NC + n) * (size_t)(COL ? ColWs::BYTES : 8 * C * C + 12 * C);
+    unsigned char *wsu = ws + ((size_t)unit * NC + n) * (size_t)(8 * C * C + 12 * C);
     float *gg = reinterpret_cast<float *>(wsu + 8 * C * C);
-    static_assert(!COL || (DK == 128 && C == 64 && PREC == PREC_BF16), "column-tile workspace");
 
     // Q fragments of this wave's Q K^T tiles, fetched together with K so that
     // the global latency is paid once
     Raw8<TI> qraw[MAXP][DK / 32];
 #pragma unroll
-    for (int m = 0; m < (COL ? 0 : MAXP); ++m) {
+    for (int m = 0; m < MAXP; ++m) {
         const int tt = min(wave + 4 * m, NLT - 1);
         int I = 0;
         while ((I + 1) * (I + 2) / 2 <= tt) ++I;
@@ -180,7 +235,7 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     }
     f32x4 pacc[MAXP];
 #pragma unroll
-    for (int m = 0; m < (COL ? 0 : MAXP); ++m) {
+    for (int m = 0; m < MAXP; ++m) {
         pacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int tt = wave + 4 * m;
         if (tt >= NLT) continue;
@@ -197,78 +252,8 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
     }
     __syncthreads();
 
-    // (I + A)^{-1}: 16x16 diagonal blocks by forward substitution (one wave per
-    // block, lane j < 16 solves column j) ...
-    if (wave < NT && lane < 16) {
-        const int base = 16 * wave;
-        float x[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float s = (t == lane) ? 1.f : 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < t; ++s2) s -= Am[(base + t) * CP + base + s2] * x[s2];
-            x[t] = s;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) Ti[(base + t) * CP + base + lane] = x[t];
-    }
-    __syncthreads();
-    // ... then the blocks below the diagonal by distance:
-    //   T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ   (fp32 matrix cores)
-    for (int dist = 1; dist < NT; ++dist) {
-        if (wave < NT - dist) {
-            const int J = wave, I = wave + dist;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int Kb = J; Kb < I; ++Kb) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const float a = Am[(16 * I + lr) * CP + 16 * Kb + 4 * kk + lq];
-                    const float bb = Ti[(16 * Kb + 4 * kk + lq) * CP + 16 * J + lr];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Xs[wave][(4 * lq + r) * 17 + lr] = acc[r];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const float a = Ti[(16 * I + lr) * CP + 16 * I + 4 * kk + lq];
-                const float bb = Xs[wave][(4 * kk + lq) * 17 + lr];
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ti[(16 * I + 4 * lq + r) * CP + 16 * J + lr] = -y[r];
-        }
-        __syncthreads();
-    }
+    unit_lower_inverse<C, CP>(Am, Ti, Xs, wave, lane);
 
-    if constexpr (COL) {
-        // Tm = T diag(beta): the twelve lower fragments, 16 bytes per lane; the
-        // fp64 gate prefix and the decay vectors beside them
-        using FLY = FragLayout<C>;
-        for (int idx = tid; idx < 6 * 64; idx += 256) {
-            const int pr = idx / 64, l = idx % 64;
-            const int I = pr < 2 ? pr : 2 + ((pr - 2) >> 1), kb = pr < 2 ? 0 : (pr & 1);
-            const int t = 16 * I + l % 16, i0 = 32 * kb + 8 * FLY::gperm(l / 16);
-            float tv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tv[e] = (i0 + e <= t) ? Ti[t * CP + i0 + e] * bs[i0 + e] : 0.f;
-            uint4 hi, lo;
-            split8(tv, hi, lo);
-            *reinterpret_cast<uint4 *>(wsu + 1024 * (2 * pr) + 16 * l) = hi;
-            *reinterpret_cast<uint4 *>(wsu + 1024 * (2 * pr + 1) + 16 * l) = lo;
-        }
-        if (tid < C) {
-            reinterpret_cast<double *>(wsu + ColWs::GS)[tid] = gs[tid];
-            float *E = reinterpret_cast<float *>(wsu + ColWs::E);
-            E[tid] = exp2_fast((float)gs[tid]);
-            E[C + tid] = exp2_fast((float)(gs[C - 1] - gs[tid]));   // rows past the ragged end keep g constant
-        }
-        return;
-    }
     // Gated P into Am's space (Am is dead after the inverse), zero above the diagonal.
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
@@ -330,6 +315,133 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
         gg[tid] = (float)gs[tid];
         gg[C + tid] = exp2_fast((float)gs[tid]);
         gg[2 * C + tid] = exp2_fast((float)(gs[C - 1] - gs[tid]));   // rows past the ragged end keep g constant
+    }
+}
+
+// Prepare of the column-tile path (d = 128, C = 64, bf16 k): per chunk the
+// chunk-relative fp64 gate prefix g, the gated K K^T (strictly lower, rows
+// scaled by beta), Tm = (I + A)^{-1} diag(beta) as the scan's twelve lower A
+// fragments (bf16 hi/lo pairs), and the decay vectors 2^g, 2^(gC - g) (layout
+// ColWs).  The gated Q K^T is left to the scan.  A workgroup takes the chunks
+// blockIdx.x, blockIdx.x + gridDim.x, ... of the (unit, chunk) list; the next
+// chunk's K rows and gates are fetched into registers while the current one is
+// computed, so the global latency is paid once per workgroup.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void prep_col_kernel(const uint16_t *__restrict__ k, const float *__restrict__ alpha,
+                                                       const float *__restrict__ beta, unsigned char *__restrict__ ws,
+                                                       int L, int H, int NC, int total) {
+    constexpr int DK = 128, C = 64, NT = C / 16;
+    constexpr int KP = DK + 8;   // K row pitch (elements), rows stay 16-byte aligned
+    constexpr int CP = C + 4;
+    static_assert(C * KP * 2 == C * CP * 4, "K rows and the inverse share one buffer");
+    __shared__ __attribute__((aligned(16))) unsigned char kt_raw[C * CP * 4];   // K rows, then the inverse
+    __shared__ __attribute__((aligned(16))) float Am[C * CP];
+    __shared__ float Xs[4][16 * 17];
+    __shared__ __attribute__((aligned(16))) float bs[C];
+    __shared__ double gs[C];
+    uint16_t *Ks = reinterpret_cast<uint16_t *>(kt_raw);
+    float *Ti = reinterpret_cast<float *>(kt_raw);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    Raw8<uint16_t> kraw[4];   // 16-byte pieces tid + 256 i of the chunk's [64][128] K rows
+    float a_raw = 0.f, b_raw = 0.f;
+    auto fetch = [&](int cid) __attribute__((always_inline)) {
+        const int unit = cid / NC, n = cid % NC, h = unit % H, b = unit / H;
+        const int t0 = n * C, last = min(C, L - t0) - 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, t = idx / (DK / 8), c8 = idx % (DK / 8);
+            load_raw8<uint16_t>(kraw[i], k + (((size_t)b * L + t0 + min(t, last)) * H + h) * DK + 8 * c8);
+        }
+        if (wave == 0) {
+            const size_t tok = ((size_t)b * L + t0 + min(lane, last)) * H + h;
+            a_raw = alpha[tok];
+            b_raw = beta[tok];
+        }
+    };
+    int cid = blockIdx.x;
+    if (cid < total) fetch(cid);
+    for (; cid < total; cid += gridDim.x) {
+        const int n = cid % NC;
+        const int Lc = min(C, L - n * C);
+        unsigned char *wsu = ws + (size_t)cid * ColWs::BYTES;   // cid = unit * NC + n
+        __syncthreads();   // the previous chunk's reads of the inverse, Am, gs and bs are done
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, t = idx / (DK / 8), c8 = idx % (DK / 8);
+            if (t >= Lc) zero_raw8<uint16_t>(kraw[i]);
+            *reinterpret_cast<Raw8<uint16_t> *>(Ks + t * KP + 8 * c8) = kraw[i];
+        }
+        if (wave == 0) {
+            // chunk-relative prefix of log2 alpha in fp64 (a fast decay reaches
+            // hundreds of octaves within a chunk)
+            double lg = (lane < Lc) ? (double)log2_gate(a_raw) : 0.0;
+            const float bt = (lane < Lc) ? b_raw : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const double y = __shfl_up(lg, off);
+                if (lane >= off) lg += y;
+            }
+            gs[lane] = lg;
+            bs[lane] = bt;
+        }
+        if (cid + (int)gridDim.x < total) fetch(cid + gridDim.x);   // the registers are free again
+        __syncthreads();
+
+        // Gated K K^T: wave w takes the tiles (I, w); those above the diagonal are zero
+        {
+            const double gi = gs[16 * wave + lr];
+#pragma unroll
+            for (int I = 0; I < NT; ++I) {
+                if (I < wave) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Am[(16 * I + 4 * lq + r) * CP + 16 * wave + lr] = 0.f;
+                    continue;
+                }
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb)
+                    gram_mma<PREC_BF16>(
+                        acc, *reinterpret_cast<const Raw8<uint16_t> *>(Ks + (16 * I + lr) * KP + 32 * kb + 8 * lq),
+                        *reinterpret_cast<const Raw8<uint16_t> *>(Ks + (16 * wave + lr) * KP + 32 * kb + 8 * lq));
+                // computed for every element, then selected (no branch per element)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * I + 4 * lq + r, i = 16 * wave + lr;
+                    const float v = bs[t] * exp2_fast((float)(gs[t] - gi)) * acc[r];
+                    Am[t * CP + i] = (i < t) ? v : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+        unit_lower_inverse<C, CP>(Am, Ti, Xs, wave, lane);
+
+        // Tm = T diag(beta): the twelve lower fragments, 16 bytes per lane
+        using FLY = FragLayout<C>;
+        for (int idx = tid; idx < 6 * 64; idx += 256) {
+            const int pr = idx / 64, l = idx % 64;
+            const int I = pr < 2 ? pr : 2 + ((pr - 2) >> 1), kb = pr < 2 ? 0 : (pr & 1);
+            const int t = 16 * I + l % 16, i0 = 32 * kb + 8 * FLY::gperm(l / 16);
+            const float4 x0 = *reinterpret_cast<const float4 *>(&Ti[t * CP + i0]);
+            const float4 x1 = *reinterpret_cast<const float4 *>(&Ti[t * CP + i0 + 4]);
+            const float4 b0 = *reinterpret_cast<const float4 *>(&bs[i0]);
+            const float4 b1 = *reinterpret_cast<const float4 *>(&bs[i0 + 4]);
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            float tv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = (i0 + e <= t) ? xv[e] * bv[e] : 0.f;   // Ti above is not written
+            uint4 hi, lo;
+            split8(tv, hi, lo);
+            *reinterpret_cast<uint4 *>(wsu + 1024 * (2 * pr) + 16 * l) = hi;
+            *reinterpret_cast<uint4 *>(wsu + 1024 * (2 * pr + 1) + 16 * l) = lo;
+        }
+        if (tid < C) {
+            reinterpret_cast<double *>(wsu + ColWs::GS)[tid] = gs[tid];
+            float *E = reinterpret_cast<float *>(wsu + ColWs::E);
+            E[tid] = exp2_fast((float)gs[tid]);
+            E[C + tid] = exp2_fast((float)(gs[C - 1] - gs[tid]));   // rows past the ragged end keep g constant
+        }
     }
 }
 
@@ -1510,11 +1622,13 @@ static hipError_t run(const GdnArgs &a, int phase, hipStream_t s) {
                      (size_t)NC * ColWs::BYTES < lim;
     if (phase & PHASE_PREPARE) {
         if constexpr (PREC == PREC_BF16 && D == 128 && C == 64) {
-            if (col)
-                hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI, true>), dim3(units * NC), dim3(256), 0, s,
-                                   (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (unsigned char *)a.ws, a.L,
-                                   a.H, NC);
-            else
+            if (col) {
+                // four workgroups per CU fit the LDS; each takes every grid-th chunk
+                const int total = (int)units * NC;
+                const int grid = total < 4 * device_cus() ? total : 4 * device_cus();
+                hipLaunchKernelGGL(prep_col_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t *)a.k, a.alpha,
+                                   a.beta, (unsigned char *)a.ws, a.L, a.H, NC, total);
+            } else
                 hipLaunchKernelGGL((prep_head_kernel<D, C, PREC, TI>), dim3(units * NC), dim3(256), 0, s,
                                    (const TI *)a.q, (const TI *)a.k, a.alpha, a.beta, (unsigned char *)a.ws, a.L,
                                    a.H, NC);
