@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
     "prepare": ["linear_attention_looped_amd/csrc/prefill_head.hip", "linear_attention_looped_amd/csrc/common.h"],
     "scan": ["linear_attention_looped_amd/csrc/prefill_head.hip", "linear_attention_looped_amd/csrc/common.h"],
 }
-TRAFFIC_KEYS = {"prepare": "prep_head_kernel", "scan": "scan_head_col_kernel"}
+TRAFFIC_KEYS = {"prepare": "prep_col_kernel", "scan": "scan_head_col_kernel"}
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 # fp32 FMA on the vector ALUs without packed-fp32 instructions: 256 CUs x 4 SIMDs
