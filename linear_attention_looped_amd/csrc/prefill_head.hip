@@ -1155,19 +1155,22 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
 //   U = Tm R                   (and of U, U2) into B operands over the tokens;
 //   S = 2^gC S + K^T U2        K^T by LDS transpose reads of the K rows;
 //   O = 2^g X_Q + P U          Tm and P are A fragments whose K-columns follow
-//                              the same order p(g).
+//                              the same order p(g) (taken a chunk later).
 // Tm (the inverse factor) and the gate prefix come from the prepare kernel's
 // workspace; P = exp2(g_t - g_i) q_t.k_i is formed in the workgroup by the P
 // wave from the chunk's K and Q rows already in LDS, while the state waves
-// take X, R, U and the state update; a second barrier per chunk hands P over
-// before the output product.  So Q K^T never travels through HBM.
+// take X, R, U and the state update, so Q K^T never travels through HBM.  The
+// output product P U of a chunk is off the recurrence: the state waves take it
+// in the next chunk's phase, beside that chunk's K S and Q S, from 2^g X_Q and
+// U carried in registers and P left in its buffer, so one barrier per chunk
+// suffices and the recurrence never waits for P.
 // The state waves issue no global loads or stores: the loader wave copies the
 // chunk's read-only operands (K, Q, the lower Tm fragments, the workgroup's V
 // and gate columns, the gate prefix and decay vectors) from global memory
 // straight into LDS (buffer_load ... lds, no registers) one chunk ahead into a
 // second buffer, so the copies' issue cost and latency stay off the
-// recurrence, and stores the outputs the state waves staged in LDS one chunk
-// later by bounds-checked buffer stores, so the rows of a ragged last chunk
+// recurrence, and stores the outputs the state waves staged in LDS by
+// bounds-checked buffer stores, so the rows of a ragged last chunk
 // past L are dropped by the hardware and every wave runs straight-line code.
 // ---------------------------------------------------------------------------
 // 16-byte block swizzle of the K and Q rows in LDS (rows of 256 bytes, no
@@ -1181,13 +1184,20 @@ __device__ __forceinline__ int col_swz(int r) {
     return ((x & 8) | ((x & 3) << 1) | ((x >> 2) & 1)) ^ (((r >> 4) & 1) << 3);
 }
 
+// Token rows of the V, gate and staged-output images in LDS: row t sits at
+// tok_row(t), which swaps the two 2-bit fields of t within each 16-row block
+// (an involution).  A lane of an accumulator tile reads or writes token
+// 16 I + 4 g + r at column c: the four lane groups g then meet consecutive
+// LDS rows instead of rows four apart (the same banks for 64-byte rows).
+__device__ __forceinline__ int tok_row(int t) { return (t & ~15) | ((t & 3) << 2) | ((t >> 2) & 3); }
+
 // One chunk's operands in LDS (16-bit elements unless stated).
 template <int NWV>
 struct ColChunk {
     uint16_t K[64 * 128];       // swizzled rows
     uint16_t Q[64 * 128];       // swizzled rows
     uint16_t F[24 * 512];       // Tm, P lower-block fragments, 1 KiB each: ((m * 6 + pair) * 2 + hl)
-    uint16_t V[64 * 16 * NWV];  // the workgroup's V columns, row-major
+    uint16_t V[64 * 16 * NWV];  // the workgroup's V columns, token t in row tok_row(t)
     uint16_t G[64 * 16 * NWV];  // output-gate values, same layout
     double GS[64];              // g, the chunk-relative log2 gate prefix
     float E[128];               // 2^g [64] | 2^(gC - g) [64] (follows GS, as in the workspace)
@@ -1238,16 +1248,25 @@ __device__ __forceinline__ void pair_split(const f32x4 &a, const f32x4 &b, bf16x
     lo = as_bf16x8(l);
 }
 
+// The carry of a chunk's outputs into the next chunk's phase: O = 2^g X_Q of
+// the four token tiles, U as B operands (hi, lo) and, for the gated block, the
+// gate values of the lane's outputs.
+template <bool GATE>
+struct ColCarry {
+    f32x4 O[4];
+    bf16x8 uh[2], ul[2];
+    float gv[GATE ? 16 : 1];
+};
+
 // One chunk of a state wave (column tile `tile` of a workgroup holding VW V
-// columns): the chunk's K, Q (swizzled rows), Tm / P lower fragments, V (and
-// gate) images and decay vectors in LDS; the tile's state S in registers
-// (updated in place); the chunk's outputs written to the staging image ob
-// ([64][VW] of TO).  mid() runs before the first read of P, which comes last
-// (the state update does not need it).
-template <int VW, bool GATE, typename TO, typename MID>
+// columns), all but the output product: the chunk's K, Q (swizzled rows), Tm
+// lower fragments, V (and gate) images and decay vectors in LDS; the tile's
+// state S in registers (updated in place); the chunk's 2^g X_Q, U and gate
+// values left in cr for scan_chunk_out.
+template <int VW, bool GATE>
 __device__ __forceinline__ void scan_chunk(const uint16_t *cK, const uint16_t *cQ, const uint16_t *cF,
                                            const uint16_t *cV, const uint16_t *cG, const float *cE,
-                                           f32x4 (&S)[8], TO *ob, int tile, int lane, MID &&mid) {
+                                           f32x4 (&S)[8], ColCarry<GATE> &cr, int tile, int lane) {
     constexpr int C = 64;
     const int c = lane & 15, g = lane >> 4;
     const int gp = ((g & 1) << 1) | (g >> 1);   // lane group g holds K-block rows 8 gp .. 8 gp + 7
@@ -1272,13 +1291,14 @@ __device__ __forceinline__ void scan_chunk(const uint16_t *cK, const uint16_t *c
         }
     }
     // R = V - 2^g X_K;  O = 2^g X_Q
-    f32x4 R[4], O[4];
+    f32x4 R[4];
+    f32x4 (&O)[4] = cr.O;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const f32x4 ev = *reinterpret_cast<const f32x4 *>(&cE[16 * I + 4 * g]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float vv = bf16_to_f32(cV[(16 * I + 4 * g + r) * VW + 16 * tile + c]);
+            const float vv = bf16_to_f32(cV[(16 * I + 4 * r + g) * VW + 16 * tile + c]);   // row tok_row(t)
             R[I][r] = vv - ev[r] * xk[I][r];
             O[I][r] = ev[r] * xq[I][r];
         }
@@ -1302,7 +1322,8 @@ __device__ __forceinline__ void scan_chunk(const uint16_t *cK, const uint16_t *c
         }
     }
     // U and U2 = 2^(gC - g) U as B operands over the tokens 32 kb + 8 gp + 0..7
-    bf16x8 uh[2], ul[2], u2h[2], u2l[2];
+    bf16x8 (&uh)[2] = cr.uh, (&ul)[2] = cr.ul;
+    bf16x8 u2h[2], u2l[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         float x[8], x2[8];
@@ -1346,25 +1367,40 @@ __device__ __forceinline__ void scan_chunk(const uint16_t *cK, const uint16_t *c
             S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2l[kb], S[m], 0, 0, 0);
         }
     }
-    mid();   // P's fragments are in cF past this point
-    // O += P U, gated, held for the store after the next barrier
+    if constexpr (GATE) {
+        // output gate of the looped block (sigmoid(z_g) as bf16), read before
+        // the loader reuses the buffer
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                cr.gv[4 * I + r] = bf16_to_f32(cG[(16 * I + 4 * r + g) * VW + 16 * tile + c]);   // row tok_row(t)
+    }
+}
+
+// The output product of a chunk, taken in the next chunk's phase: O += P U
+// with P's lower A fragments (written by the P wave in cF), gated, staged in
+// ob ([64][VW] of TO, token t in row tok_row(t)) for the loader's stores.
+template <int VW, bool GATE, typename TO>
+__device__ __forceinline__ void scan_chunk_out(const uint16_t *cF, ColCarry<GATE> &cr, TO *ob, int tile, int lane) {
+    const int c = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
+        f32x4 O = cr.O[I];
 #pragma unroll
         for (int kb = 0; kb <= I / 2; ++kb) {
             const int pr = 6 + (I < 2 ? I : 2 + 2 * (I - 2) + kb);
             const bf16x8 ph = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr) + 8 * lane]);
             const bf16x8 pl = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr + 1) + 8 * lane]);
-            O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, uh[kb], O[I], 0, 0, 0);
-            O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, uh[kb], O[I], 0, 0, 0);
-            O[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ul[kb], O[I], 0, 0, 0);
+            O = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, cr.uh[kb], O, 0, 0, 0);
+            O = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, cr.uh[kb], O, 0, 0, 0);
+            O = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, cr.ul[kb], O, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float o = O[I][r];
-            // output gate of the looped block: o * sigmoid(z_g), bf16 gate values
-            if constexpr (GATE) o *= bf16_to_f32(cG[(16 * I + 4 * g + r) * VW + 16 * tile + c]);
-            store1<TO>(&ob[(16 * I + 4 * g + r) * VW + 16 * tile + c], o);
+            float o = O[r];
+            if constexpr (GATE) o *= cr.gv[4 * I + r];
+            store1<TO>(&ob[(16 * I + 4 * r + g) * VW + 16 * tile + c], o);   // row tok_row(t)
         }
     }
 }
@@ -1412,8 +1448,8 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     // A loader wave's share of chunk n's copies into cb: piece p = li + NLD i of
     // each kind (K rows 4p .. 4p + 3 with swizzled blocks, the same Q rows, the
     // Tm fragments of the six lower (tile, K-block) pairs, 1 KiB pieces of the
-    // row-major [64][VW] V and gate images) and, from loader 0, the gate prefix
-    // and decay vectors.
+    // [64][VW] V and gate images, token t in row tok_row(t)) and, from loader 0,
+    // the gate prefix and decay vectors.
     auto issue_all = [&](int n, ColChunk<NWV> &cb) __attribute__((always_inline)) {
         const unsigned sk = (unsigned)(n * C) * tok * 2u;   // byte offset of the chunk's first token
         const unsigned sw = (unsigned)n * WSB;
@@ -1432,7 +1468,7 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
 #pragma unroll
         for (int i = 0; i < 2 * NWV / NLD; ++i) {
             const int p = li + NLD * i;
-            const int idx = 64 * p + lane, r = idx / (2 * NWV), part = idx % (2 * NWV);
+            const int idx = 64 * p + lane, r = tok_row(idx / (2 * NWV)), part = idx % (2 * NWV);
             const unsigned off = (unsigned)r * tok * 2u + 2u * (unsigned)(vw0 + 8 * part);
             dma16(vrs, off, sk, &cb.V[512 * p]);
             if constexpr (GATE) dma16(grs, off, sk, &cb.G[512 * p]);
@@ -1444,15 +1480,15 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     // work on chunk n (the last chunk copies itself again, unused).  A loader
     // reaches barrier n only once its copies of chunk n have landed; barrier n
     // also orders every wave's reads of chunk n - 1 before the copies into that
-    // buffer.  Every wave passes barriers 0 .. NC and the middle barrier of
-    // each chunk.
-    // Staged outputs of chunk n (row-major [64][VW] of TO) to global memory,
-    // 16 bytes per lane; rows past L are dropped by the buffer bounds.
+    // buffer.  Every wave passes barriers 0 .. NC + 1.
+    // Staged outputs of chunk n ([64][VW] of TO, token t in row tok_row(t)) to
+    // global memory, 16 bytes per lane; rows past L are dropped by the buffer
+    // bounds.
     constexpr int OPR = VW * (int)sizeof(TO) / 16;   // 16-byte pieces per output row
     auto store_staged = [&](int n, const TO *ob) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NWV * (int)sizeof(TO) / NLD; ++i) {   // NWV sizeof(TO) KiB per chunk
-            const int p = li + NLD * i, idx = 64 * p + lane, r = idx / OPR, part = idx % OPR;
+            const int p = li + NLD * i, idx = 64 * p + lane, r = tok_row(idx / OPR), part = idx % OPR;
             const u32x4 x = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(ob) + 16 * idx);
             __builtin_amdgcn_raw_buffer_store_b128(x, ors, (int)((unsigned)r * tok * (unsigned)sizeof(TO) +
                                                                  (unsigned)(vw0 * (int)sizeof(TO) + 16 * part)),
@@ -1461,8 +1497,9 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     };
     // P wave: after barrier n, chunk n's P = exp2(g_t - g_i) q_t.k_i (i <= t < Lc)
     // from its K and Q rows and gate prefix in lds(n & 1), as the lower A
-    // fragments F[12 ..] of that buffer; the chunk's middle barrier hands them
-    // to the state waves, which meanwhile form K S, Q S and U.  The products are
+    // fragments F[12 ..] of that buffer (which the loader never writes); barrier
+    // n + 1 hands them to the state waves, which take the output product of
+    // chunk n in the phase of chunk n + 1.  The products are
     // taken transposed, P^T = K Q^T, so that a lane holds four tokens i of one
     // row t per tile: the state's pair regrouping of two such tiles then gives
     // the A fragment of a (row tile, K-block) pair in registers.
@@ -1523,33 +1560,29 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
         for (int n = 0; n < NC; n += 2) {
             __syncthreads();
             pstep(n, lds0);
-            __syncthreads();
             if (n + 1 < NC) {
                 __syncthreads();
                 pstep(n + 1, lds1);
-                __syncthreads();
             }
         }
-        __syncthreads();
+        __syncthreads();   // barrier NC
+        __syncthreads();   // barrier NC + 1
         return;
     }
     if (loader) {
-        // barrier n (n = 0 .. NC): chunk n's copies have landed and chunk n - 1's
-        // outputs are staged; the copies of chunk n + 1 and the stores of chunk
-        // n - 1 follow it
+        // barrier n (n = 0 .. NC + 1): chunk n's copies have landed and chunk
+        // n - 2's outputs are staged; the copies of chunk n + 1 and the stores
+        // of chunk n - 2 follow it
         auto lstep = [&](int n, ColChunk<NWV> &nxt, const TO *ob) __attribute__((always_inline)) {
             wait_vmem_all();
             __syncthreads();
             if (n < NC) issue_all(min(n + 1, NC - 1), nxt);
-            if (n > 0) store_staged(n - 1, ob);
-            // the chunk's middle barrier: nothing of a loader's to publish there, so
-            // no fence, which would wait for the copies just issued
-            if (n < NC) __builtin_amdgcn_s_barrier();
+            if (n >= 2) store_staged(n - 2, ob);
         };
         issue_all(0, lds0);
-        for (int n = 0; n <= NC; n += 2) {
-            lstep(n, lds1, osb1);
-            if (n + 1 <= NC) lstep(n + 1, lds0, osb0);
+        for (int n = 0; n <= NC + 1; n += 2) {
+            lstep(n, lds1, osb0);
+            if (n + 1 <= NC + 1) lstep(n + 1, lds0, osb1);
         }
         wait_vmem_all();   // the spare copies land before the workgroup ends
         return;
@@ -1565,23 +1598,31 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
             for (int r = 0; r < 4; ++r) S[m][r] = state_in[((size_t)unit * D + 16 * m + 4 * g + r) * D + col];
     }
 
-    auto compute = [&](const ColChunk<NWV> &cb, TO *ob) __attribute__((always_inline)) {
-        scan_chunk<VW, GATE, TO>(cb.K, cb.Q, cb.F, cb.V, cb.G, cb.E, S, ob, wave, lane,
-                                 []() __attribute__((always_inline)) { __syncthreads(); });
+    ColCarry<GATE> cr;
+    auto compute = [&](const ColChunk<NWV> &cb) __attribute__((always_inline)) {
+        scan_chunk<VW, GATE>(cb.K, cb.Q, cb.F, cb.V, cb.G, cb.E, S, cr, wave, lane);
+    };
+    auto finish = [&](const ColChunk<NWV> &cb, TO *ob) __attribute__((always_inline)) {
+        scan_chunk_out<VW, GATE, TO>(cb.F, cr, ob, wave, lane);
     };
 
-    // State waves: chunk n from lds(n & 1) after barrier n (P after the chunk's
-    // middle barrier), outputs staged in osb(n & 1) for the loaders (which
-    // stored that buffer's previous contents before barrier n); barrier NC
-    // hands over the last chunk's outputs.
+    // State waves: after barrier n, chunk n - 1's output product (its P from
+    // lds((n - 1) & 1), staged in osb((n - 1) & 1), which the loader stored
+    // before barrier n) and chunk n's recurrence from lds(n & 1); barrier
+    // NC + 1 hands over the last chunk's outputs.
     for (int n = 0; n < NC; n += 2) {
         __syncthreads();
-        compute(lds0, osb0);
+        if (n > 0) finish(lds1, osb1);
+        compute(lds0);
         if (n + 1 < NC) {
             __syncthreads();
-            compute(lds1, osb1);
+            finish(lds0, osb0);
+            compute(lds1);
         }
     }
+    __syncthreads();
+    if ((NC - 1) & 1) finish(lds1, osb1);
+    else finish(lds0, osb0);
     __syncthreads();
 
     if (state_out) {
