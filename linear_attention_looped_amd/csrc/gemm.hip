@@ -114,9 +114,9 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     auto dma_tile = [&](int kt, auto bufc) {
         uint16_t *Ad = decltype(bufc)::value ? A1 : A0;
         uint16_t *Bd = decltype(bufc)::value ? B1 : B0;
-        const int k0 = kt * BK;
-        const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(Ag + k0, abytes - 2 * k0);
-        const __amdgpu_buffer_rsrc_t rb = gemm_rsrc(Bg + k0, bbytes - 2 * k0);
+        const int k0 = kt * BK;   // kt may be one past the last tile: empty views, the copies write zeros
+        const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(Ag + k0, max(abytes - 2 * k0, 0));
+        const __amdgpu_buffer_rsrc_t rb = gemm_rsrc(Bg + k0, max(bbytes - 2 * k0, 0));
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
             gemm_dma16(ra, Ad + 512 * (wave + 4 * n), voa[n]);
@@ -174,10 +174,31 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
             products(fa[ks & 1], fb[ks & 1]);
         }
     };
-    auto tail = [&](auto nextc) {   // k-step 3, with k-step 0 of the tile in nextc
+    // k-step 3, with k-step 0 of the tile in nextc and the copies of K-tile kn
+    // into buffer dmac (empty views past the last tile), one copy per product so
+    // that the copies' issue time overlaps the matrix pipe
+    auto tail = [&](auto nextc, int kn, auto dmac) {
         static_assert(BK / 16 == 4, "k-step 3 uses the odd fragment set");
         frags(nextc, 0, fa[0], fb[0]);
-        products(fa[1], fb[1]);
+        dma_tile(kn, dmac);
+        const bf16x8 *xa = fa[1], *xb = fb[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // K is a multiple of 128 (the looped drivers require d_model and H*d to be),
@@ -194,16 +215,13 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
         head(c0);                         // K-tile kt
         wait_vmem_all();                  // K-tile kt + 1 (buffer 1) has landed
         __syncthreads();
-        if (kt + 2 < KT) dma_tile(kt + 2, c0);
-        __builtin_amdgcn_sched_barrier(0);
-        tail(c1);
+        tail(c1, min(kt + 2, KT), c0);    // K-tile kt + 2 into buffer 0
         head(c1);                         // K-tile kt + 1
         wait_vmem_all();                  // K-tile kt + 2 (buffer 0) has landed
         __syncthreads();
-        if (kt + 3 < KT) dma_tile(kt + 3, c1);
-        __builtin_amdgcn_sched_barrier(0);
-        tail(c0);                         // past the last tile its reads are stale and unused
+        tail(c0, min(kt + 3, KT), c1);    // past the last tile its reads are stale and unused
     }
+    wait_vmem_all();   // the empty copies past the last tile have landed
     __syncthreads();   // the epilogue stages through the K-tile buffers
 
     // ---- epilogue: register r of tile (i, j) holds
