@@ -262,7 +262,9 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + 4 * lq + r, s = 16 * J + lr;
-            As[t * CQ + s] = s < t ? bt[t] * dexp2(g[t], g[s]) * acc[r] : 0.f;
+            // computed for every element, then selected (see materialize)
+            const float v = materialize(bt[t] * dexp2(g[t], g[s]) * acc[r]);
+            As[t * CQ + s] = s < t ? v : 0.f;
         }
     }
     // the lower tiles of Q K^T stay in registers until K and Q are dead
@@ -327,7 +329,8 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(const TI *__restrict__ q,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + 4 * lq + r, s = 16 * J + lr;
-            Ps[t * CQ + s] = (s <= t && t < n) ? dexp2(g[t], g[s]) * pacc[m][r] : 0.f;
+            const float v = materialize(dexp2(g[t], g[s]) * pacc[m][r]);
+            Ps[t * CQ + s] = (s <= t && t < n) ? v : 0.f;
         }
     }
     __syncthreads();
@@ -1134,7 +1137,7 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = R0 + 4 * lq + r, s = 16 * j + lr;
-                const float gam = dexp2(g[t], g[min(s, t)]);
+                const float gam = materialize(dexp2(g[t], g[min(s, t)]));
                 X1[t * CQ + s] = (s <= t && t < n) ? ap[j][r] * gam : 0.f;
                 X2[t * CQ + s] = at[j][r];
                 X3[t * CQ + s] = qk[j][r];
@@ -1268,14 +1271,20 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
     //     (A = beta_t K K^T Gam) ; dbeta from A: sum_s dA_ts (k_t . k_s) Gam_ts
     for (int idx = tid; idx < BC * BC; idx += BNT) {
         const int t = idx / BC, s = idx % BC;
-        const float gts = s < t ? dexp2(g[t], g[s]) : 0.f;
+        const float gfull = materialize(dexp2(g[t], g[s]));   // every element, then selected
+        const float gts = s < t ? gfull : 0.f;
         const float kg = X3[t * CQ + s] * gts;
         const float e = X2[t * CQ + s] * bt[t] * gts;
         if (s < t) X1[s * CQ + t] = e;
         if (s <= t) X1[t * CQ + s] = e;
         Pt[t * CQ + s] = fmaf(X2[t * CQ + s], bt[t] * kg, Pt[t * CQ + s]);
     }
-    for (int s = wv; s < lane; s += 4) dbt = fmaf(X2[lane * CQ + s], X3[lane * CQ + s] * dexp2(g[lane], g[s]), dbt);
+    // the same terms in the same order as a loop over s < lane, taken for every
+    // s and selected, so no lane waits behind another's loads
+    for (int s = wv; s < BC; s += 4) {
+        const float v = materialize(fmaf(X2[lane * CQ + s], X3[lane * CQ + s] * dexp2(g[lane], g[s]), dbt));
+        dbt = s < lane ? v : dbt;
+    }
     __syncthreads();
     // (f) dK += (E + E^T) K
     {
@@ -1352,7 +1361,10 @@ __global__ __launch_bounds__(BNT) void bwd_grads_kernel(const TI *__restrict__ q
         pre -= j < n ? gd[j] : 0.f;
         float cross = 0.f;
 #pragma unroll 8
-        for (int i = 0; i < BC; ++i) cross += i < j ? Pt[j * CQ + i] : 0.f;
+        for (int i = 0; i < BC; ++i) {
+            const float v = Pt[j * CQ + i];
+            cross += i < j ? v : 0.f;
+        }
         if (j < n) {
             dlog_alpha[row0 + (size_t)j * H] = suf + pre + cross + dexp2(gC, 0.0) * x;
             dbeta[row0 + (size_t)j * H] = (redb[j] + redb[j + 64]) + (redb[j + 128] + redb[j + 192]);

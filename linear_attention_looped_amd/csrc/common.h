@@ -243,6 +243,14 @@ __device__ __forceinline__ float log2_gate(float a) {
     return fmaxf(__builtin_amdgcn_logf(fmaxf(a, 1e-38f)), -116.f);
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// x computed where it stands, for every lane: the compiler may not sink the work
+// behind it into the arm of a later select (it turns such a select of a value
+// fed by a one-use LDS load into a branch per element, serialising load, wait
+// and exp).  An empty asm with x as a register operand; no instruction.
+__device__ __forceinline__ float materialize(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // fp32 -> bf16 bits, round to nearest even (hardware conversion).
 __device__ __forceinline__ uint16_t bf16_bits(float x) {

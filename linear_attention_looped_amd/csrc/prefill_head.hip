@@ -230,7 +230,9 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
-            Am[t * CP + i] = (i < t) ? bs[t] * exp2_fast((float)(gs[t] - gs[i])) * acc[r] : 0.f;
+            // computed for every element, then selected (see materialize)
+            const float v = materialize(bs[t] * exp2_fast((float)(gs[t] - gs[i])) * acc[r]);
+            Am[t * CP + i] = (i < t) ? v : 0.f;
         }
     }
     f32x4 pacc[MAXP];
@@ -265,7 +267,8 @@ __global__ __launch_bounds__(256) void prep_head_kernel(const TI *__restrict__ q
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + 4 * lq + r, i = 16 * J + lr;
-            Am[t * CP + i] = (i <= t && t < Lc) ? exp2_fast((float)(gs[t] - gs[i])) * pacc[m][r] : 0.f;
+            const float v = materialize(exp2_fast((float)(gs[t] - gs[i])) * pacc[m][r]);
+            Am[t * CP + i] = (i <= t && t < Lc) ? v : 0.f;
         }
     }
     for (int tt = wave; tt < NT * NT; tt += 4) {
