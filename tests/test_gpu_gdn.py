@@ -109,6 +109,24 @@ def test_bf16_slow_decay_long():
     assert rel_err(S, S_ref) <= TOL_BF16
 
 
+
+@pytest.mark.parametrize("shift", [2.0, -6.0])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_column_scan_output_precision_bf16(shift, out_dtype):
+    """d128, chunk 64, bf16 q/k/v, 64 (b, h) units: the column-tile scan with two
+    tiles per workgroup, on fast (shift 2) and slow (shift -6, alpha near 1)
+    decays over eight whole chunks and a ragged one.  For bf16 outputs that scan
+    takes Q S with the state's hi half only (Q S reaches only the outputs): the
+    outputs hold the bf16 bar and the final state, which never sees that
+    product, stays at the level of the fp32-output launch (1e-4)."""
+    shape = synth.GDNShape(4, 555, 16, 128, 128, "head", shift, "bf16")
+    announce(f"column scan output precision shift={shift} out={out_dtype}")
+    x = synth.gdn_inputs(shape, seed=9)
+    o, S = run_prefill(x, shape, 64, out_dtype=out_dtype)
+    o_ref, S_ref = oracle_prefill(x)
+    assert rel_err(o, o_ref) <= TOL_BF16
+    assert rel_err(S, S_ref) <= 1e-4
+
 def test_state_passing_and_chunk_invariance_bf16():
     shape = synth.GDNShape(1, 512, 2, 128, 128, "head", 0.0, "bf16")
     announce("state passing bf16")
