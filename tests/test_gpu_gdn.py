@@ -127,6 +127,21 @@ def test_column_scan_output_precision_bf16(shift, out_dtype):
     assert rel_err(o, o_ref) <= TOL_BF16
     assert rel_err(S, S_ref) <= 1e-4
 
+
+def test_column_prepare_uneven_chunk_shares_bf16():
+    """d128, chunk 64, bf16: 3 x 16 units of 1500 tokens = 1152 chunks, more than
+    the prepare's grid of four workgroups per CU, so some workgroups take two
+    chunks (the second one's K rows and gates prefetched during the first) and
+    the others one; the last chunk of every unit is ragged (1500 = 23 x 64 + 28)."""
+    shape = synth.GDNShape(3, 1500, 16, 128, 128, "head", 1.0, "bf16")
+    announce("column prepare uneven shares")
+    x = synth.gdn_inputs(shape, seed=12)
+    S0 = np.random.default_rng(12).standard_normal((3, 16, 128, 128)).astype(np.float32) * 0.1
+    o, S = run_prefill(x, shape, 64, S0=S0)
+    o_ref, S_ref = oracle_prefill(x, S0)
+    assert rel_err(o, o_ref) <= TOL_BF16
+    assert rel_err(S, S_ref) <= TOL_BF16
+
 def test_state_passing_and_chunk_invariance_bf16():
     shape = synth.GDNShape(1, 512, 2, 128, 128, "head", 0.0, "bf16")
     announce("state passing bf16")
