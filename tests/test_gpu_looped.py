@@ -152,6 +152,20 @@ def test_looped_output_gate(B, L, D, H, d, T):
     assert rel_err(got - h0, ref - h0) <= TOL_BF16
 
 
+
+def test_looped_output_gate_two_tiles_per_workgroup():
+    """Gated looped block with 4 x 16 (b, h) units at d = 128: enough units for
+    the column-tile scan's two-tiles-per-workgroup form, whose gated instance
+    the smaller gated cases (one tile per workgroup) do not reach; ragged L."""
+    shape = synth.LoopShape(4, 100, 256, 16, 128, 1)
+    announce("gated looped, two column tiles per scan workgroup")
+    w = synth.loop_weights(shape, seed=8, gate=True)
+    h0 = synth.loop_h0(shape, seed=8)
+    got = run_looped(h0, w, shape, gate=True)
+    ref = oracle.looped_mixer(h0, w["w_in"], w["w_o"], 16, 128, 1, gate=True)
+    assert rel_err(got, ref) <= TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
+
 def test_gated_looped_decode_chain_matches_mixer():
     shape = synth.LoopShape(2, 20, 256, 2, 128, 2)
     announce("gated looped decode chain")
