@@ -1136,11 +1136,28 @@ __global__ __launch_bounds__(512) void scan_channel_tm_kernel(const uint16_t *__
     FR pa, pb;
     fetch(0, pa);
 
+    // L2 prefetch two chunks ahead: the NV column-block workgroups of a unit each
+    // touch one in NV of that chunk's 128-byte workspace lines with a 4-byte
+    // load, so the fragments fetched into registers a chunk later come from L2
+    // rather than HBM (the scan is otherwise bound by that fetch's latency).  The
+    // loaded word is only passed to an empty asm one chunk later, so nothing
+    // waits for it in between.
+    constexpr int LINES = (int)(SH::BYTES / 128), PFL = (LINES + NV - 1) / NV;
+    unsigned pf_word = 0u;
+    auto prefetch_l2 = [&](int n) __attribute__((always_inline)) {
+        asm volatile("" ::"v"(pf_word));   // the previous prefetch has landed by now
+        const int line = vb * PFL + tid;
+        if (n < NC && tid < PFL && line < LINES)
+            pf_word = *reinterpret_cast<const unsigned *>(ws + (unit * NC + (unsigned)n) * SH::BYTES +
+                                                          (size_t)line * 128);
+    };
+
     auto chunk = [&](int n, FR &cur, FR &nxt) __attribute__((always_inline)) {
         const int buf = n & 1;
         __syncthreads();   // S^T, V^T of chunk n and the outputs of chunk n - 1 are in LDS
         const int nn = min(n + 1, NC - 1);   // the last chunk re-fetches itself (unused)
         fetch(nn, nxt);
+        prefetch_l2(n + 2);
         const u32x4 vn = fetch_v(nn);
         if (n > 0) store_o(n - 1, C, buf ^ 1);
 
