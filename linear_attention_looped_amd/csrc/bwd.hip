@@ -710,6 +710,40 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
             bv = threadIdx.x < n ? beta[row0 + (size_t)threadIdx.x * H] : 0.f;
         }
     };
+    // L2 prefetch two chunks ahead of the register fetch: one 4-byte load per
+    // 128-byte line of chunk c's K and Q rows, N and P (shared by the unit's NB
+    // column blocks, so each block touches one NB-th of them) and this block's dO
+    // rows, so the fetch a chunk later hits L2.  The word only reaches an empty
+    // asm a chunk later, so nothing waits for it in between.
+    unsigned pf_word = 0u;
+    auto l2_touch = [&](int c) {
+        asm volatile("" ::"v"(pf_word));   // the previous touch has landed by now
+        if (c < 0) return;
+        const int t0 = c * BC, last = min(BC, L - t0) - 1;
+        const size_t row0 = ((size_t)b * L + t0) * H + h;
+        constexpr int KL = D * (int)sizeof(TI) / 128;       // lines per K (Q) row
+        constexpr int NPL = 2 * BC * BC * 4 / 128;          // lines of N and P
+        constexpr int SHARED = 2 * BC * KL + NPL;           // lines the NB blocks share
+        constexpr int PER = (SHARED + NB - 1) / NB;
+        const int i = (int)threadIdx.x;
+        const unsigned *p = nullptr;
+        if (i < PER) {
+            const int line = vb * PER + i;
+            if (line < BC * KL) {
+                p = reinterpret_cast<const unsigned *>(k + (row0 + (size_t)min(line / KL, last) * H) * D) +
+                    (line % KL) * 32;
+            } else if (line < 2 * BC * KL) {
+                const int j = line - BC * KL;
+                p = reinterpret_cast<const unsigned *>(q + (row0 + (size_t)min(j / KL, last) * H) * D) + (j % KL) * 32;
+            } else if (line < SHARED) {
+                p = reinterpret_cast<const unsigned *>(gnp + (unit * NC + c) * GNP_FLOATS + G_FLOATS) +
+                    (line - 2 * BC * KL) * 32;
+            }
+        } else if (i < PER + BC) {   // this block's dO rows (BV columns, within one line)
+            p = reinterpret_cast<const unsigned *>(dout + (row0 + (size_t)min(i - PER, last) * H) * D + vb * BV);
+        }
+        if (p) pf_word = *p;
+    };
     fetch(NC - 1);
     for (int c = NC - 1; c >= 0; --c) {
         const int t0 = c * BC, n = min(BC, L - t0);
@@ -726,6 +760,7 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(const TI *__restrict__ 
         // dS' entering chunk c (stored after the puts, as in the chunk-state kernel)
         state_from_lds<D, BV, VP>(dsws + (unit * NC + c) * (size_t)D * D, dS, vb * BV);
         if (c > 0) fetch(c - 1);
+        l2_touch(c - 2);
         __syncthreads();
         const double gC = g[n - 1];
         float er[4], ecr[4], br[4];   // gamma, gamma_C / gamma, beta of rows R0 + 4 (lane / 16) + r
