@@ -3,17 +3,19 @@
 //   C[m][n] = sum_k A[m][k] * B[n][k]        (A: [M, K], B: [N, K], both K-contiguous)
 //
 // which is y = x W^T for weights stored [d_out, d_in].  Workgroup tile 256 x 256
-// x 64, four waves, each wave 128 x 128 as 4 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16 (the accumulators, 256 floats per lane, live in the
-// accumulation registers: one wave per SIMD).  Per k-step of 16 a wave reads
-// four A and four B fragments for sixteen products, a third less LDS traffic
-// per multiply-add than 64 x 128 wave tiles.  A and B K-tiles are loaded
+// x 64, eight waves, each wave 64 x 128 as 2 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16 (128 accumulators per lane, so two waves share a
+// SIMD and one wave's products run while the other waits on its LDS reads).
+// Per k-step of 16 a wave reads two A and four B fragments for eight products.
+// (A four-wave form with 128 x 128 wave tiles, one wave per SIMD, reads a third
+// less LDS per product but leaves the matrix pipe idle on every LDS round trip;
+// it stays available as the NW = 4 instance.)  A and B K-tiles are loaded
 // straight into double-buffered LDS by LDS-DMA buffer loads; the workgroup
 // meets once per K-tile, before its last k-step, so that k-step's products
 // cover the next tile's first fragment reads.  LDS rows are 128 bytes with the
 // 16-byte segments XOR-swizzled by row, so fragment reads of 8 or 16
-// consecutive rows hit distinct banks.  The epilogues stage 32-row blocks of
-// the accumulators through the idle K-tile buffers and work row by row.
+// consecutive rows hit distinct banks.  The epilogues stage row blocks of the
+// accumulators through the idle K-tile buffers and work row by row.
 //
 // For the few rows of a decode step (M of a few hundred) a 64 x 128 variant
 // streams its K-tiles through five LDS stages instead (gemm_small_kernel).
@@ -42,6 +44,7 @@ namespace lt2 {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int GEMM_NW = 8;   // waves of the large-tile kernel
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
@@ -76,10 +79,18 @@ __device__ __forceinline__ void gemm_dma16(__amdgpu_buffer_rsrc_t r, uint16_t *d
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
 }
 
-template <int EPI, int DH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NW waves: 4 (wave tiles 128 x 128, one wave per SIMD) or 8 (wave tiles 64 x 128,
+// two waves per SIMD, so that one wave's products cover the other's LDS reads)
+template <int EPI, int DH, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int M, int N, int K,
                          int lda, int ldb, ProjOut po, ResidOut ro) {
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
+    constexpr int WR = 2 * BM / NW;     // rows of a wave tile
+    constexpr int NI = WR / 32;         // 32-row accumulator tiles per wave
+    constexpr int NCH = 32 / NW;        // 1 KiB DMA chunks per wave per operand and K-tile
+    constexpr int NR = NI + 4;          // fragment reads per k-step
+    constexpr int NMF = 4 * NI;         // products per k-step
     // two buffers as four distinct arrays: the compiler can then tell that the DMA
     // into one buffer does not alias the fragment reads of the other
     __shared__ __attribute__((aligned(1024))) uint16_t A0[BM * BK], A1[BM * BK], B0[BN * BK], B1[BN * BK];
@@ -101,10 +112,10 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     // range, so rows past M (N) read as zero.  K-tile kt + 2 is requested into
     // K-tile kt's buffer at kt's barrier and waited for at kt + 1's, so a tile of
     // products covers the load latency, with no staging registers.
-    int voa[8], vob[8];
+    int voa[NCH], vob[NCH];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-        const int row = 8 * (wave + 4 * n) + (lane >> 3);
+    for (int n = 0; n < NCH; ++n) {
+        const int row = 8 * (wave + NW * n) + (lane >> 3);
         const int lseg = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
         voa[n] = 2 * (row * lda + 8 * lseg);
         vob[n] = 2 * (row * ldb + 8 * lseg);
@@ -118,53 +129,52 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
         const __amdgpu_buffer_rsrc_t ra = gemm_rsrc(Ag + k0, max(abytes - 2 * k0, 0));
         const __amdgpu_buffer_rsrc_t rb = gemm_rsrc(Bg + k0, max(bbytes - 2 * k0, 0));
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            gemm_dma16(ra, Ad + 512 * (wave + 4 * n), voa[n]);
-            gemm_dma16(rb, Bd + 512 * (wave + 4 * n), vob[n]);
+        for (int n = 0; n < NCH; ++n) {
+            gemm_dma16(ra, Ad + 512 * (wave + NW * n), voa[n]);
+            gemm_dma16(rb, Bd + 512 * (wave + NW * n), vob[n]);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[NI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
     // fragment reads of k-step ks (K offset 16 ks) of one LDS buffer
-    int arow[4], brow[4];
+    int arow[NI], brow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        arow[i] = 128 * wm + 32 * i + l32;
-        brow[i] = 128 * wn + 32 * i + l32;
-    }
+    for (int i = 0; i < NI; ++i) arow[i] = WR * wm + 32 * i + l32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) brow[j] = 128 * wn + 32 * j + l32;
     // Fragments by k-step parity.  A K-tile's k-steps 0..2 run with the reads of
     // k-steps 1..3; then this wave waits for the next K-tile's DMA, the
     // workgroup meets (every read of this tile's buffer is done, so the DMA two
     // K-tiles ahead can go into it), and k-step 3 runs with the reads of the
     // next tile's k-step 0, so no tile starts on an LDS round trip.
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][NI], fb[2][4];
     auto frags = [&](auto bufc, int ks, bf16x8 *xa, bf16x8 *xb) {
         const uint16_t *As = decltype(bufc)::value ? A1 : A0;
         const uint16_t *Bs = decltype(bufc)::value ? B1 : B0;
         const int seg = 2 * ks + lh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(arow[i], seg)]);
+        for (int i = 0; i < NI; ++i) xa[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(arow[i], seg)]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(brow[j], seg)]);
     };
-    // sixteen products; the eight fragment reads issued just before go out one per product
+    // the k-step's products; the fragment reads issued just before go out one per product
     auto products = [&](const bf16x8 *xa, const bf16x8 *xb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
+        for (int n = 0; n < NR; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NR, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto head = [&](auto bufc) {   // k-steps 0 .. 2 of the tile in bufc
@@ -183,18 +193,19 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
         dma_tile(kn, dmac);
         const bf16x8 *xa = fa[1], *xb = fb[1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+        static_assert(2 * NCH == NMF, "one copy per product");
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
+        for (int n = 0; n < NR; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
+        for (int n = 0; n < NMF - NR; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
@@ -225,66 +236,81 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     __syncthreads();   // the epilogue stages through the K-tile buffers
 
     // ---- epilogue: register r of tile (i, j) holds
-    //      C[m0 + 128 wm + 32 i + 8 (r/4) + 4 lh + r%4][n0 + 128 wn + 32 j + l32] ----
+    //      C[m0 + WR wm + 32 i + 8 (r/4) + 4 lh + r%4][n0 + 128 wn + 32 j + l32] ----
+    // Blocks of SR rows of the wave's tile go through LDS, in the K-tile buffers,
+    // idle since the loop's last barrier: with four waves each wave has a buffer
+    // of its own and stages 32 rows, with eight two waves share one, 16 rows each.
+    constexpr int SR = NW == 4 ? 32 : 16;
+    constexpr int RP = 132;   // fp32 pitch of a staged row (16-byte rows, no 2-way conflict)
+    static_assert((NW / 4) * SR * RP * 4 <= BM * BK * 2, "staging fits a K-tile buffer");
+    const int sb = NW == 4 ? wave : wave >> 1;
+    float *stage = reinterpret_cast<float *>(sb == 0 ? A0 : (sb == 1 ? A1 : (sb == 2 ? B0 : B1))) +
+                   (NW == 4 ? 0 : (wave & 1) * SR * RP);
+    // rows [SR h, SR h + SR) of accumulator tile i into the stage: registers r of
+    // that block are SR/2 h .. SR/2 h + SR/2 - 1
+    auto stage_block = [&](int i, int h) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < SR / 2; ++r) {
+                const int rr = (SR / 2) * h + r;
+                stage[(8 * (rr >> 2) + 4 * lh + (rr & 3) - SR * h) * RP + 32 * j + l32] = acc[i][j][rr];
+            }
+    };
     const int nw = n0 + 128 * wn;   // first column of this wave
     if constexpr (EPI == EPI_PROJ) {
         const int Hd = po.H * po.d;
-        const int NR = po.g ? 4 : 3;                // head-width column blocks before the gates
-        if (nw < NR * Hd) {
+        const int NRB = po.g ? 4 : 3;               // head-width column blocks before the gates
+        if (nw < NRB * Hd) {
             // q, k, v or g columns; the wave's 128 columns hold whole heads (Hd % 128 == 0).
-            // One 32-row block at a time goes through LDS (the wave's own K-tile
-            // buffer, free since the loop's last barrier); a half-wave then holds a
-            // row, 4 columns per lane, so the per-head L2 norm is a reduction over
-            // the head's DH / 4 lanes and each lane stores 8 bytes.
+            // A half-wave holds a staged row, 4 columns per lane, so the per-head L2
+            // norm is a reduction over the head's DH / 4 lanes and each lane stores
+            // 8 bytes.
             const int region = nw / Hd;             // 0 q, 1 k, 2 v, 3 g
             uint16_t *dst = region == 0 ? po.q : (region == 1 ? po.k : (region == 2 ? po.v : po.g));
             const int c0 = nw - region * Hd + 4 * l32;
             const bool norm = region < 2 && po.norm;
-            constexpr int RP = 132;
-            float *stage = reinterpret_cast<float *>(wave == 0 ? A0 : (wave == 1 ? A1 : (wave == 2 ? B0 : B1)));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int h = 0; h < 32 / SR; ++h) {
+                    stage_block(i, h);
+                    const int mb = m0 + WR * wm + 32 * i + SR * h + lh;   // row of piece q is mb + 2 q
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        stage[(8 * (r >> 2) + 4 * lh + (r & 3)) * RP + 32 * j + l32] = acc[i][j][r];
-                const int mb = m0 + 128 * wm + 32 * i + lh;   // row of piece q is mb + 2 q
+                    for (int q = 0; q < SR / 2; ++q) {
+                        const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
+                        float x[4] = {c.x, c.y, c.z, c.w};
+                        if (norm) {
+                            float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
-                    float x[4] = {c.x, c.y, c.z, c.w};
-                    if (norm) {
-                        float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+                            for (int o = 1; o < DH / 4; o <<= 1) ss += __shfl_xor(ss, o);
+                            const float sc = 1.f / fmaxf(sqrtf(ss), 1e-6f);
 #pragma unroll
-                        for (int o = 1; o < DH / 4; o <<= 1) ss += __shfl_xor(ss, o);
-                        const float sc = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+                            for (int e = 0; e < 4; ++e) x[e] *= sc;
+                        } else if (region == 3) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] *= sc;
-                    } else if (region == 3) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = sigmoidf_acc(x[e]);
-                    }
-                    const int m = mb + 2 * q;
-                    if (m < M) {
-                        uint2 u;
-                        u.x = (uint32_t)bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
-                        u.y = (uint32_t)bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
-                        *reinterpret_cast<uint2 *>(&dst[(size_t)m * Hd + c0]) = u;
+                            for (int e = 0; e < 4; ++e) x[e] = sigmoidf_acc(x[e]);
+                        }
+                        const int m = mb + 2 * q;
+                        if (m < M) {
+                            uint2 u;
+                            u.x = (uint32_t)bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
+                            u.y = (uint32_t)bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
+                            *reinterpret_cast<uint2 *>(&dst[(size_t)m * Hd + c0]) = u;
+                        }
                     }
                 }
-            }
         } else {
             // gate columns: beta (first H) and alpha (next H)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < NI; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int c = nw + 32 * j + l32 - NR * Hd;
+                    const int c = nw + 32 * j + l32 - NRB * Hd;
                     if (!po.beta || c >= 2 * po.H) continue;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int m = m0 + 128 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int m = m0 + WR * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
                         if (m >= M) continue;
                         const float z = acc[i][j][r];
                         if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoidf_acc(z);
@@ -293,44 +319,39 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
                 }
         }
     } else {
-        // Residual update, one 32-row block of the wave's 128 x 128 quadrant at a
-        // time: the block goes through LDS (the wave's own K-tile buffer, free since
-        // the loop's last barrier) so that h is read and written as whole 512-byte
-        // row pieces, 16 float4 per lane, all loads of a block in flight together.
-        // N is a multiple of 128, so a wave's columns are all in range or all out.
+        // Residual update, one staged block at a time, so that h is read and
+        // written as whole 512-byte row pieces, all loads of a block in flight
+        // together.  N is a multiple of 128, so a wave's columns are all in range
+        // or all out.
         if (nw >= N) return;
-        constexpr int RP = 132;   // fp32 pitch of a staged row (16-byte rows, no 2-way conflict)
-        float *stage = reinterpret_cast<float *>(wave == 0 ? A0 : (wave == 1 ? A1 : (wave == 2 ? B0 : B1)));
         const int n = nw + 4 * l32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int h = 0; h < 32 / SR; ++h) {
+                stage_block(i, h);
+                const int mb = m0 + WR * wm + 32 * i + SR * h + lh;   // row of piece q is mb + 2 q
+                float4 hv[SR / 2];
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    stage[(8 * (r >> 2) + 4 * lh + (r & 3)) * RP + 32 * j + l32] = acc[i][j][r];
-            const int mb = m0 + 128 * wm + 32 * i + lh;   // row of piece q is mb + 2 q
-            float4 hv[16];
+                for (int q = 0; q < SR / 2; ++q) {
+                    const int m = min(mb + 2 * q, M - 1);    // rows past M load row M - 1, store nothing
+                    hv[q] = *reinterpret_cast<const float4 *>(&ro.h[(size_t)m * N + n]);
+                }
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int m = min(mb + 2 * q, M - 1);    // rows past M load row M - 1, store nothing
-                hv[q] = *reinterpret_cast<const float4 *>(&ro.h[(size_t)m * N + n]);
-            }
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
-                const float4 hn = make_float4(hv[q].x + c.x, hv[q].y + c.y, hv[q].z + c.z, hv[q].w + c.w);
-                const int m = mb + 2 * q;
-                if (m < M) {
-                    const size_t o = (size_t)m * N + n;
-                    *reinterpret_cast<float4 *>(&ro.h[o]) = hn;
-                    uint2 u;
-                    u.x = (uint32_t)bf16_bits(hn.x) | ((uint32_t)bf16_bits(hn.y) << 16);
-                    u.y = (uint32_t)bf16_bits(hn.z) | ((uint32_t)bf16_bits(hn.w) << 16);
-                    *reinterpret_cast<uint2 *>(&ro.xb[o]) = u;
+                for (int q = 0; q < SR / 2; ++q) {
+                    const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
+                    const float4 hn = make_float4(hv[q].x + c.x, hv[q].y + c.y, hv[q].z + c.z, hv[q].w + c.w);
+                    const int m = mb + 2 * q;
+                    if (m < M) {
+                        const size_t o = (size_t)m * N + n;
+                        *reinterpret_cast<float4 *>(&ro.h[o]) = hn;
+                        uint2 u;
+                        u.x = (uint32_t)bf16_bits(hn.x) | ((uint32_t)bf16_bits(hn.y) << 16);
+                        u.y = (uint32_t)bf16_bits(hn.z) | ((uint32_t)bf16_bits(hn.w) << 16);
+                        *reinterpret_cast<uint2 *>(&ro.xb[o]) = u;
+                    }
                 }
             }
-        }
     }
 }
 
@@ -582,9 +603,9 @@ hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, 
     }
     const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
     if (d == 64)
-        hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_PROJ, 64>), dim3(grid), dim3(256), 0, s, X, W, M, N, K, K, K, po, ro);
+        hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_PROJ, 64, GEMM_NW>), dim3(grid), dim3(64 * GEMM_NW), 0, s, X, W, M, N, K, K, K, po, ro);
     else
-        hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_PROJ, 128>), dim3(grid), dim3(256), 0, s, X, W, M, N, K, K, K, po, ro);
+        hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_PROJ, 128, GEMM_NW>), dim3(grid), dim3(64 * GEMM_NW), 0, s, X, W, M, N, K, K, K, po, ro);
     return hipGetLastError();
 }
 
@@ -606,7 +627,7 @@ hipError_t launch_gemm_resid(const uint16_t *O, const uint16_t *W, int M, int N,
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_RESID, 128>), dim3(grid), dim3(256), 0, s, O, W, M, N, K, K, K, po, ro);
+    hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_RESID, 128, GEMM_NW>), dim3(grid), dim3(64 * GEMM_NW), 0, s, O, W, M, N, K, K, K, po, ro);
     return hipGetLastError();
 }
 
