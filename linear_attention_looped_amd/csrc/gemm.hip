@@ -45,6 +45,24 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int GEMM_NW = 8;   // waves of the large-tile kernel
+constexpr int SHORT_M = 64;  // rows of a short tile
+
+// Tiles of the large kernel: full 256 x 256 tiles of the columns below N's last
+// multiple of 256, then, when the columns left over are 32 or fewer (the
+// projection's gate-transform columns), 64-row short tiles of those columns:
+// such a column tile costs a whole tile's K loop of A (its products are few),
+// and 64-row pieces spread that stream over four times as many compute units.
+// Otherwise the last column tile is an ordinary (partial) one.  The short
+// tiles take the block indices after the full tiles', which the hardware
+// deals round-robin to the XCDs, so every XCD gets its share of both kinds.
+__host__ __device__ inline bool gemm_short_cols(int N) { return N % BN != 0 && N % BN <= 32; }
+__host__ __device__ inline int gemm_full_col_tiles(int N) {
+    return gemm_short_cols(N) ? N / BN : (N + BN - 1) / BN;
+}
+inline unsigned gemm_grid(int M, int N) {
+    const unsigned g = (unsigned)((M + BM - 1) / BM) * (unsigned)gemm_full_col_tiles(N);
+    return gemm_short_cols(N) ? g + (unsigned)((M + SHORT_M - 1) / SHORT_M) : g;
+}
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
@@ -63,6 +81,28 @@ struct ResidOut {
 
 __device__ __forceinline__ float sigmoidf_acc(float z) { return 1.f / (1.f + expf(-z)); }
 
+// Sum over aligned groups of NL = 16 or 32 lanes, result in every lane of the
+// group, by register moves only: DPP swaps within quads, mirrored half rows and
+// mirrored rows give 16-lane sums; v_permlane16_swap exchanges neighbouring
+// rows for 32.  (A shuffle per step would be an LDS round trip each.)
+template <int CTRL>
+__device__ __forceinline__ float gemm_dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int NL>
+__device__ __forceinline__ float lanes_sum(float x) {
+    static_assert(NL == 16 || NL == 32, "16- or 32-lane groups");
+    x += gemm_dpp<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += gemm_dpp<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += gemm_dpp<0x141>(x);   // row_half_mirror
+    x += gemm_dpp<0x140>(x);   // row_mirror
+    if constexpr (NL == 32) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    return x;
+}
+
 // Element offset of 16-byte segment `seg` of LDS row `r` (64 bf16 per row).
 __device__ __forceinline__ int swz(int r, int seg) {
     return r * BK + 8 * (seg ^ (r & 7) ^ ((r >> 3) & 1));
@@ -77,6 +117,65 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void *p, int n
 // lambda of a kernel template (the host pass would drop the kernel's stub).
 __device__ __forceinline__ void gemm_dma16(__amdgpu_buffer_rsrc_t r, uint16_t *dst, int voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
+}
+
+// A short tile: SHORT_M rows of the at most 32 columns past N's last multiple
+// of 256, which in a projection are the gate-transform columns (beta, alpha).
+// Its products are few, so the K-tile pipeline would leave it waiting out one
+// memory round trip per K-tile; instead each of the NW waves takes K / NW of
+// the depth and issues its fragment loads straight from memory, eight k-steps'
+// worth in flight together, and the NW partial 64 x 32 sums meet in LDS (red0
+// for waves 0-3, red1 for 4-7, 8 KiB each).  Rows past mlim and columns past N
+// load a clamped in-range row and are not stored.
+template <int NW>
+__device__ __forceinline__ void short_gate_tile(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+                                                int lda, int ldb, int K, int m0, int mlim, int n0, int N,
+                                                const ProjOut &po, float *red0, float *red1, int wave, int lane) {
+    static_assert(SHORT_M == 64, "two 32-row accumulator tiles");
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int KS = K / (16 * NW);   // k-steps per wave (K is a multiple of 128)
+    const int kw = wave * 16 * KS + 8 * lh;
+    const uint16_t *a0 = A + (size_t)min(m0 + l32, mlim - 1) * lda + kw;
+    const uint16_t *a1 = A + (size_t)min(m0 + 32 + l32, mlim - 1) * lda + kw;
+    const uint16_t *b0 = B + (size_t)min(n0 + l32, N - 1) * ldb + kw;
+    f32x16 c0 = {}, c1 = {};
+    constexpr int KB = 8;
+    for (int ks = 0; ks < KS; ks += KB) {
+        bf16x8 xa0[KB], xa1[KB], xb[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+            if (ks + u < KS) {
+                xa0[u] = *reinterpret_cast<const bf16x8 *>(a0 + 16 * (ks + u));
+                xa1[u] = *reinterpret_cast<const bf16x8 *>(a1 + 16 * (ks + u));
+                xb[u] = *reinterpret_cast<const bf16x8 *>(b0 + 16 * (ks + u));
+            }
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+            if (ks + u < KS) {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa0[u], xb[u], c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa1[u], xb[u], c1, 0, 0, 0);
+            }
+    }
+    // register r of tile i holds row 32 i + 8 (r/4) + 4 lh + r%4, column l32
+    float *red = (wave < 4 ? red0 : red1) + (wave & 3) * (SHORT_M * 32);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * lh + (r & 3);
+        red[row * 32 + l32] = c0[r];
+        red[(32 + row) * 32 + l32] = c1[r];
+    }
+    __syncthreads();
+    const int Hd = po.H * po.d, g0 = (po.g ? 4 : 3) * Hd;   // first gate-transform column
+    for (int o = wave * 64 + lane; o < SHORT_M * 32; o += 64 * NW) {
+        float z = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) z += (w < 4 ? red0 : red1)[(w & 3) * (SHORT_M * 32) + o];
+        const int m = m0 + (o >> 5), n = n0 + (o & 31), c = n - g0;
+        if (m < mlim && n < N && po.beta && c >= 0 && c < 2 * po.H) {
+            if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoidf_acc(z);
+            else po.alpha[(size_t)m * po.H + c - po.H] = sigmoidf_acc(-z);   // exp(-softplus(z))
+        }
+    }
 }
 
 // NW waves: 4 (wave tiles 128 x 128, one wave per SIMD) or 8 (wave tiles 64 x 128,
@@ -99,10 +198,27 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, lh = lane >> 5;
-    const int n_tiles = (N + BN - 1) / BN;
-    const int logical = xcd_logical(blockIdx.x, gridDim.x);
-    const int mt = logical / n_tiles, nt = logical % n_tiles;
-    const int m0 = mt * BM, n0 = nt * BN;
+    const int n_tiles = gemm_full_col_tiles(N);
+    const int full = ((M + BM - 1) / BM) * n_tiles;
+    int m0, n0, mrows;
+    if ((int)blockIdx.x < full) {
+        const int logical = xcd_logical(blockIdx.x, full);
+        m0 = (logical / n_tiles) * BM;
+        n0 = (logical % n_tiles) * BN;
+        mrows = min(M - m0, BM);
+    } else {   // short tile of the last columns
+        m0 = ((int)blockIdx.x - full) * SHORT_M;
+        n0 = n_tiles * BN;
+        mrows = min(M - m0, SHORT_M);
+    }
+    const int mlim = m0 + mrows;   // rows past this are zero in LDS and not stored
+    if constexpr (EPI == EPI_PROJ) {
+        if ((int)blockIdx.x >= full) {
+            short_gate_tile<NW>(A, B, lda, ldb, K, m0, mlim, n0, N, po, reinterpret_cast<float *>(A0),
+                                reinterpret_cast<float *>(A1), wave, lane);
+            return;
+        }
+    }
 
     // K-tiles (256 rows x 64 bf16 of A and of B) go from memory straight into LDS
     // by LDS-DMA buffer loads, 16 bytes per lane: wave w fills the 1 KiB chunks
@@ -120,7 +236,7 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
         voa[n] = 2 * (row * lda + 8 * lseg);
         vob[n] = 2 * (row * ldb + 8 * lseg);
     }
-    const int abytes = 2 * min(M - m0, BM) * lda, bbytes = 2 * min(N - n0, BN) * ldb;
+    const int abytes = 2 * mrows * lda, bbytes = 2 * min(N - n0, BN) * ldb;
     const uint16_t *Ag = A + (size_t)m0 * lda, *Bg = B + (size_t)n0 * ldb;
     auto dma_tile = [&](int kt, auto bufc) {
         uint16_t *Ad = decltype(bufc)::value ? A1 : A0;
@@ -147,93 +263,113 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     for (int i = 0; i < NI; ++i) arow[i] = WR * wm + 32 * i + l32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) brow[j] = 128 * wn + 32 * j + l32;
-    // Fragments by k-step parity.  A K-tile's k-steps 0..2 run with the reads of
-    // k-steps 1..3; then this wave waits for the next K-tile's DMA, the
-    // workgroup meets (every read of this tile's buffer is done, so the DMA two
-    // K-tiles ahead can go into it), and k-step 3 runs with the reads of the
-    // next tile's k-step 0, so no tile starts on an LDS round trip.
-    bf16x8 fa[2][NI], fb[2][4];
-    auto frags = [&](auto bufc, int ks, bf16x8 *xa, bf16x8 *xb) {
-        const uint16_t *As = decltype(bufc)::value ? A1 : A0;
-        const uint16_t *Bs = decltype(bufc)::value ? B1 : B0;
-        const int seg = 2 * ks + lh;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) xa[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(arow[i], seg)]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xb[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(brow[j], seg)]);
-    };
-    // the k-step's products; the fragment reads issued just before go out one per product
-    auto products = [&](const bf16x8 *xa, const bf16x8 *xb) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int n = 0; n < NR; ++n) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NR, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto head = [&](auto bufc) {   // k-steps 0 .. 2 of the tile in bufc
-#pragma unroll
-        for (int ks = 0; ks < BK / 16 - 1; ++ks) {
-            frags(bufc, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-            products(fa[ks & 1], fb[ks & 1]);
-        }
-    };
-    // k-step 3, with k-step 0 of the tile in nextc and the copies of K-tile kn
-    // into buffer dmac (empty views past the last tile), one copy per product so
-    // that the copies' issue time overlaps the matrix pipe
-    auto tail = [&](auto nextc, int kn, auto dmac) {
-        static_assert(BK / 16 == 4, "k-step 3 uses the odd fragment set");
-        frags(nextc, 0, fa[0], fb[0]);
-        dma_tile(kn, dmac);
-        const bf16x8 *xa = fa[1], *xb = fb[1];
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
-        static_assert(2 * NCH == NMF, "one copy per product");
-#pragma unroll
-        for (int n = 0; n < NR; ++n) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-#pragma unroll
-        for (int n = 0; n < NMF - NR; ++n) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
 
-    // K is a multiple of 128 (the looped drivers require d_model and H*d to be),
-    // so the K-tiles come in pairs, one per buffer
-    const int KT = K / BK;
-    const std::integral_constant<int, 0> c0{};
-    const std::integral_constant<int, 1> c1{};
-    dma_tile(0, c0);
-    dma_tile(1, c1);
-    wait_vmem_all();
-    __syncthreads();
-    frags(c0, 0, fa[0], fb[0]);
-    for (int kt = 0; kt < KT; kt += 2) {
-        head(c0);                         // K-tile kt
-        wait_vmem_all();                  // K-tile kt + 1 (buffer 1) has landed
+    // The K loop for a wave whose first NJ 32-column blocks hold columns in range
+    // (4; for the last columns' tiles 1; 0 for a wave with no rows or columns in
+    // range): the other blocks' products and the unused fragment reads are left
+    // out, the copies and barriers are not.
+    auto kloop = [&](auto njc) {
+        constexpr int NJ = decltype(njc)::value;
+        constexpr int NJB = NJ > 0 ? NJ : 1;
+        constexpr int NRJ = NJ > 0 ? NI + NJ : 0;   // fragment reads per k-step
+        constexpr int NMJ = NI * NJ;                // products per k-step
+        // Fragments by k-step parity.  A K-tile's k-steps 0..2 run with the reads
+        // of k-steps 1..3; then this wave waits for the next K-tile's DMA, the
+        // workgroup meets (every read of this tile's buffer is done, so the DMA
+        // two K-tiles ahead can go into it), and k-step 3 runs with the reads of
+        // the next tile's k-step 0, so no tile starts on an LDS round trip.
+        bf16x8 fa[2][NI], fb[2][NJB];
+        auto frags = [&](auto bufc, int ks, bf16x8 *xa, bf16x8 *xb) {
+            if constexpr (NJ > 0) {
+                const uint16_t *As = decltype(bufc)::value ? A1 : A0;
+                const uint16_t *Bs = decltype(bufc)::value ? B1 : B0;
+                const int seg = 2 * ks + lh;
+#pragma unroll
+                for (int i = 0; i < NI; ++i) xa[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(arow[i], seg)]);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) xb[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(brow[j], seg)]);
+            }
+        };
+        auto mul = [&](const bf16x8 *xa, const bf16x8 *xb) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+        };
+        // the k-step's products; the fragment reads issued just before go out one per product
+        auto products = [&](const bf16x8 *xa, const bf16x8 *xb) {
+            mul(xa, xb);
+            if constexpr (NJ == 4) {
+#pragma unroll
+                for (int n = 0; n < NRJ; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, NMJ - NRJ, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto head = [&](auto bufc) {   // k-steps 0 .. 2 of the tile in bufc
+#pragma unroll
+            for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+                frags(bufc, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+                products(fa[ks & 1], fb[ks & 1]);
+            }
+        };
+        // k-step 3, with k-step 0 of the tile in nextc and the copies of K-tile kn
+        // into buffer dmac (empty views past the last tile), one copy per product
+        // so that the copies' issue time overlaps the matrix pipe
+        auto tail = [&](auto nextc, int kn, auto dmac) {
+            static_assert(BK / 16 == 4, "k-step 3 uses the odd fragment set");
+            frags(nextc, 0, fa[0], fb[0]);
+            dma_tile(kn, dmac);
+            mul(fa[1], fb[1]);
+            if constexpr (NJ == 4) {
+                static_assert(2 * NCH == NMJ, "one copy per product");
+#pragma unroll
+                for (int n = 0; n < NRJ; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+#pragma unroll
+                for (int n = 0; n < NMJ - NRJ; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // K is a multiple of 128 (the looped drivers require d_model and H*d to be),
+        // so the K-tiles come in pairs, one per buffer
+        const int KT = K / BK;
+        const std::integral_constant<int, 0> c0{};
+        const std::integral_constant<int, 1> c1{};
+        dma_tile(0, c0);
+        dma_tile(1, c1);
+        wait_vmem_all();
         __syncthreads();
-        tail(c1, min(kt + 2, KT), c0);    // K-tile kt + 2 into buffer 0
-        head(c1);                         // K-tile kt + 1
-        wait_vmem_all();                  // K-tile kt + 2 (buffer 0) has landed
-        __syncthreads();
-        tail(c0, min(kt + 3, KT), c1);    // past the last tile its reads are stale and unused
-    }
-    wait_vmem_all();   // the empty copies past the last tile have landed
-    __syncthreads();   // the epilogue stages through the K-tile buffers
+        frags(c0, 0, fa[0], fb[0]);
+        for (int kt = 0; kt < KT; kt += 2) {
+            head(c0);                         // K-tile kt
+            wait_vmem_all();                  // K-tile kt + 1 (buffer 1) has landed
+            __syncthreads();
+            tail(c1, min(kt + 2, KT), c0);    // K-tile kt + 2 into buffer 0
+            head(c1);                         // K-tile kt + 1
+            wait_vmem_all();                  // K-tile kt + 2 (buffer 0) has landed
+            __syncthreads();
+            tail(c0, min(kt + 3, KT), c1);    // past the last tile its reads are stale and unused
+        }
+        wait_vmem_all();   // the empty copies past the last tile have landed
+        __syncthreads();   // the epilogue stages through the K-tile buffers
+    };
+    // columns and rows of this wave in range (wave-uniform)
+    const int wcols = N - n0 - 128 * wn, wrows = mlim - m0 - WR * wm;
+    if (wrows > 0 && wcols > 32) kloop(std::integral_constant<int, 4>{});
+    else if (wrows > 0 && wcols > 0) kloop(std::integral_constant<int, 1>{});
+    else kloop(std::integral_constant<int, 0>{});
 
     // ---- epilogue: register r of tile (i, j) holds
     //      C[m0 + WR wm + 32 i + 8 (r/4) + 4 lh + r%4][n0 + 128 wn + 32 j + l32] ----
@@ -270,36 +406,43 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
             uint16_t *dst = region == 0 ? po.q : (region == 1 ? po.k : (region == 2 ? po.v : po.g));
             const int c0 = nw - region * Hd + 4 * l32;
             const bool norm = region < 2 && po.norm;
+            // one straight-line pass per transform (0 none, 1 L2 norm, 2 sigmoid),
+            // the choice made once per wave
+            auto blocks = [&](auto modec) {
+                constexpr int MODE = decltype(modec)::value;
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
+                for (int i = 0; i < NI; ++i)
 #pragma unroll
-                for (int h = 0; h < 32 / SR; ++h) {
-                    stage_block(i, h);
-                    const int mb = m0 + WR * wm + 32 * i + SR * h + lh;   // row of piece q is mb + 2 q
+                    for (int h = 0; h < 32 / SR; ++h) {
+                        stage_block(i, h);
+                        const int mb = m0 + WR * wm + 32 * i + SR * h + lh;   // row of piece q is mb + 2 q
 #pragma unroll
-                    for (int q = 0; q < SR / 2; ++q) {
-                        const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
-                        float x[4] = {c.x, c.y, c.z, c.w};
-                        if (norm) {
-                            float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+                        for (int q = 0; q < SR / 2; ++q) {
+                            const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
+                            float x[4] = {c.x, c.y, c.z, c.w};
+                            if constexpr (MODE == 1) {
+                                const float ss =
+                                    lanes_sum<DH / 4>(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
+                                const float sc = 1.f / fmaxf(sqrtf(ss), 1e-6f);
 #pragma unroll
-                            for (int o = 1; o < DH / 4; o <<= 1) ss += __shfl_xor(ss, o);
-                            const float sc = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+                                for (int e = 0; e < 4; ++e) x[e] *= sc;
+                            } else if constexpr (MODE == 2) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) x[e] *= sc;
-                        } else if (region == 3) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) x[e] = sigmoidf_acc(x[e]);
-                        }
-                        const int m = mb + 2 * q;
-                        if (m < M) {
-                            uint2 u;
-                            u.x = (uint32_t)bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
-                            u.y = (uint32_t)bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
-                            *reinterpret_cast<uint2 *>(&dst[(size_t)m * Hd + c0]) = u;
+                                for (int e = 0; e < 4; ++e) x[e] = sigmoidf_acc(x[e]);
+                            }
+                            const int m = mb + 2 * q;
+                            if (m < mlim) {
+                                uint2 u;
+                                u.x = (uint32_t)bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
+                                u.y = (uint32_t)bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
+                                *reinterpret_cast<uint2 *>(&dst[(size_t)m * Hd + c0]) = u;
+                            }
                         }
                     }
-                }
+            };
+            if (norm) blocks(std::integral_constant<int, 1>{});
+            else if (region == 3) blocks(std::integral_constant<int, 2>{});
+            else blocks(std::integral_constant<int, 0>{});
         } else {
             // gate columns: beta (first H) and alpha (next H)
 #pragma unroll
@@ -311,7 +454,7 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int m = m0 + WR * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                        if (m >= M) continue;
+                        if (m >= mlim) continue;
                         const float z = acc[i][j][r];
                         if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoidf_acc(z);
                         else po.alpha[(size_t)m * po.H + c - po.H] = sigmoidf_acc(-z);  // exp(-softplus(z))
@@ -334,7 +477,7 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
                 float4 hv[SR / 2];
 #pragma unroll
                 for (int q = 0; q < SR / 2; ++q) {
-                    const int m = min(mb + 2 * q, M - 1);    // rows past M load row M - 1, store nothing
+                    const int m = min(mb + 2 * q, mlim - 1);   // rows past the tile's load its last, store nothing
                     hv[q] = *reinterpret_cast<const float4 *>(&ro.h[(size_t)m * N + n]);
                 }
 #pragma unroll
@@ -342,7 +485,7 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
                     const float4 c = *reinterpret_cast<const float4 *>(&stage[(2 * q + lh) * RP + 4 * l32]);
                     const float4 hn = make_float4(hv[q].x + c.x, hv[q].y + c.y, hv[q].z + c.z, hv[q].w + c.w);
                     const int m = mb + 2 * q;
-                    if (m < M) {
+                    if (m < mlim) {
                         const size_t o = (size_t)m * N + n;
                         *reinterpret_cast<float4 *>(&ro.h[o]) = hn;
                         uint2 u;
@@ -601,7 +744,7 @@ hipError_t launch_gemm_proj(const uint16_t *X, const uint16_t *W, int M, int N, 
                                    ro);
         return hipGetLastError();
     }
-    const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
+    const unsigned grid = gemm_grid(M, N);
     if (d == 64)
         hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_PROJ, 64, GEMM_NW>), dim3(grid), dim3(64 * GEMM_NW), 0, s, X, W, M, N, K, K, K, po, ro);
     else
@@ -626,7 +769,7 @@ hipError_t launch_gemm_resid(const uint16_t *O, const uint16_t *W, int M, int N,
             hipLaunchKernelGGL((gemm_small_kernel<EPI_RESID, 128, 0>), dim3(sg), dim3(256), 0, s, O, W, M, N, K, po, ro);
         return hipGetLastError();
     }
-    const unsigned grid = (unsigned)((M + BM - 1) / BM) * (unsigned)((N + BN - 1) / BN);
+    const unsigned grid = gemm_grid(M, N);
     hipLaunchKernelGGL((gemm_bf16_nt_kernel<EPI_RESID, 128, GEMM_NW>), dim3(grid), dim3(64 * GEMM_NW), 0, s, O, W, M, N, K, K, K, po, ro);
     return hipGetLastError();
 }

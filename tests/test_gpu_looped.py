@@ -166,6 +166,23 @@ def test_looped_output_gate_two_tiles_per_workgroup():
     assert rel_err(got, ref) <= TOL_BF16
     assert rel_err(got - h0, ref - h0) <= TOL_BF16
 
+@pytest.mark.parametrize("L,D,H,d,gate", [(4000, 1024, 4, 128, True), (4000, 1024, 4, 128, False),
+                                           (3000, 1024, 8, 64, True)])
+def test_looped_large_tiles_ragged_rows(L, D, H, d, gate):
+    """Shapes with enough 256 x 256 tiles for the large GEMM kernel (the smaller
+    cases above run the small-M one), with rows that fill neither its 256-row
+    tiles nor the 64-row short tiles of the last columns (the 2H gate-transform
+    columns past N's last multiple of 256); gated and ungated, d = 128 and 64."""
+    shape = synth.LoopShape(1, L, D, H, d, 1)
+    announce(f"looped large tiles L={L} D={D} H={H} d={d} gate={gate}")
+    w = synth.loop_weights(shape, seed=11, gate=gate)
+    h0 = synth.loop_h0(shape, seed=11)
+    got = run_looped(h0, w, shape, gate=gate)
+    ref = oracle.looped_mixer(h0, w["w_in"], w["w_o"], H, d, 1, gate=gate)
+    assert rel_err(got, ref) <= TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
+
+
 def test_gated_looped_decode_chain_matches_mixer():
     shape = synth.LoopShape(2, 20, 256, 2, 128, 2)
     announce("gated looped decode chain")
