@@ -1166,7 +1166,13 @@ __global__ __launch_bounds__(512) void scan_head_bf16_kernel(const uint16_t *__r
 // output product P U of a chunk is off the recurrence: the state waves take it
 // in the next chunk's phase, beside that chunk's K S and Q S, from 2^g X_Q and
 // U carried in registers and P left in its buffer, so one barrier per chunk
-// suffices and the recurrence never waits for P.
+// suffices and the recurrence never waits for P.  Where the LDS holds the
+// carries (one tile per workgroup, or two without the gate image and with bf16
+// outputs), a separate output wave takes X_Q and the output product instead:
+// the state waves leave each new state's split and each U in LDS, and the
+// output wave forms chunk n's 2^g Q S in phase n (Q still resident) and its
+// P U, gating and stores in phase n + 1, so the state waves carry the
+// recurrence alone (82 of the 116 products per chunk).
 // The state waves issue no global loads or stores: the loader wave copies the
 // chunk's read-only operands (K, Q, the lower Tm fragments, the workgroup's V
 // and gate columns, the gate prefix and decay vectors) from global memory
@@ -1194,14 +1200,15 @@ __device__ __forceinline__ int col_swz(int r) {
 // LDS rows instead of rows four apart (the same banks for 64-byte rows).
 __device__ __forceinline__ int tok_row(int t) { return (t & ~15) | ((t & 3) << 2) | ((t >> 2) & 3); }
 
-// One chunk's operands in LDS (16-bit elements unless stated).
-template <int NWV>
+// One chunk's operands in LDS (16-bit elements unless stated); without the
+// output gate the gate image shrinks to a stub.
+template <int NWV, bool GATE>
 struct ColChunk {
     uint16_t K[64 * 128];       // swizzled rows
     uint16_t Q[64 * 128];       // swizzled rows
     uint16_t F[24 * 512];       // Tm, P lower-block fragments, 1 KiB each: ((m * 6 + pair) * 2 + hl)
     uint16_t V[64 * 16 * NWV];  // the workgroup's V columns, token t in row tok_row(t)
-    uint16_t G[64 * 16 * NWV];  // output-gate values, same layout
+    uint16_t G[GATE ? 64 * 16 * NWV : 8];   // output-gate values, same layout
     double GS[64];              // g, the chunk-relative log2 gate prefix
     float E[128];               // 2^g [64] | 2^(gC - g) [64] (follows GS, as in the workspace)
 };
@@ -1413,8 +1420,185 @@ __device__ __forceinline__ void scan_chunk_out(const uint16_t *cF, ColCarry<GATE
     }
 }
 
-template <int NWV, int NLD, bool GATE, typename TO>
-__global__ __launch_bounds__(64 * (NWV + 1 + NLD))
+// With a separate output wave (OW) the state wave keeps only the recurrence:
+// X_K = K S from the split state (sh, sl: S's hi and lo halves as B operands,
+// split at the end of the previous chunk), R, U = Tm R (U's hi and lo halves
+// left in ubw for the output wave), the state update, and the split of the
+// new state (kept in sh, sl for the next chunk and left in sbw for the output
+// wave's X_Q: the hi half, and the lo half too for QLO).  LDS carries are
+// [slot][64 lanes] of 16 bytes, each lane its own, so no bank conflicts.
+template <int VW, bool QLO>
+__device__ __forceinline__ void scan_chunk_st(const uint16_t *cK, const uint16_t *cF, const uint16_t *cV,
+                                              const float *cE, f32x4 (&S)[8], bf16x8 (&sh)[4], bf16x8 (&sl)[4],
+                                              uint4 *ubw, uint4 *sbw, int tile, int lane) {
+    constexpr int C = 64;
+    const int c = lane & 15, g = lane >> 4;
+    const int gp = ((g & 1) << 1) | (g >> 1);
+    f32x4 xk[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) xk[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const int r = 16 * I + c;
+            const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(&cK[r * 128 + 8 * ((4 * kb + gp) ^ col_swz(r))]);
+            xk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sh[kb], xk[I], 0, 0, 0);
+            xk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sl[kb], xk[I], 0, 0, 0);
+        }
+    // R = V - 2^g X_K
+    f32x4 R[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const f32x4 ev = *reinterpret_cast<const f32x4 *>(&cE[16 * I + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            R[I][r] = bf16_to_f32(cV[(16 * I + 4 * r + g) * VW + 16 * tile + c]) - ev[r] * xk[I][r];   // row tok_row(t)
+    }
+    // U = Tm R over the lower K-blocks
+    bf16x8 rh[2], rl[2];
+    pair_split(R[0], R[1], rh[0], rl[0]);
+    pair_split(R[2], R[3], rh[1], rl[1]);
+    f32x4 U[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        U[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb <= I / 2; ++kb) {
+            const int pr = I < 2 ? I : 2 + 2 * (I - 2) + kb;
+            const bf16x8 th = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr) + 8 * lane]);
+            const bf16x8 tl = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr + 1) + 8 * lane]);
+            U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rh[kb], U[I], 0, 0, 0);
+            U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, rh[kb], U[I], 0, 0, 0);
+            U[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, rl[kb], U[I], 0, 0, 0);
+        }
+    }
+    // U (to the output wave) and U2 = 2^(gC - g) U as B operands
+    bf16x8 u2h[2], u2l[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        float x[8], x2[8];
+        pair_rows(U[2 * kb], U[2 * kb + 1], x);
+        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&cE[64 + 32 * kb + 8 * gp]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&cE[64 + 32 * kb + 8 * gp + 4]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            x2[s] = w0[s] * x[s];
+            x2[4 + s] = w1[s] * x[4 + s];
+        }
+        uint4 hh, ll;
+        split8(x, hh, ll);
+        ubw[(2 * kb) * 64 + lane] = hh;
+        ubw[(2 * kb + 1) * 64 + lane] = ll;
+        split8(x2, hh, ll);
+        u2h[kb] = as_bf16x8(hh);
+        u2l[kb] = as_bf16x8(ll);
+    }
+    // S = 2^gC S + K^T U2
+    const float ec = cE[C - 1];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[m][r] *= ec;
+    const int te = c >> 2, tm = c & 3;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int r0 = 32 * kb + 8 * gp + te, r1 = r0 + 4;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int blk = 2 * m + (tm >> 1), sub = 4 * (tm & 1);
+            const short4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4 *)(&cK[r0 * 128 + 8 * (blk ^ col_swz(r0)) + sub]));
+            const short4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4 *)(&cK[r1 * 128 + 8 * (blk ^ col_swz(r1)) + sub]));
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, (__attribute__((ext_vector_type(8))) short){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1],
+                                                                    hi4[2], hi4[3]});
+            S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2h[kb], S[m], 0, 0, 0);
+            S[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u2l[kb], S[m], 0, 0, 0);
+        }
+    }
+    // the new state's split, for the next chunk here and its X_Q in the output wave
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        pair_split(S[2 * kb], S[2 * kb + 1], sh[kb], sl[kb]);
+        sbw[kb * 64 + lane] = __builtin_bit_cast(uint4, sh[kb]);
+        if constexpr (QLO) sbw[(4 + kb) * 64 + lane] = __builtin_bit_cast(uint4, sl[kb]);
+    }
+}
+
+// Output wave, chunk n's first half in phase n: O = 2^g X_Q, X_Q = Q S with the
+// state split the state wave of column tile `tile` left in sbr (Q and the
+// decay vector from chunk n's buffer).  QLO: S's lo half too.
+template <bool QLO>
+__device__ __forceinline__ void out_xq(const uint16_t *cQ, const float *cE, const uint4 *sbr, f32x4 (&O)[4],
+                                       int lane) {
+    const int c = lane & 15, g = lane >> 4;
+    const int gp = ((g & 1) << 1) | (g >> 1);
+    f32x4 xq[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) xq[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 sh = __builtin_bit_cast(bf16x8, sbr[kb * 64 + lane]);
+        bf16x8 sl;
+        if constexpr (QLO) sl = __builtin_bit_cast(bf16x8, sbr[(4 + kb) * 64 + lane]);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const int r = 16 * I + c;
+            const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(&cQ[r * 128 + 8 * ((4 * kb + gp) ^ col_swz(r))]);
+            xq[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sh, xq[I], 0, 0, 0);
+            if constexpr (QLO) xq[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, sl, xq[I], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const f32x4 ev = *reinterpret_cast<const f32x4 *>(&cE[16 * I + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[I][r] = ev[r] * xq[I][r];
+    }
+}
+
+// Output wave, chunk n's second half in phase n + 1: O += P U (P's lower A
+// fragments in chunk n's buffer, U from the state wave in ubr), gated, stored
+// straight to memory by bounds-checked buffer stores (rows past L dropped):
+// element (token 16 I + 4 g + r, column `colb` bytes into the row).
+template <bool GATE, typename TO>
+__device__ __forceinline__ void out_pu(const uint16_t *cF, const uint4 *ubr, const f32x4 (&Oc)[4], const float *gv,
+                                       __amdgpu_buffer_rsrc_t ors, unsigned tokb, unsigned colb, unsigned soff,
+                                       int lane) {
+    const int g = lane >> 4;
+    bf16x8 uh[2], ul[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        uh[kb] = __builtin_bit_cast(bf16x8, ubr[(2 * kb) * 64 + lane]);
+        ul[kb] = __builtin_bit_cast(bf16x8, ubr[(2 * kb + 1) * 64 + lane]);
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        f32x4 O = Oc[I];
+#pragma unroll
+        for (int kb = 0; kb <= I / 2; ++kb) {
+            const int pr = 6 + (I < 2 ? I : 2 + 2 * (I - 2) + kb);
+            const bf16x8 ph = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr) + 8 * lane]);
+            const bf16x8 pl = *reinterpret_cast<const bf16x8 *>(&cF[512 * (2 * pr + 1) + 8 * lane]);
+            O = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, uh[kb], O, 0, 0, 0);
+            O = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, uh[kb], O, 0, 0, 0);
+            O = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ul[kb], O, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float o = O[r];
+            if constexpr (GATE) o *= gv[4 * I + r];
+            store_buf<TO>(o, ors, (unsigned)(16 * I + 4 * g + r) * tokb + colb, soff);
+        }
+    }
+}
+
+// OW: a separate output wave (after the P wave) takes the outputs, so the state
+// waves carry the recurrence alone (scan_chunk_st, out_xq, out_pu).
+template <int NWV, int NLD, bool GATE, typename TO, bool OW>
+__global__ __launch_bounds__(64 * (NWV + 1 + OW + NLD))
 void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                           const uint16_t *__restrict__ v, const unsigned char *__restrict__ ws,
                           const float *state_in, TO *__restrict__ out, float *state_out, int L, int H, int NC,
@@ -1425,8 +1609,14 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     using FLY = FragLayout<C>;
     static_assert(FLY::on && (NWV == 1 || NWV == 2 || NWV == 4), "column scan layout");
     static_assert(NLD == 1 || NLD == 2, "loader waves split 16 K / Q pieces, 12 Tm fragments, 2 NWV V pieces");
-    __shared__ __attribute__((aligned(16))) ColChunk<NWV> lds0, lds1;
-    __shared__ __attribute__((aligned(16))) TO osb0[64 * 16 * NWV], osb1[64 * 16 * NWV];   // staged outputs
+    __shared__ __attribute__((aligned(16))) ColChunk<NWV, GATE> lds0, lds1;
+    // staged outputs (without an output wave)
+    __shared__ __attribute__((aligned(16))) TO osb0[OW ? 8 : 64 * 16 * NWV], osb1[OW ? 8 : 64 * 16 * NWV];
+    // with an output wave: each state wave's split state and U, by chunk parity
+    constexpr bool QLO = !std::is_same<TO, uint16_t>::value;
+    constexpr int SBN = QLO ? 8 : 4;   // 16-byte slots of a split state (hi; and lo for QLO)
+    __shared__ __attribute__((aligned(16))) uint4 sbuf0[OW ? NWV * SBN * 64 : 1], sbuf1[OW ? NWV * SBN * 64 : 1];
+    __shared__ __attribute__((aligned(16))) uint4 ubuf0[OW ? NWV * 4 * 64 : 1], ubuf1[OW ? NWV * 4 * 64 : 1];
 
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int vb = logical % NB;
@@ -1434,9 +1624,10 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     const int h = (int)(unit % H), b = (int)(unit / H);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // waves 0 .. NWV - 1: state (one column tile each); NWV: P; the rest: copies
-    const bool loader = wave > NWV;
-    const int li = wave - NWV - 1;                  // loader index
+    // waves 0 .. NWV - 1: state (one column tile each); NWV: P; NWV + 1: outputs
+    // (with OW); the rest: copies
+    const bool loader = wave > NWV + (OW ? 1 : 0);
+    const int li = wave - NWV - 1 - (OW ? 1 : 0);   // loader index
     const int c = lane & 15, g = lane >> 4;
     const int vw0 = VW * vb;                        // first V column of the workgroup
     const int col = vw0 + 16 * wave + c;            // a compute lane's state and output column
@@ -1458,7 +1649,7 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     // Tm fragments of the six lower (tile, K-block) pairs, 1 KiB pieces of the
     // [64][VW] V and gate images, token t in row tok_row(t)) and, from loader 0,
     // the gate prefix and decay vectors.
-    auto issue_all = [&](int n, ColChunk<NWV> &cb) __attribute__((always_inline)) {
+    auto issue_all = [&](int n, ColChunk<NWV, GATE> &cb) __attribute__((always_inline)) {
         const unsigned sk = (unsigned)(n * C) * tok * 2u;   // byte offset of the chunk's first token
         const unsigned sw = (unsigned)n * WSB;
 #pragma unroll
@@ -1512,7 +1703,7 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     // row t per tile: the state's pair regrouping of two such tiles then gives
     // the A fragment of a (row tile, K-block) pair in registers.
     if (wave == NWV) {
-        auto pstep = [&](int j, ColChunk<NWV> &cb) __attribute__((always_inline)) {
+        auto pstep = [&](int j, ColChunk<NWV, GATE> &cb) __attribute__((always_inline)) {
             const int Lc = min(C, L - j * C);
             bf16x8 kf[4][4];   // K rows 16 J + c, columns 32 kb + 8 g .. + 7
 #pragma unroll
@@ -1577,15 +1768,61 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
         __syncthreads();   // barrier NC + 1
         return;
     }
+    if constexpr (OW) {
+        // Output wave: after barrier n, chunk n - 1's output product and stores
+        // (its P in lds((n - 1) & 1), its U in ubuf((n - 1) & 1)), then chunk n's
+        // 2^g Q S (its Q in lds(n & 1), its state split in sbuf(n & 1)), carried
+        // in registers to the next phase with the chunk's gate values.
+        if (wave == NWV + 1) {
+            f32x4 Oc[NWV][4];
+            float gvc[NWV][GATE ? 16 : 1];
+            const unsigned tokb = tok * (unsigned)sizeof(TO);
+            auto second = [&](int n, const ColChunk<NWV, GATE> &pb, const uint4 *ub) __attribute__((always_inline)) {
+#pragma unroll
+                for (int w = 0; w < NWV; ++w)
+                    out_pu<GATE, TO>(pb.F, ub + w * 4 * 64, Oc[w], gvc[w], ors, tokb,
+                                     (unsigned)(vw0 + 16 * w + c) * (unsigned)sizeof(TO), (unsigned)(n * C) * tokb,
+                                     lane);
+            };
+            auto first = [&](const ColChunk<NWV, GATE> &cb, const uint4 *sb) __attribute__((always_inline)) {
+#pragma unroll
+                for (int w = 0; w < NWV; ++w) {
+                    out_xq<QLO>(cb.Q, cb.E, sb + w * SBN * 64, Oc[w], lane);
+                    if constexpr (GATE) {
+#pragma unroll
+                        for (int I = 0; I < 4; ++I)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)   // row tok_row(t)
+                                gvc[w][4 * I + r] = bf16_to_f32(cb.G[(16 * I + 4 * r + g) * VW + 16 * w + c]);
+                    }
+                }
+            };
+            for (int n = 0; n < NC; n += 2) {
+                __syncthreads();   // barrier n
+                if (n > 0) second(n - 1, lds1, ubuf1);
+                first(lds0, sbuf0);
+                if (n + 1 < NC) {
+                    __syncthreads();   // barrier n + 1
+                    second(n, lds0, ubuf0);
+                    first(lds1, sbuf1);
+                }
+            }
+            __syncthreads();   // barrier NC
+            if ((NC - 1) & 1) second(NC - 1, lds1, ubuf1);
+            else second(NC - 1, lds0, ubuf0);
+            __syncthreads();   // barrier NC + 1
+            return;
+        }
+    }
     if (loader) {
         // barrier n (n = 0 .. NC + 1): chunk n's copies have landed and chunk
         // n - 2's outputs are staged; the copies of chunk n + 1 and the stores
-        // of chunk n - 2 follow it
-        auto lstep = [&](int n, ColChunk<NWV> &nxt, const TO *ob) __attribute__((always_inline)) {
+        // of chunk n - 2 (without an output wave) follow it
+        auto lstep = [&](int n, ColChunk<NWV, GATE> &nxt, const TO *ob) __attribute__((always_inline)) {
             wait_vmem_all();
             __syncthreads();
             if (n < NC) issue_all(min(n + 1, NC - 1), nxt);
-            if (n >= 2) store_staged(n - 2, ob);
+            if (!OW && n >= 2) store_staged(n - 2, ob);
         };
         issue_all(0, lds0);
         for (int n = 0; n <= NC + 1; n += 2) {
@@ -1606,12 +1843,36 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
             for (int r = 0; r < 4; ++r) S[m][r] = state_in[((size_t)unit * D + 16 * m + 4 * g + r) * D + col];
     }
 
+    if constexpr (OW) {
+        // State waves with an output wave: chunk n's recurrence after barrier n,
+        // leaving U in ubuf(n & 1) and the next state's split in sbuf((n + 1) & 1);
+        // the initial state's split goes to sbuf0 before barrier 0.
+        bf16x8 sh[4], sl[4];
+        uint4 *const sb0 = sbuf0 + wave * SBN * 64, *const sb1 = sbuf1 + wave * SBN * 64;
+        uint4 *const ub0 = ubuf0 + wave * 4 * 64, *const ub1 = ubuf1 + wave * 4 * 64;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            pair_split(S[2 * kb], S[2 * kb + 1], sh[kb], sl[kb]);
+            sb0[kb * 64 + lane] = __builtin_bit_cast(uint4, sh[kb]);
+            if constexpr (QLO) sb0[(4 + kb) * 64 + lane] = __builtin_bit_cast(uint4, sl[kb]);
+        }
+        for (int n = 0; n < NC; n += 2) {
+            __syncthreads();   // barrier n
+            scan_chunk_st<VW, QLO>(lds0.K, lds0.F, lds0.V, lds0.E, S, sh, sl, ub0, sb1, wave, lane);
+            if (n + 1 < NC) {
+                __syncthreads();   // barrier n + 1
+                scan_chunk_st<VW, QLO>(lds1.K, lds1.F, lds1.V, lds1.E, S, sh, sl, ub1, sb0, wave, lane);
+            }
+        }
+        __syncthreads();   // barrier NC
+        __syncthreads();   // barrier NC + 1
+    } else {
     ColCarry<GATE> cr;
-    auto compute = [&](const ColChunk<NWV> &cb) __attribute__((always_inline)) {
+    auto compute = [&](const ColChunk<NWV, GATE> &cb) __attribute__((always_inline)) {
         scan_chunk<VW, GATE, !std::is_same<TO, uint16_t>::value>(cb.K, cb.Q, cb.F, cb.V, cb.G, cb.E, S, cr, wave,
                                                                   lane);
     };
-    auto finish = [&](const ColChunk<NWV> &cb, TO *ob) __attribute__((always_inline)) {
+    auto finish = [&](const ColChunk<NWV, GATE> &cb, TO *ob) __attribute__((always_inline)) {
         scan_chunk_out<VW, GATE, TO>(cb.F, cr, ob, wave, lane);
     };
 
@@ -1633,6 +1894,7 @@ void scan_head_col_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     if ((NC - 1) & 1) finish(lds1, osb1);
     else finish(lds0, osb0);
     __syncthreads();
+    }
 
     if (state_out) {
 #pragma unroll
@@ -1647,13 +1909,17 @@ size_t prefill_head_ws_bytes(int B, int L, int H, int C) {
     return (size_t)B * H * NC * (size_t)(8 * C * C + 12 * C);
 }
 
-// NWV state waves, the P wave and one loader wave: one wave per SIMD when NWV
-// is 2 (a loader's copies of a chunk take about half the chunk's time).
+// NWV state waves, the P wave, the output wave (OW) and one loader wave (a
+// loader's copies of a chunk take about half the chunk's time).
 template <int NWV, bool GATE, typename TO>
 static void launch_col(const GdnArgs &a, int NC, hipStream_t s) {
     constexpr int NLD = 1;
+    // the output wave's carries fit the LDS beside two tiles' chunk buffers only
+    // without the gate image and the fp32 state lo halves
+    constexpr bool OW = NWV == 1 || (!GATE && std::is_same<TO, uint16_t>::value);
     const unsigned units = (unsigned)a.B * (unsigned)a.H;
-    hipLaunchKernelGGL((scan_head_col_kernel<NWV, NLD, GATE, TO>), dim3(units * (8 / NWV)), dim3(64 * (NWV + 1 + NLD)),
+    hipLaunchKernelGGL((scan_head_col_kernel<NWV, NLD, GATE, TO, OW>), dim3(units * (8 / NWV)),
+                       dim3(64 * (NWV + 1 + (OW ? 1 : 0) + NLD)),
                        0, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const unsigned char *)a.ws,
                        a.state_in, (TO *)a.out, a.state_out, a.L, a.H, NC, a.gate);
