@@ -515,6 +515,14 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
 // row in the epilogue) for shapes with too few 64-row tiles to fill the GPU.
 constexpr int SBN = 128, SNS = 5;   // columns, LDS stages
 
+// Logical index of block `bid` of `n` such that each XCD (the hardware deals
+// blocks round-robin, block b to XCD b % 8) holds one contiguous run of logical
+// indices, for any n: XCD x takes n / 8 blocks, one more when x < n % 8.
+__device__ __forceinline__ int xcd_run(int bid, int n) {
+    const int q = n >> 3, r = n & 7, x = bid & 7;
+    return x * q + min(x, r) + (bid >> 3);
+}
+
 // SBM: tile rows (64; 32 for the residual product only); KTC: K-tiles known at
 // compile time (0: K at run time)
 template <int EPI, int DH, int KTC, int SBM = 64>
@@ -536,8 +544,11 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, lh = lane >> 5;
-    const int n_tiles = (N + SBN - 1) / SBN;
-    const int mt = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
+    // the row tiles sharing a weight panel are consecutive logical tiles, so
+    // one XCD's L2 fetches each panel once
+    const int m_tiles = (M + SBM - 1) / SBM;
+    const int logical = xcd_run(blockIdx.x, gridDim.x);
+    const int mt = logical % m_tiles, nt = logical / m_tiles;
     const int m0 = mt * SBM, n0 = nt * SBN;
 
     // lane i of a chunk writes bytes 16 i of it: row 8 c + i / 8, physical
