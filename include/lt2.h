@@ -349,16 +349,20 @@ lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream);
 typedef enum lt2_probe_mode {
     LT2_PROBE_COPY = 0,   /* read src, write dst */
     LT2_PROBE_READ = 1,   /* read src only (dst is not written in practice) */
-    LT2_PROBE_WRITE = 2   /* write dst only (src unused, may be NULL) */
+    LT2_PROBE_WRITE = 2,  /* write dst only (src unused, may be NULL) */
+    LT2_PROBE_TILE_COPY = 3   /* read src, write dst, each workgroup copying contiguous
+                                 tiles of 256 x unroll 16-byte elements, every load of a
+                                 tile issued before its stores */
 } lt2_probe_mode;
 
 /*
  * Bandwidth probe with a chosen launch shape, for finding the achievable HBM
  * bandwidth of each access pattern (the best over shapes is the measured
- * ceiling the memory-bound kernels are compared with).  One grid-stride
- * streaming kernel of `blocks` workgroups of 256 lanes (0 = the default of 16
- * per compute unit of a 256-CU device), each lane keeping `unroll` 16-byte
- * loads (or stores) in flight.
+ * ceiling the memory-bound kernels are compared with).  One streaming kernel
+ * of `blocks` workgroups of 256 lanes (0 = the default of 16 per compute unit
+ * of a 256-CU device), each lane keeping `unroll` 16-byte loads (or stores) in
+ * flight; grid-stride over single elements, or over whole tiles for
+ * LT2_PROBE_TILE_COPY.
  *   dst, src   device buffers of `bytes` bytes each (a multiple of 16),
  *              16-byte aligned; src may be NULL for LT2_PROBE_WRITE
  *   mode       lt2_probe_mode

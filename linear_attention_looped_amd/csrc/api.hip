@@ -235,7 +235,8 @@ lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream) 
 
 lt2_status lt2_hbm_probe(void *dst, const void *src, size_t bytes, int32_t mode, int32_t blocks, int32_t unroll,
                          void *stream) {
-    if (mode != LT2_PROBE_COPY && mode != LT2_PROBE_READ && mode != LT2_PROBE_WRITE) return LT2_ERR_UNSUPPORTED;
+    if (mode != LT2_PROBE_COPY && mode != LT2_PROBE_READ && mode != LT2_PROBE_WRITE && mode != LT2_PROBE_TILE_COPY)
+        return LT2_ERR_UNSUPPORTED;
     if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16) return LT2_ERR_UNSUPPORTED;
     if (bytes % 16 != 0 || blocks < 0 || blocks > 16777215) return LT2_ERR_SHAPE;
     if (bytes == 0) return LT2_OK;

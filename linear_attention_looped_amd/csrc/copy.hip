@@ -10,12 +10,33 @@ namespace lt2 {
 // MODE 1: read src only (each lane folds what it read into one value, written
 // to dst[global lane] only if the fold equals a value no input produces, so the
 // loads cannot be removed and nothing is written in practice); MODE 2: write a
-// constant to dst only.
+// constant to dst only; MODE 3: copy src -> dst by contiguous tiles of 256 x
+// UNROLL elements per workgroup (the access pattern of the decode step's state).
 template <int MODE, int UNROLL>
 __global__ __launch_bounds__(256) void probe_kernel(f32x4 *__restrict__ dst, const f32x4 *__restrict__ src,
                                                     size_t n) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     const size_t lane = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if constexpr (MODE == 3) {
+        // tiles of 256 * UNROLL consecutive elements, one workgroup each (tiles
+        // dealt grid-stride over the workgroups); all loads of a tile are issued
+        // before its stores
+        const size_t tile = (size_t)blockDim.x * UNROLL;
+        for (size_t base = (size_t)blockIdx.x * tile; base < n; base += (size_t)gridDim.x * tile) {
+            f32x4 r[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const size_t j = base + (size_t)u * blockDim.x + threadIdx.x;
+                if (j < n) r[u] = __builtin_nontemporal_load(src + j);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const size_t j = base + (size_t)u * blockDim.x + threadIdx.x;
+                if (j < n) __builtin_nontemporal_store(r[u], dst + j);
+            }
+        }
+        return;
+    }
     size_t i = lane;
     uint32_t fold = 0;
     for (; i + (UNROLL - 1) * stride < n; i += UNROLL * stride) {
@@ -70,6 +91,7 @@ hipError_t launch_probe(void *dst, const void *src, size_t bytes, int mode, unsi
     switch (mode) {
         case 1: return probe_u<1>(dst, src, n, blocks, unroll, s);
         case 2: return probe_u<2>(dst, src, n, blocks, unroll, s);
+        case 3: return probe_u<3>(dst, src, n, blocks, unroll, s);
         default: return probe_u<0>(dst, src, n, blocks, unroll, s);
     }
 }

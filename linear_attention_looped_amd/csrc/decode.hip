@@ -6,7 +6,8 @@
 //   o = S^T(alpha*q) - beta (q.(alpha*k)) S^T k + beta (q.k) v,
 // so the d_k x d_v fp32 state is read once and written once.
 //
-// One workgroup (256 lanes) per (b, h) unit.  Lane (rg, cg) owns four adjacent
+// One workgroup (256 lanes) per (b, h) unit, each streaming its own contiguous
+// state block.  Lane (rg, cg) owns four adjacent
 // columns 4cg..4cg+3 of rows rg, rg+RG, rg+2RG, ...: for every row step the
 // 256 lanes cover RG consecutive rows, one contiguous block of RG*d_v*4 bytes.
 // Column sums of k^T S and (alpha*q)^T S are reduced over the RG row groups in
@@ -62,6 +63,18 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const TI *__restrict__ 
     const int tid = threadIdx.x;
     const int cg = tid % CG, rg = tid / CG;
 
+    // The state's loads go out first (they do not wait for q, k and alpha).
+    // State loads and stores carry the non-temporal hint: each state block is
+    // touched once per launch, and with both hints the stream measured 92.5 us
+    // per 4096-unit launch against 106.7 us with neither (a non-temporal store
+    // alone was slower, 108.1 us).
+    float *S = state + u * (size_t)(DK * DV);
+    float4 s[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int row = rg + j * RG;
+        s[j] = __builtin_bit_cast(float4, __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + row * DV + 4 * cg)));
+    }
     for (int i = tid; i < DK; i += 256) {
         sq[i] = load1<TI>(q + u * DK + i);
         sk[i] = load1<TI>(k + u * DK + i);
@@ -69,14 +82,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const TI *__restrict__ 
     }
     __syncthreads();
 
-    float *S = state + u * (size_t)(DK * DV);
-    float4 s[RPT];
     float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-        const int row = rg + j * RG;
-        s[j] = *reinterpret_cast<const float4 *>(S + row * DV + 4 * cg);
-    }
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
         const int row = rg + j * RG;
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const TI *__restrict__ 
         n.y = a * (s[j].y - bk * kS.y) + bk * vv.y;
         n.z = a * (s[j].z - bk * kS.z) + bk * vv.z;
         n.w = a * (s[j].w - bk * kS.w) + bk * vv.w;
-        *reinterpret_cast<float4 *>(S + row * DV + 4 * cg) = n;
+        __builtin_nontemporal_store(__builtin_bit_cast(f32x4, n), reinterpret_cast<f32x4 *>(S + row * DV + 4 * cg));
     }
 }
 

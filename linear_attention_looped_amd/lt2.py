@@ -440,7 +440,7 @@ def lt2_hbm_copy(dst, src, stream=None):
     return dst
 
 
-PROBE_COPY, PROBE_READ, PROBE_WRITE = 0, 1, 2
+PROBE_COPY, PROBE_READ, PROBE_WRITE, PROBE_TILE_COPY = 0, 1, 2, 3
 
 
 def lt2_hbm_probe(dst, src, mode: int = PROBE_COPY, blocks: int = 0, unroll: int = 4, stream=None):

@@ -117,7 +117,8 @@ def test_probe_validation():
     L = lt2.lib()
     P = ctypes.c_void_p
     assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 0, 0, 0, 4, None) == 0
-    assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 32, 3, 0, 4, None) == 4       # unknown mode
+    assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 32, 4, 0, 4, None) == 4       # unknown mode
+    assert L.lt2_hbm_probe(P(FAKE), None, 32, 3, 0, 4, None) == 1         # tile copy reads src
     assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 32, 0, 0, 3, None) == 4       # unroll not built
     assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 40, 0, 0, 4, None) == 2
     assert L.lt2_hbm_probe(P(FAKE), P(FAKE), 32, 0, -1, 4, None) == 2
