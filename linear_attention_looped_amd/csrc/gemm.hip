@@ -79,7 +79,16 @@ struct ResidOut {
     uint16_t *xb;          // [M, N] bf16 copy
 };
 
-__device__ __forceinline__ float sigmoidf_acc(float z) { return 1.f / (1.f + expf(-z)); }
+// sigmoid(z) = 1 / (1 + 2^(-z log2 e)) on the hardware exp2 and reciprocal
+// (each within about 1 ulp, no range branches; z -> -inf gives 1 / inf = 0,
+// z -> +inf gives 1).  The library expf and divide put range-check branches
+// around every element of the epilogue.
+__device__ __forceinline__ float sigmoid_hw(float z) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * z));
+}
+// 1 / max(|x|, 1e-6) from the sum of squares, as one hardware reciprocal square
+// root (sqrt is monotone, so max(sqrt(ss), 1e-6) = sqrt(max(ss, 1e-12)))
+__device__ __forceinline__ float inv_norm(float ss) { return __builtin_amdgcn_rsqf(fmaxf(ss, 1e-12f)); }
 
 // Sum over aligned groups of NL = 16 or 32 lanes, result in every lane of the
 // group, by register moves only: DPP swaps within quads, mirrored half rows and
@@ -172,8 +181,8 @@ __device__ __forceinline__ void short_gate_tile(const uint16_t *__restrict__ A, 
         for (int w = 0; w < NW; ++w) z += (w < 4 ? red0 : red1)[(w & 3) * (SHORT_M * 32) + o];
         const int m = m0 + (o >> 5), n = n0 + (o & 31), c = n - g0;
         if (m < mlim && n < N && po.beta && c >= 0 && c < 2 * po.H) {
-            if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoidf_acc(z);
-            else po.alpha[(size_t)m * po.H + c - po.H] = sigmoidf_acc(-z);   // exp(-softplus(z))
+            if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoid_hw(z);
+            else po.alpha[(size_t)m * po.H + c - po.H] = sigmoid_hw(-z);   // exp(-softplus(z))
         }
     }
 }
@@ -423,12 +432,12 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
                             if constexpr (MODE == 1) {
                                 const float ss =
                                     lanes_sum<DH / 4>(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
-                                const float sc = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+                                const float sc = inv_norm(ss);
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) x[e] *= sc;
                             } else if constexpr (MODE == 2) {
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) x[e] = sigmoidf_acc(x[e]);
+                                for (int e = 0; e < 4; ++e) x[e] = sigmoid_hw(x[e]);
                             }
                             const int m = mb + 2 * q;
                             if (m < mlim) {
@@ -456,8 +465,8 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
                         const int m = m0 + WR * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
                         if (m >= mlim) continue;
                         const float z = acc[i][j][r];
-                        if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoidf_acc(z);
-                        else po.alpha[(size_t)m * po.H + c - po.H] = sigmoidf_acc(-z);  // exp(-softplus(z))
+                        if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoid_hw(z);
+                        else po.alpha[(size_t)m * po.H + c - po.H] = sigmoid_hw(-z);  // exp(-softplus(z))
                     }
                 }
         }
@@ -699,7 +708,7 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
                 for (int j = 0; j < 32; ++j) ss += cr[j] * cr[j];
                 ss += __shfl_xor(ss, 1);                      // 64 columns
                 if constexpr (DH == 128) ss += __shfl_xor(ss, 2);   // 128 columns
-                scale = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+                scale = inv_norm(ss);
             }
             if (m < M) {
                 const int c = n0 - region * Hd + c0;
@@ -710,8 +719,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
                     for (int e = 0; e < 4; ++e) {
                         float x0 = cr[j + 2 * e] * scale, x1 = cr[j + 2 * e + 1] * scale;
                         if (region == 3) {
-                            x0 = sigmoidf_acc(x0);
-                            x1 = sigmoidf_acc(x1);
+                            x0 = sigmoid_hw(x0);
+                            x1 = sigmoid_hw(x1);
                         }
                         o[e] = (uint32_t)bf16_bits(x0) | ((uint32_t)bf16_bits(x1) << 16);
                     }
@@ -724,8 +733,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(const uint16_t *__restr
                 const int c = n0 + c0 + j - NR * Hd;
                 if (c >= 2 * po.H) break;
                 const float z = cr[j];
-                if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoidf_acc(z);
-                else po.alpha[(size_t)m * po.H + c - po.H] = sigmoidf_acc(-z);
+                if (c < po.H) po.beta[(size_t)m * po.H + c] = sigmoid_hw(z);
+                else po.alpha[(size_t)m * po.H + c - po.H] = sigmoid_hw(-z);
             }
         }
     }
