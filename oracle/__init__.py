@@ -228,6 +228,35 @@ def swa(q, k, v, window: int):
     return o
 
 
+def swa_decode_step(q, k, v, k_cache, v_cache, pos, window: int):
+    """One decode token of causal sliding-window attention, per sequence, with
+    the window held as a ring of the last w keys and values.
+
+    q, k, v [B, H, d]; k_cache, v_cache [B, H, w, d] (updated in place, fp64);
+    pos [B] = tokens each sequence has already seen.  The new key and value go
+    to ring slot pos mod w; the query then attends to every filled slot, which
+    are the tokens max(0, pos-w+1) .. pos:
+        o = sum_j softmax_j(q . k_j / sqrt(d)) v_j
+    (the softmax does not depend on the order of the slots).  Returns o
+    [B, H, d] fp64."""
+    q, k, v = map(_f64, (q, k, v))
+    B, H, d = q.shape
+    assert k_cache.shape[:2] == (B, H) and k_cache.shape[2] == window and window >= 1
+    o = np.empty((B, H, v.shape[2]), np.float64)
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        p = int(pos[b])
+        slot = p % window
+        k_cache[b, :, slot] = k[b]
+        v_cache[b, :, slot] = v[b]
+        n = min(p + 1, window)                       # filled slots: 0 .. n-1
+        for h in range(H):
+            s = k_cache[b, h, :n] @ q[b, h] * scale  # [n]
+            e = np.exp(s - s.max())
+            o[b, h] = (e / e.sum()) @ v_cache[b, h, :n]
+    return o
+
+
 def swa_layer(h, w_in, w_o, H: int, d: int, window: int, gate: bool = False):
     """One window-attention layer of the looped hybrid on h [B,L,D]:
 

@@ -178,3 +178,54 @@ def test_receptive_field_of_the_looped_window_block_is_T_times_w(T, w):
     inside = (t >= j) & (t <= j + T * (w - 1))
     assert np.all(diff[~inside] == 0.0)
     assert np.all(diff[inside] > 0.0)
+
+
+# ---- decode form: the window as a ring of the last w keys and values ----
+
+def decode_chain(q, k, v, w, start=None):
+    """oracle.swa_decode_step applied token by token from empty rings."""
+    B, L, H, d = q.shape
+    kc, vc = np.zeros((B, H, w, d)), np.zeros((B, H, w, d))
+    out = np.empty((B, L, H, d))
+    for t in range(L):
+        out[:, t] = oracle.swa_decode_step(q[:, t], k[:, t], v[:, t], kc, vc, np.full(B, t), w)
+    return out
+
+
+@pytest.mark.parametrize("L,w", [(9, 1), (20, 3), (20, 8), (13, 30)])
+def test_decode_chain_is_window_attention(L, w):
+    """Token-by-token decode through the ring equals torch's banded attention
+    (and the oracle's prefill) at every token, across the ring's wrap-around."""
+    q, k, v = rand_qkv(5, 2, L, 3, 6)
+    got = decode_chain(q, k, v, w)
+    i = np.arange(L)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - w)
+    mask = np.where(band, 0.0, -np.inf)
+    np.testing.assert_allclose(got, torch_attention(q, k, v, mask=mask), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got, oracle.swa(q, k, v, w), rtol=1e-12, atol=1e-12)
+
+
+def test_decode_window_one_returns_v():
+    q, k, v = rand_qkv(6, 2, 5, 2, 4)
+    np.testing.assert_array_equal(decode_chain(q, k, v, 1), v)
+
+
+def test_decode_ring_order_and_positions():
+    """A full ring whose slots are permuted gives the same output (the softmax
+    ignores slot order); a sequence that has seen p < w - 1 tokens attends only
+    to slots 0 .. p, whatever the other slots hold."""
+    g = np.random.default_rng(7)
+    B, H, w, d = 2, 3, 6, 4
+    kc, vc = g.standard_normal((B, H, w, d)), g.standard_normal((B, H, w, d))
+    q, k, v = (g.standard_normal((B, H, d)) for _ in range(3))
+    pos = np.array([13, 2])
+    o = oracle.swa_decode_step(q, k, v, kc.copy(), vc.copy(), pos, w)
+    perm = g.permutation(w)                       # slot s of the permuted ring holds slot perm[s]
+    kp, vp = kc[:, :, perm].copy(), vc[:, :, perm].copy()
+    s1 = int(np.argsort(perm)[13 % w])            # where the slot the new token replaces went
+    op = oracle.swa_decode_step(q[:1], k[:1], v[:1], kp[:1], vp[:1], np.array([w + s1]), w)
+    np.testing.assert_allclose(op[0], o[0], rtol=1e-12, atol=1e-12)
+    kz, vz = kc.copy(), vc.copy()
+    kz[1, :, 3:], vz[1, :, 3:] = 1e3, -1e3        # unfilled slots of sequence 1
+    oz = oracle.swa_decode_step(q, k, v, kz, vz, pos, w)
+    np.testing.assert_allclose(oz[1], o[1], rtol=1e-12, atol=1e-12)
