@@ -23,7 +23,8 @@ Also measured in the same run (reported under "extra"):
     lt2_gdn_decode_step launch per (token, loop); state GB/s against HBM peak and
     against the measured copy ceiling;
   * the looped block (T=4), with and without the output gate; the looped decode
-    chain; the per-channel-gate prefill; window attention; the looped hybrid
+    chain; the per-channel-gate prefill; window attention and its decode step
+    (ring of the last 512 keys and values); the looped hybrid
     block (gated delta, window 512) at T=2 (four layer applications, the depth
     its parity tests cover); the backward pass of the headline workload.
 cpu_baseline: the fp64 oracle on the whole headline workload (16,384 tokens x
@@ -561,6 +562,38 @@ def _slab_inputs(synth, shape, b0, nb):
     return out
 
 
+def bench_swa_decode(args, torch, lt2, launches=32):
+    """Decode step of the window mixer: 256 sequences x 16 heads, d = 128,
+    window 512, full rings (position 4095), bf16 q/k/v/out; the rings are
+    streamed once per launch.  Two ring sets alternate so that consecutive
+    launches do not re-read the last one's from the last-level cache.  Inputs
+    drawn on the device with a fixed generator."""
+    B, H, d, w = 256, 16, 128, 512
+    g = torch.Generator(device="cuda").manual_seed(4321)
+    rings = [tuple((torch.randn((B, H, w, d), device="cuda", generator=g) * 0.1).to(torch.bfloat16)
+                   for _ in range(2)) for _ in range(2)]
+    q, k, v = (torch.randn((B, H, d), device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    pos = torch.full((B,), 4095, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
+    for i in range(4):
+        lt2.lt2_swa_decode_step(q, k, v, *rings[i % 2], pos, w, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        lt2.lt2_swa_decode_step(q, k, v, *rings[i % 2], pos, w, out=out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes = B * H * (2.0 * w * d * 2 + 4 * d * 2 + 2 * d * 2)   # rings read, q/k/v/o, the new slot written
+    del rings
+    torch.cuda.empty_cache()
+    log(f"swa decode {us:.1f} us per launch ({nbytes / us / 1e3:.0f} GB/s)")
+    return dict(B=B, H=H, d=d, window=w, us_per_launch=us, bytes_per_launch=nbytes, gbs=nbytes / us / 1e3,
+                hbm_frac=nbytes / us / 1e3 / HBM_PEAK_GBS, tokens_per_s=B / (us / 1e6))
+
+
 def bench_decode_flat(args, torch, lt2, launches=64):
     """Decode-step time against the context length behind the state (the pages'
     flat decode throughput): the 4096-unit state of the decode workload (256
@@ -710,6 +743,7 @@ def main():
     lde = None if args.no_looped_decode else bench_looped_decode(args, torch, lt2, synth)
     flat = None if (args.no_decode or args.no_decode_flat) else bench_decode_flat(args, torch, lt2)
     swa = None if args.no_swa else bench_swa(args, torch, lt2, synth)
+    swd = None if args.no_swa else bench_swa_decode(args, torch, lt2)
     hyb = None if args.no_hybrid else bench_hybrid(args, torch, lt2, synth)
     bwd = None if args.no_backward else bench_backward(args, torch, lt2, synth)
     bwc = None if (args.no_backward or args.no_channel) else bench_backward_channel(args, torch, lt2, synth)
@@ -758,6 +792,8 @@ def main():
         extra["decode_flat"] = flat
     if swa:
         extra["swa_prefill"] = swa
+    if swd:
+        extra["swa_decode"] = dict(swd, copy_ceiling_frac=swd["gbs"] / copy["gbs"])
     if hyb:
         extra["hybrid"] = hyb
     if bwd:

@@ -293,6 +293,34 @@ typedef struct lt2_swa_desc {
 lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *k, const void *v,
                            void *out, void *stream);
 
+/*
+ * One decode token of the sliding-window mixer (the decode form of
+ * lt2_swa_prefill; LT2 explainer, paithon.it, section "Sostituire il motore":
+ * each token attends to the w most recent positions, itself included).  For
+ * every batch entry b and head, the window is a ring of the last w keys and
+ * values: the new token's k and v are written to ring slot pos[b] mod w, then
+ *     o = sum_j softmax_j(q . k_j / sqrt(d)) v_j
+ * over the filled slots, which hold the tokens max(0, pos[b]-w+1) .. pos[b]
+ * (the softmax does not depend on the order of the slots).
+ *   desc              B, H, d, window; L must be 1; qkv_dtype LT2_BF16
+ *   q, k, v           [B, H, d] bf16, the new token, 16-byte aligned
+ *   k_cache, v_cache  [B, H, window, d] bf16, owned by the caller and updated
+ *                     in place (slot pos[b] mod window); slots past pos[b] are
+ *                     never read while pos[b] < window - 1, so fresh rings need
+ *                     no initialisation
+ *   pos               [B] int32 in device memory: tokens sequence b has already
+ *                     seen (the new token's position); negative values are
+ *                     taken as 0.  The call does not advance it.
+ *   out               [B, H, d] bf16 or fp32 (desc->out_dtype), 16-byte aligned
+ * Scores, the softmax and the value sums are fp32.  No workspace.
+ * Errors: LT2_ERR_SHAPE for L != 1, negative B, H or d <= 0, window < 1 or
+ * B * H beyond 2^31 - 1; LT2_ERR_DTYPE / LT2_ERR_UNSUPPORTED as for
+ * lt2_swa_prefill; LT2_ERR_NULL for a missing pointer when B > 0;
+ * LT2_ERR_ALIGN for misaligned buffers (pos: 4 bytes).
+ */
+lt2_status lt2_swa_decode_step(const lt2_swa_desc *desc, const void *q, const void *k, const void *v,
+                               void *k_cache, void *v_cache, const int32_t *pos, void *out, void *stream);
+
 /* Layer kinds of the looped hybrid block. */
 #define LT2_MAX_LAYERS 8
 typedef enum lt2_mixer_kind {

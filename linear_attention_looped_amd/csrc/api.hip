@@ -225,6 +225,28 @@ lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *
     return hip_status(launch_swa(a, (hipStream_t)stream));
 }
 
+lt2_status lt2_swa_decode_step(const lt2_swa_desc *desc, const void *q, const void *k, const void *v,
+                               void *k_cache, void *v_cache, const int32_t *pos, void *out, void *stream) {
+    if (!desc) return LT2_ERR_NULL;
+    if (desc->B < 0 || desc->L != 1 || desc->H <= 0 || desc->d <= 0 || desc->window < 1) return LT2_ERR_SHAPE;
+    if ((desc->qkv_dtype != LT2_F32 && desc->qkv_dtype != LT2_BF16) ||
+        (desc->out_dtype != LT2_F32 && desc->out_dtype != LT2_BF16))
+        return LT2_ERR_DTYPE;
+    if (desc->qkv_dtype != LT2_BF16 || (desc->d != 64 && desc->d != 128)) return LT2_ERR_UNSUPPORTED;
+    // one workgroup per (b, h): the grid must fit its 31-bit limit
+    if ((int64_t)desc->B * desc->H > 0x7fffffffLL) return LT2_ERR_SHAPE;
+    if (desc->B > 0 && (!q || !k || !v || !k_cache || !v_cache || !pos || !out)) return LT2_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(out, 16) || !aligned(pos, 4))
+        return LT2_ERR_ALIGN;
+    if (desc->B == 0) return LT2_OK;
+    SwaDecodeArgs a;
+    a.B = desc->B; a.H = desc->H; a.d = desc->d; a.window = desc->window;
+    a.out_bf16 = desc->out_dtype == LT2_BF16;
+    a.q = q; a.k = k; a.v = v; a.k_cache = k_cache; a.v_cache = v_cache; a.pos = pos; a.out = out;
+    return hip_status(launch_swa_decode(a, (hipStream_t)stream));
+}
+
 lt2_status lt2_hbm_copy(void *dst, const void *src, size_t bytes, void *stream) {
     if (bytes == 0) return LT2_OK;
     if (!dst || !src) return LT2_ERR_NULL;

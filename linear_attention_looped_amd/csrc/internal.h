@@ -59,6 +59,16 @@ struct SwaArgs {
 };
 hipError_t launch_swa(const SwaArgs &a, hipStream_t s);
 
+// One decode token of the window mixer against per-(b, h) rings of w keys/values.
+struct SwaDecodeArgs {
+    int B, H, d, window, out_bf16;
+    const void *q, *k, *v;
+    void *k_cache, *v_cache;
+    const int32_t *pos;
+    void *out;
+};
+hipError_t launch_swa_decode(const SwaDecodeArgs &a, hipStream_t s);
+
 // Backward pass of the gated-delta prefill, scalar gate; gradients fp32.
 struct GdnBwdArgs {
     int B, L, H, d, qkv_bf16, dout_bf16;

@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.lt2_gdn_backward.restype = S
         L.lt2_swa_prefill.argtypes = [ctypes.POINTER(lt2_swa_desc), P, P, P, P, P]
         L.lt2_swa_prefill.restype = S
+        L.lt2_swa_decode_step.argtypes = [ctypes.POINTER(lt2_swa_desc), P, P, P, P, P, P, P, P]
+        L.lt2_swa_decode_step.restype = S
         HD = ctypes.POINTER(lt2_hybrid_desc)
         L.lt2_hybrid_mixer_workspace_size.argtypes = [HD]
         L.lt2_hybrid_mixer_workspace_size.restype = Z
@@ -387,6 +389,32 @@ def lt2_swa_prefill(q, k, v, window: int, out=None, out_dtype=None, stream=None)
     _on_device(dev, q=q, k=k, v=v, out=out)
     code = lib().lt2_swa_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream))
     _check("lt2_swa_prefill", code)
+    return out
+
+
+def lt2_swa_decode_step(q, k, v, k_cache, v_cache, pos, window: int, out=None, out_dtype=None, stream=None):
+    """One decode token of sliding-window attention per sequence.  q, k, v
+    [B,H,d] bf16 (the new token); k_cache, v_cache [B,H,window,d] bf16 rings,
+    updated in place at slot pos[b] % window; pos [B] int32 on the device (the
+    tokens each sequence has already seen; not advanced).  Returns out [B,H,d]
+    (bf16, or ``out_dtype`` / the dtype of ``out``)."""
+    B, H, d = _dims(q, 3, "q")
+    _expect(q, "q", dtypes=_FLOATS)
+    dev = q.device
+    w = int(window)
+    _expect(k, "k", (B, H, d), q.dtype)
+    _expect(v, "v", (B, H, d), q.dtype)
+    _expect(k_cache, "k_cache", (B, H, w, d), q.dtype)
+    _expect(v_cache, "v_cache", (B, H, w, d), q.dtype)
+    _expect(pos, "pos", (B,), torch.int32)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype or torch.bfloat16, device=dev)
+    _expect(out, "out", (B, H, d), _FLOATS)
+    desc = swa_desc(B, 1, H, d, w, _dt(q), _dt(out))
+    _on_device(dev, q=q, k=k, v=v, k_cache=k_cache, v_cache=v_cache, pos=pos, out=out)
+    code = lib().lt2_swa_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(pos), _ptr(out), _stream(stream))
+    _check("lt2_swa_decode_step", code)
     return out
 
 

@@ -133,6 +133,16 @@ int main(void) {
         EXPECT(lt2_swa_prefill(&s, F, F, F, F, NULL), LT2_ERR_SHAPE);
         s.L = 300; s.H = 3; s.qkv_dtype = 0;
         EXPECT(lt2_swa_prefill(&s, F, F, F, F, NULL), LT2_ERR_UNSUPPORTED);
+        /* decode step: one token (L = 1) only; refused calls launch nothing */
+        lt2_swa_desc sd = {2, 2, 3, 128, 64, 1, 1};
+        EXPECT(lt2_swa_decode_step(&sd, F, F, F, F, F, (const int32_t *)F, F, NULL), LT2_ERR_SHAPE);
+        sd.L = 1;
+        sd.window = 0;
+        EXPECT(lt2_swa_decode_step(&sd, F, F, F, F, F, (const int32_t *)F, F, NULL), LT2_ERR_SHAPE);
+        sd.window = 64;
+        EXPECT(lt2_swa_decode_step(&sd, F, F, F, NULL, F, (const int32_t *)F, F, NULL), LT2_ERR_NULL);
+        sd.B = 0;
+        EXPECT(lt2_swa_decode_step(&sd, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL), LT2_OK);
         EXPECT(lt2_hbm_copy(F, F, 17, NULL), LT2_ERR_SHAPE);
         EXPECT(lt2_hbm_probe(F, F, 32, 7, 0, 4, NULL), LT2_ERR_UNSUPPORTED);
         EXPECT(lt2_hbm_probe(F, F, 32, 0, -5, 4, NULL), LT2_ERR_SHAPE);

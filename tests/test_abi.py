@@ -244,6 +244,30 @@ def test_swa_null_and_alignment():
     assert swa_call(good_swa(B=0), q=None, k=None, v=None, out=None) == 0
 
 
+def swa_dec_call(desc, q=FAKE, k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, pos=FAKE, out=FAKE):
+    P = ctypes.c_void_p
+    return lt2.lib().lt2_swa_decode_step(ctypes.byref(desc), P(q), P(k), P(v), P(kc), P(vc), P(pos), P(out), None)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(L=2), 2), (dict(L=0), 2), (dict(B=-1), 2), (dict(H=0), 2),
+                                     (dict(window=0), 2), (dict(d=96), 4), (dict(qkv_dtype=0), 4),
+                                     (dict(out_dtype=7), 3), (dict(B=1 << 20, H=1 << 12), 2)])
+def test_swa_decode_rejects_bad_descriptor(kw, code):
+    """The window decode step takes one token (L = 1) of bf16 q/k/v with d 64 or
+    128, and at most 2^31 - 1 (b, h) workgroups; nothing is launched."""
+    assert swa_dec_call(good_swa(**{"L": 1, **kw})) == code
+
+
+def test_swa_decode_null_and_alignment():
+    assert lt2.lib().lt2_swa_decode_step(None, None, None, None, None, None, None, None, None) == 1
+    for name in ("q", "k", "v", "kc", "vc", "pos", "out"):
+        assert swa_dec_call(good_swa(L=1), **{name: None}) == 1, name
+    assert swa_dec_call(good_swa(L=1), kc=FAKE + 8) == 6
+    assert swa_dec_call(good_swa(L=1), pos=FAKE + 2) == 6
+    # no sequences: nothing is read or written
+    assert swa_dec_call(good_swa(L=1, B=0), q=None, k=None, v=None, kc=None, vc=None, pos=None, out=None) == 0
+
+
 def hybrid_call(desc, h=FAKE, w_in=(FAKE,), w_o=(FAKE,), ws=FAKE, ws_bytes=1 << 40, arrays=True):
     P = ctypes.c_void_p
     wi = (P * len(w_in))(*w_in) if arrays else None

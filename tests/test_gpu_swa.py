@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from linear_attention_looped_amd import lt2, synth
-from gpu_util import TOL_BF16, announce, dev, host, rel_err
+from gpu_util import TOL_BF16, TOL_F32, announce, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -93,3 +93,80 @@ def test_swa_value_reaches_exactly_its_window_on_gpu():
     inside = (t >= j) & (t <= j + 199)
     assert np.all(diff[~inside] == 0.0)
     assert np.all(diff[inside] > 0.0)
+
+
+# ---- decode form: one token per sequence against rings of the last w keys/values ----
+
+def ring_history(g, B, H, w, d, pos):
+    """Rings holding a random bf16 history of pos[b] tokens (token t at slot t % w)."""
+    kc = np.zeros((B, H, w, d), np.float32)
+    vc = np.zeros((B, H, w, d), np.float32)
+    for b in range(B):
+        for t in range(max(0, pos[b] - w), pos[b]):
+            kc[b, :, t % w] = synth.bf16_round(g.standard_normal((H, d)).astype(np.float32) / np.sqrt(d))
+            vc[b, :, t % w] = synth.bf16_round(g.standard_normal((H, d)).astype(np.float32))
+    return kc, vc
+
+
+@pytest.mark.parametrize("d,L,w", [(64, 40, 1), (128, 70, 16), (64, 70, 64), (128, 50, 100), (128, 130, 37)])
+def test_swa_decode_chain_matches_oracle(d, L, w):
+    """Token-by-token decode from empty rings equals the window attention of the
+    whole sequence at every token (rings wrapping when L > w, partly filled
+    when L < w); fp32 outputs at the fp32 bar (the inputs are bf16-valued, the
+    arithmetic fp32), bf16 outputs at the bf16 bar."""
+    B, H = 2, 3
+    announce(f"swa decode chain d={d} L={L} w={w}")
+    x = synth.swa_inputs(synth.SWAShape(B, L, H, d, w), seed=11)
+    ref = oracle.swa(x["q"], x["k"], x["v"], w)
+    for out_dtype, tol in ((torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)):
+        kc = torch.zeros((B, H, w, d), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+        q, k, v = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+        outs = []
+        for t in range(L):
+            outs.append(lt2.lt2_swa_decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                                                kc, vc, pos, w, out_dtype=out_dtype))
+            pos += 1
+        torch.cuda.synchronize()
+        got = np.stack([host(o) for o in outs], axis=1)
+        assert rel_err(got, ref) <= tol, out_dtype
+
+
+def test_swa_decode_ragged_positions():
+    """Sequences at different positions (empty ring, partly filled, full, long
+    past wrap-around) in one call: each output against the oracle's decode step,
+    and the new key and value land in slot pos % w of each ring (bit-exact)."""
+    g = np.random.default_rng(12)
+    B, H, w, d = 4, 2, 37, 128
+    pos = np.array([0, 5, 36, 200])
+    announce(f"swa decode ragged positions {pos.tolist()} w={w}")
+    kc, vc = ring_history(g, B, H, w, d, pos)
+    q, k, v = (synth.bf16_round(g.standard_normal((B, H, d)).astype(np.float32)) for _ in range(3))
+    kc_ref, vc_ref = kc.astype(np.float64), vc.astype(np.float64)
+    ref = oracle.swa_decode_step(q, k, v, kc_ref, vc_ref, pos, w)
+    tk, tv = dev(kc, torch.bfloat16), dev(vc, torch.bfloat16)
+    out = lt2.lt2_swa_decode_step(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), tk, tv,
+                                  torch.from_numpy(pos.astype(np.int32)).to("cuda"), w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_err(host(out), ref) <= TOL_F32
+    np.testing.assert_array_equal(host(tk), kc_ref)
+    np.testing.assert_array_equal(host(tv), vc_ref)
+
+
+def test_swa_decode_full_size_rings():
+    """A decode step of 16 sequences x 16 heads, d 128, window 512 on full rings
+    (position 4095) against the oracle's decode step, bf16 output."""
+    g = np.random.default_rng(13)
+    B, H, w, d = 16, 16, 512, 128
+    announce("swa decode full rings B16 H16 w512")
+    kc = synth.bf16_round(g.standard_normal((B, H, w, d)).astype(np.float32) / np.sqrt(d))
+    vc = synth.bf16_round(g.standard_normal((B, H, w, d)).astype(np.float32))
+    q, k, v = (synth.bf16_round(g.standard_normal((B, H, d)).astype(np.float32)) for _ in range(3))
+    pos = np.full(B, 4095)
+    ref = oracle.swa_decode_step(q, k, v, kc.astype(np.float64), vc.astype(np.float64), pos, w)
+    out = lt2.lt2_swa_decode_step(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16),
+                                  dev(kc, torch.bfloat16), dev(vc, torch.bfloat16),
+                                  torch.from_numpy(pos.astype(np.int32)).to("cuda"), w)
+    torch.cuda.synchronize()
+    assert rel_err(host(out), ref) <= TOL_BF16
