@@ -26,7 +26,8 @@ Also measured in the same run (reported under "extra"):
     chain; the per-channel-gate prefill; window attention and its decode step
     (ring of the last 512 keys and values); the looped hybrid
     block (gated delta, window 512) at T=2 (four layer applications, the depth
-    its parity tests cover); the backward pass of the headline workload.
+    its parity tests cover) and its decode chain; the backward pass of the
+    headline workload.
 cpu_baseline: the fp64 oracle on the whole headline workload (16,384 tokens x
 16 heads), passes repeated for at least 5 s, timed on the host cores (their
 count and model recorded).
@@ -594,6 +595,48 @@ def bench_swa_decode(args, torch, lt2, launches=32):
                 hbm_frac=nbytes / us / 1e3 / HBM_PEAK_GBS, tokens_per_s=B / (us / 1e6))
 
 
+def bench_hybrid_decode(args, torch, lt2, steps=8):
+    """Looped hybrid decode chain: 256 sequences, d_model 2048, H16 d128, the
+    (gated delta, window 512) stack at T = 2 (its tested depth), one token per
+    sequence per call at position 4095 (full rings); states, rings and weights
+    drawn on the device with a fixed generator."""
+    B, D, H, d, T, w = 256, 2048, 16, 128, 2, 512
+    g = torch.Generator(device="cuda").manual_seed(999)
+    layers = []
+    for kind, rows in (("gdn", 3 * H * d + 2 * H), ("swa", 3 * H * d)):
+        layers.append((kind, (torch.randn((rows, D), device="cuda", generator=g) / D ** 0.5).to(torch.bfloat16),
+                       (torch.randn((D, H * d), device="cuda", generator=g) / D ** 0.5).to(torch.bfloat16)))
+    states = torch.randn((T, 1, B, H, d, d), device="cuda", generator=g) * 0.02
+    kr = (torch.randn((T, 1, B, H, w, d), device="cuda", generator=g) * 0.1).to(torch.bfloat16)
+    vr = torch.randn((T, 1, B, H, w, d), device="cuda", generator=g).to(torch.bfloat16)
+    pos = torch.full((B,), 4095, dtype=torch.int32, device="cuda")
+    rows = torch.randn((steps + 2, B, D), device="cuda", generator=g)
+    h = torch.empty((B, D), device="cuda")
+    ws = torch.empty(lt2.lt2_hybrid_decode_workspace_size(lt2.hybrid_desc(B, 1, D, H, d, T, ["gdn", "swa"], w)),
+                     dtype=torch.uint8, device="cuda")
+    for i in range(2):
+        h.copy_(rows[i])
+        lt2.lt2_hybrid_decode_step(h, layers, states, kr, vr, pos, H, d, T, w, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        h.copy_(rows[2 + i])
+        a.record(stream)
+        lt2.lt2_hybrid_decode_step(h, layers, states, kr, vr, pos, H, d, T, w, workspace=ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    weight_bytes = sum(wi.numel() + wo.numel() for _, wi, wo in layers) * 2.0
+    step_bytes = T * (2.0 * B * H * d * d * 4 + 2.0 * B * H * w * d * 2 + weight_bytes)
+    del layers, states, kr, vr, rows
+    torch.cuda.empty_cache()
+    log(f"hybrid decode {ms:.3f} ms per token step ({step_bytes / ms / 1e6:.0f} GB/s)")
+    return dict(B=B, d_model=D, H=H, d=d, T=T, layers=["gdn", "swa"], window=w, ms_per_token=ms,
+                tokens_per_s=B / (ms / 1e3), bytes_per_token=step_bytes, gbs=step_bytes / ms / 1e6,
+                hbm_frac=step_bytes / ms / 1e6 / HBM_PEAK_GBS)
+
+
 def bench_decode_flat(args, torch, lt2, launches=64):
     """Decode-step time against the context length behind the state (the pages'
     flat decode throughput): the 4096-unit state of the decode workload (256
@@ -745,6 +788,7 @@ def main():
     swa = None if args.no_swa else bench_swa(args, torch, lt2, synth)
     swd = None if args.no_swa else bench_swa_decode(args, torch, lt2)
     hyb = None if args.no_hybrid else bench_hybrid(args, torch, lt2, synth)
+    hdc = None if args.no_hybrid else bench_hybrid_decode(args, torch, lt2)
     bwd = None if args.no_backward else bench_backward(args, torch, lt2, synth)
     bwc = None if (args.no_backward or args.no_channel) else bench_backward_channel(args, torch, lt2, synth)
     cpu = None if args.no_cpu else cpu_baseline(synth)
@@ -796,6 +840,8 @@ def main():
         extra["swa_decode"] = dict(swd, copy_ceiling_frac=swd["gbs"] / copy["gbs"])
     if hyb:
         extra["hybrid"] = hyb
+    if hdc:
+        extra["hybrid_decode"] = hdc
     if bwd:
         extra["backward"] = bwd
     if bwc:

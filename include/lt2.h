@@ -368,6 +368,32 @@ lt2_status lt2_hybrid_mixer(const lt2_hybrid_desc *desc, const float *h_in, floa
                             size_t ws_bytes, void *stream);
 
 /*
+ * Looped hybrid decode: one new token per sequence through the T loops of the
+ * shared layer stack of lt2_hybrid_mixer (LT2 summary page, hybrid strategies
+ * across depth and iterations; the mixers' decode forms as in
+ * lt2_gdn_decode_step and lt2_swa_decode_step).  Loop tau's layer l carries its
+ * own recurrent state (gated-delta layers) or ring of the last w keys and
+ * values (window layers) across calls; by causality, token-by-token calls from
+ * zero states and empty rings reproduce lt2_hybrid_mixer on the whole sequence.
+ *   desc      as lt2_hybrid_mixer with L = 1 (chunk is not used)
+ *   h         [B, d_model] fp32, the token's residual stream, updated in place
+ *   W_in, W_o host arrays of n_layers device pointers, layouts as
+ *             lt2_hybrid_mixer
+ *   states    [T, n_gdn, B, H, d_head, d_head] fp32, in place (n_gdn = number of
+ *             gated-delta layers, indexed in stack order); may be NULL if none
+ *   k_rings, v_rings  [T, n_swa, B, H, window, d_head] bf16, in place (n_swa =
+ *             number of window layers); slot pos[b] mod window is written
+ *   pos       [B] int32 in device memory: tokens sequence b has already seen;
+ *             not advanced by the call
+ *   ws        lt2_hybrid_decode_workspace_size(desc) bytes, 256-byte aligned
+ * Errors: as lt2_hybrid_mixer; LT2_ERR_SHAPE for L != 1.
+ */
+size_t lt2_hybrid_decode_workspace_size(const lt2_hybrid_desc *desc);
+lt2_status lt2_hybrid_decode_step(const lt2_hybrid_desc *desc, float *h, const void *const *W_in,
+                                  const void *const *W_o, float *states, void *k_rings, void *v_rings,
+                                  const int32_t *pos, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Bandwidth probe: copy `bytes` (a multiple of 16) from src to dst with one
  * streaming kernel.  Used to measure the achievable HBM bandwidth.
  */

@@ -464,4 +464,46 @@ lt2_status lt2_hybrid_mixer(const lt2_hybrid_desc *desc, const float *h_in, floa
     return hip_status(launch_hybrid(a, (hipStream_t)stream));
 }
 
+size_t lt2_hybrid_decode_workspace_size(const lt2_hybrid_desc *desc) {
+    if (check_hybrid(desc) != LT2_OK || desc->L != 1 || desc->B == 0) return 0;
+    return loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head, desc->out_gate).total;
+}
+
+lt2_status lt2_hybrid_decode_step(const lt2_hybrid_desc *desc, float *h, const void *const *W_in,
+                                  const void *const *W_o, float *states, void *k_rings, void *v_rings,
+                                  const int32_t *pos, void *ws, size_t ws_bytes, void *stream) {
+    lt2_status st = check_hybrid(desc);
+    if (st != LT2_OK) return st;
+    if (desc->L != 1) return LT2_ERR_SHAPE;
+    int n_gdn = 0, n_swa = 0;
+    for (int i = 0; i < desc->n_layers; ++i) (desc->kinds[i] == LT2_MIXER_GDN ? n_gdn : n_swa)++;
+    // one workgroup per (b, h) in the decode kernels
+    if ((int64_t)desc->B * desc->H > 0x7fffffffLL) return LT2_ERR_SHAPE;
+    const bool work = desc->B > 0 && desc->T > 0;
+    if (work && (!h || !W_in || !W_o || !pos || (n_gdn > 0 && !states) || (n_swa > 0 && (!k_rings || !v_rings))))
+        return LT2_ERR_NULL;
+    if (!aligned(h, 16) || !aligned(states, 16) || !aligned(k_rings, 16) || !aligned(v_rings, 16) || !aligned(pos, 4))
+        return LT2_ERR_ALIGN;
+    if (work)
+        for (int i = 0; i < desc->n_layers; ++i) {
+            if (!W_in[i] || !W_o[i]) return LT2_ERR_NULL;
+            if (!aligned(W_in[i], 16) || !aligned(W_o[i], 16)) return LT2_ERR_ALIGN;
+        }
+    const size_t need = work ? loop_decode_layout(desc->B, desc->d_model, desc->H, desc->d_head, desc->out_gate).total : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 256)) return LT2_ERR_ALIGN;
+    if (!work) return LT2_OK;
+    HybridDecodeArgs a{};
+    a.B = desc->B; a.D = desc->d_model; a.H = desc->H; a.d = desc->d_head; a.T = desc->T;
+    a.gated = desc->out_gate; a.window = desc->window; a.n_layers = desc->n_layers;
+    for (int i = 0; i < desc->n_layers; ++i) {
+        a.kinds[i] = desc->kinds[i];
+        a.W_in[i] = static_cast<const uint16_t *>(W_in[i]);
+        a.W_o[i] = static_cast<const uint16_t *>(W_o[i]);
+    }
+    a.h = h; a.states = states; a.k_rings = static_cast<uint16_t *>(k_rings);
+    a.v_rings = static_cast<uint16_t *>(v_rings); a.pos = pos; a.ws = ws;
+    return hip_status(launch_hybrid_decode(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -66,6 +66,7 @@ struct SwaDecodeArgs {
     void *k_cache, *v_cache;
     const int32_t *pos;
     void *out;
+    const uint16_t *gate = nullptr;   // [B, H, d] bf16 output gate, or null
 };
 hipError_t launch_swa_decode(const SwaDecodeArgs &a, hipStream_t s);
 
@@ -126,6 +127,20 @@ struct LoopDecodeArgs {
 };
 LoopLayout loop_decode_layout(int B, int D, int H, int d, bool gated);
 hipError_t launch_looped_decode(const LoopDecodeArgs &a, hipStream_t s);
+
+// Looped hybrid decode: one token per sequence through T loops of the layer
+// stack; gated-delta layer states and window-layer rings per (loop, layer).
+struct HybridDecodeArgs {
+    int B, D, H, d, T, gated, window, n_layers;
+    int kinds[HYBRID_MAX_LAYERS];
+    float *h;                          // [B, D] fp32, in place
+    const uint16_t *W_in[HYBRID_MAX_LAYERS], *W_o[HYBRID_MAX_LAYERS];
+    float *states;                     // [T, n_gdn, B, H, d, d] fp32
+    uint16_t *k_rings, *v_rings;       // [T, n_swa, B, H, window, d] bf16
+    const int32_t *pos;                // [B]
+    void *ws;
+};
+hipError_t launch_hybrid_decode(const HybridDecodeArgs &a, hipStream_t s);
 hipError_t launch_state_init(float *dst, const float *src, size_t n, hipStream_t s);
 
 }  // namespace lt2

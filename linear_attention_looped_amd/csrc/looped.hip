@@ -165,4 +165,52 @@ hipError_t launch_hybrid(const HybridArgs &a, hipStream_t s) {
     return hipSuccess;
 }
 
+hipError_t launch_hybrid_decode(const HybridDecodeArgs &a, hipStream_t s) {
+    const int M = a.B, Hd = a.H * a.d, NR = a.gated ? 4 : 3;
+    unsigned char *ws = static_cast<unsigned char *>(a.ws);
+    const LoopLayout w = loop_decode_layout(a.B, a.D, a.H, a.d, a.gated);
+    uint16_t *gt = a.gated ? reinterpret_cast<uint16_t *>(ws + w.g) : nullptr;
+    uint16_t *xb = reinterpret_cast<uint16_t *>(ws + w.xb);
+    uint16_t *q = reinterpret_cast<uint16_t *>(ws + w.q);
+    uint16_t *k = reinterpret_cast<uint16_t *>(ws + w.k);
+    uint16_t *v = reinterpret_cast<uint16_t *>(ws + w.v);
+    float *beta = reinterpret_cast<float *>(ws + w.beta);
+    float *alpha = reinterpret_cast<float *>(ws + w.alpha);
+    uint16_t *o = reinterpret_cast<uint16_t *>(ws + w.o);
+    int n_gdn = 0, n_swa = 0;
+    for (int i = 0; i < a.n_layers; ++i) (a.kinds[i] == 0 ? n_gdn : n_swa)++;
+    const size_t state_elems = (size_t)a.B * a.H * a.d * a.d;
+    const size_t ring_elems = (size_t)a.B * a.H * a.window * a.d;
+
+    hipError_t e = launch_cast_residual(a.h, a.h, xb, (size_t)M * a.D, s);
+    if (e != hipSuccess) return e;
+    GdnArgs g{};
+    g.B = a.B; g.L = 1; g.H = a.H; g.dk = a.d; g.dv = a.d; g.chunk = 64;
+    g.qkv_bf16 = 1; g.out_bf16 = 1; g.channel = 0;
+    g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta; g.out = o; g.gate = gt;
+    SwaDecodeArgs sw{};
+    sw.B = a.B; sw.H = a.H; sw.d = a.d; sw.window = a.window; sw.out_bf16 = 1;
+    sw.q = q; sw.k = k; sw.v = v; sw.pos = a.pos; sw.out = o; sw.gate = gt;
+    for (int t = 0; t < a.T; ++t) {
+        int gi = 0, si = 0;   // this loop's gated-delta and window layers so far
+        for (int i = 0; i < a.n_layers; ++i) {
+            if (a.kinds[i] == 0) {
+                e = launch_gemm_proj(xb, a.W_in[i], M, NR * Hd + 2 * a.H, a.D, q, k, v, gt, beta, alpha, a.H, a.d, s);
+                g.state_in = g.state_out = a.states + ((size_t)t * n_gdn + gi++) * state_elems;
+                if (e == hipSuccess) e = launch_decode(g, s);
+            } else {
+                e = launch_gemm_proj(xb, a.W_in[i], M, NR * Hd, a.D, q, k, v, gt, nullptr, nullptr, a.H, a.d, s,
+                                     false);
+                const size_t r = ((size_t)t * n_swa + si++) * ring_elems;
+                sw.k_cache = a.k_rings + r;
+                sw.v_cache = a.v_rings + r;
+                if (e == hipSuccess) e = launch_swa_decode(sw, s);
+            }
+            if (e == hipSuccess) e = launch_gemm_resid(o, a.W_o[i], M, a.D, Hd, a.h, xb, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
 }  // namespace lt2

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const uint16_t *__restr
                                                          const uint16_t *__restrict__ k,
                                                          const uint16_t *__restrict__ v, uint16_t *__restrict__ kc,
                                                          uint16_t *__restrict__ vc, const int32_t *__restrict__ pos,
-                                                         TO *__restrict__ out, int H, int W, float qscale) {
+                                                         TO *__restrict__ out, int H, int W, float qscale,
+                                                         const uint16_t *__restrict__ gate) {
     constexpr int G = D / 8;       // lanes per key
     constexpr int NG = 256 / G;    // key groups
     static_assert(64 % G == 0, "a key group lies within one wave");
@@ -133,7 +134,9 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const uint16_t *__restr
             num += f * gacc[g][tid];
             den += f * gsum[g];
         }
-        out[unit * D + tid] = to_out<TO>(num / den);
+        float o = num / den;
+        if (gate) o *= bf16_to_f32(gate[unit * D + tid]);   // output gate of the looped hybrid block
+        out[unit * D + tid] = to_out<TO>(o);
     }
 }
 
@@ -144,11 +147,13 @@ hipError_t launch_d(const SwaDecodeArgs &a, hipStream_t s) {
     if (a.out_bf16)
         hipLaunchKernelGGL((swa_decode_kernel<D, uint16_t>), dim3(grid), dim3(256), 0, s, (const uint16_t *)a.q,
                            (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.k_cache,
-                           (uint16_t *)a.v_cache, a.pos, (uint16_t *)a.out, a.H, a.window, qscale);
+                           (uint16_t *)a.v_cache, a.pos, (uint16_t *)a.out, a.H, a.window, qscale,
+                           a.gate);
     else
         hipLaunchKernelGGL((swa_decode_kernel<D, float>), dim3(grid), dim3(256), 0, s, (const uint16_t *)a.q,
                            (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.k_cache,
-                           (uint16_t *)a.v_cache, a.pos, (float *)a.out, a.H, a.window, qscale);
+                           (uint16_t *)a.v_cache, a.pos, (float *)a.out, a.H, a.window, qscale,
+                           a.gate);
     return hipGetLastError();
 }
 

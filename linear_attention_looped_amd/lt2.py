@@ -97,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.lt2_hybrid_mixer_workspace_size.restype = Z
         L.lt2_hybrid_mixer.argtypes = [HD, P, P, P, P, P, Z, P]
         L.lt2_hybrid_mixer.restype = S
+        L.lt2_hybrid_decode_workspace_size.argtypes = [HD]
+        L.lt2_hybrid_decode_workspace_size.restype = Z
+        L.lt2_hybrid_decode_step.argtypes = [HD, P, P, P, P, P, P, P, P, Z, P]
+        L.lt2_hybrid_decode_step.restype = S
         L.lt2_hbm_copy.argtypes = [P, P, Z, P]
         L.lt2_hbm_copy.restype = S
         L.lt2_hbm_probe.argtypes = [P, P, Z, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
@@ -456,6 +460,52 @@ def lt2_hybrid_mixer(h_in, layers, H: int, d_head: int, T: int, window: int, chu
                                   ctypes.cast(w_o, ctypes.c_void_p), _ptr(workspace), nbytes, _stream(stream))
     _check("lt2_hybrid_mixer", code)
     return h_out
+
+
+def lt2_hybrid_decode_step(h, layers, states, k_rings, v_rings, pos, H: int, d_head: int, T: int, window: int,
+                           workspace=None, stream=None, out_gate: bool = False):
+    """One decode token per sequence through T loops of a shared layer stack
+    (``layers`` as for lt2_hybrid_mixer).  h [B,D] fp32, states
+    [T,n_gdn,B,H,d,d] fp32 and the rings [T,n_swa,B,H,window,d] bf16 are
+    updated in place; pos [B] int32 on the device (not advanced).  Returns h."""
+    B, D = _dims(h, 2, "h")
+    _expect(h, "h", dtypes=torch.float32)
+    dev = h.device
+    if not 1 <= len(layers) <= LT2_MAX_LAYERS:
+        raise ValueError(f"a hybrid block has 1 .. {LT2_MAX_LAYERS} layers, got {len(layers)}")
+    for i, (kind, w_in, w_o) in enumerate(layers):
+        if kind not in _KINDS:
+            raise ValueError(f"layer {i}: unknown kind {kind!r}")
+        _expect(w_in, f"layer {i} W_in", (_w_in_rows(H, d_head, out_gate, kind == "gdn"), D), torch.bfloat16)
+        _expect(w_o, f"layer {i} W_o", (D, H * d_head), torch.bfloat16)
+    n_gdn = sum(k == "gdn" for k, _, _ in layers)
+    n_swa = len(layers) - n_gdn
+    tensors = dict(h=h, pos=pos)
+    _expect(pos, "pos", (B,), torch.int32)
+    if n_gdn:
+        _expect(states, "states", (T, n_gdn, B, H, d_head, d_head), torch.float32)
+        tensors["states"] = states
+    if n_swa:
+        _expect(k_rings, "k_rings", (T, n_swa, B, H, int(window), d_head), torch.bfloat16)
+        _expect(v_rings, "v_rings", (T, n_swa, B, H, int(window), d_head), torch.bfloat16)
+        tensors.update(k_rings=k_rings, v_rings=v_rings)
+    desc = hybrid_desc(B, 1, D, H, d_head, T, [k for k, _, _ in layers], int(window), 64, out_gate)
+    workspace, nbytes = _ws(workspace, lt2_hybrid_decode_workspace_size(desc), dev)
+    n = len(layers)
+    w_in = (ctypes.c_void_p * n)(*[w.data_ptr() for _, w, _ in layers])
+    w_o = (ctypes.c_void_p * n)(*[w.data_ptr() for _, _, w in layers])
+    _on_device(dev, **tensors, **{f"layer{i}_W_in": w for i, (_, w, _) in enumerate(layers)},
+               **{f"layer{i}_W_o": w for i, (_, _, w) in enumerate(layers)})
+    code = lib().lt2_hybrid_decode_step(ctypes.byref(desc), _ptr(h), ctypes.cast(w_in, ctypes.c_void_p),
+                                        ctypes.cast(w_o, ctypes.c_void_p), _ptr(states) if n_gdn else None,
+                                        _ptr(k_rings) if n_swa else None, _ptr(v_rings) if n_swa else None,
+                                        _ptr(pos), _ptr(workspace), nbytes, _stream(stream))
+    _check("lt2_hybrid_decode_step", code)
+    return h
+
+
+def lt2_hybrid_decode_workspace_size(desc: lt2_hybrid_desc) -> int:
+    return int(lib().lt2_hybrid_decode_workspace_size(ctypes.byref(desc)))
 
 
 def lt2_hbm_copy(dst, src, stream=None):

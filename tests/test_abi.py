@@ -337,3 +337,29 @@ def test_backward_validation():
     # nothing to do for an empty batch
     assert bwd_call(good_desc(B=0), q=None, k=None, v=None, alpha=None, beta=None, d_out=None, dq=None, dk=None,
                     dv=None, dla=None, db=None, ws=None, ws_bytes=0) == 0
+
+
+def hybrid_dec_call(desc, h=FAKE, w_in=(FAKE, FAKE), w_o=(FAKE, FAKE), states=FAKE, kr=FAKE, vr=FAKE, pos=FAKE,
+                    ws=FAKE, ws_bytes=1 << 40):
+    P = ctypes.c_void_p
+    wi = (P * len(w_in))(*w_in)
+    wo = (P * len(w_o))(*w_o)
+    return lt2.lib().lt2_hybrid_decode_step(ctypes.byref(desc), P(h), ctypes.cast(wi, P), ctypes.cast(wo, P),
+                                            P(states), P(kr), P(vr), P(pos), P(ws), ws_bytes, None)
+
+
+def test_hybrid_decode_validation():
+    """The looped hybrid decode step takes one token (L = 1); every refused call
+    returns before any launch."""
+    assert hybrid_dec_call(good_hybrid(L=2)) == 2
+    assert hybrid_dec_call(good_hybrid(L=1, window=0)) == 2
+    assert hybrid_dec_call(good_hybrid(L=1), h=None) == 1
+    assert hybrid_dec_call(good_hybrid(L=1), pos=None) == 1
+    assert hybrid_dec_call(good_hybrid(L=1), kr=None) == 1                     # a window layer needs its rings
+    assert hybrid_dec_call(good_hybrid(("gdn",), L=1), w_in=(FAKE,), w_o=(FAKE,), states=None) == 1
+    assert hybrid_dec_call(good_hybrid(L=1), states=FAKE + 8) == 6
+    assert hybrid_dec_call(good_hybrid(L=1), ws_bytes=16) == 5
+    need = lt2.lib().lt2_hybrid_decode_workspace_size(ctypes.byref(good_hybrid(L=1)))
+    assert need > 0 and lt2.lib().lt2_hybrid_decode_workspace_size(ctypes.byref(good_hybrid(L=2))) == 0
+    assert hybrid_dec_call(good_hybrid(L=1, B=0), h=None, states=None, kr=None, vr=None, pos=None, ws=None,
+                           ws_bytes=0) == 0

@@ -115,3 +115,34 @@ def test_hybrid_full_size_prefix():
     ref = oracle.hybrid_mixer(h0[0:1, :P], hl, shape.H, shape.d, shape.T, 512)
     assert rel_err(got[0:1, :P], ref) <= TOL_BF16
     assert rel_err(got[0:1, :P] - h0[0:1, :P], ref - h0[0:1, :P]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("kinds,window,gate", [(("gdn", "swa"), 8, False), (("swa", "gdn"), 5, True),
+                                               (("swa",), 3, False), (("gdn", "swa"), 64, False)])
+def test_hybrid_decode_chain_matches_mixer(kinds, window, gate):
+    """Token-by-token looped hybrid decode from zero states and empty rings gives,
+    for every token, the h of the oracle's hybrid block on the whole sequence
+    (every layer is causal); rings wrap when L > w, stay partly filled when
+    L < w.  Four layer applications at most (T 2), as for the prefill cases."""
+    B, L, D, H, d, T = 2, 24, 256, 2, 64, 2
+    shape = synth.LoopShape(B, L, D, H, d, T)
+    announce(f"hybrid decode chain kinds={kinds} w={window} gate={gate}")
+    host_layers, dev_layers = make_layers(shape, kinds, seed=6, gate=gate)
+    h0 = synth.loop_h0(shape, seed=6)
+    ref = oracle.hybrid_mixer(h0, host_layers, H, d, T, window, gate=gate)
+    n_gdn = sum(k == "gdn" for k in kinds)
+    n_swa = len(kinds) - n_gdn
+    states = torch.zeros((T, max(n_gdn, 1), B, H, d, d), dtype=torch.float32, device="cuda")[:, :n_gdn]
+    kr = torch.zeros((T, max(n_swa, 1), B, H, window, d), dtype=torch.bfloat16, device="cuda")[:, :n_swa]
+    vr = torch.zeros_like(kr)
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+    got = np.empty_like(h0)
+    for t in range(L):
+        h = torch.from_numpy(np.ascontiguousarray(h0[:, t], np.float32)).to("cuda")
+        lt2.lt2_hybrid_decode_step(h, dev_layers, states.contiguous() if n_gdn else None, kr if n_swa else None,
+                                   vr if n_swa else None, pos, H, d, T, window, out_gate=gate)
+        got[:, t] = host(h)
+        pos += 1
+    torch.cuda.synchronize()
+    assert rel_err(got, ref) <= TOL_BF16
+    assert rel_err(got - h0, ref - h0) <= TOL_BF16
