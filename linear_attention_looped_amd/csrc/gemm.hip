@@ -197,8 +197,6 @@ void gemm_bf16_nt_kernel(const uint16_t *__restrict__ A, const uint16_t *__restr
     constexpr int WR = 2 * BM / NW;     // rows of a wave tile
     constexpr int NI = WR / 32;         // 32-row accumulator tiles per wave
     constexpr int NCH = 32 / NW;        // 1 KiB DMA chunks per wave per operand and K-tile
-    constexpr int NR = NI + 4;          // fragment reads per k-step
-    constexpr int NMF = 4 * NI;         // products per k-step
     // two buffers as four distinct arrays: the compiler can then tell that the DMA
     // into one buffer does not alias the fragment reads of the other
     __shared__ __attribute__((aligned(1024))) uint16_t A0[BM * BK], A1[BM * BK], B0[BN * BK], B1[BN * BK];
