@@ -13,7 +13,8 @@
 // each group keeps an online softmax (running maximum, sum and its lanes' eight
 // output channels) in base 2, the score scale log2(e)/sqrt(d) folded into q.
 // The groups' partial results meet in LDS at the end.  The ring is streamed
-// once (2 w d bytes of bf16 per (b, h) and token): the kernel is HBM-bound.
+// once (2 w d bytes of bf16 per (b, h) and token): the kernel is HBM-bound and
+// reads nearly only, so its ceiling is the read stream's.
 //
 // The new key and value are written to their slot and also kept in LDS; a
 // group reading that slot takes the LDS copy, so no lane depends on seeing the
@@ -84,17 +85,19 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const uint16_t *__restr
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     const uint4 *kr = reinterpret_cast<const uint4 *>(kc + ring) + gl;
     const uint4 *vr = reinterpret_cast<const uint4 *>(vc + ring) + gl;
-    // each group's next key and value are loaded one step ahead
+    // each group's next key and value are loaded one step ahead, with the
+    // non-temporal hint (each ring row is read once per launch): 189.8 -> 170.1
+    // us on 256 x 16 rings of 512 (loading a second key ahead: 172.8 us)
     uint4 kp = kn, vp = vn;
     if (grp < n) {
-        kp = kr[(size_t)grp * G];
-        vp = vr[(size_t)grp * G];
+        kp = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kr + (size_t)grp * G)));
+        vp = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vr + (size_t)grp * G)));
     }
     for (int j = grp; j < n; j += NG) {
         uint4 ku = kp, vu = vp;
         if (j + NG < n) {
-            kp = kr[(size_t)(j + NG) * G];
-            vp = vr[(size_t)(j + NG) * G];
+            kp = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kr + (size_t)(j + NG) * G)));
+            vp = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vr + (size_t)(j + NG) * G)));
         }
         if (j == slot) {   // uniform over the group
             ku = kn;
