@@ -424,6 +424,31 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(const float *__rest
     }
 }
 
+// The same sums four elements at a time when the token count is a multiple of
+// four (every partial buffer then starts 16-byte aligned and no group of four
+// straddles two outputs): 16-byte non-temporal loads (each partial is read
+// once), all NCB of an element group in flight, added in the same order as
+// above, so the results are bit-identical.
+template <int NCB>
+__global__ __launch_bounds__(256) void kda_bwd_reduce4_kernel(const float *__restrict__ part, size_t n_tok, int D,
+                                                              float *__restrict__ dq, float *__restrict__ dk,
+                                                              float *__restrict__ dla, float *__restrict__ dbeta) {
+    const size_t n_row = n_tok * (size_t)D, stride4 = (3 * n_row + n_tok) / 4;
+    const f32x4 *p4 = reinterpret_cast<const f32x4 *>(part);
+    for (size_t i4 = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i4 < stride4; i4 += (size_t)gridDim.x * blockDim.x) {
+        f32x4 x[NCB];
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) x[c] = __builtin_nontemporal_load(p4 + (size_t)c * stride4 + i4);
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) sum += x[c];
+        const size_t i = 4 * i4;
+        float *dst = i < n_row ? dq + i : (i < 2 * n_row ? dk + (i - n_row)
+                                                            : (i < 3 * n_row ? dla + (i - 2 * n_row) : dbeta + (i - 3 * n_row)));
+        *reinterpret_cast<f32x4 *>(dst) = sum;
+    }
+}
+
 template <int D, typename TI, typename TO>
 hipError_t run_kda(const GdnBwdArgs &a, hipStream_t s) {
     const KdaLayout w = kda_layout(a.B, a.L, a.H, D);
@@ -438,9 +463,19 @@ hipError_t run_kda(const GdnBwdArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const size_t n_tok = (size_t)a.B * a.L * a.H;
     const size_t total = 3 * n_tok * D + n_tok;
-    const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
-    hipLaunchKernelGGL(kda_bwd_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, D / KBV, n_tok, D, a.dq, a.dk,
-                       a.dlog_alpha, a.dbeta);
+    // the vector form needs 16-byte aligned outputs too (the row gradients are)
+    const bool vec = n_tok % 4 == 0 && ((uintptr_t)a.dq | (uintptr_t)a.dk | (uintptr_t)a.dlog_alpha |
+                                        (uintptr_t)a.dbeta) % 16 == 0;
+    if (vec) {
+        const size_t total4 = total / 4;
+        const unsigned blocks = (unsigned)((total4 + 255) / 256 < 65536 ? (total4 + 255) / 256 : 65536);
+        hipLaunchKernelGGL((kda_bwd_reduce4_kernel<D / KBV>), dim3(blocks), dim3(256), 0, s, part, n_tok, D, a.dq,
+                           a.dk, a.dlog_alpha, a.dbeta);
+    } else {
+        const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+        hipLaunchKernelGGL(kda_bwd_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, D / KBV, n_tok, D, a.dq, a.dk,
+                           a.dlog_alpha, a.dbeta);
+    }
     return hipGetLastError();
 }
 
