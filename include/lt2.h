@@ -307,14 +307,15 @@ lt2_status lt2_swa_prefill(const lt2_swa_desc *desc, const void *q, const void *
  *   k_cache, v_cache  [B, H, window, d] bf16, owned by the caller and updated
  *                     in place (slot pos[b] mod window); slots past pos[b] are
  *                     never read while pos[b] < window - 1, so fresh rings need
- *                     no initialisation
+ *                     no initialisation; two distinct, non-overlapping buffers
+ *                     (out must not overlap q, k, v or the rings either)
  *   pos               [B] int32 in device memory: tokens sequence b has already
  *                     seen (the new token's position); negative values are
  *                     taken as 0.  The call does not advance it.
  *   out               [B, H, d] bf16 or fp32 (desc->out_dtype), 16-byte aligned
  * Scores, the softmax and the value sums are fp32.  No workspace.
- * Errors: LT2_ERR_SHAPE for L != 1, negative B, H or d <= 0, window < 1 or
- * B * H beyond 2^31 - 1; LT2_ERR_DTYPE / LT2_ERR_UNSUPPORTED as for
+ * Errors: LT2_ERR_SHAPE for L != 1, negative B, H or d <= 0, window < 1,
+ * B * H beyond 2^31 - 1 or overlapping rings; LT2_ERR_DTYPE / LT2_ERR_UNSUPPORTED as for
  * lt2_swa_prefill; LT2_ERR_NULL for a missing pointer when B > 0;
  * LT2_ERR_ALIGN for misaligned buffers (pos: 4 bytes).
  */
@@ -382,11 +383,12 @@ lt2_status lt2_hybrid_mixer(const lt2_hybrid_desc *desc, const float *h_in, floa
  *   states    [T, n_gdn, B, H, d_head, d_head] fp32, in place (n_gdn = number of
  *             gated-delta layers, indexed in stack order); may be NULL if none
  *   k_rings, v_rings  [T, n_swa, B, H, window, d_head] bf16, in place (n_swa =
- *             number of window layers); slot pos[b] mod window is written
+ *             number of window layers), two non-overlapping buffers; slot
+ *             pos[b] mod window is written
  *   pos       [B] int32 in device memory: tokens sequence b has already seen;
  *             not advanced by the call
  *   ws        lt2_hybrid_decode_workspace_size(desc) bytes, 256-byte aligned
- * Errors: as lt2_hybrid_mixer; LT2_ERR_SHAPE for L != 1.
+ * Errors: as lt2_hybrid_mixer; LT2_ERR_SHAPE for L != 1 or overlapping rings.
  */
 size_t lt2_hybrid_decode_workspace_size(const lt2_hybrid_desc *desc);
 lt2_status lt2_hybrid_decode_step(const lt2_hybrid_desc *desc, float *h, const void *const *W_in,

@@ -240,6 +240,10 @@ lt2_status lt2_swa_decode_step(const lt2_swa_desc *desc, const void *q, const vo
         !aligned(out, 16) || !aligned(pos, 4))
         return LT2_ERR_ALIGN;
     if (desc->B == 0) return LT2_OK;
+    // the rings are distinct buffers (the kernel writes one slot of each and reads the others)
+    const size_t ring_bytes = (size_t)desc->B * desc->H * desc->window * desc->d * 2;
+    const uintptr_t kb = (uintptr_t)k_cache, vb = (uintptr_t)v_cache;
+    if (kb < vb + ring_bytes && vb < kb + ring_bytes) return LT2_ERR_SHAPE;
     SwaDecodeArgs a;
     a.B = desc->B; a.H = desc->H; a.d = desc->d; a.window = desc->window;
     a.out_bf16 = desc->out_dtype == LT2_BF16;
@@ -493,6 +497,12 @@ lt2_status lt2_hybrid_decode_step(const lt2_hybrid_desc *desc, float *h, const v
     if (need > 0 && (!ws || ws_bytes < need)) return LT2_ERR_WORKSPACE;
     if (need > 0 && !aligned(ws, 256)) return LT2_ERR_ALIGN;
     if (!work) return LT2_OK;
+    if (n_swa > 0) {   // distinct key and value rings
+        const size_t ring_bytes =
+            (size_t)desc->T * n_swa * desc->B * desc->H * desc->window * desc->d_head * 2;
+        const uintptr_t kb = (uintptr_t)k_rings, vb = (uintptr_t)v_rings;
+        if (kb < vb + ring_bytes && vb < kb + ring_bytes) return LT2_ERR_SHAPE;
+    }
     HybridDecodeArgs a{};
     a.B = desc->B; a.D = desc->d_model; a.H = desc->H; a.d = desc->d_head; a.T = desc->T;
     a.gated = desc->out_gate; a.window = desc->window; a.n_layers = desc->n_layers;

@@ -264,6 +264,8 @@ def test_swa_decode_null_and_alignment():
         assert swa_dec_call(good_swa(L=1), **{name: None}) == 1, name
     assert swa_dec_call(good_swa(L=1), kc=FAKE + 8) == 6
     assert swa_dec_call(good_swa(L=1), pos=FAKE + 2) == 6
+    assert swa_dec_call(good_swa(L=1), kc=FAKE, vc=FAKE) == 2                  # one buffer as both rings
+    assert swa_dec_call(good_swa(L=1), kc=FAKE, vc=FAKE + 4096) == 2           # overlapping rings
     # no sequences: nothing is read or written
     assert swa_dec_call(good_swa(L=1, B=0), q=None, k=None, v=None, kc=None, vc=None, pos=None, out=None) == 0
 
@@ -359,6 +361,7 @@ def test_hybrid_decode_validation():
     assert hybrid_dec_call(good_hybrid(("gdn",), L=1), w_in=(FAKE,), w_o=(FAKE,), states=None) == 1
     assert hybrid_dec_call(good_hybrid(L=1), states=FAKE + 8) == 6
     assert hybrid_dec_call(good_hybrid(L=1), ws_bytes=16) == 5
+    assert hybrid_dec_call(good_hybrid(L=1), kr=FAKE, vr=FAKE) == 2            # one buffer as both rings
     need = lt2.lib().lt2_hybrid_decode_workspace_size(ctypes.byref(good_hybrid(L=1)))
     assert need > 0 and lt2.lib().lt2_hybrid_decode_workspace_size(ctypes.byref(good_hybrid(L=2))) == 0
     assert hybrid_dec_call(good_hybrid(L=1, B=0), h=None, states=None, kr=None, vr=None, pos=None, ws=None,
